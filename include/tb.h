@@ -1,0 +1,153 @@
+/*
+ * tb.h -- C ABI of the theta-bundle projection library (libtb.so), gfx950.
+ *
+ * The theta bundle ("The theta bundle", weightless docs, component table)
+ * replaces a projection's dense weight [out_dim, in_dim] by
+ *     W0 [out_dim, in_dim]   shared by every layer of a band, per family,
+ *     s  [out_dim]           per layer, a scale of each output row of W0,
+ *     U  [out_dim, rank]     per layer, left factor of the low-rank delta,
+ *     V  [in_dim,  rank]     per layer, right factor of the low-rank delta,
+ * with the weight rebuilt as diag(s) . W0 + U . V^T.  The band whose W0 a
+ * layer uses comes from the contiguous band map ("Banded sharing", section
+ * "How layers map to bands").
+ *
+ * Conventions shared by every entry point
+ *   - Matrices are dense, row-major, with the leading dimension equal to the
+ *     row length.  All pointers except band_out are DEVICE pointers on the
+ *     current HIP device.  The caller owns all memory; the library allocates
+ *     nothing, frees nothing and keeps no pointer after a call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device work is enqueued on it asynchronously; outputs are valid once
+ *     the caller synchronises that stream.  No entry point synchronises.
+ *   - Arguments are checked on the host before anything is enqueued.  On any
+ *     status other than TB_OK nothing was enqueued and no output was written.
+ *     tb_last_error() then describes the problem (per calling thread).
+ *   - Matrix base pointers (x, w0, u, v, original, reconstructed, w_out) must
+ *     be 16-byte aligned and in_dim / cols must be a multiple of 8; otherwise
+ *     the call returns TB_ERR_UNSUPPORTED.  Every Gemma-shaped projection
+ *     satisfies this.  s and y need only element alignment.
+ *   - Sizes are 64-bit; an element count must fit in int64.
+ */
+#ifndef TB_H
+#define TB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tb_status {
+  TB_OK = 0,
+  TB_ERR_INVALID_ARGUMENT = 1, /* a NULL pointer, a size out of range, ...  */
+  TB_ERR_UNSUPPORTED = 2,      /* alignment / divisibility / dtype combination */
+  TB_ERR_HIP = 3               /* the HIP runtime refused a query or launch  */
+} tb_status;
+
+typedef enum tb_dtype {
+  TB_F32 = 0,  /* IEEE binary32 */
+  TB_BF16 = 1  /* bfloat16, round-to-nearest-even on every store */
+} tb_dtype;
+
+/* Bytes of workspace whose first TB_WORKSPACE_CONTROL_BYTES must be zero. */
+#define TB_WORKSPACE_CONTROL_BYTES 65536
+
+/* Fixed workspace size of tb_rel_frobenius_error. */
+#define TB_FROBENIUS_WORKSPACE_BYTES 65536
+
+/*
+ * tb_band_index -- band of one layer ("Banded sharing", "How layers map to
+ * bands").  The num_layers layers are split into num_bands contiguous bands
+ * whose sizes differ by at most one, the earlier bands taking the remainder:
+ * with q = num_layers / num_bands and m = num_layers % num_bands, bands
+ * 0..m-1 hold q+1 layers and the others q.  num_bands = 1 shares one W0 by
+ * all layers; num_bands = num_layers is passthrough (band == layer).
+ *
+ *   num_layers >= 1, 1 <= num_bands <= num_layers, 0 <= layer < num_layers,
+ *   band_out is a HOST pointer.  Host-only and pure; it touches no device.
+ *   Errors: TB_ERR_INVALID_ARGUMENT (band_out untouched).
+ */
+tb_status tb_band_index(int32_t num_layers, int32_t num_bands, int32_t layer, int32_t *band_out);
+
+/*
+ * tb_linear_forward_workspace_size -- bytes of workspace tb_linear_forward
+ * needs for these sizes on the current device (host-only query; it reads the
+ * device's compute-unit count once).  *bytes_out >= TB_WORKSPACE_CONTROL_BYTES.
+ */
+tb_status tb_linear_forward_workspace_size(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
+                                           tb_dtype dtype, size_t *bytes_out);
+
+/*
+ * tb_linear_forward -- one theta-bundle projection.
+ *
+ *     y[t, o] = s[o] * sum_i x[t, i] W0[o, i]  +  sum_j (sum_i x[t, i] V[i, j]) U[o, j]
+ *
+ * i.e. y = s (.) (x . W0^T) + (x . V) . U^T, the transpose of the
+ * reconstruction formula weight = diag(s) W0 + U V^T ("The theta bundle"),
+ * applied without forming the weight.  W0 is the block of the layer's band
+ * (the caller selects it with tb_band_index).
+ *
+ *   x  [m, in_dim]        activations              (dtype)
+ *   s  [out_dim]          row scale                (dtype)
+ *   w0 [out_dim, in_dim]  shared block             (dtype)
+ *   u  [out_dim, rank]    left factor              (dtype; NULL allowed iff rank == 0)
+ *   v  [in_dim, rank]     right factor             (dtype; NULL allowed iff rank == 0)
+ *   y  [m, out_dim]       output                   (dtype), written, must not alias inputs
+ *   m >= 1 tokens, out_dim >= 1, in_dim >= 8 and % 8 == 0, rank >= 0.
+ *   Arithmetic: products and sums in fp32 (bf16 inputs are exact in fp32);
+ *   the scale is applied to the fp32 sum before the delta is added; for bf16
+ *   the intermediate x . V is rounded to bf16 before it meets U.  y is
+ *   rounded once at the end.  Results are deterministic run to run.
+ *   workspace: device buffer of at least tb_linear_forward_workspace_size()
+ *   bytes, 256-byte aligned.  Its first TB_WORKSPACE_CONTROL_BYTES bytes are
+ *   control words that must be zero before the first call that uses the
+ *   buffer; every call that completes leaves them zero again.  Calls that may
+ *   run at the same time (different streams) must not share a workspace.
+ *   Errors: TB_ERR_INVALID_ARGUMENT, TB_ERR_UNSUPPORTED, TB_ERR_HIP.
+ */
+tb_status tb_linear_forward(const void *x, const void *s, const void *w0, const void *u, const void *v,
+                            void *y, int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
+                            tb_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * tb_reconstruct_weight -- w_out = diag(s) . W0 + U . V^T ("The theta bundle",
+ * reconstruct_weight(s, W0, U, V)).
+ *
+ *   s [out_dim], w0 [out_dim, in_dim], u [out_dim, rank], v [in_dim, rank]
+ *   in in_dtype; w_out [out_dim, in_dim] in out_dtype.  rank >= 0 (u, v may
+ *   be NULL iff rank == 0), in_dim % 8 == 0.  fp32 accumulation; with
+ *   rank == 0 and fp32 output the result is exact (s * W0 of bf16 inputs is
+ *   representable in fp32).  Errors as above.
+ */
+tb_status tb_reconstruct_weight(const void *s, const void *w0, const void *u, const void *v, void *w_out,
+                                int64_t out_dim, int64_t in_dim, int64_t rank,
+                                tb_dtype in_dtype, tb_dtype out_dtype, void *stream);
+
+/*
+ * tb_rel_frobenius_error -- ||original - reconstructed||_F / ||original||_F
+ * ("Quality", section "Reconstruction error"; the argument order of
+ * relative_frobenius_error(original, reconstructed) in "The theta bundle").
+ *
+ *   original, reconstructed: [rows, cols] in dtype, cols % 8 == 0.
+ *   result_device: DEVICE pointer to one double, written.  Differences,
+ *   squares and sums are taken in fp64 in a fixed order (deterministic).
+ *   When the difference is zero the result is 0; when only the original is
+ *   zero it is +inf.  workspace: >= TB_FROBENIUS_WORKSPACE_BYTES device bytes,
+ *   8-byte aligned (no zeroing needed).  Errors as above.
+ */
+tb_status tb_rel_frobenius_error(const void *original, const void *reconstructed, int64_t rows, int64_t cols,
+                                 tb_dtype dtype, double *result_device, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *tb_status_string(tb_status status);
+
+/* Description of the last failure on the calling thread ("" if none). */
+const char *tb_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TB_H */

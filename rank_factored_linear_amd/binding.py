@@ -1,0 +1,198 @@
+"""Thin Python binding of libtb.so (ctypes).
+
+Argument marshalling only: every step of the projection runs in the HIP
+kernels behind the C ABI declared in ``include/tb.h``.  PyTorch supplies
+device memory and the current HIP stream.  There is no fallback: if the
+library is missing or fails to load, the import raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtb.so")
+
+TB_OK, TB_ERR_INVALID_ARGUMENT, TB_ERR_UNSUPPORTED, TB_ERR_HIP = 0, 1, 2, 3
+TB_F32, TB_BF16 = 0, 1
+WORKSPACE_CONTROL_BYTES = 65536
+FROBENIUS_WORKSPACE_BYTES = 65536
+
+EXPORTED = (
+    "tb_band_index", "tb_linear_forward_workspace_size", "tb_linear_forward",
+    "tb_reconstruct_weight", "tb_rel_frobenius_error", "tb_status_string", "tb_last_error",
+)
+
+
+class TBError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libtb status {status}: {message}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m rank_factored_linear_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    c_i32, c_i64, c_p, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    lib.tb_band_index.argtypes = [c_i32, c_i32, c_i32, ctypes.POINTER(c_i32)]
+    lib.tb_linear_forward_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_i64, ctypes.c_int, ctypes.POINTER(c_sz)]
+    lib.tb_linear_forward.argtypes = [c_p, c_p, c_p, c_p, c_p, c_p, c_i64, c_i64, c_i64, c_i64, ctypes.c_int, c_p, c_sz, c_p]
+    lib.tb_reconstruct_weight.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i64, c_i64, c_i64, ctypes.c_int, ctypes.c_int, c_p]
+    lib.tb_rel_frobenius_error.argtypes = [c_p, c_p, c_i64, c_i64, ctypes.c_int, c_p, c_p, c_sz, c_p]
+    lib.tb_status_string.argtypes = [ctypes.c_int]
+    lib.tb_status_string.restype = ctypes.c_char_p
+    lib.tb_last_error.argtypes = []
+    lib.tb_last_error.restype = ctypes.c_char_p
+    for name in ("tb_band_index", "tb_linear_forward_workspace_size", "tb_linear_forward",
+                 "tb_reconstruct_weight", "tb_rel_frobenius_error"):
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int) -> None:
+    if status != TB_OK:
+        raise TBError(status, lib.tb_last_error().decode())
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return TB_BF16
+    if dt == torch.float32:
+        return TB_F32
+    raise TBError(TB_ERR_UNSUPPORTED, f"dtype {dt} is not supported (bfloat16 or float32)")
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise TBError(TB_ERR_INVALID_ARGUMENT, "tensors must live on the GPU")
+            if not t.is_contiguous():
+                raise TBError(TB_ERR_UNSUPPORTED, "tensors must be contiguous")
+
+
+# ---------------------------------------------------------------------------
+# Workspace: one zero-initialised buffer per (device, stream), grown on
+# demand.  The library returns its control words to zero after every call.
+# ---------------------------------------------------------------------------
+_ws_lock = threading.Lock()
+_ws: dict = {}
+
+
+def workspace_for(nbytes: int) -> torch.Tensor:
+    dev = torch.cuda.current_device()
+    key = (dev, torch.cuda.current_stream().cuda_stream)
+    with _ws_lock:
+        buf = _ws.get(key)
+        if buf is None or buf.numel() < nbytes:
+            size = max(nbytes, WORKSPACE_CONTROL_BYTES)
+            size = (size + (1 << 20) - 1) >> 20 << 20
+            buf = torch.zeros(size, dtype=torch.uint8, device=f"cuda:{dev}")
+            _ws[key] = buf
+        return buf
+
+
+def workspace_error_word() -> int:
+    """Sticky error word of the current stream's workspace (nonzero if a bounded wait timed out)."""
+    key = (torch.cuda.current_device(), torch.cuda.current_stream().cuda_stream)
+    buf = _ws.get(key)
+    if buf is None:
+        return 0
+    return int(buf[:32].view(torch.int32)[5].item())
+
+
+# ---------------------------------------------------------------------------
+# Entry points
+# ---------------------------------------------------------------------------
+
+
+def band_index(num_layers: int, num_bands: int, layer: int) -> int:
+    out = ctypes.c_int32(-1)
+    _check(lib.tb_band_index(num_layers, num_bands, layer, ctypes.byref(out)))
+    return out.value
+
+
+def linear_forward_workspace_size(m: int, out_dim: int, in_dim: int, rank: int, dtype: torch.dtype) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.tb_linear_forward_workspace_size(m, out_dim, in_dim, rank, _dtype_code(dtype), ctypes.byref(out)))
+    return out.value
+
+
+def linear_forward(x: torch.Tensor, s: torch.Tensor, W0: torch.Tensor, U: torch.Tensor | None,
+                   V: torch.Tensor | None, out: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y = s * (x @ W0.T) + (x @ V) @ U.T on the GPU, via tb_linear_forward."""
+    m, in_dim = x.shape
+    out_dim = W0.shape[0]
+    rank = 0 if U is None else U.shape[1]
+    if U is not None and rank == 0:
+        U = V = None
+    _need_cuda(x, s, W0, U, V, out)
+    dt = _dtype_code(x.dtype)
+    for t in (s, W0, U, V):
+        if t is not None and t.dtype != x.dtype:
+            raise TBError(TB_ERR_INVALID_ARGUMENT, "all inputs must share one dtype")
+    if tuple(W0.shape) != (out_dim, in_dim) or tuple(s.shape) != (out_dim,):
+        raise TBError(TB_ERR_INVALID_ARGUMENT, "W0 must be [out, in] and s [out]")
+    if rank and (tuple(U.shape) != (out_dim, rank) or tuple(V.shape) != (in_dim, rank)):
+        raise TBError(TB_ERR_INVALID_ARGUMENT, "U must be [out, rank] and V [in, rank]")
+    if out is None:
+        out = torch.empty((m, out_dim), dtype=x.dtype, device=x.device)
+    need = linear_forward_workspace_size(m, out_dim, in_dim, rank, x.dtype)
+    ws = workspace if workspace is not None else workspace_for(need)
+    _check(lib.tb_linear_forward(_ptr(x), _ptr(s), _ptr(W0), _ptr(U), _ptr(V), _ptr(out), m, out_dim, in_dim, rank,
+                                 dt, _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return out
+
+
+def reconstruct_weight(s: torch.Tensor, W0: torch.Tensor, U: torch.Tensor | None, V: torch.Tensor | None,
+                       out_dtype: torch.dtype = torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
+    """diag(s) @ W0 + U @ V.T on the GPU, via tb_reconstruct_weight."""
+    out_dim, in_dim = W0.shape
+    rank = 0 if U is None else U.shape[1]
+    if U is not None and rank == 0:
+        U = V = None
+    _need_cuda(s, W0, U, V, out)
+    if out is None:
+        out = torch.empty((out_dim, in_dim), dtype=out_dtype, device=W0.device)
+    _check(lib.tb_reconstruct_weight(_ptr(s), _ptr(W0), _ptr(U), _ptr(V), _ptr(out), out_dim, in_dim, rank,
+                                     _dtype_code(W0.dtype), _dtype_code(out.dtype), _stream()))
+    return out
+
+
+_frob_ws: dict = {}
+
+
+def rel_frobenius_error(original: torch.Tensor, reconstructed: torch.Tensor,
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """||original - reconstructed||_F / ||original||_F as a 0-d float64 GPU tensor (no sync)."""
+    _need_cuda(original, reconstructed, out)
+    if original.shape != reconstructed.shape or original.dtype != reconstructed.dtype or original.dim() != 2:
+        raise TBError(TB_ERR_INVALID_ARGUMENT, "original and reconstructed must be 2-D with one shape and dtype")
+    rows, cols = original.shape
+    if out is None:
+        out = torch.empty((), dtype=torch.float64, device=original.device)
+    key = (torch.cuda.current_device(), torch.cuda.current_stream().cuda_stream)
+    ws = _frob_ws.get(key)
+    if ws is None:
+        ws = torch.empty(FROBENIUS_WORKSPACE_BYTES, dtype=torch.uint8, device=original.device)
+        _frob_ws[key] = ws
+    _check(lib.tb_rel_frobenius_error(_ptr(original), _ptr(reconstructed), rows, cols, _dtype_code(original.dtype),
+                                      _ptr(out), _ptr(ws), ws.numel(), _stream()))
+    return out

@@ -1,0 +1,205 @@
+// C ABI of libtb: host-side argument checks and dispatch.  Every check runs
+// before anything is enqueued, so a failing call leaves all outputs untouched.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "tb_host.h"
+
+namespace tb {
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+tb_status fail(tb_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+tb_status ok() {
+  g_last_error[0] = '\0';
+  return TB_OK;
+}
+
+tb_status hip_fail(hipError_t e, const char* what) {
+  return fail(TB_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+size_t esize(tb_dtype d) { return d == TB_BF16 ? 2 : 4; }
+bool valid_dtype(tb_dtype d) { return d == TB_F32 || d == TB_BF16; }
+
+constexpr int kMaxDevices = 64;
+int g_cus[kMaxDevices];  // 0 = not queried yet (benign race: every writer stores the same value)
+
+// Shapes the kernels index with 32-bit ints.
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+
+tb_status check_dims(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank) {
+  if (m < 1 || out_dim < 1 || in_dim < 1 || rank < 0)
+    return fail(TB_ERR_INVALID_ARGUMENT, "need m >= 1, out_dim >= 1, in_dim >= 1, rank >= 0 (got %lld, %lld, %lld, %lld)",
+                (long long)m, (long long)out_dim, (long long)in_dim, (long long)rank);
+  if (m > kMaxDim || out_dim > kMaxDim || in_dim > kMaxDim || rank > kMaxDim)
+    return fail(TB_ERR_UNSUPPORTED, "a dimension exceeds 2^30");
+  if (in_dim % 8 != 0) return fail(TB_ERR_UNSUPPORTED, "in_dim %lld is not a multiple of 8", (long long)in_dim);
+  return TB_OK;
+}
+
+}  // namespace
+
+int device_cu_count(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return int(e);
+  if (dev >= 0 && dev < kMaxDevices && g_cus[dev] > 0) {
+    *cus = g_cus[dev];
+    return 0;
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return int(e);
+  if (n < 2) n = 2;
+  if (dev >= 0 && dev < kMaxDevices) g_cus[dev] = n;
+  *cus = n;
+  return 0;
+}
+
+}  // namespace tb
+
+using namespace tb;
+
+extern "C" {
+
+tb_status tb_band_index(int32_t num_layers, int32_t num_bands, int32_t layer, int32_t* band_out) {
+  if (band_out == nullptr) return fail(TB_ERR_INVALID_ARGUMENT, "band_out is NULL");
+  if (num_layers < 1) return fail(TB_ERR_INVALID_ARGUMENT, "num_layers %d < 1", num_layers);
+  if (num_bands < 1 || num_bands > num_layers)
+    return fail(TB_ERR_INVALID_ARGUMENT, "num_bands %d outside [1, %d]", num_bands, num_layers);
+  if (layer < 0 || layer >= num_layers)
+    return fail(TB_ERR_INVALID_ARGUMENT, "layer %d outside [0, %d)", layer, num_layers);
+  // q layers per band, the first m bands one more; they end at layer m(q+1).
+  const int32_t q = num_layers / num_bands, m = num_layers % num_bands;
+  const int32_t big = m * (q + 1);
+  *band_out = layer < big ? layer / (q + 1) : m + (layer - big) / q;
+  return ok();
+}
+
+tb_status tb_linear_forward_workspace_size(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, tb_dtype dtype,
+                                           size_t* bytes_out) {
+  if (bytes_out == nullptr) return fail(TB_ERR_INVALID_ARGUMENT, "bytes_out is NULL");
+  if (!valid_dtype(dtype)) return fail(TB_ERR_INVALID_ARGUMENT, "unknown dtype %d", int(dtype));
+  tb_status st = check_dims(m, out_dim, in_dim, rank);
+  if (st != TB_OK) return st;
+  int cus = 0;
+  if (int e = device_cu_count(&cus)) return hip_fail(hipError_t(e), "querying the compute-unit count");
+  size_t bytes;
+  if (dtype == TB_BF16 && m > kDecodeMaxTokens) {
+    bytes = plan_gemm(m, out_dim, in_dim, rank).bytes;
+  } else {
+    const int64_t mm = m < kDecodeMaxTokens ? m : kDecodeMaxTokens;
+    bytes = plan_decode(mm, out_dim, in_dim, rank, cus).bytes;
+  }
+  *bytes_out = bytes;
+  return ok();
+}
+
+tb_status tb_linear_forward(const void* x, const void* s, const void* w0, const void* u, const void* v, void* y,
+                            int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, tb_dtype dtype,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype)) return fail(TB_ERR_INVALID_ARGUMENT, "unknown dtype %d", int(dtype));
+  tb_status st = check_dims(m, out_dim, in_dim, rank);
+  if (st != TB_OK) return st;
+  if (!x || !s || !w0 || !y || !workspace) return fail(TB_ERR_INVALID_ARGUMENT, "x, s, w0, y and workspace must be non-NULL");
+  if (rank > 0 && (!u || !v)) return fail(TB_ERR_INVALID_ARGUMENT, "u and v must be non-NULL when rank > 0");
+  if (!aligned16(x) || !aligned16(w0) || (rank > 0 && (!aligned16(u) || !aligned16(v))))
+    return fail(TB_ERR_UNSUPPORTED, "x, w0, u and v must be 16-byte aligned");
+  if (!aligned_to(s, esize(dtype)) || !aligned_to(y, esize(dtype)))
+    return fail(TB_ERR_UNSUPPORTED, "s and y must be aligned to their element size");
+  if (!aligned_to(workspace, 256)) return fail(TB_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  int cus = 0;
+  if (int e = device_cu_count(&cus)) return hip_fail(hipError_t(e), "querying the compute-unit count");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+
+  if (dtype == TB_BF16 && m > kDecodeMaxTokens) {
+    const GemmPlan p = plan_gemm(m, out_dim, in_dim, rank);
+    if (workspace_bytes < p.bytes)
+      return fail(TB_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is below the %zu needed", workspace_bytes, p.bytes);
+    hipError_t e = launch_forward_gemm(p, x, s, w0, u, v, y, m, out_dim, in_dim, rank, workspace, hs);
+    if (e != hipSuccess) return hip_fail(e, "launching the prefill projection");
+    return ok();
+  }
+  // Few tokens (or fp32): the fused single-launch kernel, 64 tokens at a time.
+  const int64_t mm = m < kDecodeMaxTokens ? m : kDecodeMaxTokens;
+  const DecodePlan p = plan_decode(mm, out_dim, in_dim, rank, cus);
+  if (workspace_bytes < p.bytes)
+    return fail(TB_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is below the %zu needed", workspace_bytes, p.bytes);
+  const size_t es = esize(dtype);
+  for (int64_t t0 = 0; t0 < m; t0 += kDecodeMaxTokens) {
+    const int64_t mt = (m - t0) < kDecodeMaxTokens ? (m - t0) : kDecodeMaxTokens;
+    const DecodePlan pt = mt == mm ? p : plan_decode(mt, out_dim, in_dim, rank, cus);
+    const char* xt = static_cast<const char*>(x) + size_t(t0) * size_t(in_dim) * es;
+    char* yt = static_cast<char*>(y) + size_t(t0) * size_t(out_dim) * es;
+    hipError_t e = launch_forward_decode(pt, dtype, xt, s, w0, u, v, yt, mt, out_dim, in_dim, rank, workspace, hs);
+    if (e != hipSuccess) return hip_fail(e, "launching the decode projection");
+  }
+  return ok();
+}
+
+tb_status tb_reconstruct_weight(const void* s, const void* w0, const void* u, const void* v, void* w_out,
+                                int64_t out_dim, int64_t in_dim, int64_t rank, tb_dtype in_dtype, tb_dtype out_dtype,
+                                void* stream) {
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return fail(TB_ERR_INVALID_ARGUMENT, "unknown dtype");
+  tb_status st = check_dims(1, out_dim, in_dim, rank);
+  if (st != TB_OK) return st;
+  if (!s || !w0 || !w_out) return fail(TB_ERR_INVALID_ARGUMENT, "s, w0 and w_out must be non-NULL");
+  if (rank > 0 && (!u || !v)) return fail(TB_ERR_INVALID_ARGUMENT, "u and v must be non-NULL when rank > 0");
+  if (!aligned16(w0) || !aligned16(w_out) || (rank > 0 && (!aligned16(u) || !aligned16(v))))
+    return fail(TB_ERR_UNSUPPORTED, "w0, w_out, u and v must be 16-byte aligned");
+  if (!aligned_to(s, esize(in_dtype))) return fail(TB_ERR_UNSUPPORTED, "s must be aligned to its element size");
+  hipError_t e = launch_reconstruct(in_dtype, out_dtype, s, w0, u, v, w_out, out_dim, in_dim, rank,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launching reconstruct");
+  return ok();
+}
+
+tb_status tb_rel_frobenius_error(const void* original, const void* reconstructed, int64_t rows, int64_t cols,
+                                 tb_dtype dtype, double* result_device, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (!valid_dtype(dtype)) return fail(TB_ERR_INVALID_ARGUMENT, "unknown dtype %d", int(dtype));
+  if (!original || !reconstructed || !result_device || !workspace)
+    return fail(TB_ERR_INVALID_ARGUMENT, "original, reconstructed, result and workspace must be non-NULL");
+  if (rows < 1 || cols < 1) return fail(TB_ERR_INVALID_ARGUMENT, "rows and cols must be >= 1");
+  if (rows > (int64_t(1) << 40) / cols) return fail(TB_ERR_UNSUPPORTED, "matrix too large");
+  if (cols % 8 != 0) return fail(TB_ERR_UNSUPPORTED, "cols %lld is not a multiple of 8", (long long)cols);
+  if (!aligned16(original) || !aligned16(reconstructed))
+    return fail(TB_ERR_UNSUPPORTED, "original and reconstructed must be 16-byte aligned");
+  if (!aligned_to(result_device, 8) || !aligned_to(workspace, 16))
+    return fail(TB_ERR_UNSUPPORTED, "result must be 8-byte and workspace 16-byte aligned");
+  if (workspace_bytes < TB_FROBENIUS_WORKSPACE_BYTES)
+    return fail(TB_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is below %d", workspace_bytes, TB_FROBENIUS_WORKSPACE_BYTES);
+  int cus = 0;
+  if (int e = device_cu_count(&cus)) return hip_fail(hipError_t(e), "querying the compute-unit count");
+  hipError_t e = launch_frobenius(dtype, original, reconstructed, rows * cols, result_device, workspace, cus,
+                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launching the Frobenius reduction");
+  return ok();
+}
+
+const char* tb_status_string(tb_status status) {
+  switch (status) {
+    case TB_OK: return "ok";
+    case TB_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case TB_ERR_UNSUPPORTED: return "unsupported layout or size";
+    case TB_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* tb_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// relative_frobenius_error(original, reconstructed) =
+//     ||original - reconstructed||_F / ||original||_F
+// ("Quality", section "Reconstruction error").
+//
+// Two passes, no atomics, so the result is the same on every run:
+//   pass 1: each workgroup walks a grid-stride set of 8-element chunks and
+//           sums (a - b)^2 and a^2 in fp64 (differences taken in fp64), then
+//           reduces its threads in a fixed tree order into one partial pair;
+//   pass 2: one workgroup sums the partial pairs in a fixed order and writes
+//           the ratio.  0 when the difference is zero, +inf when only the
+//           original is zero.
+// HBM-bound: every element of both matrices is read once.
+#include "tb_device.h"
+#include "tb_host.h"
+
+namespace tb {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxPartials = TB_FROBENIUS_WORKSPACE_BYTES / 16;
+
+template <typename E>
+__device__ __forceinline__ void load8_f64(const E* p, double* out) {
+  if constexpr (sizeof(E) == 2) {
+    const uint4 q = *reinterpret_cast<const uint4*>(p);
+    const uint32_t u4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = double(bf16_to_f32(uint16_t(u4[e / 2] >> (16 * (e % 2)))));
+  } else {
+    const float4 lo = reinterpret_cast<const float4*>(p)[0];
+    const float4 hi = reinterpret_cast<const float4*>(p)[1];
+    out[0] = lo.x; out[1] = lo.y; out[2] = lo.z; out[3] = lo.w;
+    out[4] = hi.x; out[5] = hi.y; out[6] = hi.z; out[7] = hi.w;
+  }
+}
+
+__device__ __forceinline__ void block_reduce2(double& a, double& b, double* sa, double* sb) {
+  const int tid = threadIdx.x;
+  sa[tid] = a;
+  sb[tid] = b;
+  __syncthreads();
+  for (int h = kThreads / 2; h > 0; h >>= 1) {
+    if (tid < h) {
+      sa[tid] += sa[tid + h];
+      sb[tid] += sb[tid + h];
+    }
+    __syncthreads();
+  }
+  a = sa[0];
+  b = sb[0];
+}
+
+template <typename E>
+__global__ __launch_bounds__(kThreads) void frob_pass1(const E* __restrict__ a, const E* __restrict__ b, int64_t n8,
+                                                       double2* __restrict__ partial) {
+  __shared__ double sa[kThreads], sb[kThreads];
+  double num = 0.0, den = 0.0;
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  for (int64_t c = int64_t(blockIdx.x) * kThreads + threadIdx.x; c < n8; c += stride) {
+    double va[8], vb[8];
+    load8_f64<E>(a + c * 8, va);
+    load8_f64<E>(b + c * 8, vb);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double d = va[e] - vb[e];
+      num += d * d;
+      den += va[e] * va[e];
+    }
+  }
+  block_reduce2(num, den, sa, sb);
+  if (threadIdx.x == 0) partial[blockIdx.x] = make_double2(num, den);
+}
+
+__global__ __launch_bounds__(kThreads) void frob_pass2(const double2* __restrict__ partial, int np, double* result) {
+  __shared__ double sa[kThreads], sb[kThreads];
+  double num = 0.0, den = 0.0;
+  for (int i = threadIdx.x; i < np; i += kThreads) {
+    num += partial[i].x;
+    den += partial[i].y;
+  }
+  block_reduce2(num, den, sa, sb);
+  if (threadIdx.x == 0) {
+    double r;
+    if (num == 0.0) r = 0.0;
+    else if (den == 0.0) r = __builtin_inf();
+    else r = sqrt(num) / sqrt(den);
+    *result = r;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_frobenius(tb_dtype dtype, const void* a, const void* b, int64_t n, double* result, void* workspace,
+                            int cus, hipStream_t stream) {
+  const int64_t n8 = n / 8;
+  int64_t blocks = (n8 + kThreads - 1) / kThreads;
+  const int64_t cap = int64_t(cus) * 8 < kMaxPartials ? int64_t(cus) * 8 : kMaxPartials;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  double2* partial = static_cast<double2*>(workspace);
+  if (dtype == TB_BF16)
+    hipLaunchKernelGGL(frob_pass1<bf16_t>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
+                       static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b), n8, partial);
+  else
+    hipLaunchKernelGGL(frob_pass1<float>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
+                       static_cast<const float*>(a), static_cast<const float*>(b), n8, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(frob_pass2, dim3(1), dim3(kThreads), 0, stream, partial, int(blocks), result);
+  return hipGetLastError();
+}
+
+}  // namespace tb

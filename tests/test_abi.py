@@ -1,0 +1,141 @@
+"""Host-side tests of libtb's C ABI (no GPU needed).
+
+They load the library, check that it exports every symbol the header
+declares, compare tb_band_index with the oracle's band map bit for bit, and
+check that invalid arguments are refused on the host before anything could
+be enqueued (only argument combinations that fail validation are passed, so no
+device is touched).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from conftest import ROOT, BAND_FIXTURES, read_band_fixture
+
+binding = pytest.importorskip("rank_factored_linear_amd.binding")
+lib = binding.lib
+
+HEADER = os.path.join(ROOT, "include", "tb.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tb_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("tb_band_index", "tb_linear_forward", "tb_reconstruct_weight", "tb_rel_frobenius_error"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert names
+    for name in names:
+        assert hasattr(lib, name), name
+        assert name in binding.EXPORTED, name
+
+
+def test_band_index_matches_oracle_bit_exact():
+    out = ctypes.c_int32()
+    for L in range(1, 129):
+        for G in range(1, L + 1):
+            want = oracle.band_map(L, G)
+            for l in range(L):
+                assert lib.tb_band_index(L, G, l, ctypes.byref(out)) == 0
+                assert out.value == want[l], (L, G, l)
+
+
+@pytest.mark.parametrize("name", BAND_FIXTURES)
+def test_band_index_golden(name):
+    L, G, want = read_band_fixture(name)
+    assert [binding.band_index(L, G, l) for l in range(L)] == want
+
+
+def test_band_index_large_counts():
+    # Far beyond the model sizes; checks the closed form's integer arithmetic.
+    for L, G in ((1_000_003, 7), (2**31 - 1, 3), (2**31 - 1, 2**31 - 1), (65536, 1)):
+        sizes = [L // G + (1 if b < L % G else 0) for b in range(G)] if G < 10 else None
+        for l in (0, 1, L // 2, L - 2, L - 1):
+            b = binding.band_index(L, G, l)
+            if sizes is not None:
+                start = sum(sizes[:b])
+                assert start <= l < start + sizes[b]
+            else:
+                assert b == l  # G == L
+
+
+@pytest.mark.parametrize("args", [(0, 1, 0), (5, 0, 0), (5, 6, 0), (5, 2, 5), (5, 2, -1), (-3, 1, 0)])
+def test_band_index_invalid_leaves_output(args):
+    out = ctypes.c_int32(-77)
+    st = lib.tb_band_index(*args, ctypes.byref(out))
+    assert st == binding.TB_ERR_INVALID_ARGUMENT
+    assert out.value == -77
+    assert lib.tb_last_error().decode()
+
+
+def test_band_index_null_output():
+    assert lib.tb_band_index(4, 2, 0, None) == binding.TB_ERR_INVALID_ARGUMENT
+
+
+def test_status_strings():
+    for code in range(4):
+        assert lib.tb_status_string(code).decode()
+    assert lib.tb_status_string(99).decode() == "unknown status"
+
+
+FAKE = 0x100000  # 256-byte aligned non-NULL address; never dereferenced below
+
+
+def _fwd(**kw):
+    a = dict(x=FAKE, s=FAKE, w0=FAKE, u=FAKE, v=FAKE, y=FAKE, m=8, o=64, i=64, r=16, dt=binding.TB_BF16,
+             ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.tb_linear_forward(a["x"], a["s"], a["w0"], a["u"], a["v"], a["y"], a["m"], a["o"], a["i"], a["r"],
+                                 a["dt"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(m=0), 1), (dict(o=0), 1), (dict(i=0), 1), (dict(r=-1), 1), (dict(dt=7), 1),
+    (dict(x=None), 1), (dict(s=None), 1), (dict(w0=None), 1), (dict(y=None), 1), (dict(ws=None), 1),
+    (dict(u=None), 1), (dict(v=None), 1),
+    (dict(i=60), 2), (dict(x=FAKE + 8), 2), (dict(w0=FAKE + 4), 2), (dict(u=FAKE + 2), 2),
+    (dict(s=FAKE + 1), 2), (dict(y=FAKE + 1), 2), (dict(ws=FAKE + 16), 2), (dict(m=1 << 31), 2),
+])
+def test_forward_rejects_before_launch(kw, status):
+    assert _fwd(**kw) == status
+    assert lib.tb_last_error().decode()
+
+
+def test_reconstruct_rejects_before_launch():
+    f = lib.tb_reconstruct_weight
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 64, 64, 8, 1, 0, None) == 1
+    assert f(FAKE, FAKE, None, FAKE, FAKE, 64, 64, 8, 1, 0, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 8, 1, 0, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 12, 8, 1, 0, None) == 2
+    assert f(FAKE, FAKE + 2, FAKE, FAKE, FAKE, 64, 64, 8, 1, 0, None) == 2
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 8, 1, 5, None) == 1
+
+
+def test_frobenius_rejects_before_launch():
+    f = lib.tb_rel_frobenius_error
+    ws = binding.FROBENIUS_WORKSPACE_BYTES
+    assert f(None, FAKE, 4, 8, 0, FAKE, FAKE, ws, None) == 1
+    assert f(FAKE, FAKE, 0, 8, 0, FAKE, FAKE, ws, None) == 1
+    assert f(FAKE, FAKE, 4, 6, 0, FAKE, FAKE, ws, None) == 2
+    assert f(FAKE, FAKE, 4, 8, 0, FAKE, FAKE, ws - 1, None) == 1
+    assert f(FAKE, FAKE, 4, 8, 9, FAKE, FAKE, ws, None) == 1
+    assert f(FAKE, FAKE + 4, 4, 8, 0, FAKE, FAKE, ws, None) == 2
+
+
+def test_workspace_size_rejects_bad_arguments():
+    out = ctypes.c_size_t(0)
+    assert lib.tb_linear_forward_workspace_size(0, 64, 64, 0, 0, ctypes.byref(out)) == 1
+    assert lib.tb_linear_forward_workspace_size(1, 64, 64, 0, 0, None) == 1
+    assert lib.tb_linear_forward_workspace_size(1, 64, 63, 0, 0, ctypes.byref(out)) == 2

@@ -1,0 +1,32 @@
+"""Host-side checks of bench.py's contract (no GPU)."""
+
+import json
+import os
+import subprocess
+import sys
+
+from conftest import ROOT
+
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_multi_gpu_request_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_algorithmic_counts():
+    # 60-layer gate projection, 16 tokens, rank 256 (bf16).
+    O, I, R, M = 21504, 5376, 256, 16
+    assert bench.call_bytes(M, O, I, R) == 2 * (O * I + R * (O + I) + O + M * (I + O))
+    assert bench.call_flops(M, O, I, R) == 2 * M * (O * I + R * (O + I))
+    # Per-layer W0 bytes of the 60-layer stack: 913,833,984.
+    from rank_factored_linear_amd import inputs
+    assert sum(2 * o * i for o, i in inputs.SHAPES_60.values()) == 913_833_984
+    assert sum(2 * o * i for o, i in inputs.SHAPES_26.values()) == 53_673_984
+
+
+def test_traffic_record_requires_current_kernel_source(tmp_path, monkeypatch):
+    assert len(bench.kernel_source_digest()) == 16

@@ -1,0 +1,299 @@
+"""GPU parity: libtb through its C ABI against the float64 oracle.
+
+Every test calls the HIP kernels through ``rank_factored_linear_amd.binding``
+(ctypes over tb.h) and compares with the oracle on the exact stored inputs.
+Tolerances: relative Frobenius error <= 5e-3 (bf16 inputs, fp32 accumulate)
+or <= 1e-5 (fp32); band indices and rank-0 fp32 reconstruction bit-exact.
+Large workloads compare sampled outputs that the oracle computes row by row.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from rank_factored_linear_amd import inputs as gen
+from parity_util import BF16_TOL, F32_TOL, bits_to_device, exact, f32_to_device, sample_rows, tol_for
+
+pytestmark = pytest.mark.gpu
+
+tb = pytest.importorskip("rank_factored_linear_amd.binding")
+DEV = "cuda"
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def test_native_library_is_loaded():
+    with open("/proc/self/maps") as f:
+        maps = f.read()
+    assert os.path.realpath(tb.LIB_PATH) in maps
+    assert torch.cuda.is_available()
+    _say("device:", torch.cuda.get_device_name(0))
+
+
+# ---------------------------------------------------------------------------
+# Tiny fp32 stack: oracle decomposition, GPU forward / reconstruct / error
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("rank", [16, 256])
+def test_tiny_fp32_stack(rank):
+    _say(f"tiny fp32 stack rank={rank}")
+    weights, x = gen.tiny_stack()
+    bun = oracle.decompose(weights, 2, rank)
+    x32 = x.astype(np.float32)
+    for l in range(gen.TINY_LAYERS):
+        band = tb.band_index(gen.TINY_LAYERS, 2, l)
+        assert band == bun["band"][l] == gen.TINY_LAYER_BAND[l]
+        W0 = bun["W0"][band].astype(np.float32)
+        s = bun["s"][l].astype(np.float32)
+        U = bun["U"][l].astype(np.float32)
+        V = bun["V"][l].astype(np.float32)
+        y = tb.linear_forward(f32_to_device(x32), f32_to_device(s), f32_to_device(W0), f32_to_device(U), f32_to_device(V))
+        want = oracle.forward(x32, s, W0, U, V)
+        err = oracle.relative_frobenius_error(want, exact(y))
+        assert err <= F32_TOL, (l, err)
+        rec = tb.reconstruct_weight(f32_to_device(s), f32_to_device(W0), f32_to_device(U), f32_to_device(V))
+        rw = oracle.reconstruct_weight(s, W0, U, V)
+        assert oracle.relative_frobenius_error(rw, exact(rec)) <= F32_TOL
+        orig = f32_to_device(weights[l].astype(np.float32))
+        e_gpu = float(tb.rel_frobenius_error(orig, rec).item())
+        e_ref = oracle.relative_frobenius_error(exact(orig), exact(rec))
+        assert abs(e_gpu - e_ref) <= 1e-9 + 1e-9 * e_ref
+        if rank == 256:
+            assert e_gpu < 1e-5  # a full-rank delta leaves only fp32 rounding
+
+
+# ---------------------------------------------------------------------------
+# Passthrough 26-layer bf16 stack: output equals the plain layer x W^T
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("family", gen.FAMILIES)
+def test_passthrough_stack_bf16(family):
+    for layer in (0, 13, 25):
+        assert tb.band_index(26, 26, layer) == layer
+        b = gen.bundle_bf16_host(2, family, gen.SHAPES_26, layer, layer, 0, passthrough=True)
+        W = bits_to_device(b["W0"])
+        s = bits_to_device(b["s"])
+        Wd = exact(W)
+        for M in (1, 8, 64):
+            _say(f"passthrough {family} layer={layer} M={M}")
+            x = bits_to_device(gen.activations_bf16_host(2, family, gen.SHAPES_26, layer, M))
+            y = tb.linear_forward(x, s, W, None, None)
+            err = oracle.relative_frobenius_error(oracle.forward_dense(exact(x), Wd), exact(y))
+            assert err <= BF16_TOL, (layer, M, err)
+        rec = tb.reconstruct_weight(s, W, None, None, out_dtype=torch.float32)
+        assert np.array_equal(exact(rec), Wd)                    # rebuilt weight is the original
+        assert float(tb.rel_frobenius_error(W.float(), rec).item()) == 0.0
+
+
+# ---------------------------------------------------------------------------
+# Banded 26-layer bf16 stack, rank 128, G in {1, 4}
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("M", [4, 2048])
+@pytest.mark.parametrize("family", gen.FAMILIES)
+def test_banded_stack_bf16(G, M, family):
+    want_bands = oracle.band_map(26, G)
+    for layer in (0, 6, 7, 19, 20, 25):
+        band = tb.band_index(26, G, layer)
+        assert band == want_bands[layer]
+        _say(f"banded G={G} M={M} {family} layer={layer} band={band}")
+        b = gen.bundle_bf16_host(3, family, gen.SHAPES_26, layer, band, 128)
+        t = {k: bits_to_device(v) for k, v in b.items()}
+        x = bits_to_device(gen.activations_bf16_host(3, family, gen.SHAPES_26, layer, M))
+        y = tb.linear_forward(x, t["s"], t["W0"], t["U"], t["V"])
+        tsel = sample_rows(M, 96, seed=layer)
+        want = oracle.forward(exact(x)[tsel], exact(t["s"]), exact(t["W0"]), exact(t["U"]), exact(t["V"]))
+        err = oracle.relative_frobenius_error(want, exact(y)[tsel])
+        assert err <= BF16_TOL, (layer, err)
+
+
+# ---------------------------------------------------------------------------
+# Large 60-layer bf16 stack, rank 256, drawn on the device; sampled outputs
+# ---------------------------------------------------------------------------
+
+
+def _large_case(G, layer, family, M):
+    band = tb.band_index(60, G, layer)
+    assert band == oracle.band_index(60, G, layer)
+    W0 = gen.device_w0(torch, 4, family, gen.SHAPES_60, band)
+    bun = gen.device_bundle(torch, 4, family, gen.SHAPES_60, layer, band, 256, with_w0=False)
+    x = gen.device_activations(torch, 4, family, gen.SHAPES_60, layer, M)
+    y = tb.linear_forward(x, bun["s"], W0, bun["U"], bun["V"])
+    O = W0.shape[0]
+    osel = sample_rows(O, 384, seed=layer + 7)
+    tsel = sample_rows(M, 48, seed=layer + 11)
+    oi = torch.from_numpy(osel).to(DEV)
+    ti = torch.from_numpy(tsel).to(DEV)
+    want = oracle.forward(exact(x.index_select(0, ti)), exact(bun["s"].index_select(0, oi)),
+                          exact(W0.index_select(0, oi)), exact(bun["U"].index_select(0, oi)), exact(bun["V"]))
+    got = exact(y.index_select(0, ti).index_select(1, oi))
+    return oracle.relative_frobenius_error(want, got)
+
+
+@pytest.mark.parametrize("G,layer", [(6, 0), (6, 59), (60, 29)])
+@pytest.mark.parametrize("M", [1, 16, 4096])
+@pytest.mark.parametrize("family", gen.FAMILIES)
+def test_large_stack_bf16(G, layer, M, family):
+    _say(f"large G={G} layer={layer} M={M} {family}")
+    err = _large_case(G, layer, family, M)
+    assert err <= BF16_TOL, err
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# Reconstruction path bf16 -> fp32 and relative Frobenius error, 60 layers G=6
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("rank", [256, 0])
+@pytest.mark.parametrize("family", gen.FAMILIES)
+def test_reconstruct_large(rank, family):
+    for layer in (0, 59):
+        band = tb.band_index(60, 6, layer)
+        _say(f"reconstruct rank={rank} {family} layer={layer} band={band}")
+        W0 = gen.device_w0(torch, 5, family, gen.SHAPES_60, band)
+        bun = gen.device_bundle(torch, 5, family, gen.SHAPES_60, layer, band, rank, with_w0=False)
+        U, V = (bun["U"], bun["V"]) if rank else (None, None)
+        rec = tb.reconstruct_weight(bun["s"], W0, U, V, out_dtype=torch.float32)
+        orig = gen.device_original(torch, W0, 5, family, layer)
+        e_gpu = float(tb.rel_frobenius_error(orig, rec).item())
+        # Oracle on sampled rows for the reconstruction ...
+        osel = sample_rows(W0.shape[0], 256, seed=layer + 3)
+        oi = torch.from_numpy(osel).to(DEV)
+        Us = exact(bun["U"].index_select(0, oi)) if rank else np.zeros((len(osel), 0))
+        Vs = exact(bun["V"]) if rank else np.zeros((W0.shape[1], 0))
+        want = oracle.reconstruct_weight(exact(bun["s"].index_select(0, oi)), exact(W0.index_select(0, oi)), Us, Vs)
+        got = exact(rec.index_select(0, oi))
+        if rank == 0:
+            assert np.array_equal(want, got)        # s * W0 of bf16 values is exact in fp32
+        else:
+            assert oracle.relative_frobenius_error(want, got) <= F32_TOL
+        # ... and on the whole matrices for the error measure.
+        e_ref = oracle.relative_frobenius_error(exact(orig), exact(rec))
+        assert abs(e_gpu - e_ref) <= 1e-9 * max(e_ref, 1.0), (e_gpu, e_ref)
+        del W0, bun, rec, orig
+        torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# Edge cases: ragged shapes, both dtypes, both kernels
+# ---------------------------------------------------------------------------
+
+EDGE_SHAPES = [  # (M, out, in, rank)
+    (1, 1, 8, 0), (1, 5, 16, 1), (3, 17, 40, 4), (16, 64, 64, 32), (17, 100, 264, 12), (33, 130, 520, 40),
+    (64, 64, 64, 8), (5, 48, 8192, 256), (2, 300, 1000, 300), (65, 130, 264, 12), (130, 257, 136, 20),
+    (200, 300, 1000, 300), (257, 129, 72, 0), (96, 2048, 512, 64),
+]
+
+
+def _rand_case(M, O, I, R, dtype, seed):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    mk = lambda *shape, sd=1.0: (torch.randn(*shape, generator=g) * sd).to(dtype).to(DEV)
+    x = mk(M, I)
+    W0 = mk(O, I, sd=0.02)
+    s = (1.0 + 0.1 * torch.rand(O, generator=g)).to(dtype).to(DEV)
+    U = mk(O, R, sd=0.01) if R else None
+    V = mk(I, R, sd=0.01) if R else None
+    return x, s, W0, U, V
+
+
+def _oracle_forward(x, s, W0, U, V):
+    R = 0 if U is None else U.shape[1]
+    Ud = exact(U) if R else np.zeros((W0.shape[0], 0))
+    Vd = exact(V) if R else np.zeros((W0.shape[1], 0))
+    return oracle.forward(exact(x), exact(s), exact(W0), Ud, Vd)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("shape", EDGE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_forward_edge_shapes(shape, dtype):
+    M, O, I, R = shape
+    _say(f"edge forward {shape} {dtype}")
+    x, s, W0, U, V = _rand_case(M, O, I, R, dtype, seed=sum(shape))
+    # Guard bands around the output catch out-of-bounds stores.
+    guard = 4096
+    buf = torch.full((guard + M * O + guard,), 7.0, dtype=dtype, device=DEV)
+    y = buf[guard:guard + M * O].view(M, O)
+    tb.linear_forward(x, s, W0, U, V, out=y)
+    err = oracle.relative_frobenius_error(_oracle_forward(x, s, W0, U, V), exact(y))
+    assert err <= tol_for(dtype), err
+    assert bool((buf[:guard] == 7.0).all()) and bool((buf[guard + M * O:] == 7.0).all())
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(17, 40, 4), (130, 264, 12), (64, 512, 256), (33, 72, 0), (1, 8, 3)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_reconstruct_edge_shapes(shape, dtype):
+    O, I, R = shape
+    _, s, W0, U, V = _rand_case(1, O, I, R, dtype, seed=O + I + R)
+    Ud = exact(U) if R else np.zeros((O, 0))
+    Vd = exact(V) if R else np.zeros((I, 0))
+    want = oracle.reconstruct_weight(exact(s), exact(W0), Ud, Vd)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        rec = tb.reconstruct_weight(s, W0, U, V, out_dtype=out_dtype)
+        err = oracle.relative_frobenius_error(want, exact(rec))
+        assert err <= (F32_TOL if out_dtype == torch.float32 else BF16_TOL), (out_dtype, err)
+        if R == 0 and out_dtype == torch.float32:
+            assert np.array_equal(want, exact(rec))
+
+
+def test_frobenius_closed_forms():
+    g = torch.Generator(device="cpu").manual_seed(3)
+    for dtype in (torch.float32, torch.bfloat16):
+        A = torch.randn(37, 64, generator=g).to(dtype).to(DEV)
+        Z = torch.zeros_like(A)
+        assert float(tb.rel_frobenius_error(A, A).item()) == 0.0
+        assert float(tb.rel_frobenius_error(A, Z).item()) == pytest.approx(1.0, abs=1e-15)
+        assert float(tb.rel_frobenius_error(Z, A).item()) == float("inf")
+        assert float(tb.rel_frobenius_error(Z, Z).item()) == 0.0
+        B = (A.double() * 2).to(dtype)
+        assert float(tb.rel_frobenius_error(A, B).item()) == pytest.approx(1.0, rel=1e-12)
+        assert float(tb.rel_frobenius_error(B, A).item()) == pytest.approx(0.5, rel=1e-12)
+        want = oracle.relative_frobenius_error(exact(A), exact(B * 0.75))
+        assert float(tb.rel_frobenius_error(A, (B * 0.75).to(dtype)).item()) == pytest.approx(want, rel=1e-12)
+    big = torch.randn(1000, 4104, generator=g).to(DEV)
+    other = big + 1e-3 * torch.randn(1000, 4104, generator=g).to(DEV)
+    want = oracle.relative_frobenius_error(exact(big), exact(other))
+    assert float(tb.rel_frobenius_error(big, other).item()) == pytest.approx(want, rel=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Determinism and workspace state
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("shape", [(16, 6912, 1152, 128), (4, 256, 1152, 128), (2048, 1152, 6912, 128), (1, 2048, 5376, 256)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_bitwise_deterministic_and_workspace_clean(shape):
+    M, O, I, R = shape
+    x, s, W0, U, V = _rand_case(M, O, I, R, torch.bfloat16, seed=99)
+    ys = [tb.linear_forward(x, s, W0, U, V).clone() for _ in range(3)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(ys[0].view(torch.int16), y.view(torch.int16))
+    ws = tb.workspace_for(0)
+    assert int(ws[:tb.WORKSPACE_CONTROL_BYTES].count_nonzero().item()) == 0
+    assert tb.workspace_error_word() == 0
+
+
+def test_stream_ordering_many_calls():
+    # Back-to-back calls of different shapes on one stream reuse the
+    # workspace; each must see clean control words.
+    cases = [(1, 8192, 5376, 256), (16, 2048, 5376, 256), (4, 256, 1152, 128), (64, 1152, 6912, 0), (8, 21504, 5376, 256)]
+    data = [_rand_case(*c, torch.bfloat16, seed=i) for i, c in enumerate(cases)]
+    outs = [tb.linear_forward(*d) for d in data for _ in range(2)]
+    torch.cuda.synchronize()
+    for i, d in enumerate(data):
+        ref = _oracle_forward(*d)
+        for y in outs[2 * i: 2 * i + 2]:
+            assert oracle.relative_frobenius_error(ref, exact(y)) <= BF16_TOL
+    assert tb.workspace_error_word() == 0
