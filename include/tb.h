@@ -50,7 +50,7 @@ typedef enum tb_dtype {
   TB_BF16 = 1  /* bfloat16, round-to-nearest-even on every store */
 } tb_dtype;
 
-/* Bytes of workspace whose first TB_WORKSPACE_CONTROL_BYTES must be zero. */
+/* Leading bytes of a forward workspace that hold control words. */
 #define TB_WORKSPACE_CONTROL_BYTES 65536
 
 /* Fixed workspace size of tb_rel_frobenius_error. */
@@ -101,9 +101,12 @@ tb_status tb_linear_forward_workspace_size(int64_t m, int64_t out_dim, int64_t i
  *   rounded once at the end.  Results are deterministic run to run.
  *   workspace: device buffer of at least tb_linear_forward_workspace_size()
  *   bytes, 256-byte aligned.  Its first TB_WORKSPACE_CONTROL_BYTES bytes are
- *   control words that must be zero before the first call that uses the
- *   buffer; every call that completes leaves them zero again.  Calls that may
- *   run at the same time (different streams) must not share a workspace.
+ *   control words: they must be zero before the first call that uses the
+ *   buffer and must not be changed by the caller afterwards (each completed
+ *   call leaves them ready for the next; word 2 is a sticky error flag that
+ *   becomes nonzero only if a bounded internal wait timed out, in which case
+ *   that call's y is NaN).  Calls that may run at the same time (different
+ *   streams) must not share a workspace.
  *   Errors: TB_ERR_INVALID_ARGUMENT, TB_ERR_UNSUPPORTED, TB_ERR_HIP.
  */
 tb_status tb_linear_forward(const void *x, const void *s, const void *w0, const void *u, const void *v,

@@ -89,7 +89,8 @@ def _need_cuda(*ts):
 
 # ---------------------------------------------------------------------------
 # Workspace: one zero-initialised buffer per (device, stream), grown on
-# demand.  The library returns its control words to zero after every call.
+# demand.  Its control words are zero when created and the library keeps
+# them consistent from call to call.
 # ---------------------------------------------------------------------------
 _ws_lock = threading.Lock()
 _ws: dict = {}
@@ -114,7 +115,7 @@ def workspace_error_word() -> int:
     buf = _ws.get(key)
     if buf is None:
         return 0
-    return int(buf[:32].view(torch.int32)[5].item())
+    return int(buf[:32].view(torch.int32)[2].item())
 
 
 # ---------------------------------------------------------------------------

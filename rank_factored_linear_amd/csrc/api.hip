@@ -2,6 +2,8 @@
 // before anything is enqueued, so a failing call leaves all outputs untouched.
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
+
+#include <atomic>
 #include <stdio.h>
 
 #include "tb_host.h"
@@ -51,6 +53,15 @@ tb_status check_dims(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank) {
 }
 
 }  // namespace
+
+unsigned next_epoch() {
+  static std::atomic<unsigned> counter{0};
+  unsigned e;
+  do {
+    e = counter.fetch_add(1u, std::memory_order_relaxed) + 1u;
+  } while (e == 0u);
+  return e;
+}
 
 int device_cu_count(int* cus) {
   int dev = 0;
@@ -144,7 +155,8 @@ tb_status tb_linear_forward(const void* x, const void* s, const void* w0, const 
     const DecodePlan pt = mt == mm ? p : plan_decode(mt, out_dim, in_dim, rank, cus);
     const char* xt = static_cast<const char*>(x) + size_t(t0) * size_t(in_dim) * es;
     char* yt = static_cast<char*>(y) + size_t(t0) * size_t(out_dim) * es;
-    hipError_t e = launch_forward_decode(pt, dtype, xt, s, w0, u, v, yt, mt, out_dim, in_dim, rank, workspace, hs);
+    hipError_t e =
+        launch_forward_decode(pt, dtype, xt, s, w0, u, v, yt, mt, out_dim, in_dim, rank, workspace, next_epoch(), hs);
     if (e != hipSuccess) return hip_fail(e, "launching the decode projection");
   }
   return ok();

@@ -4,30 +4,29 @@
 //   transpose of weight = diag(s) W0 + U V^T applied to x)
 //
 // At these token counts the projection is bound by HBM bandwidth: every byte
-// of W0 is read once, and U, V, s once.  Workgroups take a role from a ticket
-// counter in the workspace, in the order they start running:
+// of W0 is read once, and U, V, s once.  The grid holds two kinds of
+// workgroups, told apart by their index:
 //
-//   producers (tickets 0..NP-1) compute T = x . V.  Each first sums its
-//     slice of in_dim into a private partial; after all producers arrive
-//     (they are all resident, see below) each sums one slice of the M x r
-//     outputs over the partials in a fixed order.  The last to finish raises
-//     the T-ready flag.
-//   consumers (the other tickets) each own 64 output rows and one slice of
-//     in_dim.  Four waves stream the W0 rows through v_mfma 16x16x32 (x is the
-//     16-token B operand, zero-padded), reduce in LDS in a fixed order, and,
-//     when in_dim is split over KS workgroups, the last of the KS to arrive
-//     sums the KS partials in slice order.  That workgroup scales each row by
-//     s, waits for T, adds T . U^T with the matrix cores and stores y.
+//   producers (indices 0..NP-1) compute T = x . V on the matrix cores, each
+//     over four k32 steps of in_dim, into private partials.  They meet at a
+//     barrier (they hold the lowest indices, so they are dispatched first and
+//     are all resident), then each sums one slice of T over all partials in a
+//     fixed order and stores it; the last to finish raises a ready flag that
+//     carries this call's epoch.
+//   consumers (the rest) each own a contiguous, balanced range of at most
+//     16*RT output rows over the whole of in_dim.  Eight waves take the k32
+//     steps round-robin, streaming W0 rows through v_mfma 16x16x32 with x as
+//     the 16-token B operand (zero padded), and reduce in LDS in a fixed
+//     order.  The epilogue scales each row by s, waits for the flag, adds
+//     T . U^T on the matrix cores and stores y rounded once.
 //
-// Deadlock freedom: a workgroup takes its ticket after it starts running, so
-// any consumer that waits for T runs after all NP producer tickets have been
-// taken by running workgroups, and producers wait only for each other
-// (NP <= compute units / 2, so all of them are resident together).  Every
-// wait is bounded (tb::wait_at_least); a timeout sets an error word and
-// poisons the output with NaN instead of hanging.
-//
-// The last workgroup to finish returns every control word to zero, so the
-// same workspace serves the next call on the stream.
+// All data that crosses workgroups (partials, T, counters, flag) is written
+// and read with device-scope (sc1) accesses, which are coherent across XCDs
+// without writing back or invalidating the L2; a writer waits for its stores
+// to complete (s_waitcnt) before it counts itself in.  No workgroup ever
+// fences, takes a ticket or waits on a consumer, and the flag needs no reset
+// because each call brings a new epoch.  Every wait is bounded: a timeout
+// sets an error word and poisons the output with NaN instead of hanging.
 #include "tb_device.h"
 #include "tb_host.h"
 
@@ -35,11 +34,21 @@ namespace tb {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRows = 64;          // output rows per consumer workgroup
-constexpr int kStageRows = 256;    // rows of x staged in LDS per producer pass
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kVCols = 256;          // columns of V per producer pass
+constexpr int kVPitch = 40;          // LDS pitch (elements) of the transposed V tile
+constexpr int kStageChunks = 32 * (kVCols / 8) / kThreads;  // 16-byte V chunks per thread per step
+constexpr int kMaxProducers = 256;   // at most one per compute unit: all resident together
+constexpr int kStepsPerProducer = 4;  // k32 steps of V per producer (one batch of loads)
 
-enum Ctrl { kTicket = 0, kDone = 1, kArrive1 = 2, kArrive2 = 3, kTReady = 4, kErr = 5 };
+// Control words: [kFlag] T-ready epoch, [kErr] sticky timeout flag,
+// [kArrive] / [kDepart] producer barrier, [kPublished] T slices stored.
+enum Ctrl { kFlag = 1, kErr = 2, kArrive = 3, kDepart = 4, kPublished = 5 };
+
+// Loads kept in flight per wave scale down with the token tiles so that the
+// kernel fits 128 VGPRs (two 512-thread workgroups per compute unit).
+constexpr int per_tile_budget(int base, int nt) { return base / nt > 0 ? base / nt : 1; }
 
 struct DecodeArgs {
   const void* x;
@@ -49,124 +58,270 @@ struct DecodeArgs {
   const void* v;
   void* y;
   int M, O, I, R;
-  int NG, KS, S, NP;
-  unsigned total;
+  int S, NP, NB;
+  unsigned epoch;
   unsigned* ctrl;
-  unsigned* gcount;
   float* tpart;
   float* tfull;
-  float4* ppart;
 };
 
+// Device-scope (sc1) 32-bit accesses: coherent across XCDs without touching
+// the rest of the L2.
+__device__ __forceinline__ uint32_t load_coherent(const void* p) {
+  return __hip_atomic_load(static_cast<const uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(void* p, uint32_t v) {
+  __hip_atomic_store(static_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned add_coherent(unsigned* p, unsigned v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// B fragment of T (published zero padded as [16*NT][Rp]) read coherently.
+template <typename E> __device__ __forceinline__ Frag8<E> load_t_frag(const void* p);
+template <> __device__ __forceinline__ Frag8<bf16_t> load_t_frag<bf16_t>(const void* p) {
+  const uint32_t* q = static_cast<const uint32_t*>(p);
+  Frag8<bf16_t> f;
+  f.v = make_uint4(load_coherent(q), load_coherent(q + 1), load_coherent(q + 2), load_coherent(q + 3));
+  return f;
+}
+template <> __device__ __forceinline__ Frag8<float> load_t_frag<float>(const void* p) {
+  const uint32_t* q = static_cast<const uint32_t*>(p);
+  Frag8<float> f;
+  f.lo = make_float4(__uint_as_float(load_coherent(q)), __uint_as_float(load_coherent(q + 1)),
+                     __uint_as_float(load_coherent(q + 2)), __uint_as_float(load_coherent(q + 3)));
+  f.hi = make_float4(__uint_as_float(load_coherent(q + 4)), __uint_as_float(load_coherent(q + 5)),
+                     __uint_as_float(load_coherent(q + 6)), __uint_as_float(load_coherent(q + 7)));
+  return f;
+}
+
+// Bounded waits (about 0.1 s at most; relaxed polling, no cache invalidation).
+__device__ __forceinline__ bool wait_for_epoch(const unsigned* flag, unsigned epoch) {
+  for (int it = 0; it < (1 << 20); ++it) {
+    if (load_coherent(flag) == epoch) return true;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return false;
+}
+__device__ __forceinline__ bool wait_for_count(const unsigned* counter, unsigned target) {
+  for (int it = 0; it < (1 << 20); ++it) {
+    if (load_coherent(counter) >= target) return true;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return false;
+}
+
+// Wait until this wave's outstanding memory operations have completed: its
+// device-scope stores are then visible to every XCD.  Each wave runs it before
+// the barrier that precedes an arrival.
+__device__ __forceinline__ void drain_stores() { __builtin_amdgcn_s_waitcnt(0); }
+
+// ---------------------------------------------------------------------------
+// Producer: partial T over k32 steps [p*S/NP, (p+1)*S/NP) of in_dim, then,
+// after the producer barrier, one slice of T summed over all partials.
+// ---------------------------------------------------------------------------
+// Chunk c of a 32 x kVCols tile of V is row (c % 32), columns 8*(c / 32)..+7:
+// consecutive lanes take consecutive rows, so their transposed LDS stores
+// fall in consecutive banks.
 template <typename E>
-__device__ void produce_xv(const DecodeArgs& a, int p, int NT, float* smem) {
+__device__ __forceinline__ Frag8<E> load_v_chunk(const E* V, int k0, int jc0, int I, int R, bool valigned, int c) {
+  const int row = c % 32, cg = (c / 32) * 8;
+  const int gi = k0 + row, gj = jc0 + cg;
+  if (gi >= I || gj >= R) return zero_frag<E>();
+  const E* src = V + size_t(gi) * R + gj;
+  return (valigned && gj + 8 <= R) ? load_frag<E>(src) : load_frag_partial<E>(src, min(8, R - gj));
+}
+
+template <typename E, typename Raw>
+__device__ __forceinline__ void store_v_chunk(Raw* vt, int c, const Frag8<E>& f) {
+  const int row = c % 32, cg = (c / 32) * 8;
+  Raw vals[8];
+  __builtin_memcpy(vals, &f, sizeof(vals));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) vt[(cg + e) * kVPitch + row] = vals[e];
+}
+
+template <typename E, int NT>
+__device__ void produce_xv(const DecodeArgs& a, int p, void* smem) {
+  using Raw = typename std::conditional<sizeof(E) == 2, uint16_t, float>::type;
+  // k32 steps whose loads are in flight together (bounded by registers).
+  constexpr int kBatch = per_tile_budget(sizeof(E) == 2 ? 4 : 2, NT);
+  Raw* vt = static_cast<Raw*>(smem);  // [kVCols][kVPitch]
   const E* X = static_cast<const E*>(a.x);
   const E* V = static_cast<const E*>(a.v);
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
+  const int lr = l & 15, kq = (l >> 4) * 8;
   const int M = a.M, I = a.I, R = a.R;
-  const int i0 = int(int64_t(p) * I / a.NP), i1 = int(int64_t(p + 1) * I / a.NP);
-  const int RC = R < kThreads ? R : kThreads;   // columns per pass
-  const int PH = kThreads / RC;                 // row phases
-  const int jl = tid % RC, ph = tid / RC;
-  float* xs = smem;                   // [16][kStageRows]
-  float* red = smem + 16 * kStageRows;  // [PH][16][RC]
-  float* tp = a.tpart + size_t(p) * M * R;
+  const int s0 = int(int64_t(p) * a.S / a.NP), s1 = int(int64_t(p + 1) * a.S / a.NP);
+  const bool valigned = (R % 8) == 0;
+  const int n = M * R;
+  float* tp = a.tpart + size_t(p) * n;
+  constexpr int kTilesPerWave = kVCols / 16 / kWaves;  // 2
 
-  for (int tg = 0; tg < NT; ++tg) {
-    for (int jc0 = 0; jc0 < R; jc0 += RC) {
-      const int j = jc0 + jl;
-      float acc[16];
+  for (int jc0 = 0; jc0 < R; jc0 += kVCols) {
+    f32x4 acc[NT][kTilesPerWave];
 #pragma unroll
-      for (int mm = 0; mm < 16; ++mm) acc[mm] = 0.f;
-      for (int c0 = i0; c0 < i1; c0 += kStageRows) {
-        const int cn = min(kStageRows, i1 - c0);
-        for (int idx = tid; idx < 16 * kStageRows; idx += kThreads) {
-          const int mm = idx / kStageRows, ii = idx % kStageRows;
-          const int tok = tg * 16 + mm;
-          xs[idx] = (tok < M && ii < cn) ? to_f32<E>(X[size_t(tok) * I + c0 + ii]) : 0.f;
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int c = 0; c < kTilesPerWave; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b0 = s0; b0 < s1; b0 += kBatch) {
+      // Issue every load of the batch first.
+      Frag8<E> rv[kBatch][kStageChunks], rx[kBatch][NT];
+#pragma unroll
+      for (int bi = 0; bi < kBatch; ++bi) {
+        const int k0 = (b0 + bi) * 32;
+        const bool live = b0 + bi < s1;
+#pragma unroll
+        for (int q = 0; q < kStageChunks; ++q)
+          rv[bi][q] = live ? load_v_chunk<E>(V, k0, jc0, I, R, valigned, tid + kThreads * q) : zero_frag<E>();
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int tok = t * 16 + lr;
+          rx[bi][t] = load_frag_if<E>(X + size_t(tok) * I + k0 + kq, live && tok < M && k0 + kq < I);
         }
-        __syncthreads();
-        if (ph < PH && j < R) {
-          for (int ii = ph; ii < cn; ii += PH) {
-            const float vj = to_f32<E>(V[size_t(c0 + ii) * R + j]);
+      }
 #pragma unroll
-            for (int mm = 0; mm < 16; ++mm) acc[mm] += xs[mm * kStageRows + ii] * vj;
-          }
+      for (int bi = 0; bi < kBatch; ++bi) {
+        if (b0 + bi >= s1) break;
+        __syncthreads();  // the previous step's reads of vt are done
+#pragma unroll
+        for (int q = 0; q < kStageChunks; ++q) store_v_chunk<E, Raw>(vt, tid + kThreads * q, rv[bi][q]);
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < kTilesPerWave; ++c) {
+          const int col = (w * kTilesPerWave + c) * 16 + lr;
+          const Frag8<E> fv = load_frag<E>(reinterpret_cast<const E*>(&vt[col * kVPitch + kq]));
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[t][c] = mma_k32(rx[bi][t], fv, acc[t][c]);
         }
-        __syncthreads();
       }
-      if (ph < PH) {
-#pragma unroll
-        for (int mm = 0; mm < 16; ++mm) red[(ph * 16 + mm) * RC + jl] = acc[mm];
-      }
-      __syncthreads();
-      for (int idx = tid; idx < 16 * RC; idx += kThreads) {
-        const int mm = idx / RC, jj = idx % RC;
-        float sum = 0.f;
-        for (int q = 0; q < PH; ++q) sum += red[(q * 16 + mm) * RC + jj];
-        const int tok = tg * 16 + mm;
-        if (tok < M && jc0 + jj < R) tp[size_t(tok) * R + jc0 + jj] = sum;
-      }
-      __syncthreads();
     }
+    // C layout: lane holds tokens 4*(l/16)+e of tile t, column lr of tile c.
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int c = 0; c < kTilesPerWave; ++c) {
+        const int j = jc0 + (w * kTilesPerWave + c) * 16 + lr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int tok = t * 16 + (l >> 4) * 4 + e;
+          if (tok < M && j < R) store_coherent(&tp[size_t(tok) * R + j], __float_as_uint(acc[t][c][e]));
+        }
+      }
   }
 
-  // All producers' partials complete: reduce one slice of the M x R outputs.
-  __threadfence();
-  __syncthreads();
+  // Barrier of the producers.  The last to depart resets the counters (every
+  // producer has seen the full count by then).
   __shared__ unsigned s_ok;
+  __shared__ float s_red[kThreads];
+  drain_stores();
+  __syncthreads();
   if (tid == 0) {
-    atomic_add_agent(&a.ctrl[kArrive1], 1u);
-    const bool ok = wait_at_least(&a.ctrl[kArrive1], unsigned(a.NP));
+    add_coherent(&a.ctrl[kArrive], 1u);
+    const bool ok = wait_for_count(&a.ctrl[kArrive], unsigned(a.NP));
     if (!ok) atomicOr(&a.ctrl[kErr], 1u);
+    if (add_coherent(&a.ctrl[kDepart], 1u) == unsigned(a.NP - 1)) {
+      store_coherent(&a.ctrl[kArrive], 0u);
+      store_coherent(&a.ctrl[kDepart], 0u);
+    }
     s_ok = ok;
   }
   __syncthreads();
-  __threadfence();
-  const int n = M * R;
-  const int q0 = int(int64_t(p) * n / a.NP), q1 = int(int64_t(p + 1) * n / a.NP);
-  for (int idx = q0 + tid; idx < q1; idx += kThreads) {
-    float sum = 0.f;
-    for (int q = 0; q < a.NP; ++q) sum += a.tpart[size_t(q) * n + idx];
-    a.tfull[idx] = s_ok ? sum : __builtin_nanf("");
+
+  // This producer's slice of T, published zero padded as [16*NT][Rp] in the
+  // operand type, two elements per 32-bit word.  `tpo` threads share one word:
+  // each sums a contiguous run of partials, then the runs are added in order.
+  const int Rp = (R + 31) / 32 * 32;
+  const int n_words = 16 * NT * Rp / 2;
+  const int w0_ = int(int64_t(p) * n_words / a.NP), w1_ = int(int64_t(p + 1) * n_words / a.NP);
+  const int nw = w1_ - w0_;
+  int tpo = 1;
+  while (tpo * 2 * nw <= kThreads && tpo * 2 <= a.NP) tpo *= 2;
+  const int per_pass = kThreads / tpo;
+  const int sub = tid % tpo, q0 = sub * a.NP / tpo, q1 = (sub + 1) * a.NP / tpo;
+  for (int wb = w0_; wb < w1_; wb += per_pass) {
+    const int word = wb + tid / tpo;
+    float part[2] = {0.f, 0.f};
+    if (word < w1_) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int idx = 2 * word + h, tok = idx / Rp, j = idx % Rp;
+        if (tok < M && j < R) {
+          const float* src = a.tpart + size_t(tok) * R + j;
+          int q = q0;
+          for (; q + 8 <= q1; q += 8) {
+            float v8[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v8[u] = __uint_as_float(load_coherent(src + size_t(q + u) * n));
+#pragma unroll
+            for (int u = 0; u < 8; ++u) part[h] += v8[u];
+          }
+          for (; q < q1; ++q) part[h] += __uint_as_float(load_coherent(src + size_t(q) * n));
+        }
+      }
+    }
+    __syncthreads();
+    s_red[tid] = part[0];
+    __syncthreads();
+    float lo = 0.f;
+    if (sub == 0)
+      for (int k = 0; k < tpo; ++k) lo += s_red[tid + k];
+    __syncthreads();
+    s_red[tid] = part[1];
+    __syncthreads();
+    if (sub == 0 && word < w1_) {
+      float hi = 0.f;
+      for (int k = 0; k < tpo; ++k) hi += s_red[tid + k];
+      if (!s_ok) lo = hi = __builtin_nanf("");
+      uint32_t bits;
+      if constexpr (sizeof(E) == 2) {
+        bits = uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+        store_coherent(reinterpret_cast<uint32_t*>(a.tfull) + word, bits);
+      } else {
+        store_coherent(reinterpret_cast<uint32_t*>(a.tfull) + 2 * word, __float_as_uint(lo));
+        store_coherent(reinterpret_cast<uint32_t*>(a.tfull) + 2 * word + 1, __float_as_uint(hi));
+      }
+    }
   }
-  __threadfence();
+  drain_stores();
   __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = atomic_add_agent(&a.ctrl[kArrive2], 1u);
-    if (prev == unsigned(a.NP - 1)) atomic_store_agent(&a.ctrl[kTReady], 1u);
+  if (tid == 0 && add_coherent(&a.ctrl[kPublished], 1u) == unsigned(a.NP - 1)) {
+    store_coherent(&a.ctrl[kPublished], 0u);
+    store_coherent(&a.ctrl[kFlag], a.epoch);
   }
 }
 
-template <typename E, int NT, int UNR>
+// ---------------------------------------------------------------------------
+// Consumer: output rows [c*16*RT, (c+1)*16*RT) over the whole of in_dim.
+// ---------------------------------------------------------------------------
+template <typename E, int NT, int RT, int UNR>
 __device__ void consume(const DecodeArgs& a, int c, f32x4* red) {
   const E* X = static_cast<const E*>(a.x);
   const E* W0 = static_cast<const E*>(a.w0);
   const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
   const int lr = l & 15, kq = (l >> 4) * 8;
-  const int M = a.M, O = a.O, I = a.I, R = a.R;
-  const int g = c / a.KS, ks = c % a.KS;
-  const int o_base = g * kRows;
-  const int s_begin = int(int64_t(ks) * a.S / a.KS), s_end = int(int64_t(ks + 1) * a.S / a.KS);
+  const int M = a.M, I = a.I, R = a.R;
+  // Balanced contiguous row range [o_base, o_end) of this workgroup; the
+  // tiles' rows past o_end are masked.
+  const int o_base = int(int64_t(c) * a.O / a.NB), o_end = int(int64_t(c + 1) * a.O / a.NB);
 
-  f32x4 acc[4][NT];
+  f32x4 acc[RT][NT];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Waves take the k32 steps of the slice round-robin, UNR steps at a time.
-  for (int st = s_begin + w; st < s_end; st += 4 * UNR) {
-    Frag8<E> fa[UNR][4], fb[UNR][NT];
+  for (int st = w; st < a.S; st += kWaves * UNR) {
+    Frag8<E> fa[UNR][RT], fb[UNR][NT];
 #pragma unroll
     for (int uu = 0; uu < UNR; ++uu) {
-      const int step = st + 4 * uu;
+      const int step = st + kWaves * uu;
       const int k = step * 32 + kq;
-      const bool kv = step < s_end && k < I;
+      const bool kv = step < a.S && k < I;
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
+      for (int rt = 0; rt < RT; ++rt) {
         const int row = o_base + rt * 16 + lr;
-        fa[uu][rt] = load_frag_if<E>(W0 + size_t(row) * I + k, kv && row < O);
+        fa[uu][rt] = load_frag_if<E>(W0 + size_t(row) * I + k, kv && row < o_end);
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
@@ -177,141 +332,115 @@ __device__ void consume(const DecodeArgs& a, int c, f32x4* red) {
 #pragma unroll
     for (int uu = 0; uu < UNR; ++uu)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[rt][t] = mma_k32(fa[uu][rt], fb[uu][t], acc[rt][t]);
   }
 
-  // Fixed-order reduction of the four waves; wave w keeps row tile w.
+  // Fixed-order reduction over the eight waves; wave q < RT*NT keeps tile q.
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int t = 0; t < NT; ++t) red[((w * 4 + rt) * NT + t) * kWave + l] = acc[rt][t];
+    for (int t = 0; t < NT; ++t) red[((w * RT + rt) * NT + t) * kWave + l] = acc[rt][t];
   __syncthreads();
-  f32x4 sum[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    sum[t] = red[((0 * 4 + w) * NT + t) * kWave + l];
-    sum[t] += red[((1 * 4 + w) * NT + t) * kWave + l];
-    sum[t] += red[((2 * 4 + w) * NT + t) * kWave + l];
-    sum[t] += red[((3 * 4 + w) * NT + t) * kWave + l];
-  }
 
-  __shared__ unsigned s_flag;
-  if (a.KS > 1) {
-    float4* slot = a.ppart + (size_t(g * a.KS + ks) * 4 + w) * NT * kWave;
+  const bool mine = w < RT * NT;
+  const int rt = mine ? w / NT : 0, t = mine ? w % NT : 0;
+  f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (mine) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-      if (t * 16 + lr < M) slot[t * kWave + l] = make_float4(sum[t].x, sum[t].y, sum[t].z, sum[t].w);
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_flag = (atomic_add_agent(&a.gcount[g], 1u) == unsigned(a.KS - 1));
-    __syncthreads();
-    if (!s_flag) return;
-    __threadfence();
-#pragma unroll
-    for (int t = 0; t < NT; ++t) sum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int q = 0; q < a.KS; ++q) {
-      const float4* sl = a.ppart + (size_t(g * a.KS + q) * 4 + w) * NT * kWave;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (t * 16 + lr < M) {
-          const float4 v4 = sl[t * kWave + l];
-          sum[t] += f32x4{v4.x, v4.y, v4.z, v4.w};
-        }
-      }
-    }
-    if (tid == 0) atomic_store_agent(&a.gcount[g], 0u);
+    for (int q = 0; q < kWaves; ++q) sum += red[((q * RT + rt) * NT + t) * kWave + l];
   }
 
   // Epilogue: row scale, then the rank-r delta, then one rounding.
   const E* S_ = static_cast<const E*>(a.s);
-  const int orow0 = o_base + w * 16 + (l >> 4) * 4;
-  float sc[4];
+  const int orow0 = o_base + rt * 16 + (l >> 4) * 4;
+  const int tok = t * 16 + lr;
+  if (mine) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) sc[e] = (orow0 + e < O) ? to_f32<E>(S_[orow0 + e]) : 0.f;
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sum[t][e] *= sc[e];
+    for (int e = 0; e < 4; ++e) sum[e] *= (orow0 + e < o_end) ? to_f32<E>(S_[orow0 + e]) : 0.f;
+  }
 
+  bool ok = true;
   if (R > 0) {
+    __shared__ unsigned s_ok;
     if (tid == 0) {
-      const bool ok = wait_at_least(&a.ctrl[kTReady], 1u);
-      if (!ok) atomicOr(&a.ctrl[kErr], 1u);
-      s_flag = ok;
+      const bool got = wait_for_epoch(&a.ctrl[kFlag], a.epoch);
+      if (!got) atomicOr(&a.ctrl[kErr], 1u);
+      s_ok = got;
     }
     __syncthreads();
-    __threadfence();
-    const bool ok = s_flag;
-    const E* U = static_cast<const E*>(a.u);
-    const int urow = o_base + w * 16 + lr;
-    const bool aligned = (R % 8) == 0;
-    for (int kk = 0; kk < R; kk += 32) {
-      const int j = kk + kq;
-      Frag8<E> fu = zero_frag<E>();
-      if (urow < O && j < R)
-        fu = aligned ? load_frag<E>(U + size_t(urow) * R + j) : load_frag_partial<E>(U + size_t(urow) * R + j, min(8, R - j));
+    ok = s_ok;
+    if (mine) {
+      const E* U = static_cast<const E*>(a.u);
+      const E* T = reinterpret_cast<const E*>(a.tfull);
+      const int urow = o_base + rt * 16 + lr;
+      const int Rp = (R + 31) / 32 * 32;
+      const bool aligned = (R % 8) == 0;
+      constexpr int kEpi = 4;  // k32 steps of the rank tail whose loads are in flight together
+      for (int kb = 0; kb < R; kb += 32 * kEpi) {
+        Frag8<E> fu[kEpi], ft[kEpi];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int tok = t * 16 + lr;
-        float tv[8];
+        for (int q = 0; q < kEpi; ++q) {
+          const int j = kb + 32 * q + kq;
+          fu[q] = zero_frag<E>();
+          ft[q] = zero_frag<E>();
+          if (j < Rp) ft[q] = load_t_frag<E>(T + size_t(tok) * Rp + j);
+          if (urow < o_end && j < R)
+            fu[q] = aligned ? load_frag<E>(U + size_t(urow) * R + j) : load_frag_partial<E>(U + size_t(urow) * R + j, min(8, R - j));
+        }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) tv[e] = (tok < M && j + e < R) ? a.tfull[size_t(tok) * R + j + e] : 0.f;
-        sum[t] = mma_k32(fu, frag_from_f32<E>(tv), sum[t]);
+        for (int q = 0; q < kEpi; ++q) sum = mma_k32(fu[q], ft[q], sum);
       }
     }
-    if (!ok) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) sum[t] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-    }
   }
+  if (!mine) return;
+  if (!ok) sum = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
 
   E* Y = static_cast<E*>(a.y);
+  if (tok < M) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int tok = t * 16 + lr;
-    if (tok < M) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (orow0 + e < O) Y[size_t(tok) * O + orow0 + e] = from_f32<E>(sum[t][e]);
-    }
+    for (int e = 0; e < 4; ++e)
+      if (orow0 + e < o_end) Y[size_t(tok) * a.O + orow0 + e] = from_f32<E>(sum[e]);
   }
 }
 
-template <typename E, int NT>
+template <typename E, int NT, int RT>
 __global__ __launch_bounds__(kThreads) void forward_decode_kernel(DecodeArgs a) {
-  constexpr int kConsumerLds = 4 * 4 * NT * kWave * 16;           // bytes
-  constexpr int kProducerLds = (16 * kStageRows + 16 * kThreads) * 4;
+  constexpr int kConsumerLds = kWaves * RT * NT * kWave * 16;
+  constexpr int kProducerLds = kVCols * kVPitch * int(sizeof(E));
   constexpr int kLds = kConsumerLds > kProducerLds ? kConsumerLds : kProducerLds;
   __shared__ float4 smem[kLds / 16];
-  __shared__ unsigned s_ticket;
-  if (threadIdx.x == 0) s_ticket = atomic_add_agent(&a.ctrl[kTicket], 1u);
-  __syncthreads();
-  const unsigned ticket = s_ticket;
-  if (ticket < unsigned(a.NP)) {
-    produce_xv<E>(a, int(ticket), NT, reinterpret_cast<float*>(smem));
+  if (int(blockIdx.x) < a.NP) {
+    produce_xv<E, NT>(a, int(blockIdx.x), smem);
   } else {
-    constexpr int UNR = sizeof(E) == 2 ? 4 : 2;
-    consume<E, NT, UNR>(a, int(ticket - a.NP), reinterpret_cast<f32x4*>(smem));
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomic_add_agent(&a.ctrl[kDone], 1u);
-    if (prev == a.total - 1) {
-      atomic_store_agent(&a.ctrl[kTicket], 0u);
-      atomic_store_agent(&a.ctrl[kArrive1], 0u);
-      atomic_store_agent(&a.ctrl[kArrive2], 0u);
-      atomic_store_agent(&a.ctrl[kTReady], 0u);
-      atomic_store_agent(&a.ctrl[kDone], 0u);
-    }
+    constexpr int UNR = per_tile_budget(sizeof(E) == 2 ? 4 : 2, NT);
+    consume<E, NT, RT, UNR>(a, int(blockIdx.x) - a.NP, reinterpret_cast<f32x4*>(smem));
   }
 }
 
-template <typename E, int NT>
-hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((forward_decode_kernel<E, NT>), dim3(a.total), dim3(kThreads), 0, stream, a);
+template <typename E, int NT, int RT>
+hipError_t launch_t(const DecodeArgs& a, int blocks, hipStream_t stream) {
+  hipLaunchKernelGGL((forward_decode_kernel<E, NT, RT>), dim3(blocks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_e(const DecodePlan& p, const DecodeArgs& a, hipStream_t stream) {
+  const int blocks = p.NP + p.NG;
+  if (p.NT == 1) {
+    switch (p.RT) {
+      case 4: return launch_t<E, 1, 4>(a, blocks, stream);
+      case 3: return launch_t<E, 1, 3>(a, blocks, stream);
+      case 2: return launch_t<E, 1, 2>(a, blocks, stream);
+      default: return launch_t<E, 1, 1>(a, blocks, stream);
+    }
+  }
+  if (p.NT == 2) {
+    if (p.RT == 2) return launch_t<E, 2, 2>(a, blocks, stream);
+    return launch_t<E, 2, 1>(a, blocks, stream);
+  }
+  return launch_t<E, 4, 1>(a, blocks, stream);
 }
 
 }  // namespace
@@ -319,59 +448,49 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
 DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus) {
   DecodePlan p{};
   p.NT = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
-  p.NG = int((out_dim + kRows - 1) / kRows);
   p.S = int((in_dim + 31) / 32);
-  const int target = 8 * cus;
-  int ks = 1;
-  if (p.NG < target) {
-    ks = (target + p.NG - 1) / p.NG;
-    const int max_ks = p.S / 4 > 1 ? p.S / 4 : 1;
-    if (ks > max_ks) ks = max_ks;
-  }
-  if (ks > 1 && p.NG > kMaxGroupCounters) ks = 1;
-  p.KS = ks;
+  // Consumers: a multiple of the compute-unit count, each with a balanced row
+  // range of at most 16 * (4 / NT) rows; RT tiles cover the widest range.
+  const int64_t max_rows = 16 * (4 / p.NT);
+  int64_t nb = cus;
+  while ((out_dim + nb - 1) / nb > max_rows) nb += cus;
+  if (nb > out_dim) nb = out_dim;
+  p.NG = int(nb);
+  const int64_t rows = (out_dim + nb - 1) / nb;
+  p.RT = int((rows + 15) / 16);
   if (rank > 0) {
-    int np = int((in_dim + 31) / 32);
-    if (np > 128) np = 128;
-    if (np > cus / 2) np = cus / 2;
+    int np = (p.S + kStepsPerProducer - 1) / kStepsPerProducer;
+    const int cap = cus < kMaxProducers ? cus : kMaxProducers;
+    if (np > cap) np = cap;
     if (np < 1) np = 1;
     p.NP = np;
   } else {
     p.NP = 0;
   }
+  const size_t rp = size_t((rank + 31) / 32 * 32);
   size_t off = kControlBytes;
-  p.off_tpart = off;
+  p.off_tpart = off;  // NP partials of [m][rank] fp32
   off = align_up(off + size_t(p.NP) * size_t(m) * size_t(rank) * 4, 256);
-  p.off_tfull = off;
-  off = align_up(off + size_t(m) * size_t(rank) * 4, 256);
-  p.off_ppart = off;
-  if (p.KS > 1) off = align_up(off + size_t(p.NG) * p.KS * 4 * p.NT * kWave * 16, 256);
+  p.off_tfull = off;  // T, [16*NT][rp], fp32 or bf16
+  off = align_up(off + size_t(16 * p.NT) * rp * 4, 256);
   p.bytes = off;
   return p;
 }
 
 hipError_t launch_forward_decode(const DecodePlan& p, tb_dtype dtype, const void* x, const void* s, const void* w0,
                                  const void* u, const void* v, void* y, int64_t m, int64_t out_dim, int64_t in_dim,
-                                 int64_t rank, void* workspace, hipStream_t stream) {
+                                 int64_t rank, void* workspace, unsigned epoch, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   DecodeArgs a;
   a.x = x; a.s = s; a.w0 = w0; a.u = u; a.v = v; a.y = y;
   a.M = int(m); a.O = int(out_dim); a.I = int(in_dim); a.R = int(rank);
-  a.NG = p.NG; a.KS = p.KS; a.S = p.S; a.NP = p.NP;
-  a.total = unsigned(p.NP + p.NG * p.KS);
+  a.S = p.S; a.NP = p.NP; a.NB = p.NG;
+  a.epoch = epoch;
   a.ctrl = reinterpret_cast<unsigned*>(ws);
-  a.gcount = reinterpret_cast<unsigned*>(ws + 256);
   a.tpart = reinterpret_cast<float*>(ws + p.off_tpart);
   a.tfull = reinterpret_cast<float*>(ws + p.off_tfull);
-  a.ppart = reinterpret_cast<float4*>(ws + p.off_ppart);
-  if (dtype == TB_BF16) {
-    if (p.NT == 1) return launch_t<bf16_t, 1>(a, stream);
-    if (p.NT == 2) return launch_t<bf16_t, 2>(a, stream);
-    return launch_t<bf16_t, 4>(a, stream);
-  }
-  if (p.NT == 1) return launch_t<float, 1>(a, stream);
-  if (p.NT == 2) return launch_t<float, 2>(a, stream);
-  return launch_t<float, 4>(a, stream);
+  if (dtype == TB_BF16) return launch_e<bf16_t>(p, a, stream);
+  return launch_e<float>(p, a, stream);
 }
 
 }  // namespace tb

@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace tb {
 
 constexpr int kWave = 64;
@@ -117,30 +119,11 @@ __device__ __forceinline__ f32x4 mma_k32(const Frag8<float>& a, const Frag8<floa
   return c;
 }
 
-// Agent-scope synchronisation primitives.  Plain stores made before
-// fence_release() are visible to another workgroup (on any XCD) that observes
-// the following atomic and then runs fence_acquire().
-__device__ __forceinline__ void fence_release() { __atomic_thread_fence(__ATOMIC_RELEASE); }
-__device__ __forceinline__ void fence_acquire() { __atomic_thread_fence(__ATOMIC_ACQUIRE); }
-
+// Agent-scope read-modify-write with acquire/release semantics.  On gfx950
+// the release and acquire parts write back and invalidate the XCD's L2, so
+// only a handful of workgroups per launch may use it.
 __device__ __forceinline__ unsigned atomic_add_agent(unsigned* p, unsigned v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ unsigned atomic_load_agent(const unsigned* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void atomic_store_agent(unsigned* p, unsigned v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Bounded wait until *p >= target.  Returns false after the spin limit
-// (about 0.1 s), so a wait can never hang the device.
-__device__ __forceinline__ bool wait_at_least(const unsigned* p, unsigned target) {
-  for (int it = 0; it < (1 << 20); ++it) {
-    if (atomic_load_agent(p) >= target) return true;
-    __builtin_amdgcn_s_sleep(2);
-  }
-  return false;
 }
 
 }  // namespace tb

@@ -22,18 +22,21 @@ constexpr int kDecodeMaxTokens = 64;
 
 struct DecodePlan {
   int NT;   // 16-token column tiles (1, 2 or 4)
-  int NG;   // 64-row output groups
-  int KS;   // split of the in_dim steps across workgroups
+  int RT;   // 16-row output tiles per consumer workgroup (1, 2 or 4)
+  int NG;   // consumer workgroups
   int S;    // k32 steps over in_dim
   int NP;   // producer workgroups computing x . V
-  size_t off_tpart, off_tfull, off_ppart, bytes;
+  size_t off_tpart, off_tfull, bytes;
 };
 
 DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus);
 
 hipError_t launch_forward_decode(const DecodePlan& p, tb_dtype dtype, const void* x, const void* s, const void* w0,
                                  const void* u, const void* v, void* y, int64_t m, int64_t out_dim, int64_t in_dim,
-                                 int64_t rank, void* workspace, hipStream_t stream);
+                                 int64_t rank, void* workspace, unsigned epoch, hipStream_t stream);
+
+// A fresh nonzero value per launch that publishes through a workspace flag.
+unsigned next_epoch();
 
 // ---- forward, prefill token counts (bf16, m > kDecodeMaxTokens) ----------
 struct GemmPlan {
