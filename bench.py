@@ -205,7 +205,7 @@ def main():
         unit = "GB/s"
         value = step_bytes / (ms * 1e-3) / 1e9
         achieved = launch_bytes.sum() / (per_call_ms.sum() * 1e-3) / 1e9
-        kernel = "forward_decode_kernel<bf16,%d>" % (1 if M <= 16 else (2 if M <= 32 else 4))
+        kernel = "forward_decode_kernel<bf16,%d,RT>" % (1 if M <= 16 else (2 if M <= 32 else 4))
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
         per_launch = float(launch_bytes.mean())
