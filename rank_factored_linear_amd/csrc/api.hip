@@ -3,7 +3,6 @@
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
 
-#include <atomic>
 #include <stdio.h>
 
 #include "tb_host.h"
@@ -53,15 +52,6 @@ tb_status check_dims(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank) {
 }
 
 }  // namespace
-
-unsigned next_epoch() {
-  static std::atomic<unsigned> counter{0};
-  unsigned e;
-  do {
-    e = counter.fetch_add(1u, std::memory_order_relaxed) + 1u;
-  } while (e == 0u);
-  return e;
-}
 
 int device_cu_count(int* cus) {
   int dev = 0;
@@ -144,7 +134,10 @@ tb_status tb_linear_forward(const void* x, const void* s, const void* w0, const 
     if (e != hipSuccess) return hip_fail(e, "launching the prefill projection");
     return ok();
   }
-  // Few tokens (or fp32): the fused single-launch kernel, 64 tokens at a time.
+  // Few tokens (or fp32): the streaming decode path, 64 tokens at a time.
+  // Its loads address a row block (at most 96 rows) with 32-bit byte offsets.
+  if (in_dim * int64_t(esize(dtype)) * 96 >= (int64_t(1) << 32))
+    return fail(TB_ERR_UNSUPPORTED, "in_dim %lld is too large for the few-token path", (long long)in_dim);
   const int64_t mm = m < kDecodeMaxTokens ? m : kDecodeMaxTokens;
   const DecodePlan p = plan_decode(mm, out_dim, in_dim, rank, cus);
   if (workspace_bytes < p.bytes)
@@ -156,7 +149,7 @@ tb_status tb_linear_forward(const void* x, const void* s, const void* w0, const 
     const char* xt = static_cast<const char*>(x) + size_t(t0) * size_t(in_dim) * es;
     char* yt = static_cast<char*>(y) + size_t(t0) * size_t(out_dim) * es;
     hipError_t e =
-        launch_forward_decode(pt, dtype, xt, s, w0, u, v, yt, mt, out_dim, in_dim, rank, workspace, next_epoch(), hs);
+        launch_forward_decode(pt, dtype, xt, s, w0, u, v, yt, mt, out_dim, in_dim, rank, workspace, hs);
     if (e != hipSuccess) return hip_fail(e, "launching the decode projection");
   }
   return ok();

@@ -1,32 +1,43 @@
-// Fused theta-bundle projection for few tokens (m <= 64): one launch.
+// Theta-bundle projection for few tokens (m <= 64): one launch.
 //
 //   y = s (.) (x . W0^T) + (x . V) . U^T        ("The theta bundle": the
 //   transpose of weight = diag(s) W0 + U V^T applied to x)
 //
 // At these token counts the projection is bound by HBM bandwidth: every byte
 // of W0 is read once, and U, V, s once.  The grid holds two kinds of
-// workgroups, told apart by their index:
+// workgroup, the producers first, so that on every XCD the hardware dispatches
+// them ahead of any streaming workgroup; producers never wait, so the
+// streamers' waits on them always end.
 //
-//   producers (indices 0..NP-1) compute T = x . V on the matrix cores, each
-//     over four k32 steps of in_dim, into private partials.  They meet at a
-//     barrier (they hold the lowest indices, so they are dispatched first and
-//     are all resident), then each sums one slice of T over all partials in a
-//     fixed order and stores it; the last to finish raises a ready flag that
-//     carries this call's epoch.
-//   consumers (the rest) each own a contiguous, balanced range of at most
-//     16*RT output rows over the whole of in_dim.  Eight waves take the k32
-//     steps round-robin, streaming W0 rows through v_mfma 16x16x32 with x as
-//     the 16-token B operand (zero padded), and reduce in LDS in a fixed
-//     order.  The epilogue scales each row by s, waits for the flag, adds
-//     T . U^T on the matrix cores and stores y rounded once.
+//   producers (rank > 0): T = x . V.  Producer (kt, cb) owns the 16 columns
+//     [16cb, 16cb+16) of T over the k-slice kt of in_dim: no exchange with
+//     other producers.  Its waves take k32 steps round-robin, each loading a
+//     32 x 16 block of V (transposed through a wave-private LDS tile) and the
+//     x fragments, and multiply on the matrix cores; the eight partials are
+//     summed in LDS in a fixed order.  With several k-slices each producer
+//     stores its fp32 partial and the last of the column block to arrive sums
+//     them in k-slice order; the final block is published as T [16*NT][Rp] in
+//     the operand type and counted in a done word.
+//   streamers: the output rows are cut into NRB balanced row blocks of at
+//     most 16*TILES rows and in_dim into KS k-slices; streamer (rb, ks) owns
+//     one pair.  Each of its eight waves takes k32 steps round-robin and keeps
+//     D steps of W0 fragments (A operand, 16 rows x 32 k per tile, straight
+//     from HBM into registers) and x fragments (B operand, 16 tokens, served
+//     by the L2) in flight: one continuous software pipeline per wave with no
+//     workgroup barrier.  Afterwards each wave scales its rows by s (fetched
+//     at the start); the streamer of the last k-slice also adds its waves'
+//     k32 steps of T . U^T once every column block of T is published (U
+//     fetched before the stream).  The eight partials are summed in LDS in a
+//     fixed order.
+//     With one k-slice the result is stored rounded once; otherwise each
+//     streamer stores its fp32 partial, and the last of the row block to
+//     arrive sums the KS partials in k-slice order and stores y.
 //
-// All data that crosses workgroups (partials, T, counters, flag) is written
-// and read with device-scope (sc1) accesses, which are coherent across XCDs
-// without writing back or invalidating the L2; a writer waits for its stores
-// to complete (s_waitcnt) before it counts itself in.  No workgroup ever
-// fences, takes a ticket or waits on a consumer, and the flag needs no reset
-// because each call brings a new epoch.  Every wait is bounded: a timeout
-// sets an error word and poisons the output with NaN instead of hanging.
+// Data crossing workgroups (T partials, y partials, counters) moves only
+// through device-scope (sc1) 32-bit accesses, coherent across XCDs without
+// writing back or invalidating any L2; a writer drains its stores before it
+// counts itself in.  Every wait is bounded: a timeout sets the sticky error
+// word and poisons the affected y with NaN.
 #include "tb_device.h"
 #include "tb_host.h"
 
@@ -36,19 +47,14 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kVCols = 256;          // columns of V per producer pass
-constexpr int kVPitch = 40;          // LDS pitch (elements) of the transposed V tile
-constexpr int kStageChunks = 32 * (kVCols / 8) / kThreads;  // 16-byte V chunks per thread per step
-constexpr int kMaxProducers = 256;   // at most one per compute unit: all resident together
-constexpr int kStepsPerProducer = 4;  // k32 steps of V per producer (one batch of loads)
 
-// Control words: [kFlag] T-ready epoch, [kErr] sticky timeout flag,
-// [kArrive] / [kDepart] producer barrier, [kPublished] T slices stored.
-enum Ctrl { kFlag = 1, kErr = 2, kArrive = 3, kDepart = 4, kPublished = 5 };
-
-// Loads kept in flight per wave scale down with the token tiles so that the
-// kernel fits 128 VGPRs (two 512-thread workgroups per compute unit).
-constexpr int per_tile_budget(int base, int nt) { return base / nt > 0 ? base / nt : 1; }
+// Control words: [kErr] sticky timeout flag, [kDone] column blocks of T
+// published, [kFinish] rank streamers past their read of T; from word
+// kCbCounters on, one arrival counter per column block of T (k-sliced
+// producers), from kRbCounters on one per row block (k-sliced streamers).
+enum Ctrl { kErr = 2, kDone = 5, kFinish = 6 };
+constexpr int kCbCounters = 64;
+constexpr int kRbCounters = kCbCounters + kMaxGroupCounters / 2;
 
 struct DecodeArgs {
   const void* x;
@@ -58,11 +64,12 @@ struct DecodeArgs {
   const void* v;
   void* y;
   int M, O, I, R;
-  int S, NP, NB;
-  unsigned epoch;
+  int NCB, KT;       // producers: NCB column blocks x KT k-slices
+  int NRB, KS, RBR;  // streamers: NRB row blocks x KS k-slices; RBR rows per block at most
   unsigned* ctrl;
-  float* tpart;
-  float* tfull;
+  float* tpart;  // [KT][16*NT][Rp] fp32 partials (KT > 1)
+  void* tfull;   // [16*NT][Rp] T in the operand type
+  float* ypart;  // [NRB][KS][16*NT][RBR] fp32 (KS > 1)
 };
 
 // Device-scope (sc1) 32-bit accesses: coherent across XCDs without touching
@@ -77,32 +84,7 @@ __device__ __forceinline__ unsigned add_coherent(unsigned* p, unsigned v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// B fragment of T (published zero padded as [16*NT][Rp]) read coherently.
-template <typename E> __device__ __forceinline__ Frag8<E> load_t_frag(const void* p);
-template <> __device__ __forceinline__ Frag8<bf16_t> load_t_frag<bf16_t>(const void* p) {
-  const uint32_t* q = static_cast<const uint32_t*>(p);
-  Frag8<bf16_t> f;
-  f.v = make_uint4(load_coherent(q), load_coherent(q + 1), load_coherent(q + 2), load_coherent(q + 3));
-  return f;
-}
-template <> __device__ __forceinline__ Frag8<float> load_t_frag<float>(const void* p) {
-  const uint32_t* q = static_cast<const uint32_t*>(p);
-  Frag8<float> f;
-  f.lo = make_float4(__uint_as_float(load_coherent(q)), __uint_as_float(load_coherent(q + 1)),
-                     __uint_as_float(load_coherent(q + 2)), __uint_as_float(load_coherent(q + 3)));
-  f.hi = make_float4(__uint_as_float(load_coherent(q + 4)), __uint_as_float(load_coherent(q + 5)),
-                     __uint_as_float(load_coherent(q + 6)), __uint_as_float(load_coherent(q + 7)));
-  return f;
-}
-
-// Bounded waits (about 0.1 s at most; relaxed polling, no cache invalidation).
-__device__ __forceinline__ bool wait_for_epoch(const unsigned* flag, unsigned epoch) {
-  for (int it = 0; it < (1 << 20); ++it) {
-    if (load_coherent(flag) == epoch) return true;
-    __builtin_amdgcn_s_sleep(2);
-  }
-  return false;
-}
+// Bounded wait (relaxed polling, no cache invalidation).
 __device__ __forceinline__ bool wait_for_count(const unsigned* counter, unsigned target) {
   for (int it = 0; it < (1 << 20); ++it) {
     if (load_coherent(counter) >= target) return true;
@@ -112,335 +94,438 @@ __device__ __forceinline__ bool wait_for_count(const unsigned* counter, unsigned
 }
 
 // Wait until this wave's outstanding memory operations have completed: its
-// device-scope stores are then visible to every XCD.  Each wave runs it before
-// the barrier that precedes an arrival.
+// device-scope stores are then visible to every XCD.
 __device__ __forceinline__ void drain_stores() { __builtin_amdgcn_s_waitcnt(0); }
 
-// ---------------------------------------------------------------------------
-// Producer: partial T over k32 steps [p*S/NP, (p+1)*S/NP) of in_dim, then,
-// after the producer barrier, one slice of T summed over all partials.
-// ---------------------------------------------------------------------------
-// Chunk c of a 32 x kVCols tile of V is row (c % 32), columns 8*(c / 32)..+7:
-// consecutive lanes take consecutive rows, so their transposed LDS stores
-// fall in consecutive banks.
+template <typename E> constexpr int frag_vgprs() { return sizeof(E) == 2 ? 4 : 8; }
+
+// Eight elements k..k+7 of one row of a [rows][R] matrix (zero past R).
 template <typename E>
-__device__ __forceinline__ Frag8<E> load_v_chunk(const E* V, int k0, int jc0, int I, int R, bool valigned, int c) {
-  const int row = c % 32, cg = (c / 32) * 8;
-  const int gi = k0 + row, gj = jc0 + cg;
-  if (gi >= I || gj >= R) return zero_frag<E>();
-  const E* src = V + size_t(gi) * R + gj;
-  return (valigned && gj + 8 <= R) ? load_frag<E>(src) : load_frag_partial<E>(src, min(8, R - gj));
+__device__ __forceinline__ Frag8<E> load_row8(const E* row, int k, int R, bool aligned) {
+  if (k >= R) return zero_frag<E>();
+  return aligned ? load_frag<E>(row + k) : load_frag_partial<E>(row + k, min(8, R - k));
 }
 
-template <typename E, typename Raw>
-__device__ __forceinline__ void store_v_chunk(Raw* vt, int c, const Frag8<E>& f) {
-  const int row = c % 32, cg = (c / 32) * 8;
-  Raw vals[8];
-  __builtin_memcpy(vals, &f, sizeof(vals));
-#pragma unroll
-  for (int e = 0; e < 8; ++e) vt[(cg + e) * kVPitch + row] = vals[e];
-}
+// ---------------------------------------------------------------------------
+// Producers.
+// ---------------------------------------------------------------------------
+constexpr int kVtPitch = 40;  // elements per column of a wave's transposed 16 x 32 V tile
 
 template <typename E, int NT>
-__device__ void produce_xv(const DecodeArgs& a, int p, void* smem) {
+__device__ void produce_t(const DecodeArgs& a, int p, uint8_t* smem) {
   using Raw = typename std::conditional<sizeof(E) == 2, uint16_t, float>::type;
-  // k32 steps whose loads are in flight together (bounded by registers).
-  constexpr int kBatch = per_tile_budget(sizeof(E) == 2 ? 4 : 2, NT);
-  Raw* vt = static_cast<Raw*>(smem);  // [kVCols][kVPitch]
+  constexpr int D = 8 / (1 + NT) > 0 ? 8 / (1 + NT) : 1;  // k32 steps in flight per wave
   const E* X = static_cast<const E*>(a.x);
   const E* V = static_cast<const E*>(a.v);
-  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
-  const int lr = l & 15, kq = (l >> 4) * 8;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid / kWave), l = tid % kWave;
+  const int lr = l & 15, q4 = l >> 4, kq = q4 * 8;
   const int M = a.M, I = a.I, R = a.R;
-  const int s0 = int(int64_t(p) * a.S / a.NP), s1 = int(int64_t(p + 1) * a.S / a.NP);
+  const int cb = p % a.NCB, kt = p / a.NCB;
+  const int S = (I + 31) / 32;
+  const int s0 = int(int64_t(kt) * S / a.KT), s1 = int(int64_t(kt + 1) * S / a.KT);
+  const int n = s1 - s0 > w ? (s1 - s0 - w + kWaves - 1) / kWaves : 0;
   const bool valigned = (R % 8) == 0;
-  const int n = M * R;
-  float* tp = a.tpart + size_t(p) * n;
-  constexpr int kTilesPerWave = kVCols / 16 / kWaves;  // 2
+  // This lane's piece of a 32 x 16 block of V: row l/2, columns 8*(l%2)..+7.
+  const int vr = l >> 1, vc = cb * 16 + (l & 1) * 8;
+  Raw* vt = reinterpret_cast<Raw*>(smem) + w * (16 * kVtPitch);  // [16 cols][kVtPitch], this wave's
 
-  for (int jc0 = 0; jc0 < R; jc0 += kVCols) {
-    f32x4 acc[NT][kTilesPerWave];
+  f32x4 acc[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+  for (int c = 0; c < NT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (n > 0) {
+    Frag8<E> vf[D], xf[D][NT];
+    auto issue = [&](Frag8<E>& fv, Frag8<E> (&fx)[NT], int i) {
+      const int k0 = (s0 + w + i * kWaves) * 32;
+      fv = k0 + vr < I ? load_row8<E>(V + size_t(k0 + vr) * R, vc, R, valigned) : zero_frag<E>();
+      const bool kv = k0 + kq < I;
 #pragma unroll
-      for (int c = 0; c < kTilesPerWave; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int b0 = s0; b0 < s1; b0 += kBatch) {
-      // Issue every load of the batch first.
-      Frag8<E> rv[kBatch][kStageChunks], rx[kBatch][NT];
+      for (int c = 0; c < NT; ++c)
+        fx[c] = load_frag_if<E>(X + size_t(min(c * 16 + lr, M - 1)) * I + (kv ? k0 + kq : 0), kv);
+    };
 #pragma unroll
-      for (int bi = 0; bi < kBatch; ++bi) {
-        const int k0 = (b0 + bi) * 32;
-        const bool live = b0 + bi < s1;
+    for (int d = 0; d < D; ++d) issue(vf[d], xf[d], min(d, n - 1));
+    for (int i0 = 0; i0 < n; i0 += D) {
 #pragma unroll
-        for (int q = 0; q < kStageChunks; ++q)
-          rv[bi][q] = live ? load_v_chunk<E>(V, k0, jc0, I, R, valigned, tid + kThreads * q) : zero_frag<E>();
+      for (int d = 0; d < D; ++d) {
+        if (i0 + d < n) {
+          // Transpose the V piece through the wave's LDS tile: column j of the
+          // block holds k = 0..31 contiguously.
+          Raw vals[8];
+          __builtin_memcpy(vals, &vf[d], sizeof(vals));
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const int tok = t * 16 + lr;
-          rx[bi][t] = load_frag_if<E>(X + size_t(tok) * I + k0 + kq, live && tok < M && k0 + kq < I);
-        }
-      }
+          for (int e = 0; e < 8; ++e) vt[((l & 1) * 8 + e) * kVtPitch + vr] = vals[e];
+          __builtin_amdgcn_wave_barrier();
+          const Frag8<E> fb = load_frag<E>(reinterpret_cast<const E*>(&vt[lr * kVtPitch + kq]));
 #pragma unroll
-      for (int bi = 0; bi < kBatch; ++bi) {
-        if (b0 + bi >= s1) break;
-        __syncthreads();  // the previous step's reads of vt are done
-#pragma unroll
-        for (int q = 0; q < kStageChunks; ++q) store_v_chunk<E, Raw>(vt, tid + kThreads * q, rv[bi][q]);
-        __syncthreads();
-#pragma unroll
-        for (int c = 0; c < kTilesPerWave; ++c) {
-          const int col = (w * kTilesPerWave + c) * 16 + lr;
-          const Frag8<E> fv = load_frag<E>(reinterpret_cast<const E*>(&vt[col * kVPitch + kq]));
-#pragma unroll
-          for (int t = 0; t < NT; ++t) acc[t][c] = mma_k32(rx[bi][t], fv, acc[t][c]);
+          for (int c = 0; c < NT; ++c) acc[c] = mma_k32(xf[d][c], fb, acc[c]);
+          __builtin_amdgcn_sched_barrier(0);
+          mfma_operand_guard();
+          __builtin_amdgcn_sched_barrier(0);
+          issue(vf[d], xf[d], min(i0 + d + D, n - 1));
         }
       }
     }
-    // C layout: lane holds tokens 4*(l/16)+e of tile t, column lr of tile c.
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int c = 0; c < kTilesPerWave; ++c) {
-        const int j = jc0 + (w * kTilesPerWave + c) * 16 + lr;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int tok = t * 16 + (l >> 4) * 4 + e;
-          if (tok < M && j < R) store_coherent(&tp[size_t(tok) * R + j], __float_as_uint(acc[t][c][e]));
-        }
-      }
   }
 
-  // Barrier of the producers.  The last to depart resets the counters (every
-  // producer has seen the full count by then).
-  __shared__ unsigned s_ok;
-  __shared__ float s_red[kThreads];
+  // Sum the eight waves' tiles in a fixed order; C holds tokens
+  // 4*(l/16)+e of token tile c, column lr of the block.  The block's result
+  // goes to LDS as [16*NT tokens][16 columns].
+  __syncthreads();  // every wave is done with its V tile
+  f32x4* red = reinterpret_cast<f32x4*>(smem);  // [kWaves][NT][kWave]
+  float* blk = reinterpret_cast<float*>(smem + kWaves * NT * kWave * 16);
+#pragma unroll
+  for (int c = 0; c < NT; ++c) red[(w * NT + c) * kWave + l] = acc[c];
+  __syncthreads();
+  if (w < NT) {
+    f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) sum += red[(v * NT + w) * kWave + l];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int tok = w * 16 + q4 * 4 + e;
+      blk[tok * 16 + lr] = tok < M ? sum[e] : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // With one k-slice the block is final.  Otherwise store this slice's
+  // partial; the last producer of the column block to arrive sums the KT
+  // partials in k-slice order.  Either way the final block is published in
+  // the operand type, two columns per 32-bit word, and counted in kDone.
+  const int Rp = a.NCB * 16;
+  __shared__ unsigned s_last;
+  bool last = true;
+  if (a.KT > 1) {
+    float* tp = a.tpart + size_t(kt) * (16 * NT) * Rp + cb * 16;
+    for (int i = tid; i < 16 * NT * 16; i += kThreads) store_coherent(&tp[(i / 16) * Rp + i % 16], __float_as_uint(blk[i]));
+    drain_stores();
+    __syncthreads();
+    if (tid == 0) s_last = add_coherent(&a.ctrl[kCbCounters + cb], 1u) == unsigned(a.KT - 1);
+    __syncthreads();
+    last = s_last;
+  }
+  if (!last) return;
+  for (int i = tid; i < 16 * NT * 8; i += kThreads) {  // word i: token i/8, columns 2*(i%8) and +1
+    const int tok = i / 8, col = 2 * (i % 8);
+    float v0 = 0.f, v1 = 0.f;
+    if (a.KT > 1) {
+      for (int k = 0; k < a.KT; ++k) {
+        const float* src = a.tpart + (size_t(k) * (16 * NT) + tok) * Rp + cb * 16 + col;
+        v0 += k == kt ? blk[tok * 16 + col] : __uint_as_float(load_coherent(src));
+        v1 += k == kt ? blk[tok * 16 + col + 1] : __uint_as_float(load_coherent(src + 1));
+      }
+    } else {
+      v0 = blk[tok * 16 + col];
+      v1 = blk[tok * 16 + col + 1];
+    }
+    if constexpr (sizeof(E) == 2) {
+      uint32_t* tf = static_cast<uint32_t*>(a.tfull);
+      store_coherent(&tf[(size_t(tok) * Rp + cb * 16 + col) / 2], uint32_t(f32_to_bf16(v0)) | (uint32_t(f32_to_bf16(v1)) << 16));
+    } else {
+      float* tf = static_cast<float*>(a.tfull);
+      store_coherent(&tf[size_t(tok) * Rp + cb * 16 + col], __float_as_uint(v0));
+      store_coherent(&tf[size_t(tok) * Rp + cb * 16 + col + 1], __float_as_uint(v1));
+    }
+  }
   drain_stores();
   __syncthreads();
   if (tid == 0) {
-    add_coherent(&a.ctrl[kArrive], 1u);
-    const bool ok = wait_for_count(&a.ctrl[kArrive], unsigned(a.NP));
-    if (!ok) atomicOr(&a.ctrl[kErr], 1u);
-    if (add_coherent(&a.ctrl[kDepart], 1u) == unsigned(a.NP - 1)) {
-      store_coherent(&a.ctrl[kArrive], 0u);
-      store_coherent(&a.ctrl[kDepart], 0u);
-    }
-    s_ok = ok;
-  }
-  __syncthreads();
-
-  // This producer's slice of T, published zero padded as [16*NT][Rp] in the
-  // operand type, two elements per 32-bit word.  `tpo` threads share one word:
-  // each sums a contiguous run of partials, then the runs are added in order.
-  const int Rp = (R + 31) / 32 * 32;
-  const int n_words = 16 * NT * Rp / 2;
-  const int w0_ = int(int64_t(p) * n_words / a.NP), w1_ = int(int64_t(p + 1) * n_words / a.NP);
-  const int nw = w1_ - w0_;
-  int tpo = 1;
-  while (tpo * 2 * nw <= kThreads && tpo * 2 <= a.NP) tpo *= 2;
-  const int per_pass = kThreads / tpo;
-  const int sub = tid % tpo, q0 = sub * a.NP / tpo, q1 = (sub + 1) * a.NP / tpo;
-  for (int wb = w0_; wb < w1_; wb += per_pass) {
-    const int word = wb + tid / tpo;
-    float part[2] = {0.f, 0.f};
-    if (word < w1_) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int idx = 2 * word + h, tok = idx / Rp, j = idx % Rp;
-        if (tok < M && j < R) {
-          const float* src = a.tpart + size_t(tok) * R + j;
-          int q = q0;
-          for (; q + 8 <= q1; q += 8) {
-            float v8[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) v8[u] = __uint_as_float(load_coherent(src + size_t(q + u) * n));
-#pragma unroll
-            for (int u = 0; u < 8; ++u) part[h] += v8[u];
-          }
-          for (; q < q1; ++q) part[h] += __uint_as_float(load_coherent(src + size_t(q) * n));
-        }
-      }
-    }
-    __syncthreads();
-    s_red[tid] = part[0];
-    __syncthreads();
-    float lo = 0.f;
-    if (sub == 0)
-      for (int k = 0; k < tpo; ++k) lo += s_red[tid + k];
-    __syncthreads();
-    s_red[tid] = part[1];
-    __syncthreads();
-    if (sub == 0 && word < w1_) {
-      float hi = 0.f;
-      for (int k = 0; k < tpo; ++k) hi += s_red[tid + k];
-      if (!s_ok) lo = hi = __builtin_nanf("");
-      uint32_t bits;
-      if constexpr (sizeof(E) == 2) {
-        bits = uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
-        store_coherent(reinterpret_cast<uint32_t*>(a.tfull) + word, bits);
-      } else {
-        store_coherent(reinterpret_cast<uint32_t*>(a.tfull) + 2 * word, __float_as_uint(lo));
-        store_coherent(reinterpret_cast<uint32_t*>(a.tfull) + 2 * word + 1, __float_as_uint(hi));
-      }
-    }
-  }
-  drain_stores();
-  __syncthreads();
-  if (tid == 0 && add_coherent(&a.ctrl[kPublished], 1u) == unsigned(a.NP - 1)) {
-    store_coherent(&a.ctrl[kPublished], 0u);
-    store_coherent(&a.ctrl[kFlag], a.epoch);
+    if (a.KT > 1) store_coherent(&a.ctrl[kCbCounters + cb], 0u);
+    add_coherent(&a.ctrl[kDone], 1u);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Consumer: output rows [c*16*RT, (c+1)*16*RT) over the whole of in_dim.
+// Streamers.
 // ---------------------------------------------------------------------------
-template <typename E, int NT, int RT, int UNR>
-__device__ void consume(const DecodeArgs& a, int c, f32x4* red) {
+// k32 steps in flight per wave: D steps of TILES W0 fragments and NT x
+// fragments take at most 64 VGPRs.
+template <typename E, int NT, int TILES> constexpr int pipe_depth() {
+  return 64 / ((TILES + NT) * frag_vgprs<E>()) > 0 ? 64 / ((TILES + NT) * frag_vgprs<E>()) : 1;
+}
+
+// T for token row `tok`, columns k..k+7 (published by the producers of this
+// launch): device-scope 32-bit loads.
+template <typename E>
+__device__ __forceinline__ Frag8<E> load_t(const DecodeArgs& a, int tok, int k) {
+  const uint32_t* q = static_cast<const uint32_t*>(a.tfull) + (size_t(tok) * (a.NCB * 16) + k) * sizeof(E) / 4;
+  Frag8<E> f;
+  if constexpr (sizeof(E) == 2) {
+    f.v = make_uint4(load_coherent(q), load_coherent(q + 1), load_coherent(q + 2), load_coherent(q + 3));
+  } else {
+    f.lo = make_float4(__uint_as_float(load_coherent(q)), __uint_as_float(load_coherent(q + 1)),
+                       __uint_as_float(load_coherent(q + 2)), __uint_as_float(load_coherent(q + 3)));
+    f.hi = make_float4(__uint_as_float(load_coherent(q + 4)), __uint_as_float(load_coherent(q + 5)),
+                       __uint_as_float(load_coherent(q + 6)), __uint_as_float(load_coherent(q + 7)));
+  }
+  return f;
+}
+
+template <typename E, int NT, int TILES>
+__device__ void stream_rows(const DecodeArgs& a, int b, uint8_t* smem) {
+  constexpr int D = pipe_depth<E, NT, TILES>();
+  constexpr int kPairs = TILES * NT;
   const E* X = static_cast<const E*>(a.x);
   const E* W0 = static_cast<const E*>(a.w0);
-  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
-  const int lr = l & 15, kq = (l >> 4) * 8;
-  const int M = a.M, I = a.I, R = a.R;
-  // Balanced contiguous row range [o_base, o_end) of this workgroup; the
-  // tiles' rows past o_end are masked.
-  const int o_base = int(int64_t(c) * a.O / a.NB), o_end = int(int64_t(c + 1) * a.O / a.NB);
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid / kWave), l = tid % kWave;
+  const int lr = l & 15, q4 = l >> 4, kq = q4 * 8;
+  const int M = a.M, I = a.I, R = a.R, KS = a.KS, RBR = a.RBR;
+  const int rb = b / KS, ks = b % KS;
+  const int r0 = int(int64_t(rb) * a.O / a.NRB), r1 = int(int64_t(rb + 1) * a.O / a.NRB);
+  const int nrows = r1 - r0;
+  const bool rank_unit = R > 0 && ks == KS - 1;
 
-  f32x4 acc[RT][NT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // LDS: the cross-wave reduction, then the row scale, then the block's
+  // result [16*NT][RBR].
+  f32x4* red = reinterpret_cast<f32x4*>(smem);
+  float* sbuf = reinterpret_cast<float*>(smem + kWaves * 4 * kWave * 16);
+  float* res = sbuf + 16 * TILES;
 
-  for (int st = w; st < a.S; st += kWaves * UNR) {
-    Frag8<E> fa[UNR][RT], fb[UNR][NT];
+  // The row scale, fetched now and used after the stream.
+  const E* S_ = static_cast<const E*>(a.s);
+  const float s_mine = tid < nrows ? to_f32<E>(S_[r0 + tid]) : 0.f;
+
+  // Byte offsets, from the block's first row, of the row of each tile this
+  // lane loads, clamped into the block (rows past it are computed on
+  // duplicate data and never stored); likewise for the token rows of x.  The
+  // bases are uniform, so the loads take scalar base + 32-bit vector offset.
+  const char* wbase = reinterpret_cast<const char*>(W0 + size_t(r0) * I);
+  const char* xbase = reinterpret_cast<const char*>(X);
+  uint32_t woff[TILES], xoff[NT];
 #pragma unroll
-    for (int uu = 0; uu < UNR; ++uu) {
-      const int step = st + kWaves * uu;
-      const int k = step * 32 + kq;
-      const bool kv = step < a.S && k < I;
+  for (int t = 0; t < TILES; ++t) woff[t] = uint32_t(min(t * 16 + lr, nrows - 1)) * uint32_t(I) * sizeof(E);
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int row = o_base + rt * 16 + lr;
-        fa[uu][rt] = load_frag_if<E>(W0 + size_t(row) * I + k, kv && row < o_end);
-      }
+  for (int c = 0; c < NT; ++c) xoff[c] = uint32_t(min(c * 16 + lr, M - 1)) * uint32_t(I) * sizeof(E);
+
+  // U for this wave's first k32 step of the rank, fetched before the stream
+  // when it fits the register budget (else after it).
+  constexpr bool kPrefetchU = TILES * frag_vgprs<E>() <= 16;
+  const int RS = (R + 31) / 32;
+  const bool ualigned = (R % 8) == 0;
+  const E* Ub = static_cast<const E*>(a.u) + size_t(r0) * R;
+  Frag8<E> uf[TILES];
+  if (kPrefetchU && rank_unit && w < RS) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int tok = t * 16 + lr;
-        fb[uu][t] = load_frag_if<E>(X + size_t(tok) * I + k, kv && tok < M);
-      }
-    }
-#pragma unroll
-    for (int uu = 0; uu < UNR; ++uu)
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[rt][t] = mma_k32(fa[uu][rt], fb[uu][t], acc[rt][t]);
+    for (int t = 0; t < TILES; ++t) uf[t] = load_row8<E>(Ub + size_t(min(t * 16 + lr, nrows - 1)) * R, w * 32 + kq, R, ualigned);
   }
 
-  // Fixed-order reduction over the eight waves; wave q < RT*NT keeps tile q.
+  f32x4 acc[TILES][NT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+  for (int t = 0; t < TILES; ++t)
 #pragma unroll
-    for (int t = 0; t < NT; ++t) red[((w * RT + rt) * NT + t) * kWave + l] = acc[rt][t];
+    for (int c = 0; c < NT; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mma_step = [&](const Frag8<E> (&fw)[TILES], const Frag8<E> (&fx)[NT]) {
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+      for (int c = 0; c < NT; ++c) acc[t][c] = mma_k32(fw[t], fx[c], acc[t][c]);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_operand_guard();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Full k32 steps sa + w, sa + w + 8, ... of this k-slice: n of them for
+  // this wave, in a software pipeline D steps deep.  The loop body is
+  // straight-line code: loads are unconditional (step indexes clamped into
+  // the slice, so refills past a wave's last step re-read it and go unused),
+  // and every wave runs the same whole rounds (those of wave 0, which has the
+  // most steps) and meets the others at a barrier after each: left alone the
+  // waves drift apart by many microseconds and the stragglers finish with
+  // few loads in flight.  The remainder after whole rounds is consumed after
+  // the loop.
+  const int s_full = I / 32;
+  const int sa = int(int64_t(ks) * s_full / KS), sb = int(int64_t(ks + 1) * s_full / KS);
+  const int n = sb - sa > w ? (sb - sa - w + kWaves - 1) / kWaves : 0;
+  const int n0 = (sb - sa + kWaves - 1) / kWaves;  // wave 0's steps, the most
+  if (n0 > 0) {
+    Frag8<E> wf[D][TILES], xf[D][NT];
+#define TB_ISSUE(SLOT, IDX)                                                                               \
+    do {                                                                                                  \
+      const uint32_t kb_ = uint32_t(min(sa + w + (IDX) * kWaves, sb - 1) * 32 + kq) * sizeof(E);          \
+      _Pragma("unroll") for (int t = 0; t < TILES; ++t)                                                   \
+        wf[SLOT][t] = load_frag<E>(reinterpret_cast<const E*>(wbase + (woff[t] + kb_)));                  \
+      _Pragma("unroll") for (int c = 0; c < NT; ++c)                                                      \
+        xf[SLOT][c] = load_frag<E>(reinterpret_cast<const E*>(xbase + (xoff[c] + kb_)));                  \
+    } while (0)
+#pragma unroll
+    for (int d = 0; d < D; ++d) TB_ISSUE(d, d);
+    const int whole = n0 / D * D;
+    for (int i0 = 0; i0 < whole; i0 += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        if (i0 + d < n) mma_step(wf[d], xf[d]);
+        TB_ISSUE(d, i0 + d + D);
+        // Keep each slot's refill right behind its use: clustering the
+        // refills at the end of the round would drain the pipeline.
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_barrier();
+    }
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d)
+      if (whole + d < n) mma_step(wf[d], xf[d]);
+#undef TB_ISSUE
+  }
+  // The partial last step (in_dim not a multiple of 32), masked per lane.
+  if (s_full * 32 < I && ks == KS - 1 && w == 0) {
+    const int k = s_full * 32 + kq;
+    const bool kv = k < I;
+    const uint32_t kb = uint32_t(kv ? k : I - 8) * sizeof(E);
+    Frag8<E> fw[TILES], fx[NT];
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) fw[t] = load_frag_if<E>(reinterpret_cast<const E*>(wbase + (woff[t] + kb)), kv);
+#pragma unroll
+    for (int c = 0; c < NT; ++c) fx[c] = load_frag_if<E>(reinterpret_cast<const E*>(xbase + (xoff[c] + kb)), kv);
+    mma_step(fw, fx);
+  }
+
+  // Row scale: C rows 4*(l/16)+e of each tile.
+  if (tid < nrows) sbuf[tid] = s_mine;
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < TILES; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = t * 16 + q4 * 4 + e;
+      const float sc = row < nrows ? sbuf[row] : 0.f;
+#pragma unroll
+      for (int c = 0; c < NT; ++c) acc[t][c][e] *= sc;
+    }
+
+  // The rank-r delta: this wave's k32 steps of T . U^T, once T is complete.
+  if (rank_unit) {
+    const bool ok = wait_for_count(&a.ctrl[kDone], unsigned(a.NCB));
+    if (!ok && l == 0) atomicOr(&a.ctrl[kErr], 1u);
+    for (int rs = w; rs < RS; rs += kWaves) {
+      if (rs != w || !kPrefetchU) {
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+          uf[t] = load_row8<E>(Ub + size_t(min(t * 16 + lr, nrows - 1)) * R, rs * 32 + kq, R, ualigned);
+      }
+      Frag8<E> ft[NT];
+#pragma unroll
+      for (int c = 0; c < NT; ++c) ft[c] = load_t<E>(a, c * 16 + lr, rs * 32 + kq);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < TILES; ++t)
+#pragma unroll
+        for (int c = 0; c < NT; ++c) acc[t][c] = mma_k32(uf[t], ft[c], acc[t][c]);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_operand_guard();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (!ok) {
+      const float nan = __builtin_nanf("");
+#pragma unroll
+      for (int t = 0; t < TILES; ++t)
+#pragma unroll
+        for (int c = 0; c < NT; ++c) acc[t][c] = f32x4{nan, nan, nan, nan};
+    }
+  }
+
+  // Sum the eight waves' partials in a fixed order, four (tile, token tile)
+  // pairs per round, into the block's result.
+#pragma unroll
+  for (int p0 = 0; p0 < kPairs; p0 += 4) {
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (p0 + q < kPairs) red[(w * 4 + q) * kWave + l] = acc[(p0 + q) / NT][(p0 + q) % NT];
+    __syncthreads();
+    if (w < 4 && p0 + w < kPairs) {
+      f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) sum += red[(v * 4 + w) * kWave + l];
+      const int t = (p0 + w) / NT, c = (p0 + w) % NT;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) res[(c * 16 + lr) * RBR + t * 16 + q4 * 4 + e] = sum[e];
+    }
+  }
   __syncthreads();
 
-  const bool mine = w < RT * NT;
-  const int rt = mine ? w / NT : 0, t = mine ? w % NT : 0;
-  f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (mine) {
-#pragma unroll
-    for (int q = 0; q < kWaves; ++q) sum += red[((q * RT + rt) * NT + t) * kWave + l];
-  }
-
-  // Epilogue: row scale, then the rank-r delta, then one rounding.
-  const E* S_ = static_cast<const E*>(a.s);
-  const int orow0 = o_base + rt * 16 + (l >> 4) * 4;
-  const int tok = t * 16 + lr;
-  if (mine) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sum[e] *= (orow0 + e < o_end) ? to_f32<E>(S_[orow0 + e]) : 0.f;
-  }
-
-  bool ok = true;
-  if (R > 0) {
-    __shared__ unsigned s_ok;
-    if (tid == 0) {
-      const bool got = wait_for_epoch(&a.ctrl[kFlag], a.epoch);
-      if (!got) atomicOr(&a.ctrl[kErr], 1u);
-      s_ok = got;
-    }
-    __syncthreads();
-    ok = s_ok;
-    if (mine) {
-      const E* U = static_cast<const E*>(a.u);
-      const E* T = reinterpret_cast<const E*>(a.tfull);
-      const int urow = o_base + rt * 16 + lr;
-      const int Rp = (R + 31) / 32 * 32;
-      const bool aligned = (R % 8) == 0;
-      constexpr int kEpi = 4;  // k32 steps of the rank tail whose loads are in flight together
-      for (int kb = 0; kb < R; kb += 32 * kEpi) {
-        Frag8<E> fu[kEpi], ft[kEpi];
-#pragma unroll
-        for (int q = 0; q < kEpi; ++q) {
-          const int j = kb + 32 * q + kq;
-          fu[q] = zero_frag<E>();
-          ft[q] = zero_frag<E>();
-          if (j < Rp) ft[q] = load_t_frag<E>(T + size_t(tok) * Rp + j);
-          if (urow < o_end && j < R)
-            fu[q] = aligned ? load_frag<E>(U + size_t(urow) * R + j) : load_frag_partial<E>(U + size_t(urow) * R + j, min(8, R - j));
-        }
-#pragma unroll
-        for (int q = 0; q < kEpi; ++q) sum = mma_k32(fu[q], ft[q], sum);
-      }
-    }
-  }
-  if (!mine) return;
-  if (!ok) sum = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-
+  // Store y, or this k-slice's partial (the last of the row block to arrive
+  // sums all KS partials in k-slice order).
   E* Y = static_cast<E*>(a.y);
-  if (tok < M) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (orow0 + e < o_end) Y[size_t(tok) * a.O + orow0 + e] = from_f32<E>(sum[e]);
-  }
-}
-
-template <typename E, int NT, int RT>
-__global__ __launch_bounds__(kThreads) void forward_decode_kernel(DecodeArgs a) {
-  constexpr int kConsumerLds = kWaves * RT * NT * kWave * 16;
-  constexpr int kProducerLds = kVCols * kVPitch * int(sizeof(E));
-  constexpr int kLds = kConsumerLds > kProducerLds ? kConsumerLds : kProducerLds;
-  __shared__ float4 smem[kLds / 16];
-  if (int(blockIdx.x) < a.NP) {
-    produce_xv<E, NT>(a, int(blockIdx.x), smem);
+  const int nel = M * nrows;
+  if (KS == 1) {
+    for (int i = tid; i < nel; i += kThreads) {
+      const int tok = i / nrows, row = i % nrows;
+      Y[size_t(tok) * a.O + r0 + row] = from_f32<E>(res[tok * RBR + row]);
+    }
   } else {
-    constexpr int UNR = per_tile_budget(sizeof(E) == 2 ? 4 : 2, NT);
-    consume<E, NT, RT, UNR>(a, int(blockIdx.x) - a.NP, reinterpret_cast<f32x4*>(smem));
+    __shared__ unsigned s_last;
+    float* mine = a.ypart + (size_t(rb) * KS + ks) * (16 * NT) * RBR;
+    for (int i = tid; i < nel; i += kThreads) {
+      const int tok = i / nrows, row = i % nrows;
+      store_coherent(&mine[tok * RBR + row], __float_as_uint(res[tok * RBR + row]));
+    }
+    drain_stores();
+    __syncthreads();
+    if (tid == 0) s_last = add_coherent(&a.ctrl[kRbCounters + rb], 1u) == unsigned(KS - 1);
+    __syncthreads();
+    if (s_last) {
+      const float* blk = a.ypart + size_t(rb) * KS * (16 * NT) * RBR;
+      for (int i = tid; i < nel; i += kThreads) {
+        const int tok = i / nrows, row = i % nrows;
+        float sum = 0.f;
+        for (int k = 0; k < KS; ++k)
+          sum += k == ks ? res[tok * RBR + row]
+                         : __uint_as_float(load_coherent(&blk[(size_t(k) * (16 * NT) + tok) * RBR + row]));
+        Y[size_t(tok) * a.O + r0 + row] = from_f32<E>(sum);
+      }
+      if (tid == 0) store_coherent(&a.ctrl[kRbCounters + rb], 0u);
+    }
+  }
+
+  // The last rank streamer past its read of T resets the producers' count.
+  if (rank_unit && tid == 0 && add_coherent(&a.ctrl[kFinish], 1u) == unsigned(a.NRB - 1)) {
+    store_coherent(&a.ctrl[kDone], 0u);
+    store_coherent(&a.ctrl[kFinish], 0u);
   }
 }
 
-template <typename E, int NT, int RT>
-hipError_t launch_t(const DecodeArgs& a, int blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((forward_decode_kernel<E, NT, RT>), dim3(blocks), dim3(kThreads), 0, stream, a);
+constexpr int kReduceBytes = kWaves * 4 * kWave * 16;  // the streamers' cross-wave reduction
+
+template <int NT, int TILES>
+constexpr int smem_bytes() {
+  return kReduceBytes + int(sizeof(float)) * (16 * TILES + 16 * NT * 16 * TILES);
+}
+
+template <typename E, int NT, int TILES>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void decode_kernel(DecodeArgs a) {
+  static_assert(kWaves * 16 * kVtPitch * sizeof(E) <= kReduceBytes, "the producers' V tiles fit");
+  static_assert(kWaves * NT * kWave * 16 + 16 * NT * 16 * 4 <= smem_bytes<NT, TILES>(), "the producers' reduction fits");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<NT, TILES>()];
+  const int b = int(blockIdx.x), np = a.NCB * a.KT;
+  if (b < np) produce_t<E, NT>(a, b, smem);
+  else stream_rows<E, NT, TILES>(a, b - np, smem);
+}
+
+template <typename E, int NT, int TILES>
+hipError_t launch_t(const DecodePlan& p, const DecodeArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_kernel<E, NT, TILES>), dim3(p.NP + p.NB), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 template <typename E>
 hipError_t launch_e(const DecodePlan& p, const DecodeArgs& a, hipStream_t stream) {
-  const int blocks = p.NP + p.NG;
   if (p.NT == 1) {
-    switch (p.RT) {
-      case 4: return launch_t<E, 1, 4>(a, blocks, stream);
-      case 3: return launch_t<E, 1, 3>(a, blocks, stream);
-      case 2: return launch_t<E, 1, 2>(a, blocks, stream);
-      default: return launch_t<E, 1, 1>(a, blocks, stream);
+    switch (p.TILES) {
+      case 1: return launch_t<E, 1, 1>(p, a, stream);
+      case 2: return launch_t<E, 1, 2>(p, a, stream);
+      case 4: return launch_t<E, 1, 4>(p, a, stream);
+      default: return launch_t<E, 1, 6>(p, a, stream);
     }
   }
   if (p.NT == 2) {
-    if (p.RT == 2) return launch_t<E, 2, 2>(a, blocks, stream);
-    return launch_t<E, 2, 1>(a, blocks, stream);
+    switch (p.TILES) {
+      case 1: return launch_t<E, 2, 1>(p, a, stream);
+      case 2: return launch_t<E, 2, 2>(p, a, stream);
+      default: return launch_t<E, 2, 4>(p, a, stream);
+    }
   }
-  return launch_t<E, 4, 1>(a, blocks, stream);
+  return p.TILES == 1 ? launch_t<E, 4, 1>(p, a, stream) : launch_t<E, 4, 2>(p, a, stream);
 }
 
 }  // namespace
@@ -448,47 +533,72 @@ hipError_t launch_e(const DecodePlan& p, const DecodeArgs& a, hipStream_t stream
 DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus) {
   DecodePlan p{};
   p.NT = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
-  p.S = int((in_dim + 31) / 32);
-  // Consumers: a multiple of the compute-unit count, each with a balanced row
-  // range of at most 16 * (4 / NT) rows; RT tiles cover the widest range.
-  const int64_t max_rows = 16 * (4 / p.NT);
-  int64_t nb = cus;
-  while ((out_dim + nb - 1) / nb > max_rows) nb += cus;
-  if (nb > out_dim) nb = out_dim;
-  p.NG = int(nb);
-  const int64_t rows = (out_dim + nb - 1) / nb;
-  p.RT = int((rows + 15) / 16);
-  if (rank > 0) {
-    int np = (p.S + kStepsPerProducer - 1) / kStepsPerProducer;
-    const int cap = cus < kMaxProducers ? cus : kMaxProducers;
-    if (np > cap) np = cap;
-    if (np < 1) np = 1;
-    p.NP = np;
+  const int64_t max_rows = 16 * (p.NT == 1 ? 6 : (p.NT == 2 ? 4 : 2));
+  const int64_t s_full = in_dim / 32;
+  // Streamers.  Every streamer of a row block reads all of x for its k-slice,
+  // so the x traffic grows with the number of row blocks: use as few blocks
+  // as the widest tile set allows and split in_dim so that there is about one
+  // streamer per compute unit (each wave keeping at least four k32 steps).
+  const int64_t nrb_min = (out_dim + max_rows - 1) / max_rows;
+  int64_t ks = 1, nrb;
+  if (nrb_min >= cus) {
+    nrb = cus;
+    while ((out_dim + nrb - 1) / nrb > max_rows) nrb += cus;
   } else {
-    p.NP = 0;
+    ks = cus / nrb_min;
+    const int64_t ks_cap = s_full / 32 > 1 ? s_full / 32 : 1;
+    if (ks > ks_cap) ks = ks_cap;
+    if (ks > 16) ks = 16;
+    nrb = cus / ks;
+    if (nrb < nrb_min) nrb = nrb_min;
   }
-  const size_t rp = size_t((rank + 31) / 32 * 32);
+  if (nrb > out_dim) nrb = out_dim;
+  if (ks > 1 && nrb > kMaxGroupCounters / 2) ks = 1;  // one arrival counter per row block
+  const int64_t tiles = ((out_dim + nrb - 1) / nrb + 15) / 16;
+  p.TILES = tiles <= 1 ? 1 : (tiles <= 2 ? 2 : (tiles <= 4 ? 4 : 6));
+  p.NRB = int(nrb);
+  p.KS = int(ks);
+  p.NB = p.NRB * p.KS;
+  // Producers: 16 columns of T each, over k-slices of about 1024 of in_dim
+  // (four k32 steps per wave: one round of loads).
+  if (rank > 0) {
+    const int64_t rp = (rank + 31) / 32 * 32;
+    p.NCB = int(rp / 16);
+    int64_t kt = (in_dim + 1023) / 1024;
+    if (kt > 16) kt = 16;
+    if (p.NCB > kMaxGroupCounters / 2) kt = 1;  // one arrival counter per column block
+    p.KT = int(kt);
+  } else {
+    p.NCB = 0;
+    p.KT = 1;
+  }
+  p.NP = p.NCB * p.KT;
+  const size_t rows16 = size_t(16 * p.NT);
+  const size_t rbr = size_t(16 * p.TILES);
   size_t off = kControlBytes;
-  p.off_tpart = off;  // NP partials of [m][rank] fp32
-  off = align_up(off + size_t(p.NP) * size_t(m) * size_t(rank) * 4, 256);
-  p.off_tfull = off;  // T, [16*NT][rp], fp32 or bf16
-  off = align_up(off + size_t(16 * p.NT) * rp * 4, 256);
+  p.off_tpart = off;  // [KT][16*NT][Rp] fp32 (KT > 1)
+  off = align_up(off + (p.KT > 1 ? size_t(p.KT) * rows16 * size_t(p.NCB) * 16 * 4 : 0), 256);
+  p.off_tfull = off;  // [16*NT][Rp], fp32 or bf16
+  off = align_up(off + rows16 * size_t(p.NCB) * 16 * 4, 256);
+  p.off_ypart = off;  // [NRB][KS][16*NT][RBR] fp32
+  off = align_up(off + (p.KS > 1 ? size_t(p.NRB) * size_t(p.KS) * rows16 * rbr * 4 : 0), 256);
   p.bytes = off;
   return p;
 }
 
 hipError_t launch_forward_decode(const DecodePlan& p, tb_dtype dtype, const void* x, const void* s, const void* w0,
                                  const void* u, const void* v, void* y, int64_t m, int64_t out_dim, int64_t in_dim,
-                                 int64_t rank, void* workspace, unsigned epoch, hipStream_t stream) {
+                                 int64_t rank, void* workspace, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   DecodeArgs a;
   a.x = x; a.s = s; a.w0 = w0; a.u = u; a.v = v; a.y = y;
   a.M = int(m); a.O = int(out_dim); a.I = int(in_dim); a.R = int(rank);
-  a.S = p.S; a.NP = p.NP; a.NB = p.NG;
-  a.epoch = epoch;
+  a.NCB = p.NCB; a.KT = p.KT;
+  a.NRB = p.NRB; a.KS = p.KS; a.RBR = 16 * p.TILES;
   a.ctrl = reinterpret_cast<unsigned*>(ws);
   a.tpart = reinterpret_cast<float*>(ws + p.off_tpart);
-  a.tfull = reinterpret_cast<float*>(ws + p.off_tfull);
+  a.tfull = ws + p.off_tfull;
+  a.ypart = reinterpret_cast<float*>(ws + p.off_ypart);
   if (dtype == TB_BF16) return launch_e<bf16_t>(p, a, stream);
   return launch_e<float>(p, a, stream);
 }

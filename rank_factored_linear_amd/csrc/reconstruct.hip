@@ -73,6 +73,9 @@ __global__ __launch_bounds__(kThreads) void reconstruct_lowrank_kernel(const EI*
       if (vrow < I && j < R)
         fb = aligned ? load_frag<EI>(v + size_t(vrow) * R + j) : load_frag_partial<EI>(v + size_t(vrow) * R + j, min(8, R - j));
       acc[ct] = mma_k32(fa, fb, acc[ct]);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_operand_guard();
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 #pragma unroll

@@ -10,7 +10,7 @@
 namespace tb {
 
 constexpr size_t kControlBytes = TB_WORKSPACE_CONTROL_BYTES;
-constexpr int kMaxGroupCounters = int((kControlBytes - 256) / 4);
+constexpr int kMaxGroupCounters = int(kControlBytes / 4) - 64;  // words 64.. of the control region
 
 // Compute units of the current device (queried once per device).
 int device_cu_count(int* cus);
@@ -21,22 +21,20 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 constexpr int kDecodeMaxTokens = 64;
 
 struct DecodePlan {
-  int NT;   // 16-token column tiles (1, 2 or 4)
-  int RT;   // 16-row output tiles per consumer workgroup (1, 2 or 4)
-  int NG;   // consumer workgroups
-  int S;    // k32 steps over in_dim
-  int NP;   // producer workgroups computing x . V
-  size_t off_tpart, off_tfull, bytes;
+  int NT;        // 16-token column tiles (1, 2 or 4)
+  int TILES;     // 16-row tiles each streaming workgroup is built for (1, 2, 4 or 6)
+  int NRB, KS;   // streaming row blocks and k-slices of in_dim
+  int NB;        // streaming workgroups (NRB * KS)
+  int NCB, KT;   // x . V producers: 16-column blocks of T and k-slices of in_dim
+  int NP;        // producer workgroups (NCB * KT)
+  size_t off_tpart, off_tfull, off_ypart, bytes;
 };
 
 DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus);
 
 hipError_t launch_forward_decode(const DecodePlan& p, tb_dtype dtype, const void* x, const void* s, const void* w0,
                                  const void* u, const void* v, void* y, int64_t m, int64_t out_dim, int64_t in_dim,
-                                 int64_t rank, void* workspace, unsigned epoch, hipStream_t stream);
-
-// A fresh nonzero value per launch that publishes through a workspace flag.
-unsigned next_epoch();
+                                 int64_t rank, void* workspace, hipStream_t stream);
 
 // ---- forward, prefill token counts (bf16, m > kDecodeMaxTokens) ----------
 struct GemmPlan {
