@@ -110,6 +110,7 @@ __device__ __forceinline__ Frag8<E> load_row8(const E* row, int k, int R, bool a
 // Producers.
 // ---------------------------------------------------------------------------
 constexpr int kVtPitch = 40;  // elements per column of a wave's transposed 16 x 32 V tile
+constexpr int kMaxKT = 16;    // k-slices of the producers at most
 
 template <typename E, int NT>
 __device__ void produce_t(const DecodeArgs& a, int p, uint8_t* smem) {
@@ -210,11 +211,22 @@ __device__ void produce_t(const DecodeArgs& a, int p, uint8_t* smem) {
     const int tok = i / 8, col = 2 * (i % 8);
     float v0 = 0.f, v1 = 0.f;
     if (a.KT > 1) {
-      for (int k = 0; k < a.KT; ++k) {
+      // All partials are fetched at once (one round trip), then summed in
+      // k-slice order.
+      float p0[kMaxKT], p1[kMaxKT];
+#pragma unroll
+      for (int k = 0; k < kMaxKT; ++k) {
         const float* src = a.tpart + (size_t(k) * (16 * NT) + tok) * Rp + cb * 16 + col;
-        v0 += k == kt ? blk[tok * 16 + col] : __uint_as_float(load_coherent(src));
-        v1 += k == kt ? blk[tok * 16 + col + 1] : __uint_as_float(load_coherent(src + 1));
+        const bool other = k < a.KT && k != kt;
+        p0[k] = other ? __uint_as_float(load_coherent(src)) : blk[tok * 16 + col];
+        p1[k] = other ? __uint_as_float(load_coherent(src + 1)) : blk[tok * 16 + col + 1];
       }
+#pragma unroll
+      for (int k = 0; k < kMaxKT; ++k)
+        if (k < a.KT) {
+          v0 += p0[k];
+          v1 += p1[k];
+        }
     } else {
       v0 = blk[tok * 16 + col];
       v1 = blk[tok * 16 + col + 1];
@@ -565,7 +577,7 @@ DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
     const int64_t rp = (rank + 31) / 32 * 32;
     p.NCB = int(rp / 16);
     int64_t kt = (in_dim + 1023) / 1024;
-    if (kt > 16) kt = 16;
+    if (kt > kMaxKT) kt = kMaxKT;
     if (p.NCB > kMaxGroupCounters / 2) kt = 1;  // one arrival counter per column block
     p.KT = int(kt);
   } else {
