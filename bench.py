@@ -54,7 +54,25 @@ def parse():
     ap.add_argument("--bands", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the oracle timing")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain device copies of a known size (scales the HBM byte counters)")
     return ap.parse_args()
+
+
+COPY_BYTES = 512 << 20
+
+
+def copy_calibration():
+    """Plain 512 MiB device-to-device copies: what the FETCH_SIZE / WRITE_SIZE counters read for them
+    against the bytes actually moved gives the scale applied to the projection kernel's counters."""
+    import torch
+    torch.cuda.set_device(0)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES, "copies": 4}), flush=True)
 
 
 def call_bytes(M, O, I, R, e=2):
@@ -91,6 +109,9 @@ def counter_traffic(kernel, workload_tag):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is not sharded across GPUs",
               file=sys.stderr)
@@ -205,7 +226,7 @@ def main():
         unit = "GB/s"
         value = step_bytes / (ms * 1e-3) / 1e9
         achieved = launch_bytes.sum() / (per_call_ms.sum() * 1e-3) / 1e9
-        kernel = "forward_decode_kernel<bf16,%d,RT>" % (1 if M <= 16 else (2 if M <= 32 else 4))
+        kernel = "decode_kernel<bf16,%d,*>" % (1 if M <= 16 else (2 if M <= 32 else 4))
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
         per_launch = float(launch_bytes.mean())

@@ -96,9 +96,11 @@ tb_status tb_linear_forward_workspace_size(int64_t m, int64_t out_dim, int64_t i
  *   y  [m, out_dim]       output                   (dtype), written, must not alias inputs
  *   m >= 1 tokens, out_dim >= 1, in_dim >= 8 and % 8 == 0, rank >= 0.
  *   Arithmetic: products and sums in fp32 (bf16 inputs are exact in fp32);
- *   the scale is applied to the fp32 sum before the delta is added; for bf16
- *   the intermediate x . V is rounded to bf16 before it meets U.  y is
- *   rounded once at the end.  Results are deterministic run to run.
+ *   the scale multiplies fp32 sums of x . W0^T before the delta is added; for
+ *   bf16 the intermediate x . V is rounded to bf16 before it meets U.  y is
+ *   rounded once at the end.  Results are deterministic run to run.  For
+ *   m <= 64, in_dim * element size * 96 must stay below 2^32 (else
+ *   TB_ERR_UNSUPPORTED).
  *   workspace: device buffer of at least tb_linear_forward_workspace_size()
  *   bytes, 256-byte aligned.  Its first TB_WORKSPACE_CONTROL_BYTES bytes are
  *   control words: they must be zero before the first call that uses the
@@ -137,7 +139,7 @@ tb_status tb_reconstruct_weight(const void *s, const void *w0, const void *u, co
  *   squares and sums are taken in fp64 in a fixed order (deterministic).
  *   When the difference is zero the result is 0; when only the original is
  *   zero it is +inf.  workspace: >= TB_FROBENIUS_WORKSPACE_BYTES device bytes,
- *   8-byte aligned (no zeroing needed).  Errors as above.
+ *   16-byte aligned (no zeroing needed).  Errors as above.
  */
 tb_status tb_rel_frobenius_error(const void *original, const void *reconstructed, int64_t rows, int64_t cols,
                                  tb_dtype dtype, double *result_device, void *workspace,

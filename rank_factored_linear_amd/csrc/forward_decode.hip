@@ -9,10 +9,11 @@
 // them ahead of any streaming workgroup; producers never wait, so the
 // streamers' waits on them always end.
 //
-//   producers (rank > 0): T = x . V.  Producer (kt, cb) owns the 16 columns
-//     [16cb, 16cb+16) of T over the k-slice kt of in_dim: no exchange with
-//     other producers.  Its waves take k32 steps round-robin, each loading a
-//     32 x 16 block of V (transposed through a wave-private LDS tile) and the
+//   producers (rank > 0): T = x . V.  Producer (kt, cb) owns the 64 columns
+//     [64cb, 64cb+64) of T over the k-slice kt of in_dim: no exchange with
+//     other producers until the end.  Its waves take k32 steps round-robin,
+//     each loading a 32 x 64 block of V in whole 128-byte row segments
+//     (transposed through a wave-private LDS tile) and the
 //     x fragments, and multiply on the matrix cores; the eight partials are
 //     summed in LDS in a fixed order.  With several k-slices each producer
 //     stores its fp32 partial and the last of the column block to arrive sums
@@ -109,13 +110,28 @@ __device__ __forceinline__ Frag8<E> load_row8(const E* row, int k, int R, bool a
 // ---------------------------------------------------------------------------
 // Producers.
 // ---------------------------------------------------------------------------
-constexpr int kVtPitch = 40;  // elements per column of a wave's transposed 16 x 32 V tile
+constexpr int kVtPitch = 40;  // elements per column of a wave's transposed 64 x 32 V tile
 constexpr int kMaxKT = 16;    // k-slices of the producers at most
+constexpr int kCbCols = 64;   // columns of T per producer: 128 contiguous bytes of a bf16 row of V
+
+// k32 steps in flight per producer wave (registers: 4 V pieces and NT x
+// fragments per step).
+template <typename E, int NT> constexpr int producer_depth() {
+  return sizeof(E) == 2 ? (NT == 1 ? 3 : (NT == 2 ? 2 : 1)) : 1;
+}
+
+template <typename E, int NT>
+constexpr int producer_smem() {
+  using Raw = typename std::conditional<sizeof(E) == 2, uint16_t, float>::type;
+  constexpr int tiles = kWaves * kCbCols * kVtPitch * int(sizeof(Raw));
+  constexpr int reduce = kWaves * NT * kWave * 16 + 16 * NT * kCbCols * 4;
+  return tiles > reduce ? tiles : reduce;
+}
 
 template <typename E, int NT>
 __device__ void produce_t(const DecodeArgs& a, int p, uint8_t* smem) {
   using Raw = typename std::conditional<sizeof(E) == 2, uint16_t, float>::type;
-  constexpr int D = 8 / (1 + NT) > 0 ? 8 / (1 + NT) : 1;  // k32 steps in flight per wave
+  constexpr int D = producer_depth<E, NT>();
   const E* X = static_cast<const E*>(a.x);
   const E* V = static_cast<const E*>(a.v);
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid / kWave), l = tid % kWave;
@@ -126,19 +142,27 @@ __device__ void produce_t(const DecodeArgs& a, int p, uint8_t* smem) {
   const int s0 = int(int64_t(kt) * S / a.KT), s1 = int(int64_t(kt + 1) * S / a.KT);
   const int n = s1 - s0 > w ? (s1 - s0 - w + kWaves - 1) / kWaves : 0;
   const bool valigned = (R % 8) == 0;
-  // This lane's piece of a 32 x 16 block of V: row l/2, columns 8*(l%2)..+7.
-  const int vr = l >> 1, vc = cb * 16 + (l & 1) * 8;
-  Raw* vt = reinterpret_cast<Raw*>(smem) + w * (16 * kVtPitch);  // [16 cols][kVtPitch], this wave's
+  // A step's 32 x 64 block of V is four loads per lane: load q covers rows
+  // 8q .. 8q+7 with lane l taking row 8q + l/8, columns 8*(l%8) .. +7, so
+  // each load reads whole 128-byte row segments.
+  const int vr = l >> 3, vc = cb * kCbCols + (l & 7) * 8;
+  Raw* vt = reinterpret_cast<Raw*>(smem) + w * (kCbCols * kVtPitch);  // [64 cols][kVtPitch], this wave's
 
-  f32x4 acc[NT];
+  f32x4 acc[4][NT];
 #pragma unroll
-  for (int c = 0; c < NT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int c = 0; c < NT; ++c) acc[j][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (n > 0) {
-    Frag8<E> vf[D], xf[D][NT];
-    auto issue = [&](Frag8<E>& fv, Frag8<E> (&fx)[NT], int i) {
+    Frag8<E> vf[D][4], xf[D][NT];
+    auto issue = [&](Frag8<E> (&fv)[4], Frag8<E> (&fx)[NT], int i) {
       const int k0 = (s0 + w + i * kWaves) * 32;
-      fv = k0 + vr < I ? load_row8<E>(V + size_t(k0 + vr) * R, vc, R, valigned) : zero_frag<E>();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = k0 + 8 * q + vr;
+        fv[q] = row < I ? load_row8<E>(V + size_t(row) * R, vc, R, valigned) : zero_frag<E>();
+      }
       const bool kv = k0 + kq < I;
 #pragma unroll
       for (int c = 0; c < NT; ++c)
@@ -150,16 +174,24 @@ __device__ void produce_t(const DecodeArgs& a, int p, uint8_t* smem) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         if (i0 + d < n) {
-          // Transpose the V piece through the wave's LDS tile: column j of the
-          // block holds k = 0..31 contiguously.
-          Raw vals[8];
-          __builtin_memcpy(vals, &vf[d], sizeof(vals));
+          // Transpose the block through the wave's LDS tile: column j holds
+          // k = 0..31 contiguously.
 #pragma unroll
-          for (int e = 0; e < 8; ++e) vt[((l & 1) * 8 + e) * kVtPitch + vr] = vals[e];
+          for (int q = 0; q < 4; ++q) {
+            Raw vals[8];
+            __builtin_memcpy(vals, &vf[d][q], sizeof(vals));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vt[((l & 7) * 8 + e) * kVtPitch + 8 * q + vr] = vals[e];
+          }
           __builtin_amdgcn_wave_barrier();
-          const Frag8<E> fb = load_frag<E>(reinterpret_cast<const E*>(&vt[lr * kVtPitch + kq]));
+          Frag8<E> fb[4];
 #pragma unroll
-          for (int c = 0; c < NT; ++c) acc[c] = mma_k32(xf[d][c], fb, acc[c]);
+          for (int j = 0; j < 4; ++j) fb[j] = load_frag<E>(reinterpret_cast<const E*>(&vt[(16 * j + lr) * kVtPitch + kq]));
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int c = 0; c < NT; ++c) acc[j][c] = mma_k32(xf[d][c], fb[j], acc[j][c]);
           __builtin_amdgcn_sched_barrier(0);
           mfma_operand_guard();
           __builtin_amdgcn_sched_barrier(0);
@@ -169,23 +201,26 @@ __device__ void produce_t(const DecodeArgs& a, int p, uint8_t* smem) {
     }
   }
 
-  // Sum the eight waves' tiles in a fixed order; C holds tokens
-  // 4*(l/16)+e of token tile c, column lr of the block.  The block's result
-  // goes to LDS as [16*NT tokens][16 columns].
-  __syncthreads();  // every wave is done with its V tile
+  // Sum the eight waves' tiles in a fixed order, one 16-column tile at a
+  // time; C holds tokens 4*(l/16)+e of token tile c, column lr of the tile.
+  // The block's result goes to LDS as [16*NT tokens][64 columns].
   f32x4* red = reinterpret_cast<f32x4*>(smem);  // [kWaves][NT][kWave]
   float* blk = reinterpret_cast<float*>(smem + kWaves * NT * kWave * 16);
 #pragma unroll
-  for (int c = 0; c < NT; ++c) red[(w * NT + c) * kWave + l] = acc[c];
-  __syncthreads();
-  if (w < NT) {
-    f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 4; ++j) {
+    __syncthreads();  // the V tiles, or the previous tile's sums, are done with
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) sum += red[(v * NT + w) * kWave + l];
+    for (int c = 0; c < NT; ++c) red[(w * NT + c) * kWave + l] = acc[j][c];
+    __syncthreads();
+    if (w < NT) {
+      f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int tok = w * 16 + q4 * 4 + e;
-      blk[tok * 16 + lr] = tok < M ? sum[e] : 0.f;
+      for (int v = 0; v < kWaves; ++v) sum += red[(v * NT + w) * kWave + l];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tok = w * 16 + q4 * 4 + e;
+        blk[tok * kCbCols + 16 * j + lr] = tok < M ? sum[e] : 0.f;
+      }
     }
   }
   __syncthreads();
@@ -194,12 +229,14 @@ __device__ void produce_t(const DecodeArgs& a, int p, uint8_t* smem) {
   // partial; the last producer of the column block to arrive sums the KT
   // partials in k-slice order.  Either way the final block is published in
   // the operand type, two columns per 32-bit word, and counted in kDone.
-  const int Rp = a.NCB * 16;
+  const int Rp = a.NCB * kCbCols;
+  const int col0 = cb * kCbCols;
   __shared__ unsigned s_last;
   bool last = true;
   if (a.KT > 1) {
-    float* tp = a.tpart + size_t(kt) * (16 * NT) * Rp + cb * 16;
-    for (int i = tid; i < 16 * NT * 16; i += kThreads) store_coherent(&tp[(i / 16) * Rp + i % 16], __float_as_uint(blk[i]));
+    float* tp = a.tpart + size_t(kt) * (16 * NT) * Rp + col0;
+    for (int i = tid; i < 16 * NT * kCbCols; i += kThreads)
+      store_coherent(&tp[(i / kCbCols) * Rp + i % kCbCols], __float_as_uint(blk[i]));
     drain_stores();
     __syncthreads();
     if (tid == 0) s_last = add_coherent(&a.ctrl[kCbCounters + cb], 1u) == unsigned(a.KT - 1);
@@ -207,8 +244,8 @@ __device__ void produce_t(const DecodeArgs& a, int p, uint8_t* smem) {
     last = s_last;
   }
   if (!last) return;
-  for (int i = tid; i < 16 * NT * 8; i += kThreads) {  // word i: token i/8, columns 2*(i%8) and +1
-    const int tok = i / 8, col = 2 * (i % 8);
+  for (int i = tid; i < 16 * NT * kCbCols / 2; i += kThreads) {  // word i: token i/32, columns 2*(i%32) and +1
+    const int tok = i / (kCbCols / 2), col = 2 * (i % (kCbCols / 2));
     float v0 = 0.f, v1 = 0.f;
     if (a.KT > 1) {
       // All partials are fetched at once (one round trip), then summed in
@@ -216,10 +253,10 @@ __device__ void produce_t(const DecodeArgs& a, int p, uint8_t* smem) {
       float p0[kMaxKT], p1[kMaxKT];
 #pragma unroll
       for (int k = 0; k < kMaxKT; ++k) {
-        const float* src = a.tpart + (size_t(k) * (16 * NT) + tok) * Rp + cb * 16 + col;
+        const float* src = a.tpart + (size_t(k) * (16 * NT) + tok) * Rp + col0 + col;
         const bool other = k < a.KT && k != kt;
-        p0[k] = other ? __uint_as_float(load_coherent(src)) : blk[tok * 16 + col];
-        p1[k] = other ? __uint_as_float(load_coherent(src + 1)) : blk[tok * 16 + col + 1];
+        p0[k] = other ? __uint_as_float(load_coherent(src)) : blk[tok * kCbCols + col];
+        p1[k] = other ? __uint_as_float(load_coherent(src + 1)) : blk[tok * kCbCols + col + 1];
       }
 #pragma unroll
       for (int k = 0; k < kMaxKT; ++k)
@@ -228,16 +265,16 @@ __device__ void produce_t(const DecodeArgs& a, int p, uint8_t* smem) {
           v1 += p1[k];
         }
     } else {
-      v0 = blk[tok * 16 + col];
-      v1 = blk[tok * 16 + col + 1];
+      v0 = blk[tok * kCbCols + col];
+      v1 = blk[tok * kCbCols + col + 1];
     }
     if constexpr (sizeof(E) == 2) {
       uint32_t* tf = static_cast<uint32_t*>(a.tfull);
-      store_coherent(&tf[(size_t(tok) * Rp + cb * 16 + col) / 2], uint32_t(f32_to_bf16(v0)) | (uint32_t(f32_to_bf16(v1)) << 16));
+      store_coherent(&tf[(size_t(tok) * Rp + col0 + col) / 2], uint32_t(f32_to_bf16(v0)) | (uint32_t(f32_to_bf16(v1)) << 16));
     } else {
       float* tf = static_cast<float*>(a.tfull);
-      store_coherent(&tf[size_t(tok) * Rp + cb * 16 + col], __float_as_uint(v0));
-      store_coherent(&tf[size_t(tok) * Rp + cb * 16 + col + 1], __float_as_uint(v1));
+      store_coherent(&tf[size_t(tok) * Rp + col0 + col], __float_as_uint(v0));
+      store_coherent(&tf[size_t(tok) * Rp + col0 + col + 1], __float_as_uint(v1));
     }
   }
   drain_stores();
@@ -261,7 +298,7 @@ template <typename E, int NT, int TILES> constexpr int pipe_depth() {
 // launch): device-scope 32-bit loads.
 template <typename E>
 __device__ __forceinline__ Frag8<E> load_t(const DecodeArgs& a, int tok, int k) {
-  const uint32_t* q = static_cast<const uint32_t*>(a.tfull) + (size_t(tok) * (a.NCB * 16) + k) * sizeof(E) / 4;
+  const uint32_t* q = static_cast<const uint32_t*>(a.tfull) + (size_t(tok) * (a.NCB * kCbCols) + k) * sizeof(E) / 4;
   Frag8<E> f;
   if constexpr (sizeof(E) == 2) {
     f.v = make_uint4(load_coherent(q), load_coherent(q + 1), load_coherent(q + 2), load_coherent(q + 3));
@@ -499,16 +536,15 @@ __device__ void stream_rows(const DecodeArgs& a, int b, uint8_t* smem) {
 
 constexpr int kReduceBytes = kWaves * 4 * kWave * 16;  // the streamers' cross-wave reduction
 
-template <int NT, int TILES>
+template <typename E, int NT, int TILES>
 constexpr int smem_bytes() {
-  return kReduceBytes + int(sizeof(float)) * (16 * TILES + 16 * NT * 16 * TILES);
+  constexpr int streamer = kReduceBytes + int(sizeof(float)) * (16 * TILES + 16 * NT * 16 * TILES);
+  return streamer > producer_smem<E, NT>() ? streamer : producer_smem<E, NT>();
 }
 
 template <typename E, int NT, int TILES>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void decode_kernel(DecodeArgs a) {
-  static_assert(kWaves * 16 * kVtPitch * sizeof(E) <= kReduceBytes, "the producers' V tiles fit");
-  static_assert(kWaves * NT * kWave * 16 + 16 * NT * 16 * 4 <= smem_bytes<NT, TILES>(), "the producers' reduction fits");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<NT, TILES>()];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<E, NT, TILES>()];
   const int b = int(blockIdx.x), np = a.NCB * a.KT;
   if (b < np) produce_t<E, NT>(a, b, smem);
   else stream_rows<E, NT, TILES>(a, b - np, smem);
@@ -571,12 +607,11 @@ DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
   p.NRB = int(nrb);
   p.KS = int(ks);
   p.NB = p.NRB * p.KS;
-  // Producers: 16 columns of T each, over k-slices of about 1024 of in_dim
-  // (four k32 steps per wave: one round of loads).
+  // Producers: 64 columns of T each, over k-slices of about 768 of in_dim
+  // (three k32 steps per wave: one round of loads at 16 tokens).
   if (rank > 0) {
-    const int64_t rp = (rank + 31) / 32 * 32;
-    p.NCB = int(rp / 16);
-    int64_t kt = (in_dim + 1023) / 1024;
+    p.NCB = int((rank + kCbCols - 1) / kCbCols);
+    int64_t kt = (in_dim + 767) / 768;
     if (kt > kMaxKT) kt = kMaxKT;
     if (p.NCB > kMaxGroupCounters / 2) kt = 1;  // one arrival counter per column block
     p.KT = int(kt);
@@ -589,9 +624,9 @@ DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
   const size_t rbr = size_t(16 * p.TILES);
   size_t off = kControlBytes;
   p.off_tpart = off;  // [KT][16*NT][Rp] fp32 (KT > 1)
-  off = align_up(off + (p.KT > 1 ? size_t(p.KT) * rows16 * size_t(p.NCB) * 16 * 4 : 0), 256);
+  off = align_up(off + (p.KT > 1 ? size_t(p.KT) * rows16 * size_t(p.NCB) * kCbCols * 4 : 0), 256);
   p.off_tfull = off;  // [16*NT][Rp], fp32 or bf16
-  off = align_up(off + rows16 * size_t(p.NCB) * 16 * 4, 256);
+  off = align_up(off + rows16 * size_t(p.NCB) * kCbCols * 4, 256);
   p.off_ypart = off;  // [NRB][KS][16*NT][RBR] fp32
   off = align_up(off + (p.KS > 1 ? size_t(p.NRB) * size_t(p.KS) * rows16 * rbr * 4 : 0), 256);
   p.bytes = off;
