@@ -100,7 +100,7 @@ tb_status tb_linear_forward_workspace_size(int64_t m, int64_t out_dim, int64_t i
   if (int e = device_cu_count(&cus)) return hip_fail(hipError_t(e), "querying the compute-unit count");
   size_t bytes;
   if (dtype == TB_BF16 && m > kDecodeMaxTokens) {
-    bytes = plan_gemm(m, out_dim, in_dim, rank).bytes;
+    bytes = plan_gemm(m, out_dim, in_dim, rank, cus).bytes;
   } else {
     const int64_t mm = m < kDecodeMaxTokens ? m : kDecodeMaxTokens;
     bytes = plan_decode(mm, out_dim, in_dim, rank, cus).bytes;
@@ -127,7 +127,7 @@ tb_status tb_linear_forward(const void* x, const void* s, const void* w0, const 
   hipStream_t hs = static_cast<hipStream_t>(stream);
 
   if (dtype == TB_BF16 && m > kDecodeMaxTokens) {
-    const GemmPlan p = plan_gemm(m, out_dim, in_dim, rank);
+    const GemmPlan p = plan_gemm(m, out_dim, in_dim, rank, cus);
     if (workspace_bytes < p.bytes)
       return fail(TB_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is below the %zu needed", workspace_bytes, p.bytes);
     hipError_t e = launch_forward_gemm(p, x, s, w0, u, v, y, m, out_dim, in_dim, rank, workspace, hs);

@@ -6,14 +6,16 @@
 // ("The theta bundle": the transpose of weight = diag(s) W0 + U V^T applied
 // to x.)  Step 2 is a matrix-core GEMM whose operands are both contiguous
 // along the reduction dimension (x rows over in_dim, W0 rows over in_dim).
-// Tiles of x and W0 are staged through LDS with double buffering: the global
-// loads for step k+1 are in flight while the matrix cores work on step k.
-// The epilogue scales each output column by s in fp32 and then continues the
-// same accumulators over the rank dimension with T and U (both contiguous
-// along r), so the rank-r delta costs r/in_dim extra reduction steps and no
-// extra pass over y.
+// The scale by s is applied in fp32 to the finished sums of x . W0^T, and the
+// same accumulators then continue over the rank dimension with T and U (both
+// contiguous along r), so the rank-r delta costs r/in_dim extra reduction
+// steps and no extra pass over y.  Rows that are 16-byte aligned (in_dim and
+// rank multiples of 8) take the 256 x 256 stream-K kernel; other shapes take
+// a general 128 x 128 kernel.
 #include "tb_device.h"
 #include "tb_host.h"
+
+#include <algorithm>
 
 namespace tb {
 
@@ -71,8 +73,9 @@ __global__ __launch_bounds__(kThreads) void xv_gemm_kernel(const bf16_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Main GEMM.  Workgroup tile 128 tokens x 128 outputs x 64 in_dim per stage;
-// four waves in a 2 x 2 arrangement, each owning 64 x 64 (4 x 4 tiles).
+// General GEMM (any in_dim and rank).  Workgroup tile 128 tokens x 128
+// outputs x 64 in_dim per stage; four waves in a 2 x 2 arrangement, each
+// owning 64 x 64 (4 x 4 tiles).
 // ---------------------------------------------------------------------------
 constexpr int BM = 128, BN = 128, BK = 64, PITCH = BK + 8;  // 144-byte LDS rows
 
@@ -209,27 +212,735 @@ __global__ __launch_bounds__(kThreads) void forward_gemm_kernel(GemmArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Shared by the two matrix-core kernels below.
+// ---------------------------------------------------------------------------
+constexpr int kCounterBase = 64;              // control words from here count arrivals
+constexpr unsigned kRsrcFlags = 0x00020000u;  // buffer descriptor word 3: 32-bit data format
+constexpr int kCoherent = 16;                 // sc1: device-scope access, coherent across XCDs
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_byte;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+// Lane addresses in an LDS ring are passed through an empty asm statement so
+// the compiler keeps each as one register and folds every per-step,
+// per-buffer displacement (all below 64 KB) into the instruction's immediate
+// offset instead of materialising one register per displacement.
+__device__ __forceinline__ lds_byte* opaque(lds_byte* p) {
+  asm volatile("" : "+v"(p));
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// Main GEMM for 16-byte aligned rows (in_dim and rank multiples of 8).
+//
+// Output tiles of 256 tokens x 256 outputs; eight waves, each owning 128 x 64
+// as 4 x 2 accumulator tiles of v_mfma_f32_32x32x16_bf16.  The reduction runs
+// in k-tiles of 64 through a two-buffer LDS ring (rows padded from 128 to 144
+// bytes, so the 16-byte fragment reads of 16 consecutive rows fall in distinct
+// bank groups and every k16 step is a fixed offset from one lane address)
+// fed from two register sets of buffer loads: the fetch of
+// k-tile k+2 is issued before k-tile k is multiplied, so each fetch has two
+// k-tiles' time to land.  Rows past the matrix and chunks past the reduction
+// length read as zero.
+//
+// The rank tail runs through the same pipeline: after the last k-tile of
+// x . W0^T the accumulators are scaled by s and the reduction continues over
+// the rank dimension with T = x . V (from the workspace) and U, both
+// contiguous along r.
+//
+// Workgroups are persistent, one per compute unit.  When the tile count is
+// not a multiple of the workgroup count, the leading tiles are shared out by
+// k-tiles (stream-K): workgroup p takes k-tiles [p * ipw, (p + 1) * ipw) of
+// their concatenation, so every workgroup does the same number of k-tiles.  A
+// workgroup that holds only part of a tile's reduction stores its fp32 partial;
+// the last of the tile's workgroups to arrive sums all partials in k order
+// (so the result does not depend on arrival order) and finishes the tile.
+// ---------------------------------------------------------------------------
+namespace big {
+
+constexpr int BM = 256, BN = 256, BK = 64, kThreads = 512;
+constexpr int kPitch = BK * 2 + 16;       // LDS row: 64 bf16 + 16 bytes of padding
+constexpr int kTileBytes = BM * kPitch;   // one operand's k-tile in LDS
+// LDS ring [A0][A1][B0][B1]: buffer 1 sits a fixed 36 KB after buffer 0, so
+// both are reached from the same lane addresses through immediate offsets.
+constexpr int kBOffset = 2 * kTileBytes;
+constexpr int kRingBytes = 4 * kTileBytes;
+constexpr int kPartFloats = BM * BN;      // fp32 partial of one output tile
+
+struct Args {
+  const bf16_t* x;
+  const bf16_t* s;
+  const bf16_t* w0;
+  const bf16_t* u;
+  const bf16_t* t;
+  bf16_t* y;
+  int M, O, I, R;
+  int tiles_m, tiles_n;
+  int KT, KR;        // k-tiles of in_dim and of rank
+  int sk_tiles;      // tiles [0, sk_tiles) are shared out by k-tiles
+  int ipw;           // k-tiles per workgroup over those tiles
+  int xcd_major;     // 1: workgroup g takes position (g % 8) * (grid / 8) + g / 8
+  unsigned* ctrl;
+  float* part;       // [2 * grid][kPartFloats] partials: a workgroup's first and last tile
+};
+
+// Buffer descriptors and lane offsets of one GEMM's operands for one tile.
+struct Operands {
+  __amdgpu_buffer_rsrc_t ra, rb;
+  int va;       // byte offset of this lane's chunk: row tid / 8, chunk tid % 8
+  int rowstep;  // bytes of 64 rows
+  int kel;      // reduction length in elements
+};
+
+__device__ __forceinline__ Operands make_operands(const bf16_t* a, int arows, const bf16_t* b, int brows, int m0,
+                                                  int n0, int k) {
+  Operands o;
+  const int ar = min(arows - m0, BM), br = min(brows - n0, BN);
+  o.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(a + size_t(m0) * k), 0, ar * k * 2, kRsrcFlags);
+  o.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(b + size_t(n0) * k), 0, br * k * 2, kRsrcFlags);
+  o.va = int(threadIdx.x >> 3) * k * 2 + int(threadIdx.x & 7) * 16;
+  o.rowstep = 64 * k * 2;
+  o.kel = k;
+  return o;
+}
+
+// Global fragments of k-tile kt: four 16-byte chunks of each operand per lane.
+__device__ __forceinline__ void fetch(const Operands& o, int kt, u32x4 (&pa)[4], u32x4 (&pb)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    pa[j] = __builtin_amdgcn_raw_buffer_load_b128(o.ra, o.va, kt * BK * 2 + j * o.rowstep, 0);
+    pb[j] = __builtin_amdgcn_raw_buffer_load_b128(o.rb, o.va, kt * BK * 2 + j * o.rowstep, 0);
+  }
+}
+
+// Lane addresses in the LDS ring, built once per workgroup (see opaque()).
+struct Lanes {
+  lds_byte* a_rd;  // A fragment row wm*128 + lane%32, k half lane/32
+  lds_byte* b_rd;  // B fragment row wn*64 + lane%32, k half lane/32
+  lds_byte* a_wr;  // staging row tid/8, chunk tid%8 of A
+  lds_byte* b_wr;  // same of B
+};
+
+__device__ __forceinline__ Lanes make_lanes(uint8_t* ring) {
+  lds_byte* base = (lds_byte*)ring;
+  const int w = int(threadIdx.x) / kWave, l = int(threadIdx.x) % kWave, lr = l & 31, hi = l >> 5;
+  const int wm = w >> 2, wn = w & 3;
+  Lanes ln;
+  ln.a_rd = opaque(base + (wm * 128 + lr) * kPitch + hi * 16);
+  ln.b_rd = opaque(base + kBOffset + (wn * 64 + lr) * kPitch + hi * 16);
+  ln.a_wr = opaque(base + int(threadIdx.x >> 3) * kPitch + int(threadIdx.x & 7) * 16);
+  ln.b_wr = opaque(base + kBOffset + int(threadIdx.x >> 3) * kPitch + int(threadIdx.x & 7) * 16);
+  return ln;
+}
+
+// Write k-tile kt's fragments to LDS buffer BUF; in a k-tile that runs past
+// the reduction length the chunks at or beyond it become zero.
+template <int BUF>
+__device__ __forceinline__ void stage(const Lanes& ln, const Operands& o, int kt, u32x4 (&pa)[4], u32x4 (&pb)[4]) {
+  const int left = o.kel - kt * BK;
+  if (left < BK) {
+    const bool keep = int(threadIdx.x & 7) * 8 < left;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pa[j] = keep ? pa[j] : u32x4{0u, 0u, 0u, 0u};
+      pb[j] = keep ? pb[j] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    *reinterpret_cast<lds_u32x4*>(ln.a_wr + BUF * kTileBytes + j * 64 * kPitch) = pa[j];
+    *reinterpret_cast<lds_u32x4*>(ln.b_wr + BUF * kTileBytes + j * 64 * kPitch) = pb[j];
+  }
+}
+
+// Operand fragments of k16 step st from buffer BUF: A rows wm*128 + 32i +
+// lane%32, B rows wn*64 + 32j + lane%32, k = 16 st + 8 (lane / 32) + 0..7.
+template <int BUF>
+__device__ __forceinline__ void read_frags(const Lanes& ln, int st, u32x4 (&fa)[4], u32x4 (&fb)[2]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    fa[i] = *reinterpret_cast<const lds_u32x4*>(ln.a_rd + BUF * kTileBytes + i * 32 * kPitch + st * 32);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    fb[j] = *reinterpret_cast<const lds_u32x4*>(ln.b_rd + BUF * kTileBytes + j * 32 * kPitch + st * 32);
+}
+
+__device__ __forceinline__ void mma_step(const u32x4 (&fa)[4], const u32x4 (&fb)[2], f32x16 (&acc)[4][2]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[i]),
+                                                          __builtin_bit_cast(bf16x8, fb[j]), acc[i][j], 0, 0, 0);
+}
+
+// One k-tile from LDS buffer BUF: four k16 steps, each step's fragments read
+// while the previous step multiplies.  The scheduling fences keep the reads
+// ahead of the previous step's products instead of letting them sink next to
+// their first use.
+template <int BUF>
+__device__ __forceinline__ void multiply_tile(const Lanes& ln, f32x16 (&acc)[4][2]) {
+  u32x4 fa0[4], fb0[2], fa1[4], fb1[2];
+  read_frags<BUF>(ln, 0, fa0, fb0);
+  read_frags<BUF>(ln, 1, fa1, fb1);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_step(fa0, fb0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags<BUF>(ln, 2, fa0, fb0);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_step(fa1, fb1, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags<BUF>(ln, 3, fa1, fb1);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_step(fa0, fb0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_step(fa1, fb1, acc);
+}
+
+// acc += A[rows, kb*64 : ke*64] . B[rows, same]^T.  Leaves the LDS ring free.
+__device__ __forceinline__ void k_loop(const Operands& o, int kb, int ke, f32x16 (&acc)[4][2], const Lanes& ln) {
+  const int n = ke - kb;
+  u32x4 pa0[4], pb0[4], pa1[4], pb1[4];
+  fetch(o, kb, pa0, pb0);
+  fetch(o, min(kb + 1, ke - 1), pa1, pb1);
+  stage<0>(ln, o, kb, pa0, pb0);
+  __syncthreads();
+  for (int k = 0; k < n; k += 2) {
+    const int k1 = min(kb + k + 1, ke - 1), k2 = min(kb + k + 2, ke - 1), k3 = min(kb + k + 3, ke - 1);
+    fetch(o, k2, pa0, pb0);
+    __builtin_amdgcn_sched_barrier(0);
+    multiply_tile<0>(ln, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    stage<1>(ln, o, k1, pa1, pb1);
+    __syncthreads();
+    if (k + 1 < n) {
+      fetch(o, k3, pa1, pb1);
+      __builtin_amdgcn_sched_barrier(0);
+      multiply_tile<1>(ln, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      stage<0>(ln, o, k2, pa0, pb0);
+      __syncthreads();
+    }
+  }
+}
+
+// Tile u of the processing order -> (token tile, output tile): groups of
+// eight token tiles are walked column by column, so workgroups that run
+// together share x and W0 rows in L2.
+__device__ __forceinline__ void tile_coords(const Args& a, int u, int& tm, int& tn) {
+  const int per_group = 8 * a.tiles_n;
+  const int first = (u / per_group) * 8, gsize = min(a.tiles_m - first, 8), r = u % per_group;
+  tm = first + r % gsize;
+  tn = r / gsize;
+}
+
+// Partial slot of stream-K position p for tile u: 0 for the tile its range
+// starts in, 1 for the tile it ends in.
+__device__ __forceinline__ int part_slot(const Args& a, int p, int u) {
+  return 2 * p + (p * a.ipw < u * a.KT ? 1 : 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const Args& a, int slot) {
+  return __builtin_amdgcn_make_buffer_rsrc(a.part + size_t(slot) * kPartFloats, 0, kPartFloats * 4, kRsrcFlags);
+}
+
+// Partials are laid out as the accumulators sit in registers: 16-byte piece
+// q = (2i + j) * 4 + c of every lane, lanes contiguous.
+__device__ __forceinline__ void store_partial(const Args& a, int slot, const f32x16 (&acc)[4][2]) {
+  const __amdgpu_buffer_rsrc_t rs = part_rsrc(a, slot);
+  const int lane_off = int(threadIdx.x) * 16;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32x4 v = {__float_as_uint(acc[i][j][4 * c]), __float_as_uint(acc[i][j][4 * c + 1]),
+                         __float_as_uint(acc[i][j][4 * c + 2]), __float_as_uint(acc[i][j][4 * c + 3])};
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs, lane_off, ((i * 2 + j) * 4 + c) * kThreads * 16, kCoherent);
+      }
+}
+
+// acc = partial (first) or acc += partial.
+__device__ __forceinline__ void add_partial(const Args& a, int slot, bool first, f32x16 (&acc)[4][2]) {
+  const __amdgpu_buffer_rsrc_t rs = part_rsrc(a, slot);
+  const int lane_off = int(threadIdx.x) * 16;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off, ((i * 2 + j) * 4 + c) * kThreads * 16,
+                                                              kCoherent);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[i][j][4 * c + e] = first ? __uint_as_float(v[e]) : acc[i][j][4 * c + e] + __uint_as_float(v[e]);
+      }
+}
+
+// Scale by s, add T . U^T, round to bf16 and store.
+__device__ __forceinline__ void finish_tile(const Args& a, int m0, int n0, f32x16 (&acc)[4][2], const Lanes& ln) {
+  const int w = int(threadIdx.x) / kWave, l = int(threadIdx.x) % kWave, lr = l & 31, hi = l >> 5;
+  const int wm = w >> 2, wn = w & 3;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wn * 64 + j * 32 + lr;
+    const float sc = n < a.O ? bf16_to_f32(a.s[n].bits) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i][j] *= sc;
+  }
+  if (a.R > 0) {
+    const Operands r = make_operands(a.t, a.M, a.u, a.O, m0, n0, a.R);
+    k_loop(r, 0, a.KR, acc, ln);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn * 64 + j * 32 + lr;
+      if (n >= a.O) continue;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = m0 + wm * 128 + i * 32 + 8 * b + 4 * hi + e;
+          if (m < a.M) a.y[size_t(m) * a.O + n] = bf16_t{f32_to_bf16(acc[i][j][4 * b + e])};
+        }
+    }
+}
+
+// k-tiles [kb, ke) of tile u; finishes the tile if it holds the whole
+// reduction or arrives last among the tile's workgroups.
+__device__ __forceinline__ void do_tile(const Args& a, int u, int kb, int ke, int pos, const Lanes& ln,
+                                        unsigned* s_last) {
+  int tm, tn;
+  tile_coords(a, u, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  k_loop(make_operands(a.x, a.M, a.w0, a.O, m0, n0, a.I), kb, ke, acc, ln);
+  if (kb > 0 || ke < a.KT) {
+    const int first = (u * a.KT) / a.ipw, last = (u * a.KT + a.KT - 1) / a.ipw;
+    store_partial(a, part_slot(a, pos, u), acc);
+    __builtin_amdgcn_s_waitcnt(0);  // partial written through before counting in
+    __syncthreads();
+    if (threadIdx.x == 0)
+      *s_last = __hip_atomic_fetch_add(&a.ctrl[kCounterBase + u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                unsigned(last - first);
+    __syncthreads();
+    if (!*s_last) return;
+    for (int q = first; q <= last; ++q) add_partial(a, part_slot(a, q, u), q == first, acc);
+    if (threadIdx.x == 0)
+      __hip_atomic_store(&a.ctrl[kCounterBase + u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  finish_tile(a, m0, n0, acc, ln);
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void gemm_kernel(Args a) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes];
+  __shared__ unsigned s_last;
+  const int g = int(blockIdx.x), G = int(gridDim.x);
+  const int pos = a.xcd_major ? (g % 8) * (G / 8) + g / 8 : g;
+  const Lanes ln = make_lanes(ring);
+  if (a.sk_tiles > 0) {
+    const int total = a.sk_tiles * a.KT;
+    const int end = min(total, (pos + 1) * a.ipw);
+    for (int it = pos * a.ipw; it < end;) {
+      const int u = it / a.KT, kb = it - u * a.KT, ke = min(a.KT, kb + (end - it));
+      do_tile(a, u, kb, ke, pos, ln, &s_last);
+      it += ke - kb;
+    }
+  }
+  const int tiles = a.tiles_m * a.tiles_n;
+  for (int u = a.sk_tiles + pos; u < tiles; u += G) do_tile(a, u, 0, a.KT, pos, ln, &s_last);
+}
+
+}  // namespace big
+
+// ---------------------------------------------------------------------------
+// T = x . V for many tokens.  V is [in_dim, r] with r contiguous, so its
+// k-tiles are staged in LDS as they sit in memory (rows of k) and the matrix
+// core's B fragments (eight consecutive k of one column per lane) are read
+// with the transposing LDS read: within each group of 16 lanes, lane i
+// receives element i % 4 of the 8-byte chunks addressed by lanes 4e + i / 4
+// (e = 0..3), so lanes that point at rows kb + j / 4, columns nb + 4 (j % 4)
+// each receive four consecutive k of column nb + i.
+//
+// Workgroup tile: 64 tokens x 256 columns of T, four waves of 64 x 64 (2 x 2
+// tiles of v_mfma_f32_32x32x16_bf16), k-tiles of 64 double-buffered in LDS
+// from two register sets of buffer loads.  The reduction over in_dim is split
+// into KS slices so the grid fills the chip; with KS > 1 each slice stores its
+// fp32 partial and the last of a tile's slices to arrive sums them in slice
+// order and stores T rounded to bf16.
+// ---------------------------------------------------------------------------
+namespace xv {
+
+constexpr int BM = 64, BN = 256, BK = 64, kThreads = 256;
+constexpr int kXPitch = BK * 2 + 16;   // 144-byte rows of the x tile
+constexpr int kVPitch = BN * 2 + 64;   // 576-byte rows of the V tile: 16 banks of skew per row
+constexpr int kXTile = BM * kXPitch;   // 9 KB
+constexpr int kVTile = BK * kVPitch;   // 36 KB
+constexpr int kRingBytes = 2 * kVTile + 2 * kXTile;  // [V0][V1][X0][X1]
+constexpr int kPartFloats = BM * BN;
+
+struct Args {
+  const bf16_t* x;
+  const bf16_t* v;
+  bf16_t* t;
+  int M, I, R;
+  int RB, CB, KT;  // row blocks, column blocks, k-tiles of in_dim
+  int KS, kps;     // k-slices and k-tiles per slice
+  unsigned* ctrl;
+  float* part;     // [RB * CB][KS][kPartFloats]
+};
+
+struct Lanes {
+  lds_byte* x_rd;   // A fragment: row lane%32, k half lane/32
+  lds_byte* v_rd0;  // transposing B reads, buffer 0 / 1
+  lds_byte* v_rd1;
+  lds_byte* x_wr;   // x staging: row tid/8, chunk tid%8
+  lds_byte* v_wr0;  // V staging: k-row tid/32, chunk tid%32, buffer 0 / 1
+  lds_byte* v_wr1;
+};
+
+__device__ __forceinline__ Lanes make_lanes(uint8_t* ring) {
+  lds_byte* base = (lds_byte*)ring;
+  const int tid = int(threadIdx.x), w = tid / kWave, l = tid % kWave, lr = l & 31, hi = l >> 5;
+  const int g = l >> 4, j16 = l & 15;
+  const int vrow = 8 * (g >> 1) + (j16 >> 2), vcol = 64 * w + 16 * (g & 1) + 4 * (j16 & 3);
+  Lanes ln;
+  ln.x_rd = opaque(base + 2 * kVTile + lr * kXPitch + hi * 16);
+  ln.v_rd0 = opaque(base + vrow * kVPitch + vcol * 2);
+  ln.v_rd1 = opaque(base + kVTile + vrow * kVPitch + vcol * 2);
+  ln.x_wr = opaque(base + 2 * kVTile + (tid >> 3) * kXPitch + (tid & 7) * 16);
+  ln.v_wr0 = opaque(base + (tid >> 5) * kVPitch + (tid & 31) * 16);
+  ln.v_wr1 = opaque(base + kVTile + (tid >> 5) * kVPitch + (tid & 31) * 16);
+  return ln;
+}
+
+struct Src {
+  __amdgpu_buffer_rsrc_t rx, rv;
+  int xoff, voff;     // lane byte offsets: x row tid/8 chunk tid%8; V k-row tid/32 chunk tid%32
+  int xstep, vstep;   // bytes of 32 x rows / 8 V rows
+  int I, ncols;       // reduction length; valid columns of this column block
+};
+
+__device__ __forceinline__ void fetch(const Src& s, int kt, u32x4 (&px)[2], u32x4 (&pv)[8]) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) px[q] = __builtin_amdgcn_raw_buffer_load_b128(s.rx, s.xoff, kt * BK * 2 + q * s.xstep, 0);
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    pv[q] = __builtin_amdgcn_raw_buffer_load_b128(s.rv, s.voff, kt * 8 * s.vstep + q * s.vstep, 0);
+}
+
+template <int BUF>
+__device__ __forceinline__ void stage(const Lanes& ln, const Src& s, int kt, u32x4 (&px)[2], u32x4 (&pv)[8]) {
+  // x chunks at or past in_dim would read the next row: zero them.  V rows
+  // past in_dim read as zero from the buffer bound; V columns past r of this
+  // block would read the next row: zero them.
+  if (s.I - kt * BK < BK) {
+    const bool keep = int(threadIdx.x & 7) * 8 < s.I - kt * BK;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) px[q] = keep ? px[q] : u32x4{0u, 0u, 0u, 0u};
+  }
+  if (s.ncols < BN) {
+    const bool keep = int(threadIdx.x & 31) * 8 < s.ncols;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) pv[q] = keep ? pv[q] : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) *reinterpret_cast<lds_u32x4*>(ln.x_wr + BUF * kXTile + q * 32 * kXPitch) = px[q];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) *reinterpret_cast<lds_u32x4*>((BUF ? ln.v_wr1 : ln.v_wr0) + q * 8 * kVPitch) = pv[q];
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+template <int BUF>
+__device__ __forceinline__ void read_frags(const Lanes& ln, int st, u32x4 (&fa)[2], u32x4 (&fb)[2]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    fa[i] = *reinterpret_cast<const lds_u32x4*>(ln.x_rd + BUF * kXTile + i * 32 * kXPitch + st * 32);
+  lds_byte* vr = BUF ? ln.v_rd1 : ln.v_rd0;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vr + (16 * st) * kVPitch + 64 * j));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vr + (16 * st + 4) * kVPitch + 64 * j));
+    fb[j] = u32x4{uint32_t(uint16_t(lo[0])) | (uint32_t(uint16_t(lo[1])) << 16),
+                  uint32_t(uint16_t(lo[2])) | (uint32_t(uint16_t(lo[3])) << 16),
+                  uint32_t(uint16_t(hi[0])) | (uint32_t(uint16_t(hi[1])) << 16),
+                  uint32_t(uint16_t(hi[2])) | (uint32_t(uint16_t(hi[3])) << 16)};
+  }
+}
+
+__device__ __forceinline__ void mma_step(const u32x4 (&fa)[2], const u32x4 (&fb)[2], f32x16 (&acc)[2][2]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[i]),
+                                                          __builtin_bit_cast(bf16x8, fb[j]), acc[i][j], 0, 0, 0);
+}
+
+template <int BUF>
+__device__ __forceinline__ void multiply_tile(const Lanes& ln, f32x16 (&acc)[2][2]) {
+  u32x4 fa0[2], fb0[2], fa1[2], fb1[2];
+  read_frags<BUF>(ln, 0, fa0, fb0);
+  read_frags<BUF>(ln, 1, fa1, fb1);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_step(fa0, fb0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags<BUF>(ln, 2, fa0, fb0);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_step(fa1, fb1, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags<BUF>(ln, 3, fa1, fb1);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_step(fa0, fb0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_step(fa1, fb1, acc);
+}
+
+__global__ __launch_bounds__(kThreads) void xv_kernel(Args a) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes];
+  __shared__ unsigned s_last;
+  const int tid = int(threadIdx.x);
+  const int b = int(blockIdx.x), ks = b % a.KS, tile = b / a.KS;
+  const int rb = tile / a.CB, cb = tile % a.CB;
+  const int m0 = rb * BM, n0 = cb * BN;
+  const int kb = ks * a.kps, ke = min(a.KT, kb + a.kps);
+  const Lanes ln = make_lanes(ring);
+  Src s;
+  s.rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(a.x + size_t(m0) * a.I), 0,
+                                          min(a.M - m0, BM) * a.I * 2, kRsrcFlags);
+  s.rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(a.v + n0), 0, (a.I * a.R - n0) * 2, kRsrcFlags);
+  s.xoff = (tid >> 3) * a.I * 2 + (tid & 7) * 16;
+  s.voff = (tid >> 5) * a.R * 2 + (tid & 31) * 16;
+  s.xstep = 32 * a.I * 2;
+  s.vstep = 8 * a.R * 2;
+  s.I = a.I;
+  s.ncols = min(BN, a.R - n0);
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  if (kb < ke) {
+    const int n = ke - kb;
+    u32x4 px0[2], pv0[8], px1[2], pv1[8];
+    fetch(s, kb, px0, pv0);
+    fetch(s, min(kb + 1, ke - 1), px1, pv1);
+    stage<0>(ln, s, kb, px0, pv0);
+    __syncthreads();
+    for (int k = 0; k < n; k += 2) {
+      const int k1 = min(kb + k + 1, ke - 1), k2 = min(kb + k + 2, ke - 1), k3 = min(kb + k + 3, ke - 1);
+      fetch(s, k2, px0, pv0);
+      __builtin_amdgcn_sched_barrier(0);
+      multiply_tile<0>(ln, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      stage<1>(ln, s, k1, px1, pv1);
+      __syncthreads();
+      if (k + 1 < n) {
+        fetch(s, k3, px1, pv1);
+        __builtin_amdgcn_sched_barrier(0);
+        multiply_tile<1>(ln, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        stage<0>(ln, s, k2, px0, pv0);
+        __syncthreads();
+      }
+    }
+  }
+
+  if (a.KS > 1) {
+    // Partial in register order: 16-byte piece q = (2i + j) * 4 + c of every lane.
+    float* blk = a.part + size_t(tile) * a.KS * kPartFloats;
+    const __amdgpu_buffer_rsrc_t mine =
+        __builtin_amdgcn_make_buffer_rsrc(blk + size_t(ks) * kPartFloats, 0, kPartFloats * 4, kRsrcFlags);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const u32x4 val = {__float_as_uint(acc[i][j][4 * c]), __float_as_uint(acc[i][j][4 * c + 1]),
+                             __float_as_uint(acc[i][j][4 * c + 2]), __float_as_uint(acc[i][j][4 * c + 3])};
+          __builtin_amdgcn_raw_buffer_store_b128(val, mine, tid * 16, ((i * 2 + j) * 4 + c) * kThreads * 16,
+                                                 kCoherent);
+        }
+    __builtin_amdgcn_s_waitcnt(0);  // partial written through before counting in
+    __syncthreads();
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(&a.ctrl[kCounterBase + tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               unsigned(a.KS - 1);
+    __syncthreads();
+    if (!s_last) return;
+    for (int q = 0; q < a.KS; ++q) {
+      const __amdgpu_buffer_rsrc_t src =
+          __builtin_amdgcn_make_buffer_rsrc(blk + size_t(q) * kPartFloats, 0, kPartFloats * 4, kRsrcFlags);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const u32x4 val = __builtin_amdgcn_raw_buffer_load_b128(
+                src, tid * 16, ((i * 2 + j) * 4 + c) * kThreads * 16, kCoherent);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[i][j][4 * c + e] = q == 0 ? __uint_as_float(val[e]) : acc[i][j][4 * c + e] + __uint_as_float(val[e]);
+          }
+    }
+    if (tid == 0) __hip_atomic_store(&a.ctrl[kCounterBase + tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const int w = tid / kWave, l = tid % kWave, lr = l & 31, hi = l >> 5;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + 64 * w + 32 * j + lr;
+      if (n >= a.R) continue;
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = m0 + 32 * i + 8 * bb + 4 * hi + e;
+          if (m < a.M) a.t[size_t(m) * a.R + n] = bf16_t{f32_to_bf16(acc[i][j][4 * bb + e])};
+        }
+    }
+}
+
+}  // namespace xv
+
 }  // namespace
 
-GemmPlan plan_gemm(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank) {
-  (void)out_dim;
-  (void)in_dim;
+namespace {
+
+// Cost model of the stream-K plan, in k-tiles of one workgroup: storing a
+// 256 x 256 fp32 partial and reading one back each cost about as much as a
+// few k-tiles of multiplication.
+constexpr int kStoreCost = 6, kLoadCost = 4;
+
+}  // namespace
+
+GemmPlan plan_gemm(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus) {
   GemmPlan p{};
   p.off_t = kControlBytes;
-  p.bytes = align_up(p.off_t + size_t(m) * size_t(rank) * 2, 256);
+  const size_t off = align_up(p.off_t + size_t(m) * size_t(rank) * 2, 256);
+  p.bytes = off;
+  // The stream-K kernel addresses one tile's rows with 32-bit byte offsets.
+  p.big = in_dim % 8 == 0 && rank % 8 == 0 && in_dim < (int64_t(1) << 22) && rank < (int64_t(1) << 22) &&
+          in_dim * rank < (int64_t(1) << 30);
+  if (!p.big) return p;
+  // x . V: enough k-slices to give every compute unit a workgroup, each at
+  // least two k-tiles long and at most 16 partials per tile.
+  size_t o2 = off;
+  if (rank > 0) {
+    p.xv_rb = int((m + xv::BM - 1) / xv::BM);
+    p.xv_cb = int((rank + xv::BN - 1) / xv::BN);
+    p.xv_kt = int((in_dim + xv::BK - 1) / xv::BK);
+    const int64_t tiles = int64_t(p.xv_rb) * p.xv_cb;
+    int64_t ks = tiles >= cus ? 1 : cus / tiles;
+    ks = std::min<int64_t>(ks, std::min<int64_t>(16, std::max<int64_t>(1, p.xv_kt / 2)));
+    if (tiles > kMaxGroupCounters) ks = 1;
+    p.xv_kps = int((p.xv_kt + ks - 1) / ks);
+    p.xv_ks = int((p.xv_kt + p.xv_kps - 1) / p.xv_kps);
+    p.off_xvpart = o2;
+    if (p.xv_ks > 1) o2 = align_up(o2 + size_t(tiles) * p.xv_ks * xv::kPartFloats * 4, 256);
+  }
+  const size_t off_big = o2;
+  p.bytes = o2;
+  p.tiles_m = int((m + big::BM - 1) / big::BM);
+  p.tiles_n = int((out_dim + big::BN - 1) / big::BN);
+  p.KT = int((in_dim + big::BK - 1) / big::BK);
+  p.KR = int((rank + big::BK - 1) / big::BK);
+  const int64_t tiles = int64_t(p.tiles_m) * p.tiles_n, KT = p.KT;
+  const int G = cus >= 8 ? cus / 8 * 8 : cus;
+  const auto round8 = [&](int64_t g) { return int(cus >= 8 ? std::min<int64_t>(G, (g + 7) / 8 * 8) : std::min<int64_t>(G, g)); };
+
+  // Data-parallel: whole tiles, ceil(tiles / G) rounds.
+  int64_t best = (tiles + G - 1) / G * KT;
+  p.grid = round8(tiles);
+  p.sk_tiles = 0;
+  p.ipw = 0;
+  // Stream-K over the leading sk tiles, the rest in whole rounds.
+  const int64_t rounds = tiles / G, rem = tiles % G;
+  if (rem != 0) {
+    const int64_t cands[2] = {rem, rounds > 0 ? rem + G : -1};
+    for (int64_t sk : cands) {
+      if (sk <= 0 || sk > kMaxGroupCounters) continue;
+      for (int div = 1; div <= 8; div *= 2) {
+        // Without whole rounds the grid may shrink so partials stay large.
+        if (div > 1 && sk != tiles) break;
+        const int grid = round8((G + div - 1) / div);
+        const int64_t ipw = (sk * KT + grid - 1) / grid;
+        if (ipw < 1) continue;
+        const int64_t segs = (KT - 1 + ipw - 1) / ipw + 1;
+        const int64_t cost = (tiles - sk) / G * KT + ipw + kStoreCost + kLoadCost * segs;
+        if (cost < best) {
+          best = cost;
+          p.grid = sk == tiles ? grid : G;
+          p.sk_tiles = int(sk);
+          p.ipw = int(ipw);
+        }
+      }
+    }
+  }
+  p.xcd_major = p.grid % 8 == 0 ? 1 : 0;
+  p.off_part = off_big;
+  if (p.sk_tiles > 0) p.bytes = off_big + size_t(2) * p.grid * big::kPartFloats * 4;
   return p;
 }
 
 hipError_t launch_forward_gemm(const GemmPlan& p, const void* x, const void* s, const void* w0, const void* u,
                                const void* v, void* y, int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
                                void* workspace, hipStream_t stream) {
-  bf16_t* t = reinterpret_cast<bf16_t*>(static_cast<char*>(workspace) + p.off_t);
-  if (rank > 0) {
+  char* ws = static_cast<char*>(workspace);
+  bf16_t* t = reinterpret_cast<bf16_t*>(ws + p.off_t);
+  if (rank > 0 && p.big) {
+    xv::Args a;
+    a.x = static_cast<const bf16_t*>(x);
+    a.v = static_cast<const bf16_t*>(v);
+    a.t = t;
+    a.M = int(m); a.I = int(in_dim); a.R = int(rank);
+    a.RB = p.xv_rb; a.CB = p.xv_cb; a.KT = p.xv_kt;
+    a.KS = p.xv_ks; a.kps = p.xv_kps;
+    a.ctrl = reinterpret_cast<unsigned*>(ws);
+    a.part = reinterpret_cast<float*>(ws + p.off_xvpart);
+    hipLaunchKernelGGL(xv::xv_kernel, dim3(unsigned(p.xv_rb * p.xv_cb * p.xv_ks)), dim3(xv::kThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else if (rank > 0) {
     dim3 grid(unsigned((m + kTM - 1) / kTM), unsigned((rank + kTN - 1) / kTN));
     hipLaunchKernelGGL(xv_gemm_kernel, grid, dim3(kThreads), 0, stream, static_cast<const bf16_t*>(x),
                        static_cast<const bf16_t*>(v), t, int(m), int(in_dim), int(rank));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  if (p.big) {
+    big::Args a;
+    a.x = static_cast<const bf16_t*>(x);
+    a.s = static_cast<const bf16_t*>(s);
+    a.w0 = static_cast<const bf16_t*>(w0);
+    a.u = static_cast<const bf16_t*>(u);
+    a.t = t;
+    a.y = static_cast<bf16_t*>(y);
+    a.M = int(m); a.O = int(out_dim); a.I = int(in_dim); a.R = int(rank);
+    a.tiles_m = p.tiles_m; a.tiles_n = p.tiles_n;
+    a.KT = p.KT; a.KR = p.KR;
+    a.sk_tiles = p.sk_tiles; a.ipw = p.ipw; a.xcd_major = p.xcd_major;
+    a.ctrl = reinterpret_cast<unsigned*>(ws);
+    a.part = reinterpret_cast<float*>(ws + p.off_part);
+    hipLaunchKernelGGL(big::gemm_kernel, dim3(unsigned(p.grid)), dim3(big::kThreads), 0, stream, a);
+    return hipGetLastError();
   }
   GemmArgs a;
   a.x = static_cast<const bf16_t*>(x);

@@ -38,9 +38,17 @@ hipError_t launch_forward_decode(const DecodePlan& p, tb_dtype dtype, const void
 
 // ---- forward, prefill token counts (bf16, m > kDecodeMaxTokens) ----------
 struct GemmPlan {
-  size_t off_t, bytes;
+  int big;              // 1: 256 x 256 stream-K kernel (in_dim, rank multiples of 8); 0: general kernel
+  int grid;             // persistent workgroups of the stream-K kernel
+  int tiles_m, tiles_n; // 256 x 256 output tiles
+  int KT, KR;           // k-tiles (64) of in_dim and of rank
+  int sk_tiles, ipw;    // leading tiles shared out by k-tiles, k-tiles per workgroup
+  int xcd_major;        // workgroup positions spread XCD-major (grid a multiple of 8)
+  int xv_rb, xv_cb;     // x . V on the aligned path: 64-token row blocks, 256-column blocks of T
+  int xv_kt, xv_ks, xv_kps;  // its k-tiles (64), k-slices and k-tiles per slice
+  size_t off_t, off_xvpart, off_part, bytes;
 };
-GemmPlan plan_gemm(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank);
+GemmPlan plan_gemm(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus);
 
 hipError_t launch_forward_gemm(const GemmPlan& p, const void* x, const void* s, const void* w0, const void* u,
                                const void* v, void* y, int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,

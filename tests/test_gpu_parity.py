@@ -192,6 +192,9 @@ EDGE_SHAPES = [  # (M, out, in, rank)
     (1, 1, 8, 0), (1, 5, 16, 1), (3, 17, 40, 4), (16, 64, 64, 32), (17, 100, 264, 12), (33, 130, 520, 40),
     (64, 64, 64, 8), (5, 48, 8192, 256), (2, 300, 1000, 300), (65, 130, 264, 12), (130, 257, 136, 20),
     (200, 300, 1000, 300), (257, 129, 72, 0), (96, 2048, 512, 64),
+    # 16-byte aligned rows: the 256 x 256 kernel with ragged tiles and k tails,
+    # the last one shared out by k-tiles over 128 workgroups.
+    (300, 520, 200, 24), (513, 1000, 1032, 136), (1100, 700, 4104, 40), (700, 600, 1000, 264),
 ]
 
 
