@@ -251,17 +251,26 @@ __device__ __forceinline__ lds_byte* opaque(lds_byte* p) {
 // the rank dimension with T = x . V (from the workspace) and U, both
 // contiguous along r.
 //
-// Workgroups are persistent, one per compute unit.  When the tile count is
-// not a multiple of the workgroup count, the leading tiles are shared out by
-// k-tiles (stream-K): workgroup p takes k-tiles [p * ipw, (p + 1) * ipw) of
-// their concatenation, so every workgroup does the same number of k-tiles.  A
-// workgroup that holds only part of a tile's reduction stores its fp32 partial;
-// the last of the tile's workgroups to arrive sums all partials in k order
-// (so the result does not depend on arrival order) and finishes the tile.
+// Workgroups are persistent, one per compute unit, and take whole tiles in
+// rounds.  When the tile count leaves a last, partly filled round, those
+// remainder tiles are each split into S equal k-slices and the slices are
+// handed out slice-major, so the workgroups running together hold the same
+// k-range of neighbouring tiles and share their x and W0 k-tiles in L2.  A
+// slice stores its fp32 partial; the last of a tile's slices to arrive sums
+// all S partials in slice order (so the result does not depend on arrival
+// order) and finishes the tile.
 // ---------------------------------------------------------------------------
 namespace big {
 
-constexpr int BM = 256, BN = 256, BK = 64, kThreads = 512;
+#ifndef TB_BIG_WAVES
+#define TB_BIG_WAVES 8
+#endif
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kWaves = TB_BIG_WAVES, kThreads = kWaves * kWave;
+constexpr int WN = kWaves / 2;            // waves along the output columns (two along the tokens)
+constexpr int TJ = BN / WN / 32;          // 32-column accumulator tiles per wave
+constexpr int kRows = kThreads / 8;       // rows one round of 16-byte chunks stages
+constexpr int kChunks = BM / kRows;       // chunks per operand per lane per k-tile
 constexpr int kPitch = BK * 2 + 16;       // LDS row: 64 bf16 + 16 bytes of padding
 constexpr int kTileBytes = BM * kPitch;   // one operand's k-tile in LDS
 // LDS ring [A0][A1][B0][B1]: buffer 1 sits a fixed 36 KB after buffer 0, so
@@ -280,18 +289,18 @@ struct Args {
   int M, O, I, R;
   int tiles_m, tiles_n;
   int KT, KR;        // k-tiles of in_dim and of rank
-  int sk_tiles;      // tiles [0, sk_tiles) are shared out by k-tiles
-  int ipw;           // k-tiles per workgroup over those tiles
+  int split_tiles;   // tiles [0, split_tiles) are split into S k-slices ...
+  int S, kps;        // ... of kps k-tiles each (the last may be shorter)
   int xcd_major;     // 1: workgroup g takes position (g % 8) * (grid / 8) + g / 8
   unsigned* ctrl;
-  float* part;       // [2 * grid][kPartFloats] partials: a workgroup's first and last tile
+  float* part;       // [S * split_tiles][kPartFloats] partials, slice-major
 };
 
 // Buffer descriptors and lane offsets of one GEMM's operands for one tile.
 struct Operands {
   __amdgpu_buffer_rsrc_t ra, rb;
   int va;       // byte offset of this lane's chunk: row tid / 8, chunk tid % 8
-  int rowstep;  // bytes of 64 rows
+  int rowstep;  // bytes of kRows rows
   int kel;      // reduction length in elements
 };
 
@@ -302,15 +311,15 @@ __device__ __forceinline__ Operands make_operands(const bf16_t* a, int arows, co
   o.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(a + size_t(m0) * k), 0, ar * k * 2, kRsrcFlags);
   o.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(b + size_t(n0) * k), 0, br * k * 2, kRsrcFlags);
   o.va = int(threadIdx.x >> 3) * k * 2 + int(threadIdx.x & 7) * 16;
-  o.rowstep = 64 * k * 2;
+  o.rowstep = kRows * k * 2;
   o.kel = k;
   return o;
 }
 
-// Global fragments of k-tile kt: four 16-byte chunks of each operand per lane.
-__device__ __forceinline__ void fetch(const Operands& o, int kt, u32x4 (&pa)[4], u32x4 (&pb)[4]) {
+// Global fragments of k-tile kt: kChunks 16-byte chunks of each operand per lane.
+__device__ __forceinline__ void fetch(const Operands& o, int kt, u32x4 (&pa)[kChunks], u32x4 (&pb)[kChunks]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < kChunks; ++j) {
     pa[j] = __builtin_amdgcn_raw_buffer_load_b128(o.ra, o.va, kt * BK * 2 + j * o.rowstep, 0);
     pb[j] = __builtin_amdgcn_raw_buffer_load_b128(o.rb, o.va, kt * BK * 2 + j * o.rowstep, 0);
   }
@@ -318,74 +327,88 @@ __device__ __forceinline__ void fetch(const Operands& o, int kt, u32x4 (&pa)[4],
 
 // Lane addresses in the LDS ring, built once per workgroup (see opaque()).
 struct Lanes {
-  lds_byte* a_rd;  // A fragment row wm*128 + lane%32, k half lane/32
-  lds_byte* b_rd;  // B fragment row wn*64 + lane%32, k half lane/32
-  lds_byte* a_wr;  // staging row tid/8, chunk tid%8 of A
-  lds_byte* b_wr;  // same of B
+  lds_byte* a_rd;     // A fragment row wm*128 + lane%32, k half lane/32
+  lds_byte* b_rd;     // B fragment row wn*(BN/WN) + lane%32, k half lane/32
+  lds_byte* a_wr[2];  // staging row tid/8, chunk tid%8 of A, per buffer
+  lds_byte* b_wr[2];  // same of B
 };
 
 __device__ __forceinline__ Lanes make_lanes(uint8_t* ring) {
   lds_byte* base = (lds_byte*)ring;
   const int w = int(threadIdx.x) / kWave, l = int(threadIdx.x) % kWave, lr = l & 31, hi = l >> 5;
-  const int wm = w >> 2, wn = w & 3;
+  const int wm = w / WN, wn = w % WN;
+  const int wr = int(threadIdx.x >> 3) * kPitch + int(threadIdx.x & 7) * 16;
   Lanes ln;
   ln.a_rd = opaque(base + (wm * 128 + lr) * kPitch + hi * 16);
-  ln.b_rd = opaque(base + kBOffset + (wn * 64 + lr) * kPitch + hi * 16);
-  ln.a_wr = opaque(base + int(threadIdx.x >> 3) * kPitch + int(threadIdx.x & 7) * 16);
-  ln.b_wr = opaque(base + kBOffset + int(threadIdx.x >> 3) * kPitch + int(threadIdx.x & 7) * 16);
+  ln.b_rd = opaque(base + kBOffset + (wn * (BN / WN) + lr) * kPitch + hi * 16);
+  ln.a_wr[0] = opaque(base + wr);
+  ln.b_wr[0] = opaque(base + kBOffset + wr);
+  if constexpr ((kChunks - 1) * kRows * kPitch + kTileBytes < 65536) {
+    // Buffer 1's stores fit in the immediate offset of buffer 0's address.
+    ln.a_wr[1] = ln.a_wr[0] + kTileBytes;
+    ln.b_wr[1] = ln.b_wr[0] + kTileBytes;
+  } else {
+    ln.a_wr[1] = opaque(base + kTileBytes + wr);
+    ln.b_wr[1] = opaque(base + kBOffset + kTileBytes + wr);
+  }
   return ln;
 }
 
 // Write k-tile kt's fragments to LDS buffer BUF; in a k-tile that runs past
 // the reduction length the chunks at or beyond it become zero.
 template <int BUF>
-__device__ __forceinline__ void stage(const Lanes& ln, const Operands& o, int kt, u32x4 (&pa)[4], u32x4 (&pb)[4]) {
+__device__ __forceinline__ void stage(const Lanes& ln, const Operands& o, int kt, u32x4 (&pa)[kChunks],
+                                      u32x4 (&pb)[kChunks]) {
   const int left = o.kel - kt * BK;
   if (left < BK) {
     const bool keep = int(threadIdx.x & 7) * 8 < left;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kChunks; ++j) {
       pa[j] = keep ? pa[j] : u32x4{0u, 0u, 0u, 0u};
       pb[j] = keep ? pb[j] : u32x4{0u, 0u, 0u, 0u};
     }
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    *reinterpret_cast<lds_u32x4*>(ln.a_wr + BUF * kTileBytes + j * 64 * kPitch) = pa[j];
-    *reinterpret_cast<lds_u32x4*>(ln.b_wr + BUF * kTileBytes + j * 64 * kPitch) = pb[j];
+  for (int j = 0; j < kChunks; ++j) {
+    *reinterpret_cast<lds_u32x4*>(ln.a_wr[BUF] + j * kRows * kPitch) = pa[j];
+    *reinterpret_cast<lds_u32x4*>(ln.b_wr[BUF] + j * kRows * kPitch) = pb[j];
   }
 }
 
 // Operand fragments of k16 step st from buffer BUF: A rows wm*128 + 32i +
-// lane%32, B rows wn*64 + 32j + lane%32, k = 16 st + 8 (lane / 32) + 0..7.
+// lane%32, B rows wn*(BN/WN) + 32j + lane%32, k = 16 st + 8 (lane / 32) + 0..7.
 template <int BUF>
-__device__ __forceinline__ void read_frags(const Lanes& ln, int st, u32x4 (&fa)[4], u32x4 (&fb)[2]) {
+__device__ __forceinline__ void read_frags(const Lanes& ln, int st, u32x4 (&fa)[4], u32x4 (&fb)[TJ]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     fa[i] = *reinterpret_cast<const lds_u32x4*>(ln.a_rd + BUF * kTileBytes + i * 32 * kPitch + st * 32);
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < TJ; ++j)
     fb[j] = *reinterpret_cast<const lds_u32x4*>(ln.b_rd + BUF * kTileBytes + j * 32 * kPitch + st * 32);
 }
 
-__device__ __forceinline__ void mma_step(const u32x4 (&fa)[4], const u32x4 (&fb)[2], f32x16 (&acc)[4][2]) {
+__device__ __forceinline__ void mma_step(const u32x4 (&fa)[4], const u32x4 (&fb)[TJ], f32x16 (&acc)[4][TJ]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TJ; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[i]),
                                                           __builtin_bit_cast(bf16x8, fb[j]), acc[i][j], 0, 0, 0);
 }
 
-// One k-tile from LDS buffer BUF: four k16 steps, each step's fragments read
-// while the previous step multiplies.  The scheduling fences keep the reads
-// ahead of the previous step's products instead of letting them sink next to
-// their first use.
+// One k-tile in software-pipelined form.  On entry tile k sits in LDS buffer
+// BUF and its k16 steps 0 and 1 are in (fa0, fb0) and (fa1, fb1); the global
+// fragments of tile k+1 are in (pa, pb).  The fetch of tile k+2 goes to
+// (qa, qb).  Steps 2 and 3 are read while steps 0 and 1 multiply, tile k+1 is
+// written to the other buffer while step 1 multiplies, and the barrier falls
+// between steps 2 and 3, so step 3's products cover the barrier and the first
+// reads of tile k+1.  On exit the invariant holds for tile k+1.
 template <int BUF>
-__device__ __forceinline__ void multiply_tile(const Lanes& ln, f32x16 (&acc)[4][2]) {
-  u32x4 fa0[4], fb0[2], fa1[4], fb1[2];
-  read_frags<BUF>(ln, 0, fa0, fb0);
-  read_frags<BUF>(ln, 1, fa1, fb1);
+__device__ __forceinline__ void k_step(const Operands& o, const Lanes& ln, int k1, int k2, u32x4 (&pa)[kChunks],
+                                       u32x4 (&pb)[kChunks], u32x4 (&qa)[kChunks], u32x4 (&qb)[kChunks],
+                                       u32x4 (&fa0)[4], u32x4 (&fb0)[TJ], u32x4 (&fa1)[4], u32x4 (&fb1)[TJ],
+                                       f32x16 (&acc)[4][TJ]) {
+  fetch(o, k2, qa, qb);
   __builtin_amdgcn_sched_barrier(0);
   mma_step(fa0, fb0, acc);
   __builtin_amdgcn_sched_barrier(0);
@@ -395,36 +418,37 @@ __device__ __forceinline__ void multiply_tile(const Lanes& ln, f32x16 (&acc)[4][
   __builtin_amdgcn_sched_barrier(0);
   read_frags<BUF>(ln, 3, fa1, fb1);
   __builtin_amdgcn_sched_barrier(0);
+  stage<1 - BUF>(ln, o, k1, pa, pb);
+  __builtin_amdgcn_sched_barrier(0);
   mma_step(fa0, fb0, acc);
   __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  read_frags<1 - BUF>(ln, 0, fa0, fb0);
+  __builtin_amdgcn_sched_barrier(0);
   mma_step(fa1, fb1, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags<1 - BUF>(ln, 1, fa1, fb1);
 }
 
 // acc += A[rows, kb*64 : ke*64] . B[rows, same]^T.  Leaves the LDS ring free.
-__device__ __forceinline__ void k_loop(const Operands& o, int kb, int ke, f32x16 (&acc)[4][2], const Lanes& ln) {
+__device__ __forceinline__ void k_loop(const Operands& o, int kb, int ke, f32x16 (&acc)[4][TJ], const Lanes& ln) {
   const int n = ke - kb;
-  u32x4 pa0[4], pb0[4], pa1[4], pb1[4];
+  u32x4 pa0[kChunks], pb0[kChunks], pa1[kChunks], pb1[kChunks];
+  u32x4 fa0[4], fb0[TJ], fa1[4], fb1[TJ];
   fetch(o, kb, pa0, pb0);
   fetch(o, min(kb + 1, ke - 1), pa1, pb1);
   stage<0>(ln, o, kb, pa0, pb0);
   __syncthreads();
+  read_frags<0>(ln, 0, fa0, fb0);
+  read_frags<0>(ln, 1, fa1, fb1);
   for (int k = 0; k < n; k += 2) {
-    const int k1 = min(kb + k + 1, ke - 1), k2 = min(kb + k + 2, ke - 1), k3 = min(kb + k + 3, ke - 1);
-    fetch(o, k2, pa0, pb0);
-    __builtin_amdgcn_sched_barrier(0);
-    multiply_tile<0>(ln, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    stage<1>(ln, o, k1, pa1, pb1);
-    __syncthreads();
-    if (k + 1 < n) {
-      fetch(o, k3, pa1, pb1);
-      __builtin_amdgcn_sched_barrier(0);
-      multiply_tile<1>(ln, acc);
-      __builtin_amdgcn_sched_barrier(0);
-      stage<0>(ln, o, k2, pa0, pb0);
-      __syncthreads();
-    }
+    // Tiles past the end are fetched, staged and read again as the last
+    // tile (clamped), and never multiplied.
+    k_step<0>(o, ln, min(kb + k + 1, ke - 1), min(kb + k + 2, ke - 1), pa1, pb1, pa0, pb0, fa0, fb0, fa1, fb1, acc);
+    if (k + 1 < n)
+      k_step<1>(o, ln, min(kb + k + 2, ke - 1), min(kb + k + 3, ke - 1), pa0, pb0, pa1, pb1, fa0, fb0, fa1, fb1, acc);
   }
+  __syncthreads();
 }
 
 // Tile u of the processing order -> (token tile, output tile): groups of
@@ -437,44 +461,38 @@ __device__ __forceinline__ void tile_coords(const Args& a, int u, int& tm, int& 
   tn = r / gsize;
 }
 
-// Partial slot of stream-K position p for tile u: 0 for the tile its range
-// starts in, 1 for the tile it ends in.
-__device__ __forceinline__ int part_slot(const Args& a, int p, int u) {
-  return 2 * p + (p * a.ipw < u * a.KT ? 1 : 0);
-}
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const Args& a, int slot) {
   return __builtin_amdgcn_make_buffer_rsrc(a.part + size_t(slot) * kPartFloats, 0, kPartFloats * 4, kRsrcFlags);
 }
 
 // Partials are laid out as the accumulators sit in registers: 16-byte piece
-// q = (2i + j) * 4 + c of every lane, lanes contiguous.
-__device__ __forceinline__ void store_partial(const Args& a, int slot, const f32x16 (&acc)[4][2]) {
+// q = (TJ i + j) * 4 + c of every lane, lanes contiguous.
+__device__ __forceinline__ void store_partial(const Args& a, int slot, const f32x16 (&acc)[4][TJ]) {
   const __amdgpu_buffer_rsrc_t rs = part_rsrc(a, slot);
   const int lane_off = int(threadIdx.x) * 16;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const u32x4 v = {__float_as_uint(acc[i][j][4 * c]), __float_as_uint(acc[i][j][4 * c + 1]),
                          __float_as_uint(acc[i][j][4 * c + 2]), __float_as_uint(acc[i][j][4 * c + 3])};
-        __builtin_amdgcn_raw_buffer_store_b128(v, rs, lane_off, ((i * 2 + j) * 4 + c) * kThreads * 16, kCoherent);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs, lane_off, ((i * TJ + j) * 4 + c) * kThreads * 16, kCoherent);
       }
 }
 
 // acc = partial (first) or acc += partial.
-__device__ __forceinline__ void add_partial(const Args& a, int slot, bool first, f32x16 (&acc)[4][2]) {
+__device__ __forceinline__ void add_partial(const Args& a, int slot, bool first, f32x16 (&acc)[4][TJ]) {
   const __amdgpu_buffer_rsrc_t rs = part_rsrc(a, slot);
   const int lane_off = int(threadIdx.x) * 16;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off, ((i * 2 + j) * 4 + c) * kThreads * 16,
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off, ((i * TJ + j) * 4 + c) * kThreads * 16,
                                                               kCoherent);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -483,12 +501,12 @@ __device__ __forceinline__ void add_partial(const Args& a, int slot, bool first,
 }
 
 // Scale by s, add T . U^T, round to bf16 and store.
-__device__ __forceinline__ void finish_tile(const Args& a, int m0, int n0, f32x16 (&acc)[4][2], const Lanes& ln) {
+__device__ __forceinline__ void finish_tile(const Args& a, int m0, int n0, f32x16 (&acc)[4][TJ], const Lanes& ln) {
   const int w = int(threadIdx.x) / kWave, l = int(threadIdx.x) % kWave, lr = l & 31, hi = l >> 5;
-  const int wm = w >> 2, wn = w & 3;
+  const int wm = w / WN, wn = w % WN;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + wn * 64 + j * 32 + lr;
+  for (int j = 0; j < TJ; ++j) {
+    const int n = n0 + wn * (BN / WN) + j * 32 + lr;
     const float sc = n < a.O ? bf16_to_f32(a.s[n].bits) : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i][j] *= sc;
@@ -500,8 +518,8 @@ __device__ __forceinline__ void finish_tile(const Args& a, int m0, int n0, f32x1
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn * 64 + j * 32 + lr;
+    for (int j = 0; j < TJ; ++j) {
+      const int n = n0 + wn * (BN / WN) + j * 32 + lr;
       if (n >= a.O) continue;
 #pragma unroll
       for (int b = 0; b < 4; ++b)
@@ -515,51 +533,48 @@ __device__ __forceinline__ void finish_tile(const Args& a, int m0, int n0, f32x1
 
 // k-tiles [kb, ke) of tile u; finishes the tile if it holds the whole
 // reduction or arrives last among the tile's workgroups.
-__device__ __forceinline__ void do_tile(const Args& a, int u, int kb, int ke, int pos, const Lanes& ln,
+// k-tiles [kb, ke) of tile u: the whole reduction (slice < 0) or k-slice
+// `slice`; finishes the tile if it holds the whole reduction or is the last
+// of the tile's slices to arrive.
+__device__ __forceinline__ void do_tile(const Args& a, int u, int kb, int ke, int slice, const Lanes& ln,
                                         unsigned* s_last) {
   int tm, tn;
   tile_coords(a, u, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  f32x16 acc[4][2];
+  f32x16 acc[4][TJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
   k_loop(make_operands(a.x, a.M, a.w0, a.O, m0, n0, a.I), kb, ke, acc, ln);
-  if (kb > 0 || ke < a.KT) {
-    const int first = (u * a.KT) / a.ipw, last = (u * a.KT + a.KT - 1) / a.ipw;
-    store_partial(a, part_slot(a, pos, u), acc);
+  if (slice >= 0) {
+    store_partial(a, slice * a.split_tiles + u, acc);
     __builtin_amdgcn_s_waitcnt(0);  // partial written through before counting in
     __syncthreads();
     if (threadIdx.x == 0)
       *s_last = __hip_atomic_fetch_add(&a.ctrl[kCounterBase + u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                unsigned(last - first);
+                unsigned(a.S - 1);
     __syncthreads();
     if (!*s_last) return;
-    for (int q = first; q <= last; ++q) add_partial(a, part_slot(a, q, u), q == first, acc);
+    for (int q = 0; q < a.S; ++q) add_partial(a, q * a.split_tiles + u, q == 0, acc);
     if (threadIdx.x == 0)
       __hip_atomic_store(&a.ctrl[kCounterBase + u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   finish_tile(a, m0, n0, acc, ln);
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void gemm_kernel(Args a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4))) void gemm_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes];
   __shared__ unsigned s_last;
   const int g = int(blockIdx.x), G = int(gridDim.x);
   const int pos = a.xcd_major ? (g % 8) * (G / 8) + g / 8 : g;
   const Lanes ln = make_lanes(ring);
-  if (a.sk_tiles > 0) {
-    const int total = a.sk_tiles * a.KT;
-    const int end = min(total, (pos + 1) * a.ipw);
-    for (int it = pos * a.ipw; it < end;) {
-      const int u = it / a.KT, kb = it - u * a.KT, ke = min(a.KT, kb + (end - it));
-      do_tile(a, u, kb, ke, pos, ln, &s_last);
-      it += ke - kb;
-    }
+  for (int v = pos; v < a.split_tiles * a.S; v += G) {
+    const int u = v % a.split_tiles, slice = v / a.split_tiles;
+    do_tile(a, u, slice * a.kps, min(a.KT, (slice + 1) * a.kps), slice, ln, &s_last);
   }
   const int tiles = a.tiles_m * a.tiles_n;
-  for (int u = a.sk_tiles + pos; u < tiles; u += G) do_tile(a, u, 0, a.KT, pos, ln, &s_last);
+  for (int u = a.split_tiles + pos; u < tiles; u += G) do_tile(a, u, 0, a.KT, -1, ln, &s_last);
 }
 
 }  // namespace big
@@ -824,10 +839,11 @@ __global__ __launch_bounds__(kThreads) void xv_kernel(Args a) {
 
 namespace {
 
-// Cost model of the stream-K plan, in k-tiles of one workgroup: storing a
-// 256 x 256 fp32 partial and reading one back each cost about as much as a
-// few k-tiles of multiplication.
-constexpr int kStoreCost = 6, kLoadCost = 4;
+// Cost model of the split remainder round, in k-tiles of one workgroup:
+// storing a 256 x 256 fp32 partial and reading one back each cost about as
+// much as a few k-tiles of multiplication; slices shorter than kMinSlice
+// k-tiles are not worth their partials.
+constexpr int kStoreCost = 6, kLoadCost = 4, kMinSlice = 4;
 
 }  // namespace
 
@@ -866,37 +882,30 @@ GemmPlan plan_gemm(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int
   const int G = cus >= 8 ? cus / 8 * 8 : cus;
   const auto round8 = [&](int64_t g) { return int(cus >= 8 ? std::min<int64_t>(G, (g + 7) / 8 * 8) : std::min<int64_t>(G, g)); };
 
-  // Data-parallel: whole tiles, ceil(tiles / G) rounds.
+  // Whole tiles in ceil(tiles / G) rounds ...
   int64_t best = (tiles + G - 1) / G * KT;
   p.grid = round8(tiles);
-  p.sk_tiles = 0;
-  p.ipw = 0;
-  // Stream-K over the leading sk tiles, the rest in whole rounds.
+  p.split_tiles = 0;
+  p.S = 1;
+  p.kps = p.KT;
+  // ... or the whole rounds plus the remainder tiles split into S k-slices,
+  // all slices in one extra round.
   const int64_t rounds = tiles / G, rem = tiles % G;
-  if (rem != 0) {
-    const int64_t cands[2] = {rem, rounds > 0 ? rem + G : -1};
-    for (int64_t sk : cands) {
-      if (sk <= 0 || sk > kMaxGroupCounters) continue;
-      for (int div = 1; div <= 8; div *= 2) {
-        // Without whole rounds the grid may shrink so partials stay large.
-        if (div > 1 && sk != tiles) break;
-        const int grid = round8((G + div - 1) / div);
-        const int64_t ipw = (sk * KT + grid - 1) / grid;
-        if (ipw < 1) continue;
-        const int64_t segs = (KT - 1 + ipw - 1) / ipw + 1;
-        const int64_t cost = (tiles - sk) / G * KT + ipw + kStoreCost + kLoadCost * segs;
-        if (cost < best) {
-          best = cost;
-          p.grid = sk == tiles ? grid : G;
-          p.sk_tiles = int(sk);
-          p.ipw = int(ipw);
-        }
-      }
+  for (int64_t S = 2; rem != 0 && S <= 16 && rem * S <= G; ++S) {
+    const int64_t kps = (KT + S - 1) / S, slices = (KT + kps - 1) / kps;
+    if (kps < kMinSlice) break;
+    const int64_t cost = rounds * KT + kps + kStoreCost + kLoadCost * slices;
+    if (cost < best && rem <= kMaxGroupCounters) {
+      best = cost;
+      p.split_tiles = int(rem);
+      p.S = int(slices);
+      p.kps = int(kps);
+      p.grid = rounds > 0 ? G : round8(rem * slices);
     }
   }
   p.xcd_major = p.grid % 8 == 0 ? 1 : 0;
   p.off_part = off_big;
-  if (p.sk_tiles > 0) p.bytes = off_big + size_t(2) * p.grid * big::kPartFloats * 4;
+  if (p.split_tiles > 0) p.bytes = off_big + size_t(p.split_tiles) * p.S * big::kPartFloats * 4;
   return p;
 }
 
@@ -936,7 +945,7 @@ hipError_t launch_forward_gemm(const GemmPlan& p, const void* x, const void* s, 
     a.M = int(m); a.O = int(out_dim); a.I = int(in_dim); a.R = int(rank);
     a.tiles_m = p.tiles_m; a.tiles_n = p.tiles_n;
     a.KT = p.KT; a.KR = p.KR;
-    a.sk_tiles = p.sk_tiles; a.ipw = p.ipw; a.xcd_major = p.xcd_major;
+    a.split_tiles = p.split_tiles; a.S = p.S; a.kps = p.kps; a.xcd_major = p.xcd_major;
     a.ctrl = reinterpret_cast<unsigned*>(ws);
     a.part = reinterpret_cast<float*>(ws + p.off_part);
     hipLaunchKernelGGL(big::gemm_kernel, dim3(unsigned(p.grid)), dim3(big::kThreads), 0, stream, a);

@@ -42,7 +42,8 @@ struct GemmPlan {
   int grid;             // persistent workgroups of the stream-K kernel
   int tiles_m, tiles_n; // 256 x 256 output tiles
   int KT, KR;           // k-tiles (64) of in_dim and of rank
-  int sk_tiles, ipw;    // leading tiles shared out by k-tiles, k-tiles per workgroup
+  int split_tiles;      // leading tiles split into S k-slices of kps k-tiles (the remainder round)
+  int S, kps;
   int xcd_major;        // workgroup positions spread XCD-major (grid a multiple of 8)
   int xv_rb, xv_cb;     // x . V on the aligned path: 64-token row blocks, 256-column blocks of T
   int xv_kt, xv_ks, xv_kps;  // its k-tiles (64), k-slices and k-tiles per slice
