@@ -234,7 +234,7 @@ def main():
         unit = "TFLOP/s"
         value = step_flops / (ms * 1e-3) / 1e12
         achieved = launch_flops.sum() / (per_call_ms.sum() * 1e-3) / 1e12
-        kernel = "forward_gemm_kernel (with xv_gemm_kernel in the same call)"
+        kernel = "big::gemm_kernel (with xv::xv_kernel in the same call)"
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
         per_launch = float(launch_flops.mean())

@@ -569,12 +569,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   const int g = int(blockIdx.x), G = int(gridDim.x);
   const int pos = a.xcd_major ? (g % 8) * (G / 8) + g / 8 : g;
   const Lanes ln = make_lanes(ring);
+#ifdef TB_CLOCKPROBE
+  const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+#endif
   for (int v = pos; v < a.split_tiles * a.S; v += G) {
     const int u = v % a.split_tiles, slice = v / a.split_tiles;
     do_tile(a, u, slice * a.kps, min(a.KT, (slice + 1) * a.kps), slice, ln, &s_last);
   }
   const int tiles = a.tiles_m * a.tiles_n;
   for (int u = a.split_tiles + pos; u < tiles; u += G) do_tile(a, u, 0, a.KT, -1, ln, &s_last);
+#ifdef TB_CLOCKPROBE
+  const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    unsigned* d = a.ctrl + 8192 + 4 * g;
+    __hip_atomic_store(d + 0, unsigned(c1 - c0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(d + 1, unsigned(r1 - r0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+#endif
 }
 
 }  // namespace big
@@ -852,10 +863,12 @@ GemmPlan plan_gemm(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int
   p.off_t = kControlBytes;
   const size_t off = align_up(p.off_t + size_t(m) * size_t(rank) * 2, 256);
   p.bytes = off;
-  // The stream-K kernel addresses one tile's rows with 32-bit byte offsets.
-  p.big = in_dim % 8 == 0 && rank % 8 == 0 && in_dim < (int64_t(1) << 22) && rank < (int64_t(1) << 22) &&
-          in_dim * rank < (int64_t(1) << 30);
-  if (!p.big) return p;
+  // The matrix-core kernels for 16-byte aligned rows address one tile's rows
+  // (and all of V) with 32-bit byte offsets.
+  p.aligned = in_dim % 8 == 0 && rank % 8 == 0 && in_dim < (int64_t(1) << 22) && rank < (int64_t(1) << 22) &&
+              in_dim * rank < (int64_t(1) << 30);
+  p.big = p.aligned;
+  if (!p.aligned) return p;
   // x . V: enough k-slices to give every compute unit a workgroup, each at
   // least two k-tiles long and at most 16 partials per tile.
   size_t o2 = off;
@@ -903,6 +916,12 @@ GemmPlan plan_gemm(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int
       p.grid = rounds > 0 ? G : round8(rem * slices);
     }
   }
+  // Fewer 256 x 256 tiles than half the compute units: the 128 x 128 kernel's
+  // four times as many workgroups finish sooner.
+  if (tiles < G / 2) {
+    p.big = 0;
+    p.split_tiles = 0;
+  }
   p.xcd_major = p.grid % 8 == 0 ? 1 : 0;
   p.off_part = off_big;
   if (p.split_tiles > 0) p.bytes = off_big + size_t(p.split_tiles) * p.S * big::kPartFloats * 4;
@@ -914,7 +933,7 @@ hipError_t launch_forward_gemm(const GemmPlan& p, const void* x, const void* s, 
                                void* workspace, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   bf16_t* t = reinterpret_cast<bf16_t*>(ws + p.off_t);
-  if (rank > 0 && p.big) {
+  if (rank > 0 && p.aligned) {
     xv::Args a;
     a.x = static_cast<const bf16_t*>(x);
     a.v = static_cast<const bf16_t*>(v);

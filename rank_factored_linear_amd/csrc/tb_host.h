@@ -38,7 +38,8 @@ hipError_t launch_forward_decode(const DecodePlan& p, tb_dtype dtype, const void
 
 // ---- forward, prefill token counts (bf16, m > kDecodeMaxTokens) ----------
 struct GemmPlan {
-  int big;              // 1: 256 x 256 stream-K kernel (in_dim, rank multiples of 8); 0: general kernel
+  int aligned;          // in_dim and rank multiples of 8: x . V by the transposing-read kernel
+  int big;              // 1: 256 x 256 kernel (needs aligned); 0: general 128 x 128 kernel
   int grid;             // persistent workgroups of the stream-K kernel
   int tiles_m, tiles_n; // 256 x 256 output tiles
   int KT, KR;           // k-tiles (64) of in_dim and of rank

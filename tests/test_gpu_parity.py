@@ -232,6 +232,22 @@ def test_forward_edge_shapes(shape, dtype):
     assert bool((buf[:guard] == 7.0).all()) and bool((buf[guard + M * O:] == 7.0).all())
 
 
+@pytest.mark.parametrize("shape", [(2048, 4096, 4104, 72), (4096, 4352, 4096, 64)], ids=["split_round", "rounds_and_split"])
+def test_forward_split_rounds(shape):
+    # 128 tiles of 256 x 256 split into two k-slices; and 272 tiles: one whole
+    # round plus 16 remainder tiles split into k-slices.  Sampled outputs.
+    M, O, I, R = shape
+    _say(f"split rounds {shape}")
+    x, s, W0, U, V = _rand_case(M, O, I, R, torch.bfloat16, seed=M + O)
+    y = tb.linear_forward(x, s, W0, U, V)
+    osel = torch.from_numpy(sample_rows(O, 384, seed=5)).to(DEV)
+    tsel = torch.from_numpy(sample_rows(M, 64, seed=6)).to(DEV)
+    want = oracle.forward(exact(x.index_select(0, tsel)), exact(s.index_select(0, osel)),
+                          exact(W0.index_select(0, osel)), exact(U.index_select(0, osel)), exact(V))
+    got = exact(y.index_select(0, tsel).index_select(1, osel))
+    assert oracle.relative_frobenius_error(want, got) <= BF16_TOL
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("shape", [(17, 40, 4), (130, 264, 12), (64, 512, 256), (33, 72, 0), (1, 8, 3)],
                          ids=lambda s: "x".join(map(str, s)))
