@@ -37,6 +37,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
 DECODE_MAX_TOKENS = 64
 
+# Projections of a layer that read the same input, grouped into one call.
+GROUPS = [["q_proj", "k_proj", "v_proj"], ["o_proj"], ["gate_proj", "up_proj"], ["down_proj"]]
+
 WORKLOADS = {
     "large60": dict(layers=60, shapes="SHAPES_60", rank=256, bands=6, tokens=16, seed=4),
     "banded26": dict(layers=26, shapes="SHAPES_26", rank=128, bands=4, tokens=4, seed=3),
@@ -53,6 +56,8 @@ def parse():
     ap.add_argument("--tokens", type=int, default=None)
     ap.add_argument("--bands", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-group", action="store_true",
+                    help="one tb_linear_forward call per projection instead of grouping q/k/v and gate/up")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the oracle timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain device copies of a known size (scales the HBM byte counters)")
@@ -156,42 +161,68 @@ def main():
                 bundles[(l, fam)] = gen.device_bundle(torch, wl["seed"], fam, shapes, l, band_of[l], R, with_w0=False)
             xs[(l, fam)] = gen.device_activations(torch, wl["seed"], fam, shapes, l, M)
     ys = {fam: torch.empty((M, shapes[fam][0]), dtype=torch.bfloat16, device=dev) for fam in gen.FAMILIES}
-    need = max(tb.linear_forward_workspace_size(M, *shapes[f], R, torch.bfloat16) for f in gen.FAMILIES)
-    ws = tb.workspace_for(need)
+    # Projections that take the same layer input go in one grouped call.
+    groups = [[f] for f in gen.FAMILIES] if args.no_group else GROUPS
+    ws_need = []
+    for grp in groups:
+        dims = (tb.Projection * len(grp))(*[tb.Projection(None, None, None, None, None, None, *shapes[f], R)
+                                            for f in grp])
+        nb = ctypes.c_size_t(0)
+        assert tb.lib.tb_linear_forward_group_workspace_size(len(grp), dims, M, tb.TB_BF16, ctypes.byref(nb)) == 0
+        ws_need.append(nb.value)
+    ws = tb.workspace_for(max(ws_need))
     torch.cuda.synchronize()
     t_setup = time.time() - t_setup
 
     # Prepared argument tuples: the timed loop only crosses the C ABI.
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    calls = []
-    for l in range(L):
-        for fam in gen.FAMILIES:
-            O, I = shapes[fam]
-            bd = bundles[(l, fam)]
-            u = bd["U"].data_ptr() if R else None
-            v = bd["V"].data_ptr() if R else None
-            calls.append((l, fam, (xs[(l, fam)].data_ptr(), bd["s"].data_ptr(), W0[(band_of[l], fam)].data_ptr(), u, v,
-                                   ys[fam].data_ptr(), M, O, I, R, tb.TB_BF16, ws.data_ptr(), ws.numel(), stream)))
     fwd = tb.lib.tb_linear_forward
+    fwd_group = tb.lib.tb_linear_forward_group
+    calls = []   # (layer, families, function, argument tuple)
+    for l in range(L):
+        for grp in groups:
+            members = []
+            for fam in grp:
+                bd = bundles[(l, fam)]
+                members.append((xs[(l, fam)], bd["s"], W0[(band_of[l], fam)], bd["U"] if R else None,
+                                bd["V"] if R else None, ys[fam]))
+            if len(grp) == 1:
+                x, s_, w0, u, v, y = members[0]
+                O, I = shapes[grp[0]]
+                argv = (x.data_ptr(), s_.data_ptr(), w0.data_ptr(), u.data_ptr() if R else None,
+                        v.data_ptr() if R else None, y.data_ptr(), M, O, I, R, tb.TB_BF16, ws.data_ptr(), ws.numel(),
+                        stream)
+                calls.append((l, grp, fwd, argv))
+            else:
+                arr = tb.projection_array(members)
+                calls.append((l, grp, fwd_group, (len(grp), arr, M, tb.TB_BF16, ws.data_ptr(), ws.numel(), stream)))
     band_idx = tb.lib.tb_band_index
     bout = ctypes.c_int32()
+    per_layer = len(groups)
 
     def step(events=None):
         n = 0
         for l in range(L):
             band_idx(L, G, l, ctypes.byref(bout))          # band select (host)
-            for fam in gen.FAMILIES:
+            for _ in range(per_layer):
                 if events is not None:
                     events[n].record()
-                st = fwd(*calls[n][2])
+                fn, argv = calls[n][2], calls[n][3]
+                st = fn(*argv)
                 if st:
                     raise RuntimeError(tb.lib.tb_last_error().decode())
                 n += 1
         if events is not None:
             events[n].record()
 
-    step_bytes = sum(call_bytes(M, *shapes[f], R) for _, f, _ in calls)
-    step_flops = sum(call_flops(M, *shapes[f], R) for _, f, _ in calls)
+    def grp_bytes(grp):
+        return sum(call_bytes(M, *shapes[f], R) for f in grp)
+
+    def grp_flops(grp):
+        return sum(call_flops(M, *shapes[f], R) for f in grp)
+
+    step_bytes = sum(grp_bytes(c[1]) for c in calls)
+    step_flops = sum(grp_flops(c[1]) for c in calls)
     decode = M <= DECODE_MAX_TOKENS
 
     for _ in range(args.warmup):
@@ -219,8 +250,8 @@ def main():
         torch.cuda.synchronize()
         per_call_ms += np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(len(calls))])
     per_call_ms /= args.steps
-    launch_bytes = np.array([call_bytes(M, *shapes[f], R) for _, f, _ in calls], dtype=np.float64)
-    launch_flops = np.array([call_flops(M, *shapes[f], R) for _, f, _ in calls], dtype=np.float64)
+    launch_bytes = np.array([grp_bytes(c[1]) for c in calls], dtype=np.float64)
+    launch_flops = np.array([grp_flops(c[1]) for c in calls], dtype=np.float64)
 
     if decode:
         unit = "GB/s"
@@ -239,7 +270,7 @@ def main():
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
         per_launch = float(launch_flops.mean())
     roof["kernel"] = kernel
-    roof["launches_per_step"] = len(calls)
+    roof["calls_per_step"] = len(calls)
     roof["avg_launch_us"] = round(float(per_call_ms.mean()) * 1e3, 2)
     roof["algorithmic_per_launch"] = round(per_launch, 1)
     tag = f"{args.workload}_M{M}_G{G}"
@@ -266,7 +297,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {L}-layer stack, 7 projections per layer, rank {R}, "
                                f"G={G} bands, {M} tokens",
-                   "layers": L, "projections_per_step": len(calls), "rank": R, "bands": G, "tokens": M,
+                   "layers": L, "projections_per_step": L * len(gen.FAMILIES),
+                   "grouping": "+".join(",".join(f.split("_")[0] for f in g) for g in groups),
+                   "rank": R, "bands": G, "tokens": M,
                    "hidden": shapes["q_proj"][1], "mlp": shapes["gate_proj"][0],
                    "step_bytes": step_bytes, "step_flops": step_flops, "parallelism": "single-gpu"},
         "roofline": roof,
@@ -295,7 +328,7 @@ def cpu_baseline(args, wl, shapes, calls, bundles, W0, xs, band_of, passthrough,
     M, R = wl["tokens"], wl["rank"]
     Mc = M if decode else min(M, 256)       # prefill: a token slice keeps it bounded
     done_bytes, done_flops, secs, used = 0, 0, 0.0, []
-    for l, fam, _ in calls:
+    for l, fam in ((c[0], f) for c in calls for f in c[1]):
         if secs > args.cpu_seconds:
             break
         O, I = shapes[fam]

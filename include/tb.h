@@ -50,8 +50,12 @@ typedef enum tb_dtype {
   TB_BF16 = 1  /* bfloat16, round-to-nearest-even on every store */
 } tb_dtype;
 
-/* Leading bytes of a forward workspace that hold control words. */
-#define TB_WORKSPACE_CONTROL_BYTES 65536
+/* Most projections one tb_linear_forward_group call takes. */
+#define TB_MAX_GROUP 8
+
+/* Leading bytes of a forward workspace that hold control words: one block of
+ * 64 KiB for each member a grouped call may have (a single call uses block 0). */
+#define TB_WORKSPACE_CONTROL_BYTES (TB_MAX_GROUP * 65536)
 
 /* Fixed workspace size of tb_rel_frobenius_error. */
 #define TB_FROBENIUS_WORKSPACE_BYTES 65536
@@ -105,15 +109,58 @@ tb_status tb_linear_forward_workspace_size(int64_t m, int64_t out_dim, int64_t i
  *   bytes, 256-byte aligned.  Its first TB_WORKSPACE_CONTROL_BYTES bytes are
  *   control words: they must be zero before the first call that uses the
  *   buffer and must not be changed by the caller afterwards (each completed
- *   call leaves them ready for the next; word 2 is a sticky error flag that
- *   becomes nonzero only if a bounded internal wait timed out, in which case
- *   that call's y is NaN).  Calls that may run at the same time (different
- *   streams) must not share a workspace.
+ *   call, single or grouped, leaves all of them ready for the next; word 2 is
+ *   a sticky error flag that becomes nonzero only if a bounded internal wait
+ *   timed out, in which case that call's y is NaN).  Calls that may run at
+ *   the same time (different streams) must not share a workspace.
  *   Errors: TB_ERR_INVALID_ARGUMENT, TB_ERR_UNSUPPORTED, TB_ERR_HIP.
  */
 tb_status tb_linear_forward(const void *x, const void *s, const void *w0, const void *u, const void *v,
                             void *y, int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
                             tb_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One projection of a group: the arguments of tb_linear_forward that may
+ * differ between its members (same meaning, layout and alignment rules).
+ */
+typedef struct tb_projection {
+  const void *x;
+  const void *s;
+  const void *w0;
+  const void *u;
+  const void *v;
+  void *y;
+  int64_t out_dim, in_dim, rank;
+} tb_projection;
+
+/*
+ * tb_linear_forward_group_workspace_size -- bytes of workspace
+ * tb_linear_forward_group needs for these projections (only their out_dim,
+ * in_dim and rank are read) at m tokens: the control bytes plus each
+ * member's buffers.
+ */
+tb_status tb_linear_forward_group_workspace_size(int32_t n, const tb_projection *projs, int64_t m, tb_dtype dtype,
+                                                 size_t *bytes_out);
+
+/*
+ * tb_linear_forward_group -- n independent theta-bundle projections (the
+ * computation of tb_linear_forward for each member, same results bit for
+ * bit) over the same token count m and dtype.  Layers apply several
+ * projections to one input (q/k/v, gate/up); each member still names its own
+ * x, which may be shared.  For m <= 64 the members whose launch plans agree
+ * run in one launch, so the fixed cost of a launch and the wait for x . V
+ * are paid once; other cases run the members one after another.
+ *   n: 1 .. TB_MAX_GROUP.  projs: host array of n members (no y may alias
+ *   any member's input or another member's y).
+ *   workspace: as for tb_linear_forward, at least
+ *   tb_linear_forward_group_workspace_size() bytes; member j uses control
+ *   block j and its own buffers after the control bytes.  A timed-out wait
+ *   in any member sets word 2 of the workspace.
+ *   Errors: TB_ERR_INVALID_ARGUMENT, TB_ERR_UNSUPPORTED, TB_ERR_HIP; a
+ *   member that fails validation fails the call before anything is launched.
+ */
+tb_status tb_linear_forward_group(int32_t n, const tb_projection *projs, int64_t m, tb_dtype dtype, void *workspace,
+                                  size_t workspace_bytes, void *stream);
 
 /*
  * tb_reconstruct_weight -- w_out = diag(s) . W0 + U . V^T ("The theta bundle",

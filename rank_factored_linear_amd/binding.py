@@ -19,13 +19,22 @@ LIB_PATH = os.path.join(_PKG, "libtb.so")
 
 TB_OK, TB_ERR_INVALID_ARGUMENT, TB_ERR_UNSUPPORTED, TB_ERR_HIP = 0, 1, 2, 3
 TB_F32, TB_BF16 = 0, 1
-WORKSPACE_CONTROL_BYTES = 65536
+MAX_GROUP = 8
+WORKSPACE_CONTROL_BYTES = MAX_GROUP * 65536
 FROBENIUS_WORKSPACE_BYTES = 65536
 
 EXPORTED = (
     "tb_band_index", "tb_linear_forward_workspace_size", "tb_linear_forward",
+    "tb_linear_forward_group_workspace_size", "tb_linear_forward_group",
     "tb_reconstruct_weight", "tb_rel_frobenius_error", "tb_status_string", "tb_last_error",
 )
+
+
+class Projection(ctypes.Structure):
+    """tb_projection: one member of a grouped forward call."""
+    _fields_ = [("x", ctypes.c_void_p), ("s", ctypes.c_void_p), ("w0", ctypes.c_void_p), ("u", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("y", ctypes.c_void_p), ("out_dim", ctypes.c_int64),
+                ("in_dim", ctypes.c_int64), ("rank", ctypes.c_int64)]
 
 
 class TBError(RuntimeError):
@@ -42,6 +51,9 @@ def _load() -> ctypes.CDLL:
     lib.tb_band_index.argtypes = [c_i32, c_i32, c_i32, ctypes.POINTER(c_i32)]
     lib.tb_linear_forward_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_i64, ctypes.c_int, ctypes.POINTER(c_sz)]
     lib.tb_linear_forward.argtypes = [c_p, c_p, c_p, c_p, c_p, c_p, c_i64, c_i64, c_i64, c_i64, ctypes.c_int, c_p, c_sz, c_p]
+    lib.tb_linear_forward_group_workspace_size.argtypes = [c_i32, ctypes.POINTER(Projection), c_i64, ctypes.c_int,
+                                                           ctypes.POINTER(c_sz)]
+    lib.tb_linear_forward_group.argtypes = [c_i32, ctypes.POINTER(Projection), c_i64, ctypes.c_int, c_p, c_sz, c_p]
     lib.tb_reconstruct_weight.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i64, c_i64, c_i64, ctypes.c_int, ctypes.c_int, c_p]
     lib.tb_rel_frobenius_error.argtypes = [c_p, c_p, c_i64, c_i64, ctypes.c_int, c_p, c_p, c_sz, c_p]
     lib.tb_status_string.argtypes = [ctypes.c_int]
@@ -49,6 +61,7 @@ def _load() -> ctypes.CDLL:
     lib.tb_last_error.argtypes = []
     lib.tb_last_error.restype = ctypes.c_char_p
     for name in ("tb_band_index", "tb_linear_forward_workspace_size", "tb_linear_forward",
+                 "tb_linear_forward_group_workspace_size", "tb_linear_forward_group",
                  "tb_reconstruct_weight", "tb_rel_frobenius_error"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
@@ -160,6 +173,44 @@ def linear_forward(x: torch.Tensor, s: torch.Tensor, W0: torch.Tensor, U: torch.
     _check(lib.tb_linear_forward(_ptr(x), _ptr(s), _ptr(W0), _ptr(U), _ptr(V), _ptr(out), m, out_dim, in_dim, rank,
                                  dt, _ptr(ws), ws.numel() * ws.element_size(), _stream()))
     return out
+
+
+def projection_array(members) -> ctypes.Array:
+    """tb_projection array for (x, s, W0, U, V, y) tuples (U, V may be None)."""
+    arr = (Projection * len(members))()
+    for j, (x, s, W0, U, V, y) in enumerate(members):
+        rank = 0 if U is None else U.shape[1]
+        arr[j] = Projection(_ptr(x), _ptr(s), _ptr(W0), _ptr(U) if rank else None, _ptr(V) if rank else None, _ptr(y),
+                            W0.shape[0], W0.shape[1], rank)
+    return arr
+
+
+def linear_forward_group(members, workspace: torch.Tensor | None = None) -> list:
+    """Several independent projections [(x, s, W0, U, V), ...] of one token count and dtype in one call
+    (tb_linear_forward_group); returns their outputs."""
+    if not 1 <= len(members) <= MAX_GROUP:
+        raise TBError(TB_ERR_INVALID_ARGUMENT, f"a group holds 1..{MAX_GROUP} projections")
+    m = members[0][0].shape[0]
+    dtype = members[0][0].dtype
+    full = []
+    for x, s, W0, U, V in members:
+        _need_cuda(x, s, W0, U, V)
+        if x.shape[0] != m or x.dtype != dtype:
+            raise TBError(TB_ERR_INVALID_ARGUMENT, "group members must share the token count and dtype")
+        for t in (s, W0, U, V):
+            if t is not None and t.dtype != dtype:
+                raise TBError(TB_ERR_INVALID_ARGUMENT, "all inputs must share one dtype")
+        if U is not None and U.shape[1] == 0:
+            U = V = None
+        y = torch.empty((m, W0.shape[0]), dtype=dtype, device=x.device)
+        full.append((x, s, W0, U, V, y))
+    arr = projection_array(full)
+    need = ctypes.c_size_t(0)
+    _check(lib.tb_linear_forward_group_workspace_size(len(full), arr, m, _dtype_code(dtype), ctypes.byref(need)))
+    ws = workspace if workspace is not None else workspace_for(need.value)
+    _check(lib.tb_linear_forward_group(len(full), arr, m, _dtype_code(dtype), _ptr(ws), ws.numel() * ws.element_size(),
+                                       _stream()))
+    return [f[5] for f in full]
 
 
 def reconstruct_weight(s: torch.Tensor, W0: torch.Tensor, U: torch.Tensor | None, V: torch.Tensor | None,

@@ -105,43 +105,55 @@ tb_status tb_linear_forward_workspace_size(int64_t m, int64_t out_dim, int64_t i
     const int64_t mm = m < kDecodeMaxTokens ? m : kDecodeMaxTokens;
     bytes = plan_decode(mm, out_dim, in_dim, rank, cus).bytes;
   }
-  *bytes_out = bytes;
+  *bytes_out = kControlBytes + bytes;
   return ok();
 }
 
-tb_status tb_linear_forward(const void* x, const void* s, const void* w0, const void* u, const void* v, void* y,
-                            int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, tb_dtype dtype,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+static_assert(TB_MAX_GROUP == kMaxProjections, "one launch takes every member of a group");
+
+namespace {
+
+// Argument checks shared by tb_linear_forward and each member of a group.
+tb_status check_projection(const void* x, const void* s, const void* w0, const void* u, const void* v, const void* y,
+                           int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, tb_dtype dtype) {
   if (!valid_dtype(dtype)) return fail(TB_ERR_INVALID_ARGUMENT, "unknown dtype %d", int(dtype));
   tb_status st = check_dims(m, out_dim, in_dim, rank);
   if (st != TB_OK) return st;
-  if (!x || !s || !w0 || !y || !workspace) return fail(TB_ERR_INVALID_ARGUMENT, "x, s, w0, y and workspace must be non-NULL");
+  if (!x || !s || !w0 || !y) return fail(TB_ERR_INVALID_ARGUMENT, "x, s, w0 and y must be non-NULL");
   if (rank > 0 && (!u || !v)) return fail(TB_ERR_INVALID_ARGUMENT, "u and v must be non-NULL when rank > 0");
   if (!aligned16(x) || !aligned16(w0) || (rank > 0 && (!aligned16(u) || !aligned16(v))))
     return fail(TB_ERR_UNSUPPORTED, "x, w0, u and v must be 16-byte aligned");
   if (!aligned_to(s, esize(dtype)) || !aligned_to(y, esize(dtype)))
     return fail(TB_ERR_UNSUPPORTED, "s and y must be aligned to their element size");
-  if (!aligned_to(workspace, 256)) return fail(TB_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
-  int cus = 0;
-  if (int e = device_cu_count(&cus)) return hip_fail(hipError_t(e), "querying the compute-unit count");
-  hipStream_t hs = static_cast<hipStream_t>(stream);
+  // The few-token path addresses a row block (at most 96 rows) with 32-bit
+  // byte offsets.
+  const bool decode = !(dtype == TB_BF16 && m > kDecodeMaxTokens);
+  if (decode && in_dim * int64_t(esize(dtype)) * 96 >= (int64_t(1) << 32))
+    return fail(TB_ERR_UNSUPPORTED, "in_dim %lld is too large for the few-token path", (long long)in_dim);
+  return TB_OK;
+}
 
+// Bytes of one projection's buffers (after the control bytes).
+size_t forward_data_bytes(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, tb_dtype dtype, int cus) {
+  if (dtype == TB_BF16 && m > kDecodeMaxTokens) return plan_gemm(m, out_dim, in_dim, rank, cus).bytes;
+  const int64_t mm = m < kDecodeMaxTokens ? m : kDecodeMaxTokens;
+  return plan_decode(mm, out_dim, in_dim, rank, cus).bytes;
+}
+
+// One projection with checked arguments: the prefill GEMM, or the decode
+// kernel over 64-token slices.  ctrl is its control block, data holds
+// forward_data_bytes, timeouts are flagged in *err_word.
+tb_status forward_one(const void* x, const void* s, const void* w0, const void* u, const void* v, void* y, int64_t m,
+                      int64_t out_dim, int64_t in_dim, int64_t rank, tb_dtype dtype, unsigned* ctrl, char* data,
+                      unsigned* err_word, int cus, hipStream_t hs) {
   if (dtype == TB_BF16 && m > kDecodeMaxTokens) {
     const GemmPlan p = plan_gemm(m, out_dim, in_dim, rank, cus);
-    if (workspace_bytes < p.bytes)
-      return fail(TB_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is below the %zu needed", workspace_bytes, p.bytes);
-    hipError_t e = launch_forward_gemm(p, x, s, w0, u, v, y, m, out_dim, in_dim, rank, workspace, hs);
+    hipError_t e = launch_forward_gemm(p, x, s, w0, u, v, y, m, out_dim, in_dim, rank, ctrl, data, hs);
     if (e != hipSuccess) return hip_fail(e, "launching the prefill projection");
     return ok();
   }
-  // Few tokens (or fp32): the streaming decode path, 64 tokens at a time.
-  // Its loads address a row block (at most 96 rows) with 32-bit byte offsets.
-  if (in_dim * int64_t(esize(dtype)) * 96 >= (int64_t(1) << 32))
-    return fail(TB_ERR_UNSUPPORTED, "in_dim %lld is too large for the few-token path", (long long)in_dim);
   const int64_t mm = m < kDecodeMaxTokens ? m : kDecodeMaxTokens;
   const DecodePlan p = plan_decode(mm, out_dim, in_dim, rank, cus);
-  if (workspace_bytes < p.bytes)
-    return fail(TB_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is below the %zu needed", workspace_bytes, p.bytes);
   const size_t es = esize(dtype);
   for (int64_t t0 = 0; t0 < m; t0 += kDecodeMaxTokens) {
     const int64_t mt = (m - t0) < kDecodeMaxTokens ? (m - t0) : kDecodeMaxTokens;
@@ -149,8 +161,95 @@ tb_status tb_linear_forward(const void* x, const void* s, const void* w0, const 
     const char* xt = static_cast<const char*>(x) + size_t(t0) * size_t(in_dim) * es;
     char* yt = static_cast<char*>(y) + size_t(t0) * size_t(out_dim) * es;
     hipError_t e =
-        launch_forward_decode(pt, dtype, xt, s, w0, u, v, yt, mt, out_dim, in_dim, rank, workspace, hs);
+        launch_forward_decode(pt, dtype, xt, s, w0, u, v, yt, mt, out_dim, in_dim, rank, ctrl, data, err_word, hs);
     if (e != hipSuccess) return hip_fail(e, "launching the decode projection");
+  }
+  return ok();
+}
+
+}  // namespace
+
+tb_status tb_linear_forward(const void* x, const void* s, const void* w0, const void* u, const void* v, void* y,
+                            int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, tb_dtype dtype,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  tb_status st = check_projection(x, s, w0, u, v, y, m, out_dim, in_dim, rank, dtype);
+  if (st != TB_OK) return st;
+  if (!workspace) return fail(TB_ERR_INVALID_ARGUMENT, "workspace must be non-NULL");
+  if (!aligned_to(workspace, 256)) return fail(TB_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  int cus = 0;
+  if (int e = device_cu_count(&cus)) return hip_fail(hipError_t(e), "querying the compute-unit count");
+  const size_t need = kControlBytes + forward_data_bytes(m, out_dim, in_dim, rank, dtype, cus);
+  if (workspace_bytes < need)
+    return fail(TB_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is below the %zu needed", workspace_bytes, need);
+  unsigned* ctrl = static_cast<unsigned*>(workspace);
+  return forward_one(x, s, w0, u, v, y, m, out_dim, in_dim, rank, dtype, ctrl, static_cast<char*>(workspace) + kControlBytes,
+                     ctrl + 2, cus, static_cast<hipStream_t>(stream));
+}
+
+tb_status tb_linear_forward_group_workspace_size(int32_t n, const tb_projection* projs, int64_t m, tb_dtype dtype,
+                                                 size_t* bytes_out) {
+  if (bytes_out == nullptr || projs == nullptr) return fail(TB_ERR_INVALID_ARGUMENT, "projs and bytes_out must be non-NULL");
+  if (n < 1 || n > TB_MAX_GROUP) return fail(TB_ERR_INVALID_ARGUMENT, "n %d outside [1, %d]", n, TB_MAX_GROUP);
+  if (!valid_dtype(dtype)) return fail(TB_ERR_INVALID_ARGUMENT, "unknown dtype %d", int(dtype));
+  for (int j = 0; j < n; ++j) {
+    tb_status st = check_dims(m, projs[j].out_dim, projs[j].in_dim, projs[j].rank);
+    if (st != TB_OK) return st;
+  }
+  int cus = 0;
+  if (int e = device_cu_count(&cus)) return hip_fail(hipError_t(e), "querying the compute-unit count");
+  size_t total = kControlBytes;
+  for (int j = 0; j < n; ++j)
+    total += forward_data_bytes(m, projs[j].out_dim, projs[j].in_dim, projs[j].rank, dtype, cus);
+  *bytes_out = total;
+  return ok();
+}
+
+tb_status tb_linear_forward_group(int32_t n, const tb_projection* projs, int64_t m, tb_dtype dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (projs == nullptr || workspace == nullptr) return fail(TB_ERR_INVALID_ARGUMENT, "projs and workspace must be non-NULL");
+  if (n < 1 || n > TB_MAX_GROUP) return fail(TB_ERR_INVALID_ARGUMENT, "n %d outside [1, %d]", n, TB_MAX_GROUP);
+  if (!aligned_to(workspace, 256)) return fail(TB_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  for (int j = 0; j < n; ++j) {
+    const tb_projection& q = projs[j];
+    tb_status st = check_projection(q.x, q.s, q.w0, q.u, q.v, q.y, m, q.out_dim, q.in_dim, q.rank, dtype);
+    if (st != TB_OK) return st;
+  }
+  int cus = 0;
+  if (int e = device_cu_count(&cus)) return hip_fail(hipError_t(e), "querying the compute-unit count");
+  size_t off[TB_MAX_GROUP], total = kControlBytes;
+  for (int j = 0; j < n; ++j) {
+    const tb_projection& q = projs[j];
+    off[j] = total;
+    total += forward_data_bytes(m, q.out_dim, q.in_dim, q.rank, dtype, cus);
+  }
+  if (workspace_bytes < total)
+    return fail(TB_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is below the %zu needed", workspace_bytes, total);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  unsigned* ctrl = reinterpret_cast<unsigned*>(ws);
+  unsigned* err = ctrl + 2;
+
+  if (m <= kDecodeMaxTokens) {
+    DecodePlan plans[TB_MAX_GROUP];
+    DecodeProjection dp[TB_MAX_GROUP];
+    bool same = true;
+    for (int j = 0; j < n; ++j) {
+      const tb_projection& q = projs[j];
+      plans[j] = plan_decode(m, q.out_dim, q.in_dim, q.rank, cus);
+      dp[j] = DecodeProjection{q.x, q.s, q.w0, q.u, q.v, q.y, q.out_dim, q.in_dim, q.rank};
+      same = same && plans[j].NT == plans[0].NT && plans[j].TILES == plans[0].TILES;
+    }
+    if (same) {
+      hipError_t e = launch_forward_decode_group(n, plans, dp, dtype, m, ctrl, ws + kControlBytes, err, hs);
+      if (e != hipSuccess) return hip_fail(e, "launching the grouped decode projections");
+      return ok();
+    }
+  }
+  for (int j = 0; j < n; ++j) {
+    const tb_projection& q = projs[j];
+    tb_status st = forward_one(q.x, q.s, q.w0, q.u, q.v, q.y, m, q.out_dim, q.in_dim, q.rank, dtype,
+                               ctrl + j * (kCtrlBlockBytes / 4), ws + off[j], err, cus, hs);
+    if (st != TB_OK) return st;
   }
   return ok();
 }

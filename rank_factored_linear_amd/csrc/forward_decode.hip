@@ -68,6 +68,7 @@ struct DecodeArgs {
   int NCB, KT;       // producers: NCB column blocks x KT k-slices
   int NRB, KS, RBR;  // streamers: NRB row blocks x KS k-slices; RBR rows per block at most
   unsigned* ctrl;
+  unsigned* err;  // sticky timeout word (word kErr of the first projection's control region)
   float* tpart;  // [KT][16*NT][Rp] fp32 partials (KT > 1)
   void* tfull;   // [16*NT][Rp] T in the operand type
   float* ypart;  // [NRB][KS][16*NT][RBR] fp32 (KS > 1)
@@ -445,7 +446,7 @@ __device__ void stream_rows(const DecodeArgs& a, int b, uint8_t* smem) {
   // The rank-r delta: this wave's k32 steps of T . U^T, once T is complete.
   if (rank_unit) {
     const bool ok = wait_for_count(&a.ctrl[kDone], unsigned(a.NCB));
-    if (!ok && l == 0) atomicOr(&a.ctrl[kErr], 1u);
+    if (!ok && l == 0) atomicOr(a.err, 1u);
     for (int rs = w; rs < RS; rs += kWaves) {
       if (rs != w || !kPrefetchU) {
 #pragma unroll
@@ -542,38 +543,57 @@ constexpr int smem_bytes() {
   return streamer > producer_smem<E, NT>() ? streamer : producer_smem<E, NT>();
 }
 
+// One launch serves a group of independent projections of the same token
+// count and tile shape: all of their producers first (in projection order),
+// then all of their streamers, so a streamer's producers always have lower
+// block indexes and have been dispatched before it.
+struct GroupArgs {
+  int n;
+  int p_end[kMaxProjections];  // producers of projections 0..j: blocks [0, p_end[j])
+  int s_end[kMaxProjections];  // streamers of projections 0..j: blocks [p_end[n-1], p_end[n-1] + s_end[j])
+  DecodeArgs a[kMaxProjections];
+};
+
 template <typename E, int NT, int TILES>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void decode_kernel(GroupArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<E, NT, TILES>()];
-  const int b = int(blockIdx.x), np = a.NCB * a.KT;
-  if (b < np) produce_t<E, NT>(a, b, smem);
-  else stream_rows<E, NT, TILES>(a, b - np, smem);
+  const int b = int(blockIdx.x), np = g.p_end[g.n - 1];
+  int j = 0;
+  if (b < np) {
+    while (b >= g.p_end[j]) ++j;
+    produce_t<E, NT>(g.a[j], b - (j ? g.p_end[j - 1] : 0), smem);
+  } else {
+    const int bs = b - np;
+    while (bs >= g.s_end[j]) ++j;
+    stream_rows<E, NT, TILES>(g.a[j], bs - (j ? g.s_end[j - 1] : 0), smem);
+  }
 }
 
 template <typename E, int NT, int TILES>
-hipError_t launch_t(const DecodePlan& p, const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<E, NT, TILES>), dim3(p.NP + p.NB), dim3(kThreads), 0, stream, a);
+hipError_t launch_t(const GroupArgs& g, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_kernel<E, NT, TILES>), dim3(g.p_end[g.n - 1] + g.s_end[g.n - 1]), dim3(kThreads), 0,
+                     stream, g);
   return hipGetLastError();
 }
 
 template <typename E>
-hipError_t launch_e(const DecodePlan& p, const DecodeArgs& a, hipStream_t stream) {
-  if (p.NT == 1) {
-    switch (p.TILES) {
-      case 1: return launch_t<E, 1, 1>(p, a, stream);
-      case 2: return launch_t<E, 1, 2>(p, a, stream);
-      case 4: return launch_t<E, 1, 4>(p, a, stream);
-      default: return launch_t<E, 1, 6>(p, a, stream);
+hipError_t launch_e(int NT, int TILES, const GroupArgs& g, hipStream_t stream) {
+  if (NT == 1) {
+    switch (TILES) {
+      case 1: return launch_t<E, 1, 1>(g, stream);
+      case 2: return launch_t<E, 1, 2>(g, stream);
+      case 4: return launch_t<E, 1, 4>(g, stream);
+      default: return launch_t<E, 1, 6>(g, stream);
     }
   }
-  if (p.NT == 2) {
-    switch (p.TILES) {
-      case 1: return launch_t<E, 2, 1>(p, a, stream);
-      case 2: return launch_t<E, 2, 2>(p, a, stream);
-      default: return launch_t<E, 2, 4>(p, a, stream);
+  if (NT == 2) {
+    switch (TILES) {
+      case 1: return launch_t<E, 2, 1>(g, stream);
+      case 2: return launch_t<E, 2, 2>(g, stream);
+      default: return launch_t<E, 2, 4>(g, stream);
     }
   }
-  return p.TILES == 1 ? launch_t<E, 4, 1>(p, a, stream) : launch_t<E, 4, 2>(p, a, stream);
+  return TILES == 1 ? launch_t<E, 4, 1>(g, stream) : launch_t<E, 4, 2>(g, stream);
 }
 
 }  // namespace
@@ -622,7 +642,7 @@ DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
   p.NP = p.NCB * p.KT;
   const size_t rows16 = size_t(16 * p.NT);
   const size_t rbr = size_t(16 * p.TILES);
-  size_t off = kControlBytes;
+  size_t off = 0;
   p.off_tpart = off;  // [KT][16*NT][Rp] fp32 (KT > 1)
   off = align_up(off + (p.KT > 1 ? size_t(p.KT) * rows16 * size_t(p.NCB) * kCbCols * 4 : 0), 256);
   p.off_tfull = off;  // [16*NT][Rp], fp32 or bf16
@@ -633,21 +653,42 @@ DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
   return p;
 }
 
+hipError_t launch_forward_decode_group(int n, const DecodePlan* plans, const DecodeProjection* projs, tb_dtype dtype,
+                                       int64_t m, unsigned* ctrl, char* data, unsigned* err_word, hipStream_t stream) {
+  if (n < 1 || n > kMaxProjections) return hipErrorInvalidValue;
+  GroupArgs g{};
+  g.n = n;
+  char* ws = data;
+  int np = 0, nb = 0;
+  for (int j = 0; j < n; ++j) {
+    const DecodePlan& p = plans[j];
+    const DecodeProjection& q = projs[j];
+    if (p.NT != plans[0].NT || p.TILES != plans[0].TILES) return hipErrorInvalidValue;
+    DecodeArgs& a = g.a[j];
+    a.x = q.x; a.s = q.s; a.w0 = q.w0; a.u = q.u; a.v = q.v; a.y = q.y;
+    a.M = int(m); a.O = int(q.out_dim); a.I = int(q.in_dim); a.R = int(q.rank);
+    a.NCB = p.NCB; a.KT = p.KT;
+    a.NRB = p.NRB; a.KS = p.KS; a.RBR = 16 * p.TILES;
+    a.ctrl = ctrl + j * (kCtrlBlockBytes / 4);
+    a.err = err_word;
+    a.tpart = reinterpret_cast<float*>(ws + p.off_tpart);
+    a.tfull = ws + p.off_tfull;
+    a.ypart = reinterpret_cast<float*>(ws + p.off_ypart);
+    np += p.NP;
+    nb += p.NB;
+    g.p_end[j] = np;
+    g.s_end[j] = nb;
+    ws += p.bytes;  // the next projection's buffers
+  }
+  if (dtype == TB_BF16) return launch_e<bf16_t>(plans[0].NT, plans[0].TILES, g, stream);
+  return launch_e<float>(plans[0].NT, plans[0].TILES, g, stream);
+}
+
 hipError_t launch_forward_decode(const DecodePlan& p, tb_dtype dtype, const void* x, const void* s, const void* w0,
                                  const void* u, const void* v, void* y, int64_t m, int64_t out_dim, int64_t in_dim,
-                                 int64_t rank, void* workspace, hipStream_t stream) {
-  char* ws = static_cast<char*>(workspace);
-  DecodeArgs a;
-  a.x = x; a.s = s; a.w0 = w0; a.u = u; a.v = v; a.y = y;
-  a.M = int(m); a.O = int(out_dim); a.I = int(in_dim); a.R = int(rank);
-  a.NCB = p.NCB; a.KT = p.KT;
-  a.NRB = p.NRB; a.KS = p.KS; a.RBR = 16 * p.TILES;
-  a.ctrl = reinterpret_cast<unsigned*>(ws);
-  a.tpart = reinterpret_cast<float*>(ws + p.off_tpart);
-  a.tfull = ws + p.off_tfull;
-  a.ypart = reinterpret_cast<float*>(ws + p.off_ypart);
-  if (dtype == TB_BF16) return launch_e<bf16_t>(p, a, stream);
-  return launch_e<float>(p, a, stream);
+                                 int64_t rank, unsigned* ctrl, char* data, unsigned* err_word, hipStream_t stream) {
+  const DecodeProjection q{x, s, w0, u, v, y, out_dim, in_dim, rank};
+  return launch_forward_decode_group(1, &p, &q, dtype, m, ctrl, data, err_word, stream);
 }
 
 }  // namespace tb

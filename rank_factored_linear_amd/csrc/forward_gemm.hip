@@ -262,11 +262,8 @@ __device__ __forceinline__ lds_byte* opaque(lds_byte* p) {
 // ---------------------------------------------------------------------------
 namespace big {
 
-#ifndef TB_BIG_WAVES
-#define TB_BIG_WAVES 8
-#endif
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kWaves = TB_BIG_WAVES, kThreads = kWaves * kWave;
+constexpr int kWaves = 8, kThreads = kWaves * kWave;
 constexpr int WN = kWaves / 2;            // waves along the output columns (two along the tokens)
 constexpr int TJ = BN / WN / 32;          // 32-column accumulator tiles per wave
 constexpr int kRows = kThreads / 8;       // rows one round of 16-byte chunks stages
@@ -569,23 +566,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   const int g = int(blockIdx.x), G = int(gridDim.x);
   const int pos = a.xcd_major ? (g % 8) * (G / 8) + g / 8 : g;
   const Lanes ln = make_lanes(ring);
-#ifdef TB_CLOCKPROBE
-  const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
-#endif
   for (int v = pos; v < a.split_tiles * a.S; v += G) {
     const int u = v % a.split_tiles, slice = v / a.split_tiles;
     do_tile(a, u, slice * a.kps, min(a.KT, (slice + 1) * a.kps), slice, ln, &s_last);
   }
   const int tiles = a.tiles_m * a.tiles_n;
   for (int u = a.split_tiles + pos; u < tiles; u += G) do_tile(a, u, 0, a.KT, -1, ln, &s_last);
-#ifdef TB_CLOCKPROBE
-  const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
-  if (threadIdx.x == 0) {
-    unsigned* d = a.ctrl + 8192 + 4 * g;
-    __hip_atomic_store(d + 0, unsigned(c1 - c0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(d + 1, unsigned(r1 - r0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-#endif
 }
 
 }  // namespace big
@@ -860,7 +846,7 @@ constexpr int kStoreCost = 6, kLoadCost = 4, kMinSlice = 4;
 
 GemmPlan plan_gemm(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus) {
   GemmPlan p{};
-  p.off_t = kControlBytes;
+  p.off_t = 0;
   const size_t off = align_up(p.off_t + size_t(m) * size_t(rank) * 2, 256);
   p.bytes = off;
   // The matrix-core kernels for 16-byte aligned rows address one tile's rows
@@ -930,8 +916,8 @@ GemmPlan plan_gemm(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int
 
 hipError_t launch_forward_gemm(const GemmPlan& p, const void* x, const void* s, const void* w0, const void* u,
                                const void* v, void* y, int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
-                               void* workspace, hipStream_t stream) {
-  char* ws = static_cast<char*>(workspace);
+                               unsigned* ctrl, char* data, hipStream_t stream) {
+  char* ws = data;
   bf16_t* t = reinterpret_cast<bf16_t*>(ws + p.off_t);
   if (rank > 0 && p.aligned) {
     xv::Args a;
@@ -941,7 +927,7 @@ hipError_t launch_forward_gemm(const GemmPlan& p, const void* x, const void* s, 
     a.M = int(m); a.I = int(in_dim); a.R = int(rank);
     a.RB = p.xv_rb; a.CB = p.xv_cb; a.KT = p.xv_kt;
     a.KS = p.xv_ks; a.kps = p.xv_kps;
-    a.ctrl = reinterpret_cast<unsigned*>(ws);
+    a.ctrl = ctrl;
     a.part = reinterpret_cast<float*>(ws + p.off_xvpart);
     hipLaunchKernelGGL(xv::xv_kernel, dim3(unsigned(p.xv_rb * p.xv_cb * p.xv_ks)), dim3(xv::kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
@@ -965,7 +951,7 @@ hipError_t launch_forward_gemm(const GemmPlan& p, const void* x, const void* s, 
     a.tiles_m = p.tiles_m; a.tiles_n = p.tiles_n;
     a.KT = p.KT; a.KR = p.KR;
     a.split_tiles = p.split_tiles; a.S = p.S; a.kps = p.kps; a.xcd_major = p.xcd_major;
-    a.ctrl = reinterpret_cast<unsigned*>(ws);
+    a.ctrl = ctrl;
     a.part = reinterpret_cast<float*>(ws + p.off_part);
     hipLaunchKernelGGL(big::gemm_kernel, dim3(unsigned(p.grid)), dim3(big::kThreads), 0, stream, a);
     return hipGetLastError();

@@ -9,8 +9,14 @@
 
 namespace tb {
 
+// The workspace starts with kControlBytes of control words: one block of
+// kCtrlBlockBytes per member of a grouped call (a single call uses block 0).
+// Each projection's buffers follow, at offsets its plan gives from its data
+// base; plan.bytes counts the buffers only.
+constexpr int kMaxProjections = TB_MAX_GROUP;
 constexpr size_t kControlBytes = TB_WORKSPACE_CONTROL_BYTES;
-constexpr int kMaxGroupCounters = int(kControlBytes / 4) - 64;  // words 64.. of the control region
+constexpr size_t kCtrlBlockBytes = kControlBytes / kMaxProjections;
+constexpr int kMaxGroupCounters = int(kCtrlBlockBytes / 4) - 64;  // words 64.. of a control block
 
 // Compute units of the current device (queried once per device).
 int device_cu_count(int* cus);
@@ -32,9 +38,27 @@ struct DecodePlan {
 
 DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus);
 
+// ctrl: the projection's control block; data: its buffers; err_word: where a
+// timed-out wait is flagged.
 hipError_t launch_forward_decode(const DecodePlan& p, tb_dtype dtype, const void* x, const void* s, const void* w0,
                                  const void* u, const void* v, void* y, int64_t m, int64_t out_dim, int64_t in_dim,
-                                 int64_t rank, void* workspace, hipStream_t stream);
+                                 int64_t rank, unsigned* ctrl, char* data, unsigned* err_word, hipStream_t stream);
+
+// Several independent projections of the same token count (<= kDecodeMaxTokens)
+// in one launch.  Their plans must agree on NT and TILES.  Projection j uses
+// control block j (from ctrl) and the buffers after the plans[0..j-1] bytes
+// (from data); timeouts of any member set *err_word.
+struct DecodeProjection {
+  const void* x;
+  const void* s;
+  const void* w0;
+  const void* u;
+  const void* v;
+  void* y;
+  int64_t out_dim, in_dim, rank;
+};
+hipError_t launch_forward_decode_group(int n, const DecodePlan* plans, const DecodeProjection* projs, tb_dtype dtype,
+                                       int64_t m, unsigned* ctrl, char* data, unsigned* err_word, hipStream_t stream);
 
 // ---- forward, prefill token counts (bf16, m > kDecodeMaxTokens) ----------
 struct GemmPlan {
@@ -54,7 +78,7 @@ GemmPlan plan_gemm(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int
 
 hipError_t launch_forward_gemm(const GemmPlan& p, const void* x, const void* s, const void* w0, const void* u,
                                const void* v, void* y, int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
-                               void* workspace, hipStream_t stream);
+                               unsigned* ctrl, char* data, hipStream_t stream);
 
 // ---- reconstruct ----------------------------------------------------------
 hipError_t launch_reconstruct(tb_dtype in_dtype, tb_dtype out_dtype, const void* s, const void* w0, const void* u,

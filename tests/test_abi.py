@@ -139,3 +139,41 @@ def test_workspace_size_rejects_bad_arguments():
     assert lib.tb_linear_forward_workspace_size(0, 64, 64, 0, 0, ctypes.byref(out)) == 1
     assert lib.tb_linear_forward_workspace_size(1, 64, 64, 0, 0, None) == 1
     assert lib.tb_linear_forward_workspace_size(1, 64, 63, 0, 0, ctypes.byref(out)) == 2
+
+
+def _group(n=2, **kw):
+    """A tb_projection array of n members with placeholder pointers; kw overrides member 0."""
+    arr = (binding.Projection * max(n, 1))()
+    for j in range(max(n, 1)):
+        a = dict(x=FAKE, s=FAKE, w0=FAKE, u=FAKE, v=FAKE, y=FAKE, o=64, i=64, r=16)
+        if j == 0:
+            a.update(kw)
+        arr[j] = binding.Projection(a["x"], a["s"], a["w0"], a["u"], a["v"], a["y"], a["o"], a["i"], a["r"])
+    return arr
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(y=None), 1), (dict(u=None), 1), (dict(o=0), 1), (dict(r=-1), 1),
+    (dict(i=60), 2), (dict(x=FAKE + 8), 2), (dict(s=FAKE + 1), 2),
+])
+def test_group_rejects_bad_member_before_launch(kw, status):
+    arr = _group(3, **kw)
+    assert lib.tb_linear_forward_group(3, arr, 8, binding.TB_BF16, FAKE, 1 << 24, None) == status
+    assert lib.tb_last_error().decode()
+
+
+def test_group_rejects_bad_call_before_launch():
+    f = lib.tb_linear_forward_group
+    arr = _group(2)
+    assert f(0, arr, 8, binding.TB_BF16, FAKE, 1 << 24, None) == 1
+    assert f(binding.MAX_GROUP + 1, arr, 8, binding.TB_BF16, FAKE, 1 << 24, None) == 1
+    assert f(2, None, 8, binding.TB_BF16, FAKE, 1 << 24, None) == 1
+    assert f(2, arr, 8, binding.TB_BF16, None, 1 << 24, None) == 1
+    assert f(2, arr, 8, binding.TB_BF16, FAKE + 16, 1 << 24, None) == 2
+    assert f(2, arr, 0, binding.TB_BF16, FAKE, 1 << 24, None) == 1
+    assert f(2, arr, 8, 7, FAKE, 1 << 24, None) == 1
+    out = ctypes.c_size_t(0)
+    g = lib.tb_linear_forward_group_workspace_size
+    assert g(0, arr, 8, binding.TB_BF16, ctypes.byref(out)) == 1
+    assert g(2, arr, 8, binding.TB_BF16, None) == 1
+    assert g(2, _group(2, i=63), 8, binding.TB_BF16, ctypes.byref(out)) == 2

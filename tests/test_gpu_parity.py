@@ -309,6 +309,42 @@ def test_bitwise_deterministic_and_workspace_clean(shape):
     assert int(ws[16:tb.WORKSPACE_CONTROL_BYTES].count_nonzero().item()) == 0
 
 
+GROUPS = {  # members (out, in, rank)
+    "qkv60": [(8192, 5376, 256), (2048, 5376, 256), (2048, 5376, 256)],
+    "gateup26": [(6912, 1152, 128), (6912, 1152, 128)],
+    "q_and_o60": [(8192, 5376, 256), (5376, 8192, 256)],  # launch plans differ: one after another
+    "ragged": [(17, 40, 4), (33, 72, 0), (130, 264, 12), (100, 264, 300)],
+}
+
+
+@pytest.mark.parametrize("M", [1, 4, 16, 64, 100])
+@pytest.mark.parametrize("group", sorted(GROUPS))
+def test_forward_group_matches_single_calls(group, M):
+    # A grouped call computes each member exactly as its own call would.
+    _say(f"group {group} M={M}")
+    members = [_rand_case(M, O, I, R, torch.bfloat16, seed=31 * j + M) for j, (O, I, R) in enumerate(GROUPS[group])]
+    ys = tb.linear_forward_group(members)
+    singles = [tb.linear_forward(*mbr) for mbr in members]
+    torch.cuda.synchronize()
+    for y, y1 in zip(ys, singles):
+        assert torch.equal(y.view(torch.int16), y1.view(torch.int16))
+    assert tb.workspace_error_word() == 0
+    if group == "ragged":
+        for mbr, y in zip(members, ys):
+            assert oracle.relative_frobenius_error(_oracle_forward(*mbr), exact(y)) <= BF16_TOL
+
+
+def test_forward_group_fp32_and_clean_workspace():
+    members = [_rand_case(8, O, I, R, torch.float32, seed=O) for (O, I, R) in GROUPS["ragged"]]
+    ys = tb.linear_forward_group(members)
+    for mbr, y in zip(members, ys):
+        assert oracle.relative_frobenius_error(_oracle_forward(*mbr), exact(y)) <= F32_TOL
+    # Every member's control block is left clean.
+    ws = tb.workspace_for(tb.WORKSPACE_CONTROL_BYTES)
+    torch.cuda.synchronize()
+    assert int(ws[:tb.WORKSPACE_CONTROL_BYTES].count_nonzero().item()) == 0
+
+
 def test_stream_ordering_many_calls():
     # Back-to-back calls of different shapes on one stream reuse the
     # workspace; each must see clean control words.
