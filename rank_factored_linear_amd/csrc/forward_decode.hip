@@ -444,9 +444,17 @@ __device__ void stream_rows(const DecodeArgs& a, int b, uint8_t* smem) {
     }
 
   // The rank-r delta: this wave's k32 steps of T . U^T, once T is complete.
+  // One wave polls the done word (every wave polling it would hammer the
+  // line the producers count into) and shares the outcome through LDS.
   if (rank_unit) {
-    const bool ok = wait_for_count(&a.ctrl[kDone], unsigned(a.NCB));
-    if (!ok && l == 0) atomicOr(a.err, 1u);
+    __shared__ unsigned s_ok;
+    if (w == 0) {
+      const bool ok0 = wait_for_count(&a.ctrl[kDone], unsigned(a.NCB));
+      if (l == 0) s_ok = ok0 ? 1u : 0u;
+    }
+    __syncthreads();
+    const bool ok = s_ok != 0u;
+    if (!ok && w == 0 && l == 0) atomicOr(a.err, 1u);
     for (int rs = w; rs < RS; rs += kWaves) {
       if (rs != w || !kPrefetchU) {
 #pragma unroll
@@ -504,16 +512,24 @@ __device__ void stream_rows(const DecodeArgs& a, int b, uint8_t* smem) {
       Y[size_t(tok) * a.O + r0 + row] = from_f32<E>(res[tok * RBR + row]);
     }
   } else {
+    // If the row block's other k-slices have all counted in already (the
+    // slice that waited for T usually arrives last), this workgroup sums
+    // their partials at once and stores none of its own; otherwise it stores
+    // its partial and counts in.  Either way the sum runs in k-slice order.
     __shared__ unsigned s_last;
-    float* mine = a.ypart + (size_t(rb) * KS + ks) * (16 * NT) * RBR;
-    for (int i = tid; i < nel; i += kThreads) {
-      const int tok = i / nrows, row = i % nrows;
-      store_coherent(&mine[tok * RBR + row], __float_as_uint(res[tok * RBR + row]));
+    if (tid == 0) s_last = load_coherent(&a.ctrl[kRbCounters + rb]) == unsigned(KS - 1) ? 1u : 0u;
+    __syncthreads();
+    if (!s_last) {
+      float* mine = a.ypart + (size_t(rb) * KS + ks) * (16 * NT) * RBR;
+      for (int i = tid; i < nel; i += kThreads) {
+        const int tok = i / nrows, row = i % nrows;
+        store_coherent(&mine[tok * RBR + row], __float_as_uint(res[tok * RBR + row]));
+      }
+      drain_stores();
+      __syncthreads();
+      if (tid == 0) s_last = add_coherent(&a.ctrl[kRbCounters + rb], 1u) == unsigned(KS - 1);
+      __syncthreads();
     }
-    drain_stores();
-    __syncthreads();
-    if (tid == 0) s_last = add_coherent(&a.ctrl[kRbCounters + rb], 1u) == unsigned(KS - 1);
-    __syncthreads();
     if (s_last) {
       const float* blk = a.ypart + size_t(rb) * KS * (16 * NT) * RBR;
       for (int i = tid; i < nel; i += kThreads) {
