@@ -238,13 +238,10 @@ __device__ __forceinline__ lds_byte* opaque(lds_byte* p) {
 //
 // Output tiles of 256 tokens x 256 outputs; eight waves, each owning 128 x 64
 // as 4 x 2 accumulator tiles of v_mfma_f32_32x32x16_bf16.  The reduction runs
-// in k-tiles of 64 through a two-buffer LDS ring (rows padded from 128 to 144
-// bytes, so the 16-byte fragment reads of 16 consecutive rows fall in distinct
-// bank groups and every k16 step is a fixed offset from one lane address)
-// fed from two register sets of buffer loads: the fetch of
-// k-tile k+2 is issued before k-tile k is multiplied, so each fetch has two
-// k-tiles' time to land.  Rows past the matrix and chunks past the reduction
-// length read as zero.
+// in k-tiles of 64 through a two-buffer LDS ring filled by direct-to-LDS
+// buffer loads (no staging through registers, no LDS store instructions: the
+// LDS instruction queue carries only the fragment reads); rows past the
+// matrix and chunks past the reduction length read as zero.
 //
 // The rank tail runs through the same pipeline: after the last k-tile of
 // x . W0^T the accumulators are scaled by s and the reduction continues over
@@ -266,15 +263,13 @@ constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kWaves = 8, kThreads = kWaves * kWave;
 constexpr int WN = kWaves / 2;            // waves along the output columns (two along the tokens)
 constexpr int TJ = BN / WN / 32;          // 32-column accumulator tiles per wave
-constexpr int kRows = kThreads / 8;       // rows one round of 16-byte chunks stages
-constexpr int kChunks = BM / kRows;       // chunks per operand per lane per k-tile
-constexpr int kPitch = BK * 2 + 16;       // LDS row: 64 bf16 + 16 bytes of padding
-constexpr int kTileBytes = BM * kPitch;   // one operand's k-tile in LDS
-// LDS ring [A0][A1][B0][B1]: buffer 1 sits a fixed 36 KB after buffer 0, so
-// both are reached from the same lane addresses through immediate offsets.
+constexpr int kTileBytes = BM * BK * 2;   // one operand's k-tile in LDS: 256 rows of 128 bytes
+// LDS ring [A0][A1][B0][B1]: buffer 1 sits 32 KB after buffer 0, within the
+// immediate offset of every lane address.
 constexpr int kBOffset = 2 * kTileBytes;
 constexpr int kRingBytes = 4 * kTileBytes;
 constexpr int kPartFloats = BM * BN;      // fp32 partial of one output tile
+constexpr unsigned kOutOfRange = 0x80000000u;  // lane offset past every buffer: the load returns zeros
 
 struct Args {
   const bf16_t* x;
@@ -293,12 +288,21 @@ struct Args {
   float* part;       // [S * split_tiles][kPartFloats] partials, slice-major
 };
 
-// Buffer descriptors and lane offsets of one GEMM's operands for one tile.
+// A k-tile of each operand goes from HBM straight into LDS: each wave issues
+// four 1 KB direct-to-LDS loads per operand (rows (4w + j) * 8 .. +7), lane l
+// of a load landing at M0 + 16 l.  Within a row the 16-byte chunks are stored
+// XOR-swizzled by (row >> 1) & 7, so the fragment reads of 16 consecutive
+// rows hit distinct banks; the swizzle is applied by choosing which global
+// chunk each lane fetches.  The loads are written as inline assembly: the
+// compiler does not see them write LDS, so it does not drain every load
+// before each LDS read, and the waits are explicit (vmcnt before the
+// barrier that publishes a k-tile).
 struct Operands {
   __amdgpu_buffer_rsrc_t ra, rb;
-  int va;       // byte offset of this lane's chunk: row tid / 8, chunk tid % 8
-  int rowstep;  // bytes of kRows rows
-  int kel;      // reduction length in elements
+  int ve, vo;      // lane offsets (row, swizzled chunk) for the even and odd loads j
+  int ce, co;      // the global chunk index each of them fetches
+  int rowstep8;    // bytes of 8 rows (soffset step between the loads j)
+  int kel;         // reduction length in elements
 };
 
 __device__ __forceinline__ Operands make_operands(const bf16_t* a, int arows, const bf16_t* b, int brows, int m0,
@@ -307,69 +311,81 @@ __device__ __forceinline__ Operands make_operands(const bf16_t* a, int arows, co
   const int ar = min(arows - m0, BM), br = min(brows - n0, BN);
   o.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(a + size_t(m0) * k), 0, ar * k * 2, kRsrcFlags);
   o.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(b + size_t(n0) * k), 0, br * k * 2, kRsrcFlags);
-  o.va = int(threadIdx.x >> 3) * k * 2 + int(threadIdx.x & 7) * 16;
-  o.rowstep = kRows * k * 2;
+  const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave), l = int(threadIdx.x) % kWave;
+  // Load j covers rows w*32 + 8j + l/8; rows of even and of odd j share the swizzle.
+  const int row_e = w * 32 + (l >> 3), row_o = row_e + 8, pos = l & 7;
+  o.ce = pos ^ ((row_e >> 1) & 7);
+  o.co = pos ^ ((row_o >> 1) & 7);
+  o.ve = row_e * k * 2 + (o.ce << 4);
+  o.vo = row_e * k * 2 + (o.co << 4);  // the soffset of load j adds its 8j rows
+  o.rowstep8 = 8 * k * 2;
   o.kel = k;
   return o;
 }
 
-// Global fragments of k-tile kt: kChunks 16-byte chunks of each operand per lane.
-__device__ __forceinline__ void fetch(const Operands& o, int kt, u32x4 (&pa)[kChunks], u32x4 (&pb)[kChunks]) {
-#pragma unroll
-  for (int j = 0; j < kChunks; ++j) {
-    pa[j] = __builtin_amdgcn_raw_buffer_load_b128(o.ra, o.va, kt * BK * 2 + j * o.rowstep, 0);
-    pb[j] = __builtin_amdgcn_raw_buffer_load_b128(o.rb, o.va, kt * BK * 2 + j * o.rowstep, 0);
-  }
-}
-
-// Lane addresses in the LDS ring, built once per workgroup (see opaque()).
+// Lane addresses in the LDS ring, built once per workgroup.
 struct Lanes {
-  lds_byte* a_rd;     // A fragment row wm*128 + lane%32, k half lane/32
-  lds_byte* b_rd;     // B fragment row wn*(BN/WN) + lane%32, k half lane/32
-  lds_byte* a_wr[2];  // staging row tid/8, chunk tid%8 of A, per buffer
-  lds_byte* b_wr[2];  // same of B
+  unsigned dma_a, dma_b;  // this wave's first 1 KB of A and of B in buffer 0 (uniform)
+  lds_byte* a_rd[4];      // A fragment of k16 step st: row wm*128 + lane%32, swizzled chunk 2st + lane/32
+  lds_byte* b_rd[4];      // B fragment of k16 step st: row wn*(BN/WN) + lane%32
 };
 
 __device__ __forceinline__ Lanes make_lanes(uint8_t* ring) {
   lds_byte* base = (lds_byte*)ring;
-  const int w = int(threadIdx.x) / kWave, l = int(threadIdx.x) % kWave, lr = l & 31, hi = l >> 5;
-  const int wm = w / WN, wn = w % WN;
-  const int wr = int(threadIdx.x >> 3) * kPitch + int(threadIdx.x & 7) * 16;
+  const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave), l = int(threadIdx.x) % kWave;
+  const int lr = l & 31, hi = l >> 5, wm = w / WN, wn = w % WN, x = (lr >> 1) & 7;
   Lanes ln;
-  ln.a_rd = opaque(base + (wm * 128 + lr) * kPitch + hi * 16);
-  ln.b_rd = opaque(base + kBOffset + (wn * (BN / WN) + lr) * kPitch + hi * 16);
-  ln.a_wr[0] = opaque(base + wr);
-  ln.b_wr[0] = opaque(base + kBOffset + wr);
-  if constexpr ((kChunks - 1) * kRows * kPitch + kTileBytes < 65536) {
-    // Buffer 1's stores fit in the immediate offset of buffer 0's address.
-    ln.a_wr[1] = ln.a_wr[0] + kTileBytes;
-    ln.b_wr[1] = ln.b_wr[0] + kTileBytes;
-  } else {
-    ln.a_wr[1] = opaque(base + kTileBytes + wr);
-    ln.b_wr[1] = opaque(base + kBOffset + kTileBytes + wr);
+  const unsigned b0 = unsigned(uintptr_t(base));
+  ln.dma_a = __builtin_amdgcn_readfirstlane(b0 + unsigned(w) * 4096u);
+  ln.dma_b = __builtin_amdgcn_readfirstlane(b0 + unsigned(kBOffset) + unsigned(w) * 4096u);
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const int chunk = ((2 * st + hi) ^ x) << 4;
+    ln.a_rd[st] = opaque(base + (wm * 128 + lr) * 128 + chunk);
+    ln.b_rd[st] = opaque(base + kBOffset + (wn * (BN / WN) + lr) * 128 + chunk);
   }
   return ln;
 }
 
-// Write k-tile kt's fragments to LDS buffer BUF; in a k-tile that runs past
-// the reduction length the chunks at or beyond it become zero.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// Four direct-to-LDS loads of one operand: load j writes 1 KB at dst + j KB
+// from the global rows at soffset soff + j * rowstep8.  M0 takes one wait
+// state before a load that reads it.
+__device__ __forceinline__ void dma4(unsigned dst, __amdgpu_buffer_rsrc_t r, int ve, int vo, int soff, int rowstep8) {
+  asm volatile(
+      "s_mov_b32 m0, %[d0]\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[ve], %[r], %[s0] offen lds\n\t"
+      "s_mov_b32 m0, %[d1]\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[r], %[s1] offen lds\n\t"
+      "s_mov_b32 m0, %[d2]\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[ve], %[r], %[s2] offen lds\n\t"
+      "s_mov_b32 m0, %[d3]\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[r], %[s3] offen lds"
+      :
+      : [d0] "s"(dst), [d1] "s"(dst + 1024u), [d2] "s"(dst + 2048u), [d3] "s"(dst + 3072u), [ve] "v"(ve), [vo] "v"(vo),
+        [r] "s"(r), [s0] "s"(soff), [s1] "s"(soff + rowstep8), [s2] "s"(soff + 2 * rowstep8),
+        [s3] "s"(soff + 3 * rowstep8)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Every direct-to-LDS load of this wave has landed.
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// k-tile kt of both operands into LDS buffer BUF (eight loads per wave).  In
+// a k-tile that runs past the reduction length, lanes whose chunk starts at or
+// beyond it fetch from past the buffer and so write zeros.
 template <int BUF>
-__device__ __forceinline__ void stage(const Lanes& ln, const Operands& o, int kt, u32x4 (&pa)[kChunks],
-                                      u32x4 (&pb)[kChunks]) {
+__device__ __forceinline__ void issue(const Operands& o, const Lanes& ln, int kt) {
+  int ve = o.ve, vo = o.vo;
   const int left = o.kel - kt * BK;
   if (left < BK) {
-    const bool keep = int(threadIdx.x & 7) * 8 < left;
-#pragma unroll
-    for (int j = 0; j < kChunks; ++j) {
-      pa[j] = keep ? pa[j] : u32x4{0u, 0u, 0u, 0u};
-      pb[j] = keep ? pb[j] : u32x4{0u, 0u, 0u, 0u};
-    }
+    ve = o.ce * 8 < left ? ve : int(kOutOfRange);
+    vo = o.co * 8 < left ? vo : int(kOutOfRange);
   }
-#pragma unroll
-  for (int j = 0; j < kChunks; ++j) {
-    *reinterpret_cast<lds_u32x4*>(ln.a_wr[BUF] + j * kRows * kPitch) = pa[j];
-    *reinterpret_cast<lds_u32x4*>(ln.b_wr[BUF] + j * kRows * kPitch) = pb[j];
-  }
+  dma4(ln.dma_a + BUF * kTileBytes, o.ra, ve, vo, kt * BK * 2, o.rowstep8);
+  dma4(ln.dma_b + BUF * kTileBytes, o.rb, ve, vo, kt * BK * 2, o.rowstep8);
 }
 
 // Operand fragments of k16 step st from buffer BUF: A rows wm*128 + 32i +
@@ -378,10 +394,10 @@ template <int BUF>
 __device__ __forceinline__ void read_frags(const Lanes& ln, int st, u32x4 (&fa)[4], u32x4 (&fb)[TJ]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    fa[i] = *reinterpret_cast<const lds_u32x4*>(ln.a_rd + BUF * kTileBytes + i * 32 * kPitch + st * 32);
+    fa[i] = *reinterpret_cast<const lds_u32x4*>(ln.a_rd[st] + BUF * kTileBytes + i * 32 * 128);
 #pragma unroll
   for (int j = 0; j < TJ; ++j)
-    fb[j] = *reinterpret_cast<const lds_u32x4*>(ln.b_rd + BUF * kTileBytes + j * 32 * kPitch + st * 32);
+    fb[j] = *reinterpret_cast<const lds_u32x4*>(ln.b_rd[st] + BUF * kTileBytes + j * 32 * 128);
 }
 
 __device__ __forceinline__ void mma_step(const u32x4 (&fa)[4], const u32x4 (&fb)[TJ], f32x16 (&acc)[4][TJ]) {
@@ -394,19 +410,15 @@ __device__ __forceinline__ void mma_step(const u32x4 (&fa)[4], const u32x4 (&fb)
 }
 
 // One k-tile in software-pipelined form.  On entry tile k sits in LDS buffer
-// BUF and its k16 steps 0 and 1 are in (fa0, fb0) and (fa1, fb1); the global
-// fragments of tile k+1 are in (pa, pb).  The fetch of tile k+2 goes to
-// (qa, qb).  Steps 2 and 3 are read while steps 0 and 1 multiply, tile k+1 is
-// written to the other buffer while step 1 multiplies, and the barrier falls
-// between steps 2 and 3, so step 3's products cover the barrier and the first
-// reads of tile k+1.  On exit the invariant holds for tile k+1.
+// BUF and its k16 steps 0 and 1 are in (fa0, fb0) and (fa1, fb1); the loads
+// of tile k+1 into the other buffer are in flight.  Steps 2 and 3 are read
+// while steps 0 and 1 multiply; the barrier falls between steps 2 and 3, once
+// tile k+1 has landed; then tile k2 is issued into BUF (free: every wave has
+// read its steps) while step 3's products cover the first reads of tile k+1.
+// On exit the invariant holds for tile k+1.
 template <int BUF>
-__device__ __forceinline__ void k_step(const Operands& o, const Lanes& ln, int k1, int k2, u32x4 (&pa)[kChunks],
-                                       u32x4 (&pb)[kChunks], u32x4 (&qa)[kChunks], u32x4 (&qb)[kChunks],
-                                       u32x4 (&fa0)[4], u32x4 (&fb0)[TJ], u32x4 (&fa1)[4], u32x4 (&fb1)[TJ],
-                                       f32x16 (&acc)[4][TJ]) {
-  fetch(o, k2, qa, qb);
-  __builtin_amdgcn_sched_barrier(0);
+__device__ __forceinline__ void k_step(const Operands& o, const Lanes& ln, int k2, u32x4 (&fa0)[4], u32x4 (&fb0)[TJ],
+                                       u32x4 (&fa1)[4], u32x4 (&fb1)[TJ], f32x16 (&acc)[4][TJ]) {
   mma_step(fa0, fb0, acc);
   __builtin_amdgcn_sched_barrier(0);
   read_frags<BUF>(ln, 2, fa0, fb0);
@@ -415,36 +427,37 @@ __device__ __forceinline__ void k_step(const Operands& o, const Lanes& ln, int k
   __builtin_amdgcn_sched_barrier(0);
   read_frags<BUF>(ln, 3, fa1, fb1);
   __builtin_amdgcn_sched_barrier(0);
-  stage<1 - BUF>(ln, o, k1, pa, pb);
-  __builtin_amdgcn_sched_barrier(0);
   mma_step(fa0, fb0, acc);
   __builtin_amdgcn_sched_barrier(0);
+  wait_dma();
   __syncthreads();
   read_frags<1 - BUF>(ln, 0, fa0, fb0);
+  __builtin_amdgcn_sched_barrier(0);
+  issue<BUF>(o, ln, k2);
   __builtin_amdgcn_sched_barrier(0);
   mma_step(fa1, fb1, acc);
   __builtin_amdgcn_sched_barrier(0);
   read_frags<1 - BUF>(ln, 1, fa1, fb1);
 }
 
-// acc += A[rows, kb*64 : ke*64] . B[rows, same]^T.  Leaves the LDS ring free.
+// acc += A[rows, kb*64 : ke*64] . B[rows, same]^T.  Leaves the LDS ring free
+// and no load in flight.
 __device__ __forceinline__ void k_loop(const Operands& o, int kb, int ke, f32x16 (&acc)[4][TJ], const Lanes& ln) {
   const int n = ke - kb;
-  u32x4 pa0[kChunks], pb0[kChunks], pa1[kChunks], pb1[kChunks];
   u32x4 fa0[4], fb0[TJ], fa1[4], fb1[TJ];
-  fetch(o, kb, pa0, pb0);
-  fetch(o, min(kb + 1, ke - 1), pa1, pb1);
-  stage<0>(ln, o, kb, pa0, pb0);
+  issue<0>(o, ln, kb);
+  issue<1>(o, ln, min(kb + 1, ke - 1));
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // tile kb has landed (the next tile's eight loads may not)
   __syncthreads();
   read_frags<0>(ln, 0, fa0, fb0);
   read_frags<0>(ln, 1, fa1, fb1);
   for (int k = 0; k < n; k += 2) {
-    // Tiles past the end are fetched, staged and read again as the last
-    // tile (clamped), and never multiplied.
-    k_step<0>(o, ln, min(kb + k + 1, ke - 1), min(kb + k + 2, ke - 1), pa1, pb1, pa0, pb0, fa0, fb0, fa1, fb1, acc);
-    if (k + 1 < n)
-      k_step<1>(o, ln, min(kb + k + 2, ke - 1), min(kb + k + 3, ke - 1), pa0, pb0, pa1, pb1, fa0, fb0, fa1, fb1, acc);
+    // Tiles past the end are loaded again as the last tile (clamped) and
+    // never multiplied.
+    k_step<0>(o, ln, min(kb + k + 2, ke - 1), fa0, fb0, fa1, fb1, acc);
+    if (k + 1 < n) k_step<1>(o, ln, min(kb + k + 3, ke - 1), fa0, fb0, fa1, fb1, acc);
   }
+  wait_dma();
   __syncthreads();
 }
 
