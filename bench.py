@@ -12,8 +12,20 @@ Workloads (synthetic, seeded; value distributions of the measured stacks):
   large60        60 layers, hidden 5376, MLP 21504, rank 256, G=6 (default)
   banded26       26 layers, hidden 1152, MLP 6912, rank 128, G=4
   passthrough26  26 layers, G=26, rank 0, s=1
+  reconstruct60  the 60-layer stack's 420 (layer, projection) weights rebuilt
+                 as diag(s) W0 + U V^T in fp32 (tb_reconstruct_weight) and
+                 compared with the originals a W0_band + N(0, 2e-3) by the
+                 relative Frobenius error (tb_rel_frobenius_error); --rank 0
+                 for the rank-0 bundle
 Token counts <= 64 report GB/s of algorithmic bytes (HBM-bound); larger
 token counts report TFLOP/s of algorithmic flops (matrix-core-bound).
+
+Beside the K-step figure the line carries the per-step spread, the same stack
+replayed from a captured graph, and the GPU clock and power sampled while the
+graph ran.  Stacks whose distinct inputs are smaller than twice the 256 MB
+Infinity Cache are timed over a rotating pool of replicas of at least 1 GiB,
+so that every step reads cold data (the figure reported); the stack-order
+figure from one replica is reported beside it.
 
 Prints one JSON line.  The roofline object covers the dominant kernel; the
 cpu_baseline object times the float64 oracle on a bounded host sample.
@@ -25,8 +37,10 @@ import argparse
 import ctypes
 import hashlib
 import json
+import math
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -36,6 +50,8 @@ METRIC = "theta-bundle projection TFLOP/s (prefill M) and GB/s (decode M), % of 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
 DECODE_MAX_TOKENS = 64
+CACHE_BYTES = 256 << 20        # MI355X Infinity Cache
+COLD_POOL_BYTES = 1 << 30
 
 # Projections of a layer that read the same input, grouped into one call.
 GROUPS = [["q_proj", "k_proj", "v_proj"], ["o_proj"], ["gate_proj", "up_proj"], ["down_proj"]]
@@ -44,17 +60,22 @@ WORKLOADS = {
     "large60": dict(layers=60, shapes="SHAPES_60", rank=256, bands=6, tokens=16, seed=4),
     "banded26": dict(layers=26, shapes="SHAPES_26", rank=128, bands=4, tokens=4, seed=3),
     "passthrough26": dict(layers=26, shapes="SHAPES_26", rank=0, bands=26, tokens=8, seed=2),
+    "reconstruct60": dict(layers=60, shapes="SHAPES_60", rank=256, bands=6, tokens=0, seed=5),
 }
 
 
 def parse():
-    ap = argparse.ArgumentParser()
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="large60", choices=sorted(WORKLOADS))
     ap.add_argument("--tokens", type=int, default=None)
     ap.add_argument("--bands", type=int, default=None)
+    ap.add_argument("--rank", type=int, default=None, help="rank of the bundles (reconstruct60 only)")
+    ap.add_argument("--replicas", type=int, default=None,
+                    help="rotating pool of input replicas (default: enough for >= 1 GiB when the stack is small)")
+    ap.add_argument("--no-graph", action="store_true", help="skip the captured-graph leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-group", action="store_true",
                     help="one tb_linear_forward call per projection instead of grouping q/k/v and gate/up")
@@ -80,12 +101,29 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES, "copies": 4}), flush=True)
 
 
+# ---- algorithmic work -------------------------------------------------------------
+
+
 def call_bytes(M, O, I, R, e=2):
+    """Forward: W0, U, V and s once, x in and y out."""
     return e * (O * I + R * (O + I) + O + M * (I + O))
 
 
 def call_flops(M, O, I, R):
     return 2 * M * (O * I + R * (O + I))
+
+
+def reconstruct_bytes(O, I, R, e_in=2, e_out=4):
+    """Reconstruct: s, W0, U and V in, the rebuilt weight out."""
+    return e_in * (O * I + R * (O + I) + O) + e_out * O * I
+
+
+def frobenius_bytes(O, I, e=4):
+    """Error: both matrices read once."""
+    return 2 * e * O * I
+
+
+# ---- counters committed under profiles/ ---------------------------------------------
 
 
 def kernel_source_digest():
@@ -112,22 +150,113 @@ def counter_traffic(kernel, workload_tag):
     return None
 
 
-def main():
-    args = parse()
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is not sharded across GPUs",
-              file=sys.stderr)
-        sys.exit(2)
+# ---- timing helpers -----------------------------------------------------------------
 
-    import numpy as np
-    import torch
 
-    from rank_factored_linear_amd import binding as tb
-    from rank_factored_linear_amd import inputs as gen
+def timed_steps(torch, run_step, steps):
+    """K steps between two events on the launch stream (the figure reported), with an event at every step
+    boundary in between for the spread."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for k in range(steps):
+        run_step(k)
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[k].elapsed_time(ev[k + 1]) for k in range(steps)]
+    return ev[0].elapsed_time(ev[-1]) / steps, per
 
+
+def spread(per_step_ms):
+    s = sorted(per_step_ms)
+    n = len(s)
+    med = s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+    return {"median_ms": round(med, 4), "min_ms": round(s[0], 4), "max_ms": round(s[-1], 4), "trials": n}
+
+
+class ClockSampler:
+    """GPU shader clock (MHz) and socket power sampled every 50 ms from a side thread (amdsmi through torch).
+    Used only around the graph leg, where the launching thread is idle."""
+
+    def __init__(self, torch):
+        self.torch, self.clk, self.pwr, self.err = torch, [], [], None
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.clk.append(float(self.torch.cuda.clock_rate(0)))
+                self.pwr.append(float(self.torch.cuda.power_draw(0)))
+            except Exception as e:        # amdsmi missing or not permitted: no figure
+                self.err = f"{type(e).__name__}: {e}"[:120]
+                return
+            self._stop.wait(0.05)
+
+    def __enter__(self):
+        self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._t.join(timeout=5)
+
+    def summary(self):
+        if not self.clk:
+            return {"available": False, "reason": self.err or "no samples"}
+        c, p = sorted(self.clk), sorted(self.pwr)
+        return {"available": True, "samples": len(c), "gfx_clock_mhz_median": c[len(c) // 2],
+                "gfx_clock_mhz_min": c[0], "gfx_clock_mhz_max": c[-1],
+                "power_median": p[len(p) // 2], "power_max": p[-1], "power_unit": "as torch.cuda.power_draw"}
+
+
+def graph_leg(torch, make_step, steps, outputs):
+    """Capture one step into a graph and replay it.  Each checked replay's outputs must equal the eager step's
+    bit for bit (the kernels are deterministic); an eager step runs before each checked replay."""
+    side = torch.cuda.Stream()
+    step_on_side = make_step(side.cuda_stream)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step_on_side()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        step_on_side()
+    torch.cuda.synchronize()
+    eager_step = make_step(torch.cuda.current_stream().cuda_stream)
+    for _ in range(2):
+        eager_step()
+        torch.cuda.synchronize()
+        want = [o.clone() for o in outputs]
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(want, outputs):
+            if not torch.equal(a.view(torch.uint8), b.view(torch.uint8)):
+                raise RuntimeError("a replay of the captured step differs from the eager step")
+    for _ in range(2):
+        g.replay()
+    with ClockSampler(torch) as clk:
+        ms, per = timed_steps(torch, lambda k: g.replay(), steps)
+    return ms, per, clk.summary()
+
+
+def _bits(torch, np, t):
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _blas_threads():
+    try:
+        import threadpoolctl
+        return max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+# ---- forward stacks -----------------------------------------------------------------
+
+
+def bench_forward(args, torch, np, tb, gen):
     wl = dict(WORKLOADS[args.workload])
     if args.tokens is not None:
         wl["tokens"] = args.tokens
@@ -136,7 +265,6 @@ def main():
     L, R, G, M = wl["layers"], wl["rank"], wl["bands"], wl["tokens"]
     shapes = getattr(gen, wl["shapes"])
     passthrough = args.workload == "passthrough26"
-    torch.cuda.set_device(0)
     dev = "cuda"
     t_setup = time.time()
 
@@ -160,6 +288,20 @@ def main():
             else:
                 bundles[(l, fam)] = gen.device_bundle(torch, wl["seed"], fam, shapes, l, band_of[l], R, with_w0=False)
             xs[(l, fam)] = gen.device_activations(torch, wl["seed"], fam, shapes, l, M)
+
+    def nbytes(t):
+        return 0 if t is None else t.numel() * t.element_size()
+
+    distinct = sum(nbytes(t) for t in W0.values()) + sum(nbytes(v) for bd in bundles.values() for v in bd.values())
+    replicas = args.replicas
+    if replicas is None:
+        replicas = 1 if distinct >= 2 * CACHE_BYTES else math.ceil(COLD_POOL_BYTES / distinct)
+    # Replica r > 0 holds copies of every weight tensor at addresses of its own; x is shared.
+    pools = [(W0, bundles)]
+    for _ in range(1, replicas):
+        pools.append(({k: t.clone() for k, t in W0.items()},
+                      {k: {n: (None if t is None else t.clone()) for n, t in bd.items()} for k, bd in bundles.items()}))
+
     ys = {fam: torch.empty((M, shapes[fam][0]), dtype=torch.bfloat16, device=dev) for fam in gen.FAMILIES}
     # Projections that take the same layer input go in one grouped call.
     groups = [[f] for f in gen.FAMILIES] if args.no_group else GROUPS
@@ -174,33 +316,39 @@ def main():
     torch.cuda.synchronize()
     t_setup = time.time() - t_setup
 
-    # Prepared argument tuples: the timed loop only crosses the C ABI.
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     fwd = tb.lib.tb_linear_forward
     fwd_group = tb.lib.tb_linear_forward_group
-    calls = []   # (layer, families, function, argument tuple)
-    for l in range(L):
-        for grp in groups:
-            members = []
-            for fam in grp:
-                bd = bundles[(l, fam)]
-                members.append((xs[(l, fam)], bd["s"], W0[(band_of[l], fam)], bd["U"] if R else None,
-                                bd["V"] if R else None, ys[fam]))
-            if len(grp) == 1:
-                x, s_, w0, u, v, y = members[0]
-                O, I = shapes[grp[0]]
-                argv = (x.data_ptr(), s_.data_ptr(), w0.data_ptr(), u.data_ptr() if R else None,
-                        v.data_ptr() if R else None, y.data_ptr(), M, O, I, R, tb.TB_BF16, ws.data_ptr(), ws.numel(),
-                        stream)
-                calls.append((l, grp, fwd, argv))
-            else:
-                arr = tb.projection_array(members)
-                calls.append((l, grp, fwd_group, (len(grp), arr, M, tb.TB_BF16, ws.data_ptr(), ws.numel(), stream)))
+
+    def build_calls(stream_handle, pool):
+        """Prepared argument tuples: the timed loop only crosses the C ABI."""
+        W0p, bundlesp = pool
+        stream = ctypes.c_void_p(stream_handle)
+        calls = []   # (layer, families, function, argument tuple)
+        for l in range(L):
+            for grp in groups:
+                members = []
+                for fam in grp:
+                    bd = bundlesp[(l, fam)]
+                    members.append((xs[(l, fam)], bd["s"], W0p[(band_of[l], fam)], bd["U"] if R else None,
+                                    bd["V"] if R else None, ys[fam]))
+                if len(grp) == 1:
+                    x, s_, w0, u, v, y = members[0]
+                    O, I = shapes[grp[0]]
+                    argv = (x.data_ptr(), s_.data_ptr(), w0.data_ptr(), u.data_ptr() if R else None,
+                            v.data_ptr() if R else None, y.data_ptr(), M, O, I, R, tb.TB_BF16, ws.data_ptr(),
+                            ws.numel(), stream)
+                    calls.append((l, grp, fwd, argv))
+                else:
+                    arr = tb.projection_array(members)   # the tuple keeps the array alive
+                    calls.append((l, grp, fwd_group, (len(grp), arr, M, tb.TB_BF16, ws.data_ptr(), ws.numel(),
+                                                      stream)))
+        return calls
+
     band_idx = tb.lib.tb_band_index
     bout = ctypes.c_int32()
     per_layer = len(groups)
 
-    def step(events=None):
+    def run(calls, events=None):
         n = 0
         for l in range(L):
             band_idx(L, G, l, ctypes.byref(bout))          # band select (host)
@@ -215,6 +363,10 @@ def main():
         if events is not None:
             events[n].record()
 
+    main_stream = torch.cuda.current_stream().cuda_stream
+    pool_calls = [build_calls(main_stream, p) for p in pools]
+    calls = pool_calls[0]
+
     def grp_bytes(grp):
         return sum(call_bytes(M, *shapes[f], R) for f in grp)
 
@@ -225,37 +377,47 @@ def main():
     step_flops = sum(grp_flops(c[1]) for c in calls)
     decode = M <= DECODE_MAX_TOKENS
 
-    for _ in range(args.warmup):
-        step()
+    def rate(ms):
+        return step_bytes / (ms * 1e-3) / 1e9 if decode else step_flops / (ms * 1e-3) / 1e12
+
+    for k in range(args.warmup):
+        run(pool_calls[k % replicas])
     torch.cuda.synchronize()
 
-    # ---- timed region --------------------------------------------------------
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for _ in range(args.steps):
-        step()
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    # ---- timed region: K steps, rotating over the pool (one replica: plain stack order) ----
+    ms, per_step = timed_steps(torch, lambda k: run(pool_calls[k % replicas]), args.steps)
     if tb.workspace_error_word() != 0:
         raise RuntimeError("a bounded wait in the projection kernel timed out")
+    effective = None
+    if replicas > 1:      # the stack from one replica: the cache-assisted stack-order figure
+        ms_eff, per_eff = timed_steps(torch, lambda k: run(calls), args.steps)
+        effective = {"value": round(rate(ms_eff), 3), "ms_per_step": round(ms_eff, 4), **spread(per_eff)}
 
-    # ---- per-launch durations of the projection kernel (same steps again) ----
+    # ---- per-launch durations of the projection kernel (same rotation again) ----
     per_call_ms = np.zeros(len(calls))
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
-    for _ in range(args.steps):
-        step(ev)
+    for k in range(args.steps):
+        run(pool_calls[k % replicas], ev)
         torch.cuda.synchronize()
         per_call_ms += np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(len(calls))])
     per_call_ms /= args.steps
     launch_bytes = np.array([grp_bytes(c[1]) for c in calls], dtype=np.float64)
     launch_flops = np.array([grp_flops(c[1]) for c in calls], dtype=np.float64)
 
+    # ---- the same step replayed from a captured graph ----------------------------
+    graph = None
+    if not args.no_graph:
+        def make_step(handle):
+            c = build_calls(handle, pools[0])
+            return lambda: run(c)
+        g_ms, g_per, clocks = graph_leg(torch, make_step, args.steps, list(ys.values()))
+        graph = {"value": round(rate(g_ms), 3), "ms_per_step": round(g_ms, 4), **spread(g_per),
+                 "pool": "replica 0", "gpu": clocks}
+        if tb.workspace_error_word() != 0:
+            raise RuntimeError("a bounded wait in the projection kernel timed out")
+
     if decode:
         unit = "GB/s"
-        value = step_bytes / (ms * 1e-3) / 1e9
         achieved = launch_bytes.sum() / (per_call_ms.sum() * 1e-3) / 1e9
         kernel = "decode_kernel<bf16,%d,*>" % (1 if M <= 16 else (2 if M <= 32 else 4))
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -263,7 +425,6 @@ def main():
         per_launch = float(launch_bytes.mean())
     else:
         unit = "TFLOP/s"
-        value = step_flops / (ms * 1e-3) / 1e12
         achieved = launch_flops.sum() / (per_call_ms.sum() * 1e-3) / 1e12
         kernel = "big::gemm_kernel (with xv::xv_kernel in the same call)"
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -273,18 +434,15 @@ def main():
     roof["calls_per_step"] = len(calls)
     roof["avg_launch_us"] = round(float(per_call_ms.mean()) * 1e3, 2)
     roof["algorithmic_per_launch"] = round(per_launch, 1)
-    tag = f"{args.workload}_M{M}_G{G}"
-    traffic = counter_traffic(kernel, tag)
-    roof["traffic"] = traffic
+    roof["traffic"] = counter_traffic(kernel, f"{args.workload}_M{M}_G{G}") if replicas == 1 else None
 
-    # ---- CPU baseline: the float64 oracle on a bounded sample ------------------
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args, wl, shapes, calls, bundles, W0, xs, band_of, passthrough, decode)
+        cpu = cpu_baseline_forward(args, wl, shapes, calls, bundles, W0, xs, band_of, decode)
 
     line = {
         "metric": METRIC,
-        "value": round(value, 2 if decode else 3),
+        "value": round(rate(ms), 2 if decode else 3),
         "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
@@ -301,7 +459,11 @@ def main():
                    "grouping": "+".join(",".join(f.split("_")[0] for f in g) for g in groups),
                    "rank": R, "bands": G, "tokens": M,
                    "hidden": shapes["q_proj"][1], "mlp": shapes["gate_proj"][0],
-                   "step_bytes": step_bytes, "step_flops": step_flops, "parallelism": "single-gpu"},
+                   "step_bytes": step_bytes, "step_flops": step_flops, "distinct_input_bytes": distinct,
+                   "replicas": replicas, "parallelism": "single-gpu"},
+        "trials": spread(per_step),
+        "effective_one_replica": effective,
+        "graph": graph,
         "roofline": roof,
         "cpu_baseline": cpu,
     }
@@ -309,21 +471,12 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(args, wl, shapes, calls, bundles, W0, xs, band_of, passthrough, decode):
-    """Time the float64 oracle on the first layer's projections of the same stack."""
+def cpu_baseline_forward(args, wl, shapes, calls, bundles, W0, xs, band_of, decode):
+    """Time the float64 oracle on the first projections of the same stack."""
     import numpy as np
     import torch
 
     import oracle
-
-    try:
-        import threadpoolctl
-        threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
-
-    def bits(t):
-        return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
     M, R = wl["tokens"], wl["rank"]
     Mc = M if decode else min(M, 256)       # prefill: a token slice keeps it bounded
@@ -333,9 +486,10 @@ def cpu_baseline(args, wl, shapes, calls, bundles, W0, xs, band_of, passthrough,
             break
         O, I = shapes[fam]
         bd = bundles[(l, fam)]
-        host = dict(x=bits(xs[(l, fam)][:Mc]), s=bits(bd["s"]), W0=bits(W0[(band_of[l], fam)]))
+        host = dict(x=_bits(torch, np, xs[(l, fam)][:Mc]), s=_bits(torch, np, bd["s"]),
+                    W0=_bits(torch, np, W0[(band_of[l], fam)]))
         if R:
-            host["U"], host["V"] = bits(bd["U"]), bits(bd["V"])
+            host["U"], host["V"] = _bits(torch, np, bd["U"]), _bits(torch, np, bd["V"])
         t = time.perf_counter()
         dec = {k: oracle.bf16_bits_to_f64(v) for k, v in host.items()}
         U = dec.get("U", np.zeros((O, 0)))
@@ -349,9 +503,211 @@ def cpu_baseline(args, wl, shapes, calls, bundles, W0, xs, band_of, passthrough,
         val, unit = done_bytes / secs / 1e9, "GB/s"
     else:
         val, unit = done_flops / secs / 1e12, "TFLOP/s"
-    return {"value": round(val, 4), "unit": unit, "cores": int(threads), "kind": "oracle",
+    return {"value": round(val, 4), "unit": unit, "cores": int(_blas_threads()), "kind": "oracle",
             "sample": f"{len(used)} projections of the same stack ({used[0]} .. {used[-1]}), {Mc} tokens, "
                       f"float64 NumPy incl. bf16 decoding, {secs:.1f} s"}
+
+
+# ---- reconstruction and error stack -------------------------------------------------------
+
+
+def bench_reconstruct(args, torch, np, tb, gen):
+    wl = dict(WORKLOADS["reconstruct60"])
+    if args.bands is not None:
+        wl["bands"] = args.bands
+    if args.rank is not None:
+        wl["rank"] = args.rank
+    L, R, G = wl["layers"], wl["rank"], wl["bands"]
+    shapes = getattr(gen, wl["shapes"])
+    seed = wl["seed"]
+    nfam = len(gen.FAMILIES)
+    t_setup = time.time()
+    band_of = []
+    for l in range(L):
+        b = ctypes.c_int32()
+        assert tb.lib.tb_band_index(L, G, l, ctypes.byref(b)) == 0
+        band_of.append(b.value)
+    W0 = {(b, fam): gen.device_w0(torch, seed, fam, shapes, b) for b in range(G) for fam in gen.FAMILIES}
+    bundles, originals = {}, {}
+    for l in range(L):
+        for fam in gen.FAMILIES:
+            bd = gen.device_bundle(torch, seed, fam, shapes, l, band_of[l], R, with_w0=False)
+            if R == 0:
+                bd["U"] = bd["V"] = None
+            bundles[(l, fam)] = bd
+            originals[(l, fam)] = gen.device_original(torch, W0[(band_of[l], fam)], seed, fam, l)
+    rebuilt = {fam: torch.empty(shapes[fam], dtype=torch.float32, device="cuda") for fam in gen.FAMILIES}
+    errors = torch.zeros(L * nfam, dtype=torch.float64, device="cuda")
+    fws = torch.empty(tb.FROBENIUS_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    t_setup = time.time() - t_setup
+
+    rec = tb.lib.tb_reconstruct_weight
+    frob = tb.lib.tb_rel_frobenius_error
+
+    def build_calls(stream_handle):
+        stream = ctypes.c_void_p(stream_handle)
+        calls = []   # (kind, family, function, argument tuple)
+        for l in range(L):
+            for j, fam in enumerate(gen.FAMILIES):
+                O, I = shapes[fam]
+                bd = bundles[(l, fam)]
+                w = rebuilt[fam]
+                calls.append(("reconstruct", fam, rec,
+                              (bd["s"].data_ptr(), W0[(band_of[l], fam)].data_ptr(),
+                               bd["U"].data_ptr() if R else None, bd["V"].data_ptr() if R else None, w.data_ptr(),
+                               O, I, R, tb.TB_BF16, tb.TB_F32, stream)))
+                calls.append(("frobenius", fam, frob,
+                              (originals[(l, fam)].data_ptr(), w.data_ptr(), O, I, tb.TB_F32,
+                               errors.data_ptr() + 8 * (l * nfam + j), fws.data_ptr(), fws.numel(), stream)))
+        return calls
+
+    band_idx = tb.lib.tb_band_index
+    bout = ctypes.c_int32()
+    per_layer = 2 * nfam
+
+    def run(calls, events=None):
+        n = 0
+        for l in range(L):
+            band_idx(L, G, l, ctypes.byref(bout))          # band select (host)
+            for _ in range(per_layer):
+                if events is not None:
+                    events[n].record()
+                st = calls[n][2](*calls[n][3])
+                if st:
+                    raise RuntimeError(tb.lib.tb_last_error().decode())
+                n += 1
+        if events is not None:
+            events[n].record()
+
+    calls = build_calls(torch.cuda.current_stream().cuda_stream)
+    nbytes = np.array([reconstruct_bytes(*shapes[c[1]], R) if c[0] == "reconstruct" else
+                       frobenius_bytes(*shapes[c[1]]) for c in calls], dtype=np.float64)
+    step_bytes = float(nbytes.sum())
+    step_flops = sum(2 * shapes[c[1]][0] * shapes[c[1]][1] * R for c in calls if c[0] == "reconstruct")
+
+    for _ in range(args.warmup):
+        run(calls)
+    torch.cuda.synchronize()
+    ms, per_step = timed_steps(torch, lambda k: run(calls), args.steps)
+    err_host = errors.cpu().numpy()
+
+    per_call_ms = np.zeros(len(calls))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+    for _ in range(args.steps):
+        run(calls, ev)
+        torch.cuda.synchronize()
+        per_call_ms += np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(len(calls))])
+    per_call_ms /= args.steps
+
+    graph = None
+    if not args.no_graph:
+        def make_step(handle):
+            c = build_calls(handle)
+            return lambda: run(c)
+        g_ms, g_per, clocks = graph_leg(torch, make_step, args.steps, [errors] + list(rebuilt.values()))
+        graph = {"value": round(step_bytes / (g_ms * 1e-3) / 1e9, 2), "ms_per_step": round(g_ms, 4),
+                 **spread(g_per), "gpu": clocks}
+
+    kernels = {}
+    for kind, name in (("reconstruct", "reconstruct_lowrank_kernel" if R else "reconstruct_rank0_kernel"),
+                       ("frobenius", "frob_pass1 + frob_pass2")):
+        sel = np.array([c[0] == kind for c in calls])
+        t = float(per_call_ms[sel].sum())
+        gbs = float(nbytes[sel].sum()) / (t * 1e-3) / 1e9
+        kernels[kind] = {"kernel": name, "ms_per_step": round(t, 4), "achieved": round(gbs, 1),
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "algorithmic_per_launch": round(float(nbytes[sel].mean()), 1)}
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    roof = {"bound": "hbm", "achieved": kernels[dom]["achieved"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": kernels[dom]["frac"], "kernel": kernels[dom]["kernel"], "calls_per_step": L * nfam,
+            "avg_launch_us": round(kernels[dom]["ms_per_step"] * 1e3 / (L * nfam), 2),
+            "algorithmic_per_launch": kernels[dom]["algorithmic_per_launch"],
+            "traffic": counter_traffic(kernels[dom]["kernel"], f"reconstruct60_R{R}_G{G}"), "kernels": kernels}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_reconstruct(args, shapes, bundles, W0, originals, band_of, L, R, gen)
+
+    line = {
+        "metric": METRIC,
+        "value": round(step_bytes / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16->f32",
+        "data": "synthetic",
+        "config": {"workload": f"reconstruct60: {L}-layer stack, 7 projections per layer, rank {R}, G={G} bands, "
+                               f"rebuilt in fp32 and compared with the originals",
+                   "layers": L, "rank": R, "bands": G, "pairs_per_step": L * nfam,
+                   "step_bytes": step_bytes, "step_flops": step_flops, "parallelism": "single-gpu",
+                   "mean_rel_error": float(err_host.mean()), "max_rel_error": float(err_host.max())},
+        "trials": spread(per_step),
+        "graph": graph,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(f"# setup {t_setup:.1f}s  step {ms:.3f} ms  per-launch sum {per_call_ms.sum():.3f} ms", file=sys.stderr)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_reconstruct(args, shapes, bundles, W0, originals, band_of, L, R, gen):
+    """Time the float64 oracle's reconstruct + error on the first (layer, projection) pairs of the stack."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    done_bytes, secs, used = 0, 0.0, []
+    for l, fam in ((l, f) for l in range(L) for f in gen.FAMILIES):
+        if secs > args.cpu_seconds:
+            break
+        O, I = shapes[fam]
+        bd = bundles[(l, fam)]
+        s_bits, w0_bits = _bits(torch, np, bd["s"]), _bits(torch, np, W0[(band_of[l], fam)])
+        u_bits = _bits(torch, np, bd["U"]) if R else None
+        v_bits = _bits(torch, np, bd["V"]) if R else None
+        orig = originals[(l, fam)].cpu().numpy()
+        t = time.perf_counter()
+        s, w0 = oracle.bf16_bits_to_f64(s_bits), oracle.bf16_bits_to_f64(w0_bits)
+        U = oracle.bf16_bits_to_f64(u_bits) if R else np.zeros((O, 0))
+        V = oracle.bf16_bits_to_f64(v_bits) if R else np.zeros((I, 0))
+        oracle.relative_frobenius_error(orig, oracle.reconstruct_weight(s, w0, U, V))
+        secs += time.perf_counter() - t
+        done_bytes += reconstruct_bytes(O, I, R) + frobenius_bytes(O, I)
+        used.append(f"{l}:{fam}")
+    return {"value": round(done_bytes / secs / 1e9, 4), "unit": "GB/s", "cores": int(_blas_threads()),
+            "kind": "oracle",
+            "sample": f"{len(used)} (layer, projection) pairs of the same stack ({used[0]} .. {used[-1]}): "
+                      f"float64 NumPy reconstruct incl. bf16 decoding, then the error, {secs:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is not sharded across GPUs",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from rank_factored_linear_amd import binding as tb
+    from rank_factored_linear_amd import inputs as gen
+
+    torch.cuda.set_device(0)
+    if args.workload == "reconstruct60":
+        bench_reconstruct(args, torch, np, tb, gen)
+    else:
+        bench_forward(args, torch, np, tb, gen)
 
 
 if __name__ == "__main__":

@@ -614,6 +614,10 @@ constexpr int kXTile = BM * kXPitch;   // 9 KB
 constexpr int kVTile = BK * kVPitch;   // 36 KB
 constexpr int kRingBytes = 2 * kVTile + 2 * kXTile;  // [V0][V1][X0][X1]
 constexpr int kPartFloats = BM * BN;
+// x tiles are read by one column block of T only (rank <= 256), while every
+// row block re-reads the V tiles: x is loaded non-temporal (the NT bit of the
+// buffer load's cache policy) so that it does not push V out of L2.
+constexpr int kXPolicy = 2;
 
 struct Args {
   const bf16_t* x;
@@ -659,7 +663,7 @@ struct Src {
 
 __device__ __forceinline__ void fetch(const Src& s, int kt, u32x4 (&px)[2], u32x4 (&pv)[8]) {
 #pragma unroll
-  for (int q = 0; q < 2; ++q) px[q] = __builtin_amdgcn_raw_buffer_load_b128(s.rx, s.xoff, kt * BK * 2 + q * s.xstep, 0);
+  for (int q = 0; q < 2; ++q) px[q] = __builtin_amdgcn_raw_buffer_load_b128(s.rx, s.xoff, kt * BK * 2 + q * s.xstep, kXPolicy);
 #pragma unroll
   for (int q = 0; q < 8; ++q)
     pv[q] = __builtin_amdgcn_raw_buffer_load_b128(s.rv, s.voff, kt * 8 * s.vstep + q * s.vstep, 0);

@@ -5,8 +5,14 @@
 // consecutive elements of one row (16-byte loads, 16/32-byte stores).
 // rank > 0 is a K = rank GEMM (U rows and V rows are both contiguous along
 // the rank dimension) on the matrix cores with the scaled copy fused into the
-// epilogue; at rank 256 it is still HBM-bound but needs far more than the
-// fp32 vector rate to keep up with HBM.
+// epilogue; at rank 256 it is still HBM-bound (6 bytes of W0 and fp32 output
+// per 512 flops) but needs far more than the fp32 vector rate to keep up.
+//
+// bf16 bundles with rank % 8 == 0 take reconstruct_mfma_kernel: 128 x 128
+// output tiles, k-tiles of 64 staged in LDS (16-byte chunks XOR-swizzled by
+// row), four waves of 64 x 64 on v_mfma_f32_32x32x16_bf16.  The product is
+// taken as V . U^T, so that each lane ends up holding four consecutive
+// columns of one output row: 8-byte W0 loads and 16-byte fp32 stores.
 #include "tb_device.h"
 #include "tb_host.h"
 
@@ -91,6 +97,441 @@ __global__ __launch_bounds__(kThreads) void reconstruct_lowrank_kernel(const EI*
   }
 }
 
+// ---- bf16 bundles, rank % 8 == 0 --------------------------------------------
+namespace mm {
+
+constexpr int BT = 128;              // output tile: BT rows of U (o) x BT rows of V (i)
+constexpr int BK = 64;               // k-tile (rank) staged in LDS
+constexpr int kRowBytes = BK * 2;    // 128-byte LDS rows of 8 16-byte chunks
+constexpr int kTileBytes = BT * kRowBytes;
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mma32(uint4 a, uint4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
+                                                 0);
+}
+
+// Byte offset of chunk c of row r inside a tile: the chunk index is XORed
+// with r % 8, so eight consecutive rows read at one chunk hit all 32 banks.
+__device__ __forceinline__ int chunk_off(int r, int c) { return r * kRowBytes + ((c ^ (r & 7)) << 4); }
+
+template <typename EO>
+__device__ __forceinline__ void store4(EO* p, float a, float b, float c, float d) {
+  if constexpr (sizeof(EO) == 4) {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+  } else {
+    *reinterpret_cast<uint2*>(p) = make_uint2(f32_to_bf16(a) | (uint32_t(f32_to_bf16(b)) << 16),
+                                              f32_to_bf16(c) | (uint32_t(f32_to_bf16(d)) << 16));
+  }
+}
+
+// blockIdx.x: 128-column block of the output (rows of V); blockIdx.y: 128-row
+// block (rows of U).  Wave w owns output rows 64 (w / 2) .. +63 and columns
+// 64 (w % 2) .. +63 of the tile.
+template <typename EO>
+__global__ __launch_bounds__(kThreads, 2) void reconstruct_mfma_kernel(const bf16_t* __restrict__ s,
+                                                                        const bf16_t* __restrict__ w0,
+                                                                        const bf16_t* __restrict__ u,
+                                                                        const bf16_t* __restrict__ v,
+                                                                        EO* __restrict__ out, int O, int I, int R) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kTileBytes];  // [U tile][V tile]
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int i0 = blockIdx.x * BT, o0 = blockIdx.y * BT;
+  const int wi = w & 1, wo = w >> 1;
+
+  // Staging: thread t moves chunk t % 8 of rows t / 8 + 32 q (q = 0..3) of both tiles.
+  const int sc = tid & 7, sr = tid >> 3;
+  uint4 su[4], sv[4];
+  auto fetch = [&](int kt) {
+    const int k = kt * BK + sc * 8;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int ro = o0 + sr + 32 * q, ri = i0 + sr + 32 * q;
+      su[q] = (ro < O && k < R) ? *reinterpret_cast<const uint4*>(u + size_t(ro) * R + k) : make_uint4(0, 0, 0, 0);
+      sv[q] = (ri < I && k < R) ? *reinterpret_cast<const uint4*>(v + size_t(ri) * R + k) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int off = chunk_off(sr + 32 * q, sc);
+      *reinterpret_cast<uint4*>(lds + off) = su[q];
+      *reinterpret_cast<uint4*>(lds + kTileBytes + off) = sv[q];
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+  const int KT = (R + BK - 1) / BK;
+  const int h = l >> 5, lr = l & 31;
+  fetch(0);
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt) __syncthreads();          // every wave has read the previous k-tile
+    stash();
+    __syncthreads();
+    if (kt + 1 < KT) fetch(kt + 1);   // lands while this k-tile multiplies
+    uint4 fa[2][4], fb[2][4];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int ri = wi * 64 + rb * 32 + lr, ro = wo * 64 + rb * 32 + lr;
+        fa[rb][ks] = *reinterpret_cast<const uint4*>(lds + kTileBytes + chunk_off(ri, ks * 2 + h));
+        fb[rb][ks] = *reinterpret_cast<const uint4*>(lds + chunk_off(ro, ks * 2 + h));
+      }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mma32(fa[rb][ks], fb[cb][ks], acc[rb][cb]);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_operand_guard();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // acc[rb][cb] element 4 b + e is C[i][o] with i = 64 wi + 32 rb + 8 b + 4 h + e and
+  // o = 64 wo + 32 cb + lr (tile-relative): out[o][i .. i+3] per (rb, cb, b).
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int o = o0 + wo * 64 + cb * 32 + lr;
+    if (o >= O) continue;
+    const float so = bf16_to_f32(s[o].bits);
+    const bf16_t* wrow = w0 + size_t(o) * I;
+    EO* orow = out + size_t(o) * I;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int i = i0 + wi * 64 + rb * 32 + 8 * b + 4 * h;   // I % 8 == 0: i < I covers i .. i+3
+        if (i >= I) continue;
+        const uint2 wv = *reinterpret_cast<const uint2*>(wrow + i);
+        const f32x16& c = acc[rb][cb];
+        store4<EO>(orow + i, c[4 * b + 0] + so * bf16_to_f32(uint16_t(wv.x)),
+                   c[4 * b + 1] + so * bf16_to_f32(uint16_t(wv.x >> 16)),
+                   c[4 * b + 2] + so * bf16_to_f32(uint16_t(wv.y)),
+                   c[4 * b + 3] + so * bf16_to_f32(uint16_t(wv.y >> 16)));
+      }
+  }
+}
+
+}  // namespace mm
+
+// ---- bf16 bundles, 192 < rank <= 256: persistent, direct-to-LDS ----------------
+//
+// One workgroup per compute unit walks its output tiles (128 x 128) in turn.
+// A tile's whole U and V (four k-tiles of 64) fit the 128 KB LDS ring, one
+// slot per k-tile, filled by direct-to-LDS buffer loads; each slot is
+// refilled for the next tile as soon as every wave has read it, so the loads
+// of tile j+1 fly while tile j multiplies.  The W0 and s values of tile j+1
+// are loaded into registers at the end of tile j's epilogue and so have a
+// whole tile's time to arrive.  The epilogue moves each wave's 64 x 64
+// accumulators through LDS (the slot of the last k-tile) so that 16 lanes
+// cover 64 consecutive outputs of one row: 128-byte W0 reads and 256-byte
+// non-temporal fp32 writes per row.
+//
+// Memory instructions complete in issue order, so the wait for a k-tile is a
+// count of the loads and stores issued after it: every load and store here
+// is issued unconditionally (lanes outside the matrix get an offset past the
+// buffer: loads return zero, stores are dropped), tiles past a workgroup's
+// last one are loaded as zeros, and the counts below are exact.
+namespace rp {
+
+constexpr int BT = 128, BK = 64, KT = 4;
+constexpr int kOpBytes = BT * BK * 2;         // one operand's k-tile: 128 rows of 128 bytes
+constexpr int kSlotBytes = 2 * kOpBytes;      // [U k-tile][V k-tile]
+constexpr int kRingBytes = KT * kSlotBytes;   // 128 KB
+constexpr int kStageRow = 256;                // epilogue staging: rows of 64 fp32 per wave
+constexpr unsigned kRsrcFlags = 0x00020000u;  // buffer descriptor word 3: 32-bit data format
+constexpr int kPast = int(0x80000000u);       // lane offset past every buffer
+constexpr int kNT = 2;                        // non-temporal cache policy
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) uint8_t lds_byte;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+
+__device__ __forceinline__ lds_byte* opaque(lds_byte* p) {
+  asm volatile("" : "+v"(p));
+  return p;
+}
+
+// Buffer views of one output tile (uniform: scalar registers).
+struct Tile {
+  int o0, i0, orows, irows;
+  __amdgpu_buffer_rsrc_t ru, rv, rw, rs, ro;
+};
+
+template <typename EO>
+__device__ __forceinline__ Tile tile_at(int t, int tiles_i, const bf16_t* s, const bf16_t* w0, const bf16_t* u,
+                                        const bf16_t* v, EO* out, int O, int I, int R) {
+  Tile g;
+  const int bo = t / tiles_i, bi = t - bo * tiles_i;
+  g.o0 = bo * BT;
+  g.i0 = bi * BT;
+  g.orows = min(O - g.o0, BT);
+  g.irows = min(I - g.i0, BT);
+  g.ru = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(u + size_t(g.o0) * R), 0, g.orows * R * 2, kRsrcFlags);
+  g.rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(v + size_t(g.i0) * R), 0, g.irows * R * 2, kRsrcFlags);
+  g.rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(w0 + size_t(g.o0) * I), 0, g.orows * I * 2, kRsrcFlags);
+  g.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(s + g.o0), 0, g.orows * 2, kRsrcFlags);
+  g.ro = __builtin_amdgcn_make_buffer_rsrc(out + size_t(g.o0) * I, 0, g.orows * I * int(sizeof(EO)), kRsrcFlags);
+  return g;
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// Four direct-to-LDS loads: load j writes 1 KB at dst + j KB (lane l at
+// +16 l) from lane offset v[j] + soff.  The buffer's range check covers the
+// lane offset only, so every lane offset carries its row and chunk (or lies
+// past the buffer: the lane then writes zeros).  M0 takes one wait state
+// before a load that reads it.
+__device__ __forceinline__ void dma4(unsigned dst, __amdgpu_buffer_rsrc_t r, const int (&v)[4], int soff) {
+  asm volatile(
+      "s_mov_b32 m0, %[d0]\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[v0], %[r], %[so] offen lds\n\t"
+      "s_mov_b32 m0, %[d1]\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[v1], %[r], %[so] offen lds\n\t"
+      "s_mov_b32 m0, %[d2]\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[v2], %[r], %[so] offen lds\n\t"
+      "s_mov_b32 m0, %[d3]\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[v3], %[r], %[so] offen lds"
+      :
+      : [d0] "s"(dst), [d1] "s"(dst + 1024u), [d2] "s"(dst + 2048u), [d3] "s"(dst + 3072u), [v0] "v"(v[0]),
+        [v1] "v"(v[1]), [v2] "v"(v[2]), [v3] "v"(v[3]), [r] "s"(r), [so] "s"(soff)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Per-lane constants of the direct-to-LDS loads: wave w fills rows
+// 32 w + 8 j + l / 8 (j = 0..3) of each operand's k-tile; lane l lands in
+// chunk l % 8 of its row and fetches the global chunk that the swizzle
+// (row >> 1) & 7 stores there.  Even and odd j share a swizzle.
+struct Dma {
+  unsigned dst;      // this wave's first KB of slot 0, U operand
+  int row, ce, co;   // row of load 0; global chunks fetched by even and odd j
+};
+
+// k-tile kt of tile g into ring slot SLOT.  Rows past the tile's, chunks past
+// the rank and every lane of a dummy tile (past the workgroup's last) write
+// zeros.
+template <int SLOT>
+__device__ __forceinline__ void issue(const Dma& d, const Tile& g, int kt, bool dummy, int R) {
+  const int left = R - kt * BK;
+  int vu[4], vv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = d.row + 8 * j, c = (j & 1) ? d.co : d.ce;
+    const bool ok = !dummy && c * 8 < left;
+    const int off = row * R * 2 + (c << 4);
+    vu[j] = (ok && row < g.orows) ? off : kPast;
+    vv[j] = (ok && row < g.irows) ? off : kPast;
+  }
+  dma4(d.dst + SLOT * kSlotBytes, g.ru, vu, kt * BK * 2);
+  dma4(d.dst + SLOT * kSlotBytes + kOpBytes, g.rv, vv, kt * BK * 2);
+}
+
+// Epilogue layout: in round cb (0, 1) lane l of wave w handles output row
+// 64 (w / 2) + 32 cb + 4 p + l / 16 (p = 0..7) and columns 64 (w % 2) + 4 (l % 16) .. +3
+// of the tile.
+struct Pre {
+  u32x2 w[2][8];
+  uint32_t s[2][8];
+};
+
+template <typename EO>
+__device__ __forceinline__ int out_off(const Tile& g, int I, int wo, int wi, int cb, int p, int l) {
+  const int orel = wo * 64 + cb * 32 + 4 * p + (l >> 4), i = g.i0 + wi * 64 + (l & 15) * 4;
+  return (orel < g.orows && i < I) ? (orel * I + i) * int(sizeof(EO)) : kPast;
+}
+
+__device__ __forceinline__ void prefetch(Pre& q, const Tile& g, bool dummy, int I, int wo, int wi, int l) {
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int orel = wo * 64 + cb * 32 + 4 * p + (l >> 4), i = g.i0 + wi * 64 + (l & 15) * 4;
+      const bool ok = !dummy && orel < g.orows && i < I;
+      q.w[cb][p] = __builtin_amdgcn_raw_buffer_load_b64(g.rw, ok ? (orel * I + i) * 2 : kPast, 0, 0);
+      q.s[cb][p] = __builtin_amdgcn_raw_buffer_load_b16(g.rs, (!dummy && orel < g.orows) ? orel * 2 : kPast, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);  // issue in order of use
+    }
+}
+
+__device__ __forceinline__ f32x16 mma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
+                                                 0);
+}
+
+// Fragments of k16 steps 0..3 of the k-tile in ring slot SLOT (A from V rows
+// 64 wi + 32 rb + lane % 32, B from U rows 64 wo + 32 cb + lane % 32, chunk
+// 2 ks + lane / 32, swizzled), then the 16 products.
+template <int SLOT>
+__device__ __forceinline__ void multiply_step(lds_byte* const (&rdU)[2][4], lds_byte* const (&rdV)[2][4],
+                                              f32x16 (&acc)[2][2]) {
+  constexpr int pr = SLOT / 2, off = (SLOT % 2) * kSlotBytes;
+  u32x4 fa[2][4], fb[2][4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      fa[r][ks] = *reinterpret_cast<const lds_u32x4*>(rdV[pr][ks] + off + kOpBytes + r * 32 * 128);
+      fb[r][ks] = *reinterpret_cast<const lds_u32x4*>(rdU[pr][ks] + off + r * 32 * 128);
+    }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mma32(fa[rb][ks], fb[cb][ks], acc[rb][cb]);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_operand_guard();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <typename EO>
+__device__ __forceinline__ void store_out(const Tile& g, int off, f32x4 c, u32x2 wv, float so) {
+  const float r0 = c[0] + so * bf16_to_f32(uint16_t(wv[0])), r1 = c[1] + so * bf16_to_f32(uint16_t(wv[0] >> 16));
+  const float r2 = c[2] + so * bf16_to_f32(uint16_t(wv[1])), r3 = c[3] + so * bf16_to_f32(uint16_t(wv[1] >> 16));
+  if constexpr (sizeof(EO) == 4) {
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(r0), __float_as_uint(r1), __float_as_uint(r2),
+                                                 __float_as_uint(r3)},
+                                           g.ro, off, 0, kNT);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{f32_to_bf16(r0) | (uint32_t(f32_to_bf16(r1)) << 16),
+                                                f32_to_bf16(r2) | (uint32_t(f32_to_bf16(r3)) << 16)},
+                                          g.ro, off, 0, kNT);
+  }
+}
+
+template <typename EO>
+__global__ __launch_bounds__(kThreads, 1) void reconstruct_persistent_kernel(const bf16_t* __restrict__ s,
+                                                                             const bf16_t* __restrict__ w0,
+                                                                             const bf16_t* __restrict__ u,
+                                                                             const bf16_t* __restrict__ v,
+                                                                             EO* __restrict__ out, int O, int I,
+                                                                             int R, int tiles_i, int tiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes];
+  const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6), l = int(threadIdx.x) & 63;
+  const int wi = w & 1, wo = w >> 1, lr = l & 31, h = l >> 5;
+  const int G = int(gridDim.x);
+  int t = int(blockIdx.x);
+  if (t >= tiles) return;
+
+  lds_byte* base = (lds_byte*)ring;
+  Dma d;
+  {
+    const int pos = l & 7;
+    d.row = w * 32 + (l >> 3);
+    d.ce = pos ^ ((d.row >> 1) & 7);
+    d.co = pos ^ (((d.row + 8) >> 1) & 7);
+    d.dst = __builtin_amdgcn_readfirstlane(unsigned(uintptr_t(base)) + unsigned(w) * 4096u);
+  }
+  // Fragment bases per slot pair (0/1, 2/3) and k16 step: U row 64 wo + lane % 32,
+  // V row 64 wi + lane % 32 (the V operand sits kOpBytes into each slot).
+  lds_byte* rdU[2][4];
+  lds_byte* rdV[2][4];
+  {
+    const int x = (lr >> 1) & 7;
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int chunk = ((2 * ks + h) ^ x) << 4;
+        rdU[pr][ks] = opaque(base + pr * 2 * kSlotBytes + (wo * 64 + lr) * 128 + chunk);
+        rdV[pr][ks] = opaque(base + pr * 2 * kSlotBytes + (wi * 64 + lr) * 128 + chunk);
+      }
+  }
+  lds_byte* stage = base + 3 * kSlotBytes + w * 8192;
+
+  f32x16 acc[2][2];
+  Pre q;
+  Tile g = tile_at<EO>(t, tiles_i, s, w0, u, v, out, O, I, R);
+  issue<0>(d, g, 0, false, R);
+  issue<1>(d, g, 1, false, R);
+  issue<2>(d, g, 2, false, R);
+  prefetch(q, g, false, I, wo, wi, l);
+
+  for (int j = 0;; ++j) {
+    const int tn = t + G;
+    const bool has_next = tn < tiles;
+    const Tile gn = tile_at<EO>(has_next ? tn : t, tiles_i, s, w0, u, v, out, O, I, R);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+    // Step k: wait for k-tile k, publish it, refill the slot every wave has
+    // just finished with, multiply.
+    if (j == 0) wait_vm<48>(); else wait_vm<63>();
+    __syncthreads();
+    issue<3>(d, g, 3, false, R);
+    multiply_step<0>(rdU, rdV, acc);
+    if (j == 0) wait_vm<48>(); else wait_vm<63>();
+    __syncthreads();
+    issue<0>(d, gn, 0, !has_next, R);
+    multiply_step<1>(rdU, rdV, acc);
+    if (j == 0) wait_vm<48>(); else wait_vm<63>();
+    __syncthreads();
+    issue<1>(d, gn, 1, !has_next, R);
+    multiply_step<2>(rdU, rdV, acc);
+    wait_vm<16>();
+    __syncthreads();
+    issue<2>(d, gn, 2, !has_next, R);
+    multiply_step<3>(rdU, rdV, acc);
+
+    // Epilogue through the staging area (slot 3, free once every wave has
+    // read its fragments).
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      __syncthreads();
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int chunk = (8 * rb + 2 * b + h) ^ (lr & 15);
+          const f32x16& c = acc[rb][cb];
+          *reinterpret_cast<lds_f32x4*>(stage + lr * kStageRow + (chunk << 4)) =
+              f32x4{c[4 * b], c[4 * b + 1], c[4 * b + 2], c[4 * b + 3]};
+        }
+      __syncthreads();
+      f32x4 c[8];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const int orel = 4 * p + (l >> 4), chunk = (l & 15) ^ (orel & 15);
+        c[p] = *reinterpret_cast<const lds_f32x4*>(stage + orel * kStageRow + (chunk << 4));
+      }
+#pragma unroll
+      for (int p = 0; p < 8; ++p)
+        store_out<EO>(g, out_off<EO>(g, I, wo, wi, cb, p, l), c[p], q.w[cb][p], bf16_to_f32(uint16_t(q.s[cb][p])));
+    }
+    prefetch(q, gn, !has_next, I, wo, wi, l);
+    if (!has_next) break;
+    t = tn;
+    g = gn;
+  }
+  wait_vm<0>();  // no load into LDS may still be in flight when the workgroup ends
+}
+
+}  // namespace rp
+
 template <typename EI, typename EO>
 hipError_t launch_typed(const void* s, const void* w0, const void* u, const void* v, void* w_out, int64_t O, int64_t I,
                         int64_t R, hipStream_t stream) {
@@ -100,6 +541,20 @@ hipError_t launch_typed(const void* s, const void* w0, const void* u, const void
     if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL((reconstruct_rank0_kernel<EI, EO>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
                        static_cast<const EI*>(s), static_cast<const EI*>(w0), static_cast<EO*>(w_out), n8, int(I));
+  } else if (sizeof(EI) == 2 && R % 8 == 0 && R > 3 * rp::BK && R <= 4 * rp::BK && I < (1 << 22) &&
+             O < (1 << 24)) {
+    int cus = 0;
+    if (int e = device_cu_count(&cus)) return hipError_t(e);
+    const int tiles_i = int((I + rp::BT - 1) / rp::BT), tiles = tiles_i * int((O + rp::BT - 1) / rp::BT);
+    const int grid = tiles < cus ? tiles : cus;
+    hipLaunchKernelGGL((rp::reconstruct_persistent_kernel<EO>), dim3(unsigned(grid)), dim3(kThreads), 0, stream,
+                       static_cast<const bf16_t*>(s), static_cast<const bf16_t*>(w0), static_cast<const bf16_t*>(u),
+                       static_cast<const bf16_t*>(v), static_cast<EO*>(w_out), int(O), int(I), int(R), tiles_i, tiles);
+  } else if (sizeof(EI) == 2 && R % 8 == 0 && (O + mm::BT - 1) / mm::BT <= 65535) {
+    dim3 grid(unsigned((I + mm::BT - 1) / mm::BT), unsigned((O + mm::BT - 1) / mm::BT));
+    hipLaunchKernelGGL((mm::reconstruct_mfma_kernel<EO>), grid, dim3(kThreads), 0, stream,
+                       static_cast<const bf16_t*>(s), static_cast<const bf16_t*>(w0), static_cast<const bf16_t*>(u),
+                       static_cast<const bf16_t*>(v), static_cast<EO*>(w_out), int(O), int(I), int(R));
   } else {
     dim3 grid(unsigned((I + 63) / 64), unsigned((O + 63) / 64));
     hipLaunchKernelGGL((reconstruct_lowrank_kernel<EI, EO>), grid, dim3(kThreads), 0, stream, static_cast<const EI*>(s),

@@ -30,3 +30,18 @@ def test_algorithmic_counts():
 
 def test_traffic_record_requires_current_kernel_source(tmp_path, monkeypatch):
     assert len(bench.kernel_source_digest()) == 16
+
+
+def test_reconstruct_and_error_bytes_per_stack():
+    # The 60-layer stack's 420 weights: rebuild in fp32 from bf16 bundles (rank 256 and 0), then read the
+    # rebuilt and the original fp32 matrices once for the error.
+    from rank_factored_linear_amd import inputs
+    shapes = inputs.SHAPES_60.values()
+    assert 60 * sum(bench.reconstruct_bytes(o, i, 256) for o, i in shapes) == 168_265_052_160
+    assert 60 * sum(bench.reconstruct_bytes(o, i, 0) for o, i in shapes) == 164_498_042_880
+    assert 60 * sum(bench.frobenius_bytes(o, i) for o, i in shapes) == 219_320_156_160
+
+
+def test_spread_of_trials():
+    assert bench.spread([3.0, 1.0, 2.0]) == {"median_ms": 2.0, "min_ms": 1.0, "max_ms": 3.0, "trials": 3}
+    assert bench.spread([4.0, 1.0, 2.0, 3.0])["median_ms"] == 2.5

@@ -249,7 +249,9 @@ def test_forward_split_rounds(shape):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
-@pytest.mark.parametrize("shape", [(17, 40, 4), (130, 264, 12), (64, 512, 256), (33, 72, 0), (1, 8, 3)],
+@pytest.mark.parametrize("shape", [(17, 40, 4), (130, 264, 12), (64, 512, 256), (33, 72, 0), (1, 8, 3), (1, 8, 8),
+                                   (130, 264, 24), (300, 520, 72), (257, 1032, 136), (128, 128, 64), (384, 8, 512),
+                                   (130, 264, 200), (300, 520, 256), (257, 1032, 248), (1, 8, 256), (2100, 2104, 256)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_reconstruct_edge_shapes(shape, dtype):
     O, I, R = shape
@@ -357,3 +359,39 @@ def test_stream_ordering_many_calls():
         for y in outs[2 * i: 2 * i + 2]:
             assert oracle.relative_frobenius_error(ref, exact(y)) <= BF16_TOL
     assert tb.workspace_error_word() == 0
+
+
+@pytest.mark.parametrize("M", [1, 16, 64, 300])
+def test_forward_replays_from_captured_graph(M):
+    # A single call and a grouped call captured into a graph: every replay writes the eager results bit for
+    # bit, with eager calls of another shape (their own workspace) between the replays.
+    _say(f"graph capture M={M}")
+    single = _rand_case(M, 2048, 5376, 256, torch.bfloat16, seed=5)
+    group = [_rand_case(M, O, I, R, torch.bfloat16, seed=7 + j) for j, (O, I, R) in enumerate(GROUPS["qkv60"])]
+    other = _rand_case(8, 256, 1152, 128, torch.bfloat16, seed=3)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):       # eager run on the capture stream sizes its workspace
+        want1 = tb.linear_forward(*single).clone()
+        wantg = [y.clone() for y in tb.linear_forward_group(group)]
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        y1 = tb.linear_forward(*single)
+        yg = tb.linear_forward_group(group)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        tb.linear_forward(*other)
+        for y in [y1] + yg:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), want1.view(torch.int16)), rep
+        for a, b in zip(yg, wantg):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), rep
+    assert tb.workspace_error_word() == 0
+    with torch.cuda.stream(side):
+        assert tb.workspace_error_word() == 0
+    assert oracle.relative_frobenius_error(_oracle_forward(*single), exact(want1)) <= BF16_TOL
