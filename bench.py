@@ -538,7 +538,7 @@ def bench_reconstruct(args, torch, np, tb, gen):
             originals[(l, fam)] = gen.device_original(torch, W0[(band_of[l], fam)], seed, fam, l)
     rebuilt = {fam: torch.empty(shapes[fam], dtype=torch.float32, device="cuda") for fam in gen.FAMILIES}
     errors = torch.zeros(L * nfam, dtype=torch.float64, device="cuda")
-    fws = torch.empty(tb.FROBENIUS_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    fws = torch.zeros(tb.FROBENIUS_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
     t_setup = time.time() - t_setup
 
@@ -610,8 +610,11 @@ def bench_reconstruct(args, torch, np, tb, gen):
                  **spread(g_per), "gpu": clocks}
 
     kernels = {}
-    for kind, name in (("reconstruct", "reconstruct_lowrank_kernel" if R else "reconstruct_rank0_kernel"),
-                       ("frobenius", "frob_pass1 + frob_pass2")):
+    rec_kernel = ("reconstruct_rank0_kernel" if R == 0 else
+                  "rp::reconstruct_persistent_kernel" if 192 < R <= 256 and R % 8 == 0 else
+                  "mm::reconstruct_mfma_kernel" if R % 8 == 0 else "reconstruct_lowrank_kernel")
+    for kind, name in (("reconstruct", rec_kernel),
+                       ("frobenius", "frob_kernel")):
         sel = np.array([c[0] == kind for c in calls])
         t = float(per_call_ms[sel].sum())
         gbs = float(nbytes[sel].sum()) / (t * 1e-3) / 1e9

@@ -243,7 +243,7 @@ def rel_frobenius_error(original: torch.Tensor, reconstructed: torch.Tensor,
     key = (torch.cuda.current_device(), torch.cuda.current_stream().cuda_stream)
     ws = _frob_ws.get(key)
     if ws is None:
-        ws = torch.empty(FROBENIUS_WORKSPACE_BYTES, dtype=torch.uint8, device=original.device)
+        ws = torch.zeros(FROBENIUS_WORKSPACE_BYTES, dtype=torch.uint8, device=original.device)
         _frob_ws[key] = ws
     _check(lib.tb_rel_frobenius_error(_ptr(original), _ptr(reconstructed), rows, cols, _dtype_code(original.dtype),
                                       _ptr(out), _ptr(ws), ws.numel(), _stream()))

@@ -2,13 +2,15 @@
 //     ||original - reconstructed||_F / ||original||_F
 // ("Quality", section "Reconstruction error").
 //
-// Two passes, no atomics, so the result is the same on every run:
-//   pass 1: each workgroup walks a grid-stride set of 8-element chunks and
-//           sums (a - b)^2 and a^2 in fp64 (differences taken in fp64), then
-//           reduces its threads in a fixed tree order into one partial pair;
-//   pass 2: one workgroup sums the partial pairs in a fixed order and writes
-//           the ratio.  0 when the difference is zero, +inf when only the
-//           original is zero.
+// One launch, no floating-point atomics, so the result is the same on every
+// run: each workgroup walks a grid-stride set of 8-element chunks and sums
+// (a - b)^2 and a^2 in fp64 (differences taken in fp64), reduces its threads
+// in a fixed tree order into one partial pair and publishes it; the last
+// workgroup to count itself in sums the partial pairs in workgroup order and
+// writes the ratio (0 when the difference is zero, +inf when only the
+// original is zero), then clears the counter for the next call.
+// Partials and the counter move through device-scope (sc1) accesses, coherent
+// across XCDs; a workgroup drains its partial before it counts itself in.
 // HBM-bound: every element of both matrices is read once.
 #include "tb_device.h"
 #include "tb_host.h"
@@ -18,7 +20,16 @@ namespace tb {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxPartials = TB_FROBENIUS_WORKSPACE_BYTES / 16;
+// The workspace holds the partial pairs; its last 16 bytes hold the arrival
+// counter.
+constexpr int kMaxPartials = TB_FROBENIUS_WORKSPACE_BYTES / 16 - 1;
+
+__device__ __forceinline__ uint64_t load_coherent64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 template <typename E>
 __device__ __forceinline__ void load8_f64(const E* p, double* out) {
@@ -52,9 +63,11 @@ __device__ __forceinline__ void block_reduce2(double& a, double& b, double* sa, 
 }
 
 template <typename E>
-__global__ __launch_bounds__(kThreads) void frob_pass1(const E* __restrict__ a, const E* __restrict__ b, int64_t n8,
-                                                       double2* __restrict__ partial) {
+__global__ __launch_bounds__(kThreads) void frob_kernel(const E* __restrict__ a, const E* __restrict__ b, int64_t n8,
+                                                        uint64_t* __restrict__ partial, unsigned* __restrict__ counter,
+                                                        double* __restrict__ result) {
   __shared__ double sa[kThreads], sb[kThreads];
+  __shared__ unsigned s_last;
   double num = 0.0, den = 0.0;
   const int64_t stride = int64_t(gridDim.x) * kThreads;
   for (int64_t c = int64_t(blockIdx.x) * kThreads + threadIdx.x; c < n8; c += stride) {
@@ -69,15 +82,19 @@ __global__ __launch_bounds__(kThreads) void frob_pass1(const E* __restrict__ a, 
     }
   }
   block_reduce2(num, den, sa, sb);
-  if (threadIdx.x == 0) partial[blockIdx.x] = make_double2(num, den);
-}
-
-__global__ __launch_bounds__(kThreads) void frob_pass2(const double2* __restrict__ partial, int np, double* result) {
-  __shared__ double sa[kThreads], sb[kThreads];
-  double num = 0.0, den = 0.0;
-  for (int i = threadIdx.x; i < np; i += kThreads) {
-    num += partial[i].x;
-    den += partial[i].y;
+  if (threadIdx.x == 0) {
+    store_coherent64(&partial[2 * blockIdx.x], __double_as_longlong(num));
+    store_coherent64(&partial[2 * blockIdx.x + 1], __double_as_longlong(den));
+    __builtin_amdgcn_s_waitcnt(0);  // the partial is visible before the count
+    s_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  num = 0.0;
+  den = 0.0;
+  for (int i = threadIdx.x; i < int(gridDim.x); i += kThreads) {
+    num += __longlong_as_double(load_coherent64(&partial[2 * i]));
+    den += __longlong_as_double(load_coherent64(&partial[2 * i + 1]));
   }
   block_reduce2(num, den, sa, sb);
   if (threadIdx.x == 0) {
@@ -86,6 +103,7 @@ __global__ __launch_bounds__(kThreads) void frob_pass2(const double2* __restrict
     else if (den == 0.0) r = __builtin_inf();
     else r = sqrt(num) / sqrt(den);
     *result = r;
+    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -98,16 +116,14 @@ hipError_t launch_frobenius(tb_dtype dtype, const void* a, const void* b, int64_
   const int64_t cap = int64_t(cus) * 8 < kMaxPartials ? int64_t(cus) * 8 : kMaxPartials;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
-  double2* partial = static_cast<double2*>(workspace);
+  uint64_t* partial = static_cast<uint64_t*>(workspace);
+  unsigned* counter = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + TB_FROBENIUS_WORKSPACE_BYTES - 16);
   if (dtype == TB_BF16)
-    hipLaunchKernelGGL(frob_pass1<bf16_t>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
-                       static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b), n8, partial);
+    hipLaunchKernelGGL(frob_kernel<bf16_t>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
+                       static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b), n8, partial, counter, result);
   else
-    hipLaunchKernelGGL(frob_pass1<float>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
-                       static_cast<const float*>(a), static_cast<const float*>(b), n8, partial);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(frob_pass2, dim3(1), dim3(kThreads), 0, stream, partial, int(blocks), result);
+    hipLaunchKernelGGL(frob_kernel<float>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
+                       static_cast<const float*>(a), static_cast<const float*>(b), n8, partial, counter, result);
   return hipGetLastError();
 }
 

@@ -1,8 +1,8 @@
 // reconstruct_weight: w_out = diag(s) . W0 + U . V^T  ("The theta bundle",
 // component table and reconstruction formula).
 //
-// rank 0 is a pure scaled copy, bound by HBM: each thread rebuilds 8
-// consecutive elements of one row (16-byte loads, 16/32-byte stores).
+// rank 0 is a pure scaled copy, bound by HBM (wave-contiguous spans, fp32
+// output streamed out non-temporal).
 // rank > 0 is a K = rank GEMM (U rows and V rows are both contiguous along
 // the rank dimension) on the matrix cores with the scaled copy fused into the
 // epilogue; at rank 256 it is still HBM-bound (6 bytes of W0 and fp32 output
@@ -22,34 +22,38 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Each wave handles 512 consecutive elements per step as two halves of 256:
+// lane l takes elements 4 l .. 4 l + 3 of each half, so every load and store
+// instruction covers one contiguous span (512 or 1024 bytes) and the fp32
+// stores fill whole cache lines; they are streamed out non-temporal.
 template <typename EI, typename EO>
 __global__ __launch_bounds__(kThreads) void reconstruct_rank0_kernel(const EI* __restrict__ s, const EI* __restrict__ w0,
-                                                                     EO* __restrict__ out, int64_t n8, int I) {
-  const int64_t stride = int64_t(gridDim.x) * kThreads;
-  for (int64_t c = int64_t(blockIdx.x) * kThreads + threadIdx.x; c < n8; c += stride) {
-    const int64_t base = c * 8;
-    const int64_t o = base / I;
-    const float sc = to_f32<EI>(s[o]);
-    float v[8];
-    if constexpr (sizeof(EI) == 2) {
-      const uint4 q = *reinterpret_cast<const uint4*>(w0 + base);
-      const uint32_t u4[4] = {q.x, q.y, q.z, q.w};
+                                                                     EO* __restrict__ out, int64_t n, int I) {
+  const int l = int(threadIdx.x) & 63;
+  const int64_t waves = int64_t(gridDim.x) * (kThreads / kWave);
+  for (int64_t wv = int64_t(blockIdx.x) * (kThreads / kWave) + (threadIdx.x >> 6); wv * 512 < n; wv += waves) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = sc * bf16_to_f32(uint16_t(u4[e / 2] >> (16 * (e % 2))));
-    } else {
-      const float4 lo = reinterpret_cast<const float4*>(w0 + base)[0];
-      const float4 hi = reinterpret_cast<const float4*>(w0 + base)[1];
-      v[0] = sc * lo.x; v[1] = sc * lo.y; v[2] = sc * lo.z; v[3] = sc * lo.w;
-      v[4] = sc * hi.x; v[5] = sc * hi.y; v[6] = sc * hi.z; v[7] = sc * hi.w;
-    }
-    if constexpr (sizeof(EO) == 4) {
-      float4* dst = reinterpret_cast<float4*>(out + base);
-      dst[0] = make_float4(v[0], v[1], v[2], v[3]);
-      dst[1] = make_float4(v[4], v[5], v[6], v[7]);
-    } else {
-      *reinterpret_cast<uint4*>(out + base) =
-          make_uint4(f32_to_bf16(v[0]) | (uint32_t(f32_to_bf16(v[1])) << 16), f32_to_bf16(v[2]) | (uint32_t(f32_to_bf16(v[3])) << 16),
-                     f32_to_bf16(v[4]) | (uint32_t(f32_to_bf16(v[5])) << 16), f32_to_bf16(v[6]) | (uint32_t(f32_to_bf16(v[7])) << 16));
+    for (int half = 0; half < 2; ++half) {
+      const int64_t base = wv * 512 + half * 256 + l * 4;   // I % 8 == 0: the four share a row
+      if (base >= n) continue;
+      const float sc = to_f32<EI>(s[base / I]);
+      float v[4];
+      if constexpr (sizeof(EI) == 2) {
+        const uint2 q = *reinterpret_cast<const uint2*>(w0 + base);
+        v[0] = sc * bf16_to_f32(uint16_t(q.x));
+        v[1] = sc * bf16_to_f32(uint16_t(q.x >> 16));
+        v[2] = sc * bf16_to_f32(uint16_t(q.y));
+        v[3] = sc * bf16_to_f32(uint16_t(q.y >> 16));
+      } else {
+        const float4 q = *reinterpret_cast<const float4*>(w0 + base);
+        v[0] = sc * q.x; v[1] = sc * q.y; v[2] = sc * q.z; v[3] = sc * q.w;
+      }
+      if constexpr (sizeof(EO) == 4) {
+        __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(out + base));
+      } else {
+        *reinterpret_cast<uint2*>(out + base) = make_uint2(f32_to_bf16(v[0]) | (uint32_t(f32_to_bf16(v[1])) << 16),
+                                                           f32_to_bf16(v[2]) | (uint32_t(f32_to_bf16(v[3])) << 16));
+      }
     }
   }
 }
@@ -230,9 +234,9 @@ __global__ __launch_bounds__(kThreads, 2) void reconstruct_mfma_kernel(const bf1
 // A tile's whole U and V (four k-tiles of 64) fit the 128 KB LDS ring, one
 // slot per k-tile, filled by direct-to-LDS buffer loads; each slot is
 // refilled for the next tile as soon as every wave has read it, so the loads
-// of tile j+1 fly while tile j multiplies.  The W0 and s values of tile j+1
-// are loaded into registers at the end of tile j's epilogue and so have a
-// whole tile's time to arrive.  The epilogue moves each wave's 64 x 64
+// of tile j+1 fly while tile j multiplies.  The W0 and s values of tile j+2
+// are loaded into registers at the end of tile j's epilogue (two register
+// sets, alternating) and so have two tiles' time to arrive.  The epilogue moves each wave's 64 x 64
 // accumulators through LDS (the slot of the last k-tile) so that 16 lanes
 // cover 64 consecutive outputs of one row: 128-byte W0 reads and 256-byte
 // non-temporal fp32 writes per row.
@@ -419,6 +423,71 @@ __device__ __forceinline__ void store_out(const Tile& g, int off, f32x4 c, u32x2
   }
 }
 
+// One output tile.  On entry k-tiles 0..2 of g are in flight into ring slots
+// 0..2 and q holds (or is loading) g's W0 and s.  Step k waits for k-tile k,
+// publishes it, refills the slot every wave has just finished with (k-tile 3
+// of g, then k-tiles 0..2 of gn), and multiplies.  The epilogue goes through
+// slot 3 and finally starts loading the W0 and s of gnn, two tiles ahead, into
+// q.  Every wait counts the loads and stores issued after the k-tile it needs:
+// two refills, one tile's stores (16) and two tiles' W0 and s loads (32 each)
+// lie between a k-tile 0..2 and its step, which the count caps at 63.
+template <typename EO>
+__device__ __forceinline__ void tile_pass(const Dma& d, lds_byte* const (&rdU)[2][4], lds_byte* const (&rdV)[2][4],
+                                          lds_byte* stage, const Tile& g, const Tile& gn, bool gn_dummy,
+                                          const Tile& gnn, bool gnn_dummy, Pre& q, int I, int R, int wo, int wi,
+                                          int l) {
+  const int lr = l & 31, h = l >> 5;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+  wait_vm<63>();
+  __syncthreads();
+  issue<3>(d, g, 3, false, R);
+  multiply_step<0>(rdU, rdV, acc);
+  wait_vm<63>();
+  __syncthreads();
+  issue<0>(d, gn, 0, gn_dummy, R);
+  multiply_step<1>(rdU, rdV, acc);
+  wait_vm<63>();
+  __syncthreads();
+  issue<1>(d, gn, 1, gn_dummy, R);
+  multiply_step<2>(rdU, rdV, acc);
+  wait_vm<16>();
+  __syncthreads();
+  issue<2>(d, gn, 2, gn_dummy, R);
+  multiply_step<3>(rdU, rdV, acc);
+
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int chunk = (8 * rb + 2 * b + h) ^ (lr & 15);
+        const f32x16& c = acc[rb][cb];
+        *reinterpret_cast<lds_f32x4*>(stage + lr * kStageRow + (chunk << 4)) =
+            f32x4{c[4 * b], c[4 * b + 1], c[4 * b + 2], c[4 * b + 3]};
+      }
+    __syncthreads();
+    f32x4 c[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int orel = 4 * p + (l >> 4), chunk = (l & 15) ^ (orel & 15);
+      c[p] = *reinterpret_cast<const lds_f32x4*>(stage + orel * kStageRow + (chunk << 4));
+    }
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+      store_out<EO>(g, out_off<EO>(g, I, wo, wi, cb, p, l), c[p], q.w[cb][p], bf16_to_f32(uint16_t(q.s[cb][p])));
+  }
+  prefetch(q, gnn, gnn_dummy, I, wo, wi, l);
+}
+
 template <typename EO>
 __global__ __launch_bounds__(kThreads, 1) void reconstruct_persistent_kernel(const bf16_t* __restrict__ s,
                                                                              const bf16_t* __restrict__ w0,
@@ -459,72 +528,28 @@ __global__ __launch_bounds__(kThreads, 1) void reconstruct_persistent_kernel(con
   }
   lds_byte* stage = base + 3 * kSlotBytes + w * 8192;
 
-  f32x16 acc[2][2];
-  Pre q;
-  Tile g = tile_at<EO>(t, tiles_i, s, w0, u, v, out, O, I, R);
+  // Tiles past the workgroup's last are dummies: their loads return zeros
+  // into free slots and registers, and nothing of them is stored.
+  auto tile = [&](int tt) { return tile_at<EO>(tt < tiles ? tt : t, tiles_i, s, w0, u, v, out, O, I, R); };
+  Pre qa, qb;   // W0 and s of the current tile and of the next, alternating
+  Tile g = tile(t);
   issue<0>(d, g, 0, false, R);
   issue<1>(d, g, 1, false, R);
   issue<2>(d, g, 2, false, R);
-  prefetch(q, g, false, I, wo, wi, l);
-
-  for (int j = 0;; ++j) {
-    const int tn = t + G;
-    const bool has_next = tn < tiles;
-    const Tile gn = tile_at<EO>(has_next ? tn : t, tiles_i, s, w0, u, v, out, O, I, R);
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
-
-    // Step k: wait for k-tile k, publish it, refill the slot every wave has
-    // just finished with, multiply.
-    if (j == 0) wait_vm<48>(); else wait_vm<63>();
-    __syncthreads();
-    issue<3>(d, g, 3, false, R);
-    multiply_step<0>(rdU, rdV, acc);
-    if (j == 0) wait_vm<48>(); else wait_vm<63>();
-    __syncthreads();
-    issue<0>(d, gn, 0, !has_next, R);
-    multiply_step<1>(rdU, rdV, acc);
-    if (j == 0) wait_vm<48>(); else wait_vm<63>();
-    __syncthreads();
-    issue<1>(d, gn, 1, !has_next, R);
-    multiply_step<2>(rdU, rdV, acc);
-    wait_vm<16>();
-    __syncthreads();
-    issue<2>(d, gn, 2, !has_next, R);
-    multiply_step<3>(rdU, rdV, acc);
-
-    // Epilogue through the staging area (slot 3, free once every wave has
-    // read its fragments).
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      __syncthreads();
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int chunk = (8 * rb + 2 * b + h) ^ (lr & 15);
-          const f32x16& c = acc[rb][cb];
-          *reinterpret_cast<lds_f32x4*>(stage + lr * kStageRow + (chunk << 4)) =
-              f32x4{c[4 * b], c[4 * b + 1], c[4 * b + 2], c[4 * b + 3]};
-        }
-      __syncthreads();
-      f32x4 c[8];
-#pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        const int orel = 4 * p + (l >> 4), chunk = (l & 15) ^ (orel & 15);
-        c[p] = *reinterpret_cast<const lds_f32x4*>(stage + orel * kStageRow + (chunk << 4));
-      }
-#pragma unroll
-      for (int p = 0; p < 8; ++p)
-        store_out<EO>(g, out_off<EO>(g, I, wo, wi, cb, p, l), c[p], q.w[cb][p], bf16_to_f32(uint16_t(q.s[cb][p])));
-    }
-    prefetch(q, gn, !has_next, I, wo, wi, l);
-    if (!has_next) break;
-    t = tn;
+  prefetch(qa, g, false, I, wo, wi, l);
+  prefetch(qb, tile(t + G), t + G >= tiles, I, wo, wi, l);
+  for (;;) {
+    Tile gn = tile(t + G);
+    tile_pass<EO>(d, rdU, rdV, stage, g, gn, t + G >= tiles, tile(t + 2 * G), t + 2 * G >= tiles, qa, I, R, wo, wi,
+                  l);
+    t += G;
+    if (t >= tiles) break;
+    g = gn;
+    gn = tile(t + G);
+    tile_pass<EO>(d, rdU, rdV, stage, g, gn, t + G >= tiles, tile(t + 2 * G), t + 2 * G >= tiles, qb, I, R, wo, wi,
+                  l);
+    t += G;
+    if (t >= tiles) break;
     g = gn;
   }
   wait_vm<0>();  // no load into LDS may still be in flight when the workgroup ends
@@ -536,11 +561,11 @@ template <typename EI, typename EO>
 hipError_t launch_typed(const void* s, const void* w0, const void* u, const void* v, void* w_out, int64_t O, int64_t I,
                         int64_t R, hipStream_t stream) {
   if (R == 0) {
-    const int64_t n8 = O * I / 8;
-    int64_t blocks = (n8 + kThreads - 1) / kThreads;
+    const int64_t n = O * I;
+    int64_t blocks = (n + 512 * (kThreads / kWave) - 1) / (512 * (kThreads / kWave));
     if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL((reconstruct_rank0_kernel<EI, EO>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
-                       static_cast<const EI*>(s), static_cast<const EI*>(w0), static_cast<EO*>(w_out), n8, int(I));
+                       static_cast<const EI*>(s), static_cast<const EI*>(w0), static_cast<EO*>(w_out), n, int(I));
   } else if (sizeof(EI) == 2 && R % 8 == 0 && R > 3 * rp::BK && R <= 4 * rp::BK && I < (1 << 22) &&
              O < (1 << 24)) {
     int cus = 0;

@@ -287,7 +287,13 @@ def test_frobenius_closed_forms():
     big = torch.randn(1000, 4104, generator=g).to(DEV)
     other = big + 1e-3 * torch.randn(1000, 4104, generator=g).to(DEV)
     want = oracle.relative_frobenius_error(exact(big), exact(other))
-    assert float(tb.rel_frobenius_error(big, other).item()) == pytest.approx(want, rel=1e-12)
+    got = [float(tb.rel_frobenius_error(big, other).item()) for _ in range(3)]
+    assert got[0] == pytest.approx(want, rel=1e-12)
+    assert got[1] == got[0] and got[2] == got[0]          # fixed summation order
+    # The arrival counter in the workspace's last 16 bytes is back at zero.
+    ws = tb._frob_ws[(torch.cuda.current_device(), torch.cuda.current_stream().cuda_stream)]
+    torch.cuda.synchronize()
+    assert int(ws[-16:].count_nonzero().item()) == 0
 
 
 # ---------------------------------------------------------------------------
