@@ -111,7 +111,14 @@ __device__ __forceinline__ Frag8<E> load_row8(const E* row, int k, int R, bool a
 // ---------------------------------------------------------------------------
 // Producers.
 // ---------------------------------------------------------------------------
-constexpr int kVtPitch = 40;  // elements per column of a wave's transposed 64 x 32 V tile
+constexpr int kVtPitch = 40;  // elements per column of a wave's transposed 64 x 32 V tile (fp32 V)
+constexpr int kVsPitch = 160; // bytes per row of a wave's staged 32 x 64 V tile (bf16 V): 5 KB, as the above
+static_assert(32 * kVsPitch <= 64 * kVtPitch * 2, "staged tile fits the wave's LDS share");
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4v lds_u32x4;
 constexpr int kMaxKT = 16;    // k-slices of the producers at most
 constexpr int kCbCols = 64;   // columns of T per producer: 128 contiguous bytes of a bf16 row of V
 
@@ -175,19 +182,47 @@ __device__ void produce_t(const DecodeArgs& a, int p, uint8_t* smem) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         if (i0 + d < n) {
-          // Transpose the block through the wave's LDS tile: column j holds
-          // k = 0..31 contiguously.
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            Raw vals[8];
-            __builtin_memcpy(vals, &vf[d][q], sizeof(vals));
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vt[((l & 7) * 8 + e) * kVtPitch + 8 * q + vr] = vals[e];
-          }
-          __builtin_amdgcn_wave_barrier();
           Frag8<E> fb[4];
+          if constexpr (sizeof(E) == 2) {
+            // Stage the block as it sits in memory (32 rows of k, 160-byte
+            // pitch) and read each lane's eight consecutive k of one column
+            // with the transposing LDS read: within 16 lanes, lane i receives
+            // element i % 4 of the 8-byte chunks addressed by lanes 4e + i / 4,
+            // so lanes pointing at rows kb + (lane % 16) / 4, columns
+            // nb + 4 (lane % 4) receive k = kb .. kb+3 of column nb + lane % 16.
+            // The pitch puts the four rows of one read on distinct banks.
+            lds_u8* st = (lds_u8*)vt;  // vt lies in LDS
 #pragma unroll
-          for (int j = 0; j < 4; ++j) fb[j] = load_frag<E>(reinterpret_cast<const E*>(&vt[(16 * j + lr) * kVtPitch + kq]));
+            for (int q = 0; q < 4; ++q)
+              *reinterpret_cast<lds_u32x4*>(st + (8 * q + vr) * kVsPitch + (l & 7) * 16) =
+                  u32x4v{vf[d][q].v.x, vf[d][q].v.y, vf[d][q].v.z, vf[d][q].v.w};
+            __builtin_amdgcn_wave_barrier();
+            const int rr = 8 * (l >> 4) + ((l & 15) >> 2), cc = 4 * (l & 3);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              lds_u8* pr = st + rr * kVsPitch + (16 * j + cc) * 2;
+              const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4*>(pr));
+              const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4*>(pr + 4 * kVsPitch));
+              fb[j].v = make_uint4(uint32_t(uint16_t(lo[0])) | (uint32_t(uint16_t(lo[1])) << 16),
+                                   uint32_t(uint16_t(lo[2])) | (uint32_t(uint16_t(lo[3])) << 16),
+                                   uint32_t(uint16_t(hi[0])) | (uint32_t(uint16_t(hi[1])) << 16),
+                                   uint32_t(uint16_t(hi[2])) | (uint32_t(uint16_t(hi[3])) << 16));
+            }
+          } else {
+            // Transpose the block through the wave's LDS tile: column j holds
+            // k = 0..31 contiguously.
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              Raw vals[8];
+              __builtin_memcpy(vals, &vf[d][q], sizeof(vals));
+#pragma unroll
+              for (int e = 0; e < 8; ++e) vt[((l & 7) * 8 + e) * kVtPitch + 8 * q + vr] = vals[e];
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              fb[j] = load_frag<E>(reinterpret_cast<const E*>(&vt[(16 * j + lr) * kVtPitch + kq]));
+          }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int j = 0; j < 4; ++j)
@@ -647,7 +682,10 @@ DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
   // (three k32 steps per wave: one round of loads at 16 tokens).
   if (rank > 0) {
     p.NCB = int((rank + kCbCols - 1) / kCbCols);
-    int64_t kt = (in_dim + 767) / 768;
+    // Short reductions (in_dim <= 1536) stay in one producer per column block:
+    // its longer load phase costs less than the extra round trips of
+    // combining k-slice partials across workgroups.
+    int64_t kt = in_dim <= 1536 ? 1 : (in_dim + 767) / 768;
     if (kt > kMaxKT) kt = kMaxKT;
     if (p.NCB > kMaxGroupCounters / 2) kt = 1;  // one arrival counter per column block
     p.KT = int(kt);
