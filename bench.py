@@ -22,7 +22,7 @@ token counts report TFLOP/s of algorithmic flops (matrix-core-bound).
 
 Beside the K-step figure the line carries the per-step spread, the same stack
 replayed from a captured graph, and the GPU clock and power sampled while the
-graph ran.  Stacks whose distinct inputs are smaller than twice the 256 MB
+graph replays for about a second more.  Stacks whose distinct inputs are smaller than twice the 256 MB
 Infinity Cache are timed over a rotating pool of replicas of at least 1 GiB,
 so that every step reads cold data (the figure reported); the stack-order
 figure from one replica is reported beside it.
@@ -175,8 +175,8 @@ def spread(per_step_ms):
 
 
 class ClockSampler:
-    """GPU shader clock (MHz) and socket power sampled every 50 ms from a side thread (amdsmi through torch).
-    Used only around the graph leg, where the launching thread is idle."""
+    """GPU shader clock (MHz) and socket power sampled every 50 ms from a side thread (amdsmi through torch),
+    around untimed graph replays."""
 
     def __init__(self, torch):
         self.torch, self.clk, self.pwr, self.err = torch, [], [], None
@@ -236,8 +236,16 @@ def graph_leg(torch, make_step, steps, outputs):
                 raise RuntimeError("a replay of the captured step differs from the eager step")
     for _ in range(2):
         g.replay()
+    ms, per = timed_steps(torch, lambda k: g.replay(), steps)
+    # Clock and power while the same replays run for about a second (outside the timed region).
     with ClockSampler(torch) as clk:
-        ms, per = timed_steps(torch, lambda k: g.replay(), steps)
+        t_end, n = time.time() + 1.0, 0
+        while time.time() < t_end or n < steps:
+            g.replay()
+            n += 1
+            if n % 4 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
     return ms, per, clk.summary()
 
 
