@@ -261,6 +261,28 @@ def _blas_threads():
         return len(os.sched_getaffinity(0))
 
 
+def _host_info():
+    """CPU model and BLAS library of the host that times the oracle."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        import threadpoolctl
+        libs = [f"{p.get('internal_api')} {p.get('version')}" for p in threadpoolctl.threadpool_info()
+                if p.get("user_api") == "blas"]
+        blas = ", ".join(libs) or None
+    except Exception:
+        pass
+    return {"cpu_model": model, "blas": blas, "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
 # ---- forward stacks -----------------------------------------------------------------
 
 
@@ -511,9 +533,12 @@ def cpu_baseline_forward(args, wl, shapes, calls, bundles, W0, xs, band_of, deco
         val, unit = done_bytes / secs / 1e9, "GB/s"
     else:
         val, unit = done_flops / secs / 1e12, "TFLOP/s"
+    step_units = sum(call_bytes(Mc, *shapes[f], R) if decode else call_flops(Mc, *shapes[f], R)
+                     for c in calls for f in c[1])
     return {"value": round(val, 4), "unit": unit, "cores": int(_blas_threads()), "kind": "oracle",
             "sample": f"{len(used)} projections of the same stack ({used[0]} .. {used[-1]}), {Mc} tokens, "
-                      f"float64 NumPy incl. bf16 decoding, {secs:.1f} s"}
+                      f"float64 NumPy incl. bf16 decoding, {secs:.1f} s",
+            "extrapolated_step_s": round(step_units / (val * (1e9 if decode else 1e12)), 2), **_host_info()}
 
 
 # ---- reconstruction and error stack -------------------------------------------------------
@@ -692,10 +717,13 @@ def cpu_baseline_reconstruct(args, shapes, bundles, W0, originals, band_of, L, R
         secs += time.perf_counter() - t
         done_bytes += reconstruct_bytes(O, I, R) + frobenius_bytes(O, I)
         used.append(f"{l}:{fam}")
-    return {"value": round(done_bytes / secs / 1e9, 4), "unit": "GB/s", "cores": int(_blas_threads()),
+    rate = done_bytes / secs
+    step = L * sum(reconstruct_bytes(o, i, R) + frobenius_bytes(o, i) for o, i in shapes.values())
+    return {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": int(_blas_threads()),
             "kind": "oracle",
             "sample": f"{len(used)} (layer, projection) pairs of the same stack ({used[0]} .. {used[-1]}): "
-                      f"float64 NumPy reconstruct incl. bf16 decoding, then the error, {secs:.1f} s"}
+                      f"float64 NumPy reconstruct incl. bf16 decoding, then the error, {secs:.1f} s",
+            "extrapolated_step_s": round(step / rate, 1), **_host_info()}
 
 
 def main():

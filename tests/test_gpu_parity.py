@@ -139,7 +139,19 @@ def _large_case(G, layer, family, M):
     return oracle.relative_frobenius_error(want, got)
 
 
-@pytest.mark.parametrize("G,layer", [(6, 0), (6, 59), (60, 29)])
+def _parity_layers(G, L=60):
+    """Layer 0, the first layer of every band and layer L-1 (with G = L: 0, L/2 - 1 and L-1)."""
+    if G == L:
+        return [0, L // 2 - 1, L - 1]
+    bands = oracle.band_map(L, G)
+    firsts = [l for l in range(L) if l == 0 or bands[l] != bands[l - 1]]
+    return sorted(set(firsts) | {L - 1})
+
+
+LARGE_SAMPLE = [(6, l) for l in _parity_layers(6)] + [(60, l) for l in _parity_layers(60)]
+
+
+@pytest.mark.parametrize("G,layer", LARGE_SAMPLE)
 @pytest.mark.parametrize("M", [1, 16, 4096])
 @pytest.mark.parametrize("family", gen.FAMILIES)
 def test_large_stack_bf16(G, layer, M, family):
@@ -157,7 +169,7 @@ def test_large_stack_bf16(G, layer, M, family):
 @pytest.mark.parametrize("rank", [256, 0])
 @pytest.mark.parametrize("family", gen.FAMILIES)
 def test_reconstruct_large(rank, family):
-    for layer in (0, 59):
+    for layer in _parity_layers(6):
         band = tb.band_index(60, 6, layer)
         _say(f"reconstruct rank={rank} {family} layer={layer} band={band}")
         W0 = gen.device_w0(torch, 5, family, gen.SHAPES_60, band)
