@@ -186,8 +186,8 @@ tb_status tb_reconstruct_weight(const void *s, const void *w0, const void *u, co
  *   squares and sums are taken in fp64 in a fixed order (deterministic).
  *   When the difference is zero the result is 0; when only the original is
  *   zero it is +inf.  workspace: >= TB_FROBENIUS_WORKSPACE_BYTES device bytes,
- *   16-byte aligned.  Bytes [TB_FROBENIUS_WORKSPACE_BYTES - 16,
- *   TB_FROBENIUS_WORKSPACE_BYTES) hold an arrival counter: zero them before
+ *   16-byte aligned.  Bytes [TB_FROBENIUS_WORKSPACE_BYTES - 8192,
+ *   TB_FROBENIUS_WORKSPACE_BYTES) hold arrival counters: zero them before
  *   the first use; every call leaves them zero (the rest needs no
  *   initialisation).  Calls that share a workspace must not overlap (keep
  *   them on one stream).  Errors as above.

@@ -50,10 +50,15 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
 
 // Control words: [kErr] sticky timeout flag, [kDone] column blocks of T
-// published, [kFinish] rank streamers past their read of T; from word
-// kCbCounters on, one arrival counter per column block of T (k-sliced
-// producers), from kRbCounters on one per row block (k-sliced streamers).
-enum Ctrl { kErr = 2, kDone = 5, kFinish = 6 };
+// published; from word kCbCounters on, one arrival counter per column block
+// of T (k-sliced producers), from kRbCounters on one per row block (k-sliced
+// streamers); from kFinishBase on, the rank streamers past their read of T,
+// counted into kFinishGroups group counters (64 words apart) and a top
+// counter bumped by the last of each group, so that a few hundred increments
+// do not queue on one word.
+enum Ctrl { kErr = 2, kDone = 5 };
+constexpr int kFinishBase = int(kCtrlBlockBytes / 4) - kFinishWords;
+constexpr int kFinishGroups = 16;
 constexpr int kCbCounters = 64;
 constexpr int kRbCounters = kCbCounters + kMaxGroupCounters / 2;
 
@@ -517,6 +522,16 @@ __device__ void stream_rows(const DecodeArgs& a, int b, uint8_t* smem) {
     }
   }
 
+  // Every wave is past its read of T: count this rank streamer in now (the
+  // answer is needed only at the end, so the atomic's round trip overlaps the
+  // reduction and the stores).
+  const unsigned fin_groups = unsigned(min(a.NRB, kFinishGroups)), fin_g = unsigned(rb) % fin_groups;
+  unsigned fin_old = 0;
+  if (rank_unit) {
+    __syncthreads();
+    if (tid == 0) fin_old = add_coherent(&a.ctrl[kFinishBase + 64 * int(fin_g)], 1u);
+  }
+
   // Sum the eight waves' partials in a fixed order, four (tile, token tile)
   // pairs per round, into the block's result.
 #pragma unroll
@@ -579,10 +594,19 @@ __device__ void stream_rows(const DecodeArgs& a, int b, uint8_t* smem) {
     }
   }
 
-  // The last rank streamer past its read of T resets the producers' count.
-  if (rank_unit && tid == 0 && add_coherent(&a.ctrl[kFinish], 1u) == unsigned(a.NRB - 1)) {
-    store_coherent(&a.ctrl[kDone], 0u);
-    store_coherent(&a.ctrl[kFinish], 0u);
+  // The last of a group clears its counter and bumps the top counter; the
+  // last there, the last rank streamer past its read of T, resets the
+  // producers' count.
+  if (rank_unit && tid == 0) {
+    const unsigned members = (unsigned(a.NRB) - fin_g + fin_groups - 1) / fin_groups;
+    if (fin_old == members - 1) {
+      store_coherent(&a.ctrl[kFinishBase + 64 * int(fin_g)], 0u);
+      unsigned* top = &a.ctrl[kFinishBase + 64 * kFinishGroups];
+      if (add_coherent(top, 1u) == fin_groups - 1) {
+        store_coherent(top, 0u);
+        store_coherent(&a.ctrl[kDone], 0u);
+      }
+    }
   }
 }
 

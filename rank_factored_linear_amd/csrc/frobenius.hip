@@ -8,7 +8,10 @@
 // in a fixed tree order into one partial pair and publishes it; the last
 // workgroup to count itself in sums the partial pairs in workgroup order and
 // writes the ratio (0 when the difference is zero, +inf when only the
-// original is zero), then clears the counter for the next call.
+// original is zero).  Counting in goes through 16 group counters (workgroup
+// b into counter b % 16, 256 bytes apart) and one top counter that the last
+// of each group bumps: thousands of increments of one word serialise at the
+// memory side for ~20 us.  Every counter is cleared by its last user.
 // Partials and the counter move through device-scope (sc1) accesses, coherent
 // across XCDs; a workgroup drains its partial before it counts itself in.
 // HBM-bound: every element of both matrices is read once.
@@ -20,9 +23,12 @@ namespace tb {
 namespace {
 
 constexpr int kThreads = 256;
-// The workspace holds the partial pairs; its last 16 bytes hold the arrival
-// counter.
-constexpr int kMaxPartials = TB_FROBENIUS_WORKSPACE_BYTES / 16 - 1;
+// The workspace holds the partial pairs; its last 8 KB hold the counters
+// (group g at byte 256 g, the top counter at byte 256 * kGroups).
+constexpr int kGroups = 16;
+constexpr int kCounterBytes = 8192;
+constexpr int kMaxPartials = (TB_FROBENIUS_WORKSPACE_BYTES - kCounterBytes) / 16;
+static_assert(256 * (kGroups + 1) <= kCounterBytes, "counters fit their area");
 
 __device__ __forceinline__ uint64_t load_coherent64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -64,7 +70,7 @@ __device__ __forceinline__ void block_reduce2(double& a, double& b, double* sa, 
 
 template <typename E>
 __global__ __launch_bounds__(kThreads) void frob_kernel(const E* __restrict__ a, const E* __restrict__ b, int64_t n8,
-                                                        uint64_t* __restrict__ partial, unsigned* __restrict__ counter,
+                                                        uint64_t* __restrict__ partial, unsigned* __restrict__ counters,
                                                         double* __restrict__ result) {
   __shared__ double sa[kThreads], sb[kThreads];
   __shared__ unsigned s_last;
@@ -86,7 +92,19 @@ __global__ __launch_bounds__(kThreads) void frob_kernel(const E* __restrict__ a,
     store_coherent64(&partial[2 * blockIdx.x], __double_as_longlong(num));
     store_coherent64(&partial[2 * blockIdx.x + 1], __double_as_longlong(den));
     __builtin_amdgcn_s_waitcnt(0);  // the partial is visible before the count
-    s_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+    const unsigned nb = gridDim.x, groups = nb < unsigned(kGroups) ? nb : unsigned(kGroups);
+    const unsigned g = blockIdx.x % groups, members = (nb - g + groups - 1) / groups;
+    unsigned* gc = counters + 64 * g;
+    unsigned* top = counters + 64 * kGroups;
+    bool last = false;
+    if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == members - 1) {
+      __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == groups - 1) {
+        __hip_atomic_store(top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = true;
+      }
+    }
+    s_last = last;
   }
   __syncthreads();
   if (!s_last) return;
@@ -103,7 +121,6 @@ __global__ __launch_bounds__(kThreads) void frob_kernel(const E* __restrict__ a,
     else if (den == 0.0) r = __builtin_inf();
     else r = sqrt(num) / sqrt(den);
     *result = r;
-    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -117,13 +134,14 @@ hipError_t launch_frobenius(tb_dtype dtype, const void* a, const void* b, int64_
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   uint64_t* partial = static_cast<uint64_t*>(workspace);
-  unsigned* counter = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + TB_FROBENIUS_WORKSPACE_BYTES - 16);
+  unsigned* counters =
+      reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + TB_FROBENIUS_WORKSPACE_BYTES - kCounterBytes);
   if (dtype == TB_BF16)
     hipLaunchKernelGGL(frob_kernel<bf16_t>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
-                       static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b), n8, partial, counter, result);
+                       static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b), n8, partial, counters, result);
   else
     hipLaunchKernelGGL(frob_kernel<float>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
-                       static_cast<const float*>(a), static_cast<const float*>(b), n8, partial, counter, result);
+                       static_cast<const float*>(a), static_cast<const float*>(b), n8, partial, counters, result);
   return hipGetLastError();
 }
 

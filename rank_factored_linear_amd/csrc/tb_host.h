@@ -16,7 +16,11 @@ namespace tb {
 constexpr int kMaxProjections = TB_MAX_GROUP;
 constexpr size_t kControlBytes = TB_WORKSPACE_CONTROL_BYTES;
 constexpr size_t kCtrlBlockBytes = kControlBytes / kMaxProjections;
-constexpr int kMaxGroupCounters = int(kCtrlBlockBytes / 4) - 64;  // words 64.. of a control block
+// The last kFinishWords words of a control block hold the decode rank
+// streamers' finish counters (16 group counters and a top counter, 64 words
+// apart); words 64 .. 64 + kMaxGroupCounters hold the per-block counters.
+constexpr int kFinishWords = 17 * 64;
+constexpr int kMaxGroupCounters = int(kCtrlBlockBytes / 4) - 64 - kFinishWords;
 
 // Compute units of the current device (queried once per device).
 int device_cu_count(int* cus);

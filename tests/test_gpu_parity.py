@@ -302,10 +302,18 @@ def test_frobenius_closed_forms():
     got = [float(tb.rel_frobenius_error(big, other).item()) for _ in range(3)]
     assert got[0] == pytest.approx(want, rel=1e-12)
     assert got[1] == got[0] and got[2] == got[0]          # fixed summation order
-    # The arrival counter in the workspace's last 16 bytes is back at zero.
+    # The arrival counters in the workspace's last 8 KB are back at zero.
     ws = tb._frob_ws[(torch.cuda.current_device(), torch.cuda.current_stream().cuda_stream)]
     torch.cuda.synchronize()
-    assert int(ws[-16:].count_nonzero().item()) == 0
+    assert int(ws[-8192:].count_nonzero().item()) == 0
+    # Grids of one to a few workgroups (fewer than the 16 counter groups) and a ragged count.
+    for rows in (1, 3, 200, 1037):
+        A = torch.randn(rows, 8 * 37, generator=g).to(DEV)
+        B = A + 1e-2 * torch.randn(rows, 8 * 37, generator=g).to(DEV)
+        want = oracle.relative_frobenius_error(exact(A), exact(B))
+        assert float(tb.rel_frobenius_error(A, B).item()) == pytest.approx(want, rel=1e-12)
+    torch.cuda.synchronize()
+    assert int(ws[-8192:].count_nonzero().item()) == 0
 
 
 # ---------------------------------------------------------------------------
