@@ -16,7 +16,9 @@ Workloads (synthetic, seeded; value distributions of the measured stacks):
                  as diag(s) W0 + U V^T in fp32 (tb_reconstruct_weight) and
                  compared with the originals a W0_band + N(0, 2e-3) by the
                  relative Frobenius error (tb_rel_frobenius_error); --rank 0
-                 for the rank-0 bundle
+                 for the rank-0 bundle; --fused measures the same errors
+                 without writing the rebuilt weight (tb_reconstruction_error),
+                 --bands/--rank give one point of a (G, rank) sweep
 Token counts <= 64 report GB/s of algorithmic bytes (HBM-bound); larger
 token counts report TFLOP/s of algorithmic flops (matrix-core-bound).
 
@@ -73,6 +75,8 @@ def parse():
     ap.add_argument("--tokens", type=int, default=None)
     ap.add_argument("--bands", type=int, default=None)
     ap.add_argument("--rank", type=int, default=None, help="rank of the bundles (reconstruct60 only)")
+    ap.add_argument("--fused", action="store_true",
+                    help="reconstruct60: measure the error without writing the rebuilt weight (tb_reconstruction_error)")
     ap.add_argument("--replicas", type=int, default=None,
                     help="rotating pool of input replicas (default: enough for >= 1 GiB when the stack is small)")
     ap.add_argument("--no-graph", action="store_true", help="skip the captured-graph leg")
@@ -121,6 +125,11 @@ def reconstruct_bytes(O, I, R, e_in=2, e_out=4):
 def frobenius_bytes(O, I, e=4):
     """Error: both matrices read once."""
     return 2 * e * O * I
+
+
+def fused_error_bytes(O, I, R, e_in=2, e_orig=4):
+    """Error without the rebuilt weight: s, W0, U, V and the original read once."""
+    return e_in * (O * I + R * (O + I) + O) + e_orig * O * I
 
 
 # ---- counters committed under profiles/ ---------------------------------------------
@@ -569,7 +578,8 @@ def bench_reconstruct(args, torch, np, tb, gen):
                 bd["U"] = bd["V"] = None
             bundles[(l, fam)] = bd
             originals[(l, fam)] = gen.device_original(torch, W0[(band_of[l], fam)], seed, fam, l)
-    rebuilt = {fam: torch.empty(shapes[fam], dtype=torch.float32, device="cuda") for fam in gen.FAMILIES}
+    rebuilt = {} if args.fused else {fam: torch.empty(shapes[fam], dtype=torch.float32, device="cuda")
+                                     for fam in gen.FAMILIES}
     errors = torch.zeros(L * nfam, dtype=torch.float64, device="cuda")
     fws = torch.zeros(tb.FROBENIUS_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
@@ -577,6 +587,8 @@ def bench_reconstruct(args, torch, np, tb, gen):
 
     rec = tb.lib.tb_reconstruct_weight
     frob = tb.lib.tb_rel_frobenius_error
+    rerr = tb.lib.tb_reconstruction_error
+    fused = args.fused
 
     def build_calls(stream_handle):
         stream = ctypes.c_void_p(stream_handle)
@@ -585,6 +597,13 @@ def bench_reconstruct(args, torch, np, tb, gen):
             for j, fam in enumerate(gen.FAMILIES):
                 O, I = shapes[fam]
                 bd = bundles[(l, fam)]
+                if fused:
+                    calls.append(("fused", fam, rerr,
+                                  (bd["s"].data_ptr(), W0[(band_of[l], fam)].data_ptr(),
+                                   bd["U"].data_ptr() if R else None, bd["V"].data_ptr() if R else None,
+                                   originals[(l, fam)].data_ptr(), O, I, R, tb.TB_BF16, tb.TB_F32,
+                                   errors.data_ptr() + 8 * (l * nfam + j), fws.data_ptr(), fws.numel(), stream)))
+                    continue
                 w = rebuilt[fam]
                 calls.append(("reconstruct", fam, rec,
                               (bd["s"].data_ptr(), W0[(band_of[l], fam)].data_ptr(),
@@ -597,7 +616,7 @@ def bench_reconstruct(args, torch, np, tb, gen):
 
     band_idx = tb.lib.tb_band_index
     bout = ctypes.c_int32()
-    per_layer = 2 * nfam
+    per_layer = (1 if fused else 2) * nfam
 
     def run(calls, events=None):
         n = 0
@@ -615,9 +634,10 @@ def bench_reconstruct(args, torch, np, tb, gen):
 
     calls = build_calls(torch.cuda.current_stream().cuda_stream)
     nbytes = np.array([reconstruct_bytes(*shapes[c[1]], R) if c[0] == "reconstruct" else
+                       fused_error_bytes(*shapes[c[1]], R) if c[0] == "fused" else
                        frobenius_bytes(*shapes[c[1]]) for c in calls], dtype=np.float64)
     step_bytes = float(nbytes.sum())
-    step_flops = sum(2 * shapes[c[1]][0] * shapes[c[1]][1] * R for c in calls if c[0] == "reconstruct")
+    step_flops = sum(2 * shapes[c[1]][0] * shapes[c[1]][1] * R for c in calls if c[0] in ("reconstruct", "fused"))
 
     for _ in range(args.warmup):
         run(calls)
@@ -638,7 +658,8 @@ def bench_reconstruct(args, torch, np, tb, gen):
         def make_step(handle):
             c = build_calls(handle)
             return lambda: run(c)
-        g_ms, g_per, clocks = graph_leg(torch, make_step, args.steps, [errors] + list(rebuilt.values()))
+        g_ms, g_per, clocks = graph_leg(torch, make_step, args.steps,
+                                        [errors] + ([] if fused else list(rebuilt.values())))
         graph = {"value": round(step_bytes / (g_ms * 1e-3) / 1e9, 2), "ms_per_step": round(g_ms, 4),
                  **spread(g_per), "gpu": clocks}
 
@@ -646,8 +667,11 @@ def bench_reconstruct(args, torch, np, tb, gen):
     rec_kernel = ("reconstruct_rank0_kernel" if R == 0 else
                   "rp::reconstruct_persistent_kernel" if 192 < R <= 256 and R % 8 == 0 else
                   "mm::reconstruct_mfma_kernel" if R % 8 == 0 else "reconstruct_lowrank_kernel")
-    for kind, name in (("reconstruct", rec_kernel),
-                       ("frobenius", "frob_kernel")):
+    fused_kernel = ("rerr_rank0_kernel" if R == 0 else
+                    "rp::reconstruct_persistent_kernel<float, true>" if 192 < R <= 256 and R % 8 == 0 else
+                    "rerr_t128_kernel" if R % 8 == 0 else "rerr_t64_kernel")
+    kinds = (("fused", fused_kernel),) if fused else (("reconstruct", rec_kernel), ("frobenius", "frob_kernel"))
+    for kind, name in kinds:
         sel = np.array([c[0] == kind for c in calls])
         t = float(per_call_ms[sel].sum())
         gbs = float(nbytes[sel].sum()) / (t * 1e-3) / 1e9
@@ -659,11 +683,12 @@ def bench_reconstruct(args, torch, np, tb, gen):
             "frac": kernels[dom]["frac"], "kernel": kernels[dom]["kernel"], "calls_per_step": L * nfam,
             "avg_launch_us": round(kernels[dom]["ms_per_step"] * 1e3 / (L * nfam), 2),
             "algorithmic_per_launch": kernels[dom]["algorithmic_per_launch"],
-            "traffic": counter_traffic(kernels[dom]["kernel"], f"reconstruct60_R{R}_G{G}"), "kernels": kernels}
+            "traffic": counter_traffic(kernels[dom]["kernel"], f"reconstruct60_R{R}_G{G}{'_fused' if fused else ''}"),
+            "kernels": kernels}
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline_reconstruct(args, shapes, bundles, W0, originals, band_of, L, R, gen)
+        cpu = cpu_baseline_reconstruct(args, shapes, bundles, W0, originals, band_of, L, R, gen, fused)
 
     line = {
         "metric": METRIC,
@@ -679,7 +704,9 @@ def bench_reconstruct(args, torch, np, tb, gen):
         "dtype": "bf16->f32",
         "data": "synthetic",
         "config": {"workload": f"reconstruct60: {L}-layer stack, 7 projections per layer, rank {R}, G={G} bands, "
-                               f"rebuilt in fp32 and compared with the originals",
+                               + ("error against the originals without writing the rebuilt weight" if fused else
+                                  "rebuilt in fp32 and compared with the originals"),
+                   "fused": fused,
                    "layers": L, "rank": R, "bands": G, "pairs_per_step": L * nfam,
                    "step_bytes": step_bytes, "step_flops": step_flops, "parallelism": "single-gpu",
                    "mean_rel_error": float(err_host.mean()), "max_rel_error": float(err_host.max())},
@@ -692,7 +719,7 @@ def bench_reconstruct(args, torch, np, tb, gen):
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline_reconstruct(args, shapes, bundles, W0, originals, band_of, L, R, gen):
+def cpu_baseline_reconstruct(args, shapes, bundles, W0, originals, band_of, L, R, gen, fused=False):
     """Time the float64 oracle's reconstruct + error on the first (layer, projection) pairs of the stack."""
     import numpy as np
     import torch
@@ -715,10 +742,11 @@ def cpu_baseline_reconstruct(args, shapes, bundles, W0, originals, band_of, L, R
         V = oracle.bf16_bits_to_f64(v_bits) if R else np.zeros((I, 0))
         oracle.relative_frobenius_error(orig, oracle.reconstruct_weight(s, w0, U, V))
         secs += time.perf_counter() - t
-        done_bytes += reconstruct_bytes(O, I, R) + frobenius_bytes(O, I)
+        done_bytes += fused_error_bytes(O, I, R) if fused else reconstruct_bytes(O, I, R) + frobenius_bytes(O, I)
         used.append(f"{l}:{fam}")
     rate = done_bytes / secs
-    step = L * sum(reconstruct_bytes(o, i, R) + frobenius_bytes(o, i) for o, i in shapes.values())
+    step = L * sum(fused_error_bytes(o, i, R) if fused else reconstruct_bytes(o, i, R) + frobenius_bytes(o, i)
+                   for o, i in shapes.values())
     return {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": int(_blas_threads()),
             "kind": "oracle",
             "sample": f"{len(used)} (layer, projection) pairs of the same stack ({used[0]} .. {used[-1]}): "

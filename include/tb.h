@@ -196,6 +196,27 @@ tb_status tb_rel_frobenius_error(const void *original, const void *reconstructed
                                  tb_dtype dtype, double *result_device, void *workspace,
                                  size_t workspace_bytes, void *stream);
 
+/*
+ * tb_reconstruction_error -- relative_frobenius_error(original,
+ * reconstruct_weight(s, W0, U, V)) without writing the rebuilt weight ("The
+ * theta bundle", reconstruction formula; "Quality", section "Reconstruction
+ * error").  The rebuilt entries are formed in fp32 as tb_reconstruct_weight
+ * forms them for fp32 output; differences, squares and sums are taken in
+ * fp64 in a fixed order (deterministic).
+ *
+ *   s [out_dim], w0 [out_dim, in_dim], u [out_dim, rank], v [in_dim, rank]
+ *   in bundle_dtype (u, v may be NULL iff rank == 0); original
+ *   [out_dim, in_dim] in original_dtype; in_dim % 8 == 0.  result_device:
+ *   DEVICE pointer to one double, written (0 when the two agree, +inf when
+ *   only the original is zero).  workspace: as for tb_rel_frobenius_error
+ *   (same size; the same arrival counters, zero before the first use and left
+ *   zero by every call).  Errors as above.
+ */
+tb_status tb_reconstruction_error(const void *s, const void *w0, const void *u, const void *v, const void *original,
+                                  int64_t out_dim, int64_t in_dim, int64_t rank, tb_dtype bundle_dtype,
+                                  tb_dtype original_dtype, double *result_device, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *tb_status_string(tb_status status);
 

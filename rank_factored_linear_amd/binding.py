@@ -26,7 +26,7 @@ FROBENIUS_WORKSPACE_BYTES = 65536
 EXPORTED = (
     "tb_band_index", "tb_linear_forward_workspace_size", "tb_linear_forward",
     "tb_linear_forward_group_workspace_size", "tb_linear_forward_group",
-    "tb_reconstruct_weight", "tb_rel_frobenius_error", "tb_status_string", "tb_last_error",
+    "tb_reconstruct_weight", "tb_rel_frobenius_error", "tb_reconstruction_error", "tb_status_string", "tb_last_error",
 )
 
 
@@ -56,13 +56,15 @@ def _load() -> ctypes.CDLL:
     lib.tb_linear_forward_group.argtypes = [c_i32, ctypes.POINTER(Projection), c_i64, ctypes.c_int, c_p, c_sz, c_p]
     lib.tb_reconstruct_weight.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i64, c_i64, c_i64, ctypes.c_int, ctypes.c_int, c_p]
     lib.tb_rel_frobenius_error.argtypes = [c_p, c_p, c_i64, c_i64, ctypes.c_int, c_p, c_p, c_sz, c_p]
+    lib.tb_reconstruction_error.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i64, c_i64, c_i64, ctypes.c_int, ctypes.c_int,
+                                            c_p, c_p, c_sz, c_p]
     lib.tb_status_string.argtypes = [ctypes.c_int]
     lib.tb_status_string.restype = ctypes.c_char_p
     lib.tb_last_error.argtypes = []
     lib.tb_last_error.restype = ctypes.c_char_p
     for name in ("tb_band_index", "tb_linear_forward_workspace_size", "tb_linear_forward",
                  "tb_linear_forward_group_workspace_size", "tb_linear_forward_group",
-                 "tb_reconstruct_weight", "tb_rel_frobenius_error"):
+                 "tb_reconstruct_weight", "tb_rel_frobenius_error", "tb_reconstruction_error"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -247,4 +249,36 @@ def rel_frobenius_error(original: torch.Tensor, reconstructed: torch.Tensor,
         _frob_ws[key] = ws
     _check(lib.tb_rel_frobenius_error(_ptr(original), _ptr(reconstructed), rows, cols, _dtype_code(original.dtype),
                                       _ptr(out), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def _error_workspace() -> torch.Tensor:
+    key = (torch.cuda.current_device(), torch.cuda.current_stream().cuda_stream)
+    ws = _frob_ws.get(key)
+    if ws is None:
+        ws = torch.zeros(FROBENIUS_WORKSPACE_BYTES, dtype=torch.uint8, device=f"cuda:{key[0]}")
+        _frob_ws[key] = ws
+    return ws
+
+
+def reconstruction_error(original: torch.Tensor, s: torch.Tensor, W0: torch.Tensor, U: torch.Tensor | None,
+                         V: torch.Tensor | None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """relative_frobenius_error(original, diag(s) @ W0 + U @ V.T) without forming the rebuilt weight, as a 0-d
+    float64 GPU tensor (no sync), via tb_reconstruction_error."""
+    out_dim, in_dim = W0.shape
+    rank = 0 if U is None else U.shape[1]
+    if U is not None and rank == 0:
+        U = V = None
+    _need_cuda(original, s, W0, U, V, out)
+    if tuple(original.shape) != (out_dim, in_dim):
+        raise TBError(TB_ERR_INVALID_ARGUMENT, "original must have W0's shape")
+    for t in (s, U, V):
+        if t is not None and t.dtype != W0.dtype:
+            raise TBError(TB_ERR_INVALID_ARGUMENT, "s, W0, U and V must share one dtype")
+    if out is None:
+        out = torch.empty((), dtype=torch.float64, device=W0.device)
+    ws = _error_workspace()
+    _check(lib.tb_reconstruction_error(_ptr(s), _ptr(W0), _ptr(U), _ptr(V), _ptr(original), out_dim, in_dim, rank,
+                                       _dtype_code(W0.dtype), _dtype_code(original.dtype), _ptr(out), _ptr(ws),
+                                       ws.numel(), _stream()))
     return out

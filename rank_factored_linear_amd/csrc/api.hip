@@ -271,6 +271,33 @@ tb_status tb_reconstruct_weight(const void* s, const void* w0, const void* u, co
   return ok();
 }
 
+tb_status tb_reconstruction_error(const void* s, const void* w0, const void* u, const void* v, const void* original,
+                                  int64_t out_dim, int64_t in_dim, int64_t rank, tb_dtype bundle_dtype,
+                                  tb_dtype original_dtype, double* result_device, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(bundle_dtype) || !valid_dtype(original_dtype)) return fail(TB_ERR_INVALID_ARGUMENT, "unknown dtype");
+  tb_status st = check_dims(1, out_dim, in_dim, rank);
+  if (st != TB_OK) return st;
+  if (!s || !w0 || !original || !result_device || !workspace)
+    return fail(TB_ERR_INVALID_ARGUMENT, "s, w0, original, result and workspace must be non-NULL");
+  if (rank > 0 && (!u || !v)) return fail(TB_ERR_INVALID_ARGUMENT, "u and v must be non-NULL when rank > 0");
+  if (!aligned16(w0) || !aligned16(original) || (rank > 0 && (!aligned16(u) || !aligned16(v))))
+    return fail(TB_ERR_UNSUPPORTED, "w0, original, u and v must be 16-byte aligned");
+  if (!aligned_to(s, esize(bundle_dtype))) return fail(TB_ERR_UNSUPPORTED, "s must be aligned to its element size");
+  if (!aligned_to(result_device, 8) || !aligned_to(workspace, 16))
+    return fail(TB_ERR_UNSUPPORTED, "result must be 8-byte and workspace 16-byte aligned");
+  if (workspace_bytes < TB_FROBENIUS_WORKSPACE_BYTES)
+    return fail(TB_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is below %d", workspace_bytes,
+                TB_FROBENIUS_WORKSPACE_BYTES);
+  if (out_dim > (int64_t(1) << 40) / in_dim) return fail(TB_ERR_UNSUPPORTED, "matrix too large");
+  int cus = 0;
+  if (int e = device_cu_count(&cus)) return hip_fail(hipError_t(e), "querying the compute-unit count");
+  hipError_t e = launch_reconstruction_error(bundle_dtype, original_dtype, s, w0, u, v, original, out_dim, in_dim, rank,
+                                             result_device, workspace, cus, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launching the reconstruction error");
+  return ok();
+}
+
 tb_status tb_rel_frobenius_error(const void* original, const void* reconstructed, int64_t rows, int64_t cols,
                                  tb_dtype dtype, double* result_device, void* workspace, size_t workspace_bytes,
                                  void* stream) {

@@ -15,6 +15,8 @@
 // columns of one output row: 8-byte W0 loads and 16-byte fp32 stores.
 #include "tb_device.h"
 #include "tb_host.h"
+#include "tb_rebuild.h"
+#include "tb_reduce.h"
 
 namespace tb {
 
@@ -58,44 +60,23 @@ __global__ __launch_bounds__(kThreads) void reconstruct_rank0_kernel(const EI* _
   }
 }
 
-// Workgroup tile: 64 rows x 64 columns; wave w owns rows 16w..16w+15.
+// 64 x 64 tiles (any element type and rank); wave w owns rows 16 w .. +15.
 template <typename EI, typename EO>
 __global__ __launch_bounds__(kThreads) void reconstruct_lowrank_kernel(const EI* __restrict__ s, const EI* __restrict__ w0,
                                                                        const EI* __restrict__ u, const EI* __restrict__ v,
                                                                        EO* __restrict__ out, int O, int I, int R) {
-  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
-  const int lr = l & 15, kq = (l >> 4) * 8;
-  const int i0 = blockIdx.x * 64, o0 = blockIdx.y * 64 + w * 16;
-  const bool aligned = (R % 8) == 0;
+  const int l = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const int i0 = blockIdx.x * rebuild::t64::BT, o0 = blockIdx.y * rebuild::t64::BT;
   f32x4 acc[4];
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int urow = o0 + lr;
-  for (int kk = 0; kk < R; kk += 32) {
-    const int j = kk + kq;
-    Frag8<EI> fa = zero_frag<EI>();
-    if (urow < O && j < R)
-      fa = aligned ? load_frag<EI>(u + size_t(urow) * R + j) : load_frag_partial<EI>(u + size_t(urow) * R + j, min(8, R - j));
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const int vrow = i0 + ct * 16 + lr;
-      Frag8<EI> fb = zero_frag<EI>();
-      if (vrow < I && j < R)
-        fb = aligned ? load_frag<EI>(v + size_t(vrow) * R + j) : load_frag_partial<EI>(v + size_t(vrow) * R + j, min(8, R - j));
-      acc[ct] = mma_k32(fa, fb, acc[ct]);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_operand_guard();
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
+  rebuild::t64::product<EI>(u, v, O, I, R, o0, i0, acc);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int o = o0 + (l >> 4) * 4 + e;
+    const int o = o0 + w * 16 + (l >> 4) * 4 + e;
     if (o >= O) continue;
     const float sc = to_f32<EI>(s[o]);
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-      const int i = i0 + ct * 16 + lr;
+      const int i = i0 + ct * 16 + (l & 15);
       if (i < I) out[size_t(o) * I + i] = from_f32<EO>(acc[ct][e] + sc * to_f32<EI>(w0[size_t(o) * I + i]));
     }
   }
@@ -103,22 +84,6 @@ __global__ __launch_bounds__(kThreads) void reconstruct_lowrank_kernel(const EI*
 
 // ---- bf16 bundles, rank % 8 == 0 --------------------------------------------
 namespace mm {
-
-constexpr int BT = 128;              // output tile: BT rows of U (o) x BT rows of V (i)
-constexpr int BK = 64;               // k-tile (rank) staged in LDS
-constexpr int kRowBytes = BK * 2;    // 128-byte LDS rows of 8 16-byte chunks
-constexpr int kTileBytes = BT * kRowBytes;
-
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-__device__ __forceinline__ f32x16 mma32(uint4 a, uint4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
-                                                 0);
-}
-
-// Byte offset of chunk c of row r inside a tile: the chunk index is XORed
-// with r % 8, so eight consecutive rows read at one chunk hit all 32 banks.
-__device__ __forceinline__ int chunk_off(int r, int c) { return r * kRowBytes + ((c ^ (r & 7)) << 4); }
 
 template <typename EO>
 __device__ __forceinline__ void store4(EO* p, float a, float b, float c, float d) {
@@ -131,78 +96,20 @@ __device__ __forceinline__ void store4(EO* p, float a, float b, float c, float d
 }
 
 // blockIdx.x: 128-column block of the output (rows of V); blockIdx.y: 128-row
-// block (rows of U).  Wave w owns output rows 64 (w / 2) .. +63 and columns
-// 64 (w % 2) .. +63 of the tile.
+// block (rows of U).
 template <typename EO>
 __global__ __launch_bounds__(kThreads, 2) void reconstruct_mfma_kernel(const bf16_t* __restrict__ s,
                                                                         const bf16_t* __restrict__ w0,
                                                                         const bf16_t* __restrict__ u,
                                                                         const bf16_t* __restrict__ v,
                                                                         EO* __restrict__ out, int O, int I, int R) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kTileBytes];  // [U tile][V tile]
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int i0 = blockIdx.x * BT, o0 = blockIdx.y * BT;
-  const int wi = w & 1, wo = w >> 1;
-
-  // Staging: thread t moves chunk t % 8 of rows t / 8 + 32 q (q = 0..3) of both tiles.
-  const int sc = tid & 7, sr = tid >> 3;
-  uint4 su[4], sv[4];
-  auto fetch = [&](int kt) {
-    const int k = kt * BK + sc * 8;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int ro = o0 + sr + 32 * q, ri = i0 + sr + 32 * q;
-      su[q] = (ro < O && k < R) ? *reinterpret_cast<const uint4*>(u + size_t(ro) * R + k) : make_uint4(0, 0, 0, 0);
-      sv[q] = (ri < I && k < R) ? *reinterpret_cast<const uint4*>(v + size_t(ri) * R + k) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto stash = [&]() {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int off = chunk_off(sr + 32 * q, sc);
-      *reinterpret_cast<uint4*>(lds + off) = su[q];
-      *reinterpret_cast<uint4*>(lds + kTileBytes + off) = sv[q];
-    }
-  };
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
-
-  const int KT = (R + BK - 1) / BK;
-  const int h = l >> 5, lr = l & 31;
-  fetch(0);
-  for (int kt = 0; kt < KT; ++kt) {
-    if (kt) __syncthreads();          // every wave has read the previous k-tile
-    stash();
-    __syncthreads();
-    if (kt + 1 < KT) fetch(kt + 1);   // lands while this k-tile multiplies
-    uint4 fa[2][4], fb[2][4];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int ri = wi * 64 + rb * 32 + lr, ro = wo * 64 + rb * 32 + lr;
-        fa[rb][ks] = *reinterpret_cast<const uint4*>(lds + kTileBytes + chunk_off(ri, ks * 2 + h));
-        fb[rb][ks] = *reinterpret_cast<const uint4*>(lds + chunk_off(ro, ks * 2 + h));
-      }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mma32(fa[rb][ks], fb[cb][ks], acc[rb][cb]);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_operand_guard();
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  // acc[rb][cb] element 4 b + e is C[i][o] with i = 64 wi + 32 rb + 8 b + 4 h + e and
-  // o = 64 wo + 32 cb + lr (tile-relative): out[o][i .. i+3] per (rb, cb, b).
+  namespace t = rebuild::t128;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[t::kLdsBytes];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int i0 = blockIdx.x * t::BT, o0 = blockIdx.y * t::BT;
+  const int wi = w & 1, wo = w >> 1, h = l >> 5, lr = l & 31;
+  t::f32x16 acc[2][2];
+  t::product(u, v, O, I, R, o0, i0, lds, acc);
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     const int o = o0 + wo * 64 + cb * 32 + lr;
@@ -217,7 +124,7 @@ __global__ __launch_bounds__(kThreads, 2) void reconstruct_mfma_kernel(const bf1
         const int i = i0 + wi * 64 + rb * 32 + 8 * b + 4 * h;   // I % 8 == 0: i < I covers i .. i+3
         if (i >= I) continue;
         const uint2 wv = *reinterpret_cast<const uint2*>(wrow + i);
-        const f32x16& c = acc[rb][cb];
+        const t::f32x16& c = acc[rb][cb];
         store4<EO>(orow + i, c[4 * b + 0] + so * bf16_to_f32(uint16_t(wv.x)),
                    c[4 * b + 1] + so * bf16_to_f32(uint16_t(wv.x >> 16)),
                    c[4 * b + 2] + so * bf16_to_f32(uint16_t(wv.y)),
@@ -377,6 +284,20 @@ __device__ __forceinline__ void prefetch(Pre& q, const Tile& g, bool dummy, int 
     }
 }
 
+// Measuring the error against an fp32 original: the original's values in the
+// epilogue layout, one tile ahead (64 registers; two tiles ahead would spill).
+__device__ __forceinline__ void load_orig(u32x4 (&o)[2][8], const Tile& g, bool dummy, int I, int wo, int wi, int l) {
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int orel = wo * 64 + cb * 32 + 4 * p + (l >> 4), i = g.i0 + wi * 64 + (l & 15) * 4;
+      const bool ok = !dummy && orel < g.orows && i < I;
+      o[cb][p] = __builtin_amdgcn_raw_buffer_load_b128(g.ro, ok ? (orel * I + i) * 4 : kPast, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 __device__ __forceinline__ f32x16 mma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
                                                  0);
@@ -430,12 +351,16 @@ __device__ __forceinline__ void store_out(const Tile& g, int off, f32x4 c, u32x2
 // slot 3 and finally starts loading the W0 and s of gnn, two tiles ahead, into
 // q.  Every wait counts the loads and stores issued after the k-tile it needs:
 // two refills, one tile's stores (16) and two tiles' W0 and s loads (32 each)
-// lie between a k-tile 0..2 and its step, which the count caps at 63.
-template <typename EO>
+// lie between a k-tile 0..2 and its step, which the count caps at 63.  When
+// measuring the error (kErr) nothing is stored: the epilogue compares with the
+// original in o, which then receives gn's original (16 loads, issued before
+// the W0 and s loads of gnn), so the counts are the same; the error sums go
+// to num and den.
+template <typename EO, bool kErr>
 __device__ __forceinline__ void tile_pass(const Dma& d, lds_byte* const (&rdU)[2][4], lds_byte* const (&rdV)[2][4],
                                           lds_byte* stage, const Tile& g, const Tile& gn, bool gn_dummy,
-                                          const Tile& gnn, bool gnn_dummy, Pre& q, int I, int R, int wo, int wi,
-                                          int l) {
+                                          const Tile& gnn, bool gnn_dummy, Pre& q, u32x4 (&o)[2][8], int I, int R,
+                                          int wo, int wi, int l, double& num, double& den) {
   const int lr = l & 31, h = l >> 5;
   f32x16 acc[2][2];
 #pragma unroll
@@ -482,20 +407,42 @@ __device__ __forceinline__ void tile_pass(const Dma& d, lds_byte* const (&rdU)[2
       c[p] = *reinterpret_cast<const lds_f32x4*>(stage + orel * kStageRow + (chunk << 4));
     }
 #pragma unroll
-    for (int p = 0; p < 8; ++p)
-      store_out<EO>(g, out_off<EO>(g, I, wo, wi, cb, p, l), c[p], q.w[cb][p], bf16_to_f32(uint16_t(q.s[cb][p])));
+    for (int p = 0; p < 8; ++p) {
+      if constexpr (kErr) {
+        // Entries outside the matrix: the original, W0 and s read as zero and the product is zero.
+        const u32x2 wv = q.w[cb][p];
+        const float so = bf16_to_f32(uint16_t(q.s[cb][p]));
+        const float wr[4] = {c[p][0] + so * bf16_to_f32(uint16_t(wv[0])), c[p][1] + so * bf16_to_f32(uint16_t(wv[0] >> 16)),
+                             c[p][2] + so * bf16_to_f32(uint16_t(wv[1])), c[p][3] + so * bf16_to_f32(uint16_t(wv[1] >> 16))};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const double ov = double(__uint_as_float(o[cb][p][e])), dd = ov - double(wr[e]);
+          num += dd * dd;
+          den += ov * ov;
+        }
+      } else {
+        store_out<EO>(g, out_off<EO>(g, I, wo, wi, cb, p, l), c[p], q.w[cb][p], bf16_to_f32(uint16_t(q.s[cb][p])));
+      }
+    }
   }
+  if constexpr (kErr) load_orig(o, gn, gn_dummy, I, wo, wi, l);
   prefetch(q, gnn, gnn_dummy, I, wo, wi, l);
 }
 
-template <typename EO>
+// kErr = false: out receives the rebuilt weight.  kErr = true: out is the
+// fp32 original (read only) and the relative error goes to *result through
+// the grid-wide sum of tb_reduce.h (partial, counters).
+template <typename EO, bool kErr>
 __global__ __launch_bounds__(kThreads, 1) void reconstruct_persistent_kernel(const bf16_t* __restrict__ s,
                                                                              const bf16_t* __restrict__ w0,
                                                                              const bf16_t* __restrict__ u,
                                                                              const bf16_t* __restrict__ v,
                                                                              EO* __restrict__ out, int O, int I,
-                                                                             int R, int tiles_i, int tiles) {
+                                                                             int R, int tiles_i, int tiles,
+                                                                             uint64_t* partial, unsigned* counters,
+                                                                             double* result) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes];
+  double num = 0.0, den = 0.0;
   const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6), l = int(threadIdx.x) & 63;
   const int wi = w & 1, wo = w >> 1, lr = l & 31, h = l >> 5;
   const int G = int(gridDim.x);
@@ -531,28 +478,37 @@ __global__ __launch_bounds__(kThreads, 1) void reconstruct_persistent_kernel(con
   // Tiles past the workgroup's last are dummies: their loads return zeros
   // into free slots and registers, and nothing of them is stored.
   auto tile = [&](int tt) { return tile_at<EO>(tt < tiles ? tt : t, tiles_i, s, w0, u, v, out, O, I, R); };
-  Pre qa, qb;   // W0 and s of the current tile and of the next, alternating
+  Pre qa, qb;         // W0 and s of the current tile and of the next, alternating
+  u32x4 oq[2][8];     // the current tile's original (kErr)
   Tile g = tile(t);
   issue<0>(d, g, 0, false, R);
   issue<1>(d, g, 1, false, R);
   issue<2>(d, g, 2, false, R);
   prefetch(qa, g, false, I, wo, wi, l);
   prefetch(qb, tile(t + G), t + G >= tiles, I, wo, wi, l);
+  if constexpr (kErr) load_orig(oq, g, false, I, wo, wi, l);
   for (;;) {
     Tile gn = tile(t + G);
-    tile_pass<EO>(d, rdU, rdV, stage, g, gn, t + G >= tiles, tile(t + 2 * G), t + 2 * G >= tiles, qa, I, R, wo, wi,
-                  l);
+    tile_pass<EO, kErr>(d, rdU, rdV, stage, g, gn, t + G >= tiles, tile(t + 2 * G), t + 2 * G >= tiles, qa, oq, I, R,
+                        wo, wi, l, num, den);
     t += G;
     if (t >= tiles) break;
     g = gn;
     gn = tile(t + G);
-    tile_pass<EO>(d, rdU, rdV, stage, g, gn, t + G >= tiles, tile(t + 2 * G), t + 2 * G >= tiles, qb, I, R, wo, wi,
-                  l);
+    tile_pass<EO, kErr>(d, rdU, rdV, stage, g, gn, t + G >= tiles, tile(t + 2 * G), t + 2 * G >= tiles, qb, oq, I, R,
+                        wo, wi, l, num, den);
     t += G;
     if (t >= tiles) break;
     g = gn;
   }
   wait_vm<0>();  // no load into LDS may still be in flight when the workgroup ends
+  if constexpr (kErr) {
+    __syncthreads();  // the ring is free: its first 4 KB hold the reduction
+    double* sa = reinterpret_cast<double*>(ring);
+    double* sb = sa + kThreads;
+    reduce::block_reduce2<kThreads>(num, den, sa, sb);
+    reduce::finish_ratio<kThreads>(num, den, partial, counters, result, sa, sb);
+  }
 }
 
 }  // namespace rp
@@ -572,11 +528,12 @@ hipError_t launch_typed(const void* s, const void* w0, const void* u, const void
     if (int e = device_cu_count(&cus)) return hipError_t(e);
     const int tiles_i = int((I + rp::BT - 1) / rp::BT), tiles = tiles_i * int((O + rp::BT - 1) / rp::BT);
     const int grid = tiles < cus ? tiles : cus;
-    hipLaunchKernelGGL((rp::reconstruct_persistent_kernel<EO>), dim3(unsigned(grid)), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((rp::reconstruct_persistent_kernel<EO, false>), dim3(unsigned(grid)), dim3(kThreads), 0, stream,
                        static_cast<const bf16_t*>(s), static_cast<const bf16_t*>(w0), static_cast<const bf16_t*>(u),
-                       static_cast<const bf16_t*>(v), static_cast<EO*>(w_out), int(O), int(I), int(R), tiles_i, tiles);
-  } else if (sizeof(EI) == 2 && R % 8 == 0 && (O + mm::BT - 1) / mm::BT <= 65535) {
-    dim3 grid(unsigned((I + mm::BT - 1) / mm::BT), unsigned((O + mm::BT - 1) / mm::BT));
+                       static_cast<const bf16_t*>(v), static_cast<EO*>(w_out), int(O), int(I), int(R), tiles_i, tiles,
+                       nullptr, nullptr, nullptr);
+  } else if (sizeof(EI) == 2 && R % 8 == 0 && (O + rebuild::t128::BT - 1) / rebuild::t128::BT <= 65535) {
+    dim3 grid(unsigned((I + rebuild::t128::BT - 1) / rebuild::t128::BT), unsigned((O + rebuild::t128::BT - 1) / rebuild::t128::BT));
     hipLaunchKernelGGL((mm::reconstruct_mfma_kernel<EO>), grid, dim3(kThreads), 0, stream,
                        static_cast<const bf16_t*>(s), static_cast<const bf16_t*>(w0), static_cast<const bf16_t*>(u),
                        static_cast<const bf16_t*>(v), static_cast<EO*>(w_out), int(O), int(I), int(R));
@@ -590,6 +547,23 @@ hipError_t launch_typed(const void* s, const void* w0, const void* u, const void
 }
 
 }  // namespace
+
+bool persistent_error_supported(int64_t out_dim, int64_t in_dim, int64_t rank) {
+  return rank % 8 == 0 && rank > 3 * rp::BK && rank <= 4 * rp::BK && in_dim < (1 << 22) && out_dim < (1 << 24);
+}
+
+hipError_t launch_reconstruction_error_persistent(const void* s, const void* w0, const void* u, const void* v,
+                                                  const float* orig, int64_t O, int64_t I, int64_t R, double* result,
+                                                  void* workspace, int cus, hipStream_t stream) {
+  const int tiles_i = int((I + rp::BT - 1) / rp::BT), tiles = tiles_i * int((O + rp::BT - 1) / rp::BT);
+  int grid = tiles < cus ? tiles : cus;
+  if (grid > reduce::kMaxPartials) grid = reduce::kMaxPartials;
+  hipLaunchKernelGGL((rp::reconstruct_persistent_kernel<float, true>), dim3(unsigned(grid)), dim3(kThreads), 0, stream,
+                     static_cast<const bf16_t*>(s), static_cast<const bf16_t*>(w0), static_cast<const bf16_t*>(u),
+                     static_cast<const bf16_t*>(v), const_cast<float*>(orig), int(O), int(I), int(R), tiles_i, tiles,
+                     reduce::partials(workspace), reduce::counters(workspace), result);
+  return hipGetLastError();
+}
 
 hipError_t launch_reconstruct(tb_dtype in_dtype, tb_dtype out_dtype, const void* s, const void* w0, const void* u,
                               const void* v, void* w_out, int64_t out_dim, int64_t in_dim, int64_t rank,

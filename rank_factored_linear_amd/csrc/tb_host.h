@@ -89,6 +89,17 @@ hipError_t launch_reconstruct(tb_dtype in_dtype, tb_dtype out_dtype, const void*
                               const void* v, void* w_out, int64_t out_dim, int64_t in_dim, int64_t rank,
                               hipStream_t stream);
 
+// ---- reconstruction error without the rebuilt weight -----------------------
+// bf16 bundles of rank 193..256 (multiple of 8) against an fp32 original: the
+// persistent direct-to-LDS rebuild kernel with an error epilogue.
+bool persistent_error_supported(int64_t out_dim, int64_t in_dim, int64_t rank);
+hipError_t launch_reconstruction_error_persistent(const void* s, const void* w0, const void* u, const void* v,
+                                                  const float* orig, int64_t out_dim, int64_t in_dim, int64_t rank,
+                                                  double* result, void* workspace, int cus, hipStream_t stream);
+hipError_t launch_reconstruction_error(tb_dtype bundle_dtype, tb_dtype orig_dtype, const void* s, const void* w0,
+                                       const void* u, const void* v, const void* orig, int64_t out_dim, int64_t in_dim,
+                                       int64_t rank, double* result, void* workspace, int cus, hipStream_t stream);
+
 // ---- relative Frobenius error ---------------------------------------------
 hipError_t launch_frobenius(tb_dtype dtype, const void* a, const void* b, int64_t n, double* result,
                             void* workspace, int cus, hipStream_t stream);

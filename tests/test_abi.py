@@ -134,6 +134,28 @@ def test_frobenius_rejects_before_launch():
     assert f(FAKE, FAKE + 4, 4, 8, 0, FAKE, FAKE, ws, None) == 2
 
 
+def test_reconstruction_error_rejects_before_launch():
+    f = lib.tb_reconstruction_error
+    ws = binding.FROBENIUS_WORKSPACE_BYTES
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 8, 1, 0, FAKE, FAKE, ws, None]
+
+    def call(**changes):
+        a = list(args)
+        for k, v in changes.items():
+            a[int(k[1:])] = v
+        return f(*a)
+    assert call(a0=None) == 1                 # s
+    assert call(a4=None) == 1                 # original
+    assert call(a2=None) == 1                 # u with rank > 0
+    assert call(a5=0) == 1                    # out_dim
+    assert call(a6=12) == 2                   # in_dim % 8
+    assert call(a4=FAKE + 4) == 2             # original alignment
+    assert call(a8=7) == 1 and call(a9=7) == 1
+    assert call(a12=ws - 1) == 1              # workspace too small
+    assert call(a10=FAKE + 4) == 2            # result alignment
+    assert lib.tb_last_error().decode()
+
+
 def test_workspace_size_rejects_bad_arguments():
     out = ctypes.c_size_t(0)
     assert lib.tb_linear_forward_workspace_size(0, 64, 64, 0, 0, ctypes.byref(out)) == 1

@@ -45,3 +45,12 @@ def test_reconstruct_and_error_bytes_per_stack():
 def test_spread_of_trials():
     assert bench.spread([3.0, 1.0, 2.0]) == {"median_ms": 2.0, "min_ms": 1.0, "max_ms": 3.0, "trials": 3}
     assert bench.spread([4.0, 1.0, 2.0, 3.0])["median_ms"] == 2.5
+
+
+def test_fused_error_bytes():
+    # The error without the rebuilt weight reads the bf16 bundle and the fp32 original once: 6 bytes per element
+    # plus the factors, against 14 for rebuilding in fp32 and then comparing.
+    O, I, R = 21504, 5376, 256
+    assert bench.fused_error_bytes(O, I, R) == 2 * (O * I + R * (O + I) + O) + 4 * O * I
+    ratio = (bench.reconstruct_bytes(O, I, R) + bench.frobenius_bytes(O, I)) / bench.fused_error_bytes(O, I, R)
+    assert 2.2 < ratio < 2.35

@@ -317,6 +317,64 @@ def test_frobenius_closed_forms():
 
 
 # ---------------------------------------------------------------------------
+# Reconstruction error without the rebuilt weight (tb_reconstruction_error)
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("bundle", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(17, 40, 4), (130, 264, 12), (64, 512, 256), (33, 72, 0), (1, 8, 3), (300, 520, 72),
+                                   (257, 1032, 136), (129, 136, 256), (2100, 2104, 64), (1000, 1000, 0), (1000, 1000, 200),
+                                   (2100, 2104, 256), (4500, 1024, 248)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_reconstruction_error_small(shape, bundle):
+    O, I, R = shape
+    _, s, W0, U, V = _rand_case(1, O, I, R, bundle, seed=O * 7 + I + R)
+    g = torch.Generator(device="cpu").manual_seed(O + R)
+    Ud = exact(U) if R else np.zeros((O, 0))
+    Vd = exact(V) if R else np.zeros((I, 0))
+    rebuilt64 = oracle.reconstruct_weight(exact(s), exact(W0), Ud, Vd)
+    for orig_dtype in (torch.float32, torch.bfloat16):
+        # An original close to the bundle's weight (error ~ 5%), in the original's own dtype.
+        orig = (torch.from_numpy(rebuilt64).float() + 0.05 * rebuilt64.std() * torch.randn(O, I, generator=g)).to(orig_dtype).to(DEV)
+        e = float(tb.reconstruction_error(orig, s, W0, U if R else None, V if R else None).item())
+        want = oracle.relative_frobenius_error(exact(orig), rebuilt64)
+        # The kernel compares with the fp32 rounding of the rebuilt entries: |change| <= 2^-24 |W| per entry.
+        assert abs(e - want) <= 1e-6 * max(want, 1e-3), (orig_dtype, e, want)
+        if orig_dtype == torch.float32:
+            rec = tb.reconstruct_weight(s, W0, U if R else None, V if R else None, out_dtype=torch.float32)
+            composed = float(tb.rel_frobenius_error(orig, rec).item())
+            assert e == pytest.approx(composed, rel=1e-12, abs=1e-15)
+    ws = tb._error_workspace()
+    torch.cuda.synchronize()
+    assert int(ws[-8192:].count_nonzero().item()) == 0
+
+
+@pytest.mark.parametrize("rank", [256, 0])
+@pytest.mark.parametrize("family", gen.FAMILIES)
+def test_reconstruction_error_large(rank, family):
+    # 60-layer shapes: equals rebuilding in fp32 and then measuring, for every band's first layer.
+    for layer in _parity_layers(6)[::3]:
+        band = tb.band_index(60, 6, layer)
+        _say(f"reconstruction error rank={rank} {family} layer={layer}")
+        W0 = gen.device_w0(torch, 5, family, gen.SHAPES_60, band)
+        bun = gen.device_bundle(torch, 5, family, gen.SHAPES_60, layer, band, rank, with_w0=False)
+        U, V = (bun["U"], bun["V"]) if rank else (None, None)
+        orig = gen.device_original(torch, W0, 5, family, layer)
+        fused = [float(tb.reconstruction_error(orig, bun["s"], W0, U, V).item()) for _ in range(2)]
+        assert fused[0] == fused[1]                      # fixed summation order
+        rec = tb.reconstruct_weight(bun["s"], W0, U, V, out_dtype=torch.float32)
+        composed = float(tb.rel_frobenius_error(orig, rec).item())
+        assert fused[0] == pytest.approx(composed, rel=1e-12)
+        if family == "k_proj":                           # the float64 oracle on the whole matrix
+            Ud = exact(U) if rank else np.zeros((W0.shape[0], 0))
+            Vd = exact(V) if rank else np.zeros((W0.shape[1], 0))
+            want = oracle.relative_frobenius_error(exact(orig), oracle.reconstruct_weight(exact(bun["s"]), exact(W0), Ud, Vd))
+            assert abs(fused[0] - want) <= 1e-6 * want
+        del W0, bun, rec, orig
+        torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
 # Determinism and workspace state
 # ---------------------------------------------------------------------------
 
