@@ -664,11 +664,12 @@ def bench_reconstruct(args, torch, np, tb, gen):
                  **spread(g_per), "gpu": clocks}
 
     kernels = {}
+    kt = (R + 63) // 64
     rec_kernel = ("reconstruct_rank0_kernel" if R == 0 else
-                  "rp::reconstruct_persistent_kernel" if 192 < R <= 256 and R % 8 == 0 else
+                  f"rp::reconstruct_persistent_kernel<float, false, {kt}>" if R <= 256 and R % 8 == 0 else
                   "mm::reconstruct_mfma_kernel" if R % 8 == 0 else "reconstruct_lowrank_kernel")
     fused_kernel = ("rerr_rank0_kernel" if R == 0 else
-                    "rp::reconstruct_persistent_kernel<float, true>" if 192 < R <= 256 and R % 8 == 0 else
+                    f"rp::reconstruct_persistent_kernel<float, true, {kt}>" if R <= 256 and R % 8 == 0 else
                     "rerr_t128_kernel" if R % 8 == 0 else "rerr_t64_kernel")
     kinds = (("fused", fused_kernel),) if fused else (("reconstruct", rec_kernel), ("frobenius", "frob_kernel"))
     for kind, name in kinds:

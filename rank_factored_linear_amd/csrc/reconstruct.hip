@@ -344,24 +344,44 @@ __device__ __forceinline__ void store_out(const Tile& g, int off, f32x4 c, u32x2
   }
 }
 
-// One output tile.  On entry k-tiles 0..2 of g are in flight into ring slots
-// 0..2 and q holds (or is loading) g's W0 and s.  Step k waits for k-tile k,
-// publishes it, refills the slot every wave has just finished with (k-tile 3
-// of g, then k-tiles 0..2 of gn), and multiplies.  The epilogue goes through
-// slot 3 and finally starts loading the W0 and s of gnn, two tiles ahead, into
-// q.  Every wait counts the loads and stores issued after the k-tile it needs:
-// two refills, one tile's stores (16) and two tiles' W0 and s loads (32 each)
-// lie between a k-tile 0..2 and its step, which the count caps at 63.  When
-// measuring the error (kErr) nothing is stored: the epilogue compares with the
-// original in o, which then receives gn's original (16 loads, issued before
-// the W0 and s loads of gnn), so the counts are the same; the error sums go
-// to num and den.
-template <typename EO, bool kErr>
+// The k-tiles of all of a workgroup's output tiles form one stream: k-tile
+// k of its n-th tile is stream entry j = n KT + k (KT = k-tiles per tile,
+// ceil(rank / 64)) and lives in ring slot j % 4.  Step j waits for entry j,
+// publishes it to every wave, refills the slot every wave has just finished
+// with (entry j + 3) and multiplies.  After a tile's last step its epilogue
+// goes through the slot that step read, then issues the tile-end loads:
+// (kErr) the original of the next tile, 16 loads, and the W0 and s of the
+// tile two ahead, 32 loads; the stores of the epilogue are 16 more (none when
+// kErr).  Every load and store is issued unconditionally, so the count of
+// memory instructions after entry j's last load when step j waits is a
+// constant: the refills of the two steps between (16) plus 48 for each tile
+// end among the three steps before j.  vmcnt counts up to 63, so 63 stands
+// for any larger count.  (The prologue issues entries 0..2 and then 64 or
+// more loads, at least as many.)
+template <int KT>
+__host__ __device__ constexpr int step_wait(int k) {
+  int ends = 0;
+  for (int r = k - 3; r < k; ++r)
+    if ((((r + 1) % KT) + KT) % KT == 0) ++ends;
+  const int n = 16 + 48 * ends;
+  return n < 63 ? n : 63;
+}
+static_assert(step_wait<4>(0) == 63 && step_wait<4>(1) == 63 && step_wait<4>(2) == 63 && step_wait<4>(3) == 16,
+              "four k-tiles per tile");
+static_assert(step_wait<1>(0) == 63 && step_wait<2>(1) == 63 && step_wait<3>(2) == 63 && step_wait<3>(3) == 63,
+              "a tile end among every three steps");
+
+template <int V> struct IC { static constexpr int value = V; };
+
+// Output tile number t (of this workgroup's sequence, stream entries from
+// J0 mod 4 on); tile(t') gives the views of a later tile.
+template <typename EO, bool kErr, int KT, int J0, typename TileFn>
 __device__ __forceinline__ void tile_pass(const Dma& d, lds_byte* const (&rdU)[2][4], lds_byte* const (&rdV)[2][4],
-                                          lds_byte* stage, const Tile& g, const Tile& gn, bool gn_dummy,
-                                          const Tile& gnn, bool gnn_dummy, Pre& q, u32x4 (&o)[2][8], int I, int R,
-                                          int wo, int wi, int l, double& num, double& den) {
-  const int lr = l & 31, h = l >> 5;
+                                          lds_byte* base, const TileFn& tile, int t, int G, int tiles, Pre& q,
+                                          u32x4 (&o)[2][8], int I, int R, int wo, int wi, int l, double& num,
+                                          double& den) {
+  const int lr = l & 31, h = l >> 5, w = wo * 2 + wi;
+  const Tile g = tile(t);
   f32x16 acc[2][2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -370,23 +390,20 @@ __device__ __forceinline__ void tile_pass(const Dma& d, lds_byte* const (&rdU)[2
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
-  wait_vm<63>();
-  __syncthreads();
-  issue<3>(d, g, 3, false, R);
-  multiply_step<0>(rdU, rdV, acc);
-  wait_vm<63>();
-  __syncthreads();
-  issue<0>(d, gn, 0, gn_dummy, R);
-  multiply_step<1>(rdU, rdV, acc);
-  wait_vm<63>();
-  __syncthreads();
-  issue<1>(d, gn, 1, gn_dummy, R);
-  multiply_step<2>(rdU, rdV, acc);
-  wait_vm<16>();
-  __syncthreads();
-  issue<2>(d, gn, 2, gn_dummy, R);
-  multiply_step<3>(rdU, rdV, acc);
+  auto step = [&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    constexpr int dn = (k + 3) / KT, kk = (k + 3) % KT;   // entry j + 3: tile t + dn G, k-tile kk
+    wait_vm<step_wait<KT>(k)>();
+    __syncthreads();
+    issue<(J0 + k + 3) % 4>(d, tile(t + dn * G), kk, t + dn * G >= tiles, R);
+    multiply_step<(J0 + k) % 4>(rdU, rdV, acc);
+  };
+  step(IC<0>{});
+  if constexpr (KT > 1) step(IC<1>{});
+  if constexpr (KT > 2) step(IC<2>{});
+  if constexpr (KT > 3) step(IC<3>{});
 
+  lds_byte* stage = base + ((J0 + KT - 1) % 4) * kSlotBytes + w * 8192;
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     __syncthreads();
@@ -425,14 +442,14 @@ __device__ __forceinline__ void tile_pass(const Dma& d, lds_byte* const (&rdU)[2
       }
     }
   }
-  if constexpr (kErr) load_orig(o, gn, gn_dummy, I, wo, wi, l);
-  prefetch(q, gnn, gnn_dummy, I, wo, wi, l);
+  if constexpr (kErr) load_orig(o, tile(t + G), t + G >= tiles, I, wo, wi, l);
+  prefetch(q, tile(t + 2 * G), t + 2 * G >= tiles, I, wo, wi, l);
 }
 
 // kErr = false: out receives the rebuilt weight.  kErr = true: out is the
 // fp32 original (read only) and the relative error goes to *result through
-// the grid-wide sum of tb_reduce.h (partial, counters).
-template <typename EO, bool kErr>
+// the grid-wide sum of tb_reduce.h (partial, counters).  KT = ceil(rank / 64).
+template <typename EO, bool kErr, int KT>
 __global__ __launch_bounds__(kThreads, 1) void reconstruct_persistent_kernel(const bf16_t* __restrict__ s,
                                                                              const bf16_t* __restrict__ w0,
                                                                              const bf16_t* __restrict__ u,
@@ -473,33 +490,29 @@ __global__ __launch_bounds__(kThreads, 1) void reconstruct_persistent_kernel(con
         rdV[pr][ks] = opaque(base + pr * 2 * kSlotBytes + (wi * 64 + lr) * 128 + chunk);
       }
   }
-  lds_byte* stage = base + 3 * kSlotBytes + w * 8192;
 
   // Tiles past the workgroup's last are dummies: their loads return zeros
   // into free slots and registers, and nothing of them is stored.
-  auto tile = [&](int tt) { return tile_at<EO>(tt < tiles ? tt : t, tiles_i, s, w0, u, v, out, O, I, R); };
+  const auto tile = [&](int tt) { return tile_at<EO>(tt < tiles ? tt : t, tiles_i, s, w0, u, v, out, O, I, R); };
   Pre qa, qb;         // W0 and s of the current tile and of the next, alternating
   u32x4 oq[2][8];     // the current tile's original (kErr)
-  Tile g = tile(t);
-  issue<0>(d, g, 0, false, R);
-  issue<1>(d, g, 1, false, R);
-  issue<2>(d, g, 2, false, R);
-  prefetch(qa, g, false, I, wo, wi, l);
+  // Stream entries 0..2.
+  issue<0>(d, tile(t), 0, false, R);
+  issue<1>(d, tile(t + (1 / KT) * G), 1 % KT, t + (1 / KT) * G >= tiles, R);
+  issue<2>(d, tile(t + (2 / KT) * G), 2 % KT, t + (2 / KT) * G >= tiles, R);
+  prefetch(qa, tile(t), false, I, wo, wi, l);
   prefetch(qb, tile(t + G), t + G >= tiles, I, wo, wi, l);
-  if constexpr (kErr) load_orig(oq, g, false, I, wo, wi, l);
+  if constexpr (kErr) load_orig(oq, tile(t), false, I, wo, wi, l);
+  // Four tiles per round, so that every slot index is a constant.
   for (;;) {
-    Tile gn = tile(t + G);
-    tile_pass<EO, kErr>(d, rdU, rdV, stage, g, gn, t + G >= tiles, tile(t + 2 * G), t + 2 * G >= tiles, qa, oq, I, R,
-                        wo, wi, l, num, den);
-    t += G;
-    if (t >= tiles) break;
-    g = gn;
-    gn = tile(t + G);
-    tile_pass<EO, kErr>(d, rdU, rdV, stage, g, gn, t + G >= tiles, tile(t + 2 * G), t + 2 * G >= tiles, qb, oq, I, R,
-                        wo, wi, l, num, den);
-    t += G;
-    if (t >= tiles) break;
-    g = gn;
+    tile_pass<EO, kErr, KT, 0>(d, rdU, rdV, base, tile, t, G, tiles, qa, oq, I, R, wo, wi, l, num, den);
+    if ((t += G) >= tiles) break;
+    tile_pass<EO, kErr, KT, KT % 4>(d, rdU, rdV, base, tile, t, G, tiles, qb, oq, I, R, wo, wi, l, num, den);
+    if ((t += G) >= tiles) break;
+    tile_pass<EO, kErr, KT, (2 * KT) % 4>(d, rdU, rdV, base, tile, t, G, tiles, qa, oq, I, R, wo, wi, l, num, den);
+    if ((t += G) >= tiles) break;
+    tile_pass<EO, kErr, KT, (3 * KT) % 4>(d, rdU, rdV, base, tile, t, G, tiles, qb, oq, I, R, wo, wi, l, num, den);
+    if ((t += G) >= tiles) break;
   }
   wait_vm<0>();  // no load into LDS may still be in flight when the workgroup ends
   if constexpr (kErr) {
@@ -511,7 +524,31 @@ __global__ __launch_bounds__(kThreads, 1) void reconstruct_persistent_kernel(con
   }
 }
 
+template <typename EO, bool kErr>
+hipError_t launch(const void* s, const void* w0, const void* u, const void* v, EO* out, int64_t O, int64_t I,
+                  int64_t R, int grid, int tiles_i, int tiles, uint64_t* partial, unsigned* counters, double* result,
+                  hipStream_t stream) {
+  const int kt = int((R + BK - 1) / BK);
+#define TB_RP_LAUNCH(K)                                                                                              \
+  hipLaunchKernelGGL((reconstruct_persistent_kernel<EO, kErr, K>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, \
+                     static_cast<const bf16_t*>(s), static_cast<const bf16_t*>(w0), static_cast<const bf16_t*>(u),  \
+                     static_cast<const bf16_t*>(v), out, int(O), int(I), int(R), tiles_i, tiles, partial, counters, \
+                     result)
+  if (kt == 1) TB_RP_LAUNCH(1);
+  else if (kt == 2) TB_RP_LAUNCH(2);
+  else if (kt == 3) TB_RP_LAUNCH(3);
+  else TB_RP_LAUNCH(4);
+#undef TB_RP_LAUNCH
+  return hipGetLastError();
+}
+
 }  // namespace rp
+
+// The persistent kernel: bf16 bundles, 0 < rank <= 256 with rank % 8 == 0,
+// and 32-bit lane offsets within a 128-row band of the output.
+bool persistent_supported(int64_t O, int64_t I, int64_t R) {
+  return R > 0 && R % 8 == 0 && R <= 4 * rp::BK && I < (1 << 22) && O < (1 << 24);
+}
 
 template <typename EI, typename EO>
 hipError_t launch_typed(const void* s, const void* w0, const void* u, const void* v, void* w_out, int64_t O, int64_t I,
@@ -522,16 +559,12 @@ hipError_t launch_typed(const void* s, const void* w0, const void* u, const void
     if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL((reconstruct_rank0_kernel<EI, EO>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
                        static_cast<const EI*>(s), static_cast<const EI*>(w0), static_cast<EO*>(w_out), n, int(I));
-  } else if (sizeof(EI) == 2 && R % 8 == 0 && R > 3 * rp::BK && R <= 4 * rp::BK && I < (1 << 22) &&
-             O < (1 << 24)) {
+  } else if (sizeof(EI) == 2 && persistent_supported(O, I, R)) {
     int cus = 0;
     if (int e = device_cu_count(&cus)) return hipError_t(e);
     const int tiles_i = int((I + rp::BT - 1) / rp::BT), tiles = tiles_i * int((O + rp::BT - 1) / rp::BT);
-    const int grid = tiles < cus ? tiles : cus;
-    hipLaunchKernelGGL((rp::reconstruct_persistent_kernel<EO, false>), dim3(unsigned(grid)), dim3(kThreads), 0, stream,
-                       static_cast<const bf16_t*>(s), static_cast<const bf16_t*>(w0), static_cast<const bf16_t*>(u),
-                       static_cast<const bf16_t*>(v), static_cast<EO*>(w_out), int(O), int(I), int(R), tiles_i, tiles,
-                       nullptr, nullptr, nullptr);
+    return rp::launch<EO, false>(s, w0, u, v, static_cast<EO*>(w_out), O, I, R, tiles < cus ? tiles : cus, tiles_i,
+                                 tiles, nullptr, nullptr, nullptr, stream);
   } else if (sizeof(EI) == 2 && R % 8 == 0 && (O + rebuild::t128::BT - 1) / rebuild::t128::BT <= 65535) {
     dim3 grid(unsigned((I + rebuild::t128::BT - 1) / rebuild::t128::BT), unsigned((O + rebuild::t128::BT - 1) / rebuild::t128::BT));
     hipLaunchKernelGGL((mm::reconstruct_mfma_kernel<EO>), grid, dim3(kThreads), 0, stream,
@@ -549,7 +582,7 @@ hipError_t launch_typed(const void* s, const void* w0, const void* u, const void
 }  // namespace
 
 bool persistent_error_supported(int64_t out_dim, int64_t in_dim, int64_t rank) {
-  return rank % 8 == 0 && rank > 3 * rp::BK && rank <= 4 * rp::BK && in_dim < (1 << 22) && out_dim < (1 << 24);
+  return persistent_supported(out_dim, in_dim, rank);
 }
 
 hipError_t launch_reconstruction_error_persistent(const void* s, const void* w0, const void* u, const void* v,
@@ -558,11 +591,8 @@ hipError_t launch_reconstruction_error_persistent(const void* s, const void* w0,
   const int tiles_i = int((I + rp::BT - 1) / rp::BT), tiles = tiles_i * int((O + rp::BT - 1) / rp::BT);
   int grid = tiles < cus ? tiles : cus;
   if (grid > reduce::kMaxPartials) grid = reduce::kMaxPartials;
-  hipLaunchKernelGGL((rp::reconstruct_persistent_kernel<float, true>), dim3(unsigned(grid)), dim3(kThreads), 0, stream,
-                     static_cast<const bf16_t*>(s), static_cast<const bf16_t*>(w0), static_cast<const bf16_t*>(u),
-                     static_cast<const bf16_t*>(v), const_cast<float*>(orig), int(O), int(I), int(R), tiles_i, tiles,
-                     reduce::partials(workspace), reduce::counters(workspace), result);
-  return hipGetLastError();
+  return rp::launch<float, true>(s, w0, u, v, const_cast<float*>(orig), O, I, R, grid, tiles_i, tiles,
+                                 reduce::partials(workspace), reduce::counters(workspace), result, stream);
 }
 
 hipError_t launch_reconstruct(tb_dtype in_dtype, tb_dtype out_dtype, const void* s, const void* w0, const void* u,

@@ -166,7 +166,7 @@ def test_large_stack_bf16(G, layer, M, family):
 # ---------------------------------------------------------------------------
 
 
-@pytest.mark.parametrize("rank", [256, 0])
+@pytest.mark.parametrize("rank", [256, 128, 0])
 @pytest.mark.parametrize("family", gen.FAMILIES)
 def test_reconstruct_large(rank, family):
     for layer in _parity_layers(6):
@@ -263,7 +263,9 @@ def test_forward_split_rounds(shape):
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("shape", [(17, 40, 4), (130, 264, 12), (64, 512, 256), (33, 72, 0), (1, 8, 3), (1, 8, 8),
                                    (130, 264, 24), (300, 520, 72), (257, 1032, 136), (128, 128, 64), (384, 8, 512),
-                                   (130, 264, 200), (300, 520, 256), (257, 1032, 248), (1, 8, 256), (2100, 2104, 256)],
+                                   (130, 264, 200), (300, 520, 256), (257, 1032, 248), (1, 8, 256), (2100, 2104, 256),
+                                   (4500, 4104, 64), (4500, 4104, 128), (4500, 4104, 192), (3000, 2056, 8),
+                                   (2100, 4104, 136)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_reconstruct_edge_shapes(shape, dtype):
     O, I, R = shape
@@ -324,7 +326,7 @@ def test_frobenius_closed_forms():
 @pytest.mark.parametrize("bundle", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("shape", [(17, 40, 4), (130, 264, 12), (64, 512, 256), (33, 72, 0), (1, 8, 3), (300, 520, 72),
                                    (257, 1032, 136), (129, 136, 256), (2100, 2104, 64), (1000, 1000, 0), (1000, 1000, 200),
-                                   (2100, 2104, 256), (4500, 1024, 248)],
+                                   (2100, 2104, 256), (4500, 1024, 248), (4500, 4104, 64), (2100, 4104, 136)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_reconstruction_error_small(shape, bundle):
     O, I, R = shape
@@ -349,7 +351,7 @@ def test_reconstruction_error_small(shape, bundle):
     assert int(ws[-8192:].count_nonzero().item()) == 0
 
 
-@pytest.mark.parametrize("rank", [256, 0])
+@pytest.mark.parametrize("rank", [256, 64, 0])
 @pytest.mark.parametrize("family", gen.FAMILIES)
 def test_reconstruction_error_large(rank, family):
     # 60-layer shapes: equals rebuilding in fp32 and then measuring, for every band's first layer.
