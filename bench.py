@@ -77,6 +77,9 @@ def parse():
     ap.add_argument("--rank", type=int, default=None, help="rank of the bundles (reconstruct60 only)")
     ap.add_argument("--fused", action="store_true",
                     help="reconstruct60: measure the error without writing the rebuilt weight (tb_reconstruction_error)")
+    ap.add_argument("--materialised", action="store_true",
+                    help="forward stacks: rebuild every layer's weight once in bf16 (outside the timed region) and "
+                         "time the dense projections of the materialise-once mode (tb_dense_forward semantics)")
     ap.add_argument("--replicas", type=int, default=None,
                     help="rotating pool of input replicas (default: enough for >= 1 GiB when the stack is small)")
     ap.add_argument("--no-graph", action="store_true", help="skip the captured-graph leg")
@@ -111,6 +114,11 @@ def copy_calibration():
 def call_bytes(M, O, I, R, e=2):
     """Forward: W0, U, V and s once, x in and y out."""
     return e * (O * I + R * (O + I) + O + M * (I + O))
+
+
+def dense_call_bytes(M, O, I, e=2):
+    """Materialise-once forward: the whole weight once, x in and y out."""
+    return e * (O * I + M * (I + O))
 
 
 def call_flops(M, O, I, R):
@@ -328,26 +336,45 @@ def bench_forward(args, torch, np, tb, gen):
                 bundles[(l, fam)] = gen.device_bundle(torch, wl["seed"], fam, shapes, l, band_of[l], R, with_w0=False)
             xs[(l, fam)] = gen.device_activations(torch, wl["seed"], fam, shapes, l, M)
 
+    # Materialise-once mode: W = diag(s) W0 + U V^T per layer, rebuilt once in
+    # bf16; each call is then a dense projection (no scale, rank 0).
+    dense = None
+    if args.materialised:
+        dense = {}
+        for l in range(L):
+            for fam in gen.FAMILIES:
+                bd = bundles[(l, fam)]
+                dense[(l, fam)] = tb.reconstruct_weight(bd["s"], W0[(band_of[l], fam)], bd["U"] if R else None,
+                                                        bd["V"] if R else None, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+
     def nbytes(t):
         return 0 if t is None else t.numel() * t.element_size()
 
-    distinct = sum(nbytes(t) for t in W0.values()) + sum(nbytes(v) for bd in bundles.values() for v in bd.values())
+    if dense is not None:
+        distinct = sum(nbytes(t) for t in dense.values())
+    else:
+        distinct = sum(nbytes(t) for t in W0.values()) + sum(nbytes(v) for bd in bundles.values() for v in bd.values())
     replicas = args.replicas
     if replicas is None:
         replicas = 1 if distinct >= 2 * CACHE_BYTES else math.ceil(COLD_POOL_BYTES / distinct)
     # Replica r > 0 holds copies of every weight tensor at addresses of its own; x is shared.
-    pools = [(W0, bundles)]
+    pools = [(W0, bundles, dense)]
     for _ in range(1, replicas):
-        pools.append(({k: t.clone() for k, t in W0.items()},
-                      {k: {n: (None if t is None else t.clone()) for n, t in bd.items()} for k, bd in bundles.items()}))
+        if dense is not None:
+            pools.append((W0, bundles, {k: t.clone() for k, t in dense.items()}))
+        else:
+            pools.append(({k: t.clone() for k, t in W0.items()},
+                          {k: {n: (None if t is None else t.clone()) for n, t in bd.items()} for k, bd in bundles.items()},
+                          None))
 
     ys = {fam: torch.empty((M, shapes[fam][0]), dtype=torch.bfloat16, device=dev) for fam in gen.FAMILIES}
     # Projections that take the same layer input go in one grouped call.
     groups = [[f] for f in gen.FAMILIES] if args.no_group else GROUPS
     ws_need = []
     for grp in groups:
-        dims = (tb.Projection * len(grp))(*[tb.Projection(None, None, None, None, None, None, *shapes[f], R)
-                                            for f in grp])
+        dims = (tb.Projection * len(grp))(*[tb.Projection(None, None, None, None, None, None, *shapes[f],
+                                                          0 if dense is not None else R) for f in grp])
         nb = ctypes.c_size_t(0)
         assert tb.lib.tb_linear_forward_group_workspace_size(len(grp), dims, M, tb.TB_BF16, ctypes.byref(nb)) == 0
         ws_need.append(nb.value)
@@ -360,7 +387,7 @@ def bench_forward(args, torch, np, tb, gen):
 
     def build_calls(stream_handle, pool):
         """Prepared argument tuples: the timed loop only crosses the C ABI."""
-        W0p, bundlesp = pool
+        W0p, bundlesp, densep = pool
         stream = ctypes.c_void_p(stream_handle)
         calls = []   # (layer, families, function, argument tuple)
         for l in range(L):
@@ -368,14 +395,18 @@ def bench_forward(args, torch, np, tb, gen):
                 members = []
                 for fam in grp:
                     bd = bundlesp[(l, fam)]
-                    members.append((xs[(l, fam)], bd["s"], W0p[(band_of[l], fam)], bd["U"] if R else None,
-                                    bd["V"] if R else None, ys[fam]))
+                    if dense is not None:
+                        members.append((xs[(l, fam)], None, densep[(l, fam)], None, None, ys[fam]))
+                    else:
+                        members.append((xs[(l, fam)], bd["s"], W0p[(band_of[l], fam)], bd["U"] if R else None,
+                                        bd["V"] if R else None, ys[fam]))
                 if len(grp) == 1:
                     x, s_, w0, u, v, y = members[0]
                     O, I = shapes[grp[0]]
-                    argv = (x.data_ptr(), s_.data_ptr(), w0.data_ptr(), u.data_ptr() if R else None,
-                            v.data_ptr() if R else None, y.data_ptr(), M, O, I, R, tb.TB_BF16, ws.data_ptr(),
-                            ws.numel(), stream)
+                    Rc = R if dense is None else 0
+                    argv = (x.data_ptr(), None if s_ is None else s_.data_ptr(), w0.data_ptr(),
+                            u.data_ptr() if Rc else None, v.data_ptr() if Rc else None, y.data_ptr(), M, O, I, Rc,
+                            tb.TB_BF16, ws.data_ptr(), ws.numel(), stream)
                     calls.append((l, grp, fwd, argv))
                 else:
                     arr = tb.projection_array(members)   # the tuple keeps the array alive
@@ -407,10 +438,12 @@ def bench_forward(args, torch, np, tb, gen):
     calls = pool_calls[0]
 
     def grp_bytes(grp):
+        if dense is not None:
+            return sum(dense_call_bytes(M, *shapes[f]) for f in grp)
         return sum(call_bytes(M, *shapes[f], R) for f in grp)
 
     def grp_flops(grp):
-        return sum(call_flops(M, *shapes[f], R) for f in grp)
+        return sum(call_flops(M, *shapes[f], 0 if dense is not None else R) for f in grp)
 
     step_bytes = sum(grp_bytes(c[1]) for c in calls)
     step_flops = sum(grp_flops(c[1]) for c in calls)
@@ -473,10 +506,11 @@ def bench_forward(args, torch, np, tb, gen):
     roof["calls_per_step"] = len(calls)
     roof["avg_launch_us"] = round(float(per_call_ms.mean()) * 1e3, 2)
     roof["algorithmic_per_launch"] = round(per_launch, 1)
-    roof["traffic"] = counter_traffic(kernel, f"{args.workload}_M{M}_G{G}") if replicas == 1 else None
+    roof["traffic"] = (counter_traffic(kernel, f"{args.workload}_M{M}_G{G}")
+                       if replicas == 1 and dense is None else None)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and dense is None:
         cpu = cpu_baseline_forward(args, wl, shapes, calls, bundles, W0, xs, band_of, decode)
 
     line = {
@@ -493,7 +527,9 @@ def bench_forward(args, torch, np, tb, gen):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {L}-layer stack, 7 projections per layer, rank {R}, "
-                               f"G={G} bands, {M} tokens",
+                               f"G={G} bands, {M} tokens"
+                               + (", materialised once (dense bf16 weights)" if dense is not None else ""),
+                   "materialised": dense is not None,
                    "layers": L, "projections_per_step": L * len(gen.FAMILIES),
                    "grouping": "+".join(",".join(f.split("_")[0] for f in g) for g in groups),
                    "rank": R, "bands": G, "tokens": M,

@@ -93,7 +93,7 @@ tb_status tb_linear_forward_workspace_size(int64_t m, int64_t out_dim, int64_t i
  * (the caller selects it with tb_band_index).
  *
  *   x  [m, in_dim]        activations              (dtype)
- *   s  [out_dim]          row scale                (dtype)
+ *   s  [out_dim]          row scale                (dtype; NULL: every row's scale is 1)
  *   w0 [out_dim, in_dim]  shared block             (dtype)
  *   u  [out_dim, rank]    left factor              (dtype; NULL allowed iff rank == 0)
  *   v  [in_dim, rank]     right factor             (dtype; NULL allowed iff rank == 0)
@@ -118,6 +118,21 @@ tb_status tb_linear_forward_workspace_size(int64_t m, int64_t out_dim, int64_t i
 tb_status tb_linear_forward(const void *x, const void *s, const void *w0, const void *u, const void *v,
                             void *y, int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
                             tb_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * tb_dense_forward -- y = x . W^T for a weight held whole: the
+ * materialise-once serving mode, where W = tb_reconstruct_weight(s, W0, U, V)
+ * is formed once in the operand type ("Banded sharing", "Set G for serving":
+ * the serve command that precomputes the weight outside the model graph;
+ * "Quality": that path costs nothing measurable) and each call then streams
+ * W alone.  It is tb_linear_forward with s = NULL (unit scale), rank 0:
+ * the same kernels, workspace (tb_linear_forward_workspace_size with rank
+ * 0), arithmetic, determinism, limits and errors.
+ *
+ *   x [m, in_dim], w [out_dim, in_dim], y [m, out_dim], all dtype, device.
+ */
+tb_status tb_dense_forward(const void *x, const void *w, void *y, int64_t m, int64_t out_dim, int64_t in_dim,
+                           tb_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * One projection of a group: the arguments of tb_linear_forward that may

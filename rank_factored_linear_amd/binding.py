@@ -24,7 +24,7 @@ WORKSPACE_CONTROL_BYTES = MAX_GROUP * 65536
 FROBENIUS_WORKSPACE_BYTES = 65536
 
 EXPORTED = (
-    "tb_band_index", "tb_linear_forward_workspace_size", "tb_linear_forward",
+    "tb_band_index", "tb_linear_forward_workspace_size", "tb_linear_forward", "tb_dense_forward",
     "tb_linear_forward_group_workspace_size", "tb_linear_forward_group",
     "tb_reconstruct_weight", "tb_rel_frobenius_error", "tb_reconstruction_error", "tb_status_string", "tb_last_error",
 )
@@ -51,6 +51,7 @@ def _load() -> ctypes.CDLL:
     lib.tb_band_index.argtypes = [c_i32, c_i32, c_i32, ctypes.POINTER(c_i32)]
     lib.tb_linear_forward_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_i64, ctypes.c_int, ctypes.POINTER(c_sz)]
     lib.tb_linear_forward.argtypes = [c_p, c_p, c_p, c_p, c_p, c_p, c_i64, c_i64, c_i64, c_i64, ctypes.c_int, c_p, c_sz, c_p]
+    lib.tb_dense_forward.argtypes = [c_p, c_p, c_p, c_i64, c_i64, c_i64, ctypes.c_int, c_p, c_sz, c_p]
     lib.tb_linear_forward_group_workspace_size.argtypes = [c_i32, ctypes.POINTER(Projection), c_i64, ctypes.c_int,
                                                            ctypes.POINTER(c_sz)]
     lib.tb_linear_forward_group.argtypes = [c_i32, ctypes.POINTER(Projection), c_i64, ctypes.c_int, c_p, c_sz, c_p]
@@ -150,10 +151,10 @@ def linear_forward_workspace_size(m: int, out_dim: int, in_dim: int, rank: int, 
     return out.value
 
 
-def linear_forward(x: torch.Tensor, s: torch.Tensor, W0: torch.Tensor, U: torch.Tensor | None,
+def linear_forward(x: torch.Tensor, s: torch.Tensor | None, W0: torch.Tensor, U: torch.Tensor | None,
                    V: torch.Tensor | None, out: torch.Tensor | None = None,
                    workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """y = s * (x @ W0.T) + (x @ V) @ U.T on the GPU, via tb_linear_forward."""
+    """y = s * (x @ W0.T) + (x @ V) @ U.T on the GPU, via tb_linear_forward (s None: unit scale)."""
     m, in_dim = x.shape
     out_dim = W0.shape[0]
     rank = 0 if U is None else U.shape[1]
@@ -164,7 +165,7 @@ def linear_forward(x: torch.Tensor, s: torch.Tensor, W0: torch.Tensor, U: torch.
     for t in (s, W0, U, V):
         if t is not None and t.dtype != x.dtype:
             raise TBError(TB_ERR_INVALID_ARGUMENT, "all inputs must share one dtype")
-    if tuple(W0.shape) != (out_dim, in_dim) or tuple(s.shape) != (out_dim,):
+    if tuple(W0.shape) != (out_dim, in_dim) or (s is not None and tuple(s.shape) != (out_dim,)):
         raise TBError(TB_ERR_INVALID_ARGUMENT, "W0 must be [out, in] and s [out]")
     if rank and (tuple(U.shape) != (out_dim, rank) or tuple(V.shape) != (in_dim, rank)):
         raise TBError(TB_ERR_INVALID_ARGUMENT, "U must be [out, rank] and V [in, rank]")
@@ -174,6 +175,25 @@ def linear_forward(x: torch.Tensor, s: torch.Tensor, W0: torch.Tensor, U: torch.
     ws = workspace if workspace is not None else workspace_for(need)
     _check(lib.tb_linear_forward(_ptr(x), _ptr(s), _ptr(W0), _ptr(U), _ptr(V), _ptr(out), m, out_dim, in_dim, rank,
                                  dt, _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return out
+
+
+def dense_forward(x: torch.Tensor, W: torch.Tensor, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y = x @ W.T on the GPU, via tb_dense_forward (a weight materialised once, e.g. by reconstruct_weight)."""
+    m, in_dim = x.shape
+    out_dim = W.shape[0]
+    _need_cuda(x, W, out)
+    if W.dtype != x.dtype:
+        raise TBError(TB_ERR_INVALID_ARGUMENT, "x and W must share one dtype")
+    if tuple(W.shape) != (out_dim, in_dim):
+        raise TBError(TB_ERR_INVALID_ARGUMENT, "W must be [out, in]")
+    if out is None:
+        out = torch.empty((m, out_dim), dtype=x.dtype, device=x.device)
+    need = linear_forward_workspace_size(m, out_dim, in_dim, 0, x.dtype)
+    ws = workspace if workspace is not None else workspace_for(need)
+    _check(lib.tb_dense_forward(_ptr(x), _ptr(W), _ptr(out), m, out_dim, in_dim, _dtype_code(x.dtype), _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream()))
     return out
 
 

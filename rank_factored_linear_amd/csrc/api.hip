@@ -119,7 +119,7 @@ tb_status check_projection(const void* x, const void* s, const void* w0, const v
   if (!valid_dtype(dtype)) return fail(TB_ERR_INVALID_ARGUMENT, "unknown dtype %d", int(dtype));
   tb_status st = check_dims(m, out_dim, in_dim, rank);
   if (st != TB_OK) return st;
-  if (!x || !s || !w0 || !y) return fail(TB_ERR_INVALID_ARGUMENT, "x, s, w0 and y must be non-NULL");
+  if (!x || !w0 || !y) return fail(TB_ERR_INVALID_ARGUMENT, "x, w0 and y must be non-NULL");
   if (rank > 0 && (!u || !v)) return fail(TB_ERR_INVALID_ARGUMENT, "u and v must be non-NULL when rank > 0");
   if (!aligned16(x) || !aligned16(w0) || (rank > 0 && (!aligned16(u) || !aligned16(v))))
     return fail(TB_ERR_UNSUPPORTED, "x, w0, u and v must be 16-byte aligned");
@@ -184,6 +184,13 @@ tb_status tb_linear_forward(const void* x, const void* s, const void* w0, const 
   unsigned* ctrl = static_cast<unsigned*>(workspace);
   return forward_one(x, s, w0, u, v, y, m, out_dim, in_dim, rank, dtype, ctrl, static_cast<char*>(workspace) + kControlBytes,
                      ctrl + 2, cus, static_cast<hipStream_t>(stream));
+}
+
+tb_status tb_dense_forward(const void* x, const void* w, void* y, int64_t m, int64_t out_dim, int64_t in_dim,
+                           tb_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!w) return fail(TB_ERR_INVALID_ARGUMENT, "w must be non-NULL");
+  return tb_linear_forward(x, nullptr, w, nullptr, nullptr, y, m, out_dim, in_dim, 0, dtype, workspace, workspace_bytes,
+                           stream);
 }
 
 tb_status tb_linear_forward_group_workspace_size(int32_t n, const tb_projection* projs, int64_t m, tb_dtype dtype,

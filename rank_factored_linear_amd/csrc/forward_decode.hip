@@ -372,9 +372,9 @@ __device__ void stream_rows(const DecodeArgs& a, int b, uint8_t* smem) {
   float* sbuf = reinterpret_cast<float*>(smem + kWaves * 4 * kWave * 16);
   float* res = sbuf + 16 * TILES;
 
-  // The row scale, fetched now and used after the stream.
+  // The row scale, fetched now and used after the stream (no s: unit scale).
   const E* S_ = static_cast<const E*>(a.s);
-  const float s_mine = tid < nrows ? to_f32<E>(S_[r0 + tid]) : 0.f;
+  const float s_mine = tid < nrows ? (S_ ? to_f32<E>(S_[r0 + tid]) : 1.f) : 0.f;
 
   // Byte offsets, from the block's first row, of the row of each tile this
   // lane loads, clamped into the block (rows past it are computed on

@@ -164,11 +164,11 @@ __global__ __launch_bounds__(kThreads) void forward_gemm_kernel(GemmArgs a) {
     __syncthreads();
   }
 
-  // Epilogue: scale output column o by s[o], add T . U^T, round once.
+  // Epilogue: scale output column o by s[o] (no s: unit scale), add T . U^T, round once.
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int o = n0 + wn * 64 + j * 16 + lr;
-    const float sc = o < a.O ? bf16_to_f32(a.s[o].bits) : 0.f;
+    const float sc = o < a.O ? (a.s ? bf16_to_f32(a.s[o].bits) : 1.f) : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i][j] *= sc;
   }
@@ -517,7 +517,7 @@ __device__ __forceinline__ void finish_tile(const Args& a, int m0, int n0, f32x1
 #pragma unroll
   for (int j = 0; j < TJ; ++j) {
     const int n = n0 + wn * (BN / WN) + j * 32 + lr;
-    const float sc = n < a.O ? bf16_to_f32(a.s[n].bits) : 0.f;
+    const float sc = n < a.O ? (a.s ? bf16_to_f32(a.s[n].bits) : 1.f) : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i][j] *= sc;
   }

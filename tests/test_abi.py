@@ -103,13 +103,29 @@ def _fwd(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(m=0), 1), (dict(o=0), 1), (dict(i=0), 1), (dict(r=-1), 1), (dict(dt=7), 1),
-    (dict(x=None), 1), (dict(s=None), 1), (dict(w0=None), 1), (dict(y=None), 1), (dict(ws=None), 1),
+    (dict(x=None), 1), (dict(s=None, w0=None), 1), (dict(w0=None), 1), (dict(y=None), 1), (dict(ws=None), 1),
     (dict(u=None), 1), (dict(v=None), 1),
     (dict(i=60), 2), (dict(x=FAKE + 8), 2), (dict(w0=FAKE + 4), 2), (dict(u=FAKE + 2), 2),
     (dict(s=FAKE + 1), 2), (dict(y=FAKE + 1), 2), (dict(ws=FAKE + 16), 2), (dict(m=1 << 31), 2),
 ])
 def test_forward_rejects_before_launch(kw, status):
     assert _fwd(**kw) == status
+    assert lib.tb_last_error().decode()
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, None, FAKE, 8, 64, 64, 1), 1),          # w
+    ((None, FAKE, FAKE, 8, 64, 64, 1), 1),          # x
+    ((FAKE, FAKE, None, 8, 64, 64, 1), 1),          # y
+    ((FAKE, FAKE, FAKE, 0, 64, 64, 1), 1),          # m
+    ((FAKE, FAKE, FAKE, 8, 64, 60, 1), 2),          # in_dim % 8
+    ((FAKE, FAKE + 4, FAKE, 8, 64, 64, 1), 2),      # w alignment
+    ((FAKE, FAKE, FAKE, 8, 64, 64, 9), 1),          # dtype
+])
+def test_dense_forward_rejects_before_launch(args, status):
+    x, w, y, m, o, i, dt = args
+    assert lib.tb_dense_forward(x, w, y, m, o, i, dt, FAKE, 1 << 20, None) == status
+    assert lib.tb_dense_forward(FAKE, FAKE, FAKE, 8, 64, 64, 1, None, 1 << 20, None) == 1   # workspace
     assert lib.tb_last_error().decode()
 
 

@@ -319,6 +319,53 @@ def test_frobenius_closed_forms():
 
 
 # ---------------------------------------------------------------------------
+# Materialise-once mode: the weight rebuilt once, then tb_dense_forward
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(1, 2048, 5376), (16, 8192, 5376), (64, 2100, 2104), (65, 136, 264), (300, 1000, 1032),
+                                   (4096, 5376, 2048)], ids=lambda s: "x".join(map(str, s)))
+def test_dense_forward(shape, dtype):
+    M, O, I = shape
+    _say(f"dense forward {shape} {dtype}")
+    x, _, W, _, _ = _rand_case(M, O, I, 0, dtype, seed=M + O + 3 * I)
+    y = tb.dense_forward(x, W)
+    tsel = torch.from_numpy(sample_rows(M, 64, seed=M)).to(DEV)
+    want = oracle.forward_dense(exact(x.index_select(0, tsel)), exact(W))
+    assert oracle.relative_frobenius_error(want, exact(y.index_select(0, tsel))) <= tol_for(dtype)
+    # No scale is the unit scale: the rank-0 projection with s = 1, bit for bit.
+    y1 = tb.linear_forward(x, torch.ones(O, dtype=dtype, device=DEV), W, None, None)
+    y0 = tb.linear_forward(x, None, W, None, None)
+    torch.cuda.synchronize()
+    ib = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(y.view(ib), y1.view(ib)) and torch.equal(y.view(ib), y0.view(ib))
+
+
+@pytest.mark.parametrize("M", [1, 16, 64, 300, 4096])
+def test_materialise_once_matches_the_fused_projection(M):
+    # The 60-layer q projection at rank 256: rebuild W in bf16 once, then y = x . W^T.
+    O, I = gen.SHAPES_60["q_proj"]
+    _say(f"materialise once M={M}")
+    x, s, W0, U, V = _rand_case(M, O, I, 256, torch.bfloat16, seed=11 + M)
+    W = tb.reconstruct_weight(s, W0, U, V, out_dtype=torch.bfloat16)
+    y_dense = tb.dense_forward(x, W)
+    y_fused = tb.linear_forward(x, s, W0, U, V)
+    tsel = torch.from_numpy(sample_rows(M, 32, seed=M)).to(DEV)
+    osel = torch.from_numpy(sample_rows(O, 512, seed=M + 1)).to(DEV)
+    xs = exact(x.index_select(0, tsel))
+    pick = lambda y: exact(y.index_select(0, tsel).index_select(1, osel))
+    want = oracle.forward(xs, exact(s.index_select(0, osel)), exact(W0.index_select(0, osel)),
+                          exact(U.index_select(0, osel)), exact(V))
+    # Both against the exact projection: the materialised weight adds one bf16 rounding per entry.
+    assert oracle.relative_frobenius_error(want, pick(y_fused)) <= BF16_TOL
+    assert oracle.relative_frobenius_error(want, pick(y_dense)) <= BF16_TOL
+    # The dense call against the exact product with the stored (rounded) weight.
+    want_w = oracle.forward_dense(xs, exact(W.index_select(0, osel)))
+    assert oracle.relative_frobenius_error(want_w, pick(y_dense)) <= BF16_TOL
+
+
+# ---------------------------------------------------------------------------
 # Reconstruction error without the rebuilt weight (tb_reconstruction_error)
 # ---------------------------------------------------------------------------
 
