@@ -18,6 +18,8 @@ from .theta_bundle import (  # noqa: F401
     shared_block,
     row_scale,
     truncated_factors,
+    orthonormal_basis,
+    randomized_factors,
     decompose,
     decomposition_error,
 )

@@ -20,6 +20,8 @@ float64 NumPy so that a reader can check it against the pages by eye.  Sources
   band's matrices, s is the per-row least-squares fit against W0, and the
   residual weight - diag(s) W0 is cut to the requested rank by a truncated SVD
   whose singular values are absorbed into U; rank 0 means no delta.
+  The randomized SVD the same section names for large matrices (Halko et
+  al., 2009) is randomized_factors, for a caller-drawn probe.
 * "Quality" (attnquant docs), section "Reconstruction error": the relative
   Frobenius error of the rebuilt weight against the true weight, averaged over
   layers and projection families.
@@ -233,6 +235,52 @@ def truncated_factors(residual: np.ndarray, rank: int) -> tuple[np.ndarray, np.n
         return np.zeros((out_dim, 0)), np.zeros((in_dim, 0))
     P, sigma, Qt = np.linalg.svd(residual, full_matrices=False)
     U = P[:, :rank] * sigma[:rank][None, :]
+    V = Qt[:rank, :].T
+    return U, V
+
+
+def orthonormal_basis(Y: np.ndarray) -> np.ndarray:
+    """Orthonormal basis of the columns of Y (reduced QR, a library step)."""
+    return np.linalg.qr(np.asarray(Y, dtype=np.float64), mode="reduced")[0]
+
+
+def randomized_factors(residual: np.ndarray, rank: int, omega: np.ndarray, power_iters: int) -> tuple[np.ndarray, np.ndarray]:
+    """U [out, rank], V [in, rank] by the randomized SVD the page names for large
+    matrices ("The theta bundle", "Low-rank residual": Halko, Martinsson and
+    Tropp, 2009): a randomized range finder with power iterations, then the
+    exact SVD of the small projected matrix.
+
+    omega [in, k] is the random probe, k = rank + oversampling, drawn by the
+    caller so that every implementation can be run on the same draw.
+      1. Q = orthonormal basis of residual . omega  (k columns).
+      2. power_iters times: Q' = basis of residual^T . Q, then
+         Q = basis of residual . Q'.  Re-orthonormalising at every half step
+         keeps the weaker directions that plain powers would round away.
+      3. B = Q^T . residual (k x in), B = P diag(sigma) Qt (exact SVD).
+      4. U = Q . P[:, :rank] . diag(sigma[:rank]), V = Qt[:rank]^T: U absorbs the
+         singular values, as in truncated_factors.
+    Readings (the page states neither): the oversampling and the number of
+    power iterations are parameters; the GPU bundle path uses k = rank + 16
+    and two power iterations.  With k >= min(out, in), or a residual of rank
+    <= k, the probe covers the whole column space and the result is the exact
+    truncated SVD.
+    """
+    R = np.asarray(residual, dtype=np.float64)
+    omega = np.asarray(omega, dtype=np.float64)
+    out_dim, in_dim = R.shape
+    if omega.ndim != 2 or omega.shape[0] != in_dim or omega.shape[1] < rank:
+        raise ValueError("omega must be [in_dim, k] with k >= rank")
+    if rank < 0 or rank > min(out_dim, in_dim) or power_iters < 0:
+        raise ValueError("rank or power_iters out of range")
+    if rank == 0:
+        return np.zeros((out_dim, 0)), np.zeros((in_dim, 0))
+    Q = orthonormal_basis(R @ omega)
+    for _ in range(power_iters):
+        Qp = orthonormal_basis(R.T @ Q)
+        Q = orthonormal_basis(R @ Qp)
+    B = Q.T @ R
+    P, sigma, Qt = np.linalg.svd(B, full_matrices=False)
+    U = Q @ (P[:, :rank] * sigma[:rank][None, :])
     V = Qt[:rank, :].T
     return U, V
 

@@ -135,6 +135,68 @@ def check_truncated_factors(impl) -> None:
         assert np.sum((Rm - U @ V.T) ** 2) == pytest.approx(np.sum(sigma[k:] ** 2), abs=1e-11)
 
 
+def check_randomized_factors(impl) -> None:
+    r = np.random.default_rng(11)
+    # 1. A probe as wide as the input space covers the column space: the exact
+    #    truncated SVD (Eckart-Young optimum of a known spectrum) at every rank.
+    O, I = 12, 8
+    P = np.linalg.qr(r.normal(size=(O, I)))[0]
+    Q = np.linalg.qr(r.normal(size=(I, I)))[0]
+    sigma = np.array([9.0, 7.0, 5.0, 3.0, 2.0, 1.0, 0.5, 0.25])
+    Rm = P @ np.diag(sigma) @ Q.T
+    om = r.normal(size=(I, I))
+    for q in (0, 1):
+        for k in range(0, I + 1):
+            U, V = impl.randomized_factors(Rm, k, om, q)
+            assert U.shape == (O, k) and V.shape == (I, k)
+            best = P[:, :k] @ np.diag(sigma[:k]) @ Q[:, :k].T
+            assert np.max(np.abs(U @ V.T - best)) <= 1e-12
+            assert np.allclose(np.linalg.norm(U, axis=0), sigma[:k], rtol=1e-12, atol=0)
+    # 2. A residual of exact rank k = 16 over eight decades: the k-column probe
+    #    spans its range, so every rank <= 16 is exact, with or without power
+    #    iterations (without oversampling, or without re-orthonormalising the
+    #    power iterations, the weak directions are lost).
+    O, I, k = 60, 40, 16
+    P = np.linalg.qr(r.normal(size=(O, k)))[0]
+    Q = np.linalg.qr(r.normal(size=(I, k)))[0]
+    sigma = 10.0 ** (-np.arange(k) / 2)
+    Rm = P @ np.diag(sigma) @ Q.T
+    om = r.normal(size=(I, k))
+    for q in (0, 3):
+        for rank in (1, 8, 12, 16):
+            U, V = impl.randomized_factors(Rm, rank, om, q)
+            best = P[:, :rank] @ np.diag(sigma[:rank]) @ Q[:, :rank].T
+            assert np.max(np.abs(U @ V.T - best)) <= 1e-12, (q, rank)
+    # 3. Halko et al. (2009), Theorem 10.5: E||A - Q Q^T A||_F^2 <= (1 + r/(p-1)) tail^2
+    #    for target rank r and oversampling p; cutting Q Q^T A to rank r adds at
+    #    most tail^2 (orthogonal pieces; B = Q^T A has singular values <= A's).
+    #    Averaged over 20 probes, with 20% for the sample mean.  Every draw is at
+    #    least the Eckart-Young optimum.
+    O, I, rank, p = 200, 150, 10, 6
+    P = np.linalg.qr(r.normal(size=(O, I)))[0]
+    Q = np.linalg.qr(r.normal(size=(I, I)))[0]
+    sigma = 1.0 / np.arange(1, I + 1)
+    Rm = P @ np.diag(sigma) @ Q.T
+    tail2 = float(np.sum(sigma[rank:] ** 2))
+    errs = []
+    for d in range(20):
+        U, V = impl.randomized_factors(Rm, rank, np.random.default_rng(100 + d).normal(size=(I, rank + p)), 0)
+        e2 = float(np.sum((Rm - U @ V.T) ** 2))
+        assert e2 >= tail2 * (1 - 1e-12)
+        errs.append(e2)
+        # 5. U absorbs the singular values: V orthonormal, U's columns orthogonal
+        #    with non-increasing norms.
+        assert np.allclose(V.T @ V, np.eye(rank), atol=1e-12)
+        G = U.T @ U
+        assert np.max(np.abs(G - np.diag(np.diag(G)))) <= 1e-12 * G[0, 0]
+        assert np.all(np.diff(np.diag(G)) <= 1e-15)
+    assert np.mean(errs) <= 1.2 * (2 + rank / (p - 1)) * tail2
+    # 4. Power iterations close the gap to the optimum.
+    for d in range(5):
+        U, V = impl.randomized_factors(Rm, rank, np.random.default_rng(200 + d).normal(size=(I, rank + p)), 6)
+        assert np.sqrt(np.sum((Rm - U @ V.T) ** 2)) <= 1.0001 * np.sqrt(tail2)
+
+
 def check_decompose(impl) -> None:
     r = np.random.default_rng(10)
     # Passthrough (G = L): W0 = W, s = 1 exactly, delta 0 and error exactly 0.
@@ -165,7 +227,7 @@ def check_decompose(impl) -> None:
 
 
 ALL_CHECKS = [check_band_map, check_forward, check_reconstruct, check_frobenius,
-              check_row_scale, check_truncated_factors, check_decompose]
+              check_row_scale, check_truncated_factors, check_randomized_factors, check_decompose]
 
 
 # ---------------------------------------------------------------------------
@@ -358,6 +420,31 @@ def _frob_squared(a, b):
     return float(num / np.sum(a * a)) if num else 0.0
 
 
+def _rand_v_absorbs(residual, rank, omega, power_iters):
+    U, V = tb.randomized_factors(residual, rank, omega, power_iters)
+    norms = np.linalg.norm(U, axis=0)
+    return U / np.where(norms > 0, norms, 1.0)[None, :], V * norms[None, :]
+
+
+def _rand_sigma_dropped(residual, rank, omega, power_iters):
+    U, V = tb.randomized_factors(residual, rank, omega, power_iters)
+    norms = np.linalg.norm(U, axis=0)
+    return U / np.where(norms > 0, norms, 1.0)[None, :], V
+
+
+def _rand_no_oversampling(residual, rank, omega, power_iters):
+    return tb.randomized_factors(residual, rank, omega[:, :rank], power_iters)
+
+
+def _rand_plain_powers(residual, rank, omega, power_iters):
+    Y = residual @ omega
+    for _ in range(power_iters):
+        Y = residual @ (residual.T @ Y)
+    Q = np.linalg.qr(Y)[0]
+    P, sg, Qt = np.linalg.svd(Q.T @ residual, full_matrices=False)
+    return Q @ (P[:, :rank] * sg[:rank][None, :]), Qt[:rank].T
+
+
 MUTANTS = [
     ("band remainder to the last bands", check_band_map,
      dict(band_sizes=_remainder_last_sizes, band_map=_remainder_last_map,
@@ -367,6 +454,12 @@ MUTANTS = [
     ("s ratio swapped", check_row_scale, dict(row_scale=_swapped_row_scale)),
     ("s normalised by the weight row", check_row_scale, dict(row_scale=_input_dot_row_scale)),
     ("V absorbs the singular values", check_truncated_factors, dict(truncated_factors=_v_absorbs)),
+    ("randomized: V absorbs the singular values", check_randomized_factors, dict(randomized_factors=_rand_v_absorbs)),
+    ("randomized: singular values dropped", check_randomized_factors, dict(randomized_factors=_rand_sigma_dropped)),
+    ("randomized: probe without oversampling", check_randomized_factors,
+     dict(randomized_factors=_rand_no_oversampling)),
+    ("randomized: power iterations not re-orthonormalised", check_randomized_factors,
+     dict(randomized_factors=_rand_plain_powers)),
     ("delta factor reversed", check_forward, dict(forward=_wrong_transposed_forward)),
     ("scale applied to the delta too", check_forward, dict(forward=_scale_after_delta)),
     ("reconstruct with a permuted V", check_reconstruct, dict(reconstruct_weight=_recon_transposed)),
