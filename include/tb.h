@@ -60,6 +60,12 @@ typedef enum tb_dtype {
 /* Fixed workspace size of tb_rel_frobenius_error. */
 #define TB_FROBENIUS_WORKSPACE_BYTES 65536
 
+/* Most layers one band may hold in tb_shared_block. */
+#define TB_MAX_BAND_LAYERS 128
+
+/* Widest random probe (k = rank + oversampling) of tb_lowrank_factors. */
+#define TB_MAX_PROBE 512
+
 /*
  * tb_band_index -- band of one layer ("Banded sharing", "How layers map to
  * bands").  The num_layers layers are split into num_bands contiguous bands
@@ -231,6 +237,65 @@ tb_status tb_reconstruction_error(const void *s, const void *w0, const void *u, 
                                   int64_t out_dim, int64_t in_dim, int64_t rank, tb_dtype bundle_dtype,
                                   tb_dtype original_dtype, double *result_device, void *workspace,
                                   size_t workspace_bytes, void *stream);
+
+/*
+ * Analytic decomposition of one projection family ("The theta bundle",
+ * section "Analytic decomposition"), in three steps per band and layer.
+ * Outputs are fp32; the caller casts them for the forward path.
+ *
+ * tb_shared_block -- W0 = the mean of the band's weight matrices (Shared
+ * block): summed in layer order in fp64, divided by n, rounded once to fp32.
+ *   weights: HOST array of n DEVICE pointers, each [out_dim, in_dim] of
+ *   weight_dtype; 1 <= n <= TB_MAX_BAND_LAYERS.  w0_out: device fp32
+ *   [out_dim, in_dim].  Errors: TB_ERR_INVALID_ARGUMENT, TB_ERR_HIP.
+ */
+tb_status tb_shared_block(const void *const *weights, int32_t n, int64_t out_dim, int64_t in_dim,
+                          tb_dtype weight_dtype, float *w0_out, void *stream);
+
+/*
+ * tb_row_scale -- s[o] = <weight[o], W0[o]> / <W0[o], W0[o]>, the per-row
+ * least-squares fit of the weight against its band's block (Per-row scale);
+ * 0 for a zero row of W0 (the minimum-norm solution).  fp64 sums in a fixed
+ * order, one rounding to fp32.
+ *   weight [out_dim, in_dim] (weight_dtype), w0 fp32 [out_dim, in_dim],
+ *   s_out fp32 [out_dim], all device.  Errors: TB_ERR_INVALID_ARGUMENT, TB_ERR_HIP.
+ */
+tb_status tb_row_scale(const void *weight, const float *w0, int64_t out_dim, int64_t in_dim, tb_dtype weight_dtype,
+                       float *s_out, void *stream);
+
+/*
+ * tb_lowrank_factors_workspace_size -- bytes of workspace tb_lowrank_factors
+ * needs (host-only query; it reads the device's compute-unit count once).
+ */
+tb_status tb_lowrank_factors_workspace_size(int64_t out_dim, int64_t in_dim, int64_t rank, int64_t k,
+                                            size_t *bytes_out);
+
+/*
+ * tb_lowrank_factors -- U [out_dim, rank], V [in_dim, rank] with U V^T the
+ * rank-r cut of the residual E = weight - diag(s) W0 by the randomized SVD
+ * the section names for large matrices (Low-rank residual; Halko,
+ * Martinsson and Tropp, 2009).  U absorbs the singular values (columns by
+ * decreasing singular value); a singular value at or below 1e-7 of the
+ * largest counts as zero and gives zero columns in U and V.
+ *   omega [in_dim, k] fp32: the random probe, drawn by the caller
+ *   (k = rank + oversampling); power_iters re-orthonormalised power
+ *   iterations (0..16).  The probe's range is found as in the method: Y = E
+ *   omega, orthonormalised; each power iteration maps through E^T and E,
+ *   orthonormalising each time; then the SVD of the k x in_dim projection.
+ *   With k = min(out_dim, in_dim) the result is the exact truncated SVD up to
+ *   rounding.  E is formed in fp32 (one rounding per entry), products in fp32,
+ *   Gram matrices, Cholesky factors and the eigen-decomposition in fp64.
+ *   weight (weight_dtype), w0, s, omega, u_out, v_out: device, 4-byte aligned.
+ *   0 <= rank <= k <= min(out_dim, in_dim, TB_MAX_PROBE); out_dim * in_dim <
+ *   2^31.  rank 0 writes nothing.  workspace: at least
+ *   tb_lowrank_factors_workspace_size() bytes, 256-byte aligned, no initial
+ *   contents.  Calls that may run at the same time must not share it.
+ *   Errors: TB_ERR_INVALID_ARGUMENT, TB_ERR_UNSUPPORTED, TB_ERR_HIP (also for
+ *   a failing rocBLAS call).
+ */
+tb_status tb_lowrank_factors(const void *weight, const float *w0, const float *s, int64_t out_dim, int64_t in_dim,
+                             int64_t rank, tb_dtype weight_dtype, const float *omega, int64_t k, int32_t power_iters,
+                             float *u_out, float *v_out, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static description of a status code. */
 const char *tb_status_string(tb_status status);

@@ -26,8 +26,12 @@ FROBENIUS_WORKSPACE_BYTES = 65536
 EXPORTED = (
     "tb_band_index", "tb_linear_forward_workspace_size", "tb_linear_forward", "tb_dense_forward",
     "tb_linear_forward_group_workspace_size", "tb_linear_forward_group",
-    "tb_reconstruct_weight", "tb_rel_frobenius_error", "tb_reconstruction_error", "tb_status_string", "tb_last_error",
+    "tb_reconstruct_weight", "tb_rel_frobenius_error", "tb_reconstruction_error",
+    "tb_shared_block", "tb_row_scale", "tb_lowrank_factors_workspace_size", "tb_lowrank_factors",
+    "tb_status_string", "tb_last_error",
 )
+MAX_BAND_LAYERS = 128
+MAX_PROBE = 512
 
 
 class Projection(ctypes.Structure):
@@ -59,6 +63,11 @@ def _load() -> ctypes.CDLL:
     lib.tb_rel_frobenius_error.argtypes = [c_p, c_p, c_i64, c_i64, ctypes.c_int, c_p, c_p, c_sz, c_p]
     lib.tb_reconstruction_error.argtypes = [c_p, c_p, c_p, c_p, c_p, c_i64, c_i64, c_i64, ctypes.c_int, ctypes.c_int,
                                             c_p, c_p, c_sz, c_p]
+    lib.tb_shared_block.argtypes = [ctypes.POINTER(c_p), c_i32, c_i64, c_i64, ctypes.c_int, c_p, c_p]
+    lib.tb_row_scale.argtypes = [c_p, c_p, c_i64, c_i64, ctypes.c_int, c_p, c_p]
+    lib.tb_lowrank_factors_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_i64, ctypes.POINTER(c_sz)]
+    lib.tb_lowrank_factors.argtypes = [c_p, c_p, c_p, c_i64, c_i64, c_i64, ctypes.c_int, c_p, c_i64, c_i32, c_p, c_p,
+                                       c_p, c_sz, c_p]
     lib.tb_status_string.argtypes = [ctypes.c_int]
     lib.tb_status_string.restype = ctypes.c_char_p
     lib.tb_last_error.argtypes = []
@@ -302,3 +311,94 @@ def reconstruction_error(original: torch.Tensor, s: torch.Tensor, W0: torch.Tens
                                        _dtype_code(W0.dtype), _dtype_code(original.dtype), _ptr(out), _ptr(ws),
                                        ws.numel(), _stream()))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Analytic decomposition
+# ---------------------------------------------------------------------------
+
+
+def shared_block(weights, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Mean of a band's weight matrices (fp32), via tb_shared_block."""
+    n = len(weights)
+    if not 1 <= n <= MAX_BAND_LAYERS:
+        raise TBError(TB_ERR_INVALID_ARGUMENT, f"a band holds 1..{MAX_BAND_LAYERS} layers")
+    out_dim, in_dim = weights[0].shape
+    for w in weights:
+        _need_cuda(w)
+        if tuple(w.shape) != (out_dim, in_dim) or w.dtype != weights[0].dtype:
+            raise TBError(TB_ERR_INVALID_ARGUMENT, "a band's matrices share one shape and dtype")
+    if out is None:
+        out = torch.empty((out_dim, in_dim), dtype=torch.float32, device=weights[0].device)
+    ptrs = (ctypes.c_void_p * n)(*[w.data_ptr() for w in weights])
+    _check(lib.tb_shared_block(ptrs, n, out_dim, in_dim, _dtype_code(weights[0].dtype), _ptr(out), _stream()))
+    return out
+
+
+def row_scale(weight: torch.Tensor, W0: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Per-row least-squares scale of weight against W0 (fp32 [out]), via tb_row_scale."""
+    _need_cuda(weight, W0)
+    if W0.dtype != torch.float32 or W0.shape != weight.shape:
+        raise TBError(TB_ERR_INVALID_ARGUMENT, "W0 must be fp32 with the weight's shape")
+    if out is None:
+        out = torch.empty(weight.shape[0], dtype=torch.float32, device=weight.device)
+    _check(lib.tb_row_scale(_ptr(weight), _ptr(W0), weight.shape[0], weight.shape[1], _dtype_code(weight.dtype),
+                            _ptr(out), _stream()))
+    return out
+
+
+def lowrank_factors_workspace_size(out_dim: int, in_dim: int, rank: int, k: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.tb_lowrank_factors_workspace_size(out_dim, in_dim, rank, k, ctypes.byref(out)))
+    return out.value
+
+
+def lowrank_factors(weight: torch.Tensor, W0: torch.Tensor, s: torch.Tensor, rank: int, omega: torch.Tensor,
+                    power_iters: int, workspace: torch.Tensor | None = None):
+    """U [out, rank], V [in, rank] (fp32) of weight - diag(s) W0 by the randomized SVD with probe omega [in, k],
+    via tb_lowrank_factors."""
+    _need_cuda(weight, W0, s, omega)
+    out_dim, in_dim = weight.shape
+    k = omega.shape[1]
+    for t in (W0, s, omega):
+        if t.dtype != torch.float32:
+            raise TBError(TB_ERR_INVALID_ARGUMENT, "W0, s and omega must be fp32")
+    if omega.shape[0] != in_dim:
+        raise TBError(TB_ERR_INVALID_ARGUMENT, "omega must be [in, k]")
+    U = torch.zeros((out_dim, rank), dtype=torch.float32, device=weight.device)
+    V = torch.zeros((in_dim, rank), dtype=torch.float32, device=weight.device)
+    need = lowrank_factors_workspace_size(out_dim, in_dim, rank, k)
+    ws = workspace if workspace is not None and workspace.numel() >= need else \
+        torch.empty(need, dtype=torch.uint8, device=weight.device)
+    _check(lib.tb_lowrank_factors(_ptr(weight), _ptr(W0), _ptr(s), out_dim, in_dim, rank, _dtype_code(weight.dtype),
+                                  _ptr(omega), k, power_iters, _ptr(U) if rank else None, _ptr(V) if rank else None,
+                                  _ptr(ws), ws.numel(), _stream()))
+    return U, V
+
+
+def decompose(weights, num_bands: int, rank: int, oversampling: int = 16, power_iters: int = 2, seed: int = 0) -> dict:
+    """One family's theta bundle on the GPU: per band the shared block, per layer the row scale and the low-rank
+    factors (randomized SVD, k = min(rank + oversampling, out, in), probe drawn from a seeded normal generator).
+    Returns {"W0": [per band], "band": [per layer], "s", "U", "V": [per layer]} of fp32 device tensors."""
+    L = len(weights)
+    bands = [band_index(L, num_bands, l) for l in range(L)]
+    out_dim, in_dim = weights[0].shape
+    W0 = [shared_block([weights[l] for l in range(L) if bands[l] == b]) for b in range(num_bands)]
+    k = min(rank + oversampling, out_dim, in_dim, MAX_PROBE)
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    res = {"W0": W0, "band": bands, "s": [], "U": [], "V": []}
+    ws = torch.empty(lowrank_factors_workspace_size(out_dim, in_dim, rank, k), dtype=torch.uint8,
+                     device=weights[0].device) if rank else None
+    for l in range(L):
+        s = row_scale(weights[l], W0[bands[l]])
+        res["s"].append(s)
+        if rank:
+            omega = torch.randn((in_dim, k), generator=gen, dtype=torch.float32).to(weights[l].device)
+            U, V = lowrank_factors(weights[l], W0[bands[l]], s, rank, omega, power_iters, ws)
+        else:
+            U = torch.zeros((out_dim, 0), dtype=torch.float32, device=weights[l].device)
+            V = torch.zeros((in_dim, 0), dtype=torch.float32, device=weights[l].device)
+        res["U"].append(U)
+        res["V"].append(V)
+    return res
+

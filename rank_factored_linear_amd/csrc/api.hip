@@ -328,6 +328,89 @@ tb_status tb_rel_frobenius_error(const void* original, const void* reconstructed
   return ok();
 }
 
+tb_status tb_shared_block(const void* const* weights, int32_t n, int64_t out_dim, int64_t in_dim, tb_dtype weight_dtype,
+                          float* w0_out, void* stream) {
+  if (!valid_dtype(weight_dtype)) return fail(TB_ERR_INVALID_ARGUMENT, "unknown dtype %d", int(weight_dtype));
+  if (!weights || !w0_out) return fail(TB_ERR_INVALID_ARGUMENT, "weights and w0_out must be non-NULL");
+  if (n < 1 || n > TB_MAX_BAND_LAYERS) return fail(TB_ERR_INVALID_ARGUMENT, "n %d outside [1, %d]", n, TB_MAX_BAND_LAYERS);
+  if (out_dim < 1 || in_dim < 1) return fail(TB_ERR_INVALID_ARGUMENT, "out_dim and in_dim must be >= 1");
+  if (out_dim > kMaxDim / in_dim) return fail(TB_ERR_UNSUPPORTED, "matrix too large");
+  for (int j = 0; j < n; ++j) {
+    if (!weights[j]) return fail(TB_ERR_INVALID_ARGUMENT, "weights[%d] is NULL", j);
+    if (!aligned_to(weights[j], esize(weight_dtype))) return fail(TB_ERR_INVALID_ARGUMENT, "weights[%d] misaligned", j);
+  }
+  if (!aligned_to(w0_out, 4)) return fail(TB_ERR_INVALID_ARGUMENT, "w0_out misaligned");
+  hipError_t e = launch_shared_block(weight_dtype, weights, n, out_dim * in_dim, w0_out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launching the shared block");
+  return ok();
+}
+
+tb_status tb_row_scale(const void* weight, const float* w0, int64_t out_dim, int64_t in_dim, tb_dtype weight_dtype,
+                       float* s_out, void* stream) {
+  if (!valid_dtype(weight_dtype)) return fail(TB_ERR_INVALID_ARGUMENT, "unknown dtype %d", int(weight_dtype));
+  if (!weight || !w0 || !s_out) return fail(TB_ERR_INVALID_ARGUMENT, "weight, w0 and s_out must be non-NULL");
+  if (out_dim < 1 || in_dim < 1) return fail(TB_ERR_INVALID_ARGUMENT, "out_dim and in_dim must be >= 1");
+  if (out_dim > kMaxDim / in_dim || out_dim > 0x7fffffff) return fail(TB_ERR_UNSUPPORTED, "matrix too large");
+  if (!aligned_to(weight, esize(weight_dtype)) || !aligned_to(w0, 4) || !aligned_to(s_out, 4))
+    return fail(TB_ERR_INVALID_ARGUMENT, "weight, w0 or s_out misaligned");
+  hipError_t e = launch_row_scale(weight_dtype, weight, w0, out_dim, in_dim, s_out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "launching the row scale");
+  return ok();
+}
+
+namespace {
+
+tb_status check_lowrank_dims(int64_t out_dim, int64_t in_dim, int64_t rank, int64_t k) {
+  if (out_dim < 1 || in_dim < 1) return fail(TB_ERR_INVALID_ARGUMENT, "out_dim and in_dim must be >= 1");
+  if (rank < 0 || k < rank) return fail(TB_ERR_INVALID_ARGUMENT, "need 0 <= rank <= k (got %lld, %lld)", (long long)rank,
+                                        (long long)k);
+  if (k < 1 || k > out_dim || k > in_dim)
+    return fail(TB_ERR_INVALID_ARGUMENT, "k %lld outside [1, min(out_dim, in_dim)]", (long long)k);
+  if (k > TB_MAX_PROBE) return fail(TB_ERR_UNSUPPORTED, "k %lld above %d", (long long)k, TB_MAX_PROBE);
+  if (out_dim >= (int64_t(1) << 31) / in_dim) return fail(TB_ERR_UNSUPPORTED, "out_dim * in_dim must stay below 2^31");
+  return TB_OK;
+}
+
+}  // namespace
+
+tb_status tb_lowrank_factors_workspace_size(int64_t out_dim, int64_t in_dim, int64_t rank, int64_t k, size_t* bytes_out) {
+  if (!bytes_out) return fail(TB_ERR_INVALID_ARGUMENT, "bytes_out is NULL");
+  tb_status st = check_lowrank_dims(out_dim, in_dim, rank, k);
+  if (st != TB_OK) return st;
+  int cus = 0;
+  if (int e = device_cu_count(&cus)) return hip_fail(hipError_t(e), "querying the compute-unit count");
+  *bytes_out = lowrank_workspace_bytes(out_dim, in_dim, k, rank, cus);
+  return ok();
+}
+
+tb_status tb_lowrank_factors(const void* weight, const float* w0, const float* s, int64_t out_dim, int64_t in_dim,
+                             int64_t rank, tb_dtype weight_dtype, const float* omega, int64_t k, int32_t power_iters,
+                             float* u_out, float* v_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(weight_dtype)) return fail(TB_ERR_INVALID_ARGUMENT, "unknown dtype %d", int(weight_dtype));
+  tb_status st = check_lowrank_dims(out_dim, in_dim, rank, k);
+  if (st != TB_OK) return st;
+  if (power_iters < 0 || power_iters > 16) return fail(TB_ERR_INVALID_ARGUMENT, "power_iters %d outside [0, 16]", power_iters);
+  if (!weight || !w0 || !s || !omega || !workspace)
+    return fail(TB_ERR_INVALID_ARGUMENT, "weight, w0, s, omega and workspace must be non-NULL");
+  if (rank > 0 && (!u_out || !v_out)) return fail(TB_ERR_INVALID_ARGUMENT, "u_out and v_out must be non-NULL");
+  if (!aligned_to(weight, esize(weight_dtype)) || !aligned_to(w0, 4) || !aligned_to(s, 4) || !aligned_to(omega, 4) ||
+      !aligned_to(u_out, 4) || !aligned_to(v_out, 4))
+    return fail(TB_ERR_INVALID_ARGUMENT, "a pointer is misaligned");
+  if (!aligned_to(workspace, 256)) return fail(TB_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  int cus = 0;
+  if (int e = device_cu_count(&cus)) return hip_fail(hipError_t(e), "querying the compute-unit count");
+  const size_t need = lowrank_workspace_bytes(out_dim, in_dim, k, rank, cus);
+  if (workspace_bytes < need)
+    return fail(TB_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is below the %zu needed", workspace_bytes, need);
+  if (rank == 0) return ok();
+  const char* what = "";
+  const int e = launch_lowrank_factors(weight_dtype, weight, w0, s, out_dim, in_dim, rank, omega, k, power_iters, u_out,
+                                       v_out, workspace, cus, static_cast<hipStream_t>(stream), &what);
+  if (e == -1) return fail(TB_ERR_HIP, "%s failed", what);
+  if (e != 0) return hip_fail(hipError_t(e), what);
+  return ok();
+}
+
 const char* tb_status_string(tb_status status) {
   switch (status) {
     case TB_OK: return "ok";

@@ -104,4 +104,15 @@ hipError_t launch_reconstruction_error(tb_dtype bundle_dtype, tb_dtype orig_dtyp
 hipError_t launch_frobenius(tb_dtype dtype, const void* a, const void* b, int64_t n, double* result,
                             void* workspace, int cus, hipStream_t stream);
 
+// ---- analytic decomposition (decompose.hip) ---------------------------------
+hipError_t launch_shared_block(tb_dtype dtype, const void* const* weights, int n, int64_t count, float* out,
+                               hipStream_t stream);
+hipError_t launch_row_scale(tb_dtype dtype, const void* weight, const float* w0, int64_t out_dim, int64_t in_dim,
+                            float* s, hipStream_t stream);
+size_t lowrank_workspace_bytes(int64_t out_dim, int64_t in_dim, int64_t k, int64_t rank, int cus);
+// 0 on success; a hipError_t code, or -1 for a rocBLAS failure, with *what naming the step.
+int launch_lowrank_factors(tb_dtype dtype, const void* weight, const float* w0, const float* s, int64_t out_dim,
+                           int64_t in_dim, int64_t rank, const float* omega, int64_t k, int power_iters, float* u_out,
+                           float* v_out, void* workspace, int cus, hipStream_t stream, const char** what);
+
 }  // namespace tb

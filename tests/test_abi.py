@@ -129,6 +129,45 @@ def test_dense_forward_rejects_before_launch(args, status):
     assert lib.tb_last_error().decode()
 
 
+def test_decomposition_rejects_before_launch():
+    ptrs = (ctypes.c_void_p * 3)(FAKE, FAKE, FAKE)
+    sb = lib.tb_shared_block
+    assert sb(None, 3, 64, 64, 1, FAKE, None) == 1
+    assert sb(ptrs, 0, 64, 64, 1, FAKE, None) == 1
+    assert sb(ptrs, binding.MAX_BAND_LAYERS + 1, 64, 64, 1, FAKE, None) == 1
+    assert sb(ptrs, 3, 0, 64, 1, FAKE, None) == 1
+    assert sb(ptrs, 3, 64, 64, 5, FAKE, None) == 1
+    assert sb(ptrs, 3, 64, 64, 1, None, None) == 1
+    bad = (ctypes.c_void_p * 3)(FAKE, None, FAKE)
+    assert sb(bad, 3, 64, 64, 1, FAKE, None) == 1
+    rs = lib.tb_row_scale
+    assert rs(None, FAKE, 64, 64, 1, FAKE, None) == 1
+    assert rs(FAKE, FAKE, 64, 0, 1, FAKE, None) == 1
+    assert rs(FAKE, FAKE + 2, 64, 64, 1, FAKE, None) == 1
+    lf = lib.tb_lowrank_factors
+    args = [FAKE, FAKE, FAKE, 64, 48, 8, 1, FAKE, 16, 2, FAKE, FAKE, FAKE, 1 << 30, None]
+
+    def call(**changes):
+        a = list(args)
+        for k, v in changes.items():
+            a[int(k[1:])] = v
+        return lf(*a)
+    assert call(a5=17) == 1                    # rank > k
+    assert call(a8=49) == 1                    # k > in_dim
+    assert call(a5=-1) == 1
+    assert call(a9=17) == 1                    # power iterations
+    assert call(a0=None) == 1 and call(a7=None) == 1 and call(a12=None) == 1
+    assert call(a10=None) == 1                 # u_out with rank > 0
+    assert call(a2=FAKE + 2) == 1              # misaligned s
+    assert call(a6=4) == 1                     # dtype
+    assert call(a3=1 << 20, a4=1 << 12) == 2   # out * in >= 2^31
+    assert call(a3=600, a4=600, a8=513, a5=8) == 2   # k above the widest probe
+    out = ctypes.c_size_t(0)
+    assert lib.tb_lowrank_factors_workspace_size(64, 48, 20, 16, ctypes.byref(out)) == 1
+    assert lib.tb_lowrank_factors_workspace_size(64, 48, 8, 16, None) == 1
+    assert lib.tb_last_error().decode()
+
+
 def test_reconstruct_rejects_before_launch():
     f = lib.tb_reconstruct_weight
     assert f(None, FAKE, FAKE, FAKE, FAKE, 64, 64, 8, 1, 0, None) == 1
