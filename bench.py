@@ -63,7 +63,10 @@ WORKLOADS = {
     "banded26": dict(layers=26, shapes="SHAPES_26", rank=128, bands=4, tokens=4, seed=3),
     "passthrough26": dict(layers=26, shapes="SHAPES_26", rank=0, bands=26, tokens=8, seed=2),
     "reconstruct60": dict(layers=60, shapes="SHAPES_60", rank=256, bands=6, tokens=0, seed=5),
+    "decompose26": dict(layers=26, shapes="SHAPES_26", rank=128, bands=4, tokens=0, seed=6),
+    "decompose60": dict(layers=60, shapes="SHAPES_60", rank=256, bands=6, tokens=0, seed=7),
 }
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32
 
 
 def parse():
@@ -80,6 +83,8 @@ def parse():
     ap.add_argument("--materialised", action="store_true",
                     help="forward stacks: rebuild every layer's weight once in bf16 (outside the timed region) and "
                          "time the dense projections of the materialise-once mode (tb_dense_forward semantics)")
+    ap.add_argument("--streams", type=int, default=4, help="decompose*: side streams the layers' factorisations use")
+    ap.add_argument("--power-iters", type=int, default=2, help="decompose*: power iterations of the randomized SVD")
     ap.add_argument("--replicas", type=int, default=None,
                     help="rotating pool of input replicas (default: enough for >= 1 GiB when the stack is small)")
     ap.add_argument("--no-graph", action="store_true", help="skip the captured-graph leg")
@@ -791,6 +796,80 @@ def cpu_baseline_reconstruct(args, shapes, bundles, W0, originals, band_of, L, R
             "extrapolated_step_s": round(step / rate, 1), **_host_info()}
 
 
+def bench_decompose(args, torch, np, tb, gen):
+    """The analytic decomposition of a whole stack on the GPU: every family's band means, row scales and
+    randomized low-rank factors (tb_shared_block, tb_row_scale, tb_lowrank_factors through decompose())."""
+    wl = dict(WORKLOADS[args.workload])
+    if args.bands is not None:
+        wl["bands"] = args.bands
+    if args.rank is not None:
+        wl["rank"] = args.rank
+    L, R, G, seed = wl["layers"], wl["rank"], wl["bands"], wl["seed"]
+    shapes = getattr(gen, wl["shapes"])
+    t_setup = time.time()
+    band_of = [tb.band_index(L, G, l) for l in range(L)]
+    # Originals: a_l * W0_band + N(0, 2e-3) in bf16 (the reconstruction workload's recipe).
+    originals = {}
+    for fam in gen.FAMILIES:
+        blocks = {b: gen.device_w0(torch, seed, fam, shapes, b) for b in set(band_of)}
+        originals[fam] = [gen.device_original(torch, blocks[band_of[l]], seed, fam, l).to(torch.bfloat16)
+                          for l in range(L)]
+        del blocks
+    torch.cuda.synchronize()
+    t_setup = time.time() - t_setup
+    orig_bytes = sum(t.numel() * t.element_size() for ts in originals.values() for t in ts)
+    ks = {fam: min(R + 16, *shapes[fam]) for fam in gen.FAMILIES}
+    q = args.power_iters
+    gemm_flops = L * sum(2 * (2 + 2 * q) * shapes[f][0] * shapes[f][1] * ks[f] +
+                         2 * (shapes[f][0] + shapes[f][1]) * ks[f] * R for f in gen.FAMILIES)
+
+    def step(keep=False):
+        out = {}
+        for fam in gen.FAMILIES:
+            out[fam] = tb.decompose(originals[fam], G, R, power_iters=q, seed=seed, streams=args.streams)
+            if not keep:
+                out[fam] = None
+        return out
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms, per_step = timed_steps(torch, lambda k: step(), args.steps)
+    # Quality of the last decomposition (the (G, rank) sweep's figure for this synthetic stack).
+    bundles = step(keep=True)
+    errs = []
+    for fam in gen.FAMILIES:
+        b = bundles[fam]
+        for l in range(L):
+            e = tb.reconstruction_error(originals[fam][l], b["s"][l], b["W0"][b["band"][l]], b["U"][l], b["V"][l])
+            errs.append(float(e.item()))
+    del bundles
+    value = orig_bytes / (ms * 1e-3) / 1e9
+    achieved = gemm_flops / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "analytic decomposition of a stack (band means, row scales, randomized low-rank factors)",
+        "value": round(value, 2),
+        "unit": "GB/s of original bf16 weights",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32 (f64 solvers)",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {L}-layer stack, 7 families, G={G}, rank {R}, "
+                               f"k = rank + 16, {q} power iterations, {args.streams} streams",
+                   "layers": L, "bands": G, "rank": R, "power_iters": q, "streams": args.streams,
+                   "matrices": L * len(gen.FAMILIES), "original_bytes": orig_bytes,
+                   "matrices_per_s": round(L * len(gen.FAMILIES) / (ms * 1e-3), 2),
+                   "mean_rel_error": float(np.mean(errs)), "parallelism": "single-gpu"},
+        "trials": spread(per_step),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / FP32_PEAK_TFLOPS, 4), "traffic": None,
+                     "note": "fp32 GEMM work of the randomized SVDs over the whole step; the fp64 "
+                             "single-workgroup solvers (Jacobi, Cholesky) take most of the rest"},
+        "cpu_baseline": None,
+    }
+    print(f"# setup {t_setup:.1f}s  step {ms:.1f} ms", file=sys.stderr)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -810,6 +889,8 @@ def main():
     torch.cuda.set_device(0)
     if args.workload == "reconstruct60":
         bench_reconstruct(args, torch, np, tb, gen)
+    elif args.workload.startswith("decompose"):
+        bench_decompose(args, torch, np, tb, gen)
     else:
         bench_forward(args, torch, np, tb, gen)
 

@@ -376,29 +376,44 @@ def lowrank_factors(weight: torch.Tensor, W0: torch.Tensor, s: torch.Tensor, ran
     return U, V
 
 
-def decompose(weights, num_bands: int, rank: int, oversampling: int = 16, power_iters: int = 2, seed: int = 0) -> dict:
+def decompose(weights, num_bands: int, rank: int, oversampling: int = 16, power_iters: int = 2, seed: int = 0,
+              streams: int = 4) -> dict:
     """One family's theta bundle on the GPU: per band the shared block, per layer the row scale and the low-rank
-    factors (randomized SVD, k = min(rank + oversampling, out, in), probe drawn from a seeded normal generator).
-    Returns {"W0": [per band], "band": [per layer], "s", "U", "V": [per layer]} of fp32 device tensors."""
+    factors (randomized SVD, k = min(rank + oversampling, out, in), probe drawn from a seeded normal generator in
+    layer order).  The layers' factorisations run on `streams` side streams (default priority, each with its own
+    workspace), so that the single-workgroup solver kernels of several layers overlap; the current stream waits
+    for all of them.  Returns {"W0": [per band], "band": [per layer], "s", "U", "V": [per layer]} of fp32
+    device tensors."""
     L = len(weights)
     bands = [band_index(L, num_bands, l) for l in range(L)]
     out_dim, in_dim = weights[0].shape
+    dev = weights[0].device
     W0 = [shared_block([weights[l] for l in range(L) if bands[l] == b]) for b in range(num_bands)]
+    res = {"W0": W0, "band": bands, "s": [row_scale(weights[l], W0[bands[l]]) for l in range(L)], "U": [], "V": []}
+    if rank == 0:
+        res["U"] = [torch.zeros((out_dim, 0), dtype=torch.float32, device=dev) for _ in range(L)]
+        res["V"] = [torch.zeros((in_dim, 0), dtype=torch.float32, device=dev) for _ in range(L)]
+        return res
     k = min(rank + oversampling, out_dim, in_dim, MAX_PROBE)
     gen = torch.Generator(device="cpu").manual_seed(seed)
-    res = {"W0": W0, "band": bands, "s": [], "U": [], "V": []}
-    ws = torch.empty(lowrank_factors_workspace_size(out_dim, in_dim, rank, k), dtype=torch.uint8,
-                     device=weights[0].device) if rank else None
+    omegas = [torch.randn((in_dim, k), generator=gen, dtype=torch.float32).to(dev) for _ in range(L)]
+    main = torch.cuda.current_stream()
+    side = [torch.cuda.Stream(device=dev) for _ in range(max(1, min(streams, L)))]
+    need = lowrank_factors_workspace_size(out_dim, in_dim, rank, k)
+    wss = [torch.empty(need, dtype=torch.uint8, device=dev) for _ in side]
+    for st, ws in zip(side, wss):
+        st.wait_stream(main)
+        ws.record_stream(st)
     for l in range(L):
-        s = row_scale(weights[l], W0[bands[l]])
-        res["s"].append(s)
-        if rank:
-            omega = torch.randn((in_dim, k), generator=gen, dtype=torch.float32).to(weights[l].device)
-            U, V = lowrank_factors(weights[l], W0[bands[l]], s, rank, omega, power_iters, ws)
-        else:
-            U = torch.zeros((out_dim, 0), dtype=torch.float32, device=weights[l].device)
-            V = torch.zeros((in_dim, 0), dtype=torch.float32, device=weights[l].device)
+        j = l % len(side)
+        with torch.cuda.stream(side[j]):
+            for t in (weights[l], W0[bands[l]], res["s"][l], omegas[l]):
+                t.record_stream(side[j])
+            U, V = lowrank_factors(weights[l], W0[bands[l]], res["s"][l], rank, omegas[l], power_iters, wss[j])
+            U.record_stream(main)
+            V.record_stream(main)
         res["U"].append(U)
         res["V"].append(V)
+    for st in side:
+        main.wait_stream(st)
     return res
-

@@ -12,17 +12,20 @@
 //   Q = basis(E Q'); B^T = E^T Q; the eigen-decomposition of B B^T = P L P^T
 //   gives B = P diag(sigma) Qt with sigma = sqrt(L); U = Q P_r diag(sigma_r),
 //   V = B^T P_r diag(1 / sigma_r).
-// basis() is CholeskyQR2: the fp64 Gram matrix of the columns, a Cholesky
+// basis() is CholeskyQR: the fp64 Gram matrix of the columns, a Cholesky
 // factor R whose pivots at or below 1e-13 of the largest diagonal entry mark
 // directions the columns do not span (their columns of Q are zero), and
-// Q = Y R^-1, twice.  The same span as a Householder QR, so the same U V^T up
-// to rounding.  The large products run as plain fp32 GEMMs (rocBLAS); the
-// Gram matrices, the Cholesky factor and its inverse and the symmetric
-// eigen-decomposition (cyclic Jacobi over a round-robin pair order, fp64) are
-// the kernels below.
+// Q = Y R^-1; one round between power iterations, two (CholeskyQR2) for the
+// final basis.  The same span as a Householder QR, so the same U V^T up to
+// rounding.  The eigenvectors of B B^T are the right singular vectors of its
+// Cholesky factor, found by one-sided Jacobi (fp64, round-robin pair order).
+// The large products and the triangular solves run as plain fp32 rocBLAS
+// calls; the Gram matrices, the Cholesky factor and the Jacobi SVD are the
+// kernels below.
 #include <rocblas/rocblas.h>
 
 #include <mutex>
+#include <vector>
 
 #include "tb_device.h"
 #include "tb_host.h"
@@ -34,9 +37,14 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kSolverThreads = 1024;
+static_assert(TB_MAX_PROBE <= kSolverThreads, "a thread per pair and per column");
 constexpr double kPivotTol = 1e-13;     // Cholesky pivot / largest diagonal entry below which a direction is dropped
 constexpr double kSigmaTol = 1e-14;     // eigenvalue / largest below which a singular value counts as zero
-constexpr double kJacobiTol = 1e-15;    // largest |a_pq| / sqrt(a_pp a_qq) at which a sweep ends the iteration
+// A sweep that sees no |gamma| / sqrt(alpha beta) above kJacobiTol ends the
+// iteration.  The factors leave in fp32, so columns orthogonal to 1e-11 are
+// plenty, and the rounding floor of a length-k fp64 dot product of two
+// orthogonal columns (~k * 1e-16 <= 5e-14) stays well below it.
+constexpr double kJacobiTol = 1e-11;
 constexpr int kMaxSweeps = 40;
 constexpr int kGramTile = 64;
 constexpr int kGramRows = 32;           // rows of the input per LDS stage
@@ -172,19 +180,23 @@ __global__ __launch_bounds__(kThreads) void gram_reduce_kernel(const double* __r
   }
 }
 
-// ---- Cholesky factor and its inverse (one workgroup, fp64) -------------------------
+// ---- Cholesky factor (one workgroup, fp64) ------------------------------------------
 
-// C = R^T R (R upper) with dropped directions: a pivot at or below kPivotTol
-// of the largest diagonal entry of C zeroes its row of R and its column and
-// row of R^-1.  M = R^-1 in fp32 (k x k, row-major).  A and X: k x k scratch.
-__global__ __launch_bounds__(kSolverThreads) void chol_inv_kernel(const double* __restrict__ C, int k,
-                                                                  double* __restrict__ A, double* __restrict__ X,
-                                                                  int* __restrict__ dropped, float* __restrict__ M) {
+// C = R^T R (R upper), right-looking, row j of the trailing matrix staged in
+// LDS.  A pivot at or below kPivotTol of the largest diagonal entry of C
+// drops direction j: row j and column j of R become those of the identity,
+// and dropped[j] = 1 (the caller zeroes column j of the input, so that the
+// triangular solve gives a zero column of Q and leaves the others alone).
+// R32 = R in fp32 (k x k, row-major, zero below the diagonal).  A: k x k scratch.
+__global__ __launch_bounds__(kSolverThreads) void cholesky_kernel(const double* __restrict__ C, int k,
+                                                                  double* __restrict__ A, int* __restrict__ dropped,
+                                                                  float* __restrict__ R32) {
+  __shared__ double s_row[TB_MAX_PROBE];
   __shared__ double s_piv, s_max;
   __shared__ int s_drop;
   const int tid = threadIdx.x;
-  const int64_t kk = int64_t(k) * k;
-  for (int64_t i = tid; i < kk; i += kSolverThreads) A[i] = C[i];
+  const int kk = k * k;
+  for (int i = tid; i < kk; i += kSolverThreads) A[i] = C[i];
   if (tid == 0) {
     double m = 0.0;
     for (int j = 0; j < k; ++j) m = fmax(m, C[size_t(j) * k + j]);
@@ -196,132 +208,172 @@ __global__ __launch_bounds__(kSolverThreads) void chol_inv_kernel(const double* 
       const double d = A[size_t(j) * k + j];
       const bool drop = !(d > kPivotTol * s_max);
       s_drop = drop;
-      s_piv = drop ? 0.0 : sqrt(d);
+      s_piv = drop ? 1.0 : sqrt(d);
       dropped[j] = drop;
-      A[size_t(j) * k + j] = s_piv;
     }
     __syncthreads();
     const double piv = s_piv;
     const bool drop = s_drop;
-    for (int l = j + 1 + tid; l < k; l += kSolverThreads) A[size_t(j) * k + l] = drop ? 0.0 : A[size_t(j) * k + l] / piv;
+    for (int l = j + tid; l < k; l += kSolverThreads) {
+      const double v = l == j ? piv : (drop ? 0.0 : A[size_t(j) * k + l] / piv);
+      s_row[l] = v;
+      A[size_t(j) * k + l] = v;
+    }
     __syncthreads();
     if (!drop) {
       const int n = k - j - 1;
-      for (int idx = tid; idx < n * n; idx += kSolverThreads) {
-        const int l = j + 1 + idx / n, m = j + 1 + idx % n;
-        if (m >= l) A[size_t(l) * k + m] -= A[size_t(j) * k + l] * A[size_t(j) * k + m];
+      // Trailing update of the upper triangle, four independent entries per
+      // thread in flight.
+      constexpr int B = 4;
+      for (int base = tid; base < n * n; base += B * kSolverThreads) {
+        int at[B];
+        double val[B], mul[B];
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+          const int idx = base + u * kSolverThreads;
+          const int l = j + 1 + idx / n, m = j + 1 + idx % n;
+          const bool live = idx < n * n && m >= l;
+          at[u] = live ? l * k + m : -1;
+          val[u] = live ? A[size_t(l) * k + m] : 0.0;
+          mul[u] = live ? s_row[l] * s_row[m] : 0.0;
+        }
+#pragma unroll
+        for (int u = 0; u < B; ++u)
+          if (at[u] >= 0) A[at[u]] = val[u] - mul[u];
       }
     }
     __syncthreads();
   }
-  // X = R^-1 by back substitution, one column per thread (k <= kSolverThreads).
-  if (tid < k) {
-    const int c = tid;
-    for (int i = 0; i < k; ++i) X[size_t(i) * k + c] = 0.0;
-    if (!dropped[c]) {
-      X[size_t(c) * k + c] = 1.0 / A[size_t(c) * k + c];
-      for (int i = c - 1; i >= 0; --i) {
-        if (dropped[i]) continue;
-        double sum = 0.0;
-        for (int m = i + 1; m <= c; ++m) sum += A[size_t(i) * k + m] * X[size_t(m) * k + c];
-        X[size_t(i) * k + c] = -sum / A[size_t(i) * k + i];
-      }
-    }
-    for (int i = 0; i < k; ++i) M[size_t(i) * k + c] = float(X[size_t(i) * k + c]);
+  // R32: the upper triangle of A; a dropped direction's column is the identity's.
+  for (int i = tid; i < kk; i += kSolverThreads) {
+    const int r = i / k, c = i % k;
+    float v = 0.f;
+    if (c >= r && !(dropped[c] && r != c)) v = float(A[i]);
+    R32[i] = v;
   }
 }
 
-// ---- symmetric eigen-decomposition (one workgroup, fp64) -----------------------------
+// Zero the columns of X [n, k] whose direction the Cholesky factor dropped.
+__global__ __launch_bounds__(kThreads) void zero_dropped_kernel(float* __restrict__ X, int64_t n, int k,
+                                                                const int* __restrict__ dropped) {
+  const int64_t total = n * k;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < total; i += int64_t(gridDim.x) * kThreads)
+    if (dropped[i % k]) X[i] = 0.f;
+}
 
-// Cyclic Jacobi: each sweep runs the kk - 1 rounds of the round-robin
-// (circle) order over kk = k rounded up to even, so that every pair (p, q)
-// is rotated once per sweep and the kk / 2 pairs of a round are disjoint and
-// rotate together: rows p, q of A, then columns p, q of A and of V (the
-// rotation J with J_pp = J_qq = c, J_pq = s, J_qp = -s, A <- J^T A J,
-// V <- V J, chosen to zero a_pq).  Ends when a whole sweep saw no
-// |a_pq| / sqrt(a_pp a_qq) above kJacobiTol.  On exit lam holds the
-// eigenvalues (diagonal of A) and perm the columns of V by decreasing
-// eigenvalue (ties by index); sweeps[0] the sweeps taken.
-__global__ __launch_bounds__(kSolverThreads) void jacobi_kernel(double* __restrict__ A, double* __restrict__ V, int k,
+// ---- singular value decomposition of the Cholesky factor (one workgroup, fp64) ---------
+
+// Sum over an aligned group of G lanes.
+template <int G>
+__device__ __forceinline__ double group_sum(double v) {
+#pragma unroll
+  for (int m = G / 2; m > 0; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// B B^T = R^T R (R from cholesky_kernel, its dropped rows taken as zero), so
+// the eigenvectors of B B^T are the right singular vectors of R.  One-sided
+// (Hestenes) Jacobi on the columns of R: each sweep runs the kk - 1 rounds of
+// the round-robin (circle) pair order over kk = k rounded up to even, so that
+// every pair (p, q) meets once per sweep and the pairs of a round are
+// disjoint; a group of G lanes per pair forms alpha = |r_p|^2, beta = |r_q|^2,
+// gamma = r_p . r_q and rotates columns p, q of R and of V (J_pp = J_qq = c,
+// J_pq = s, J_qp = -s, chosen to make the new columns orthogonal).  Columns
+// are stored contiguously (Rc, Vc: column j at j * k), so every access is a
+// whole column.  Ends when a whole sweep saw no |gamma| / sqrt(alpha beta)
+// above kJacobiTol.  On exit lam[j] = |column j of R V|^2 (the eigenvalues),
+// perm the columns by decreasing lam (ties by index), sweeps[0] the sweeps.
+template <int G, int kPer>
+__global__ __launch_bounds__(kSolverThreads) void jacobi_kernel(const double* __restrict__ Rrow,
+                                                                const int* __restrict__ dropped, int k,
+                                                                double* __restrict__ Rc, double* __restrict__ Vc,
                                                                 double* __restrict__ lam, int* __restrict__ perm,
                                                                 int* __restrict__ sweeps) {
-  __shared__ double s_c[kSolverThreads / 2], s_s[kSolverThreads / 2];
-  __shared__ int s_p[kSolverThreads / 2], s_q[kSolverThreads / 2];
-  __shared__ double s_red[kSolverThreads];
-  const int tid = threadIdx.x;
+  constexpr int kWavesJ = kSolverThreads / kWave;
+  constexpr int kGroups = kSolverThreads / G;                // pairs in flight
+  __shared__ double s_red[kWavesJ];
+  __shared__ int s_done;
+  const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
+  const int grp = tid / G, lg = tid % G;
   const int kk = k + (k & 1), P = kk / 2;
-  const int64_t k2 = int64_t(k) * k;
-  for (int64_t i = tid; i < k2; i += kSolverThreads) V[i] = (i / k == i % k) ? 1.0 : 0.0;
+  for (int idx = tid; idx < k * k; idx += kSolverThreads) {
+    const int j = idx / k, i = idx % k;   // column j, row i
+    Rc[idx] = (i <= j && !dropped[i]) ? Rrow[size_t(i) * k + j] : 0.0;
+    Vc[idx] = i == j ? 1.0 : 0.0;
+  }
   __syncthreads();
   int sweep = 0;
   for (; sweep < kMaxSweeps; ++sweep) {
     double off = 0.0;
     for (int t = 0; t < kk - 1; ++t) {
-      if (tid < P) {
-        const auto rot = [&](int x) { return ((x - 1 + t) % (kk - 1)) + 1; };
-        const int a = tid == 0 ? 0 : rot(tid), b = rot(kk - 1 - tid);
+      for (int pr = grp; pr < P; pr += kGroups) {
+        const int a = pr == 0 ? 0 : ((pr - 1 + t) % (kk - 1)) + 1, b = ((kk - 2 - pr + t) % (kk - 1)) + 1;
         const int p = a < b ? a : b, q = a < b ? b : a;
-        double c = 1.0, s = 0.0;
-        if (q < k) {
-          const double apq = A[size_t(p) * k + q], app = A[size_t(p) * k + p], aqq = A[size_t(q) * k + q];
-          const double d = sqrt(fabs(app * aqq));
-          if (d > 0.0) off = fmax(off, fabs(apq) / d);
-          else if (apq != 0.0) off = 1.0;
-          if (apq != 0.0 && fabs(apq) > 1e-18 * d) {
-            const double th = (aqq - app) / (2.0 * apq);
-            const double tt = th == 0.0             ? 1.0
-                              : fabs(th) > 1e150 ? 0.5 / th
-                                                 : copysign(1.0, th) / (fabs(th) + sqrt(th * th + 1.0));
-            c = 1.0 / sqrt(tt * tt + 1.0);
-            s = tt * c;
+        if (q >= k) continue;
+        double* cp = Rc + size_t(p) * k;
+        double* cq = Rc + size_t(q) * k;
+        double* vp = Vc + size_t(p) * k;
+        double* vq = Vc + size_t(q) * k;
+        double xp[kPer], xq[kPer], yp[kPer], yq[kPer];
+        double al = 0.0, be = 0.0, ga = 0.0;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+          const int i = lg + e * G;
+          const bool in = i < k;
+          xp[e] = in ? cp[i] : 0.0;
+          xq[e] = in ? cq[i] : 0.0;
+          yp[e] = in ? vp[i] : 0.0;
+          yq[e] = in ? vq[i] : 0.0;
+        }
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+          al += xp[e] * xp[e];
+          be += xq[e] * xq[e];
+          ga += xp[e] * xq[e];
+        }
+        al = group_sum<G>(al);
+        be = group_sum<G>(be);
+        ga = group_sum<G>(ga);
+        const double d = sqrt(al * be);
+        if (d > 0.0) off = fmax(off, fabs(ga) / d);
+        if (ga == 0.0 || !(fabs(ga) > 1e-16 * d)) continue;
+        const double z = (be - al) / (2.0 * ga);
+        const double tt = z == 0.0            ? 1.0
+                          : fabs(z) > 1e150 ? 0.5 / z
+                                            : copysign(1.0, z) / (fabs(z) + sqrt(z * z + 1.0));
+        const double c = 1.0 / sqrt(tt * tt + 1.0), sn = tt * c;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+          const int i = lg + e * G;
+          if (i < k) {
+            cp[i] = c * xp[e] - sn * xq[e];
+            cq[i] = sn * xp[e] + c * xq[e];
+            vp[i] = c * yp[e] - sn * yq[e];
+            vq[i] = sn * yp[e] + c * yq[e];
           }
         }
-        s_p[tid] = p;
-        s_q[tid] = q;
-        s_c[tid] = c;
-        s_s[tid] = s;
-      }
-      __syncthreads();
-      for (int idx = tid; idx < P * k; idx += kSolverThreads) {   // rows p, q
-        const int pr = idx / k, j = idx % k;
-        const int p = s_p[pr], q = s_q[pr];
-        const double s = s_s[pr];
-        if (q >= k || s == 0.0) continue;
-        const double c = s_c[pr], x = A[size_t(p) * k + j], y = A[size_t(q) * k + j];
-        A[size_t(p) * k + j] = c * x - s * y;
-        A[size_t(q) * k + j] = s * x + c * y;
-      }
-      __syncthreads();
-      for (int idx = tid; idx < k * P; idx += kSolverThreads) {   // columns p, q
-        const int i = idx / P, pr = idx % P;
-        const int p = s_p[pr], q = s_q[pr];
-        const double s = s_s[pr];
-        if (q >= k || s == 0.0) continue;
-        const double c = s_c[pr];
-        double x = A[size_t(i) * k + p], y = A[size_t(i) * k + q];
-        A[size_t(i) * k + p] = c * x - s * y;
-        A[size_t(i) * k + q] = s * x + c * y;
-        x = V[size_t(i) * k + p];
-        y = V[size_t(i) * k + q];
-        V[size_t(i) * k + p] = c * x - s * y;
-        V[size_t(i) * k + q] = s * x + c * y;
       }
       __syncthreads();
     }
-    s_red[tid] = off;
+    if (l == 0) s_red[w] = off;
     __syncthreads();
-    for (int h = kSolverThreads / 2; h > 0; h >>= 1) {
-      if (tid < h) s_red[tid] = fmax(s_red[tid], s_red[tid + h]);
-      __syncthreads();
+    if (tid == 0) {
+      double m = 0.0;
+      for (int i = 0; i < kWavesJ; ++i) m = fmax(m, s_red[i]);
+      s_done = m <= kJacobiTol;
     }
-    const bool done = s_red[0] <= kJacobiTol;
     __syncthreads();
-    if (done) {
+    if (s_done) {
       ++sweep;
       break;
     }
   }
-  for (int j = tid; j < k; j += kSolverThreads) lam[j] = A[size_t(j) * k + j];
+  for (int j = w; j < k; j += kWavesJ) {
+    double n2 = 0.0;
+    for (int i = l; i < k; i += kWave) n2 += Rc[size_t(j) * k + i] * Rc[size_t(j) * k + i];
+    n2 = group_sum<kWave>(n2);
+    if (l == 0) lam[j] = n2;
+  }
   __syncthreads();
   for (int j = tid; j < k; j += kSolverThreads) {
     const double lj = lam[j];
@@ -333,8 +385,9 @@ __global__ __launch_bounds__(kSolverThreads) void jacobi_kernel(double* __restri
 }
 
 // Mu = P_r diag(sigma_r), Mv = P_r diag(1 / sigma_r) (fp32, k x r), sigma_j =
-// sqrt of the j-th largest eigenvalue; a singular value at or below
-// sqrt(kSigmaTol) of the largest counts as zero (zero columns in both).
+// sqrt of the j-th largest eigenvalue, P's columns stored contiguously (Vc);
+// a singular value at or below sqrt(kSigmaTol) of the largest counts as zero
+// (zero columns in both).
 __global__ __launch_bounds__(kThreads) void assemble_kernel(const double* __restrict__ V, const double* __restrict__ lam,
                                                             const int* __restrict__ perm, int k, int r,
                                                             float* __restrict__ Mu, float* __restrict__ Mv) {
@@ -345,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void assemble_kernel(const double* __rest
     const double l = lam[col];
     const bool zero = !(l > kSigmaTol * lmax) || !(lmax > 0.0);
     const double sg = zero ? 0.0 : sqrt(l);
-    const double v = V[size_t(a) * k + col];
+    const double v = V[size_t(col) * k + a];
     Mu[idx] = zero ? 0.f : float(v * sg);
     Mv[idx] = zero ? 0.f : float(v / sg);
   }
@@ -353,9 +406,17 @@ __global__ __launch_bounds__(kThreads) void assemble_kernel(const double* __rest
 
 // ---- host side ------------------------------------------------------------------------
 
+// One rocBLAS handle per (device, stream): a handle's internal workspace
+// (the triangular solve keeps inverted diagonal blocks there) must not be
+// shared by calls that run at the same time on different streams.
 struct Blas {
   std::mutex mu;
-  rocblas_handle h[64] = {};
+  struct Entry {
+    int dev;
+    hipStream_t stream;
+    rocblas_handle h;
+  };
+  std::vector<Entry> handles;
 };
 Blas g_blas;
 
@@ -381,7 +442,7 @@ int gram_splits(int64_t n, int k, int cus) {
 }
 
 struct Layout {
-  size_t e, o1, o2, i1, i2, part, c, a, x, v, m, lam, perm, drop, sweeps, mu, mv, total;
+  size_t e, o1, i1, part, c, a, v, m, lam, perm, drop, sweeps, mu, mv, total;
 };
 
 Layout layout(int64_t O, int64_t I, int64_t k, int64_t r, int cus) {
@@ -396,13 +457,10 @@ Layout layout(int64_t O, int64_t I, int64_t k, int64_t r, int cus) {
   const int splits = gram_splits(nmax, int(k), cus);
   L.e = take(size_t(O) * I * 4);
   L.o1 = take(size_t(O) * k * 4);
-  L.o2 = take(size_t(O) * k * 4);
   L.i1 = take(size_t(I) * k * 4);
-  L.i2 = take(size_t(I) * k * 4);
   L.part = take(size_t(splits) * k * k * 8);
   L.c = take(size_t(k) * k * 8);
   L.a = take(size_t(k) * k * 8);
-  L.x = take(size_t(k) * k * 8);
   L.v = take(size_t(k) * k * 8);
   L.m = take(size_t(k) * k * 4);
   L.lam = take(size_t(k) * 8);
@@ -437,26 +495,34 @@ hipError_t gram(const Run& R, const float* A, int64_t n, double* C) {
   return hipGetLastError();
 }
 
-// X [n, k] <- orthonormal basis of its columns (CholeskyQR2), T [n, k] scratch.
-int orthonormalize(const Run& R, float* X, float* T, int64_t n, const char** what) {
+// X [n, k] <- a basis of its columns by `passes` rounds of CholeskyQR (Gram
+// matrix, Cholesky factor R, X <- X R^-1 by a triangular solve in place).
+// One round leaves the columns well conditioned (enough between power
+// iterations); two make them orthonormal to working precision.
+int orthonormalize(const Run& R, float* X, int64_t n, int passes, const char** what) {
   double* C = reinterpret_cast<double*>(R.ws + R.L.c);
-  float* M = reinterpret_cast<float*>(R.ws + R.L.m);
-  for (int pass = 0; pass < 2; ++pass) {
-    float* src = pass == 0 ? X : T;
-    float* dst = pass == 0 ? T : X;
-    if (hipError_t e = gram(R, src, n, C)) {
+  float* R32 = reinterpret_cast<float*>(R.ws + R.L.m);
+  int* dropped = reinterpret_cast<int*>(R.ws + R.L.drop);
+  for (int pass = 0; pass < passes; ++pass) {
+    if (hipError_t e = gram(R, X, n, C)) {
       *what = "Gram matrix";
       return int(e);
     }
-    hipLaunchKernelGGL(chol_inv_kernel, dim3(1), dim3(kSolverThreads), 0, R.stream, C, R.k,
-                       reinterpret_cast<double*>(R.ws + R.L.a), reinterpret_cast<double*>(R.ws + R.L.x),
-                       reinterpret_cast<int*>(R.ws + R.L.drop), M);
+    hipLaunchKernelGGL(cholesky_kernel, dim3(1), dim3(kSolverThreads), 0, R.stream, C, R.k,
+                       reinterpret_cast<double*>(R.ws + R.L.a), dropped, R32);
+    int64_t blocks = (n * R.k + kThreads - 1) / kThreads;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(zero_dropped_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, R.stream, X, n, R.k, dropped);
     if (hipError_t e = hipGetLastError()) {
       *what = "Cholesky factor";
       return int(e);
     }
-    if (gemm_rm(R.h, false, false, int(n), R.k, R.k, src, R.k, M, R.k, dst, R.k) != rocblas_status_success) {
-      *what = "rocblas_sgemm (basis)";
+    // Row-major X [n, k] is column-major X^T [k, n]; row-major R (upper) is
+    // column-major R^T (lower): solve R^T Z = X^T, Z = (X R^-1)^T.
+    const float one = 1.f;
+    if (rocblas_strsm(R.h, rocblas_side_left, rocblas_fill_lower, rocblas_operation_none, rocblas_diagonal_non_unit, R.k,
+                      int(n), &one, R32, R.k, X, R.k) != rocblas_status_success) {
+      *what = "rocblas_strsm (basis)";
       return -1;
     }
   }
@@ -507,21 +573,24 @@ int launch_lowrank_factors(tb_dtype dtype, const void* weight, const float* w0, 
     return int(hipErrorInvalidDevice);
   }
   std::lock_guard<std::mutex> lock(g_blas.mu);
-  if (!g_blas.h[dev] && rocblas_create_handle(&g_blas.h[dev]) != rocblas_status_success) {
-    g_blas.h[dev] = nullptr;
-    *what = "rocblas_create_handle";
-    return -1;
+  rocblas_handle h = nullptr;
+  for (const auto& e : g_blas.handles)
+    if (e.dev == dev && e.stream == stream) h = e.h;
+  if (!h) {
+    if (rocblas_create_handle(&h) != rocblas_status_success) {
+      *what = "rocblas_create_handle";
+      return -1;
+    }
+    g_blas.handles.push_back({dev, stream, h});
   }
-  Run R{static_cast<char*>(workspace), layout(O, I, k, r, cus), int(k), cus, stream, g_blas.h[dev]};
+  Run R{static_cast<char*>(workspace), layout(O, I, k, r, cus), int(k), cus, stream, h};
   if (rocblas_set_stream(R.h, stream) != rocblas_status_success) {
     *what = "rocblas_set_stream";
     return -1;
   }
   float* E = reinterpret_cast<float*>(R.ws + R.L.e);
   float* O1 = reinterpret_cast<float*>(R.ws + R.L.o1);
-  float* O2 = reinterpret_cast<float*>(R.ws + R.L.o2);
   float* I1 = reinterpret_cast<float*>(R.ws + R.L.i1);
-  float* I2 = reinterpret_cast<float*>(R.ws + R.L.i2);
   const int Oi = int(O), Ii = int(I), ki = int(k), ri = int(r);
 
   {
@@ -546,14 +615,16 @@ int launch_lowrank_factors(tb_dtype dtype, const void* weight, const float* w0, 
   // Range finder.
   if (gemm_rm(R.h, false, false, Oi, ki, Ii, E, Ii, omega, ki, O1, ki) != rocblas_status_success)
     return gemm_fail("rocblas_sgemm (E Omega)");
-  if (int e = orthonormalize(R, O1, O2, O, what)) return e;
+  // Between power iterations one CholeskyQR round keeps the weak directions;
+  // the final basis gets two.
+  if (int e = orthonormalize(R, O1, O, power_iters > 0 ? 1 : 2, what)) return e;
   for (int it = 0; it < power_iters; ++it) {
     if (gemm_rm(R.h, true, false, Ii, ki, Oi, E, Ii, O1, ki, I1, ki) != rocblas_status_success)
       return gemm_fail("rocblas_sgemm (E^T Q)");
-    if (int e = orthonormalize(R, I1, I2, I, what)) return e;
+    if (int e = orthonormalize(R, I1, I, 1, what)) return e;
     if (gemm_rm(R.h, false, false, Oi, ki, Ii, E, Ii, I1, ki, O1, ki) != rocblas_status_success)
       return gemm_fail("rocblas_sgemm (E Q')");
-    if (int e = orthonormalize(R, O1, O2, O, what)) return e;
+    if (int e = orthonormalize(R, O1, O, it + 1 == power_iters ? 2 : 1, what)) return e;
   }
   // B^T = E^T Q, its Gram matrix B B^T and the eigen-decomposition.
   if (gemm_rm(R.h, true, false, Ii, ki, Oi, E, Ii, O1, ki, I1, ki) != rocblas_status_success)
@@ -563,15 +634,28 @@ int launch_lowrank_factors(tb_dtype dtype, const void* weight, const float* w0, 
     *what = "Gram matrix of B";
     return int(e);
   }
+  // Its Cholesky factor, then the SVD of the factor (the eigenvectors of B B^T).
   double* A = reinterpret_cast<double*>(R.ws + R.L.a);
-  if (hipError_t e = hipMemcpyAsync(A, C, size_t(k) * k * 8, hipMemcpyDeviceToDevice, stream)) {
-    *what = "copy";
-    return int(e);
-  }
+  int* dropped = reinterpret_cast<int*>(R.ws + R.L.drop);
+  hipLaunchKernelGGL(cholesky_kernel, dim3(1), dim3(kSolverThreads), 0, stream, C, ki, A, dropped,
+                     reinterpret_cast<float*>(R.ws + R.L.m));
   double* lam = reinterpret_cast<double*>(R.ws + R.L.lam);
   int* perm = reinterpret_cast<int*>(R.ws + R.L.perm);
-  hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(kSolverThreads), 0, stream, A,
-                     reinterpret_cast<double*>(R.ws + R.L.v), ki, lam, perm, reinterpret_cast<int*>(R.ws + R.L.sweeps));
+  {
+    double* Vc = reinterpret_cast<double*>(R.ws + R.L.v);
+    int* sw = reinterpret_cast<int*>(R.ws + R.L.sweeps);
+    // Groups of 16 or 32 lanes per pair keep more pairs in flight; columns
+    // longer than 10 entries per lane take a whole wave.
+    if (ki <= 160)
+      hipLaunchKernelGGL((jacobi_kernel<16, 10>), dim3(1), dim3(kSolverThreads), 0, stream, A, dropped, ki, C, Vc, lam,
+                         perm, sw);
+    else if (ki <= 320)
+      hipLaunchKernelGGL((jacobi_kernel<32, 10>), dim3(1), dim3(kSolverThreads), 0, stream, A, dropped, ki, C, Vc, lam,
+                         perm, sw);
+    else
+      hipLaunchKernelGGL((jacobi_kernel<64, 8>), dim3(1), dim3(kSolverThreads), 0, stream, A, dropped, ki, C, Vc, lam,
+                         perm, sw);
+  }
   float* Mu = reinterpret_cast<float*>(R.ws + R.L.mu);
   float* Mv = reinterpret_cast<float*>(R.ws + R.L.mv);
   {

@@ -117,7 +117,7 @@ def _case(O, I, seed, sigma=None, dtype=torch.float32):
     return ws[0], W0, s
 
 
-@pytest.mark.parametrize("O,I,rank", [(64, 40, 8), (300, 130, 24), (130, 300, 130)], ids=lambda v: str(v))
+@pytest.mark.parametrize("O,I,rank", [(64, 40, 8), (300, 130, 24), (130, 300, 130), (600, 400, 40), (340, 700, 20)], ids=lambda v: str(v))
 def test_full_probe_is_the_exact_truncated_svd(O, I, rank):
     # k = min(out, in): the probe spans the input space, so the result is the
     # Eckart-Young optimum, here with a gap after the rank.
@@ -215,3 +215,15 @@ def test_decompose_tiny_stack_matches_the_oracle_pipeline():
         e_orc = oracle.relative_frobenius_error(exact(wd[l]), oracle.reconstruct_weight(
             exact(bun["s"][l]), exact(bun["W0"][band]), Uo, Vo))
         assert abs(e_gpu - e_orc) <= 1e-3 * e_orc
+
+
+def test_streams_give_the_same_bundle():
+    # The layers' factorisations on four side streams (each with its own
+    # workspace and rocBLAS handle) equal the one-stream run bit for bit.
+    ws = _band(8, 1000, 1032, torch.bfloat16, seed=21, lowrank=16)
+    one = tb.decompose(ws, 2, 64, seed=3, streams=1)
+    four = tb.decompose(ws, 2, 64, seed=3, streams=4)
+    torch.cuda.synchronize()
+    for l in range(8):
+        assert torch.equal(one["s"][l], four["s"][l])
+        assert torch.equal(one["U"][l], four["U"][l]) and torch.equal(one["V"][l], four["V"][l]), l
