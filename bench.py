@@ -83,7 +83,6 @@ def parse():
     ap.add_argument("--materialised", action="store_true",
                     help="forward stacks: rebuild every layer's weight once in bf16 (outside the timed region) and "
                          "time the dense projections of the materialise-once mode (tb_dense_forward semantics)")
-    ap.add_argument("--streams", type=int, default=4, help="decompose*: side streams the layers' factorisations use")
     ap.add_argument("--power-iters", type=int, default=2, help="decompose*: power iterations of the randomized SVD")
     ap.add_argument("--replicas", type=int, default=None,
                     help="rotating pool of input replicas (default: enough for >= 1 GiB when the stack is small)")
@@ -826,7 +825,7 @@ def bench_decompose(args, torch, np, tb, gen):
     def step(keep=False):
         out = {}
         for fam in gen.FAMILIES:
-            out[fam] = tb.decompose(originals[fam], G, R, power_iters=q, seed=seed, streams=args.streams)
+            out[fam] = tb.decompose(originals[fam], G, R, power_iters=q, seed=seed)
             if not keep:
                 out[fam] = None
         return out
@@ -854,8 +853,8 @@ def bench_decompose(args, torch, np, tb, gen):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32 (f64 solvers)",
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {L}-layer stack, 7 families, G={G}, rank {R}, "
-                               f"k = rank + 16, {q} power iterations, {args.streams} streams",
-                   "layers": L, "bands": G, "rank": R, "power_iters": q, "streams": args.streams,
+                               f"k = rank + 16, {q} power iterations, each band's layers batched",
+                   "layers": L, "bands": G, "rank": R, "power_iters": q,
                    "matrices": L * len(gen.FAMILIES), "original_bytes": orig_bytes,
                    "matrices_per_s": round(L * len(gen.FAMILIES) / (ms * 1e-3), 2),
                    "mean_rel_error": float(np.mean(errs)), "parallelism": "single-gpu"},

@@ -28,6 +28,7 @@ EXPORTED = (
     "tb_linear_forward_group_workspace_size", "tb_linear_forward_group",
     "tb_reconstruct_weight", "tb_rel_frobenius_error", "tb_reconstruction_error",
     "tb_shared_block", "tb_row_scale", "tb_lowrank_factors_workspace_size", "tb_lowrank_factors",
+    "tb_lowrank_factors_batch",
     "tb_status_string", "tb_last_error",
 )
 MAX_BAND_LAYERS = 128
@@ -68,6 +69,8 @@ def _load() -> ctypes.CDLL:
     lib.tb_lowrank_factors_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_i64, ctypes.POINTER(c_sz)]
     lib.tb_lowrank_factors.argtypes = [c_p, c_p, c_p, c_i64, c_i64, c_i64, ctypes.c_int, c_p, c_i64, c_i32, c_p, c_p,
                                        c_p, c_sz, c_p]
+    lib.tb_lowrank_factors_batch.argtypes = [ctypes.POINTER(c_p), c_i32, c_p, c_p, c_i64, c_i64, c_i64, ctypes.c_int, c_p,
+                                             c_i64, c_i32, c_p, c_p, c_p, c_sz, c_p]
     lib.tb_status_string.argtypes = [ctypes.c_int]
     lib.tb_status_string.restype = ctypes.c_char_p
     lib.tb_last_error.argtypes = []
@@ -376,44 +379,62 @@ def lowrank_factors(weight: torch.Tensor, W0: torch.Tensor, s: torch.Tensor, ran
     return U, V
 
 
+def lowrank_factors_batch(weights, W0: torch.Tensor, S: torch.Tensor, rank: int, omega: torch.Tensor,
+                          power_iters: int, workspace: torch.Tensor | None = None):
+    """U [n, out, rank], V [n, in, rank] (fp32) for n weights of one band (shared W0), S [n, out], omega
+    [n, in, k], via tb_lowrank_factors_batch."""
+    n = len(weights)
+    out_dim, in_dim = weights[0].shape
+    k = omega.shape[2]
+    _need_cuda(W0, S, omega, *weights)
+    for t in (W0, S, omega):
+        if t.dtype != torch.float32:
+            raise TBError(TB_ERR_INVALID_ARGUMENT, "W0, S and omega must be fp32")
+    if tuple(S.shape) != (n, out_dim) or tuple(omega.shape[:2]) != (n, in_dim):
+        raise TBError(TB_ERR_INVALID_ARGUMENT, "S must be [n, out] and omega [n, in, k]")
+    U = torch.zeros((n, out_dim, rank), dtype=torch.float32, device=W0.device)
+    V = torch.zeros((n, in_dim, rank), dtype=torch.float32, device=W0.device)
+    need = n * lowrank_factors_workspace_size(out_dim, in_dim, rank, k)
+    ws = workspace if workspace is not None and workspace.numel() >= need else \
+        torch.empty(need, dtype=torch.uint8, device=W0.device)
+    ptrs = (ctypes.c_void_p * n)(*[w.data_ptr() for w in weights])
+    _check(lib.tb_lowrank_factors_batch(ptrs, n, _ptr(W0), _ptr(S), out_dim, in_dim, rank,
+                                        _dtype_code(weights[0].dtype), _ptr(omega), k, power_iters,
+                                        _ptr(U) if rank else None, _ptr(V) if rank else None, _ptr(ws), ws.numel(),
+                                        _stream()))
+    return U, V
+
+
 def decompose(weights, num_bands: int, rank: int, oversampling: int = 16, power_iters: int = 2, seed: int = 0,
-              streams: int = 4) -> dict:
-    """One family's theta bundle on the GPU: per band the shared block, per layer the row scale and the low-rank
-    factors (randomized SVD, k = min(rank + oversampling, out, in), probe drawn from a seeded normal generator in
-    layer order).  The layers' factorisations run on `streams` side streams (default priority, each with its own
-    workspace), so that the single-workgroup solver kernels of several layers overlap; the current stream waits
-    for all of them.  Returns {"W0": [per band], "band": [per layer], "s", "U", "V": [per layer]} of fp32
-    device tensors."""
+              batch_bytes: int = 8 << 30) -> dict:
+    """One family's theta bundle on the GPU: per band the shared block and the band's layers' row scales and
+    low-rank factors, batched (tb_lowrank_factors_batch, at most `batch_bytes` of workspace per call).  The
+    randomized SVD uses k = min(rank + oversampling, out, in) and one probe per layer, drawn from a seeded normal
+    generator in layer order.  Returns {"W0": [per band], "band": [per layer], "s", "U", "V": [per layer]} of
+    fp32 device tensors."""
     L = len(weights)
     bands = [band_index(L, num_bands, l) for l in range(L)]
     out_dim, in_dim = weights[0].shape
     dev = weights[0].device
     W0 = [shared_block([weights[l] for l in range(L) if bands[l] == b]) for b in range(num_bands)]
-    res = {"W0": W0, "band": bands, "s": [row_scale(weights[l], W0[bands[l]]) for l in range(L)], "U": [], "V": []}
+    res = {"W0": W0, "band": bands, "s": [row_scale(weights[l], W0[bands[l]]) for l in range(L)],
+           "U": [None] * L, "V": [None] * L}
     if rank == 0:
         res["U"] = [torch.zeros((out_dim, 0), dtype=torch.float32, device=dev) for _ in range(L)]
         res["V"] = [torch.zeros((in_dim, 0), dtype=torch.float32, device=dev) for _ in range(L)]
         return res
     k = min(rank + oversampling, out_dim, in_dim, MAX_PROBE)
     gen = torch.Generator(device="cpu").manual_seed(seed)
-    omegas = [torch.randn((in_dim, k), generator=gen, dtype=torch.float32).to(dev) for _ in range(L)]
-    main = torch.cuda.current_stream()
-    side = [torch.cuda.Stream(device=dev) for _ in range(max(1, min(streams, L)))]
-    need = lowrank_factors_workspace_size(out_dim, in_dim, rank, k)
-    wss = [torch.empty(need, dtype=torch.uint8, device=dev) for _ in side]
-    for st, ws in zip(side, wss):
-        st.wait_stream(main)
-        ws.record_stream(st)
-    for l in range(L):
-        j = l % len(side)
-        with torch.cuda.stream(side[j]):
-            for t in (weights[l], W0[bands[l]], res["s"][l], omegas[l]):
-                t.record_stream(side[j])
-            U, V = lowrank_factors(weights[l], W0[bands[l]], res["s"][l], rank, omegas[l], power_iters, wss[j])
-            U.record_stream(main)
-            V.record_stream(main)
-        res["U"].append(U)
-        res["V"].append(V)
-    for st in side:
-        main.wait_stream(st)
+    omegas = [torch.randn((in_dim, k), generator=gen, dtype=torch.float32) for _ in range(L)]
+    per = lowrank_factors_workspace_size(out_dim, in_dim, rank, k)
+    chunk = max(1, min(MAX_BAND_LAYERS, batch_bytes // per))
+    for b in range(num_bands):
+        members = [l for l in range(L) if bands[l] == b]
+        for c0 in range(0, len(members), chunk):
+            part = members[c0:c0 + chunk]
+            S = torch.stack([res["s"][l] for l in part])
+            om = torch.stack([omegas[l] for l in part]).to(dev)
+            U, V = lowrank_factors_batch([weights[l] for l in part], W0[b], S, rank, om, power_iters)
+            for j, l in enumerate(part):
+                res["U"][l], res["V"][l] = U[j], V[j]
     return res

@@ -404,8 +404,43 @@ tb_status tb_lowrank_factors(const void* weight, const float* w0, const float* s
     return fail(TB_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is below the %zu needed", workspace_bytes, need);
   if (rank == 0) return ok();
   const char* what = "";
-  const int e = launch_lowrank_factors(weight_dtype, weight, w0, s, out_dim, in_dim, rank, omega, k, power_iters, u_out,
-                                       v_out, workspace, cus, static_cast<hipStream_t>(stream), &what);
+  const void* const weights[1] = {weight};
+  const int e = launch_lowrank_factors(weight_dtype, weights, 1, w0, s, out_dim, in_dim, rank, omega, k, power_iters,
+                                       u_out, v_out, workspace, cus, static_cast<hipStream_t>(stream), &what);
+  if (e == -1) return fail(TB_ERR_HIP, "%s failed", what);
+  if (e != 0) return hip_fail(hipError_t(e), what);
+  return ok();
+}
+
+tb_status tb_lowrank_factors_batch(const void* const* weights, int32_t n, const float* w0, const float* s,
+                                   int64_t out_dim, int64_t in_dim, int64_t rank, tb_dtype weight_dtype,
+                                   const float* omega, int64_t k, int32_t power_iters, float* u_out, float* v_out,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(weight_dtype)) return fail(TB_ERR_INVALID_ARGUMENT, "unknown dtype %d", int(weight_dtype));
+  if (!weights) return fail(TB_ERR_INVALID_ARGUMENT, "weights must be non-NULL");
+  if (n < 1 || n > TB_MAX_BAND_LAYERS) return fail(TB_ERR_INVALID_ARGUMENT, "n %d outside [1, %d]", n, TB_MAX_BAND_LAYERS);
+  tb_status st = check_lowrank_dims(out_dim, in_dim, rank, k);
+  if (st != TB_OK) return st;
+  if (power_iters < 0 || power_iters > 16) return fail(TB_ERR_INVALID_ARGUMENT, "power_iters %d outside [0, 16]", power_iters);
+  if (!w0 || !s || !omega || !workspace)
+    return fail(TB_ERR_INVALID_ARGUMENT, "w0, s, omega and workspace must be non-NULL");
+  if (rank > 0 && (!u_out || !v_out)) return fail(TB_ERR_INVALID_ARGUMENT, "u_out and v_out must be non-NULL");
+  for (int j = 0; j < n; ++j) {
+    if (!weights[j]) return fail(TB_ERR_INVALID_ARGUMENT, "weights[%d] is NULL", j);
+    if (!aligned_to(weights[j], esize(weight_dtype))) return fail(TB_ERR_INVALID_ARGUMENT, "weights[%d] misaligned", j);
+  }
+  if (!aligned_to(w0, 4) || !aligned_to(s, 4) || !aligned_to(omega, 4) || !aligned_to(u_out, 4) || !aligned_to(v_out, 4))
+    return fail(TB_ERR_INVALID_ARGUMENT, "a pointer is misaligned");
+  if (!aligned_to(workspace, 256)) return fail(TB_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  int cus = 0;
+  if (int e = device_cu_count(&cus)) return hip_fail(hipError_t(e), "querying the compute-unit count");
+  const size_t need = size_t(n) * lowrank_workspace_bytes(out_dim, in_dim, k, rank, cus);
+  if (workspace_bytes < need)
+    return fail(TB_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is below the %zu needed", workspace_bytes, need);
+  if (rank == 0) return ok();
+  const char* what = "";
+  const int e = launch_lowrank_factors(weight_dtype, weights, n, w0, s, out_dim, in_dim, rank, omega, k, power_iters,
+                                       u_out, v_out, workspace, cus, static_cast<hipStream_t>(stream), &what);
   if (e == -1) return fail(TB_ERR_HIP, "%s failed", what);
   if (e != 0) return hip_fail(hipError_t(e), what);
   return ok();

@@ -86,14 +86,38 @@ __global__ __launch_bounds__(kThreads) void row_scale_kernel(const E* __restrict
   if (threadIdx.x == 0) s[o] = den != 0.0 ? float(num / den) : 0.f;
 }
 
+// ---- batches ------------------------------------------------------------------------
+//
+// tb_lowrank_factors works on a batch of matrices of one shape.  Each matrix
+// has a workspace slice of its own (`stride` bytes apart): the kernels below
+// take the batch's first pointer into the workspace and the stride, and a
+// grid dimension for the batch index.
+
+template <typename T>
+__device__ __forceinline__ T* at_batch(T* p, int64_t stride, int b) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(p) + stride * b);
+}
+template <typename T>
+__device__ __forceinline__ const T* at_batch(const T* p, int64_t stride, int b) {
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(p) + stride * b);
+}
+
+struct WeightPtrs {
+  const void* w[TB_MAX_BAND_LAYERS];
+};
+
 // ---- residual --------------------------------------------------------------------
 
 // E = W - diag(s) W0 in fp32, one rounding (fma) per entry.  grid (column
-// blocks, row blocks), both grid-stride.
+// blocks, row blocks, batch), the first two grid-stride; s is [batch][O].
 template <typename E>
-__global__ __launch_bounds__(kThreads) void residual_kernel(const E* __restrict__ w, const float* __restrict__ w0,
-                                                            const float* __restrict__ s, int64_t O, int64_t I,
-                                                            float* __restrict__ e) {
+__global__ __launch_bounds__(kThreads) void residual_kernel(WeightPtrs wp, const float* __restrict__ w0,
+                                                            const float* __restrict__ s0, int64_t O, int64_t I,
+                                                            float* __restrict__ e0, int64_t stride) {
+  const int b = blockIdx.z;
+  const E* __restrict__ w = static_cast<const E*>(wp.w[b]);
+  const float* __restrict__ s = s0 + int64_t(b) * O;
+  float* __restrict__ e = at_batch(e0, stride, b);
   for (int64_t o = blockIdx.y; o < O; o += gridDim.y) {
     const float so = s[o];
     for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < I; i += int64_t(gridDim.x) * kThreads) {
@@ -119,9 +143,12 @@ __device__ __forceinline__ void upper_tile(int t, int T, int& ta, int& tb) {
 // Workgroup (tile, split) sums rows [split * rows_per, ...) of A [n, k]
 // (row-major fp32) into the 64 x 64 tile (ta, tb) of part[split] (fp64).
 // Thread (ty, tx) of 16 x 16 holds outputs (ta*64 + 4ty + i, tb*64 + 4tx + j).
-__global__ __launch_bounds__(kThreads) void gram_partial_kernel(const float* __restrict__ A, int64_t n, int k,
-                                                                int64_t rows_per, double* __restrict__ part) {
+__global__ __launch_bounds__(kThreads) void gram_partial_kernel(const float* __restrict__ A0, int64_t n, int k,
+                                                                int64_t rows_per, double* __restrict__ part0,
+                                                                int64_t stride) {
   __shared__ float as[kGramRows][kGramTile], bs[kGramRows][kGramTile];
+  const float* __restrict__ A = at_batch(A0, stride, blockIdx.z);
+  double* __restrict__ part = at_batch(part0, stride, blockIdx.z);
   const int T = (k + kGramTile - 1) / kGramTile;
   int ta, tb;
   upper_tile(blockIdx.x, T, ta, tb);
@@ -167,8 +194,10 @@ __global__ __launch_bounds__(kThreads) void gram_partial_kernel(const float* __r
 
 // C[a][b] = sum over splits, in split order, of the upper tile holding (a, b)
 // or (b, a): C is exactly symmetric.
-__global__ __launch_bounds__(kThreads) void gram_reduce_kernel(const double* __restrict__ part, int k, int splits,
-                                                               double* __restrict__ C) {
+__global__ __launch_bounds__(kThreads) void gram_reduce_kernel(const double* __restrict__ part0, int k, int splits,
+                                                               double* __restrict__ C0, int64_t stride) {
+  const double* __restrict__ part = at_batch(part0, stride, blockIdx.y);
+  double* __restrict__ C = at_batch(C0, stride, blockIdx.y);
   const int64_t kk = int64_t(k) * k;
   for (int64_t idx = int64_t(blockIdx.x) * kThreads + threadIdx.x; idx < kk; idx += int64_t(gridDim.x) * kThreads) {
     const int a = int(idx / k), b = int(idx % k);
@@ -188,9 +217,13 @@ __global__ __launch_bounds__(kThreads) void gram_reduce_kernel(const double* __r
 // and dropped[j] = 1 (the caller zeroes column j of the input, so that the
 // triangular solve gives a zero column of Q and leaves the others alone).
 // R32 = R in fp32 (k x k, row-major, zero below the diagonal).  A: k x k scratch.
-__global__ __launch_bounds__(kSolverThreads) void cholesky_kernel(const double* __restrict__ C, int k,
-                                                                  double* __restrict__ A, int* __restrict__ dropped,
-                                                                  float* __restrict__ R32) {
+__global__ __launch_bounds__(kSolverThreads) void cholesky_kernel(const double* __restrict__ C0, int k,
+                                                                  double* __restrict__ A0, int* __restrict__ dropped0,
+                                                                  float* __restrict__ R320, int64_t stride) {
+  const double* __restrict__ C = at_batch(C0, stride, blockIdx.x);
+  double* __restrict__ A = at_batch(A0, stride, blockIdx.x);
+  int* __restrict__ dropped = at_batch(dropped0, stride, blockIdx.x);
+  float* __restrict__ R32 = at_batch(R320, stride, blockIdx.x);
   __shared__ double s_row[TB_MAX_PROBE];
   __shared__ double s_piv, s_max;
   __shared__ int s_drop;
@@ -254,8 +287,10 @@ __global__ __launch_bounds__(kSolverThreads) void cholesky_kernel(const double* 
 }
 
 // Zero the columns of X [n, k] whose direction the Cholesky factor dropped.
-__global__ __launch_bounds__(kThreads) void zero_dropped_kernel(float* __restrict__ X, int64_t n, int k,
-                                                                const int* __restrict__ dropped) {
+__global__ __launch_bounds__(kThreads) void zero_dropped_kernel(float* __restrict__ X0, int64_t n, int k,
+                                                                const int* __restrict__ dropped0, int64_t stride) {
+  float* __restrict__ X = at_batch(X0, stride, blockIdx.y);
+  const int* __restrict__ dropped = at_batch(dropped0, stride, blockIdx.y);
   const int64_t total = n * k;
   for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < total; i += int64_t(gridDim.x) * kThreads)
     if (dropped[i % k]) X[i] = 0.f;
@@ -284,11 +319,19 @@ __device__ __forceinline__ double group_sum(double v) {
 // above kJacobiTol.  On exit lam[j] = |column j of R V|^2 (the eigenvalues),
 // perm the columns by decreasing lam (ties by index), sweeps[0] the sweeps.
 template <int G, int kPer>
-__global__ __launch_bounds__(kSolverThreads) void jacobi_kernel(const double* __restrict__ Rrow,
-                                                                const int* __restrict__ dropped, int k,
-                                                                double* __restrict__ Rc, double* __restrict__ Vc,
-                                                                double* __restrict__ lam, int* __restrict__ perm,
-                                                                int* __restrict__ sweeps) {
+__global__ __launch_bounds__(kSolverThreads) void jacobi_kernel(const double* __restrict__ Rrow0,
+                                                                const int* __restrict__ dropped0, int k,
+                                                                double* __restrict__ Rc0, double* __restrict__ Vc0,
+                                                                double* __restrict__ lam0, int* __restrict__ perm0,
+                                                                int* __restrict__ sweeps0, int64_t stride) {
+  const int bt = blockIdx.x;
+  const double* __restrict__ Rrow = at_batch(Rrow0, stride, bt);
+  const int* __restrict__ dropped = at_batch(dropped0, stride, bt);
+  double* __restrict__ Rc = at_batch(Rc0, stride, bt);
+  double* __restrict__ Vc = at_batch(Vc0, stride, bt);
+  double* __restrict__ lam = at_batch(lam0, stride, bt);
+  int* __restrict__ perm = at_batch(perm0, stride, bt);
+  int* __restrict__ sweeps = at_batch(sweeps0, stride, bt);
   constexpr int kWavesJ = kSolverThreads / kWave;
   constexpr int kGroups = kSolverThreads / G;                // pairs in flight
   __shared__ double s_red[kWavesJ];
@@ -388,9 +431,16 @@ __global__ __launch_bounds__(kSolverThreads) void jacobi_kernel(const double* __
 // sqrt of the j-th largest eigenvalue, P's columns stored contiguously (Vc);
 // a singular value at or below sqrt(kSigmaTol) of the largest counts as zero
 // (zero columns in both).
-__global__ __launch_bounds__(kThreads) void assemble_kernel(const double* __restrict__ V, const double* __restrict__ lam,
-                                                            const int* __restrict__ perm, int k, int r,
-                                                            float* __restrict__ Mu, float* __restrict__ Mv) {
+__global__ __launch_bounds__(kThreads) void assemble_kernel(const double* __restrict__ V0, const double* __restrict__ lam0,
+                                                            const int* __restrict__ perm0, int k, int r,
+                                                            float* __restrict__ Mu0, float* __restrict__ Mv0,
+                                                            int64_t stride) {
+  const int bt = blockIdx.y;
+  const double* __restrict__ V = at_batch(V0, stride, bt);
+  const double* __restrict__ lam = at_batch(lam0, stride, bt);
+  const int* __restrict__ perm = at_batch(perm0, stride, bt);
+  float* __restrict__ Mu = at_batch(Mu0, stride, bt);
+  float* __restrict__ Mv = at_batch(Mv0, stride, bt);
   const double lmax = lam[perm[0]];
   for (int idx = blockIdx.x * kThreads + threadIdx.x; idx < k * r; idx += gridDim.x * kThreads) {
     const int a = idx / r, j = idx % r;
@@ -474,54 +524,70 @@ Layout layout(int64_t O, int64_t I, int64_t k, int64_t r, int cus) {
 }
 
 struct Run {
-  char* ws;
+  char* ws;   // the first matrix's workspace slice; slice b at ws + b * L.total
   Layout L;
-  int k, cus;
+  int k, cus, n;
   hipStream_t stream;
   rocblas_handle h;
+  int64_t stride() const { return int64_t(L.total); }
+  int64_t fstride() const { return int64_t(L.total / 4); }   // in floats (L.total is a multiple of 256)
+  template <typename T>
+  T* at(size_t off) const {
+    return reinterpret_cast<T*>(ws + off);
+  }
 };
 
-// C = A^T A for A [n, k] fp32.
-hipError_t gram(const Run& R, const float* A, int64_t n, double* C) {
+// Row-major strided-batched C [M x N] = op(A) op(B) (see gemm_rm).
+rocblas_status gemm_rm_batched(const Run& R, bool ta, bool tb, int M, int N, int K, const float* A, int lda,
+                               int64_t sa, const float* B, int ldb, int64_t sb, float* C, int ldc, int64_t sc) {
+  const float one = 1.f, zero = 0.f;
+  return rocblas_sgemm_strided_batched(R.h, tb ? rocblas_operation_transpose : rocblas_operation_none,
+                                       ta ? rocblas_operation_transpose : rocblas_operation_none, N, M, K, &one, B,
+                                       ldb, sb, A, lda, sa, &zero, C, ldc, sc, R.n);
+}
+
+// C = A^T A for A [rows, k] fp32, every matrix of the batch (A, C at workspace offsets).
+hipError_t gram(const Run& R, size_t off_a, int64_t rows, size_t off_c) {
   const int k = R.k, T = (k + kGramTile - 1) / kGramTile, tiles = T * (T + 1) / 2;
-  const int splits = gram_splits(n, k, R.cus);
-  const int64_t rows_per = (n + splits - 1) / splits;
-  double* part = reinterpret_cast<double*>(R.ws + R.L.part);
-  hipLaunchKernelGGL(gram_partial_kernel, dim3(unsigned(tiles), unsigned(splits)), dim3(kThreads), 0, R.stream, A, n,
-                     k, rows_per, part);
+  const int splits = gram_splits(rows, k, R.cus);
+  const int64_t rows_per = (rows + splits - 1) / splits;
+  hipLaunchKernelGGL(gram_partial_kernel, dim3(unsigned(tiles), unsigned(splits), unsigned(R.n)), dim3(kThreads), 0,
+                     R.stream, R.at<const float>(off_a), rows, k, rows_per, R.at<double>(R.L.part), R.stride());
   const int64_t kk = int64_t(k) * k;
   const unsigned blocks = unsigned((kk + kThreads - 1) / kThreads);
-  hipLaunchKernelGGL(gram_reduce_kernel, dim3(blocks), dim3(kThreads), 0, R.stream, part, k, splits, C);
+  hipLaunchKernelGGL(gram_reduce_kernel, dim3(blocks, unsigned(R.n)), dim3(kThreads), 0, R.stream,
+                     R.at<const double>(R.L.part), k, splits, R.at<double>(off_c), R.stride());
   return hipGetLastError();
 }
 
-// X [n, k] <- a basis of its columns by `passes` rounds of CholeskyQR (Gram
-// matrix, Cholesky factor R, X <- X R^-1 by a triangular solve in place).
-// One round leaves the columns well conditioned (enough between power
-// iterations); two make them orthonormal to working precision.
-int orthonormalize(const Run& R, float* X, int64_t n, int passes, const char** what) {
-  double* C = reinterpret_cast<double*>(R.ws + R.L.c);
-  float* R32 = reinterpret_cast<float*>(R.ws + R.L.m);
-  int* dropped = reinterpret_cast<int*>(R.ws + R.L.drop);
+// X [rows, k] (workspace offset off_x) <- a basis of its columns by `passes`
+// rounds of CholeskyQR (Gram matrix, Cholesky factor R, X <- X R^-1 by a
+// triangular solve in place).  One round leaves the columns well
+// conditioned (enough between power iterations); two make them orthonormal
+// to working precision.
+int orthonormalize(const Run& R, size_t off_x, int64_t rows, int passes, const char** what) {
   for (int pass = 0; pass < passes; ++pass) {
-    if (hipError_t e = gram(R, X, n, C)) {
+    if (hipError_t e = gram(R, off_x, rows, R.L.c)) {
       *what = "Gram matrix";
       return int(e);
     }
-    hipLaunchKernelGGL(cholesky_kernel, dim3(1), dim3(kSolverThreads), 0, R.stream, C, R.k,
-                       reinterpret_cast<double*>(R.ws + R.L.a), dropped, R32);
-    int64_t blocks = (n * R.k + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(cholesky_kernel, dim3(unsigned(R.n)), dim3(kSolverThreads), 0, R.stream,
+                       R.at<const double>(R.L.c), R.k, R.at<double>(R.L.a), R.at<int>(R.L.drop), R.at<float>(R.L.m),
+                       R.stride());
+    int64_t blocks = (rows * R.k + kThreads - 1) / kThreads;
     if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(zero_dropped_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, R.stream, X, n, R.k, dropped);
+    hipLaunchKernelGGL(zero_dropped_kernel, dim3(unsigned(blocks), unsigned(R.n)), dim3(kThreads), 0, R.stream,
+                       R.at<float>(off_x), rows, R.k, R.at<const int>(R.L.drop), R.stride());
     if (hipError_t e = hipGetLastError()) {
       *what = "Cholesky factor";
       return int(e);
     }
-    // Row-major X [n, k] is column-major X^T [k, n]; row-major R (upper) is
-    // column-major R^T (lower): solve R^T Z = X^T, Z = (X R^-1)^T.
+    // Row-major X [rows, k] is column-major X^T [k, rows]; row-major R
+    // (upper) is column-major R^T (lower): solve R^T Z = X^T, Z = (X R^-1)^T.
     const float one = 1.f;
-    if (rocblas_strsm(R.h, rocblas_side_left, rocblas_fill_lower, rocblas_operation_none, rocblas_diagonal_non_unit, R.k,
-                      int(n), &one, R32, R.k, X, R.k) != rocblas_status_success) {
+    if (rocblas_strsm_strided_batched(R.h, rocblas_side_left, rocblas_fill_lower, rocblas_operation_none,
+                                      rocblas_diagonal_non_unit, R.k, int(rows), &one, R.at<const float>(R.L.m), R.k,
+                                      R.fstride(), R.at<float>(off_x), R.k, R.fstride(), R.n) != rocblas_status_success) {
       *what = "rocblas_strsm (basis)";
       return -1;
     }
@@ -560,17 +626,13 @@ size_t lowrank_workspace_bytes(int64_t O, int64_t I, int64_t k, int64_t r, int c
   return layout(O, I, k, r, cus).total;
 }
 
-int launch_lowrank_factors(tb_dtype dtype, const void* weight, const float* w0, const float* s, int64_t O, int64_t I,
-                           int64_t r, const float* omega, int64_t k, int power_iters, float* u_out, float* v_out,
-                           void* workspace, int cus, hipStream_t stream, const char** what) {
+int launch_lowrank_factors(tb_dtype dtype, const void* const* weights, int n, const float* w0, const float* s,
+                           int64_t O, int64_t I, int64_t r, const float* omega, int64_t k, int power_iters,
+                           float* u_out, float* v_out, void* workspace, int cus, hipStream_t stream, const char** what) {
   int dev = 0;
   if (hipError_t e = hipGetDevice(&dev)) {
     *what = "hipGetDevice";
     return int(e);
-  }
-  if (dev < 0 || dev >= 64) {
-    *what = "device index";
-    return int(hipErrorInvalidDevice);
   }
   std::lock_guard<std::mutex> lock(g_blas.mu);
   rocblas_handle h = nullptr;
@@ -583,94 +645,97 @@ int launch_lowrank_factors(tb_dtype dtype, const void* weight, const float* w0, 
     }
     g_blas.handles.push_back({dev, stream, h});
   }
-  Run R{static_cast<char*>(workspace), layout(O, I, k, r, cus), int(k), cus, stream, h};
+  Run R{static_cast<char*>(workspace), layout(O, I, k, r, cus), int(k), cus, n, stream, h};
   if (rocblas_set_stream(R.h, stream) != rocblas_status_success) {
     *what = "rocblas_set_stream";
     return -1;
   }
-  float* E = reinterpret_cast<float*>(R.ws + R.L.e);
-  float* O1 = reinterpret_cast<float*>(R.ws + R.L.o1);
-  float* I1 = reinterpret_cast<float*>(R.ws + R.L.i1);
+  const Layout& L = R.L;
   const int Oi = int(O), Ii = int(I), ki = int(k), ri = int(r);
+  const int64_t fs = R.fstride();
+  float* E = R.at<float>(L.e);
+  float* O1 = R.at<float>(L.o1);
+  float* I1 = R.at<float>(L.i1);
+  auto gemm_fail = [&](const char* w) {
+    *what = w;
+    return -1;
+  };
 
   {
+    WeightPtrs wp{};
+    for (int j = 0; j < n; ++j) wp.w[j] = weights[j];
     int64_t bx = (I + kThreads - 1) / kThreads;
     if (bx > 64) bx = 64;
-    const unsigned by = unsigned(O < 65535 ? O : 65535);
+    const unsigned by = unsigned(O < 4096 ? O : 4096);
     if (dtype == TB_BF16)
-      hipLaunchKernelGGL(residual_kernel<bf16_t>, dim3(unsigned(bx), by), dim3(kThreads), 0, stream,
-                         static_cast<const bf16_t*>(weight), w0, s, O, I, E);
+      hipLaunchKernelGGL(residual_kernel<bf16_t>, dim3(unsigned(bx), by, unsigned(n)), dim3(kThreads), 0, stream, wp,
+                         w0, s, O, I, E, R.stride());
     else
-      hipLaunchKernelGGL(residual_kernel<float>, dim3(unsigned(bx), by), dim3(kThreads), 0, stream,
-                         static_cast<const float*>(weight), w0, s, O, I, E);
+      hipLaunchKernelGGL(residual_kernel<float>, dim3(unsigned(bx), by, unsigned(n)), dim3(kThreads), 0, stream, wp,
+                         w0, s, O, I, E, R.stride());
     if (hipError_t e = hipGetLastError()) {
       *what = "residual";
       return int(e);
     }
   }
-  auto gemm_fail = [&](const char* w) {
-    *what = w;
-    return -1;
-  };
-  // Range finder.
-  if (gemm_rm(R.h, false, false, Oi, ki, Ii, E, Ii, omega, ki, O1, ki) != rocblas_status_success)
+  // Range finder: Y = E Omega (each matrix its own probe, [n][I][k]).
+  if (gemm_rm_batched(R, false, false, Oi, ki, Ii, E, Ii, fs, omega, ki, I * k, O1, ki, fs) != rocblas_status_success)
     return gemm_fail("rocblas_sgemm (E Omega)");
   // Between power iterations one CholeskyQR round keeps the weak directions;
   // the final basis gets two.
-  if (int e = orthonormalize(R, O1, O, power_iters > 0 ? 1 : 2, what)) return e;
+  if (int e = orthonormalize(R, L.o1, O, power_iters > 0 ? 1 : 2, what)) return e;
   for (int it = 0; it < power_iters; ++it) {
-    if (gemm_rm(R.h, true, false, Ii, ki, Oi, E, Ii, O1, ki, I1, ki) != rocblas_status_success)
+    if (gemm_rm_batched(R, true, false, Ii, ki, Oi, E, Ii, fs, O1, ki, fs, I1, ki, fs) != rocblas_status_success)
       return gemm_fail("rocblas_sgemm (E^T Q)");
-    if (int e = orthonormalize(R, I1, I, 1, what)) return e;
-    if (gemm_rm(R.h, false, false, Oi, ki, Ii, E, Ii, I1, ki, O1, ki) != rocblas_status_success)
+    if (int e = orthonormalize(R, L.i1, I, 1, what)) return e;
+    if (gemm_rm_batched(R, false, false, Oi, ki, Ii, E, Ii, fs, I1, ki, fs, O1, ki, fs) != rocblas_status_success)
       return gemm_fail("rocblas_sgemm (E Q')");
-    if (int e = orthonormalize(R, O1, O, it + 1 == power_iters ? 2 : 1, what)) return e;
+    if (int e = orthonormalize(R, L.o1, O, it + 1 == power_iters ? 2 : 1, what)) return e;
   }
-  // B^T = E^T Q, its Gram matrix B B^T and the eigen-decomposition.
-  if (gemm_rm(R.h, true, false, Ii, ki, Oi, E, Ii, O1, ki, I1, ki) != rocblas_status_success)
+  // B^T = E^T Q, its Gram matrix B B^T, the Cholesky factor of that and the
+  // SVD of the factor (the eigenvectors of B B^T).
+  if (gemm_rm_batched(R, true, false, Ii, ki, Oi, E, Ii, fs, O1, ki, fs, I1, ki, fs) != rocblas_status_success)
     return gemm_fail("rocblas_sgemm (B^T)");
-  double* C = reinterpret_cast<double*>(R.ws + R.L.c);
-  if (hipError_t e = gram(R, I1, I, C)) {
+  if (hipError_t e = gram(R, L.i1, I, L.c)) {
     *what = "Gram matrix of B";
     return int(e);
   }
-  // Its Cholesky factor, then the SVD of the factor (the eigenvectors of B B^T).
-  double* A = reinterpret_cast<double*>(R.ws + R.L.a);
-  int* dropped = reinterpret_cast<int*>(R.ws + R.L.drop);
-  hipLaunchKernelGGL(cholesky_kernel, dim3(1), dim3(kSolverThreads), 0, stream, C, ki, A, dropped,
-                     reinterpret_cast<float*>(R.ws + R.L.m));
-  double* lam = reinterpret_cast<double*>(R.ws + R.L.lam);
-  int* perm = reinterpret_cast<int*>(R.ws + R.L.perm);
+  hipLaunchKernelGGL(cholesky_kernel, dim3(unsigned(n)), dim3(kSolverThreads), 0, stream, R.at<const double>(L.c), ki,
+                     R.at<double>(L.a), R.at<int>(L.drop), R.at<float>(L.m), R.stride());
   {
-    double* Vc = reinterpret_cast<double*>(R.ws + R.L.v);
-    int* sw = reinterpret_cast<int*>(R.ws + R.L.sweeps);
+    const double* A = R.at<const double>(L.a);
+    const int* dropped = R.at<const int>(L.drop);
+    double* Rc = R.at<double>(L.c);
+    double* Vc = R.at<double>(L.v);
+    double* lam = R.at<double>(L.lam);
+    int* perm = R.at<int>(L.perm);
+    int* sw = R.at<int>(L.sweeps);
     // Groups of 16 or 32 lanes per pair keep more pairs in flight; columns
     // longer than 10 entries per lane take a whole wave.
     if (ki <= 160)
-      hipLaunchKernelGGL((jacobi_kernel<16, 10>), dim3(1), dim3(kSolverThreads), 0, stream, A, dropped, ki, C, Vc, lam,
-                         perm, sw);
+      hipLaunchKernelGGL((jacobi_kernel<16, 10>), dim3(unsigned(n)), dim3(kSolverThreads), 0, stream, A, dropped, ki,
+                         Rc, Vc, lam, perm, sw, R.stride());
     else if (ki <= 320)
-      hipLaunchKernelGGL((jacobi_kernel<32, 10>), dim3(1), dim3(kSolverThreads), 0, stream, A, dropped, ki, C, Vc, lam,
-                         perm, sw);
+      hipLaunchKernelGGL((jacobi_kernel<32, 10>), dim3(unsigned(n)), dim3(kSolverThreads), 0, stream, A, dropped, ki,
+                         Rc, Vc, lam, perm, sw, R.stride());
     else
-      hipLaunchKernelGGL((jacobi_kernel<64, 8>), dim3(1), dim3(kSolverThreads), 0, stream, A, dropped, ki, C, Vc, lam,
-                         perm, sw);
-  }
-  float* Mu = reinterpret_cast<float*>(R.ws + R.L.mu);
-  float* Mv = reinterpret_cast<float*>(R.ws + R.L.mv);
-  {
+      hipLaunchKernelGGL((jacobi_kernel<64, 8>), dim3(unsigned(n)), dim3(kSolverThreads), 0, stream, A, dropped, ki,
+                         Rc, Vc, lam, perm, sw, R.stride());
     unsigned blocks = unsigned((k * r + kThreads - 1) / kThreads);
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(assemble_kernel, dim3(blocks), dim3(kThreads), 0, stream,
-                       reinterpret_cast<const double*>(R.ws + R.L.v), lam, perm, ki, ri, Mu, Mv);
+    hipLaunchKernelGGL(assemble_kernel, dim3(blocks, unsigned(n)), dim3(kThreads), 0, stream,
+                       R.at<const double>(L.v), R.at<const double>(L.lam), R.at<const int>(L.perm), ki, ri,
+                       R.at<float>(L.mu), R.at<float>(L.mv), R.stride());
   }
   if (hipError_t e = hipGetLastError()) {
-    *what = "eigen-decomposition";
+    *what = "singular value decomposition";
     return int(e);
   }
-  if (gemm_rm(R.h, false, false, Oi, ri, ki, O1, ki, Mu, ri, u_out, ri) != rocblas_status_success)
+  if (gemm_rm_batched(R, false, false, Oi, ri, ki, O1, ki, fs, R.at<const float>(L.mu), ri, fs, u_out, ri, O * r) !=
+      rocblas_status_success)
     return gemm_fail("rocblas_sgemm (U)");
-  if (gemm_rm(R.h, false, false, Ii, ri, ki, I1, ki, Mv, ri, v_out, ri) != rocblas_status_success)
+  if (gemm_rm_batched(R, false, false, Ii, ri, ki, I1, ki, fs, R.at<const float>(L.mv), ri, fs, v_out, ri, I * r) !=
+      rocblas_status_success)
     return gemm_fail("rocblas_sgemm (V)");
   return 0;
 }
