@@ -299,17 +299,19 @@ tb_status tb_lowrank_factors(const void *weight, const float *w0, const float *s
 
 /*
  * tb_lowrank_factors_batch -- tb_lowrank_factors for n matrices of one shape
- * that share one W0 (the layers of a band), in one pass: every step runs on
- * all of them together, so the single-workgroup solvers of the n matrices
- * share the chip.  Each matrix's result equals what tb_lowrank_factors
- * computes for it up to the rounding of the batched products.
- *   weights: HOST array of n DEVICE pointers ([out_dim, in_dim], weight_dtype),
- *   1 <= n <= TB_MAX_BAND_LAYERS; s [n][out_dim], omega [n][in_dim][k],
+ * (the layers of a projection family, each with its band's W0), in one pass:
+ * every step runs on all of them together, so the single-workgroup solvers
+ * of the n matrices share the chip.  Each matrix's result equals what
+ * tb_lowrank_factors computes for it up to the rounding of the batched
+ * products.
+ *   weights, w0s: HOST arrays of n DEVICE pointers ([out_dim, in_dim]; weights
+ *   of weight_dtype, w0s fp32), 1 <= n <= TB_MAX_BAND_LAYERS; s [n][out_dim],
+ *   omega [n][in_dim][k],
  *   u_out [n][out_dim][rank], v_out [n][in_dim][rank], all fp32 device and
  *   contiguous.  workspace: n times tb_lowrank_factors_workspace_size()
  *   bytes, 256-byte aligned.  Other rules and errors as tb_lowrank_factors.
  */
-tb_status tb_lowrank_factors_batch(const void *const *weights, int32_t n, const float *w0, const float *s,
+tb_status tb_lowrank_factors_batch(const void *const *weights, int32_t n, const float *const *w0s, const float *s,
                                    int64_t out_dim, int64_t in_dim, int64_t rank, tb_dtype weight_dtype,
                                    const float *omega, int64_t k, int32_t power_iters, float *u_out, float *v_out,
                                    void *workspace, size_t workspace_bytes, void *stream);

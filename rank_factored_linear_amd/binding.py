@@ -69,7 +69,8 @@ def _load() -> ctypes.CDLL:
     lib.tb_lowrank_factors_workspace_size.argtypes = [c_i64, c_i64, c_i64, c_i64, ctypes.POINTER(c_sz)]
     lib.tb_lowrank_factors.argtypes = [c_p, c_p, c_p, c_i64, c_i64, c_i64, ctypes.c_int, c_p, c_i64, c_i32, c_p, c_p,
                                        c_p, c_sz, c_p]
-    lib.tb_lowrank_factors_batch.argtypes = [ctypes.POINTER(c_p), c_i32, c_p, c_p, c_i64, c_i64, c_i64, ctypes.c_int, c_p,
+    lib.tb_lowrank_factors_batch.argtypes = [ctypes.POINTER(c_p), c_i32, ctypes.POINTER(c_p), c_p, c_i64, c_i64, c_i64,
+                                             ctypes.c_int, c_p,
                                              c_i64, c_i32, c_p, c_p, c_p, c_sz, c_p]
     lib.tb_status_string.argtypes = [ctypes.c_int]
     lib.tb_status_string.restype = ctypes.c_char_p
@@ -379,26 +380,28 @@ def lowrank_factors(weight: torch.Tensor, W0: torch.Tensor, s: torch.Tensor, ran
     return U, V
 
 
-def lowrank_factors_batch(weights, W0: torch.Tensor, S: torch.Tensor, rank: int, omega: torch.Tensor,
+def lowrank_factors_batch(weights, W0s, S: torch.Tensor, rank: int, omega: torch.Tensor,
                           power_iters: int, workspace: torch.Tensor | None = None):
-    """U [n, out, rank], V [n, in, rank] (fp32) for n weights of one band (shared W0), S [n, out], omega
-    [n, in, k], via tb_lowrank_factors_batch."""
+    """U [n, out, rank], V [n, in, rank] (fp32) for n weights of one shape, each with its shared block (W0s: one
+    fp32 tensor for all, or a list of n), S [n, out], omega [n, in, k], via tb_lowrank_factors_batch."""
     n = len(weights)
     out_dim, in_dim = weights[0].shape
     k = omega.shape[2]
-    _need_cuda(W0, S, omega, *weights)
-    for t in (W0, S, omega):
+    W0s = list(W0s) if isinstance(W0s, (list, tuple)) else [W0s] * n
+    _need_cuda(S, omega, *weights, *W0s)
+    for t in (S, omega, *W0s):
         if t.dtype != torch.float32:
             raise TBError(TB_ERR_INVALID_ARGUMENT, "W0, S and omega must be fp32")
     if tuple(S.shape) != (n, out_dim) or tuple(omega.shape[:2]) != (n, in_dim):
         raise TBError(TB_ERR_INVALID_ARGUMENT, "S must be [n, out] and omega [n, in, k]")
-    U = torch.zeros((n, out_dim, rank), dtype=torch.float32, device=W0.device)
-    V = torch.zeros((n, in_dim, rank), dtype=torch.float32, device=W0.device)
+    U = torch.zeros((n, out_dim, rank), dtype=torch.float32, device=S.device)
+    V = torch.zeros((n, in_dim, rank), dtype=torch.float32, device=S.device)
     need = n * lowrank_factors_workspace_size(out_dim, in_dim, rank, k)
     ws = workspace if workspace is not None and workspace.numel() >= need else \
-        torch.empty(need, dtype=torch.uint8, device=W0.device)
+        torch.empty(need, dtype=torch.uint8, device=S.device)
     ptrs = (ctypes.c_void_p * n)(*[w.data_ptr() for w in weights])
-    _check(lib.tb_lowrank_factors_batch(ptrs, n, _ptr(W0), _ptr(S), out_dim, in_dim, rank,
+    w0p = (ctypes.c_void_p * n)(*[w.data_ptr() for w in W0s])
+    _check(lib.tb_lowrank_factors_batch(ptrs, n, w0p, _ptr(S), out_dim, in_dim, rank,
                                         _dtype_code(weights[0].dtype), _ptr(omega), k, power_iters,
                                         _ptr(U) if rank else None, _ptr(V) if rank else None, _ptr(ws), ws.numel(),
                                         _stream()))
@@ -406,9 +409,9 @@ def lowrank_factors_batch(weights, W0: torch.Tensor, S: torch.Tensor, rank: int,
 
 
 def decompose(weights, num_bands: int, rank: int, oversampling: int = 16, power_iters: int = 2, seed: int = 0,
-              batch_bytes: int = 8 << 30) -> dict:
-    """One family's theta bundle on the GPU: per band the shared block and the band's layers' row scales and
-    low-rank factors, batched (tb_lowrank_factors_batch, at most `batch_bytes` of workspace per call).  The
+              batch_bytes: int = 24 << 30) -> dict:
+    """One family's theta bundle on the GPU: per band the shared block, per layer the row scale, and the low-rank
+    factors of all layers batched (tb_lowrank_factors_batch, at most `batch_bytes` of workspace per call).  The
     randomized SVD uses k = min(rank + oversampling, out, in) and one probe per layer, drawn from a seeded normal
     generator in layer order.  Returns {"W0": [per band], "band": [per layer], "s", "U", "V": [per layer]} of
     fp32 device tensors."""
@@ -428,13 +431,12 @@ def decompose(weights, num_bands: int, rank: int, oversampling: int = 16, power_
     omegas = [torch.randn((in_dim, k), generator=gen, dtype=torch.float32) for _ in range(L)]
     per = lowrank_factors_workspace_size(out_dim, in_dim, rank, k)
     chunk = max(1, min(MAX_BAND_LAYERS, batch_bytes // per))
-    for b in range(num_bands):
-        members = [l for l in range(L) if bands[l] == b]
-        for c0 in range(0, len(members), chunk):
-            part = members[c0:c0 + chunk]
-            S = torch.stack([res["s"][l] for l in part])
-            om = torch.stack([omegas[l] for l in part]).to(dev)
-            U, V = lowrank_factors_batch([weights[l] for l in part], W0[b], S, rank, om, power_iters)
-            for j, l in enumerate(part):
-                res["U"][l], res["V"][l] = U[j], V[j]
+    for c0 in range(0, L, chunk):
+        part = list(range(c0, min(L, c0 + chunk)))
+        S = torch.stack([res["s"][l] for l in part])
+        om = torch.stack([omegas[l] for l in part]).to(dev)
+        U, V = lowrank_factors_batch([weights[l] for l in part], [W0[bands[l]] for l in part], S, rank, om,
+                                     power_iters)
+        for j, l in enumerate(part):
+            res["U"][l], res["V"][l] = U[j], V[j]
     return res

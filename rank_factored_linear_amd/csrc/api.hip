@@ -405,14 +405,15 @@ tb_status tb_lowrank_factors(const void* weight, const float* w0, const float* s
   if (rank == 0) return ok();
   const char* what = "";
   const void* const weights[1] = {weight};
-  const int e = launch_lowrank_factors(weight_dtype, weights, 1, w0, s, out_dim, in_dim, rank, omega, k, power_iters,
+  const float* const w0s[1] = {w0};
+  const int e = launch_lowrank_factors(weight_dtype, weights, 1, w0s, s, out_dim, in_dim, rank, omega, k, power_iters,
                                        u_out, v_out, workspace, cus, static_cast<hipStream_t>(stream), &what);
   if (e == -1) return fail(TB_ERR_HIP, "%s failed", what);
   if (e != 0) return hip_fail(hipError_t(e), what);
   return ok();
 }
 
-tb_status tb_lowrank_factors_batch(const void* const* weights, int32_t n, const float* w0, const float* s,
+tb_status tb_lowrank_factors_batch(const void* const* weights, int32_t n, const float* const* w0s, const float* s,
                                    int64_t out_dim, int64_t in_dim, int64_t rank, tb_dtype weight_dtype,
                                    const float* omega, int64_t k, int32_t power_iters, float* u_out, float* v_out,
                                    void* workspace, size_t workspace_bytes, void* stream) {
@@ -422,14 +423,15 @@ tb_status tb_lowrank_factors_batch(const void* const* weights, int32_t n, const 
   tb_status st = check_lowrank_dims(out_dim, in_dim, rank, k);
   if (st != TB_OK) return st;
   if (power_iters < 0 || power_iters > 16) return fail(TB_ERR_INVALID_ARGUMENT, "power_iters %d outside [0, 16]", power_iters);
-  if (!w0 || !s || !omega || !workspace)
-    return fail(TB_ERR_INVALID_ARGUMENT, "w0, s, omega and workspace must be non-NULL");
+  if (!w0s || !s || !omega || !workspace)
+    return fail(TB_ERR_INVALID_ARGUMENT, "w0s, s, omega and workspace must be non-NULL");
   if (rank > 0 && (!u_out || !v_out)) return fail(TB_ERR_INVALID_ARGUMENT, "u_out and v_out must be non-NULL");
   for (int j = 0; j < n; ++j) {
-    if (!weights[j]) return fail(TB_ERR_INVALID_ARGUMENT, "weights[%d] is NULL", j);
-    if (!aligned_to(weights[j], esize(weight_dtype))) return fail(TB_ERR_INVALID_ARGUMENT, "weights[%d] misaligned", j);
+    if (!weights[j] || !w0s[j]) return fail(TB_ERR_INVALID_ARGUMENT, "weights[%d] or w0s[%d] is NULL", j, j);
+    if (!aligned_to(weights[j], esize(weight_dtype)) || !aligned_to(w0s[j], 4))
+      return fail(TB_ERR_INVALID_ARGUMENT, "weights[%d] or w0s[%d] misaligned", j, j);
   }
-  if (!aligned_to(w0, 4) || !aligned_to(s, 4) || !aligned_to(omega, 4) || !aligned_to(u_out, 4) || !aligned_to(v_out, 4))
+  if (!aligned_to(s, 4) || !aligned_to(omega, 4) || !aligned_to(u_out, 4) || !aligned_to(v_out, 4))
     return fail(TB_ERR_INVALID_ARGUMENT, "a pointer is misaligned");
   if (!aligned_to(workspace, 256)) return fail(TB_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
   int cus = 0;
@@ -439,7 +441,7 @@ tb_status tb_lowrank_factors_batch(const void* const* weights, int32_t n, const 
     return fail(TB_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is below the %zu needed", workspace_bytes, need);
   if (rank == 0) return ok();
   const char* what = "";
-  const int e = launch_lowrank_factors(weight_dtype, weights, n, w0, s, out_dim, in_dim, rank, omega, k, power_iters,
+  const int e = launch_lowrank_factors(weight_dtype, weights, n, w0s, s, out_dim, in_dim, rank, omega, k, power_iters,
                                        u_out, v_out, workspace, cus, static_cast<hipStream_t>(stream), &what);
   if (e == -1) return fail(TB_ERR_HIP, "%s failed", what);
   if (e != 0) return hip_fail(hipError_t(e), what);

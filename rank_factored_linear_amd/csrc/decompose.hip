@@ -104,6 +104,7 @@ __device__ __forceinline__ const T* at_batch(const T* p, int64_t stride, int b) 
 
 struct WeightPtrs {
   const void* w[TB_MAX_BAND_LAYERS];
+  const float* w0[TB_MAX_BAND_LAYERS];
 };
 
 // ---- residual --------------------------------------------------------------------
@@ -111,11 +112,11 @@ struct WeightPtrs {
 // E = W - diag(s) W0 in fp32, one rounding (fma) per entry.  grid (column
 // blocks, row blocks, batch), the first two grid-stride; s is [batch][O].
 template <typename E>
-__global__ __launch_bounds__(kThreads) void residual_kernel(WeightPtrs wp, const float* __restrict__ w0,
-                                                            const float* __restrict__ s0, int64_t O, int64_t I,
-                                                            float* __restrict__ e0, int64_t stride) {
+__global__ __launch_bounds__(kThreads) void residual_kernel(WeightPtrs wp, const float* __restrict__ s0, int64_t O,
+                                                            int64_t I, float* __restrict__ e0, int64_t stride) {
   const int b = blockIdx.z;
   const E* __restrict__ w = static_cast<const E*>(wp.w[b]);
+  const float* __restrict__ w0 = wp.w0[b];
   const float* __restrict__ s = s0 + int64_t(b) * O;
   float* __restrict__ e = at_batch(e0, stride, b);
   for (int64_t o = blockIdx.y; o < O; o += gridDim.y) {
@@ -626,7 +627,7 @@ size_t lowrank_workspace_bytes(int64_t O, int64_t I, int64_t k, int64_t r, int c
   return layout(O, I, k, r, cus).total;
 }
 
-int launch_lowrank_factors(tb_dtype dtype, const void* const* weights, int n, const float* w0, const float* s,
+int launch_lowrank_factors(tb_dtype dtype, const void* const* weights, int n, const float* const* w0s, const float* s,
                            int64_t O, int64_t I, int64_t r, const float* omega, int64_t k, int power_iters,
                            float* u_out, float* v_out, void* workspace, int cus, hipStream_t stream, const char** what) {
   int dev = 0;
@@ -663,16 +664,19 @@ int launch_lowrank_factors(tb_dtype dtype, const void* const* weights, int n, co
 
   {
     WeightPtrs wp{};
-    for (int j = 0; j < n; ++j) wp.w[j] = weights[j];
+    for (int j = 0; j < n; ++j) {
+      wp.w[j] = weights[j];
+      wp.w0[j] = w0s[j];
+    }
     int64_t bx = (I + kThreads - 1) / kThreads;
     if (bx > 64) bx = 64;
     const unsigned by = unsigned(O < 4096 ? O : 4096);
     if (dtype == TB_BF16)
       hipLaunchKernelGGL(residual_kernel<bf16_t>, dim3(unsigned(bx), by, unsigned(n)), dim3(kThreads), 0, stream, wp,
-                         w0, s, O, I, E, R.stride());
+                         s, O, I, E, R.stride());
     else
       hipLaunchKernelGGL(residual_kernel<float>, dim3(unsigned(bx), by, unsigned(n)), dim3(kThreads), 0, stream, wp,
-                         w0, s, O, I, E, R.stride());
+                         s, O, I, E, R.stride());
     if (hipError_t e = hipGetLastError()) {
       *what = "residual";
       return int(e);

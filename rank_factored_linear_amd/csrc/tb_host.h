@@ -111,10 +111,10 @@ hipError_t launch_row_scale(tb_dtype dtype, const void* weight, const float* w0,
                             float* s, hipStream_t stream);
 // Bytes of one matrix's workspace slice; a batch of n takes n slices.
 size_t lowrank_workspace_bytes(int64_t out_dim, int64_t in_dim, int64_t k, int64_t rank, int cus);
-// A batch of n matrices of one shape and one W0: s [n][out], omega [n][in][k],
+// A batch of n matrices of one shape, each with its W0: s [n][out], omega [n][in][k],
 // u_out [n][out][rank], v_out [n][in][rank].  0 on success; a hipError_t
 // code, or -1 for a rocBLAS failure, with *what naming the step.
-int launch_lowrank_factors(tb_dtype dtype, const void* const* weights, int n, const float* w0, const float* s,
+int launch_lowrank_factors(tb_dtype dtype, const void* const* weights, int n, const float* const* w0s, const float* s,
                            int64_t out_dim, int64_t in_dim, int64_t rank, const float* omega, int64_t k, int power_iters,
                            float* u_out, float* v_out, void* workspace, int cus, hipStream_t stream, const char** what);
 

@@ -162,6 +162,20 @@ def test_decomposition_rejects_before_launch():
     assert call(a6=4) == 1                     # dtype
     assert call(a3=1 << 20, a4=1 << 12) == 2   # out * in >= 2^31
     assert call(a3=600, a4=600, a8=513, a5=8) == 2   # k above the widest probe
+    lb = lib.tb_lowrank_factors_batch
+    w3 = (ctypes.c_void_p * 3)(FAKE, FAKE, FAKE)
+    w0_bad = (ctypes.c_void_p * 3)(FAKE, None, FAKE)
+    bargs = [w3, 3, w3, FAKE, 64, 48, 8, 1, FAKE, 16, 2, FAKE, FAKE, FAKE, 1 << 30, None]
+
+    def bcall(**changes):
+        a = list(bargs)
+        for k, v in changes.items():
+            a[int(k[1:])] = v
+        return lb(*a)
+    assert bcall(a0=None) == 1 and bcall(a2=None) == 1
+    assert bcall(a1=0) == 1 and bcall(a1=binding.MAX_BAND_LAYERS + 1) == 1
+    assert bcall(a2=w0_bad) == 1                # a NULL shared block
+    assert bcall(a6=17) == 1 and bcall(a10=17) == 1
     out = ctypes.c_size_t(0)
     assert lib.tb_lowrank_factors_workspace_size(64, 48, 20, 16, ctypes.byref(out)) == 1
     assert lib.tb_lowrank_factors_workspace_size(64, 48, 8, 16, None) == 1
