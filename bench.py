@@ -84,6 +84,9 @@ def parse():
                     help="forward stacks: rebuild every layer's weight once in bf16 (outside the timed region) and "
                          "time the dense projections of the materialise-once mode (tb_dense_forward semantics)")
     ap.add_argument("--power-iters", type=int, default=2, help="decompose*: power iterations of the randomized SVD")
+    ap.add_argument("--tie-families", choices=["all", "attn"], default="all",
+                    help="forward stacks: 'attn' shares W0 for the attention families only and keeps the MLP "
+                         "projections as dense weights (rank 0, no scale, tb_dense_forward semantics)")
     ap.add_argument("--replicas", type=int, default=None,
                     help="rotating pool of input replicas (default: enough for >= 1 GiB when the stack is small)")
     ap.add_argument("--no-graph", action="store_true", help="skip the captured-graph leg")
@@ -340,13 +343,16 @@ def bench_forward(args, torch, np, tb, gen):
                 bundles[(l, fam)] = gen.device_bundle(torch, wl["seed"], fam, shapes, l, band_of[l], R, with_w0=False)
             xs[(l, fam)] = gen.device_activations(torch, wl["seed"], fam, shapes, l, M)
 
-    # Materialise-once mode: W = diag(s) W0 + U V^T per layer, rebuilt once in
-    # bf16; each call is then a dense projection (no scale, rank 0).
+    # Materialise-once mode (every family) and tie_families="attn" (the MLP
+    # families): W = diag(s) W0 + U V^T per layer, rebuilt once in bf16; each
+    # such call is a dense projection (no scale, rank 0).
+    dense_fams = set(gen.FAMILIES) if args.materialised else (
+        {"gate_proj", "up_proj", "down_proj"} if args.tie_families == "attn" else set())
     dense = None
-    if args.materialised:
+    if dense_fams:
         dense = {}
         for l in range(L):
-            for fam in gen.FAMILIES:
+            for fam in sorted(dense_fams):
                 bd = bundles[(l, fam)]
                 dense[(l, fam)] = tb.reconstruct_weight(bd["s"], W0[(band_of[l], fam)], bd["U"] if R else None,
                                                         bd["V"] if R else None, out_dtype=torch.bfloat16)
@@ -355,22 +361,19 @@ def bench_forward(args, torch, np, tb, gen):
     def nbytes(t):
         return 0 if t is None else t.numel() * t.element_size()
 
-    if dense is not None:
-        distinct = sum(nbytes(t) for t in dense.values())
-    else:
-        distinct = sum(nbytes(t) for t in W0.values()) + sum(nbytes(v) for bd in bundles.values() for v in bd.values())
+    distinct = (sum(nbytes(t) for t in (dense or {}).values()) +
+                sum(nbytes(t) for k, t in W0.items() if k[1] not in dense_fams) +
+                sum(nbytes(v) for k, bd in bundles.items() if k[1] not in dense_fams for v in bd.values()))
     replicas = args.replicas
     if replicas is None:
         replicas = 1 if distinct >= 2 * CACHE_BYTES else math.ceil(COLD_POOL_BYTES / distinct)
     # Replica r > 0 holds copies of every weight tensor at addresses of its own; x is shared.
     pools = [(W0, bundles, dense)]
     for _ in range(1, replicas):
-        if dense is not None:
-            pools.append((W0, bundles, {k: t.clone() for k, t in dense.items()}))
-        else:
-            pools.append(({k: t.clone() for k, t in W0.items()},
-                          {k: {n: (None if t is None else t.clone()) for n, t in bd.items()} for k, bd in bundles.items()},
-                          None))
+        pools.append(({k: t.clone() for k, t in W0.items() if k[1] not in dense_fams},
+                      {k: {n: (None if t is None else t.clone()) for n, t in bd.items()}
+                       for k, bd in bundles.items() if k[1] not in dense_fams},
+                      None if dense is None else {k: t.clone() for k, t in dense.items()}))
 
     ys = {fam: torch.empty((M, shapes[fam][0]), dtype=torch.bfloat16, device=dev) for fam in gen.FAMILIES}
     # Projections that take the same layer input go in one grouped call.
@@ -378,7 +381,7 @@ def bench_forward(args, torch, np, tb, gen):
     ws_need = []
     for grp in groups:
         dims = (tb.Projection * len(grp))(*[tb.Projection(None, None, None, None, None, None, *shapes[f],
-                                                          0 if dense is not None else R) for f in grp])
+                                                          0 if f in dense_fams else R) for f in grp])
         nb = ctypes.c_size_t(0)
         assert tb.lib.tb_linear_forward_group_workspace_size(len(grp), dims, M, tb.TB_BF16, ctypes.byref(nb)) == 0
         ws_need.append(nb.value)
@@ -398,16 +401,16 @@ def bench_forward(args, torch, np, tb, gen):
             for grp in groups:
                 members = []
                 for fam in grp:
-                    bd = bundlesp[(l, fam)]
-                    if dense is not None:
+                    if fam in dense_fams:
                         members.append((xs[(l, fam)], None, densep[(l, fam)], None, None, ys[fam]))
                     else:
+                        bd = bundlesp[(l, fam)]
                         members.append((xs[(l, fam)], bd["s"], W0p[(band_of[l], fam)], bd["U"] if R else None,
                                         bd["V"] if R else None, ys[fam]))
                 if len(grp) == 1:
                     x, s_, w0, u, v, y = members[0]
                     O, I = shapes[grp[0]]
-                    Rc = R if dense is None else 0
+                    Rc = 0 if grp[0] in dense_fams else R
                     argv = (x.data_ptr(), None if s_ is None else s_.data_ptr(), w0.data_ptr(),
                             u.data_ptr() if Rc else None, v.data_ptr() if Rc else None, y.data_ptr(), M, O, I, Rc,
                             tb.TB_BF16, ws.data_ptr(), ws.numel(), stream)
@@ -442,12 +445,10 @@ def bench_forward(args, torch, np, tb, gen):
     calls = pool_calls[0]
 
     def grp_bytes(grp):
-        if dense is not None:
-            return sum(dense_call_bytes(M, *shapes[f]) for f in grp)
-        return sum(call_bytes(M, *shapes[f], R) for f in grp)
+        return sum(dense_call_bytes(M, *shapes[f]) if f in dense_fams else call_bytes(M, *shapes[f], R) for f in grp)
 
     def grp_flops(grp):
-        return sum(call_flops(M, *shapes[f], 0 if dense is not None else R) for f in grp)
+        return sum(call_flops(M, *shapes[f], 0 if f in dense_fams else R) for f in grp)
 
     step_bytes = sum(grp_bytes(c[1]) for c in calls)
     step_flops = sum(grp_flops(c[1]) for c in calls)
@@ -532,8 +533,9 @@ def bench_forward(args, torch, np, tb, gen):
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {L}-layer stack, 7 projections per layer, rank {R}, "
                                f"G={G} bands, {M} tokens"
-                               + (", materialised once (dense bf16 weights)" if dense is not None else ""),
-                   "materialised": dense is not None,
+                               + (", materialised once (dense bf16 weights)" if args.materialised else
+                                  ", tie_families=attn (MLP dense)" if dense_fams else ""),
+                   "materialised": args.materialised, "tie_families": args.tie_families,
                    "layers": L, "projections_per_step": L * len(gen.FAMILIES),
                    "grouping": "+".join(",".join(f.split("_")[0] for f in g) for g in groups),
                    "rank": R, "bands": G, "tokens": M,

@@ -54,3 +54,17 @@ def test_fused_error_bytes():
     assert bench.fused_error_bytes(O, I, R) == 2 * (O * I + R * (O + I) + O) + 4 * O * I
     ratio = (bench.reconstruct_bytes(O, I, R) + bench.frobenius_bytes(O, I)) / bench.fused_error_bytes(O, I, R)
     assert 2.2 < ratio < 2.35
+
+
+def test_dense_call_bytes():
+    # A materialised weight streams O x I alone: the bundle's extra bytes are U, V and s.
+    M, O, I, R = 16, 8192, 5376, 256
+    assert bench.dense_call_bytes(M, O, I) == 2 * (O * I + M * (I + O))
+    assert bench.call_bytes(M, O, I, R) - bench.dense_call_bytes(M, O, I) == 2 * (R * (O + I) + O)
+    assert bench.call_flops(M, O, I, 0) == 2 * M * O * I
+
+
+def test_decompose_workloads_are_declared():
+    for name in ("decompose26", "decompose60"):
+        wl = bench.WORKLOADS[name]
+        assert wl["rank"] > 0 and 1 <= wl["bands"] <= wl["layers"]
