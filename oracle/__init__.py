@@ -21,5 +21,7 @@ from .theta_bundle import (  # noqa: F401
     orthonormal_basis,
     randomized_factors,
     decompose,
+    refine_shared_block,
+    als_decompose,
     decomposition_error,
 )

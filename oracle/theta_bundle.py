@@ -311,6 +311,52 @@ def decompose(weights, num_bands: int, rank: int) -> dict:
     return out
 
 
+def refine_shared_block(weights, s_list, U_list, V_list, W0_prev: np.ndarray) -> np.ndarray:
+    """One least-squares update of a band's shared block with the per-layer
+    scale and delta held fixed: the alternating least squares the "Quality"
+    page reports on (Research: why shared configurations need training).
+
+    W0 minimises sum_l ||W_l - diag(s_l) W0 - U_l V_l^T||_F^2 over the band's
+    layers; row by row the minimiser is
+        W0[o] = sum_l s_l[o] (W_l - U_l V_l^T)[o] / sum_l s_l[o]^2.
+    Reading (not on the pages): a row whose scales are all zero has no least-
+    squares information and keeps its previous value.
+    """
+    W0_prev = np.asarray(W0_prev, dtype=np.float64)
+    num = np.zeros_like(W0_prev)
+    den = np.zeros(W0_prev.shape[0])
+    for w, sl, U, V in zip(weights, s_list, U_list, V_list):
+        w, sl, U, V = (np.asarray(a, dtype=np.float64) for a in (w, sl, U, V))
+        num += sl[:, None] * (w - U @ V.T)
+        den += sl * sl
+    out = W0_prev.copy()
+    rows = den != 0.0
+    out[rows] = num[rows] / den[rows][:, None]
+    return out
+
+
+def als_decompose(weights, num_bands: int, rank: int, iters: int) -> dict:
+    """The analytic decomposition followed by `iters` rounds of alternating
+    least squares: each round refits every band's W0 with s, U, V fixed
+    (refine_shared_block), then every layer's s and U, V against the new W0
+    exactly as the analytic decomposition does (row_scale, truncated_factors)."""
+    weights = [np.asarray(w, dtype=np.float64) for w in weights]
+    bun = decompose(weights, num_bands, rank)
+    bands = bun["band"]
+    for _ in range(iters):
+        for b in range(num_bands):
+            members = [l for l in range(len(weights)) if bands[l] == b]
+            bun["W0"][b] = refine_shared_block([weights[l] for l in members], [bun["s"][l] for l in members],
+                                               [bun["U"][l] for l in members], [bun["V"][l] for l in members],
+                                               bun["W0"][b])
+        for l, w in enumerate(weights):
+            w0 = bun["W0"][bands[l]]
+            s = row_scale(w, w0)
+            U, V = truncated_factors(w - np.diag(s) @ w0, rank)
+            bun["s"][l], bun["U"][l], bun["V"][l] = s, U, V
+    return bun
+
+
 def decomposition_error(weights, bundle: dict) -> list[float]:
     """Per-layer relative Frobenius error of the rebuilt weights."""
     errs = []

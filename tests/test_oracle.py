@@ -197,6 +197,42 @@ def check_randomized_factors(impl) -> None:
         assert np.sqrt(np.sum((Rm - U @ V.T) ** 2)) <= 1.0001 * np.sqrt(tail2)
 
 
+def check_refine_shared_block(impl) -> None:
+    r = np.random.default_rng(12)
+    O, I, R, n = 5, 7, 2, 3
+    Ws = [r.normal(size=(O, I)) for _ in range(n)]
+    ss = [r.uniform(0.5, 1.5, size=O) for _ in range(n)]
+    Us = [r.normal(size=(O, R)) for _ in range(n)]
+    Vs = [r.normal(size=(I, R)) for _ in range(n)]
+    prev = r.normal(size=(O, I))
+    ss[1][2] = 0.0
+    W0 = impl.refine_shared_block(Ws, ss, Us, Vs, prev)
+    for o in range(O):
+        # Normal equations of min_x sum_l |(W_l - U_l V_l^T)[o] - s_l[o] x|^2 ...
+        g = sum(ss[l][o] * (Ws[l] - ss[l][o] * W0 - Us[l] @ Vs[l].T)[o] for l in range(n))
+        assert np.max(np.abs(g)) <= 1e-12
+        # ... and a library least-squares solve of the stacked system.
+        A = np.vstack([ss[l][o] * np.eye(I) for l in range(n)])
+        b = np.concatenate([(Ws[l] - Us[l] @ Vs[l].T)[o] for l in range(n)])
+        assert np.allclose(W0[o], np.linalg.lstsq(A, b, rcond=None)[0], rtol=1e-12, atol=1e-13)
+    # A row whose scales are all zero keeps its previous value.
+    zs = [s.copy() for s in ss]
+    for s in zs:
+        s[4] = 0.0
+    assert np.array_equal(impl.refine_shared_block(Ws, zs, Us, Vs, prev)[4], prev[4])
+    # Consistent data W_l = diag(s_l) B + U_l V_l^T: the block is recovered exactly.
+    B = r.normal(size=(O, I))
+    Wc = [np.diag(ss[l]) @ B + Us[l] @ Vs[l].T for l in range(n)]
+    assert np.max(np.abs(impl.refine_shared_block(Wc, ss, Us, Vs, prev) - B)) <= 1e-12
+    # ALS with no rounds is the analytic decomposition; passthrough is a fixed point.
+    w, _ = inputs.tiny_stack()
+    a0, d0 = impl.als_decompose(w, 2, 4, 0), impl.decompose(w, 2, 4)
+    assert all(np.array_equal(x, y) for x, y in zip(a0["W0"], d0["W0"]))
+    a2 = impl.als_decompose(w, 4, 0, 2)
+    for l in range(4):
+        assert np.max(np.abs(a2["W0"][a2["band"][l]] - w[l])) <= 1e-15 and np.allclose(a2["s"][l], 1.0, atol=1e-15)
+
+
 def check_decompose(impl) -> None:
     r = np.random.default_rng(10)
     # Passthrough (G = L): W0 = W, s = 1 exactly, delta 0 and error exactly 0.
@@ -227,7 +263,8 @@ def check_decompose(impl) -> None:
 
 
 ALL_CHECKS = [check_band_map, check_forward, check_reconstruct, check_frobenius,
-              check_row_scale, check_truncated_factors, check_randomized_factors, check_decompose]
+              check_row_scale, check_truncated_factors, check_randomized_factors, check_refine_shared_block,
+              check_decompose]
 
 
 # ---------------------------------------------------------------------------
@@ -445,6 +482,19 @@ def _rand_plain_powers(residual, rank, omega, power_iters):
     return Q @ (P[:, :rank] * sg[:rank][None, :]), Qt[:rank].T
 
 
+def _refine_by_sum_of_scales(weights, s_list, U_list, V_list, W0_prev):
+    num = sum(sl[:, None] * (w - U @ V.T) for w, sl, U, V in zip(weights, s_list, U_list, V_list))
+    den = sum(s_list)
+    out = np.array(W0_prev, dtype=np.float64)
+    rows = den != 0
+    out[rows] = num[rows] / den[rows][:, None]
+    return out
+
+
+def _refine_without_delta(weights, s_list, U_list, V_list, W0_prev):
+    return tb.refine_shared_block(weights, s_list, [0 * U for U in U_list], V_list, W0_prev)
+
+
 MUTANTS = [
     ("band remainder to the last bands", check_band_map,
      dict(band_sizes=_remainder_last_sizes, band_map=_remainder_last_map,
@@ -454,6 +504,10 @@ MUTANTS = [
     ("s ratio swapped", check_row_scale, dict(row_scale=_swapped_row_scale)),
     ("s normalised by the weight row", check_row_scale, dict(row_scale=_input_dot_row_scale)),
     ("V absorbs the singular values", check_truncated_factors, dict(truncated_factors=_v_absorbs)),
+    ("ALS: block normalised by the sum of scales", check_refine_shared_block,
+     dict(refine_shared_block=_refine_by_sum_of_scales)),
+    ("ALS: delta left out of the block update", check_refine_shared_block,
+     dict(refine_shared_block=_refine_without_delta)),
     ("randomized: V absorbs the singular values", check_randomized_factors, dict(randomized_factors=_rand_v_absorbs)),
     ("randomized: singular values dropped", check_randomized_factors, dict(randomized_factors=_rand_sigma_dropped)),
     ("randomized: probe without oversampling", check_randomized_factors,
