@@ -84,6 +84,8 @@ def parse():
                     help="forward stacks: rebuild every layer's weight once in bf16 (outside the timed region) and "
                          "time the dense projections of the materialise-once mode (tb_dense_forward semantics)")
     ap.add_argument("--power-iters", type=int, default=2, help="decompose*: power iterations of the randomized SVD")
+    ap.add_argument("--als-iters", type=int, default=0,
+                    help="decompose*: also time this many rounds of alternating least squares on the shared blocks")
     ap.add_argument("--tie-families", choices=["all", "attn"], default="all",
                     help="forward stacks: 'attn' shares W0 for the attention families only and keeps the MLP "
                          "projections as dense weights (rank 0, no scale, tb_dense_forward semantics)")
@@ -845,6 +847,21 @@ def bench_decompose(args, torch, np, tb, gen):
             e = tb.reconstruction_error(originals[fam][l], b["s"][l], b["W0"][b["band"][l]], b["U"][l], b["V"][l])
             errs.append(float(e.item()))
     del bundles
+    als = None
+    if args.als_iters > 0:
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        refined = {fam: tb.als_decompose(originals[fam], G, R, args.als_iters, power_iters=q, seed=seed)
+                   for fam in gen.FAMILIES}
+        ev[1].record()
+        torch.cuda.synchronize()
+        als_errs = [float(tb.reconstruction_error(originals[fam][l], b["s"][l], b["W0"][b["band"][l]], b["U"][l],
+                                                  b["V"][l]).item())
+                    for fam, b in refined.items() for l in range(L)]
+        als = {"iters": args.als_iters, "ms_incl_decomposition": round(ev[0].elapsed_time(ev[1]), 1),
+               "mean_rel_error": float(np.mean(als_errs))}
+        del refined
     value = orig_bytes / (ms * 1e-3) / 1e9
     achieved = gemm_flops / (ms * 1e-3) / 1e12
     line = {
@@ -859,7 +876,7 @@ def bench_decompose(args, torch, np, tb, gen):
                    "layers": L, "bands": G, "rank": R, "power_iters": q,
                    "matrices": L * len(gen.FAMILIES), "original_bytes": orig_bytes,
                    "matrices_per_s": round(L * len(gen.FAMILIES) / (ms * 1e-3), 2),
-                   "mean_rel_error": float(np.mean(errs)), "parallelism": "single-gpu"},
+                   "mean_rel_error": float(np.mean(errs)), "als": als, "parallelism": "single-gpu"},
         "trials": spread(per_step),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / FP32_PEAK_TFLOPS, 4), "traffic": None,

@@ -316,6 +316,32 @@ tb_status tb_lowrank_factors_batch(const void *const *weights, int32_t n, const 
                                    const float *omega, int64_t k, int32_t power_iters, float *u_out, float *v_out,
                                    void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * tb_refine_shared_block -- one least-squares refit of a band's shared block
+ * with each layer's scale and factors held fixed, the alternating least
+ * squares the "Quality" page reports on (Research: why shared configurations
+ * need training): row by row
+ *     W0[o] = sum_l s_l[o] (W_l - U_l V_l^T)[o] / sum_l s_l[o]^2,
+ * and a row whose scales are all zero keeps its w0_prev value (a reading).
+ * num = sum_l diag(s_l) W_l in fp64 sums (layer order, rounded to fp32),
+ * minus the n layers' deltas as one fp32 GEMM of inner dimension n * rank
+ * (rocBLAS), then the division in fp64.
+ *   weights: HOST array of n DEVICE pointers ([out_dim, in_dim], weight_dtype);
+ *   s, u, v: HOST arrays of n DEVICE fp32 pointers ([out_dim], [out_dim,
+ *   rank], [in_dim, rank]; u, v may be NULL when rank is 0); w0_prev, w0_out:
+ *   device fp32 [out_dim, in_dim] (they may be the same buffer).
+ *   1 <= n <= TB_MAX_BAND_LAYERS, 0 <= rank <= TB_MAX_PROBE, out_dim *
+ *   in_dim < 2^31.  workspace: tb_refine_shared_block_workspace_size()
+ *   bytes, 256-byte aligned.  Errors: TB_ERR_INVALID_ARGUMENT,
+ *   TB_ERR_UNSUPPORTED, TB_ERR_HIP.
+ */
+tb_status tb_refine_shared_block_workspace_size(int64_t out_dim, int64_t in_dim, int32_t n, int64_t rank,
+                                                size_t *bytes_out);
+tb_status tb_refine_shared_block(const void *const *weights, const float *const *s, const float *const *u,
+                                 const float *const *v, int32_t n, int64_t out_dim, int64_t in_dim, int64_t rank,
+                                 tb_dtype weight_dtype, const float *w0_prev, float *w0_out, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *tb_status_string(tb_status status);
 

@@ -28,7 +28,7 @@ EXPORTED = (
     "tb_linear_forward_group_workspace_size", "tb_linear_forward_group",
     "tb_reconstruct_weight", "tb_rel_frobenius_error", "tb_reconstruction_error",
     "tb_shared_block", "tb_row_scale", "tb_lowrank_factors_workspace_size", "tb_lowrank_factors",
-    "tb_lowrank_factors_batch",
+    "tb_lowrank_factors_batch", "tb_refine_shared_block_workspace_size", "tb_refine_shared_block",
     "tb_status_string", "tb_last_error",
 )
 MAX_BAND_LAYERS = 128
@@ -72,6 +72,10 @@ def _load() -> ctypes.CDLL:
     lib.tb_lowrank_factors_batch.argtypes = [ctypes.POINTER(c_p), c_i32, ctypes.POINTER(c_p), c_p, c_i64, c_i64, c_i64,
                                              ctypes.c_int, c_p,
                                              c_i64, c_i32, c_p, c_p, c_p, c_sz, c_p]
+    lib.tb_refine_shared_block_workspace_size.argtypes = [c_i64, c_i64, c_i32, c_i64, ctypes.POINTER(c_sz)]
+    lib.tb_refine_shared_block.argtypes = [ctypes.POINTER(c_p), ctypes.POINTER(c_p), ctypes.POINTER(c_p),
+                                           ctypes.POINTER(c_p), c_i32, c_i64, c_i64, c_i64, ctypes.c_int, c_p, c_p,
+                                           c_p, c_sz, c_p]
     lib.tb_status_string.argtypes = [ctypes.c_int]
     lib.tb_status_string.restype = ctypes.c_char_p
     lib.tb_last_error.argtypes = []
@@ -440,3 +444,52 @@ def decompose(weights, num_bands: int, rank: int, oversampling: int = 16, power_
         for j, l in enumerate(part):
             res["U"][l], res["V"][l] = U[j], V[j]
     return res
+
+
+def refine_shared_block(weights, s_list, U_list, V_list, W0_prev: torch.Tensor,
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """Least-squares refit of a band's shared block with every layer's s, U, V fixed (fp32), via
+    tb_refine_shared_block; `out` may be W0_prev itself."""
+    n = len(weights)
+    out_dim, in_dim = W0_prev.shape
+    rank = 0 if U_list[0] is None else U_list[0].shape[1]
+    _need_cuda(W0_prev, out, *weights, *s_list, *(U_list if rank else []), *(V_list if rank else []))
+    if out is None:
+        out = torch.empty_like(W0_prev)
+    arr = lambda ts: (ctypes.c_void_p * n)(*[t.data_ptr() for t in ts])
+    need = ctypes.c_size_t(0)
+    _check(lib.tb_refine_shared_block_workspace_size(out_dim, in_dim, n, rank, ctypes.byref(need)))
+    ws = torch.empty(need.value, dtype=torch.uint8, device=W0_prev.device)
+    _check(lib.tb_refine_shared_block(arr(weights), arr(s_list), arr(U_list) if rank else None,
+                                      arr(V_list) if rank else None, n, out_dim, in_dim, rank,
+                                      _dtype_code(weights[0].dtype), _ptr(W0_prev), _ptr(out), _ptr(ws), ws.numel(),
+                                      _stream()))
+    return out
+
+
+def als_decompose(weights, num_bands: int, rank: int, iters: int, oversampling: int = 16, power_iters: int = 2,
+                  seed: int = 0) -> dict:
+    """decompose() followed by `iters` rounds of alternating least squares: every band's W0 refitted with s, U, V
+    fixed (refine_shared_block), then every layer's s and U, V against the new W0 (new probes per round)."""
+    bun = decompose(weights, num_bands, rank, oversampling, power_iters, seed)
+    L = len(weights)
+    bands = bun["band"]
+    out_dim, in_dim = weights[0].shape
+    dev = weights[0].device
+    k = min(rank + oversampling, out_dim, in_dim, MAX_PROBE)
+    for it in range(iters):
+        for b in range(num_bands):
+            mem = [l for l in range(L) if bands[l] == b]
+            refine_shared_block([weights[l] for l in mem], [bun["s"][l] for l in mem],
+                                [bun["U"][l] if rank else None for l in mem],
+                                [bun["V"][l] if rank else None for l in mem], bun["W0"][b], out=bun["W0"][b])
+        bun["s"] = [row_scale(weights[l], bun["W0"][bands[l]]) for l in range(L)]
+        if rank:
+            gen = torch.Generator(device="cpu").manual_seed(seed + 1 + it)
+            om = torch.stack([torch.randn((in_dim, k), generator=gen, dtype=torch.float32) for _ in range(L)]).to(dev)
+            U, V = lowrank_factors_batch(weights, [bun["W0"][bands[l]] for l in range(L)], torch.stack(bun["s"]), rank,
+                                         om, power_iters)
+            bun["U"] = [U[l] for l in range(L)]
+            bun["V"] = [V[l] for l in range(L)]
+    return bun
+

@@ -448,6 +448,48 @@ tb_status tb_lowrank_factors_batch(const void* const* weights, int32_t n, const 
   return ok();
 }
 
+tb_status tb_refine_shared_block_workspace_size(int64_t out_dim, int64_t in_dim, int32_t n, int64_t rank,
+                                                size_t* bytes_out) {
+  if (!bytes_out) return fail(TB_ERR_INVALID_ARGUMENT, "bytes_out is NULL");
+  if (out_dim < 1 || in_dim < 1 || rank < 0) return fail(TB_ERR_INVALID_ARGUMENT, "need out_dim, in_dim >= 1, rank >= 0");
+  if (n < 1 || n > TB_MAX_BAND_LAYERS) return fail(TB_ERR_INVALID_ARGUMENT, "n %d outside [1, %d]", n, TB_MAX_BAND_LAYERS);
+  *bytes_out = refine_workspace_bytes(out_dim, in_dim, n, rank);
+  return ok();
+}
+
+tb_status tb_refine_shared_block(const void* const* weights, const float* const* s, const float* const* u,
+                                 const float* const* v, int32_t n, int64_t out_dim, int64_t in_dim, int64_t rank,
+                                 tb_dtype weight_dtype, const float* w0_prev, float* w0_out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(weight_dtype)) return fail(TB_ERR_INVALID_ARGUMENT, "unknown dtype %d", int(weight_dtype));
+  if (!weights || !s || !w0_prev || !w0_out || !workspace)
+    return fail(TB_ERR_INVALID_ARGUMENT, "weights, s, w0_prev, w0_out and workspace must be non-NULL");
+  if (n < 1 || n > TB_MAX_BAND_LAYERS) return fail(TB_ERR_INVALID_ARGUMENT, "n %d outside [1, %d]", n, TB_MAX_BAND_LAYERS);
+  if (out_dim < 1 || in_dim < 1 || rank < 0) return fail(TB_ERR_INVALID_ARGUMENT, "need out_dim, in_dim >= 1, rank >= 0");
+  if (out_dim >= (int64_t(1) << 31) / in_dim || rank > TB_MAX_PROBE)
+    return fail(TB_ERR_UNSUPPORTED, "out_dim * in_dim must stay below 2^31 and rank at most %d", TB_MAX_PROBE);
+  if (rank > 0 && (!u || !v)) return fail(TB_ERR_INVALID_ARGUMENT, "u and v must be non-NULL when rank > 0");
+  for (int j = 0; j < n; ++j) {
+    if (!weights[j] || !s[j] || (rank > 0 && (!u[j] || !v[j])))
+      return fail(TB_ERR_INVALID_ARGUMENT, "member %d has a NULL pointer", j);
+    if (!aligned_to(weights[j], esize(weight_dtype)) || !aligned_to(s[j], 4) ||
+        (rank > 0 && (!aligned_to(u[j], 4) || !aligned_to(v[j], 4))))
+      return fail(TB_ERR_INVALID_ARGUMENT, "member %d is misaligned", j);
+  }
+  if (!aligned_to(w0_prev, 4) || !aligned_to(w0_out, 4) || !aligned_to(workspace, 256))
+    return fail(TB_ERR_INVALID_ARGUMENT, "w0_prev, w0_out or workspace misaligned");
+  if (workspace_bytes < refine_workspace_bytes(out_dim, in_dim, n, rank))
+    return fail(TB_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is below the %zu needed", workspace_bytes,
+                refine_workspace_bytes(out_dim, in_dim, n, rank));
+  const char* what = "";
+  const int e = launch_refine_shared_block(weight_dtype, weights, s, rank > 0 ? u : nullptr, rank > 0 ? v : nullptr, n,
+                                           out_dim, in_dim, rank, w0_prev, w0_out, workspace,
+                                           static_cast<hipStream_t>(stream), &what);
+  if (e == -1) return fail(TB_ERR_HIP, "%s failed", what);
+  if (e != 0) return hip_fail(hipError_t(e), what);
+  return ok();
+}
+
 const char* tb_status_string(tb_status status) {
   switch (status) {
     case TB_OK: return "ok";

@@ -128,6 +128,60 @@ __global__ __launch_bounds__(kThreads) void residual_kernel(WeightPtrs wp, const
   }
 }
 
+// ---- least-squares refit of a shared block (alternating least squares) -------------
+//
+// W0[o] = sum_l s_l[o] (W_l - U_l V_l^T)[o] / sum_l s_l[o]^2, as
+//   num = sum_l diag(s_l) W_l             (scaled_sum_kernel, fp64 sums in layer order)
+//   num -= [s_1 U_1 | ... | s_n U_n] [V_1 | ... | V_n]^T   (one GEMM, inner dimension n r)
+//   W0 = num / den, den[o] = sum_l s_l[o]^2, or the previous row where den is 0.
+
+struct RefinePtrs {
+  const void* w[TB_MAX_BAND_LAYERS];
+  const float* s[TB_MAX_BAND_LAYERS];
+};
+
+template <typename E>
+__global__ __launch_bounds__(kThreads) void scaled_sum_kernel(RefinePtrs rp, int n, int64_t O, int64_t I,
+                                                              float* __restrict__ num) {
+  const int64_t count = O * I, stride = int64_t(gridDim.x) * kThreads;
+  for (int64_t at = int64_t(blockIdx.x) * kThreads + threadIdx.x; at < count; at += stride) {
+    const int64_t o = at / I;
+    double acc = 0.0;
+    for (int l = 0; l < n; ++l) acc += double(rp.s[l][o]) * double(to_f32<E>(static_cast<const E*>(rp.w[l])[at]));
+    num[at] = float(acc);
+  }
+}
+
+// Ucat [O][n r] = s_l[o] U_l[o][j] at column l r + j; Vcat [I][n r] = V_l[i][j].
+struct FactorPtrs {
+  const float* u[TB_MAX_BAND_LAYERS];
+  const float* v[TB_MAX_BAND_LAYERS];
+  const float* s[TB_MAX_BAND_LAYERS];
+};
+
+__global__ __launch_bounds__(kThreads) void pack_factors_kernel(FactorPtrs fp, int n, int64_t O, int64_t I, int r,
+                                                                float* __restrict__ ucat, float* __restrict__ vcat) {
+  const int64_t nr = int64_t(n) * r, total = (O + I) * nr, stride = int64_t(gridDim.x) * kThreads;
+  for (int64_t at = int64_t(blockIdx.x) * kThreads + threadIdx.x; at < total; at += stride) {
+    const int64_t row = at / nr, c = at % nr;
+    const int l = int(c / r), j = int(c % r);
+    if (row < O) ucat[at] = fp.s[l][row] * fp.u[l][row * r + j];
+    else vcat[at - O * nr] = fp.v[l][(row - O) * r + j];
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void refine_finish_kernel(RefinePtrs rp, int n, int64_t O, int64_t I,
+                                                                 const float* __restrict__ num,
+                                                                 const float* __restrict__ prev,
+                                                                 float* __restrict__ out) {
+  for (int64_t o = blockIdx.y; o < O; o += gridDim.y) {
+    double den = 0.0;
+    for (int l = 0; l < n; ++l) den += double(rp.s[l][o]) * double(rp.s[l][o]);
+    for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < I; i += int64_t(gridDim.x) * kThreads)
+      out[o * I + i] = den != 0.0 ? float(double(num[o * I + i]) / den) : prev[o * I + i];
+  }
+}
+
 // ---- Gram matrix C = A^T A (fp64) -------------------------------------------------
 
 // Upper tile (ta <= tb) number `t` of a T x T tile grid.
@@ -471,6 +525,16 @@ struct Blas {
 };
 Blas g_blas;
 
+// The handle of (dev, stream), created on first use; the caller holds g_blas.mu.
+rocblas_handle handle_for(int dev, hipStream_t stream) {
+  for (const auto& e : g_blas.handles)
+    if (e.dev == dev && e.stream == stream) return e.h;
+  rocblas_handle h = nullptr;
+  if (rocblas_create_handle(&h) != rocblas_status_success) return nullptr;
+  g_blas.handles.push_back({dev, stream, h});
+  return h;
+}
+
 // Row-major C [M x N] = op(A) op(B) with A [M x K] (or [K x M] when ta) and
 // B [K x N] (or [N x K] when tb): the column-major product C^T = op(B)^T op(A)^T.
 rocblas_status gemm_rm(rocblas_handle h, bool ta, bool tb, int M, int N, int K, const float* A, int lda,
@@ -623,6 +687,76 @@ hipError_t launch_row_scale(tb_dtype dtype, const void* weight, const float* w0,
   return hipGetLastError();
 }
 
+size_t refine_workspace_bytes(int64_t O, int64_t I, int64_t n, int64_t r) {
+  return align256(size_t(O) * I * 4) + align256(size_t(O) * n * r * 4) + align256(size_t(I) * n * r * 4);
+}
+
+int launch_refine_shared_block(tb_dtype dtype, const void* const* weights, const float* const* s,
+                               const float* const* u, const float* const* v, int n, int64_t O, int64_t I, int64_t r,
+                               const float* prev, float* out, void* workspace, hipStream_t stream, const char** what) {
+  char* ws = static_cast<char*>(workspace);
+  float* num = reinterpret_cast<float*>(ws);
+  float* ucat = reinterpret_cast<float*>(ws + align256(size_t(O) * I * 4));
+  float* vcat = reinterpret_cast<float*>(ws + align256(size_t(O) * I * 4) + align256(size_t(O) * n * r * 4));
+  RefinePtrs rp{};
+  FactorPtrs fp{};
+  for (int j = 0; j < n; ++j) {
+    rp.w[j] = weights[j];
+    rp.s[j] = fp.s[j] = s[j];
+    fp.u[j] = u ? u[j] : nullptr;
+    fp.v[j] = v ? v[j] : nullptr;
+  }
+  int64_t blocks = (O * I + kThreads - 1) / kThreads;
+  if (blocks > 65536) blocks = 65536;
+  if (dtype == TB_BF16)
+    hipLaunchKernelGGL(scaled_sum_kernel<bf16_t>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, rp, n, O, I, num);
+  else
+    hipLaunchKernelGGL(scaled_sum_kernel<float>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, rp, n, O, I, num);
+  if (hipError_t e = hipGetLastError()) {
+    *what = "scaled sum";
+    return int(e);
+  }
+  if (r > 0) {
+    int64_t pb = ((O + I) * n * r + kThreads - 1) / kThreads;
+    if (pb > 65536) pb = 65536;
+    hipLaunchKernelGGL(pack_factors_kernel, dim3(unsigned(pb)), dim3(kThreads), 0, stream, fp, n, O, I, int(r), ucat,
+                       vcat);
+    if (hipError_t e = hipGetLastError()) {
+      *what = "packing the factors";
+      return int(e);
+    }
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev)) {
+      *what = "hipGetDevice";
+      return int(e);
+    }
+    std::lock_guard<std::mutex> lock(g_blas.mu);
+    rocblas_handle h = handle_for(dev, stream);
+    if (!h || rocblas_set_stream(h, stream) != rocblas_status_success) {
+      *what = "rocBLAS handle";
+      return -1;
+    }
+    // num [O, I] -= Ucat [O, nr] . Vcat [I, nr]^T (row-major; column-major num^T = Vcat . Ucat^T).
+    const float minus = -1.f, one = 1.f;
+    const int K = int(n * r);
+    if (rocblas_sgemm(h, rocblas_operation_transpose, rocblas_operation_none, int(I), int(O), K, &minus, vcat, K, ucat,
+                      K, &one, num, int(I)) != rocblas_status_success) {
+      *what = "rocblas_sgemm (delta of the block update)";
+      return -1;
+    }
+  }
+  const unsigned by = unsigned(O < 4096 ? O : 4096);
+  int64_t bx = (I + kThreads - 1) / kThreads;
+  if (bx > 64) bx = 64;
+  hipLaunchKernelGGL(refine_finish_kernel, dim3(unsigned(bx), by), dim3(kThreads), 0, stream, rp, n, O, I, num, prev,
+                     out);
+  if (hipError_t e = hipGetLastError()) {
+    *what = "block update";
+    return int(e);
+  }
+  return 0;
+}
+
 size_t lowrank_workspace_bytes(int64_t O, int64_t I, int64_t k, int64_t r, int cus) {
   return layout(O, I, k, r, cus).total;
 }
@@ -636,15 +770,10 @@ int launch_lowrank_factors(tb_dtype dtype, const void* const* weights, int n, co
     return int(e);
   }
   std::lock_guard<std::mutex> lock(g_blas.mu);
-  rocblas_handle h = nullptr;
-  for (const auto& e : g_blas.handles)
-    if (e.dev == dev && e.stream == stream) h = e.h;
+  rocblas_handle h = handle_for(dev, stream);
   if (!h) {
-    if (rocblas_create_handle(&h) != rocblas_status_success) {
-      *what = "rocblas_create_handle";
-      return -1;
-    }
-    g_blas.handles.push_back({dev, stream, h});
+    *what = "rocblas_create_handle";
+    return -1;
   }
   Run R{static_cast<char*>(workspace), layout(O, I, k, r, cus), int(k), cus, n, stream, h};
   if (rocblas_set_stream(R.h, stream) != rocblas_status_success) {

@@ -109,6 +109,13 @@ hipError_t launch_shared_block(tb_dtype dtype, const void* const* weights, int n
                                hipStream_t stream);
 hipError_t launch_row_scale(tb_dtype dtype, const void* weight, const float* w0, int64_t out_dim, int64_t in_dim,
                             float* s, hipStream_t stream);
+// Least-squares refit of one band's shared block from its n layers' weights,
+// scales and factors (u, v may be NULL when rank is 0).
+size_t refine_workspace_bytes(int64_t out_dim, int64_t in_dim, int64_t n, int64_t rank);
+int launch_refine_shared_block(tb_dtype dtype, const void* const* weights, const float* const* s,
+                               const float* const* u, const float* const* v, int n, int64_t out_dim, int64_t in_dim,
+                               int64_t rank, const float* prev, float* out, void* workspace, hipStream_t stream,
+                               const char** what);
 // Bytes of one matrix's workspace slice; a batch of n takes n slices.
 size_t lowrank_workspace_bytes(int64_t out_dim, int64_t in_dim, int64_t k, int64_t rank, int cus);
 // A batch of n matrices of one shape, each with its W0: s [n][out], omega [n][in][k],

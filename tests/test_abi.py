@@ -176,6 +176,15 @@ def test_decomposition_rejects_before_launch():
     assert bcall(a1=0) == 1 and bcall(a1=binding.MAX_BAND_LAYERS + 1) == 1
     assert bcall(a2=w0_bad) == 1                # a NULL shared block
     assert bcall(a6=17) == 1 and bcall(a10=17) == 1
+    rf = lib.tb_refine_shared_block
+    p2 = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    n2 = (ctypes.c_void_p * 2)(FAKE, None)
+    assert rf(None, p2, p2, p2, 2, 64, 48, 8, 1, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert rf(p2, p2, None, p2, 2, 64, 48, 8, 1, FAKE, FAKE, FAKE, 1 << 30, None) == 1   # u with rank > 0
+    assert rf(p2, n2, p2, p2, 2, 64, 48, 8, 1, FAKE, FAKE, FAKE, 1 << 30, None) == 1     # a NULL scale
+    assert rf(p2, p2, p2, p2, 0, 64, 48, 8, 1, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert rf(p2, p2, p2, p2, 2, 64, 48, 8, 1, FAKE, FAKE, FAKE, 16, None) == 1          # workspace too small
+    assert rf(p2, p2, p2, p2, 2, 64, 48, 8, 1, FAKE, None, FAKE, 1 << 30, None) == 1
     out = ctypes.c_size_t(0)
     assert lib.tb_lowrank_factors_workspace_size(64, 48, 20, 16, ctypes.byref(out)) == 1
     assert lib.tb_lowrank_factors_workspace_size(64, 48, 8, 16, None) == 1

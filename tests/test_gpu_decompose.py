@@ -228,3 +228,38 @@ def test_batch_matches_single_calls():
     for l in range(8):
         u1, v1 = tb.lowrank_factors(ws[l], W0, S[l].contiguous(), 16, om[l].contiguous(), 2)
         assert _rel(exact(u1) @ exact(v1).T, exact(U[l]) @ exact(V[l]).T) <= 1e-5, l
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("n,O,I,rank", [(3, 130, 264, 8), (5, 1000, 1032, 64), (2, 300, 520, 0)], ids=lambda v: str(v))
+def test_refine_shared_block(n, O, I, rank, dtype):
+    r = np.random.default_rng(n + O + rank)
+    ws = [torch.from_numpy(r.normal(0, 0.02, (O, I)).astype(np.float32)).to(dtype).to(DEV) for _ in range(n)]
+    ss = [torch.from_numpy(r.uniform(0.5, 1.5, O).astype(np.float32)).to(DEV) for _ in range(n)]
+    for t in ss:
+        t[3] = 0.0                       # a row with all-zero scales keeps its previous value
+    Us = [torch.from_numpy(r.normal(0, 0.01, (O, rank)).astype(np.float32)).to(DEV) for _ in range(n)]
+    Vs = [torch.from_numpy(r.normal(0, 0.01, (I, rank)).astype(np.float32)).to(DEV) for _ in range(n)]
+    prev = torch.from_numpy(r.normal(0, 0.02, (O, I)).astype(np.float32)).to(DEV)
+    W0 = tb.refine_shared_block(ws, ss, Us if rank else [None] * n, Vs if rank else [None] * n, prev)
+    want = oracle.refine_shared_block([exact(w) for w in ws], [exact(t) for t in ss],
+                                      [exact(u) for u in Us], [exact(v) for v in Vs], exact(prev))
+    assert torch.equal(W0[3], prev[3])
+    assert _rel(want, exact(W0)) <= 1e-6
+
+
+def test_als_tiny_stack_matches_the_oracle():
+    # With a probe as wide as the input (k = min(out, in)) the randomized SVD is
+    # the exact one, so two ALS rounds follow the oracle's exact-SVD ALS.
+    weights, _ = gen.tiny_stack()
+    wd = [f32_to_device(w) for w in weights]
+    got = tb.als_decompose(wd, 2, 16, 2, oversampling=gen.TINY_OUT)
+    want = oracle.als_decompose(weights, 2, 16, 2)
+    for l in range(gen.TINY_LAYERS):
+        band = got["band"][l]
+        assert _rel(want["W0"][band], exact(got["W0"][band])) <= 1e-5
+        rec = tb.reconstruct_weight(got["s"][l], got["W0"][band], got["U"][l], got["V"][l])
+        e_gpu = oracle.relative_frobenius_error(weights[l], exact(rec))
+        e_orc = oracle.relative_frobenius_error(weights[l], oracle.reconstruct_weight(
+            want["s"][l], want["W0"][band], want["U"][l], want["V"][l]))
+        assert abs(e_gpu - e_orc) <= 1e-4 * e_orc, (l, e_gpu, e_orc)
