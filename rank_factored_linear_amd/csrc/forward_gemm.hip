@@ -919,9 +919,9 @@ GemmPlan plan_gemm(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int
       p.grid = rounds > 0 ? G : round8(rem * slices);
     }
   }
-  // Fewer 256 x 256 tiles than half the compute units: the 128 x 128 kernel's
-  // four times as many workgroups finish sooner.
-  if (tiles < G / 2) {
+  // Fewer workgroups than half the compute units even with the k-slices:
+  // the 128 x 128 kernel's four times as many tiles finish sooner.
+  if (p.grid < G / 2) {
     p.big = 0;
     p.split_tiles = 0;
   }
