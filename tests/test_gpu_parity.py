@@ -244,6 +244,47 @@ def test_forward_edge_shapes(shape, dtype):
     assert bool((buf[:guard] == 7.0).all()) and bool((buf[guard + M * O:] == 7.0).all())
 
 
+
+# Decode calls with a small V (in * rank * 2 bytes around 512 KiB, rank up to
+# 256, up to 32 tokens): ragged column blocks of T, k tails, several k-slices.
+SMALL_V_SHAPES = [  # (out, in, rank)
+    (6912, 1152, 128), (2048, 2048, 128), (2048, 2056, 128), (1000, 1000, 136), (3000, 520, 256),
+    (260, 1032, 200), (130, 40, 8), (4096, 1024, 256), (4096, 1056, 256),
+]
+
+
+@pytest.mark.parametrize("M", [1, 4, 16, 17, 32])
+@pytest.mark.parametrize("shape", SMALL_V_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_forward_small_v(shape, M):
+    O, I, R = shape
+    _say(f"small V {shape} M={M}")
+    x, s, W0, U, V = _rand_case(M, O, I, R, torch.bfloat16, seed=O + I + R + M)
+    guard = 4096
+    buf = torch.full((guard + M * O + guard,), 7.0, dtype=torch.bfloat16, device=DEV)
+    y = buf[guard:guard + M * O].view(M, O)
+    tb.linear_forward(x, s, W0, U, V, out=y)
+    y2 = tb.linear_forward(x, s, W0, U, V)
+    torch.cuda.synchronize()
+    assert oracle.relative_frobenius_error(_oracle_forward(x, s, W0, U, V), exact(y)) <= BF16_TOL
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    assert bool((buf[:guard] == 7.0).all()) and bool((buf[guard + M * O:] == 7.0).all())
+    assert tb.workspace_error_word() == 0
+
+
+@pytest.mark.parametrize("M", [1, 16, 32])
+def test_forward_group_small_and_large_v(M):
+    # One launch, same tile shape: a member with a 288 KiB V and one with 2.6 MiB.
+    members = [_rand_case(M, 6912, 1152, 128, torch.bfloat16, seed=M),
+               _rand_case(M, 6912, 5376, 256, torch.bfloat16, seed=M + 1)]
+    ys = tb.linear_forward_group(members)
+    singles = [tb.linear_forward(*mbr) for mbr in members]
+    torch.cuda.synchronize()
+    for mbr, y, y1 in zip(members, ys, singles):
+        assert torch.equal(y.view(torch.int16), y1.view(torch.int16))
+        assert oracle.relative_frobenius_error(_oracle_forward(*mbr), exact(y)) <= BF16_TOL
+    assert tb.workspace_error_word() == 0
+
+
 @pytest.mark.parametrize("shape", [(2048, 4096, 4104, 72), (4096, 4352, 4096, 64)], ids=["split_round", "rounds_and_split"])
 def test_forward_split_rounds(shape):
     # 128 tiles of 256 x 256 split into two k-slices; and 272 tiles: one whole
