@@ -2,8 +2,9 @@
 // before anything is enqueued, so a failing call leaves all outputs untouched.
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
-
 #include <stdio.h>
+
+#include <algorithm>
 
 #include "tb_host.h"
 
@@ -90,6 +91,26 @@ tb_status tb_band_index(int32_t num_layers, int32_t num_bands, int32_t layer, in
   return ok();
 }
 
+namespace {
+
+// Data bytes of one projection's buffers: the largest of every plan a call
+// of m tokens may take (alone or in a group; the last 64-token slice of a
+// longer fp32 call has a plan of its own).
+size_t forward_data_bytes(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, tb_dtype dtype, int cus) {
+  if (dtype == TB_BF16 && m > kDecodeMaxTokens) return plan_gemm(m, out_dim, in_dim, rank, cus).bytes;
+  size_t bytes = 0;
+  const int64_t counts[2] = {m < kDecodeMaxTokens ? m : kDecodeMaxTokens, m > kDecodeMaxTokens ? m % kDecodeMaxTokens : 0};
+  for (int64_t mt : counts) {
+    if (mt == 0) continue;
+    const size_t a = plan_decode(mt, out_dim, in_dim, rank, cus).bytes;
+    const size_t b = plan_decode_spared(mt, out_dim, in_dim, rank, cus).bytes;
+    bytes = std::max(bytes, std::max(a, b));
+  }
+  return bytes;
+}
+
+}  // namespace
+
 tb_status tb_linear_forward_workspace_size(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, tb_dtype dtype,
                                            size_t* bytes_out) {
   if (bytes_out == nullptr) return fail(TB_ERR_INVALID_ARGUMENT, "bytes_out is NULL");
@@ -98,14 +119,7 @@ tb_status tb_linear_forward_workspace_size(int64_t m, int64_t out_dim, int64_t i
   if (st != TB_OK) return st;
   int cus = 0;
   if (int e = device_cu_count(&cus)) return hip_fail(hipError_t(e), "querying the compute-unit count");
-  size_t bytes;
-  if (dtype == TB_BF16 && m > kDecodeMaxTokens) {
-    bytes = plan_gemm(m, out_dim, in_dim, rank, cus).bytes;
-  } else {
-    const int64_t mm = m < kDecodeMaxTokens ? m : kDecodeMaxTokens;
-    bytes = plan_decode(mm, out_dim, in_dim, rank, cus).bytes;
-  }
-  *bytes_out = kControlBytes + bytes;
+  *bytes_out = kControlBytes + forward_data_bytes(m, out_dim, in_dim, rank, dtype, cus);
   return ok();
 }
 
@@ -133,12 +147,6 @@ tb_status check_projection(const void* x, const void* s, const void* w0, const v
   return TB_OK;
 }
 
-// Bytes of one projection's buffers (after the control bytes).
-size_t forward_data_bytes(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, tb_dtype dtype, int cus) {
-  if (dtype == TB_BF16 && m > kDecodeMaxTokens) return plan_gemm(m, out_dim, in_dim, rank, cus).bytes;
-  const int64_t mm = m < kDecodeMaxTokens ? m : kDecodeMaxTokens;
-  return plan_decode(mm, out_dim, in_dim, rank, cus).bytes;
-}
 
 // One projection with checked arguments: the prefill GEMM, or the decode
 // kernel over 64-token slices.  ctrl is its control block, data holds
@@ -153,11 +161,11 @@ tb_status forward_one(const void* x, const void* s, const void* w0, const void* 
     return ok();
   }
   const int64_t mm = m < kDecodeMaxTokens ? m : kDecodeMaxTokens;
-  const DecodePlan p = plan_decode(mm, out_dim, in_dim, rank, cus);
+  const DecodePlan p = plan_decode_spared(mm, out_dim, in_dim, rank, cus);
   const size_t es = esize(dtype);
   for (int64_t t0 = 0; t0 < m; t0 += kDecodeMaxTokens) {
     const int64_t mt = (m - t0) < kDecodeMaxTokens ? (m - t0) : kDecodeMaxTokens;
-    const DecodePlan pt = mt == mm ? p : plan_decode(mt, out_dim, in_dim, rank, cus);
+    const DecodePlan pt = mt == mm ? p : plan_decode_spared(mt, out_dim, in_dim, rank, cus);
     const char* xt = static_cast<const char*>(x) + size_t(t0) * size_t(in_dim) * es;
     char* yt = static_cast<char*>(y) + size_t(t0) * size_t(out_dim) * es;
     hipError_t e =
@@ -237,19 +245,25 @@ tb_status tb_linear_forward_group(int32_t n, const tb_projection* projs, int64_t
   unsigned* err = ctrl + 2;
 
   if (m <= kDecodeMaxTokens) {
+    // One launch needs every member on the same tile shape: the plans that
+    // leave the producers' compute units to them if they agree, else the
+    // plain plans, else one launch per member.
     DecodePlan plans[TB_MAX_GROUP];
     DecodeProjection dp[TB_MAX_GROUP];
-    bool same = true;
-    for (int j = 0; j < n; ++j) {
-      const tb_projection& q = projs[j];
-      plans[j] = plan_decode(m, q.out_dim, q.in_dim, q.rank, cus);
-      dp[j] = DecodeProjection{q.x, q.s, q.w0, q.u, q.v, q.y, q.out_dim, q.in_dim, q.rank};
-      same = same && plans[j].NT == plans[0].NT && plans[j].TILES == plans[0].TILES;
-    }
-    if (same) {
-      hipError_t e = launch_forward_decode_group(n, plans, dp, dtype, m, ctrl, ws + kControlBytes, err, hs);
-      if (e != hipSuccess) return hip_fail(e, "launching the grouped decode projections");
-      return ok();
+    for (int spared = 1; spared >= 0; --spared) {
+      bool same = true;
+      for (int j = 0; j < n; ++j) {
+        const tb_projection& q = projs[j];
+        plans[j] = spared ? plan_decode_spared(m, q.out_dim, q.in_dim, q.rank, cus)
+                          : plan_decode(m, q.out_dim, q.in_dim, q.rank, cus);
+        dp[j] = DecodeProjection{q.x, q.s, q.w0, q.u, q.v, q.y, q.out_dim, q.in_dim, q.rank};
+        same = same && plans[j].NT == plans[0].NT && plans[j].TILES == plans[0].TILES;
+      }
+      if (same) {
+        hipError_t e = launch_forward_decode_group(n, plans, dp, dtype, m, ctrl, ws + kControlBytes, err, hs);
+        if (e != hipSuccess) return hip_fail(e, "launching the grouped decode projections");
+        return ok();
+      }
     }
   }
   for (int j = 0; j < n; ++j) {

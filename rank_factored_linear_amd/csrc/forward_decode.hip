@@ -673,7 +673,7 @@ hipError_t launch_e(int NT, int TILES, const GroupArgs& g, hipStream_t stream) {
 
 }  // namespace
 
-DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus) {
+DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int streamers) {
   DecodePlan p{};
   p.NT = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
   const int64_t max_rows = 16 * (p.NT == 1 ? 6 : (p.NT == 2 ? 4 : 2));
@@ -684,15 +684,15 @@ DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
   // streamer per compute unit (each wave keeping at least four k32 steps).
   const int64_t nrb_min = (out_dim + max_rows - 1) / max_rows;
   int64_t ks = 1, nrb;
-  if (nrb_min >= cus) {
-    nrb = cus;
-    while ((out_dim + nrb - 1) / nrb > max_rows) nrb += cus;
+  if (nrb_min >= streamers) {
+    nrb = streamers;
+    while ((out_dim + nrb - 1) / nrb > max_rows) nrb += streamers;
   } else {
-    ks = cus / nrb_min;
+    ks = streamers / nrb_min;
     const int64_t ks_cap = s_full / 32 > 1 ? s_full / 32 : 1;
     if (ks > ks_cap) ks = ks_cap;
     if (ks > 16) ks = 16;
-    nrb = cus / ks;
+    nrb = streamers / ks;
     if (nrb < nrb_min) nrb = nrb_min;
   }
   if (nrb > out_dim) nrb = out_dim;
@@ -729,6 +729,12 @@ DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
   off = align_up(off + (p.KS > 1 ? size_t(p.NRB) * size_t(p.KS) * rows16 * rbr * 4 : 0), 256);
   p.bytes = off;
   return p;
+}
+
+DecodePlan plan_decode_spared(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus) {
+  const DecodePlan p = plan_decode(m, out_dim, in_dim, rank, cus);
+  if (p.NP == 0 || 4 * p.NP >= cus) return p;
+  return plan_decode(m, out_dim, in_dim, rank, cus - p.NP);  // the producer count does not depend on the streamers
 }
 
 hipError_t launch_forward_decode_group(int n, const DecodePlan* plans, const DecodeProjection* projs, tb_dtype dtype,

@@ -40,7 +40,12 @@ struct DecodePlan {
   size_t off_tpart, off_tfull, off_ypart, bytes;
 };
 
-DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus);
+// streamers: the streaming workgroups to aim for (about one per compute unit).
+DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int streamers);
+// The same with the producers' compute units left to them when they are few
+// (under a quarter of the chip): a streamer that shares a compute unit with a
+// producer finishes several microseconds after the others.
+DecodePlan plan_decode_spared(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus);
 
 // ctrl: the projection's control block; data: its buffers; err_word: where a
 // timed-out wait is flagged.
