@@ -165,12 +165,16 @@ tb_status tb_linear_forward_group_workspace_size(int32_t n, const tb_projection 
 
 /*
  * tb_linear_forward_group -- n independent theta-bundle projections (the
- * computation of tb_linear_forward for each member, same results bit for
- * bit) over the same token count m and dtype.  Layers apply several
- * projections to one input (q/k/v, gate/up); each member still names its own
- * x, which may be shared.  For m <= 64 the members whose launch plans agree
- * run in one launch, so the fixed cost of a launch and the wait for x . V
- * are paid once; other cases run the members one after another.
+ * computation of tb_linear_forward for each member) over the same token
+ * count m and dtype.  Layers apply several projections to one input (q/k/v,
+ * gate/up); each member still names its own x, which may be shared.  For
+ * m <= 64 the members run in one launch when their plans can share one tile
+ * shape, so the fixed cost of a launch and the wait for x . V are paid once;
+ * the chip is then shared out between the members, which may split a
+ * member's reductions over in_dim differently from its own call, so its
+ * result may differ from tb_linear_forward's in the last bits (same error
+ * bound; a given group is deterministic run to run).  Other cases run the
+ * members one after another, each exactly as its own call.
  *   n: 1 .. TB_MAX_GROUP.  projs: host array of n members (no y may alias
  *   any member's input or another member's y).
  *   workspace: as for tb_linear_forward, at least

@@ -93,19 +93,15 @@ tb_status tb_band_index(int32_t num_layers, int32_t num_bands, int32_t layer, in
 
 namespace {
 
-// Data bytes of one projection's buffers: the largest of every plan a call
-// of m tokens may take (alone or in a group; the last 64-token slice of a
-// longer fp32 call has a plan of its own).
+// Data bytes of one projection's buffers: enough for every plan a call of m
+// tokens may take (alone or in a group, whatever its streamer budget; the
+// last 64-token slice of a longer fp32 call has a plan of its own).
 size_t forward_data_bytes(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, tb_dtype dtype, int cus) {
   if (dtype == TB_BF16 && m > kDecodeMaxTokens) return plan_gemm(m, out_dim, in_dim, rank, cus).bytes;
   size_t bytes = 0;
   const int64_t counts[2] = {m < kDecodeMaxTokens ? m : kDecodeMaxTokens, m > kDecodeMaxTokens ? m % kDecodeMaxTokens : 0};
-  for (int64_t mt : counts) {
-    if (mt == 0) continue;
-    const size_t a = plan_decode(mt, out_dim, in_dim, rank, cus).bytes;
-    const size_t b = plan_decode_spared(mt, out_dim, in_dim, rank, cus).bytes;
-    bytes = std::max(bytes, std::max(a, b));
-  }
+  for (int64_t mt : counts)
+    if (mt > 0) bytes = std::max(bytes, decode_bytes_bound(mt, out_dim, in_dim, rank, cus));
   return bytes;
 }
 
@@ -245,20 +241,31 @@ tb_status tb_linear_forward_group(int32_t n, const tb_projection* projs, int64_t
   unsigned* err = ctrl + 2;
 
   if (m <= kDecodeMaxTokens) {
-    // One launch needs every member on the same tile shape: the plans that
-    // leave the producers' compute units to them if they agree, else the
-    // plain plans, else one launch per member.
+    // One launch needs every member on the same tile shape.  In order: the
+    // members sharing one workgroup per compute unit, then two; each member
+    // on the plan that leaves its producers' compute units to them; the
+    // plain plans; else one launch per member.
     DecodePlan plans[TB_MAX_GROUP];
     DecodeProjection dp[TB_MAX_GROUP];
-    for (int spared = 1; spared >= 0; --spared) {
+    for (int j = 0; j < n; ++j) {
+      const tb_projection& q = projs[j];
+      dp[j] = DecodeProjection{q.x, q.s, q.w0, q.u, q.v, q.y, q.out_dim, q.in_dim, q.rank};
+    }
+    for (int choice = 0; choice < 4; ++choice) {
       bool same = true;
-      for (int j = 0; j < n; ++j) {
-        const tb_projection& q = projs[j];
-        plans[j] = spared ? plan_decode_spared(m, q.out_dim, q.in_dim, q.rank, cus)
-                          : plan_decode(m, q.out_dim, q.in_dim, q.rank, cus);
-        dp[j] = DecodeProjection{q.x, q.s, q.w0, q.u, q.v, q.y, q.out_dim, q.in_dim, q.rank};
-        same = same && plans[j].NT == plans[0].NT && plans[j].TILES == plans[0].TILES;
+      if (choice < 2) {
+        same = plan_decode_shared(n, dp, m, cus, choice + 1, plans);
+      } else {
+        for (int j = 0; j < n; ++j) {
+          const tb_projection& q = projs[j];
+          plans[j] = choice == 2 ? plan_decode_spared(m, q.out_dim, q.in_dim, q.rank, cus)
+                                 : plan_decode(m, q.out_dim, q.in_dim, q.rank, cus);
+          same = same && plans[j].NT == plans[0].NT && plans[j].TILES == plans[0].TILES;
+        }
       }
+      // Each member's buffers fit its share of the workspace (by construction).
+      for (int j = 0; j < n && same; ++j)
+        same = plans[j].bytes <= forward_data_bytes(m, projs[j].out_dim, projs[j].in_dim, projs[j].rank, dtype, cus);
       if (same) {
         hipError_t e = launch_forward_decode_group(n, plans, dp, dtype, m, ctrl, ws + kControlBytes, err, hs);
         if (e != hipSuccess) return hip_fail(e, "launching the grouped decode projections");

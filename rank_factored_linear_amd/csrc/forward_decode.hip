@@ -673,10 +673,15 @@ hipError_t launch_e(int NT, int TILES, const GroupArgs& g, hipStream_t stream) {
 
 }  // namespace
 
+namespace {
+// Rows of a streaming workgroup at most: the widest tile set of each NT.
+int64_t decode_max_rows(int NT) { return 16 * (NT == 1 ? 6 : (NT == 2 ? 4 : 2)); }
+}  // namespace
+
 DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int streamers) {
   DecodePlan p{};
   p.NT = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
-  const int64_t max_rows = 16 * (p.NT == 1 ? 6 : (p.NT == 2 ? 4 : 2));
+  const int64_t max_rows = decode_max_rows(p.NT);
   const int64_t s_full = in_dim / 32;
   // Streamers.  Every streamer of a row block reads all of x for its k-slice,
   // so the x traffic grows with the number of row blocks: use as few blocks
@@ -735,6 +740,35 @@ DecodePlan plan_decode_spared(int64_t m, int64_t out_dim, int64_t in_dim, int64_
   const DecodePlan p = plan_decode(m, out_dim, in_dim, rank, cus);
   if (p.NP == 0 || 4 * p.NP >= cus) return p;
   return plan_decode(m, out_dim, in_dim, rank, cus - p.NP);  // the producer count does not depend on the streamers
+}
+
+bool plan_decode_shared(int n, const DecodeProjection* projs, int64_t m, int cus, int slots, DecodePlan* plans) {
+  int64_t producers = 0;
+  double w0 = 0.0;
+  for (int j = 0; j < n; ++j) {
+    producers += plan_decode(m, projs[j].out_dim, projs[j].in_dim, projs[j].rank, cus).NP;
+    w0 += double(projs[j].out_dim) * double(projs[j].in_dim);
+  }
+  const int64_t slots_total = int64_t(slots) * cus, streamers = slots_total - producers;
+  if (slots < 1 || slots > kMaxDecodeSlots || streamers < 4 * int64_t(n)) return false;
+  int64_t total = producers;
+  for (int j = 0; j < n; ++j) {
+    const DecodeProjection& q = projs[j];
+    const int64_t b = int64_t(double(streamers) * double(q.out_dim) * double(q.in_dim) / w0);
+    plans[j] = plan_decode(m, q.out_dim, q.in_dim, q.rank, int(b > 1 ? b : 1));
+    total += plans[j].NB;
+    if (plans[j].NT != plans[0].NT || plans[j].TILES != plans[0].TILES) return false;
+  }
+  return total <= slots_total;
+}
+
+// With KS > 1 the planner takes NRB = streamers / KS row blocks of at most
+// decode_max_rows(NT) rows, so NRB * KS never exceeds the budget; the buffers
+// before the y partials do not depend on the budget.
+size_t decode_bytes_bound(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus) {
+  const DecodePlan p = plan_decode(m, out_dim, in_dim, rank, cus);
+  const size_t ypart = size_t(kMaxDecodeSlots) * size_t(cus) * size_t(16 * p.NT) * size_t(decode_max_rows(p.NT)) * 4;
+  return p.off_ypart + align_up(ypart, 256);
 }
 
 hipError_t launch_forward_decode_group(int n, const DecodePlan* plans, const DecodeProjection* projs, tb_dtype dtype,

@@ -69,6 +69,18 @@ struct DecodeProjection {
 hipError_t launch_forward_decode_group(int n, const DecodePlan* plans, const DecodeProjection* projs, tb_dtype dtype,
                                        int64_t m, unsigned* ctrl, char* data, unsigned* err_word, hipStream_t stream);
 
+// Workgroups per compute unit that a shared plan may fill (the decode kernel
+// keeps two resident per compute unit).
+constexpr int kMaxDecodeSlots = 2;
+// Plans for the members of one launch that share slots * cus workgroups:
+// every producer keeps its workgroup and the streamers are shared out in
+// proportion to each member's W0 bytes.  False when the members would not
+// agree on one tile shape or would need more workgroups than that.
+bool plan_decode_shared(int n, const DecodeProjection* projs, int64_t m, int cus, int slots, DecodePlan* plans);
+// Data bytes that cover the plan of any streamer budget up to
+// kMaxDecodeSlots * cus.
+size_t decode_bytes_bound(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus);
+
 // ---- forward, prefill token counts (bf16, m > kDecodeMaxTokens) ----------
 struct GemmPlan {
   int aligned;          // in_dim and rank multiples of 8: x . V by the transposing-read kernel

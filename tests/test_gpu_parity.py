@@ -273,14 +273,12 @@ def test_forward_small_v(shape, M):
 
 @pytest.mark.parametrize("M", [1, 16, 32])
 def test_forward_group_small_and_large_v(M):
-    # One launch, same tile shape: a member with a 288 KiB V and one with 2.6 MiB.
+    # One call with a member with a 288 KiB V and one with 2.6 MiB.
     members = [_rand_case(M, 6912, 1152, 128, torch.bfloat16, seed=M),
                _rand_case(M, 6912, 5376, 256, torch.bfloat16, seed=M + 1)]
     ys = tb.linear_forward_group(members)
-    singles = [tb.linear_forward(*mbr) for mbr in members]
     torch.cuda.synchronize()
-    for mbr, y, y1 in zip(members, ys, singles):
-        assert torch.equal(y.view(torch.int16), y1.view(torch.int16))
+    for mbr, y in zip(members, ys):
         assert oracle.relative_frobenius_error(_oracle_forward(*mbr), exact(y)) <= BF16_TOL
     assert tb.workspace_error_word() == 0
 
@@ -496,18 +494,24 @@ GROUPS = {  # members (out, in, rank)
 @pytest.mark.parametrize("M", [1, 4, 16, 64, 100])
 @pytest.mark.parametrize("group", sorted(GROUPS))
 def test_forward_group_matches_single_calls(group, M):
-    # A grouped call computes each member exactly as its own call would.
+    # A grouped call computes each member as its own call would.  In one
+    # decode launch the chip is shared out between the members, so a member's
+    # k-slices (and its last bits) may differ from its own call's; prefill
+    # members run one after another, bit for bit as their own calls.
     _say(f"group {group} M={M}")
     members = [_rand_case(M, O, I, R, torch.bfloat16, seed=31 * j + M) for j, (O, I, R) in enumerate(GROUPS[group])]
     ys = tb.linear_forward_group(members)
+    ys2 = tb.linear_forward_group(members)
     singles = [tb.linear_forward(*mbr) for mbr in members]
     torch.cuda.synchronize()
-    for y, y1 in zip(ys, singles):
-        assert torch.equal(y.view(torch.int16), y1.view(torch.int16))
-    assert tb.workspace_error_word() == 0
-    if group == "ragged":
-        for mbr, y in zip(members, ys):
+    for mbr, y, y2, y1 in zip(members, ys, ys2, singles):
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+        if M > 64:
+            assert torch.equal(y.view(torch.int16), y1.view(torch.int16))
+        else:
+            assert oracle.relative_frobenius_error(exact(y1), exact(y)) <= BF16_TOL
             assert oracle.relative_frobenius_error(_oracle_forward(*mbr), exact(y)) <= BF16_TOL
+    assert tb.workspace_error_word() == 0
 
 
 def test_forward_group_fp32_and_clean_workspace():
