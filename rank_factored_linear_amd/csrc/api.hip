@@ -157,11 +157,12 @@ tb_status forward_one(const void* x, const void* s, const void* w0, const void* 
     return ok();
   }
   const int64_t mm = m < kDecodeMaxTokens ? m : kDecodeMaxTokens;
-  const DecodePlan p = plan_decode_spared(mm, out_dim, in_dim, rank, cus);
   const size_t es = esize(dtype);
+  const int64_t w0_bytes = out_dim * in_dim * int64_t(es);
+  const DecodePlan p = plan_decode_spared(mm, out_dim, in_dim, rank, cus, w0_bytes);
   for (int64_t t0 = 0; t0 < m; t0 += kDecodeMaxTokens) {
     const int64_t mt = (m - t0) < kDecodeMaxTokens ? (m - t0) : kDecodeMaxTokens;
-    const DecodePlan pt = mt == mm ? p : plan_decode_spared(mt, out_dim, in_dim, rank, cus);
+    const DecodePlan pt = mt == mm ? p : plan_decode_spared(mt, out_dim, in_dim, rank, cus, w0_bytes);
     const char* xt = static_cast<const char*>(x) + size_t(t0) * size_t(in_dim) * es;
     char* yt = static_cast<char*>(y) + size_t(t0) * size_t(out_dim) * es;
     hipError_t e =
@@ -247,19 +248,21 @@ tb_status tb_linear_forward_group(int32_t n, const tb_projection* projs, int64_t
     // plain plans; else one launch per member.
     DecodePlan plans[TB_MAX_GROUP];
     DecodeProjection dp[TB_MAX_GROUP];
+    int64_t w0_bytes = 0;
     for (int j = 0; j < n; ++j) {
       const tb_projection& q = projs[j];
       dp[j] = DecodeProjection{q.x, q.s, q.w0, q.u, q.v, q.y, q.out_dim, q.in_dim, q.rank};
+      w0_bytes += q.out_dim * q.in_dim * int64_t(esize(dtype));
     }
     for (int choice = 0; choice < 4; ++choice) {
       bool same = true;
       if (choice < 2) {
-        same = plan_decode_shared(n, dp, m, cus, choice + 1, plans);
+        same = plan_decode_shared(n, dp, m, cus, choice + 1, w0_bytes, plans);
       } else {
         for (int j = 0; j < n; ++j) {
           const tb_projection& q = projs[j];
-          plans[j] = choice == 2 ? plan_decode_spared(m, q.out_dim, q.in_dim, q.rank, cus)
-                                 : plan_decode(m, q.out_dim, q.in_dim, q.rank, cus);
+          plans[j] = choice == 2 ? plan_decode_spared(m, q.out_dim, q.in_dim, q.rank, cus, w0_bytes)
+                                 : plan_decode(m, q.out_dim, q.in_dim, q.rank, cus, w0_bytes);
           same = same && plans[j].NT == plans[0].NT && plans[j].TILES == plans[0].TILES;
         }
       }

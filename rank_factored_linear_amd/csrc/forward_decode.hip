@@ -676,9 +676,16 @@ hipError_t launch_e(int NT, int TILES, const GroupArgs& g, hipStream_t stream) {
 namespace {
 // Rows of a streaming workgroup at most: the widest tile set of each NT.
 int64_t decode_max_rows(int NT) { return 16 * (NT == 1 ? 6 : (NT == 2 ? 4 : 2)); }
+// Producer k-slices: about 768 of in_dim (three k32 steps per wave, one
+// round of loads at 16 tokens) when T must be ready early; about 2816
+// (eleven steps per wave) when the launch streams at least 112 MiB of W0
+// (over ~20 us), which hides the longer chain and leaves fewer producers to
+// share compute units with the streamers.
+constexpr int64_t kShortSlice = 768, kLongSlice = 2816;
+constexpr int64_t kLongStreamBytes = int64_t(112) << 20;
 }  // namespace
 
-DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int streamers) {
+DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int streamers, int64_t stream_bytes) {
   DecodePlan p{};
   p.NT = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
   const int64_t max_rows = decode_max_rows(p.NT);
@@ -707,14 +714,15 @@ DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
   p.NRB = int(nrb);
   p.KS = int(ks);
   p.NB = p.NRB * p.KS;
-  // Producers: 64 columns of T each, over k-slices of about 768 of in_dim
-  // (three k32 steps per wave: one round of loads at 16 tokens).
+  // Producers: 64 columns of T each, over k-slices of in_dim (kShortSlice,
+  // or kLongSlice behind a long stream).
   if (rank > 0) {
     p.NCB = int((rank + kCbCols - 1) / kCbCols);
     // Short reductions (in_dim <= 1536) stay in one producer per column block:
     // its longer load phase costs less than the extra round trips of
     // combining k-slice partials across workgroups.
-    int64_t kt = in_dim <= 1536 ? 1 : (in_dim + 767) / 768;
+    const int64_t slice = stream_bytes >= kLongStreamBytes ? kLongSlice : kShortSlice;
+    int64_t kt = in_dim <= 1536 ? 1 : (in_dim + slice - 1) / slice;
     if (kt > kMaxKT) kt = kMaxKT;
     if (p.NCB > kMaxGroupCounters / 2) kt = 1;  // one arrival counter per column block
     p.KT = int(kt);
@@ -736,17 +744,19 @@ DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
   return p;
 }
 
-DecodePlan plan_decode_spared(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus) {
-  const DecodePlan p = plan_decode(m, out_dim, in_dim, rank, cus);
+DecodePlan plan_decode_spared(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus, int64_t stream_bytes) {
+  const DecodePlan p = plan_decode(m, out_dim, in_dim, rank, cus, stream_bytes);
   if (p.NP == 0 || 4 * p.NP >= cus) return p;
-  return plan_decode(m, out_dim, in_dim, rank, cus - p.NP);  // the producer count does not depend on the streamers
+  // The producer count does not depend on the streamers.
+  return plan_decode(m, out_dim, in_dim, rank, cus - p.NP, stream_bytes);
 }
 
-bool plan_decode_shared(int n, const DecodeProjection* projs, int64_t m, int cus, int slots, DecodePlan* plans) {
+bool plan_decode_shared(int n, const DecodeProjection* projs, int64_t m, int cus, int slots, int64_t stream_bytes,
+                        DecodePlan* plans) {
   int64_t producers = 0;
   double w0 = 0.0;
   for (int j = 0; j < n; ++j) {
-    producers += plan_decode(m, projs[j].out_dim, projs[j].in_dim, projs[j].rank, cus).NP;
+    producers += plan_decode(m, projs[j].out_dim, projs[j].in_dim, projs[j].rank, cus, stream_bytes).NP;
     w0 += double(projs[j].out_dim) * double(projs[j].in_dim);
   }
   const int64_t slots_total = int64_t(slots) * cus, streamers = slots_total - producers;
@@ -755,7 +765,7 @@ bool plan_decode_shared(int n, const DecodeProjection* projs, int64_t m, int cus
   for (int j = 0; j < n; ++j) {
     const DecodeProjection& q = projs[j];
     const int64_t b = int64_t(double(streamers) * double(q.out_dim) * double(q.in_dim) / w0);
-    plans[j] = plan_decode(m, q.out_dim, q.in_dim, q.rank, int(b > 1 ? b : 1));
+    plans[j] = plan_decode(m, q.out_dim, q.in_dim, q.rank, int(b > 1 ? b : 1), stream_bytes);
     total += plans[j].NB;
     if (plans[j].NT != plans[0].NT || plans[j].TILES != plans[0].TILES) return false;
   }
@@ -763,10 +773,11 @@ bool plan_decode_shared(int n, const DecodeProjection* projs, int64_t m, int cus
 }
 
 // With KS > 1 the planner takes NRB = streamers / KS row blocks of at most
-// decode_max_rows(NT) rows, so NRB * KS never exceeds the budget; the buffers
-// before the y partials do not depend on the budget.
+// decode_max_rows(NT) rows, so NRB * KS never exceeds the budget.  The
+// buffers before the y partials do not depend on the budget and are largest
+// with the short producer k-slices.
 size_t decode_bytes_bound(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus) {
-  const DecodePlan p = plan_decode(m, out_dim, in_dim, rank, cus);
+  const DecodePlan p = plan_decode(m, out_dim, in_dim, rank, cus, 0);
   const size_t ypart = size_t(kMaxDecodeSlots) * size_t(cus) * size_t(16 * p.NT) * size_t(decode_max_rows(p.NT)) * 4;
   return p.off_ypart + align_up(ypart, 256);
 }

@@ -40,12 +40,14 @@ struct DecodePlan {
   size_t off_tpart, off_tfull, off_ypart, bytes;
 };
 
-// streamers: the streaming workgroups to aim for (about one per compute unit).
-DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int streamers);
+// streamers: the streaming workgroups to aim for (about one per compute
+// unit); stream_bytes: the W0 bytes of the whole launch, which set how long
+// the producers' k-slices may be.
+DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int streamers, int64_t stream_bytes);
 // The same with the producers' compute units left to them when they are few
 // (under a quarter of the chip): a streamer that shares a compute unit with a
 // producer finishes several microseconds after the others.
-DecodePlan plan_decode_spared(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus);
+DecodePlan plan_decode_spared(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus, int64_t stream_bytes);
 
 // ctrl: the projection's control block; data: its buffers; err_word: where a
 // timed-out wait is flagged.
@@ -76,7 +78,8 @@ constexpr int kMaxDecodeSlots = 2;
 // every producer keeps its workgroup and the streamers are shared out in
 // proportion to each member's W0 bytes.  False when the members would not
 // agree on one tile shape or would need more workgroups than that.
-bool plan_decode_shared(int n, const DecodeProjection* projs, int64_t m, int cus, int slots, DecodePlan* plans);
+bool plan_decode_shared(int n, const DecodeProjection* projs, int64_t m, int cus, int slots, int64_t stream_bytes,
+                        DecodePlan* plans);
 // Data bytes that cover the plan of any streamer budget up to
 // kMaxDecodeSlots * cus.
 size_t decode_bytes_bound(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus);
