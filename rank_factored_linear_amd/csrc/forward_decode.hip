@@ -629,8 +629,14 @@ struct GroupArgs {
   DecodeArgs a[kMaxProjections];
 };
 
+// Waves per SIMD that the register budget is cut for: four (two workgroups
+// per compute unit), except for the 64-token, 64-row variant, whose
+// accumulators need more registers (one workgroup per compute unit).
+template <int NT, int TILES> constexpr int decode_waves_per_eu() { return NT * TILES >= 16 ? 2 : 4; }
+
 template <typename E, int NT, int TILES>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void decode_kernel(GroupArgs g) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<NT, TILES>()))) void
+decode_kernel(GroupArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<E, NT, TILES>()];
   const int b = int(blockIdx.x), np = g.p_end[g.n - 1];
   int j = 0;
@@ -668,14 +674,17 @@ hipError_t launch_e(int NT, int TILES, const GroupArgs& g, hipStream_t stream) {
       default: return launch_t<E, 2, 4>(g, stream);
     }
   }
-  return TILES == 1 ? launch_t<E, 4, 1>(g, stream) : launch_t<E, 4, 2>(g, stream);
+  if (TILES == 1) return launch_t<E, 4, 1>(g, stream);
+  if (TILES == 2) return launch_t<E, 4, 2>(g, stream);
+  return launch_t<E, 4, 4>(g, stream);
 }
 
 }  // namespace
 
 namespace {
 // Rows of a streaming workgroup at most: the widest tile set of each NT.
-int64_t decode_max_rows(int NT) { return 16 * (NT == 1 ? 6 : (NT == 2 ? 4 : 2)); }
+// Every row block re-reads x, so at 33-64 tokens wide blocks matter most.
+int64_t decode_max_rows(int NT) { return 16 * (NT == 1 ? 6 : 4); }
 // Producer k-slices: about 768 of in_dim (three k32 steps per wave, one
 // round of loads at 16 tokens) when T must be ready early; about 2816
 // (eleven steps per wave) when the launch streams at least 112 MiB of W0

@@ -271,6 +271,26 @@ def test_forward_small_v(shape, M):
     assert tb.workspace_error_word() == 0
 
 
+
+# 33-64 tokens: 64-row streaming tiles (TILES = 4 with NT = 4), ragged row
+# blocks and k tails, both dtypes.
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("M", [33, 48, 64])
+@pytest.mark.parametrize("shape", [(8192, 5376, 256), (2100, 1032, 136), (21504, 1152, 128), (700, 4104, 40)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_forward_wide_rows_many_tokens(shape, M, dtype):
+    O, I, R = shape
+    _say(f"wide rows {shape} M={M} {dtype}")
+    x, s, W0, U, V = _rand_case(M, O, I, R, dtype, seed=O + M)
+    guard = 4096
+    buf = torch.full((guard + M * O + guard,), 7.0, dtype=dtype, device=DEV)
+    y = buf[guard:guard + M * O].view(M, O)
+    tb.linear_forward(x, s, W0, U, V, out=y)
+    torch.cuda.synchronize()
+    assert oracle.relative_frobenius_error(_oracle_forward(x, s, W0, U, V), exact(y)) <= tol_for(dtype)
+    assert bool((buf[:guard] == 7.0).all()) and bool((buf[guard + M * O:] == 7.0).all())
+    assert tb.workspace_error_word() == 0
+
 @pytest.mark.parametrize("M", [1, 16, 32])
 def test_forward_group_small_and_large_v(M):
     # One call with a member with a 288 KiB V and one with 2.6 MiB.
