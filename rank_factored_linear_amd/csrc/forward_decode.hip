@@ -630,9 +630,10 @@ struct GroupArgs {
 };
 
 // Waves per SIMD that the register budget is cut for: four (two workgroups
-// per compute unit), except for the 64-token, 64-row variant, whose
-// accumulators need more registers (one workgroup per compute unit).
-template <int NT, int TILES> constexpr int decode_waves_per_eu() { return NT * TILES >= 16 ? 2 : 4; }
+// per compute unit), except for the 32-token, 96-row and the 64-token,
+// 64-row variants, whose accumulators need more registers (one workgroup per
+// compute unit).
+template <int NT, int TILES> constexpr int decode_waves_per_eu() { return NT * TILES >= 12 ? 2 : 4; }
 
 template <typename E, int NT, int TILES>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<NT, TILES>()))) void
@@ -671,7 +672,8 @@ hipError_t launch_e(int NT, int TILES, const GroupArgs& g, hipStream_t stream) {
     switch (TILES) {
       case 1: return launch_t<E, 2, 1>(g, stream);
       case 2: return launch_t<E, 2, 2>(g, stream);
-      default: return launch_t<E, 2, 4>(g, stream);
+      case 4: return launch_t<E, 2, 4>(g, stream);
+      default: return launch_t<E, 2, 6>(g, stream);
     }
   }
   if (TILES == 1) return launch_t<E, 4, 1>(g, stream);
@@ -683,8 +685,8 @@ hipError_t launch_e(int NT, int TILES, const GroupArgs& g, hipStream_t stream) {
 
 namespace {
 // Rows of a streaming workgroup at most: the widest tile set of each NT.
-// Every row block re-reads x, so at 33-64 tokens wide blocks matter most.
-int64_t decode_max_rows(int NT) { return 16 * (NT == 1 ? 6 : 4); }
+// Every row block re-reads x, so the more tokens, the more wide blocks matter.
+int64_t decode_max_rows(int NT) { return 16 * (NT <= 2 ? 6 : 4); }
 // Producer k-slices: about 768 of in_dim (three k32 steps per wave, one
 // round of loads at 16 tokens) when T must be ready early; about 2816
 // (eleven steps per wave) when the launch streams at least 112 MiB of W0

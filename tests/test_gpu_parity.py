@@ -272,10 +272,10 @@ def test_forward_small_v(shape, M):
 
 
 
-# 33-64 tokens: 64-row streaming tiles (TILES = 4 with NT = 4), ragged row
-# blocks and k tails, both dtypes.
+# 17-64 tokens: the widest streaming tiles (96 rows with NT = 2, 64 rows with
+# NT = 4), ragged row blocks and k tails, both dtypes.
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
-@pytest.mark.parametrize("M", [33, 48, 64])
+@pytest.mark.parametrize("M", [17, 32, 33, 48, 64])
 @pytest.mark.parametrize("shape", [(8192, 5376, 256), (2100, 1032, 136), (21504, 1152, 128), (700, 4104, 40)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_forward_wide_rows_many_tokens(shape, M, dtype):
