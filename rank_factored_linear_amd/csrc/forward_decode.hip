@@ -688,11 +688,11 @@ namespace {
 // Every row block re-reads x, so the more tokens, the more wide blocks matter.
 int64_t decode_max_rows(int NT) { return 16 * (NT <= 2 ? 6 : 4); }
 // Producer k-slices: about 768 of in_dim (three k32 steps per wave, one
-// round of loads at 16 tokens) when T must be ready early; about 2816
-// (eleven steps per wave) when the launch streams at least 112 MiB of W0
-// (over ~20 us), which hides the longer chain and leaves fewer producers to
-// share compute units with the streamers.
-constexpr int64_t kShortSlice = 768, kLongSlice = 2816;
+// round of loads at 16 tokens) when T must be ready early; about 5632
+// (22 steps per wave) when the launch streams at least 112 MiB of W0 (over
+// ~20 us), which hides the longer chain and leaves fewer producers to share
+// compute units with the streamers.
+constexpr int64_t kShortSlice = 768, kLongSlice = 5632;
 constexpr int64_t kLongStreamBytes = int64_t(112) << 20;
 }  // namespace
 
