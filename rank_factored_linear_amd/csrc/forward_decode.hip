@@ -630,9 +630,9 @@ struct GroupArgs {
 };
 
 // Waves per SIMD that the register budget is cut for: four (two workgroups
-// per compute unit), except for the 32-token, 96-row and the 64-token,
-// 64-row variants, whose accumulators need more registers (one workgroup per
-// compute unit).
+// per compute unit), except for the variants of 32 tokens x 96 rows and of
+// 64 tokens x 64 or 96 rows, whose accumulators need more registers (one
+// workgroup per compute unit).
 template <int NT, int TILES> constexpr int decode_waves_per_eu() { return NT * TILES >= 12 ? 2 : 4; }
 
 template <typename E, int NT, int TILES>
@@ -678,15 +678,16 @@ hipError_t launch_e(int NT, int TILES, const GroupArgs& g, hipStream_t stream) {
   }
   if (TILES == 1) return launch_t<E, 4, 1>(g, stream);
   if (TILES == 2) return launch_t<E, 4, 2>(g, stream);
-  return launch_t<E, 4, 4>(g, stream);
+  if (TILES == 4) return launch_t<E, 4, 4>(g, stream);
+  return launch_t<E, 4, 6>(g, stream);
 }
 
 }  // namespace
 
 namespace {
-// Rows of a streaming workgroup at most: the widest tile set of each NT.
+// Rows of a streaming workgroup at most (six 16-row tiles at every NT).
 // Every row block re-reads x, so the more tokens, the more wide blocks matter.
-int64_t decode_max_rows(int NT) { return 16 * (NT <= 2 ? 6 : 4); }
+int64_t decode_max_rows(int) { return 96; }
 // Producer k-slices: about 768 of in_dim (three k32 steps per wave, one
 // round of loads at 16 tokens) when T must be ready early; about 5632
 // (22 steps per wave) when the launch streams at least 112 MiB of W0 (over

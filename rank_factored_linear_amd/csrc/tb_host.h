@@ -73,7 +73,7 @@ hipError_t launch_forward_decode_group(int n, const DecodePlan* plans, const Dec
 
 // Workgroups per compute unit that a shared plan may fill (the decode kernel
 // keeps two resident per compute unit; one for 32 tokens x 96 rows and for
-// 64 tokens x 64 rows).
+// 64 tokens x 64 or 96 rows).
 constexpr int kMaxDecodeSlots = 2;
 // Plans for the members of one launch that share slots * cus workgroups:
 // every producer keeps its workgroup and the streamers are shared out in
