@@ -7,6 +7,7 @@ or <= 1e-5 (fp32); band indices and rank-0 fp32 reconstruction bit-exact.
 Large workloads compare sampled outputs that the oracle computes row by row.
 """
 
+import ctypes
 import os
 
 import numpy as np
@@ -533,6 +534,36 @@ def test_forward_group_matches_single_calls(group, M):
             assert oracle.relative_frobenius_error(_oracle_forward(*mbr), exact(y)) <= BF16_TOL
     assert tb.workspace_error_word() == 0
 
+
+
+WIDE_GROUP = [(8192, 5376, 256), (17, 40, 4), (2048, 5376, 256), (130, 264, 12), (6912, 1152, 128), (100, 264, 300),
+              (21504, 1152, 0), (33, 72, 0)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("M", [1, 16, 17, 32, 33, 64])
+def test_group_stays_inside_its_workspace(M, dtype):
+    # Eight members of very different sizes share the chip in one launch; a
+    # guard band right after the queried workspace must stay untouched, and
+    # every member must match its own call within the tolerance.
+    _say(f"workspace guard M={M} {dtype}")
+    members = [_rand_case(M, O, I, R, dtype, seed=7 * j + M) for j, (O, I, R) in enumerate(WIDE_GROUP)]
+    dims = [(x, s_, W0, U, V, torch.empty((M, W0.shape[0]), dtype=dtype, device=DEV)) for x, s_, W0, U, V in members]
+    need = ctypes.c_size_t(0)
+    assert tb.lib.tb_linear_forward_group_workspace_size(len(dims), tb.projection_array(dims), M,
+                                                          tb._dtype_code(dtype), ctypes.byref(need)) == 0
+    guard = 1 << 20
+    buf = torch.zeros(need.value + guard, dtype=torch.uint8, device=DEV)
+    buf[need.value:] = 0xA5
+    ys = tb.linear_forward_group(members, workspace=buf[:need.value])
+    singles = [tb.linear_forward(*mbr) for mbr in members]
+    torch.cuda.synchronize()
+    assert bool((buf[need.value:] == 0xA5).all())
+    assert int(buf[:tb.WORKSPACE_CONTROL_BYTES].count_nonzero().item()) == 0
+    for y, y1 in zip(ys, singles):
+        assert oracle.relative_frobenius_error(exact(y1), exact(y)) <= tol_for(dtype)
+    for mbr, y in list(zip(members, ys))[1::2]:   # the small members against the oracle
+        assert oracle.relative_frobenius_error(_oracle_forward(*mbr), exact(y)) <= tol_for(dtype)
 
 def test_forward_group_fp32_and_clean_workspace():
     members = [_rand_case(8, O, I, R, torch.float32, seed=O) for (O, I, R) in GROUPS["ragged"]]
