@@ -99,7 +99,8 @@ namespace {
 size_t forward_data_bytes(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, tb_dtype dtype, int cus) {
   if (dtype == TB_BF16 && m > kDecodeMaxTokens) return plan_gemm(m, out_dim, in_dim, rank, cus).bytes;
   size_t bytes = 0;
-  const int64_t counts[2] = {m < kDecodeMaxTokens ? m : kDecodeMaxTokens, m > kDecodeMaxTokens ? m % kDecodeMaxTokens : 0};
+  const int64_t counts[2] = {m < kDecodeMaxTokens ? m : kDecodeMaxTokens,
+                             m > kDecodeMaxTokens ? m % kDecodeMaxTokens : 0};
   for (int64_t mt : counts)
     if (mt > 0) bytes = std::max(bytes, decode_bytes_bound(mt, out_dim, in_dim, rank, cus));
   return bytes;
@@ -142,7 +143,6 @@ tb_status check_projection(const void* x, const void* s, const void* w0, const v
     return fail(TB_ERR_UNSUPPORTED, "in_dim %lld is too large for the few-token path", (long long)in_dim);
   return TB_OK;
 }
-
 
 // One projection with checked arguments: the prefill GEMM, or the decode
 // kernel over 64-token slices.  ctrl is its control block, data holds
