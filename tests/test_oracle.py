@@ -233,6 +233,53 @@ def check_refine_shared_block(impl) -> None:
         assert np.max(np.abs(a2["W0"][a2["band"][l]] - w[l])) <= 1e-15 and np.allclose(a2["s"][l], 1.0, atol=1e-15)
 
 
+def _als_stack():
+    """Four 12 x 9 layers in two bands: a per-band block under per-row scales, a rank-3 term and noise."""
+    r = np.random.default_rng(13)
+    O, I = 12, 9
+    B = [r.normal(size=(O, I)) for _ in range(2)]
+    return [r.uniform(0.6, 1.4, size=O)[:, None] * B[l // 2] + r.normal(size=(O, 3)) @ r.normal(size=(3, I))
+            + 0.3 * r.normal(size=(O, I)) for l in range(4)]
+
+
+def check_als_decompose(impl) -> None:
+    # Invariants of the bundle returned after one and two rounds, each checked
+    # with numbers the oracle does not compute itself.
+    Ws, G, rank = _als_stack(), 2, 2
+    for iters in (1, 2):
+        prev = impl.als_decompose(Ws, G, rank, iters - 1)
+        cur = impl.als_decompose(Ws, G, rank, iters)
+        assert cur["band"] == [0, 0, 1, 1]
+        for l, w in enumerate(Ws):
+            w0 = cur["W0"][cur["band"][l]]
+            s, U, V = cur["s"][l], cur["U"][l], cur["V"][l]
+            # (a) s is the row-wise least-squares fit against the RETURNED block:
+            #     the residual row is orthogonal to the block row.
+            for o in range(w.shape[0]):
+                assert abs(np.dot(w[o] - s[o] * w0[o], w0[o])) <= 1e-11 * np.dot(w0[o], w0[o]), (iters, l, o)
+            # (b) U V^T is the Eckart-Young cut of the RETURNED residual: its error
+            #     is the sum of the residual's smallest squared singular values,
+            #     taken here from the eigenvalues of the Gram matrix (another
+            #     library routine than the oracle's SVD); V is orthonormal and U = E V.
+            E = w - s[:, None] * w0
+            lam = np.sort(np.linalg.eigvalsh(E.T @ E))[::-1]
+            tail = float(np.sum(np.clip(lam[rank:], 0.0, None)))
+            assert np.sum((E - U @ V.T) ** 2) == pytest.approx(tail, rel=1e-9, abs=1e-12), (iters, l)
+            assert np.allclose(V.T @ V, np.eye(rank), atol=1e-12) and np.allclose(U, E @ V, atol=1e-11)
+        # (c) Each returned block solves the block least-squares problem for the
+        #     PREVIOUS round's scales and factors: the normal equations
+        #     sum_l s_l[o] (W_l - s_l[o] W0 - U_l V_l^T)[o] = 0 hold row by row.
+        for b in range(G):
+            members = [l for l in range(len(Ws)) if cur["band"][l] == b]
+            w0 = cur["W0"][b]
+            for o in range(w0.shape[0]):
+                g = sum(prev["s"][l][o] * (Ws[l] - prev["s"][l][o] * w0 - prev["U"][l] @ prev["V"][l].T)[o]
+                        for l in members)
+                assert np.max(np.abs(g)) <= 1e-11, (iters, b, o)
+        # A round changes the block (the pins above are not met trivially).
+        assert max(np.max(np.abs(a - c)) for a, c in zip(prev["W0"], cur["W0"])) > 1e-3
+
+
 def check_decompose(impl) -> None:
     r = np.random.default_rng(10)
     # Passthrough (G = L): W0 = W, s = 1 exactly, delta 0 and error exactly 0.
@@ -264,7 +311,7 @@ def check_decompose(impl) -> None:
 
 ALL_CHECKS = [check_band_map, check_forward, check_reconstruct, check_frobenius,
               check_row_scale, check_truncated_factors, check_randomized_factors, check_refine_shared_block,
-              check_decompose]
+              check_als_decompose, check_decompose]
 
 
 # ---------------------------------------------------------------------------
@@ -495,7 +542,46 @@ def _refine_without_delta(weights, s_list, U_list, V_list, W0_prev):
     return tb.refine_shared_block(weights, s_list, [0 * U for U in U_list], V_list, W0_prev)
 
 
+def _als_variant(weights, num_bands, rank, iters, *, s_from_old_block=False, keep_factors=False,
+                 block_from_first_round=False, refit_before_block=False):
+    """als_decompose with one planted mistake (each keyword plants one)."""
+    weights = [np.asarray(w, dtype=np.float64) for w in weights]
+    bun = tb.decompose(weights, num_bands, rank)
+    first = {k: list(bun[k]) for k in ("s", "U", "V")}
+    bands = bun["band"]
+
+    def refit_layers(blocks_for_s, blocks_for_delta):
+        for l, w in enumerate(weights):
+            s = tb.row_scale(w, blocks_for_s[bands[l]])
+            if not keep_factors:
+                bun["U"][l], bun["V"][l] = tb.truncated_factors(w - np.diag(s) @ blocks_for_delta[bands[l]], rank)
+            bun["s"][l] = s
+
+    for _ in range(iters):
+        if refit_before_block:
+            refit_layers(bun["W0"], bun["W0"])
+        old = list(bun["W0"])
+        src = first if block_from_first_round else bun
+        for b in range(num_bands):
+            members = [l for l in range(len(weights)) if bands[l] == b]
+            bun["W0"][b] = tb.refine_shared_block([weights[l] for l in members], [src["s"][l] for l in members],
+                                                  [src["U"][l] for l in members], [src["V"][l] for l in members],
+                                                  bun["W0"][b])
+        if not refit_before_block:
+            refit_layers(old if s_from_old_block else bun["W0"], bun["W0"])
+    return bun
+
+
+def _als(**plant):
+    return lambda weights, num_bands, rank, iters: _als_variant(weights, num_bands, rank, iters, **plant)
+
+
 MUTANTS = [
+    ("ALS: s refit against the previous block", check_als_decompose, dict(als_decompose=_als(s_from_old_block=True))),
+    ("ALS: U, V not refit", check_als_decompose, dict(als_decompose=_als(keep_factors=True))),
+    ("ALS: block refit from the first round's factors", check_als_decompose,
+     dict(als_decompose=_als(block_from_first_round=True))),
+    ("ALS: layers refit before the block", check_als_decompose, dict(als_decompose=_als(refit_before_block=True))),
     ("band remainder to the last bands", check_band_map,
      dict(band_sizes=_remainder_last_sizes, band_map=_remainder_last_map,
           band_index=lambda L, G, l: _remainder_last_map(L, G)[l])),
@@ -526,3 +612,12 @@ MUTANTS = [
 def test_planted_mistake_is_caught(name, check, overrides):
     with pytest.raises(AssertionError):
         check(_mutant(**overrides))
+
+
+def test_als_variant_without_a_plant_passes():
+    # The harness that plants the ALS mistakes computes the oracle's rounds
+    # when nothing is planted, so each caught mutant differs by its plant only.
+    check_als_decompose(_mutant(als_decompose=_als()))
+    w = _als_stack()
+    a, b = tb.als_decompose(w, 2, 2, 2), _als()(w, 2, 2, 2)
+    assert all(np.array_equal(p, q) for p, q in zip(a["W0"], b["W0"]))
