@@ -112,12 +112,74 @@ def _stream() -> ctypes.c_void_p:
 
 
 def _need_cuda(*ts):
+    """Every tensor is contiguous and lives on the current GPU (the device the library launches on)."""
     for t in ts:
         if t is not None:
             if not t.is_cuda:
                 raise TBError(TB_ERR_INVALID_ARGUMENT, "tensors must live on the GPU")
+            if t.device.index != torch.cuda.current_device():
+                raise TBError(TB_ERR_INVALID_ARGUMENT,
+                              f"tensor on {t.device}, but the current device is cuda:{torch.cuda.current_device()}")
             if not t.is_contiguous():
                 raise TBError(TB_ERR_UNSUPPORTED, "tensors must be contiguous")
+
+
+# Shape and dtype checks run before the device checks and before anything
+# crosses the C ABI: the library sees raw pointers only, so a mis-sized
+# tensor would otherwise become out-of-bounds device reads or writes.
+
+
+def _expect(name: str, t: torch.Tensor, shape, dtype: torch.dtype | None = None) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise TBError(TB_ERR_INVALID_ARGUMENT, f"{name} must be {list(shape)}, got {list(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TBError(TB_ERR_INVALID_ARGUMENT, f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _expect_out(out: torch.Tensor | None, shape, dtype: torch.dtype | None = None) -> None:
+    if out is not None:
+        _expect("out", out, shape, dtype)
+
+
+def _output(out: torch.Tensor | None, shape, dtype: torch.dtype, like: torch.Tensor) -> torch.Tensor:
+    """A new output of this shape and dtype on like's device, or the caller's `out` after checking it."""
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    _expect("out", out, shape, dtype)
+    if out.device != like.device:
+        raise TBError(TB_ERR_INVALID_ARGUMENT, f"out is on {out.device}, the inputs on {like.device}")
+    return out
+
+
+def _projection_dims(x, s, W0, U, V):
+    """(m, out_dim, in_dim, rank, U, V) of one projection after checking every operand against x and W0:
+    x [m, in], W0 [out, in], s [out] or None, U [out, rank] and V [in, rank] or both None; one dtype.
+    A rank-0 U/V pair becomes None."""
+    if x.dim() != 2 or W0.dim() != 2:
+        raise TBError(TB_ERR_INVALID_ARGUMENT, "x must be [m, in] and W0 [out, in]")
+    _dtype_code(x.dtype)
+    m, in_dim = x.shape
+    out_dim = W0.shape[0]
+    _expect("W0", W0, (out_dim, in_dim), x.dtype)
+    if s is not None:
+        _expect("s", s, (out_dim,), x.dtype)
+    if (U is None) != (V is None):
+        raise TBError(TB_ERR_INVALID_ARGUMENT, "U and V are given together or not at all")
+    rank = 0
+    if U is not None:
+        if U.dim() != 2:
+            raise TBError(TB_ERR_INVALID_ARGUMENT, "U must be [out, rank]")
+        rank = U.shape[1]
+        _expect("U", U, (out_dim, rank), x.dtype)
+        _expect("V", V, (in_dim, rank), x.dtype)
+        if rank == 0:
+            U = V = None
+    return m, out_dim, in_dim, rank, U, V
+
+
+def _workspace_bytes(ws: torch.Tensor) -> int:
+    _need_cuda(ws)
+    return ws.numel() * ws.element_size()
 
 
 # ---------------------------------------------------------------------------
@@ -172,45 +234,28 @@ def linear_forward(x: torch.Tensor, s: torch.Tensor | None, W0: torch.Tensor, U:
                    V: torch.Tensor | None, out: torch.Tensor | None = None,
                    workspace: torch.Tensor | None = None) -> torch.Tensor:
     """y = s * (x @ W0.T) + (x @ V) @ U.T on the GPU, via tb_linear_forward (s None: unit scale)."""
-    m, in_dim = x.shape
-    out_dim = W0.shape[0]
-    rank = 0 if U is None else U.shape[1]
-    if U is not None and rank == 0:
-        U = V = None
+    m, out_dim, in_dim, rank, U, V = _projection_dims(x, s, W0, U, V)
+    _expect_out(out, (m, out_dim), x.dtype)
     _need_cuda(x, s, W0, U, V, out)
-    dt = _dtype_code(x.dtype)
-    for t in (s, W0, U, V):
-        if t is not None and t.dtype != x.dtype:
-            raise TBError(TB_ERR_INVALID_ARGUMENT, "all inputs must share one dtype")
-    if tuple(W0.shape) != (out_dim, in_dim) or (s is not None and tuple(s.shape) != (out_dim,)):
-        raise TBError(TB_ERR_INVALID_ARGUMENT, "W0 must be [out, in] and s [out]")
-    if rank and (tuple(U.shape) != (out_dim, rank) or tuple(V.shape) != (in_dim, rank)):
-        raise TBError(TB_ERR_INVALID_ARGUMENT, "U must be [out, rank] and V [in, rank]")
-    if out is None:
-        out = torch.empty((m, out_dim), dtype=x.dtype, device=x.device)
+    out = _output(out, (m, out_dim), x.dtype, x)
     need = linear_forward_workspace_size(m, out_dim, in_dim, rank, x.dtype)
     ws = workspace if workspace is not None else workspace_for(need)
     _check(lib.tb_linear_forward(_ptr(x), _ptr(s), _ptr(W0), _ptr(U), _ptr(V), _ptr(out), m, out_dim, in_dim, rank,
-                                 dt, _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+                                 _dtype_code(x.dtype), _ptr(ws), _workspace_bytes(ws), _stream()))
     return out
 
 
 def dense_forward(x: torch.Tensor, W: torch.Tensor, out: torch.Tensor | None = None,
                   workspace: torch.Tensor | None = None) -> torch.Tensor:
     """y = x @ W.T on the GPU, via tb_dense_forward (a weight materialised once, e.g. by reconstruct_weight)."""
-    m, in_dim = x.shape
-    out_dim = W.shape[0]
+    m, out_dim, in_dim, _, _, _ = _projection_dims(x, None, W, None, None)
+    _expect_out(out, (m, out_dim), x.dtype)
     _need_cuda(x, W, out)
-    if W.dtype != x.dtype:
-        raise TBError(TB_ERR_INVALID_ARGUMENT, "x and W must share one dtype")
-    if tuple(W.shape) != (out_dim, in_dim):
-        raise TBError(TB_ERR_INVALID_ARGUMENT, "W must be [out, in]")
-    if out is None:
-        out = torch.empty((m, out_dim), dtype=x.dtype, device=x.device)
+    out = _output(out, (m, out_dim), x.dtype, x)
     need = linear_forward_workspace_size(m, out_dim, in_dim, 0, x.dtype)
     ws = workspace if workspace is not None else workspace_for(need)
     _check(lib.tb_dense_forward(_ptr(x), _ptr(W), _ptr(out), m, out_dim, in_dim, _dtype_code(x.dtype), _ptr(ws),
-                                ws.numel() * ws.element_size(), _stream()))
+                                _workspace_bytes(ws), _stream()))
     return out
 
 
@@ -224,69 +269,85 @@ def projection_array(members) -> ctypes.Array:
     return arr
 
 
-def linear_forward_group(members, workspace: torch.Tensor | None = None) -> list:
+def linear_forward_group(members, workspace: torch.Tensor | None = None, outs=None) -> list:
     """Several independent projections [(x, s, W0, U, V), ...] of one token count and dtype in one call
-    (tb_linear_forward_group); returns their outputs."""
+    (tb_linear_forward_group); returns their outputs (written into `outs` when given)."""
     if not 1 <= len(members) <= MAX_GROUP:
         raise TBError(TB_ERR_INVALID_ARGUMENT, f"a group holds 1..{MAX_GROUP} projections")
-    m = members[0][0].shape[0]
-    dtype = members[0][0].dtype
-    full = []
-    for x, s, W0, U, V in members:
-        _need_cuda(x, s, W0, U, V)
-        if x.shape[0] != m or x.dtype != dtype:
+    if outs is not None and len(outs) != len(members):
+        raise TBError(TB_ERR_INVALID_ARGUMENT, "one output per member")
+    dims = []
+    for j, (x, s, W0, U, V) in enumerate(members):
+        m, out_dim, in_dim, rank, U, V = _projection_dims(x, s, W0, U, V)
+        if m != members[0][0].shape[0] or x.dtype != members[0][0].dtype:
             raise TBError(TB_ERR_INVALID_ARGUMENT, "group members must share the token count and dtype")
-        for t in (s, W0, U, V):
-            if t is not None and t.dtype != dtype:
-                raise TBError(TB_ERR_INVALID_ARGUMENT, "all inputs must share one dtype")
-        if U is not None and U.shape[1] == 0:
-            U = V = None
-        y = torch.empty((m, W0.shape[0]), dtype=dtype, device=x.device)
+        if outs is not None:
+            _expect_out(outs[j], (m, out_dim), x.dtype)
+        dims.append((x, s, W0, U, V))
+    full = []
+    for j, (x, s, W0, U, V) in enumerate(dims):
+        _need_cuda(x, s, W0, U, V)
+        y = _output(None if outs is None else outs[j], (x.shape[0], W0.shape[0]), x.dtype, x)
+        _need_cuda(y)
         full.append((x, s, W0, U, V, y))
+    m, dtype = members[0][0].shape[0], members[0][0].dtype
     arr = projection_array(full)
     need = ctypes.c_size_t(0)
     _check(lib.tb_linear_forward_group_workspace_size(len(full), arr, m, _dtype_code(dtype), ctypes.byref(need)))
     ws = workspace if workspace is not None else workspace_for(need.value)
-    _check(lib.tb_linear_forward_group(len(full), arr, m, _dtype_code(dtype), _ptr(ws), ws.numel() * ws.element_size(),
+    _check(lib.tb_linear_forward_group(len(full), arr, m, _dtype_code(dtype), _ptr(ws), _workspace_bytes(ws),
                                        _stream()))
     return [f[5] for f in full]
 
 
+def _bundle_dims(s, W0, U, V):
+    """(out_dim, in_dim, rank, U, V) of a bundle after checking s [out], U [out, rank], V [in, rank] against W0
+    (one dtype); a rank-0 U/V pair becomes None."""
+    if W0.dim() != 2:
+        raise TBError(TB_ERR_INVALID_ARGUMENT, "W0 must be [out, in]")
+    _dtype_code(W0.dtype)
+    out_dim, in_dim = W0.shape
+    _expect("s", s, (out_dim,), W0.dtype)
+    if (U is None) != (V is None):
+        raise TBError(TB_ERR_INVALID_ARGUMENT, "U and V are given together or not at all")
+    rank = 0
+    if U is not None:
+        if U.dim() != 2:
+            raise TBError(TB_ERR_INVALID_ARGUMENT, "U must be [out, rank]")
+        rank = U.shape[1]
+        _expect("U", U, (out_dim, rank), W0.dtype)
+        _expect("V", V, (in_dim, rank), W0.dtype)
+        if rank == 0:
+            U = V = None
+    return out_dim, in_dim, rank, U, V
+
+
 def reconstruct_weight(s: torch.Tensor, W0: torch.Tensor, U: torch.Tensor | None, V: torch.Tensor | None,
                        out_dtype: torch.dtype = torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
-    """diag(s) @ W0 + U @ V.T on the GPU, via tb_reconstruct_weight."""
-    out_dim, in_dim = W0.shape
-    rank = 0 if U is None else U.shape[1]
-    if U is not None and rank == 0:
-        U = V = None
+    """diag(s) @ W0 + U @ V.T on the GPU, via tb_reconstruct_weight (into `out` when given; its dtype wins)."""
+    out_dim, in_dim, rank, U, V = _bundle_dims(s, W0, U, V)
+    _expect_out(out, (out_dim, in_dim))
     _need_cuda(s, W0, U, V, out)
-    if out is None:
-        out = torch.empty((out_dim, in_dim), dtype=out_dtype, device=W0.device)
+    out = _output(out, (out_dim, in_dim), out_dtype if out is None else out.dtype, W0)
     _check(lib.tb_reconstruct_weight(_ptr(s), _ptr(W0), _ptr(U), _ptr(V), _ptr(out), out_dim, in_dim, rank,
                                      _dtype_code(W0.dtype), _dtype_code(out.dtype), _stream()))
     return out
 
 
-_frob_ws: dict = {}
+def _expect_error_out(out: torch.Tensor | None) -> None:
+    """The error lands in one device double."""
+    if out is not None and (out.dtype != torch.float64 or out.numel() != 1):
+        raise TBError(TB_ERR_INVALID_ARGUMENT, f"out must hold one float64, got {out.dtype} {list(out.shape)}")
 
 
-def rel_frobenius_error(original: torch.Tensor, reconstructed: torch.Tensor,
-                        out: torch.Tensor | None = None) -> torch.Tensor:
-    """||original - reconstructed||_F / ||original||_F as a 0-d float64 GPU tensor (no sync)."""
-    _need_cuda(original, reconstructed, out)
-    if original.shape != reconstructed.shape or original.dtype != reconstructed.dtype or original.dim() != 2:
-        raise TBError(TB_ERR_INVALID_ARGUMENT, "original and reconstructed must be 2-D with one shape and dtype")
-    rows, cols = original.shape
+def _error_output(out: torch.Tensor | None, like: torch.Tensor) -> torch.Tensor:
     if out is None:
-        out = torch.empty((), dtype=torch.float64, device=original.device)
-    key = (torch.cuda.current_device(), torch.cuda.current_stream().cuda_stream)
-    ws = _frob_ws.get(key)
-    if ws is None:
-        ws = torch.zeros(FROBENIUS_WORKSPACE_BYTES, dtype=torch.uint8, device=original.device)
-        _frob_ws[key] = ws
-    _check(lib.tb_rel_frobenius_error(_ptr(original), _ptr(reconstructed), rows, cols, _dtype_code(original.dtype),
-                                      _ptr(out), _ptr(ws), ws.numel(), _stream()))
+        return torch.empty((), dtype=torch.float64, device=like.device)
+    _need_cuda(out)
     return out
+
+
+_frob_ws: dict = {}
 
 
 def _error_workspace() -> torch.Tensor:
@@ -298,22 +359,33 @@ def _error_workspace() -> torch.Tensor:
     return ws
 
 
+def rel_frobenius_error(original: torch.Tensor, reconstructed: torch.Tensor,
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """||original - reconstructed||_F / ||original||_F as a 0-d float64 GPU tensor (no sync)."""
+    if original.dim() != 2:
+        raise TBError(TB_ERR_INVALID_ARGUMENT, "original must be 2-D")
+    _dtype_code(original.dtype)
+    _expect("reconstructed", reconstructed, original.shape, original.dtype)
+    _expect_error_out(out)
+    _need_cuda(original, reconstructed)
+    rows, cols = original.shape
+    out = _error_output(out, original)
+    ws = _error_workspace()
+    _check(lib.tb_rel_frobenius_error(_ptr(original), _ptr(reconstructed), rows, cols, _dtype_code(original.dtype),
+                                      _ptr(out), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
 def reconstruction_error(original: torch.Tensor, s: torch.Tensor, W0: torch.Tensor, U: torch.Tensor | None,
                          V: torch.Tensor | None, out: torch.Tensor | None = None) -> torch.Tensor:
     """relative_frobenius_error(original, diag(s) @ W0 + U @ V.T) without forming the rebuilt weight, as a 0-d
     float64 GPU tensor (no sync), via tb_reconstruction_error."""
-    out_dim, in_dim = W0.shape
-    rank = 0 if U is None else U.shape[1]
-    if U is not None and rank == 0:
-        U = V = None
-    _need_cuda(original, s, W0, U, V, out)
-    if tuple(original.shape) != (out_dim, in_dim):
-        raise TBError(TB_ERR_INVALID_ARGUMENT, "original must have W0's shape")
-    for t in (s, U, V):
-        if t is not None and t.dtype != W0.dtype:
-            raise TBError(TB_ERR_INVALID_ARGUMENT, "s, W0, U and V must share one dtype")
-    if out is None:
-        out = torch.empty((), dtype=torch.float64, device=W0.device)
+    out_dim, in_dim, rank, U, V = _bundle_dims(s, W0, U, V)
+    _expect("original", original, (out_dim, in_dim))
+    _dtype_code(original.dtype)
+    _expect_error_out(out)
+    _need_cuda(original, s, W0, U, V)
+    out = _error_output(out, W0)
     ws = _error_workspace()
     _check(lib.tb_reconstruction_error(_ptr(s), _ptr(W0), _ptr(U), _ptr(V), _ptr(original), out_dim, in_dim, rank,
                                        _dtype_code(W0.dtype), _dtype_code(original.dtype), _ptr(out), _ptr(ws),
@@ -331,13 +403,14 @@ def shared_block(weights, out: torch.Tensor | None = None) -> torch.Tensor:
     n = len(weights)
     if not 1 <= n <= MAX_BAND_LAYERS:
         raise TBError(TB_ERR_INVALID_ARGUMENT, f"a band holds 1..{MAX_BAND_LAYERS} layers")
+    if weights[0].dim() != 2:
+        raise TBError(TB_ERR_INVALID_ARGUMENT, "weights must be [out, in]")
     out_dim, in_dim = weights[0].shape
-    for w in weights:
-        _need_cuda(w)
-        if tuple(w.shape) != (out_dim, in_dim) or w.dtype != weights[0].dtype:
-            raise TBError(TB_ERR_INVALID_ARGUMENT, "a band's matrices share one shape and dtype")
-    if out is None:
-        out = torch.empty((out_dim, in_dim), dtype=torch.float32, device=weights[0].device)
+    for j, w in enumerate(weights):
+        _expect(f"weights[{j}]", w, (out_dim, in_dim), weights[0].dtype)
+    _expect_out(out, (out_dim, in_dim), torch.float32)
+    _need_cuda(*weights, out)
+    out = _output(out, (out_dim, in_dim), torch.float32, weights[0])
     ptrs = (ctypes.c_void_p * n)(*[w.data_ptr() for w in weights])
     _check(lib.tb_shared_block(ptrs, n, out_dim, in_dim, _dtype_code(weights[0].dtype), _ptr(out), _stream()))
     return out
@@ -345,11 +418,12 @@ def shared_block(weights, out: torch.Tensor | None = None) -> torch.Tensor:
 
 def row_scale(weight: torch.Tensor, W0: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """Per-row least-squares scale of weight against W0 (fp32 [out]), via tb_row_scale."""
-    _need_cuda(weight, W0)
-    if W0.dtype != torch.float32 or W0.shape != weight.shape:
-        raise TBError(TB_ERR_INVALID_ARGUMENT, "W0 must be fp32 with the weight's shape")
-    if out is None:
-        out = torch.empty(weight.shape[0], dtype=torch.float32, device=weight.device)
+    if weight.dim() != 2:
+        raise TBError(TB_ERR_INVALID_ARGUMENT, "weight must be [out, in]")
+    _expect("W0", W0, weight.shape, torch.float32)
+    _expect_out(out, (weight.shape[0],), torch.float32)
+    _need_cuda(weight, W0, out)
+    out = _output(out, (weight.shape[0],), torch.float32, weight)
     _check(lib.tb_row_scale(_ptr(weight), _ptr(W0), weight.shape[0], weight.shape[1], _dtype_code(weight.dtype),
                             _ptr(out), _stream()))
     return out
@@ -365,14 +439,14 @@ def lowrank_factors(weight: torch.Tensor, W0: torch.Tensor, s: torch.Tensor, ran
                     power_iters: int, workspace: torch.Tensor | None = None):
     """U [out, rank], V [in, rank] (fp32) of weight - diag(s) W0 by the randomized SVD with probe omega [in, k],
     via tb_lowrank_factors."""
-    _need_cuda(weight, W0, s, omega)
+    if weight.dim() != 2 or omega.dim() != 2:
+        raise TBError(TB_ERR_INVALID_ARGUMENT, "weight must be [out, in] and omega [in, k]")
     out_dim, in_dim = weight.shape
     k = omega.shape[1]
-    for t in (W0, s, omega):
-        if t.dtype != torch.float32:
-            raise TBError(TB_ERR_INVALID_ARGUMENT, "W0, s and omega must be fp32")
-    if omega.shape[0] != in_dim:
-        raise TBError(TB_ERR_INVALID_ARGUMENT, "omega must be [in, k]")
+    _expect("W0", W0, (out_dim, in_dim), torch.float32)
+    _expect("s", s, (out_dim,), torch.float32)
+    _expect("omega", omega, (in_dim, k), torch.float32)
+    _need_cuda(weight, W0, s, omega)
     U = torch.zeros((out_dim, rank), dtype=torch.float32, device=weight.device)
     V = torch.zeros((in_dim, rank), dtype=torch.float32, device=weight.device)
     need = lowrank_factors_workspace_size(out_dim, in_dim, rank, k)
@@ -389,15 +463,19 @@ def lowrank_factors_batch(weights, W0s, S: torch.Tensor, rank: int, omega: torch
     """U [n, out, rank], V [n, in, rank] (fp32) for n weights of one shape, each with its shared block (W0s: one
     fp32 tensor for all, or a list of n), S [n, out], omega [n, in, k], via tb_lowrank_factors_batch."""
     n = len(weights)
+    if weights[0].dim() != 2 or omega.dim() != 3:
+        raise TBError(TB_ERR_INVALID_ARGUMENT, "weights must be [out, in] and omega [n, in, k]")
     out_dim, in_dim = weights[0].shape
     k = omega.shape[2]
     W0s = list(W0s) if isinstance(W0s, (list, tuple)) else [W0s] * n
+    if len(W0s) != n:
+        raise TBError(TB_ERR_INVALID_ARGUMENT, "one shared block per weight")
+    for j in range(n):
+        _expect(f"weights[{j}]", weights[j], (out_dim, in_dim), weights[0].dtype)
+        _expect(f"W0s[{j}]", W0s[j], (out_dim, in_dim), torch.float32)
+    _expect("S", S, (n, out_dim), torch.float32)
+    _expect("omega", omega, (n, in_dim, k), torch.float32)
     _need_cuda(S, omega, *weights, *W0s)
-    for t in (S, omega, *W0s):
-        if t.dtype != torch.float32:
-            raise TBError(TB_ERR_INVALID_ARGUMENT, "W0, S and omega must be fp32")
-    if tuple(S.shape) != (n, out_dim) or tuple(omega.shape[:2]) != (n, in_dim):
-        raise TBError(TB_ERR_INVALID_ARGUMENT, "S must be [n, out] and omega [n, in, k]")
     U = torch.zeros((n, out_dim, rank), dtype=torch.float32, device=S.device)
     V = torch.zeros((n, in_dim, rank), dtype=torch.float32, device=S.device)
     need = n * lowrank_factors_workspace_size(out_dim, in_dim, rank, k)
@@ -451,11 +529,20 @@ def refine_shared_block(weights, s_list, U_list, V_list, W0_prev: torch.Tensor,
     """Least-squares refit of a band's shared block with every layer's s, U, V fixed (fp32), via
     tb_refine_shared_block; `out` may be W0_prev itself."""
     n = len(weights)
+    if W0_prev.dim() != 2 or not (len(s_list) == len(U_list) == len(V_list) == n):
+        raise TBError(TB_ERR_INVALID_ARGUMENT, "W0_prev must be [out, in], with s, U, V lists as long as weights")
     out_dim, in_dim = W0_prev.shape
+    _expect("W0_prev", W0_prev, (out_dim, in_dim), torch.float32)
     rank = 0 if U_list[0] is None else U_list[0].shape[1]
+    for j in range(n):
+        _expect(f"weights[{j}]", weights[j], (out_dim, in_dim), weights[0].dtype)
+        _expect(f"s[{j}]", s_list[j], (out_dim,), torch.float32)
+        if rank:
+            _expect(f"U[{j}]", U_list[j], (out_dim, rank), torch.float32)
+            _expect(f"V[{j}]", V_list[j], (in_dim, rank), torch.float32)
+    _expect_out(out, (out_dim, in_dim), torch.float32)
     _need_cuda(W0_prev, out, *weights, *s_list, *(U_list if rank else []), *(V_list if rank else []))
-    if out is None:
-        out = torch.empty_like(W0_prev)
+    out = _output(out, (out_dim, in_dim), torch.float32, W0_prev)
     arr = lambda ts: (ctypes.c_void_p * n)(*[t.data_ptr() for t in ts])
     need = ctypes.c_size_t(0)
     _check(lib.tb_refine_shared_block_workspace_size(out_dim, in_dim, n, rank, ctypes.byref(need)))
