@@ -115,10 +115,15 @@ tb_status tb_linear_forward_workspace_size(int64_t m, int64_t out_dim, int64_t i
  *   bytes, 256-byte aligned.  Its first TB_WORKSPACE_CONTROL_BYTES bytes are
  *   control words: they must be zero before the first call that uses the
  *   buffer and must not be changed by the caller afterwards (each completed
- *   call, single or grouped, leaves all of them ready for the next; word 2 is
- *   a sticky error flag that becomes nonzero only if a bounded internal wait
- *   timed out, in which case that call's y is NaN).  Calls that may run at
- *   the same time (different streams) must not share a workspace.
+ *   call, single or grouped, leaves all of them ready for the next).  Word 2
+ *   (uint32) is a sticky error flag: it becomes nonzero only when a bounded
+ *   internal wait times out (the rows of y behind that wait are NaN), and a
+ *   timed-out call may leave other control words stale.  While word 2 is set,
+ *   every forward call on the workspace (tb_linear_forward, tb_dense_forward,
+ *   tb_linear_forward_group) writes NaN to all of its y and reads or writes no
+ *   other control word; zeroing the first TB_WORKSPACE_CONTROL_BYTES bytes
+ *   again makes the workspace usable.  Calls that may run at the same time
+ *   (different streams) must not share a workspace.
  *   Errors: TB_ERR_INVALID_ARGUMENT, TB_ERR_UNSUPPORTED, TB_ERR_HIP.
  */
 tb_status tb_linear_forward(const void *x, const void *s, const void *w0, const void *u, const void *v,
@@ -345,6 +350,17 @@ tb_status tb_refine_shared_block(const void *const *weights, const float *const 
                                  const float *const *v, int32_t n, int64_t out_dim, int64_t in_dim, int64_t rank,
                                  tb_dtype weight_dtype, const float *w0_prev, float *w0_out, void *workspace,
                                  size_t workspace_bytes, void *stream);
+
+/*
+ * tb_debug_set_wait_polls -- bound, in polls about 0.1 us apart, of the
+ * forward kernels' one internal wait (a decode streamer waiting for the
+ * x . V products of its launch); default 1 << 20 (about 0.1 s).  It applies to
+ * launches enqueued after the call, process-wide.  For tests of the timeout
+ * path: 0 makes every such wait give up at once, so word 2 of the workspace
+ * is set and y is NaN, with every kernel exiting normally.
+ *   polls >= 0.  Errors: TB_ERR_INVALID_ARGUMENT.  Host-only.
+ */
+tb_status tb_debug_set_wait_polls(int32_t polls);
 
 /* Static description of a status code. */
 const char *tb_status_string(tb_status status);

@@ -29,8 +29,9 @@ EXPORTED = (
     "tb_reconstruct_weight", "tb_rel_frobenius_error", "tb_reconstruction_error",
     "tb_shared_block", "tb_row_scale", "tb_lowrank_factors_workspace_size", "tb_lowrank_factors",
     "tb_lowrank_factors_batch", "tb_refine_shared_block_workspace_size", "tb_refine_shared_block",
-    "tb_status_string", "tb_last_error",
+    "tb_debug_set_wait_polls", "tb_status_string", "tb_last_error",
 )
+DEFAULT_WAIT_POLLS = 1 << 20
 MAX_BAND_LAYERS = 128
 MAX_PROBE = 512
 
@@ -76,6 +77,7 @@ def _load() -> ctypes.CDLL:
     lib.tb_refine_shared_block.argtypes = [ctypes.POINTER(c_p), ctypes.POINTER(c_p), ctypes.POINTER(c_p),
                                            ctypes.POINTER(c_p), c_i32, c_i64, c_i64, c_i64, ctypes.c_int, c_p, c_p,
                                            c_p, c_sz, c_p]
+    lib.tb_debug_set_wait_polls.argtypes = [c_i32]
     lib.tb_status_string.argtypes = [ctypes.c_int]
     lib.tb_status_string.restype = ctypes.c_char_p
     lib.tb_last_error.argtypes = []
@@ -202,6 +204,11 @@ def workspace_for(nbytes: int) -> torch.Tensor:
             buf = torch.zeros(size, dtype=torch.uint8, device=f"cuda:{dev}")
             _ws[key] = buf
         return buf
+
+
+def set_wait_polls(polls: int = DEFAULT_WAIT_POLLS) -> None:
+    """Bound of the decode kernels' wait for x . V (tb_debug_set_wait_polls); 0 forces the timeout path."""
+    _check(lib.tb_debug_set_wait_polls(polls))
 
 
 def workspace_error_word() -> int:

@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "tb_host.h"
 
@@ -53,6 +54,12 @@ tb_status check_dims(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank) {
 }
 
 }  // namespace
+
+namespace {
+std::atomic<int> g_wait_polls{1 << 20};
+}  // namespace
+
+int decode_wait_polls() { return g_wait_polls.load(std::memory_order_relaxed); }
 
 int device_cu_count(int* cus) {
   int dev = 0;
@@ -152,7 +159,7 @@ tb_status forward_one(const void* x, const void* s, const void* w0, const void* 
                       unsigned* err_word, int cus, hipStream_t hs) {
   if (dtype == TB_BF16 && m > kDecodeMaxTokens) {
     const GemmPlan p = plan_gemm(m, out_dim, in_dim, rank, cus);
-    hipError_t e = launch_forward_gemm(p, x, s, w0, u, v, y, m, out_dim, in_dim, rank, ctrl, data, hs);
+    hipError_t e = launch_forward_gemm(p, x, s, w0, u, v, y, m, out_dim, in_dim, rank, ctrl, data, err_word, hs);
     if (e != hipSuccess) return hip_fail(e, "launching the prefill projection");
     return ok();
   }
@@ -511,6 +518,12 @@ tb_status tb_refine_shared_block(const void* const* weights, const float* const*
                                            static_cast<hipStream_t>(stream), &what);
   if (e == -1) return fail(TB_ERR_HIP, "%s failed", what);
   if (e != 0) return hip_fail(hipError_t(e), what);
+  return ok();
+}
+
+tb_status tb_debug_set_wait_polls(int32_t polls) {
+  if (polls < 0) return fail(TB_ERR_INVALID_ARGUMENT, "polls %d < 0", polls);
+  g_wait_polls.store(polls, std::memory_order_relaxed);
   return ok();
 }
 

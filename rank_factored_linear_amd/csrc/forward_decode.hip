@@ -74,6 +74,7 @@ struct DecodeArgs {
   int NRB, KS, RBR;  // streamers: NRB row blocks x KS k-slices; RBR rows per block at most
   unsigned* ctrl;
   unsigned* err;  // sticky timeout word (word kErr of the first projection's control region)
+  int polls;      // bound of the streamers' wait for T, in polls
   float* tpart;  // [KT][16*NT][Rp] fp32 partials (KT > 1)
   void* tfull;   // [16*NT][Rp] T in the operand type
   float* ypart;  // [NRB][KS][16*NT][RBR] fp32 (KS > 1)
@@ -91,9 +92,10 @@ __device__ __forceinline__ unsigned add_coherent(unsigned* p, unsigned v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Bounded wait (relaxed polling, no cache invalidation).
-__device__ __forceinline__ bool wait_for_count(const unsigned* counter, unsigned target) {
-  for (int it = 0; it < (1 << 20); ++it) {
+// Bounded wait (relaxed polling, no cache invalidation): at most `polls`
+// polls (about 0.1 us apart).
+__device__ __forceinline__ bool wait_for_count(const unsigned* counter, unsigned target, int polls) {
+  for (int it = 0; it < polls; ++it) {
     if (load_coherent(counter) >= target) return true;
     __builtin_amdgcn_s_sleep(1);
   }
@@ -160,6 +162,11 @@ __device__ void produce_t(const DecodeArgs& a, int p, uint8_t* smem) {
   // each load reads whole 128-byte row segments.
   const int vr = l >> 3, vc = cb * kCbCols + (l & 7) * 8;
   Raw* vt = reinterpret_cast<Raw*>(smem) + w * (kCbCols * kVtPitch);  // [64 cols][kVtPitch], this wave's
+  // The sticky error word as this launch found it (thread 0's copy decides,
+  // after the k-loop): a workspace left by a timed-out wait may hold stale
+  // counts, so a poisoned launch publishes nothing and counts nothing.
+  const uint32_t err_at_entry = load_coherent(a.err);
+  __shared__ unsigned s_poisoned_p;
 
   f32x4 acc[4][NT];
 #pragma unroll
@@ -247,6 +254,7 @@ __device__ void produce_t(const DecodeArgs& a, int p, uint8_t* smem) {
   // The block's result goes to LDS as [16*NT tokens][64 columns].
   f32x4* red = reinterpret_cast<f32x4*>(smem);  // [kWaves][NT][kWave]
   float* blk = reinterpret_cast<float*>(smem + kWaves * NT * kWave * 16);
+  if (tid == 0) s_poisoned_p = err_at_entry;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     __syncthreads();  // the V tiles, or the previous tile's sums, are done with
@@ -272,6 +280,7 @@ __device__ void produce_t(const DecodeArgs& a, int p, uint8_t* smem) {
   // the operand type, two columns per 32-bit word, and counted in kDone.
   const int Rp = a.NCB * kCbCols;
   const int col0 = cb * kCbCols;
+  if (s_poisoned_p != 0u) return;
   __shared__ unsigned s_last;
   bool last = true;
   if (a.KT > 1) {
@@ -365,6 +374,11 @@ __device__ void stream_rows(const DecodeArgs& a, int b, uint8_t* smem) {
   const int r0 = int(int64_t(rb) * a.O / a.NRB), r1 = int(int64_t(rb + 1) * a.O / a.NRB);
   const int nrows = r1 - r0;
   const bool rank_unit = R > 0 && ks == KS - 1;
+  // The sticky error word as this launch found it (thread 0's copy decides,
+  // after the stream): a poisoned launch writes NaN to its rows and leaves
+  // every counter alone.
+  const uint32_t err_at_entry = load_coherent(a.err);
+  __shared__ unsigned s_poisoned;
 
   // LDS: the cross-wave reduction, then the row scale, then the block's
   // result [16*NT][RBR].
@@ -472,7 +486,14 @@ __device__ void stream_rows(const DecodeArgs& a, int b, uint8_t* smem) {
 
   // Row scale: C rows 4*(l/16)+e of each tile.
   if (tid < nrows) sbuf[tid] = s_mine;
+  if (tid == 0) s_poisoned = err_at_entry;
   __syncthreads();
+  E* Y = static_cast<E*>(a.y);
+  if (s_poisoned != 0u) {
+    const E nan = from_f32<E>(__builtin_nanf(""));
+    for (int i = tid; i < M * nrows; i += kThreads) Y[size_t(i / nrows) * a.O + r0 + i % nrows] = nan;
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < TILES; ++t)
 #pragma unroll
@@ -489,7 +510,7 @@ __device__ void stream_rows(const DecodeArgs& a, int b, uint8_t* smem) {
   if (rank_unit) {
     __shared__ unsigned s_ok;
     if (w == 0) {
-      const bool ok0 = wait_for_count(&a.ctrl[kDone], unsigned(a.NCB));
+      const bool ok0 = wait_for_count(&a.ctrl[kDone], unsigned(a.NCB), a.polls);
       if (l == 0) s_ok = ok0 ? 1u : 0u;
     }
     __syncthreads();
@@ -554,7 +575,6 @@ __device__ void stream_rows(const DecodeArgs& a, int b, uint8_t* smem) {
 
   // Store y, or this k-slice's partial (the last of the row block to arrive
   // sums all KS partials in k-slice order).
-  E* Y = static_cast<E*>(a.y);
   const int nel = M * nrows;
   if (KS == 1) {
     for (int i = tid; i < nel; i += kThreads) {
@@ -812,6 +832,7 @@ hipError_t launch_forward_decode_group(int n, const DecodePlan* plans, const Dec
     a.NRB = p.NRB; a.KS = p.KS; a.RBR = 16 * p.TILES;
     a.ctrl = ctrl + j * (kCtrlBlockBytes / 4);
     a.err = err_word;
+    a.polls = decode_wait_polls();
     a.tpart = reinterpret_cast<float*>(ws + p.off_tpart);
     a.tfull = ws + p.off_tfull;
     a.ypart = reinterpret_cast<float*>(ws + p.off_ypart);

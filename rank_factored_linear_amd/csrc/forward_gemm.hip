@@ -88,7 +88,15 @@ struct GemmArgs {
   bf16_t* y;
   int M, O, I, R;
   int tiles_m, tiles_n;
+  const unsigned* err;  // sticky error word: while set, y is written as NaN
 };
+
+// The workspace's sticky error word, read once at kernel entry (relaxed,
+// device scope).  A set word means an earlier call on this workspace timed
+// out and may have left stale counts behind.
+__device__ __forceinline__ uint32_t load_error_word(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __device__ __forceinline__ void gemm_load_stage(const GemmArgs& a, int m0, int n0, int k0, Frag8<bf16_t> (&ra)[4],
                                                 Frag8<bf16_t> (&rb)[4]) {
@@ -131,6 +139,7 @@ __global__ __launch_bounds__(kThreads) void forward_gemm_kernel(GemmArgs a) {
   const int tm = first_m + (bid % per_group) % gsize;
   const int tn = (bid % per_group) / gsize;
   const int m0 = tm * BM, n0 = tn * BN;
+  const uint32_t err_at_entry = load_error_word(a.err);
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -197,6 +206,7 @@ __global__ __launch_bounds__(kThreads) void forward_gemm_kernel(GemmArgs a) {
         for (int j = 0; j < 4; ++j) acc[i][j] = mma_k32(fa[i], fb[j], acc[i][j]);
     }
   }
+  const bool poisoned = err_at_entry != 0u;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -206,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void forward_gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = m0 + wm * 64 + i * 16 + (l >> 4) * 4 + e;
-        if (m < a.M) a.y[size_t(m) * a.O + o] = bf16_t{f32_to_bf16(acc[i][j][e])};
+        if (m < a.M) a.y[size_t(m) * a.O + o] = bf16_t{f32_to_bf16(poisoned ? __builtin_nanf("") : acc[i][j][e])};
       }
     }
   }
@@ -285,6 +295,7 @@ struct Args {
   int S, kps;        // ... of kps k-tiles each (the last may be shorter)
   int xcd_major;     // 1: workgroup g takes position (g % 8) * (grid / 8) + g / 8
   unsigned* ctrl;
+  const unsigned* err;  // sticky error word: while set, tiles are written as NaN and no counter is touched
   float* part;       // [S * split_tiles][kPartFloats] partials, slice-major
 };
 
@@ -547,7 +558,7 @@ __device__ __forceinline__ void finish_tile(const Args& a, int m0, int n0, f32x1
 // `slice`; finishes the tile if it holds the whole reduction or is the last
 // of the tile's slices to arrive.
 __device__ __forceinline__ void do_tile(const Args& a, int u, int kb, int ke, int slice, const Lanes& ln,
-                                        unsigned* s_last) {
+                                        unsigned* s_last, uint32_t err_at_entry) {
   int tm, tn;
   tile_coords(a, u, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
@@ -557,6 +568,19 @@ __device__ __forceinline__ void do_tile(const Args& a, int u, int kb, int ke, in
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
   k_loop(make_operands(a.x, a.M, a.w0, a.O, m0, n0, a.I), kb, ke, acc, ln);
+  // Poisoned workspace (thread 0's copy of the error word decides for the
+  // workgroup): NaN over the tile, no partial, no counter.
+  if (threadIdx.x == 0) *s_last = err_at_entry;
+  __syncthreads();
+  if (*s_last != 0u) {
+    for (int e = int(threadIdx.x); e < BM * BN; e += kThreads) {
+      const int m = m0 + e / BN, n = n0 + e % BN;
+      if (m < a.M && n < a.O) a.y[size_t(m) * a.O + n] = bf16_t{f32_to_bf16(__builtin_nanf(""))};
+    }
+    __syncthreads();  // every wave is past its read of *s_last before it is reused
+    return;
+  }
+  __syncthreads();
   if (slice >= 0) {
     store_partial(a, slice * a.split_tiles + u, acc);
     __builtin_amdgcn_s_waitcnt(0);  // partial written through before counting in
@@ -579,12 +603,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   const int g = int(blockIdx.x), G = int(gridDim.x);
   const int pos = a.xcd_major ? (g % 8) * (G / 8) + g / 8 : g;
   const Lanes ln = make_lanes(ring);
+  const uint32_t err_at_entry = load_error_word(a.err);
   for (int v = pos; v < a.split_tiles * a.S; v += G) {
     const int u = v % a.split_tiles, slice = v / a.split_tiles;
-    do_tile(a, u, slice * a.kps, min(a.KT, (slice + 1) * a.kps), slice, ln, &s_last);
+    do_tile(a, u, slice * a.kps, min(a.KT, (slice + 1) * a.kps), slice, ln, &s_last, err_at_entry);
   }
   const int tiles = a.tiles_m * a.tiles_n;
-  for (int u = a.split_tiles + pos; u < tiles; u += G) do_tile(a, u, 0, a.KT, -1, ln, &s_last);
+  for (int u = a.split_tiles + pos; u < tiles; u += G) do_tile(a, u, 0, a.KT, -1, ln, &s_last, err_at_entry);
 }
 
 }  // namespace big
@@ -627,6 +652,7 @@ struct Args {
   int RB, CB, KT;  // row blocks, column blocks, k-tiles of in_dim
   int KS, kps;     // k-slices and k-tiles per slice
   unsigned* ctrl;
+  const unsigned* err;  // sticky error word: while set, nothing is published and no counter is touched
   float* part;     // [RB * CB][KS][kPartFloats]
 };
 
@@ -747,6 +773,7 @@ __global__ __launch_bounds__(kThreads) void xv_kernel(Args a) {
   const int m0 = rb * BM, n0 = cb * BN;
   const int kb = ks * a.kps, ke = min(a.KT, kb + a.kps);
   const Lanes ln = make_lanes(ring);
+  const uint32_t err_at_entry = load_error_word(a.err);
   Src s;
   s.rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(a.x + size_t(m0) * a.I), 0,
                                           min(a.M - m0, BM) * a.I * 2, kRsrcFlags);
@@ -789,6 +816,11 @@ __global__ __launch_bounds__(kThreads) void xv_kernel(Args a) {
     }
   }
 
+  // Poisoned workspace: the projection's y is written as NaN, so T is not needed.
+  if (tid == 0) s_last = err_at_entry;
+  __syncthreads();
+  if (s_last != 0u) return;
+  __syncthreads();
   if (a.KS > 1) {
     // Partial in register order: 16-byte piece q = (2i + j) * 4 + c of every lane.
     float* blk = a.part + size_t(tile) * a.KS * kPartFloats;
@@ -933,7 +965,7 @@ GemmPlan plan_gemm(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int
 
 hipError_t launch_forward_gemm(const GemmPlan& p, const void* x, const void* s, const void* w0, const void* u,
                                const void* v, void* y, int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
-                               unsigned* ctrl, char* data, hipStream_t stream) {
+                               unsigned* ctrl, char* data, const unsigned* err_word, hipStream_t stream) {
   char* ws = data;
   bf16_t* t = reinterpret_cast<bf16_t*>(ws + p.off_t);
   if (rank > 0 && p.aligned) {
@@ -945,6 +977,7 @@ hipError_t launch_forward_gemm(const GemmPlan& p, const void* x, const void* s, 
     a.RB = p.xv_rb; a.CB = p.xv_cb; a.KT = p.xv_kt;
     a.KS = p.xv_ks; a.kps = p.xv_kps;
     a.ctrl = ctrl;
+    a.err = err_word;
     a.part = reinterpret_cast<float*>(ws + p.off_xvpart);
     hipLaunchKernelGGL(xv::xv_kernel, dim3(unsigned(p.xv_rb * p.xv_cb * p.xv_ks)), dim3(xv::kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
@@ -969,6 +1002,7 @@ hipError_t launch_forward_gemm(const GemmPlan& p, const void* x, const void* s, 
     a.KT = p.KT; a.KR = p.KR;
     a.split_tiles = p.split_tiles; a.S = p.S; a.kps = p.kps; a.xcd_major = p.xcd_major;
     a.ctrl = ctrl;
+    a.err = err_word;
     a.part = reinterpret_cast<float*>(ws + p.off_part);
     hipLaunchKernelGGL(big::gemm_kernel, dim3(unsigned(p.grid)), dim3(big::kThreads), 0, stream, a);
     return hipGetLastError();
@@ -983,6 +1017,7 @@ hipError_t launch_forward_gemm(const GemmPlan& p, const void* x, const void* s, 
   a.M = int(m); a.O = int(out_dim); a.I = int(in_dim); a.R = int(rank);
   a.tiles_m = int((m + BM - 1) / BM);
   a.tiles_n = int((out_dim + BN - 1) / BN);
+  a.err = err_word;
   hipLaunchKernelGGL(forward_gemm_kernel, dim3(unsigned(a.tiles_m * a.tiles_n)), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }

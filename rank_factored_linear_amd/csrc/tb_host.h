@@ -30,6 +30,10 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // ---- forward, skinny token counts (m <= kDecodeMaxTokens) -----------------
 constexpr int kDecodeMaxTokens = 64;
 
+// Bound of the decode streamers' wait for x . V, in polls (default 1 << 20,
+// about 0.1 s); tb_debug_set_wait_polls changes it for later launches.
+int decode_wait_polls();
+
 struct DecodePlan {
   int NT;        // 16-token column tiles (1, 2 or 4)
   int TILES;     // 16-row tiles each streaming workgroup is built for (1, 2, 4 or 6)
@@ -101,9 +105,11 @@ struct GemmPlan {
 };
 GemmPlan plan_gemm(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus);
 
+// err_word: the sticky error word of the workspace; while it is set the
+// launch writes NaN to y and touches no counter.
 hipError_t launch_forward_gemm(const GemmPlan& p, const void* x, const void* s, const void* w0, const void* u,
                                const void* v, void* y, int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
-                               unsigned* ctrl, char* data, hipStream_t stream);
+                               unsigned* ctrl, char* data, const unsigned* err_word, hipStream_t stream);
 
 // ---- reconstruct ----------------------------------------------------------
 hipError_t launch_reconstruct(tb_dtype in_dtype, tb_dtype out_dtype, const void* s, const void* w0, const void* u,
