@@ -130,6 +130,31 @@ tb_status tb_linear_forward(const void *x, const void *s, const void *w0, const 
                             void *y, int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
                             tb_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Bytes of the device scratch that tb_linear_forward_no_alloc uses (96 MiB on
+ * every GPU the library runs on, held until the process ends). */
+#define TB_NO_ALLOC_SCRATCH_BYTES (96u << 20)
+
+/*
+ * tb_linear_forward_no_alloc -- tb_linear_forward for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The same computation, kernels, results
+ * (bit for bit) and argument rules as tb_linear_forward, but the workspace is
+ * the library's own static device array of TB_NO_ALLOC_SCRATCH_BYTES on the
+ * current device; the call allocates and frees nothing.
+ *   Every call on one GPU shares that GPU's array: calls that may overlap on
+ *   one GPU (several streams, several host threads) race and must be
+ *   serialised by the caller.  Each call first clears the array's control
+ *   words (a small kernel on `stream`), so a call whose internal wait timed
+ *   out (word 2 set, its y NaN) does not affect the next.  The array keeps
+ *   the last call's contents.
+ *   Errors: as tb_linear_forward; TB_ERR_UNSUPPORTED when the call would need
+ *   more than TB_NO_ALLOC_SCRATCH_BYTES of workspace
+ *   (tb_linear_forward_workspace_size tells), with nothing enqueued.
+ */
+tb_status tb_linear_forward_no_alloc(const void *x, const void *s, const void *w0, const void *u, const void *v,
+                                     void *y, int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
+                                     tb_dtype dtype, void *stream);
+
 /*
  * tb_dense_forward -- y = x . W^T for a weight held whole: the
  * materialise-once serving mode, where W = tb_reconstruct_weight(s, W0, U, V)

@@ -29,8 +29,9 @@ EXPORTED = (
     "tb_reconstruct_weight", "tb_rel_frobenius_error", "tb_reconstruction_error",
     "tb_shared_block", "tb_row_scale", "tb_lowrank_factors_workspace_size", "tb_lowrank_factors",
     "tb_lowrank_factors_batch", "tb_refine_shared_block_workspace_size", "tb_refine_shared_block",
-    "tb_debug_set_wait_polls", "tb_status_string", "tb_last_error",
+    "tb_debug_set_wait_polls", "tb_status_string", "tb_last_error", "tb_linear_forward_no_alloc",
 )
+NO_ALLOC_SCRATCH_BYTES = 96 << 20
 DEFAULT_WAIT_POLLS = 1 << 20
 MAX_BAND_LAYERS = 128
 MAX_PROBE = 512
@@ -78,6 +79,8 @@ def _load() -> ctypes.CDLL:
                                            ctypes.POINTER(c_p), c_i32, c_i64, c_i64, c_i64, ctypes.c_int, c_p, c_p,
                                            c_p, c_sz, c_p]
     lib.tb_debug_set_wait_polls.argtypes = [c_i32]
+    lib.tb_linear_forward_no_alloc.argtypes = [c_p, c_p, c_p, c_p, c_p, c_p, c_i64, c_i64, c_i64, c_i64, ctypes.c_int,
+                                               c_p]
     lib.tb_status_string.argtypes = [ctypes.c_int]
     lib.tb_status_string.restype = ctypes.c_char_p
     lib.tb_last_error.argtypes = []
@@ -249,6 +252,19 @@ def linear_forward(x: torch.Tensor, s: torch.Tensor | None, W0: torch.Tensor, U:
     ws = workspace if workspace is not None else workspace_for(need)
     _check(lib.tb_linear_forward(_ptr(x), _ptr(s), _ptr(W0), _ptr(U), _ptr(V), _ptr(out), m, out_dim, in_dim, rank,
                                  _dtype_code(x.dtype), _ptr(ws), _workspace_bytes(ws), _stream()))
+    return out
+
+
+def linear_forward_no_alloc(x: torch.Tensor, s: torch.Tensor | None, W0: torch.Tensor, U: torch.Tensor | None,
+                            V: torch.Tensor | None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """linear_forward with the library's static device scratch as its workspace (tb_linear_forward_no_alloc):
+    with `out` given, nothing is allocated."""
+    m, out_dim, in_dim, rank, U, V = _projection_dims(x, s, W0, U, V)
+    _expect_out(out, (m, out_dim), x.dtype)
+    _need_cuda(x, s, W0, U, V, out)
+    out = _output(out, (m, out_dim), x.dtype, x)
+    _check(lib.tb_linear_forward_no_alloc(_ptr(x), _ptr(s), _ptr(W0), _ptr(U), _ptr(V), _ptr(out), m, out_dim, in_dim,
+                                          rank, _dtype_code(x.dtype), _stream()))
     return out
 
 

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "tb_host.h"
 
@@ -196,6 +197,80 @@ tb_status tb_linear_forward(const void* x, const void* s, const void* w0, const 
   unsigned* ctrl = static_cast<unsigned*>(workspace);
   return forward_one(x, s, w0, u, v, y, m, out_dim, in_dim, rank, dtype, ctrl, static_cast<char*>(workspace) + kControlBytes,
                      ctrl + 2, cus, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+// ---- the forward call that allocates nothing --------------------------------
+//
+// Its workspace is this file-scope device array, one per GPU, laid out as a
+// forward workspace: control words first, then the projection's buffers.  In
+// host code `scratch` names a host-side stand-in, never the device memory:
+// every host use goes through the address hipGetSymbolAddress gives for the
+// current device, looked up once per device.
+namespace tb {
+namespace {
+
+static_assert(TB_NO_ALLOC_SCRATCH_BYTES >= kControlBytes + (size_t(1) << 20), "scratch holds the control words");
+static __device__ __align__(256) unsigned char scratch[TB_NO_ALLOC_SCRATCH_BYTES];
+
+struct ScratchSlot {
+  std::once_flag once;
+  unsigned char* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// The device address of this device's scratch (set-up on its first use).
+hipError_t device_scratch(unsigned char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&slot] {
+    void* p = nullptr;
+    slot.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    slot.ptr = static_cast<unsigned char*>(p);
+  });
+  if (slot.err != hipSuccess) return slot.err;
+  *out = slot.ptr;
+  return hipSuccess;
+}
+
+// Clears one control block (a small kernel rather than a memset, so that the
+// call can be captured into a graph).
+__global__ void clear_control_block(unsigned* words) {
+  const int i = int(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < int(kCtrlBlockBytes / 4)) words[i] = 0u;
+}
+
+}  // namespace
+}  // namespace tb
+
+extern "C" {
+
+tb_status tb_linear_forward_no_alloc(const void* x, const void* s, const void* w0, const void* u, const void* v,
+                                     void* y, int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
+                                     tb_dtype dtype, void* stream) {
+  tb_status st = check_projection(x, s, w0, u, v, y, m, out_dim, in_dim, rank, dtype);
+  if (st != TB_OK) return st;
+  int cus = 0;
+  if (int e = device_cu_count(&cus)) return hip_fail(hipError_t(e), "querying the compute-unit count");
+  const size_t need = kControlBytes + forward_data_bytes(m, out_dim, in_dim, rank, dtype, cus);
+  if (need > TB_NO_ALLOC_SCRATCH_BYTES)
+    return fail(TB_ERR_UNSUPPORTED, "this call needs %zu bytes of scratch, above the %zu of the static buffer "
+                "(tb_linear_forward takes a workspace of any size)", need, size_t(TB_NO_ALLOC_SCRATCH_BYTES));
+  unsigned char* base = nullptr;
+  if (hipError_t e = device_scratch(&base)) return hip_fail(e, "looking up the static scratch");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  unsigned* ctrl = reinterpret_cast<unsigned*>(base);
+  // A single call uses control block 0 only.  It starts from zero every time,
+  // so a call whose wait timed out does not poison the ones after it.
+  hipLaunchKernelGGL(clear_control_block, dim3(unsigned(kCtrlBlockBytes / 4 / 256)), dim3(256), 0, hs, ctrl);
+  if (hipError_t e = hipGetLastError()) return hip_fail(e, "clearing the scratch's control words");
+  return forward_one(x, s, w0, u, v, y, m, out_dim, in_dim, rank, dtype, ctrl,
+                     reinterpret_cast<char*>(base) + kControlBytes, ctrl + 2, cus, hs);
 }
 
 tb_status tb_dense_forward(const void* x, const void* w, void* y, int64_t m, int64_t out_dim, int64_t in_dim,
