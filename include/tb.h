@@ -115,7 +115,8 @@ tb_status tb_linear_forward_workspace_size(int64_t m, int64_t out_dim, int64_t i
  *   bytes, 256-byte aligned.  Its first TB_WORKSPACE_CONTROL_BYTES bytes are
  *   control words: they must be zero before the first call that uses the
  *   buffer and must not be changed by the caller afterwards (each completed
- *   call, single or grouped, leaves all of them ready for the next).  Word 2
+ *   call, single or grouped, leaves all of them ready for the next; some
+ *   carry state from call to call).  Word 2
  *   (uint32) is a sticky error flag: it becomes nonzero only when a bounded
  *   internal wait times out (the rows of y behind that wait are NaN), and a
  *   timed-out call may leave other control words stale.  While word 2 is set,

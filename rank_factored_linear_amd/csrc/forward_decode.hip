@@ -56,7 +56,7 @@ constexpr int kWaves = kThreads / kWave;
 // counted into kFinishGroups group counters (64 words apart) and a top
 // counter bumped by the last of each group, so that a few hundred increments
 // do not queue on one word.
-enum Ctrl { kErr = 2, kDone = 5 };
+enum Ctrl { kErr = 2, kParity = 3, kDone = 5 };
 constexpr int kFinishBase = int(kCtrlBlockBytes / 4) - kFinishWords;
 constexpr int kFinishGroups = 16;
 constexpr int kCbCounters = 64;
@@ -79,6 +79,24 @@ struct DecodeArgs {
   void* tfull;   // [16*NT][Rp] T in the operand type
   float* ypart;  // [NRB][KS][16*NT][RBR] fp32 (KS > 1)
 };
+
+// The x . V exchange in the control block (when it fits): T [16*NT][Rp] in
+// the operand type, packed into 32-bit words (two bf16 or one fp32) and stored
+// complemented.  A NaN is stored as the canonical quiet NaN, so no payload is
+// all ones and no stored word is zero: a zero word is one not written yet.
+// Producers store their columns once; each rank-streamer wave polls just the
+// words it multiplies, so T needs no separate done count, no drain before it
+// and no extra round trip to learn that it is complete.  A launch exchanges T
+// in the half of the exchange words that its control block's parity word
+// names; its producers clear the other half once they are done, and the last
+// rank streamer flips the parity, so the next launch finds a cleared half and
+// no launch spends time clearing on its critical path.  Every workgroup reads
+// the parity before it counts itself in anywhere, so none can see the flip.
+__device__ __forceinline__ uint16_t t_bf16(float v) { return v != v ? uint16_t(0x7FC0u) : f32_to_bf16(v); }
+__device__ __forceinline__ uint32_t t_f32(float v) { return v != v ? 0x7FC00000u : __float_as_uint(v); }
+template <typename E> __host__ __device__ constexpr int t_words(int NT, int Rp) {
+  return 16 * NT * Rp * int(sizeof(E)) / 4;
+}
 
 // Device-scope (sc1) 32-bit accesses: coherent across XCDs without touching
 // the rest of the L2.
@@ -143,7 +161,9 @@ constexpr int producer_smem() {
   return tiles > reduce ? tiles : reduce;
 }
 
-template <typename E, int NT>
+// TCTRL: T goes out as the control block's coded words; else into tfull,
+// counted in kDone.
+template <typename E, int NT, bool TCTRL>
 __device__ void produce_t(const DecodeArgs& a, int p, uint8_t* smem) {
   using Raw = typename std::conditional<sizeof(E) == 2, uint16_t, float>::type;
   constexpr int D = producer_depth<E, NT>();
@@ -166,6 +186,7 @@ __device__ void produce_t(const DecodeArgs& a, int p, uint8_t* smem) {
   // after the k-loop): a workspace left by a timed-out wait may hold stale
   // counts, so a poisoned launch publishes nothing and counts nothing.
   const uint32_t err_at_entry = load_coherent(a.err);
+  const uint32_t parity = TCTRL ? load_coherent(&a.ctrl[kParity]) & 1u : 0u;
   __shared__ unsigned s_poisoned_p;
 
   f32x4 acc[4][NT];
@@ -277,7 +298,8 @@ __device__ void produce_t(const DecodeArgs& a, int p, uint8_t* smem) {
   // With one k-slice the block is final.  Otherwise store this slice's
   // partial; the last producer of the column block to arrive sums the KT
   // partials in k-slice order.  Either way the final block is published in
-  // the operand type, two columns per 32-bit word, and counted in kDone.
+  // the operand type, two columns per 32-bit word: as coded words in the
+  // control block (TCTRL), else in tfull and counted in kDone.
   const int Rp = a.NCB * kCbCols;
   const int col0 = cb * kCbCols;
   if (s_poisoned_p != 0u) return;
@@ -293,7 +315,16 @@ __device__ void produce_t(const DecodeArgs& a, int p, uint8_t* smem) {
     __syncthreads();
     last = s_last;
   }
-  if (!last) return;
+  // Share of the other exchange half that this producer clears when done.
+  const auto clear_other_half = [&] {
+    uint32_t* other = a.ctrl + kTWordBase + (1u - parity) * kTHalfWords;
+    const int np = a.NCB * a.KT, per = (kTHalfWords + np - 1) / np;
+    for (int i = p * per + tid; i < min(kTHalfWords, (p + 1) * per); i += kThreads) store_coherent(&other[i], 0u);
+  };
+  if (!last) {
+    if constexpr (TCTRL) clear_other_half();
+    return;
+  }
   for (int i = tid; i < 16 * NT * kCbCols / 2; i += kThreads) {  // word i: token i/32, columns 2*(i%32) and +1
     const int tok = i / (kCbCols / 2), col = 2 * (i % (kCbCols / 2));
     float v0 = 0.f, v1 = 0.f;
@@ -318,7 +349,15 @@ __device__ void produce_t(const DecodeArgs& a, int p, uint8_t* smem) {
       v0 = blk[tok * kCbCols + col];
       v1 = blk[tok * kCbCols + col + 1];
     }
-    if constexpr (sizeof(E) == 2) {
+    if constexpr (TCTRL) {
+      uint32_t* tw = a.ctrl + kTWordBase + parity * kTHalfWords;
+      if constexpr (sizeof(E) == 2) {
+        store_coherent(&tw[(tok * Rp + col0 + col) / 2], ~(uint32_t(t_bf16(v0)) | (uint32_t(t_bf16(v1)) << 16)));
+      } else {
+        store_coherent(&tw[tok * Rp + col0 + col], ~t_f32(v0));
+        store_coherent(&tw[tok * Rp + col0 + col + 1], ~t_f32(v1));
+      }
+    } else if constexpr (sizeof(E) == 2) {
       uint32_t* tf = static_cast<uint32_t*>(a.tfull);
       store_coherent(&tf[(size_t(tok) * Rp + col0 + col) / 2], uint32_t(f32_to_bf16(v0)) | (uint32_t(f32_to_bf16(v1)) << 16));
     } else {
@@ -326,6 +365,13 @@ __device__ void produce_t(const DecodeArgs& a, int p, uint8_t* smem) {
       store_coherent(&tf[size_t(tok) * Rp + col0 + col], __float_as_uint(v0));
       store_coherent(&tf[size_t(tok) * Rp + col0 + col + 1], __float_as_uint(v1));
     }
+  }
+  if constexpr (TCTRL) {
+    // The coded words need no count: the arrival counter is cleared for the
+    // next launch, then this producer's share of the other half.
+    if (tid == 0 && a.KT > 1) store_coherent(&a.ctrl[kCbCounters + cb], 0u);
+    clear_other_half();
+    return;
   }
   drain_stores();
   __syncthreads();
@@ -361,7 +407,7 @@ __device__ __forceinline__ Frag8<E> load_t(const DecodeArgs& a, int tok, int k) 
   return f;
 }
 
-template <typename E, int NT, int TILES>
+template <typename E, int NT, int TILES, bool TCTRL>
 __device__ void stream_rows(const DecodeArgs& a, int b, uint8_t* smem) {
   constexpr int D = pipe_depth<E, NT, TILES>();
   constexpr int kPairs = TILES * NT;
@@ -378,6 +424,7 @@ __device__ void stream_rows(const DecodeArgs& a, int b, uint8_t* smem) {
   // after the stream): a poisoned launch writes NaN to its rows and leaves
   // every counter alone.
   const uint32_t err_at_entry = load_coherent(a.err);
+  const uint32_t parity = TCTRL && rank_unit ? load_coherent(&a.ctrl[kParity]) & 1u : 0u;
   __shared__ unsigned s_poisoned;
 
   // LDS: the cross-wave reduction, then the row scale, then the block's
@@ -505,10 +552,91 @@ __device__ void stream_rows(const DecodeArgs& a, int b, uint8_t* smem) {
     }
 
   // The rank-r delta: this wave's k32 steps of T . U^T, once T is complete.
-  // One wave polls the done word (every wave polling it would hammer the
-  // line the producers count into) and shares the outcome through LDS.
-  if (rank_unit) {
-    __shared__ unsigned s_ok;
+  __shared__ unsigned s_ok;
+  if (TCTRL && rank_unit) {
+    // Each wave loads its U fragments, then polls the coded words of T it
+    // multiplies (the first poll overlaps U's loads); a wave that gives up
+    // turns the whole workgroup's result into NaN.
+    if (tid == 0) s_ok = 1u;
+    __syncthreads();
+    const uint32_t* tw = a.ctrl + kTWordBase + parity * kTHalfWords;
+    const int Rp = a.NCB * kCbCols;
+    for (int rs = w; rs < RS; rs += kWaves) {
+      if (rs != w || !kPrefetchU) {
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+          uf[t] = load_row8<E>(Ub + size_t(min(t * 16 + lr, nrows - 1)) * R, rs * 32 + kq, R, ualigned);
+      }
+      constexpr int kW = sizeof(E) == 2 ? 4 : 8;  // words of one lane's 8 columns
+      uint32_t words[NT][kW];
+      // Thousands of waves poll at once: one lane probes one word of the
+      // fragment until it is written, then the wave loads the fragment and
+      // checks every word.  (Polling whole fragments flooded the memory-side
+      // cache that also serves the W0 stream: 60-layer gate,up 98 -> 106 us;
+      // loading the whole fragment at the first attempt and probing only
+      // after that cost gate,up 1 us.)
+      bool ready = false;
+      const uint32_t* probe = tw + (rs * 32) * int(sizeof(E)) / 4;
+      for (int it = 0; it < a.polls; ++it) {
+        uint32_t seen = 1u;
+        if (l == 0) seen = load_coherent(probe);
+        if (__builtin_amdgcn_readfirstlane(seen) == 0u) {
+          __builtin_amdgcn_s_sleep(8);
+          continue;
+        }
+        bool mine = true;
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          const uint32_t* q = tw + ((c * 16 + lr) * Rp + rs * 32 + kq) * int(sizeof(E)) / 4;
+#pragma unroll
+          for (int e = 0; e < kW; ++e) {
+            words[c][e] = load_coherent(q + e);
+            mine = mine && words[c][e] != 0u;
+          }
+        }
+        if (__builtin_amdgcn_ballot_w64(!mine) == 0) {
+          ready = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+      }
+      if (!ready) {
+        if (l == 0) s_ok = 0u;   // only ever cleared: a benign race between waves
+        break;
+      }
+      Frag8<E> ft[NT];
+#pragma unroll
+      for (int c = 0; c < NT; ++c) {
+        if constexpr (sizeof(E) == 2) {
+          ft[c].v = make_uint4(~words[c][0], ~words[c][1], ~words[c][2], ~words[c][3]);
+        } else {
+          ft[c].lo = make_float4(__uint_as_float(~words[c][0]), __uint_as_float(~words[c][1]),
+                                 __uint_as_float(~words[c][2]), __uint_as_float(~words[c][3]));
+          ft[c].hi = make_float4(__uint_as_float(~words[c][4]), __uint_as_float(~words[c][5]),
+                                 __uint_as_float(~words[c][6]), __uint_as_float(~words[c][7]));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < TILES; ++t)
+#pragma unroll
+        for (int c = 0; c < NT; ++c) acc[t][c] = mma_k32(uf[t], ft[c], acc[t][c]);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_operand_guard();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    if (s_ok == 0u) {
+      if (tid == 0) atomicOr(a.err, 1u);
+      const float nan = __builtin_nanf("");
+#pragma unroll
+      for (int t = 0; t < TILES; ++t)
+#pragma unroll
+        for (int c = 0; c < NT; ++c) acc[t][c] = f32x4{nan, nan, nan, nan};
+    }
+  } else if (rank_unit) {
+    // One wave polls the done word (every wave polling it would hammer the
+    // line the producers count into) and shares the outcome through LDS.
     if (w == 0) {
       const bool ok0 = wait_for_count(&a.ctrl[kDone], unsigned(a.NCB), a.polls);
       if (l == 0) s_ok = ok0 ? 1u : 0u;
@@ -616,7 +744,7 @@ __device__ void stream_rows(const DecodeArgs& a, int b, uint8_t* smem) {
 
   // The last of a group clears its counter and bumps the top counter; the
   // last there, the last rank streamer past its read of T, resets the
-  // producers' count.
+  // producers' count, or flips the exchange parity.
   if (rank_unit && tid == 0) {
     const unsigned members = (unsigned(a.NRB) - fin_g + fin_groups - 1) / fin_groups;
     if (fin_old == members - 1) {
@@ -624,7 +752,8 @@ __device__ void stream_rows(const DecodeArgs& a, int b, uint8_t* smem) {
       unsigned* top = &a.ctrl[kFinishBase + 64 * kFinishGroups];
       if (add_coherent(top, 1u) == fin_groups - 1) {
         store_coherent(top, 0u);
-        store_coherent(&a.ctrl[kDone], 0u);
+        if (TCTRL) store_coherent(&a.ctrl[kParity], parity ^ 1u);
+        else store_coherent(&a.ctrl[kDone], 0u);
       }
     }
   }
@@ -653,53 +782,58 @@ struct GroupArgs {
 // per compute unit), except for the variants of 32 tokens x 96 rows and of
 // 64 tokens x 64 or 96 rows, whose accumulators need more registers (one
 // workgroup per compute unit).
-template <int NT, int TILES> constexpr int decode_waves_per_eu() { return NT * TILES >= 12 ? 2 : 4; }
+// fp32 fragments take twice the registers: every fp32 variant is cut for two
+// waves per SIMD, and the planner plans them so.
+template <typename E, int NT, int TILES> constexpr int decode_waves_per_eu() {
+  return sizeof(E) == 4 || NT * TILES >= 12 ? 2 : 4;
+}
 
-template <typename E, int NT, int TILES>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<NT, TILES>()))) void
+template <typename E, int NT, int TILES, bool TCTRL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<E, NT, TILES>()))) void
 decode_kernel(GroupArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<E, NT, TILES>()];
   const int b = int(blockIdx.x), np = g.p_end[g.n - 1];
   int j = 0;
   if (b < np) {
     while (b >= g.p_end[j]) ++j;
-    produce_t<E, NT>(g.a[j], b - (j ? g.p_end[j - 1] : 0), smem);
+    produce_t<E, NT, TCTRL>(g.a[j], b - (j ? g.p_end[j - 1] : 0), smem);
   } else {
     const int bs = b - np;
     while (bs >= g.s_end[j]) ++j;
-    stream_rows<E, NT, TILES>(g.a[j], bs - (j ? g.s_end[j - 1] : 0), smem);
+    stream_rows<E, NT, TILES, TCTRL>(g.a[j], bs - (j ? g.s_end[j - 1] : 0), smem);
   }
 }
 
 template <typename E, int NT, int TILES>
-hipError_t launch_t(const GroupArgs& g, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<E, NT, TILES>), dim3(g.p_end[g.n - 1] + g.s_end[g.n - 1]), dim3(kThreads), 0,
-                     stream, g);
+hipError_t launch_t(bool tctrl, const GroupArgs& g, hipStream_t stream) {
+  const dim3 grid(g.p_end[g.n - 1] + g.s_end[g.n - 1]);
+  if (tctrl) hipLaunchKernelGGL((decode_kernel<E, NT, TILES, true>), grid, dim3(kThreads), 0, stream, g);
+  else hipLaunchKernelGGL((decode_kernel<E, NT, TILES, false>), grid, dim3(kThreads), 0, stream, g);
   return hipGetLastError();
 }
 
 template <typename E>
-hipError_t launch_e(int NT, int TILES, const GroupArgs& g, hipStream_t stream) {
+hipError_t launch_e(int NT, int TILES, bool tctrl, const GroupArgs& g, hipStream_t stream) {
   if (NT == 1) {
     switch (TILES) {
-      case 1: return launch_t<E, 1, 1>(g, stream);
-      case 2: return launch_t<E, 1, 2>(g, stream);
-      case 4: return launch_t<E, 1, 4>(g, stream);
-      default: return launch_t<E, 1, 6>(g, stream);
+      case 1: return launch_t<E, 1, 1>(tctrl, g, stream);
+      case 2: return launch_t<E, 1, 2>(tctrl, g, stream);
+      case 4: return launch_t<E, 1, 4>(tctrl, g, stream);
+      default: return launch_t<E, 1, 6>(tctrl, g, stream);
     }
   }
   if (NT == 2) {
     switch (TILES) {
-      case 1: return launch_t<E, 2, 1>(g, stream);
-      case 2: return launch_t<E, 2, 2>(g, stream);
-      case 4: return launch_t<E, 2, 4>(g, stream);
-      default: return launch_t<E, 2, 6>(g, stream);
+      case 1: return launch_t<E, 2, 1>(tctrl, g, stream);
+      case 2: return launch_t<E, 2, 2>(tctrl, g, stream);
+      case 4: return launch_t<E, 2, 4>(tctrl, g, stream);
+      default: return launch_t<E, 2, 6>(tctrl, g, stream);
     }
   }
-  if (TILES == 1) return launch_t<E, 4, 1>(g, stream);
-  if (TILES == 2) return launch_t<E, 4, 2>(g, stream);
-  if (TILES == 4) return launch_t<E, 4, 4>(g, stream);
-  return launch_t<E, 4, 6>(g, stream);
+  if (TILES == 1) return launch_t<E, 4, 1>(tctrl, g, stream);
+  if (TILES == 2) return launch_t<E, 4, 2>(tctrl, g, stream);
+  if (TILES == 4) return launch_t<E, 4, 4>(tctrl, g, stream);
+  return launch_t<E, 4, 6>(tctrl, g, stream);
 }
 
 }  // namespace
@@ -710,25 +844,42 @@ namespace {
 int64_t decode_max_rows(int) { return 96; }
 // Producer k-slices: about 768 of in_dim (three k32 steps per wave, one
 // round of loads at 16 tokens) when T must be ready early; about 5632
-// (22 steps per wave) when the launch streams at least 112 MiB of W0 (over
-// ~20 us), which hides the longer chain and leaves fewer producers to share
-// compute units with the streamers.
+// (22 steps per wave) when the launch streams at least 56 Mi elements of W0
+// (112 MiB of bf16, over ~20 us), which hides the longer chain and leaves
+// fewer producers to take compute units from the streamers.  (Slices sized
+// to half of a compute unit's share of W0 were tried: the q,k,v producers
+// then finished long before the streams, but their extra compute units made
+// the streams and the 60-layer stack at 16 tokens slower, 227 -> 234 us per
+// layer.)
 constexpr int64_t kShortSlice = 768, kLongSlice = 5632;
-constexpr int64_t kLongStreamBytes = int64_t(112) << 20;
+constexpr int64_t kLongStreamElems = int64_t(56) << 20;
+// x sizes (tokens x in_dim) up to which the streamers take one k-slice each:
+// the x that every row block re-reads is small next to the cost of combining
+// k-slice partials across workgroups.  Measured per call, one slice against
+// the k-sliced plan: 60-layer o at 1 / 8 tokens 25.6 -> 23.1 / 26.9 -> 25.8
+// us, down at 1 token 45.8 -> 42.4 us; 26-layer down at 4 / 8 tokens 15.0 ->
+// 13.0 / 15.1 -> 13.7 us.  60-layer down at 8 tokens (172K elements of x)
+// loses 2.4 us, at 16 tokens 8.5 us.
+constexpr int64_t kOneSliceX = 65536;
 }  // namespace
 
-DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int streamers, int64_t stream_bytes) {
+DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int streamers, int cus,
+                       int64_t stream_elems) {
   DecodePlan p{};
   p.NT = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
   const int64_t max_rows = decode_max_rows(p.NT);
   const int64_t s_full = in_dim / 32;
   // Streamers.  Every streamer of a row block reads all of x for its k-slice,
-  // so the x traffic grows with the number of row blocks: use as few blocks
-  // as the widest tile set allows and split in_dim so that there is about one
-  // streamer per compute unit (each wave keeping at least four k32 steps).
+  // so the x traffic grows with the number of row blocks.  A small x
+  // (kOneSliceX): one k-slice, as many row blocks as streamers (no partials
+  // to combine across workgroups).  Otherwise use as few blocks as the widest
+  // tile set allows and split in_dim so that there is about one streamer per
+  // compute unit (each wave keeping at least four k32 steps).
   const int64_t nrb_min = (out_dim + max_rows - 1) / max_rows;
   int64_t ks = 1, nrb;
-  if (nrb_min >= streamers) {
+  if (m * in_dim <= kOneSliceX) {
+    nrb = nrb_min > streamers ? nrb_min : int64_t(streamers);
+  } else if (nrb_min >= streamers) {
     nrb = streamers;
     while ((out_dim + nrb - 1) / nrb > max_rows) nrb += streamers;
   } else {
@@ -746,14 +897,13 @@ DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
   p.NRB = int(nrb);
   p.KS = int(ks);
   p.NB = p.NRB * p.KS;
-  // Producers: 64 columns of T each, over k-slices of in_dim (kShortSlice,
-  // or kLongSlice behind a long stream).
+  // Producers: 64 columns of T each, over k-slices of in_dim.
   if (rank > 0) {
     p.NCB = int((rank + kCbCols - 1) / kCbCols);
     // Short reductions (in_dim <= 1536) stay in one producer per column block:
     // its longer load phase costs less than the extra round trips of
     // combining k-slice partials across workgroups.
-    const int64_t slice = stream_bytes >= kLongStreamBytes ? kLongSlice : kShortSlice;
+    const int64_t slice = stream_elems >= kLongStreamElems ? kLongSlice : kShortSlice;
     int64_t kt = in_dim <= 1536 ? 1 : (in_dim + slice - 1) / slice;
     if (kt > kMaxKT) kt = kMaxKT;
     if (p.NCB > kMaxGroupCounters / 2) kt = 1;  // one arrival counter per column block
@@ -776,19 +926,19 @@ DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
   return p;
 }
 
-DecodePlan plan_decode_spared(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus, int64_t stream_bytes) {
-  const DecodePlan p = plan_decode(m, out_dim, in_dim, rank, cus, stream_bytes);
+DecodePlan plan_decode_spared(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus, int64_t stream_elems) {
+  const DecodePlan p = plan_decode(m, out_dim, in_dim, rank, cus, cus, stream_elems);
   if (p.NP == 0 || 4 * p.NP >= cus) return p;
   // The producer count does not depend on the streamers.
-  return plan_decode(m, out_dim, in_dim, rank, cus - p.NP, stream_bytes);
+  return plan_decode(m, out_dim, in_dim, rank, cus - p.NP, cus, stream_elems);
 }
 
-bool plan_decode_shared(int n, const DecodeProjection* projs, int64_t m, int cus, int slots, int64_t stream_bytes,
+bool plan_decode_shared(int n, const DecodeProjection* projs, int64_t m, int cus, int slots, int64_t stream_elems,
                         DecodePlan* plans) {
   int64_t producers = 0;
   double w0 = 0.0;
   for (int j = 0; j < n; ++j) {
-    producers += plan_decode(m, projs[j].out_dim, projs[j].in_dim, projs[j].rank, cus, stream_bytes).NP;
+    producers += plan_decode(m, projs[j].out_dim, projs[j].in_dim, projs[j].rank, cus, cus, stream_elems).NP;
     w0 += double(projs[j].out_dim) * double(projs[j].in_dim);
   }
   const int64_t slots_total = int64_t(slots) * cus, streamers = slots_total - producers;
@@ -797,7 +947,7 @@ bool plan_decode_shared(int n, const DecodeProjection* projs, int64_t m, int cus
   for (int j = 0; j < n; ++j) {
     const DecodeProjection& q = projs[j];
     const int64_t b = int64_t(double(streamers) * double(q.out_dim) * double(q.in_dim) / w0);
-    plans[j] = plan_decode(m, q.out_dim, q.in_dim, q.rank, int(b > 1 ? b : 1), stream_bytes);
+    plans[j] = plan_decode(m, q.out_dim, q.in_dim, q.rank, int(b > 1 ? b : 1), cus, stream_elems);
     total += plans[j].NB;
     if (plans[j].NT != plans[0].NT || plans[j].TILES != plans[0].TILES) return false;
   }
@@ -809,7 +959,7 @@ bool plan_decode_shared(int n, const DecodeProjection* projs, int64_t m, int cus
 // buffers before the y partials do not depend on the budget and are largest
 // with the short producer k-slices.
 size_t decode_bytes_bound(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus) {
-  const DecodePlan p = plan_decode(m, out_dim, in_dim, rank, cus, 0);
+  const DecodePlan p = plan_decode(m, out_dim, in_dim, rank, cus, cus, 0);
   const size_t ypart = size_t(kMaxDecodeSlots) * size_t(cus) * size_t(16 * p.NT) * size_t(decode_max_rows(p.NT)) * 4;
   return p.off_ypart + align_up(ypart, 256);
 }
@@ -821,6 +971,7 @@ hipError_t launch_forward_decode_group(int n, const DecodePlan* plans, const Dec
   g.n = n;
   char* ws = data;
   int np = 0, nb = 0;
+  bool tctrl = true;
   for (int j = 0; j < n; ++j) {
     const DecodePlan& p = plans[j];
     const DecodeProjection& q = projs[j];
@@ -836,14 +987,17 @@ hipError_t launch_forward_decode_group(int n, const DecodePlan* plans, const Dec
     a.tpart = reinterpret_cast<float*>(ws + p.off_tpart);
     a.tfull = ws + p.off_tfull;
     a.ypart = reinterpret_cast<float*>(ws + p.off_ypart);
+    // T through the control block's coded words when every member's fits.
+    tctrl = tctrl && (dtype == TB_BF16 ? t_words<bf16_t>(p.NT, p.NCB * kCbCols)
+                                       : t_words<float>(p.NT, p.NCB * kCbCols)) <= kTHalfWords;
     np += p.NP;
     nb += p.NB;
     g.p_end[j] = np;
     g.s_end[j] = nb;
     ws += p.bytes;  // the next projection's buffers
   }
-  if (dtype == TB_BF16) return launch_e<bf16_t>(plans[0].NT, plans[0].TILES, g, stream);
-  return launch_e<float>(plans[0].NT, plans[0].TILES, g, stream);
+  if (dtype == TB_BF16) return launch_e<bf16_t>(plans[0].NT, plans[0].TILES, tctrl, g, stream);
+  return launch_e<float>(plans[0].NT, plans[0].TILES, tctrl, g, stream);
 }
 
 hipError_t launch_forward_decode(const DecodePlan& p, tb_dtype dtype, const void* x, const void* s, const void* w0,

@@ -16,11 +16,20 @@ namespace tb {
 constexpr int kMaxProjections = TB_MAX_GROUP;
 constexpr size_t kControlBytes = TB_WORKSPACE_CONTROL_BYTES;
 constexpr size_t kCtrlBlockBytes = kControlBytes / kMaxProjections;
-// The last kFinishWords words of a control block hold the decode rank
-// streamers' finish counters (16 group counters and a top counter, 64 words
-// apart); words 64 .. 64 + kMaxGroupCounters hold the per-block counters.
+// Layout of a control block, in 32-bit words: 0 .. 63 single words (word 2:
+// the sticky error flag, word 3: the parity of the x . V exchange);
+// 64 .. 64 + kMaxGroupCounters the per-block arrival counters; then the decode
+// launches' x . V exchange, two halves of kTHalfWords (T coded so that a zero
+// word means "not written yet"; a launch uses the half its parity names and
+// clears the other); the last kFinishWords the decode rank streamers' finish
+// counters (16 group counters and a top counter, 64 words apart).  Between
+// calls every word is zero except the parity word and the exchange half the
+// next call does not use.
 constexpr int kFinishWords = 17 * 64;
-constexpr int kMaxGroupCounters = int(kCtrlBlockBytes / 4) - 64 - kFinishWords;
+constexpr int kMaxGroupCounters = 1024;
+constexpr int kTWordBase = 64 + kMaxGroupCounters;
+constexpr int kTHalfWords = (int(kCtrlBlockBytes / 4) - kFinishWords - kTWordBase) / 2 / 64 * 64;
+static_assert(kTHalfWords >= 4096, "a half holds 16 tokens x rank 256 in fp32");
 
 // Compute units of the current device (queried once per device).
 int device_cu_count(int* cus);
@@ -45,13 +54,15 @@ struct DecodePlan {
 };
 
 // streamers: the streaming workgroups to aim for (about one per compute
-// unit); stream_bytes: the W0 bytes of the whole launch, which set how long
-// the producers' k-slices may be.
-DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int streamers, int64_t stream_bytes);
+// unit); cus: the compute units; stream_elems: the W0 elements of the whole
+// launch, whose share per compute unit sets how long the producers'
+// k-slices may be.
+DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int streamers, int cus,
+                       int64_t stream_elems);
 // The same with the producers' compute units left to them when they are few
 // (under a quarter of the chip): a streamer that shares a compute unit with a
 // producer finishes several microseconds after the others.
-DecodePlan plan_decode_spared(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus, int64_t stream_bytes);
+DecodePlan plan_decode_spared(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus, int64_t stream_elems);
 
 // ctrl: the projection's control block; data: its buffers; err_word: where a
 // timed-out wait is flagged.
@@ -79,11 +90,14 @@ hipError_t launch_forward_decode_group(int n, const DecodePlan* plans, const Dec
 // keeps two resident per compute unit; one for 32 tokens x 96 rows and for
 // 64 tokens x 64 or 96 rows).
 constexpr int kMaxDecodeSlots = 2;
+// Whether a decode variant's registers leave room for two workgroups per
+// compute unit (four waves per SIMD).
+inline bool decode_fits_two_per_cu(tb_dtype dtype, int NT, int TILES) { return dtype == TB_BF16 && NT * TILES < 12; }
 // Plans for the members of one launch that share slots * cus workgroups:
 // every producer keeps its workgroup and the streamers are shared out in
 // proportion to each member's W0 bytes.  False when the members would not
 // agree on one tile shape or would need more workgroups than that.
-bool plan_decode_shared(int n, const DecodeProjection* projs, int64_t m, int cus, int slots, int64_t stream_bytes,
+bool plan_decode_shared(int n, const DecodeProjection* projs, int64_t m, int cus, int slots, int64_t stream_elems,
                         DecodePlan* plans);
 // Data bytes that cover the plan of any streamer budget up to
 // kMaxDecodeSlots * cus.

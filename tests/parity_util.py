@@ -145,3 +145,25 @@ def tile_sample(n: int, seed: int, tile: int = TILE) -> np.ndarray:
     r = np.random.default_rng(seed)
     pick = {min(b + int(r.integers(tile)), n - 1) for b in range(0, n, tile)} | {0, n - 1}
     return np.array(sorted(pick))
+
+
+# ---------------------------------------------------------------------------
+# Forward workspace control words
+# ---------------------------------------------------------------------------
+# The library's control block layout (64 KiB per group member): word 2 is the
+# sticky error flag, word 3 the parity of the decode x . V exchange, words
+# 1088 .. 15295 the two exchange halves; every other word (the arrival, done
+# and finish counters) must be zero between calls.
+CTRL_BLOCK_WORDS = 16384
+CTRL_PARITY_WORD = 3
+CTRL_EXCHANGE = (64 + 1024, CTRL_BLOCK_WORDS - 17 * 64)
+
+
+def stale_control_words(ctrl_bytes) -> int:
+    """Number of control words that should be zero between calls and are not (the parity word and the
+    exchange halves, which legitimately carry the last call's state, are left out)."""
+    import torch
+    words = ctrl_bytes.view(torch.int32).view(-1, CTRL_BLOCK_WORDS).clone()
+    words[:, CTRL_PARITY_WORD] = 0
+    words[:, CTRL_EXCHANGE[0]:CTRL_EXCHANGE[1]] = 0
+    return int(words.count_nonzero().item())
