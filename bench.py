@@ -59,9 +59,9 @@ COLD_POOL_BYTES = 1 << 30
 GROUPS = [["q_proj", "k_proj", "v_proj"], ["o_proj"], ["gate_proj", "up_proj"], ["down_proj"]]
 
 WORKLOADS = {
-    "large60": dict(layers=60, shapes="SHAPES_60", rank=256, bands=6, tokens=16, seed=4),
-    "banded26": dict(layers=26, shapes="SHAPES_26", rank=128, bands=4, tokens=4, seed=3),
-    "passthrough26": dict(layers=26, shapes="SHAPES_26", rank=0, bands=26, tokens=8, seed=2),
+    "large60": dict(layers=60, shapes="SHAPES_60", rank=256, bands=6, tokens=16, seed=4, prefill=4096),
+    "banded26": dict(layers=26, shapes="SHAPES_26", rank=128, bands=4, tokens=4, seed=3, prefill=2048),
+    "passthrough26": dict(layers=26, shapes="SHAPES_26", rank=0, bands=26, tokens=8, seed=2, prefill=0),
     "reconstruct60": dict(layers=60, shapes="SHAPES_60", rank=256, bands=6, tokens=0, seed=5),
     "decompose26": dict(layers=26, shapes="SHAPES_26", rank=128, bands=4, tokens=0, seed=6),
     "decompose60": dict(layers=60, shapes="SHAPES_60", rank=256, bands=6, tokens=0, seed=7),
@@ -92,6 +92,10 @@ def parse():
     ap.add_argument("--replicas", type=int, default=None,
                     help="rotating pool of input replicas (default: enough for >= 1 GiB when the stack is small)")
     ap.add_argument("--no-graph", action="store_true", help="skip the captured-graph leg")
+    ap.add_argument("--prefill-tokens", type=int, default=None,
+                    help="token count of the prefill object beside a decode line (default: the workload's, "
+                         "4096 for large60, 2048 for banded26; 0: none)")
+    ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-group", action="store_true",
                     help="one tb_linear_forward call per projection instead of grouping q/k/v and gate/up")
@@ -171,6 +175,21 @@ def counter_traffic(kernel, workload_tag):
         rec = data.get(workload_tag)
         if rec and rec.get("kernel_source_digest") == kernel_source_digest() and rec.get("kernel") == kernel:
             return rec.get("bytes_per_launch")
+    except Exception:
+        return None
+    return None
+
+
+def profile_durations(tag):
+    """Average duration per call of the dominant kernel(s) in the committed rocprofv3 kernel trace of the same
+    bench command, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "kernel_durations.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(tag)
+        if rec and rec.get("kernel_source_digest") == kernel_source_digest():
+            return {"file": rec["file"], "avg_call_us": rec["avg_call_us"], "kernel": rec["kernel"]}
     except Exception:
         return None
     return None
@@ -324,7 +343,7 @@ def bench_forward(args, torch, np, tb, gen):
     dev = "cuda"
     t_setup = time.time()
 
-    # ---- resident inputs ---------------------------------------------------
+    # ---- resident weights ----------------------------------------------------
     band_of = []
     for l in range(L):
         b = ctypes.c_int32()
@@ -335,7 +354,7 @@ def bench_forward(args, torch, np, tb, gen):
     for b in range(G):
         for fam in gen.FAMILIES:
             W0[(b, fam)] = gen.device_w0(torch, wl["seed"], fam, shapes, b)
-    bundles, xs = {}, {}
+    bundles = {}
     for l in range(L):
         for fam in gen.FAMILIES:
             if passthrough:
@@ -343,7 +362,6 @@ def bench_forward(args, torch, np, tb, gen):
                 bundles[(l, fam)] = {"s": torch.ones(O, dtype=torch.bfloat16, device=dev), "U": None, "V": None}
             else:
                 bundles[(l, fam)] = gen.device_bundle(torch, wl["seed"], fam, shapes, l, band_of[l], R, with_w0=False)
-            xs[(l, fam)] = gen.device_activations(torch, wl["seed"], fam, shapes, l, M)
 
     # Materialise-once mode (every family) and tie_families="attn" (the MLP
     # families): W = diag(s) W0 + U V^T per layer, rebuilt once in bf16; each
@@ -376,158 +394,192 @@ def bench_forward(args, torch, np, tb, gen):
                       {k: {n: (None if t is None else t.clone()) for n, t in bd.items()}
                        for k, bd in bundles.items() if k[1] not in dense_fams},
                       None if dense is None else {k: t.clone() for k, t in dense.items()}))
-
-    ys = {fam: torch.empty((M, shapes[fam][0]), dtype=torch.bfloat16, device=dev) for fam in gen.FAMILIES}
     # Projections that take the same layer input go in one grouped call.
     groups = [[f] for f in gen.FAMILIES] if args.no_group else GROUPS
-    ws_need = []
-    for grp in groups:
-        dims = (tb.Projection * len(grp))(*[tb.Projection(None, None, None, None, None, None, *shapes[f],
-                                                          0 if f in dense_fams else R) for f in grp])
-        nb = ctypes.c_size_t(0)
-        assert tb.lib.tb_linear_forward_group_workspace_size(len(grp), dims, M, tb.TB_BF16, ctypes.byref(nb)) == 0
-        ws_need.append(nb.value)
-    ws = tb.workspace_for(max(ws_need))
     torch.cuda.synchronize()
     t_setup = time.time() - t_setup
 
     fwd = tb.lib.tb_linear_forward
     fwd_group = tb.lib.tb_linear_forward_group
-
-    def build_calls(stream_handle, pool):
-        """Prepared argument tuples: the timed loop only crosses the C ABI."""
-        W0p, bundlesp, densep = pool
-        stream = ctypes.c_void_p(stream_handle)
-        calls = []   # (layer, families, function, argument tuple)
-        for l in range(L):
-            for grp in groups:
-                members = []
-                for fam in grp:
-                    if fam in dense_fams:
-                        members.append((xs[(l, fam)], None, densep[(l, fam)], None, None, ys[fam]))
-                    else:
-                        bd = bundlesp[(l, fam)]
-                        members.append((xs[(l, fam)], bd["s"], W0p[(band_of[l], fam)], bd["U"] if R else None,
-                                        bd["V"] if R else None, ys[fam]))
-                if len(grp) == 1:
-                    x, s_, w0, u, v, y = members[0]
-                    O, I = shapes[grp[0]]
-                    Rc = 0 if grp[0] in dense_fams else R
-                    argv = (x.data_ptr(), None if s_ is None else s_.data_ptr(), w0.data_ptr(),
-                            u.data_ptr() if Rc else None, v.data_ptr() if Rc else None, y.data_ptr(), M, O, I, Rc,
-                            tb.TB_BF16, ws.data_ptr(), ws.numel(), stream)
-                    calls.append((l, grp, fwd, argv))
-                else:
-                    arr = tb.projection_array(members)   # the tuple keeps the array alive
-                    calls.append((l, grp, fwd_group, (len(grp), arr, M, tb.TB_BF16, ws.data_ptr(), ws.numel(),
-                                                      stream)))
-        return calls
-
     band_idx = tb.lib.tb_band_index
     bout = ctypes.c_int32()
     per_layer = len(groups)
 
-    def run(calls, events=None):
-        n = 0
-        for l in range(L):
-            band_idx(L, G, l, ctypes.byref(bout))          # band select (host)
-            for _ in range(per_layer):
-                if events is not None:
-                    events[n].record()
-                fn, argv = calls[n][2], calls[n][3]
-                st = fn(*argv)
-                if st:
-                    raise RuntimeError(tb.lib.tb_last_error().decode())
-                n += 1
-        if events is not None:
-            events[n].record()
+    def time_stack(M, steps, warmup, with_graph, with_cpu, cpu_seconds):
+        """One leg: K steps of the whole stack at M tokens over the resident weights (one JSON object)."""
+        t0 = time.time()
+        xs = {(l, fam): gen.device_activations(torch, wl["seed"], fam, shapes, l, M)
+              for l in range(L) for fam in gen.FAMILIES}
+        ys = {fam: torch.empty((M, shapes[fam][0]), dtype=torch.bfloat16, device=dev) for fam in gen.FAMILIES}
+        ws_need = []
+        for grp in groups:
+            dims = (tb.Projection * len(grp))(*[tb.Projection(None, None, None, None, None, None, *shapes[f],
+                                                              0 if f in dense_fams else R) for f in grp])
+            nb = ctypes.c_size_t(0)
+            assert tb.lib.tb_linear_forward_group_workspace_size(len(grp), dims, M, tb.TB_BF16, ctypes.byref(nb)) == 0
+            ws_need.append(nb.value)
+        ws = tb.workspace_for(max(ws_need))
 
-    main_stream = torch.cuda.current_stream().cuda_stream
-    pool_calls = [build_calls(main_stream, p) for p in pools]
-    calls = pool_calls[0]
+        def build_calls(stream_handle, pool):
+            """Prepared argument tuples: the timed loop only crosses the C ABI."""
+            W0p, bundlesp, densep = pool
+            stream = ctypes.c_void_p(stream_handle)
+            calls = []   # (layer, families, function, argument tuple)
+            for l in range(L):
+                for grp in groups:
+                    members = []
+                    for fam in grp:
+                        if fam in dense_fams:
+                            members.append((xs[(l, fam)], None, densep[(l, fam)], None, None, ys[fam]))
+                        else:
+                            bd = bundlesp[(l, fam)]
+                            members.append((xs[(l, fam)], bd["s"], W0p[(band_of[l], fam)], bd["U"] if R else None,
+                                            bd["V"] if R else None, ys[fam]))
+                    if len(grp) == 1:
+                        x, s_, w0, u, v, y = members[0]
+                        O, I = shapes[grp[0]]
+                        Rc = 0 if grp[0] in dense_fams else R
+                        argv = (x.data_ptr(), None if s_ is None else s_.data_ptr(), w0.data_ptr(),
+                                u.data_ptr() if Rc else None, v.data_ptr() if Rc else None, y.data_ptr(), M, O, I,
+                                Rc, tb.TB_BF16, ws.data_ptr(), ws.numel(), stream)
+                        calls.append((l, grp, fwd, argv))
+                    else:
+                        arr = tb.projection_array(members)   # the tuple keeps the array alive
+                        calls.append((l, grp, fwd_group, (len(grp), arr, M, tb.TB_BF16, ws.data_ptr(), ws.numel(),
+                                                          stream)))
+            return calls
 
-    def grp_bytes(grp):
-        return sum(dense_call_bytes(M, *shapes[f]) if f in dense_fams else call_bytes(M, *shapes[f], R) for f in grp)
+        def run(calls):
+            n = 0
+            for l in range(L):
+                band_idx(L, G, l, ctypes.byref(bout))          # band select (host)
+                for _ in range(per_layer):
+                    fn, argv = calls[n][2], calls[n][3]
+                    st = fn(*argv)
+                    if st:
+                        raise RuntimeError(tb.lib.tb_last_error().decode())
+                    n += 1
 
-    def grp_flops(grp):
-        return sum(call_flops(M, *shapes[f], 0 if f in dense_fams else R) for f in grp)
+        main_stream = torch.cuda.current_stream().cuda_stream
+        pool_calls = [build_calls(main_stream, p) for p in pools]
+        calls = pool_calls[0]
 
-    step_bytes = sum(grp_bytes(c[1]) for c in calls)
-    step_flops = sum(grp_flops(c[1]) for c in calls)
-    decode = M <= DECODE_MAX_TOKENS
+        def grp_bytes(grp):
+            return sum(dense_call_bytes(M, *shapes[f]) if f in dense_fams else call_bytes(M, *shapes[f], R)
+                       for f in grp)
 
-    def rate(ms):
-        return step_bytes / (ms * 1e-3) / 1e9 if decode else step_flops / (ms * 1e-3) / 1e12
+        def grp_flops(grp):
+            return sum(call_flops(M, *shapes[f], 0 if f in dense_fams else R) for f in grp)
 
-    for k in range(args.warmup):
-        run(pool_calls[k % replicas])
-    torch.cuda.synchronize()
+        step_bytes = sum(grp_bytes(c[1]) for c in calls)
+        step_flops = sum(grp_flops(c[1]) for c in calls)
+        decode = M <= DECODE_MAX_TOKENS
 
-    # ---- timed region: K steps, rotating over the pool (one replica: plain stack order) ----
-    ms, per_step = timed_steps(torch, lambda k: run(pool_calls[k % replicas]), args.steps)
-    if tb.workspace_error_word() != 0:
-        raise RuntimeError("a bounded wait in the projection kernel timed out")
-    effective = None
-    if replicas > 1:      # the stack from one replica: the cache-assisted stack-order figure
-        ms_eff, per_eff = timed_steps(torch, lambda k: run(calls), args.steps)
-        effective = {"value": round(rate(ms_eff), 3), "ms_per_step": round(ms_eff, 4), **spread(per_eff)}
+        def rate(ms):
+            return step_bytes / (ms * 1e-3) / 1e9 if decode else step_flops / (ms * 1e-3) / 1e12
 
-    # ---- per-launch durations of the projection kernel (same rotation again) ----
-    per_call_ms = np.zeros(len(calls))
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
-    for k in range(args.steps):
-        run(pool_calls[k % replicas], ev)
+        for k in range(warmup):
+            run(pool_calls[k % replicas])
         torch.cuda.synchronize()
-        per_call_ms += np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(len(calls))])
-    per_call_ms /= args.steps
-    launch_bytes = np.array([grp_bytes(c[1]) for c in calls], dtype=np.float64)
-    launch_flops = np.array([grp_flops(c[1]) for c in calls], dtype=np.float64)
+        t_prep = time.time() - t0
 
-    # ---- the same step replayed from a captured graph ----------------------------
-    graph = None
-    if not args.no_graph:
-        def make_step(handle):
-            c = build_calls(handle, pools[0])
-            return lambda: run(c)
-        g_ms, g_per, clocks = graph_leg(torch, make_step, args.steps, list(ys.values()))
-        graph = {"value": round(rate(g_ms), 3), "ms_per_step": round(g_ms, 4), **spread(g_per),
-                 "pool": "replica 0", "gpu": clocks}
+        # ---- timed region: K steps, rotating over the pool (one replica: plain stack order) ----
+        ms, per_step = timed_steps(torch, lambda k: run(pool_calls[k % replicas]), steps)
         if tb.workspace_error_word() != 0:
             raise RuntimeError("a bounded wait in the projection kernel timed out")
+        effective = None
+        if replicas > 1:      # the stack from one replica: the cache-assisted stack-order figure
+            ms_eff, per_eff = timed_steps(torch, lambda k: run(calls), steps)
+            effective = {"value": round(rate(ms_eff), 3), "ms_per_step": round(ms_eff, 4), **spread(per_eff)}
 
-    if decode:
-        unit = "GB/s"
-        achieved = launch_bytes.sum() / (per_call_ms.sum() * 1e-3) / 1e9
-        kernel = "decode_kernel<bf16,%d,*>" % (1 if M <= 16 else (2 if M <= 32 else 4))
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
-        per_launch = float(launch_bytes.mean())
-    else:
-        unit = "TFLOP/s"
-        achieved = launch_flops.sum() / (per_call_ms.sum() * 1e-3) / 1e12
-        kernel = "big::gemm_kernel (with xv::xv_kernel in the same call)"
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
-        per_launch = float(launch_flops.mean())
-    roof["kernel"] = kernel
-    roof["calls_per_step"] = len(calls)
-    roof["avg_launch_us"] = round(float(per_call_ms.mean()) * 1e3, 2)
-    roof["algorithmic_per_launch"] = round(per_launch, 1)
-    roof["traffic"] = (counter_traffic(kernel, f"{args.workload}_M{M}_G{G}")
-                       if replicas == 1 and dense is None else None)
+        # ---- the same step replayed from a captured graph ----------------------------
+        graph = None
+        if with_graph:
+            def make_step(handle):
+                c = build_calls(handle, pools[0])
+                return lambda: run(c)
+            g_ms, g_per, clocks = graph_leg(torch, make_step, steps, list(ys.values()))
+            graph = {"value": round(rate(g_ms), 3), "ms_per_step": round(g_ms, 4), **spread(g_per),
+                     "pool": "replica 0", "gpu": clocks}
+            if tb.workspace_error_word() != 0:
+                raise RuntimeError("a bounded wait in the projection kernel timed out")
 
-    cpu = None
-    if not args.no_cpu_baseline and dense is None:
-        cpu = cpu_baseline_forward(args, wl, shapes, calls, bundles, W0, xs, band_of, decode)
+        # ---- roofline of the dominant kernel ---------------------------------------
+        # The timed region holds nothing but the launches of the projection calls
+        # (decode: one decode_kernel launch per call; prefill: x . V then the GEMM per
+        # call), so its duration over the launch count is the average duration per
+        # call, gaps between launches included (an upper bound; the committed
+        # rocprofv3 kernel trace of the same command gives the kernel time alone).
+        per_call_us = ms * 1e3 / len(calls)
+        launch_bytes = float(np.mean([grp_bytes(c[1]) for c in calls]))
+        launch_flops = float(np.mean([grp_flops(c[1]) for c in calls]))
+        nt = 1 if M <= 16 else (2 if M <= 32 else 4)
+        tag = f"{args.workload}_M{M}_G{G}" + ("" if R == wl["rank"] else f"_R{R}")
+        if decode:
+            kernel = f"decode_kernel<bf16,{nt},*>"
+            achieved = launch_bytes / (per_call_us * 1e-6) / 1e9
+            roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "kernel": kernel, "launches_per_call": 1}
+            per_launch = launch_bytes
+        else:
+            kernel = "big::gemm_kernel" if R == 0 or dense_fams == set(gen.FAMILIES) else \
+                "xv::xv_kernel + big::gemm_kernel"
+            achieved = launch_flops / (per_call_us * 1e-6) / 1e12
+            roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "kernel": kernel,
+                    "launches_per_call": 1 if "+" not in kernel else 2}
+            per_launch = launch_flops
+        roof["calls_per_step"] = len(calls)
+        roof["avg_call_us"] = round(per_call_us, 2)
+        roof["algorithmic_per_call"] = round(per_launch, 1)
+        roof["traffic"] = counter_traffic(kernel, tag) if replicas == 1 and dense is None else None
+        prof = profile_durations(tag)
+        if prof is not None:
+            roof["profile"] = {**prof, "frac_from_profile": round(
+                (launch_bytes / (prof["avg_call_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS) if decode else
+                (launch_flops / (prof["avg_call_us"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS), 4)}
+
+        cpu = None
+        if with_cpu and dense is None:
+            cpu = cpu_baseline_forward(cpu_seconds, wl, shapes, calls, bundles, W0, xs, band_of, decode, M, R)
+
+        out = {
+            "value": round(rate(ms), 2 if decode else 3),
+            "unit": "GB/s" if decode else "TFLOP/s",
+            "steps": steps,
+            "warmup": warmup,
+            "ms_per_step": round(ms, 4),
+            "tokens": M,
+            "step_bytes": step_bytes,
+            "step_flops": step_flops,
+            "trials": spread(per_step),
+            "effective_one_replica": effective,
+            "graph": graph,
+            "roofline": roof,
+            "cpu_baseline": cpu,
+        }
+        print(f"# M={M}: inputs and warm-up {t_prep:.1f}s  step {ms:.3f} ms  {out['value']} {out['unit']}",
+              file=sys.stderr, flush=True)
+        del xs, ys, pool_calls, calls
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        return out
+
+    leg = time_stack(M, args.steps, args.warmup, not args.no_graph, not args.no_cpu_baseline, args.cpu_seconds)
+    prefill = None
+    pm = wl.get("prefill", 0) if args.prefill_tokens is None else args.prefill_tokens
+    if pm and M <= DECODE_MAX_TOKENS:
+        prefill = time_stack(pm, args.prefill_steps, 2, False, not args.no_cpu_baseline, args.cpu_seconds / 2)
+        prefill["config"] = f"{args.workload}: the same resident stack at {pm} tokens (matrix-core-bound)"
 
     line = {
         "metric": METRIC,
-        "value": round(rate(ms), 2 if decode else 3),
-        "unit": unit,
+        "value": leg["value"],
+        "unit": leg["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": leg["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -542,30 +594,31 @@ def bench_forward(args, torch, np, tb, gen):
                    "grouping": "+".join(",".join(f.split("_")[0] for f in g) for g in groups),
                    "rank": R, "bands": G, "tokens": M,
                    "hidden": shapes["q_proj"][1], "mlp": shapes["gate_proj"][0],
-                   "step_bytes": step_bytes, "step_flops": step_flops, "distinct_input_bytes": distinct,
+                   "step_bytes": leg["step_bytes"], "step_flops": leg["step_flops"], "distinct_input_bytes": distinct,
                    "replicas": replicas, "parallelism": "single-gpu"},
-        "trials": spread(per_step),
-        "effective_one_replica": effective,
-        "graph": graph,
-        "roofline": roof,
-        "cpu_baseline": cpu,
+        "trials": leg["trials"],
+        "effective_one_replica": leg["effective_one_replica"],
+        "graph": leg["graph"],
+        "roofline": leg["roofline"],
+        "cpu_baseline": leg["cpu_baseline"],
+        "prefill": prefill,
     }
-    print(f"# setup {t_setup:.1f}s  step {ms:.3f} ms  per-launch sum {per_call_ms.sum():.3f} ms", file=sys.stderr)
+    print(f"# setup {t_setup:.1f}s  step {leg['ms_per_step']:.3f} ms", file=sys.stderr)
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline_forward(args, wl, shapes, calls, bundles, W0, xs, band_of, decode):
-    """Time the float64 oracle on the first projections of the same stack."""
+def cpu_baseline_forward(cpu_seconds, wl, shapes, calls, bundles, W0, xs, band_of, decode, M, R):
+    """Time the float64 oracle on the first projections of the same stack (prefill: a 256-token slice of each,
+    whose flops scale linearly to the whole token count)."""
     import numpy as np
     import torch
 
     import oracle
 
-    M, R = wl["tokens"], wl["rank"]
     Mc = M if decode else min(M, 256)       # prefill: a token slice keeps it bounded
     done_bytes, done_flops, secs, used = 0, 0, 0.0, []
     for l, fam in ((c[0], f) for c in calls for f in c[1]):
-        if secs > args.cpu_seconds:
+        if secs > cpu_seconds:
             break
         O, I = shapes[fam]
         bd = bundles[(l, fam)]
@@ -586,7 +639,7 @@ def cpu_baseline_forward(args, wl, shapes, calls, bundles, W0, xs, band_of, deco
         val, unit = done_bytes / secs / 1e9, "GB/s"
     else:
         val, unit = done_flops / secs / 1e12, "TFLOP/s"
-    step_units = sum(call_bytes(Mc, *shapes[f], R) if decode else call_flops(Mc, *shapes[f], R)
+    step_units = sum(call_bytes(M, *shapes[f], R) if decode else call_flops(M, *shapes[f], R)
                      for c in calls for f in c[1])
     return {"value": round(val, 4), "unit": unit, "cores": int(_blas_threads()), "kind": "oracle",
             "sample": f"{len(used)} projections of the same stack ({used[0]} .. {used[-1]}), {Mc} tokens, "
