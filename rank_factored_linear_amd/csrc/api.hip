@@ -105,13 +105,40 @@ namespace {
 // tokens may take (alone or in a group, whatever its streamer budget; the
 // last 64-token slice of a longer fp32 call has a plan of its own).
 size_t forward_data_bytes(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, tb_dtype dtype, int cus) {
-  if (dtype == TB_BF16 && m > kDecodeMaxTokens) return plan_gemm(m, out_dim, in_dim, rank, cus).bytes;
+  if (dtype == TB_BF16 && m > kDecodeMaxTokens) return plan_gemm(1, &out_dim, m, in_dim, rank, cus).bytes;
   size_t bytes = 0;
   const int64_t counts[2] = {m < kDecodeMaxTokens ? m : kDecodeMaxTokens,
                              m > kDecodeMaxTokens ? m % kDecodeMaxTokens : 0};
   for (int64_t mt : counts)
     if (mt > 0) bytes = std::max(bytes, decode_bytes_bound(mt, out_dim, in_dim, rank, cus));
   return bytes;
+}
+
+// Whether the members of a group run as one launch of each prefill kernel:
+// bf16, more than kDecodeMaxTokens tokens, and one in_dim and rank for all
+// (q, k and v of a layer; gate and up).
+bool fused_prefill(int n, const tb_projection* projs, int64_t m, tb_dtype dtype) {
+  if (dtype != TB_BF16 || m <= kDecodeMaxTokens || n < 2) return false;
+  for (int j = 1; j < n; ++j)
+    if (projs[j].in_dim != projs[0].in_dim || projs[j].rank != projs[0].rank) return false;
+  return true;
+}
+
+GemmPlan fused_prefill_plan(int n, const tb_projection* projs, int64_t m, int cus) {
+  int64_t outs[TB_MAX_GROUP];
+  for (int j = 0; j < n; ++j) outs[j] = projs[j].out_dim;
+  return plan_gemm(n, outs, m, projs[0].in_dim, projs[0].rank, cus);
+}
+
+// Data bytes of a group: every member's own buffers one after another (the
+// members may run as calls of their own), or the fused launch's buffers if
+// they are more.
+size_t group_data_bytes(int n, const tb_projection* projs, int64_t m, tb_dtype dtype, int cus) {
+  size_t total = 0;
+  for (int j = 0; j < n; ++j)
+    total += forward_data_bytes(m, projs[j].out_dim, projs[j].in_dim, projs[j].rank, dtype, cus);
+  if (fused_prefill(n, projs, m, dtype)) total = std::max(total, fused_prefill_plan(n, projs, m, cus).bytes);
+  return total;
 }
 
 }  // namespace
@@ -159,8 +186,9 @@ tb_status forward_one(const void* x, const void* s, const void* w0, const void* 
                       int64_t out_dim, int64_t in_dim, int64_t rank, tb_dtype dtype, unsigned* ctrl, char* data,
                       unsigned* err_word, int cus, hipStream_t hs) {
   if (dtype == TB_BF16 && m > kDecodeMaxTokens) {
-    const GemmPlan p = plan_gemm(m, out_dim, in_dim, rank, cus);
-    hipError_t e = launch_forward_gemm(p, x, s, w0, u, v, y, m, out_dim, in_dim, rank, ctrl, data, err_word, hs);
+    const GemmPlan p = plan_gemm(1, &out_dim, m, in_dim, rank, cus);
+    const Projection q{x, s, w0, u, v, y, out_dim, in_dim, rank};
+    hipError_t e = launch_forward_gemm(p, &q, m, in_dim, rank, ctrl, data, err_word, hs);
     if (e != hipSuccess) return hip_fail(e, "launching the prefill projection");
     return ok();
   }
@@ -291,10 +319,7 @@ tb_status tb_linear_forward_group_workspace_size(int32_t n, const tb_projection*
   }
   int cus = 0;
   if (int e = device_cu_count(&cus)) return hip_fail(hipError_t(e), "querying the compute-unit count");
-  size_t total = kControlBytes;
-  for (int j = 0; j < n; ++j)
-    total += forward_data_bytes(m, projs[j].out_dim, projs[j].in_dim, projs[j].rank, dtype, cus);
-  *bytes_out = total;
+  *bytes_out = kControlBytes + group_data_bytes(n, projs, m, dtype, cus);
   return ok();
 }
 
@@ -310,12 +335,13 @@ tb_status tb_linear_forward_group(int32_t n, const tb_projection* projs, int64_t
   }
   int cus = 0;
   if (int e = device_cu_count(&cus)) return hip_fail(hipError_t(e), "querying the compute-unit count");
-  size_t off[TB_MAX_GROUP], total = kControlBytes;
+  size_t off[TB_MAX_GROUP], at = kControlBytes;
   for (int j = 0; j < n; ++j) {
     const tb_projection& q = projs[j];
-    off[j] = total;
-    total += forward_data_bytes(m, q.out_dim, q.in_dim, q.rank, dtype, cus);
+    off[j] = at;
+    at += forward_data_bytes(m, q.out_dim, q.in_dim, q.rank, dtype, cus);
   }
+  const size_t total = kControlBytes + group_data_bytes(n, projs, m, dtype, cus);
   if (workspace_bytes < total)
     return fail(TB_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is below the %zu needed", workspace_bytes, total);
   hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -329,11 +355,11 @@ tb_status tb_linear_forward_group(int32_t n, const tb_projection* projs, int64_t
     // on the plan that leaves its producers' compute units to them; the
     // plain plans; else one launch per member.
     DecodePlan plans[TB_MAX_GROUP];
-    DecodeProjection dp[TB_MAX_GROUP];
+    Projection dp[TB_MAX_GROUP];
     int64_t w0_elems = 0;
     for (int j = 0; j < n; ++j) {
       const tb_projection& q = projs[j];
-      dp[j] = DecodeProjection{q.x, q.s, q.w0, q.u, q.v, q.y, q.out_dim, q.in_dim, q.rank};
+      dp[j] = Projection{q.x, q.s, q.w0, q.u, q.v, q.y, q.out_dim, q.in_dim, q.rank};
       w0_elems += q.out_dim * q.in_dim;
     }
     for (int choice = 0; choice < 4; ++choice) {
@@ -360,6 +386,19 @@ tb_status tb_linear_forward_group(int32_t n, const tb_projection* projs, int64_t
         return ok();
       }
     }
+  }
+  if (fused_prefill(n, projs, m, dtype)) {
+    // One x . V launch and one GEMM launch for every member, in control
+    // block 0, with the buffers from the data base.
+    Projection gp[TB_MAX_GROUP];
+    for (int j = 0; j < n; ++j) {
+      const tb_projection& q = projs[j];
+      gp[j] = Projection{q.x, q.s, q.w0, q.u, q.v, q.y, q.out_dim, q.in_dim, q.rank};
+    }
+    const GemmPlan p = fused_prefill_plan(n, projs, m, cus);
+    hipError_t e = launch_forward_gemm(p, gp, m, projs[0].in_dim, projs[0].rank, ctrl, ws + kControlBytes, err, hs);
+    if (e != hipSuccess) return hip_fail(e, "launching the grouped prefill projections");
+    return ok();
   }
   for (int j = 0; j < n; ++j) {
     const tb_projection& q = projs[j];

@@ -933,7 +933,7 @@ DecodePlan plan_decode_spared(int64_t m, int64_t out_dim, int64_t in_dim, int64_
   return plan_decode(m, out_dim, in_dim, rank, cus - p.NP, cus, stream_elems);
 }
 
-bool plan_decode_shared(int n, const DecodeProjection* projs, int64_t m, int cus, int slots, int64_t stream_elems,
+bool plan_decode_shared(int n, const Projection* projs, int64_t m, int cus, int slots, int64_t stream_elems,
                         DecodePlan* plans) {
   int64_t producers = 0;
   double w0 = 0.0;
@@ -945,7 +945,7 @@ bool plan_decode_shared(int n, const DecodeProjection* projs, int64_t m, int cus
   if (slots < 1 || slots > kMaxDecodeSlots || streamers < 4 * int64_t(n)) return false;
   int64_t total = producers;
   for (int j = 0; j < n; ++j) {
-    const DecodeProjection& q = projs[j];
+    const Projection& q = projs[j];
     const int64_t b = int64_t(double(streamers) * double(q.out_dim) * double(q.in_dim) / w0);
     plans[j] = plan_decode(m, q.out_dim, q.in_dim, q.rank, int(b > 1 ? b : 1), cus, stream_elems);
     total += plans[j].NB;
@@ -964,7 +964,7 @@ size_t decode_bytes_bound(int64_t m, int64_t out_dim, int64_t in_dim, int64_t ra
   return p.off_ypart + align_up(ypart, 256);
 }
 
-hipError_t launch_forward_decode_group(int n, const DecodePlan* plans, const DecodeProjection* projs, tb_dtype dtype,
+hipError_t launch_forward_decode_group(int n, const DecodePlan* plans, const Projection* projs, tb_dtype dtype,
                                        int64_t m, unsigned* ctrl, char* data, unsigned* err_word, hipStream_t stream) {
   if (n < 1 || n > kMaxProjections) return hipErrorInvalidValue;
   GroupArgs g{};
@@ -974,7 +974,7 @@ hipError_t launch_forward_decode_group(int n, const DecodePlan* plans, const Dec
   bool tctrl = true;
   for (int j = 0; j < n; ++j) {
     const DecodePlan& p = plans[j];
-    const DecodeProjection& q = projs[j];
+    const Projection& q = projs[j];
     if (p.NT != plans[0].NT || p.TILES != plans[0].TILES) return hipErrorInvalidValue;
     DecodeArgs& a = g.a[j];
     a.x = q.x; a.s = q.s; a.w0 = q.w0; a.u = q.u; a.v = q.v; a.y = q.y;
@@ -1003,7 +1003,7 @@ hipError_t launch_forward_decode_group(int n, const DecodePlan* plans, const Dec
 hipError_t launch_forward_decode(const DecodePlan& p, tb_dtype dtype, const void* x, const void* s, const void* w0,
                                  const void* u, const void* v, void* y, int64_t m, int64_t out_dim, int64_t in_dim,
                                  int64_t rank, unsigned* ctrl, char* data, unsigned* err_word, hipStream_t stream) {
-  const DecodeProjection q{x, s, w0, u, v, y, out_dim, in_dim, rank};
+  const Projection q{x, s, w0, u, v, y, out_dim, in_dim, rank};
   return launch_forward_decode_group(1, &p, &q, dtype, m, ctrl, data, err_word, stream);
 }
 

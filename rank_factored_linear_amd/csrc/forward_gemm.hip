@@ -79,15 +79,25 @@ __global__ __launch_bounds__(kThreads) void xv_gemm_kernel(const bf16_t* __restr
 // ---------------------------------------------------------------------------
 constexpr int BM = 128, BN = 128, BK = 64, PITCH = BK + 8;  // 144-byte LDS rows
 
-struct GemmArgs {
+// One projection of a launch (its output tiles are workgroups start[j] ..
+// start[j+1] - 1 of the grid).
+struct GemmMember {
   const bf16_t* x;
   const bf16_t* s;
   const bf16_t* w0;
   const bf16_t* u;
   const bf16_t* t;
   bf16_t* y;
-  int M, O, I, R;
-  int tiles_m, tiles_n;
+  int O, tiles_n;
+};
+
+// The projections of one launch share the token count, in_dim and rank.
+struct GemmArgs {
+  int n;
+  int start[kMaxProjections + 1];
+  GemmMember mem[kMaxProjections];
+  int M, I, R;
+  int tiles_m;
   const unsigned* err;  // sticky error word: while set, y is written as NaN
 };
 
@@ -98,16 +108,16 @@ __device__ __forceinline__ uint32_t load_error_word(const unsigned* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void gemm_load_stage(const GemmArgs& a, int m0, int n0, int k0, Frag8<bf16_t> (&ra)[4],
-                                                Frag8<bf16_t> (&rb)[4]) {
+__device__ __forceinline__ void gemm_load_stage(const GemmArgs& a, const GemmMember& mb, int m0, int n0, int k0,
+                                                Frag8<bf16_t> (&ra)[4], Frag8<bf16_t> (&rb)[4]) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int c = tid + kThreads * q;
     const int row = c / 8, kc = k0 + (c % 8) * 8;
     const int am = m0 + row, bn = n0 + row;
-    ra[q] = load_frag_if<bf16_t>(a.x + size_t(am) * a.I + kc, am < a.M && kc < a.I);
-    rb[q] = load_frag_if<bf16_t>(a.w0 + size_t(bn) * a.I + kc, bn < a.O && kc < a.I);
+    ra[q] = load_frag_if<bf16_t>(mb.x + size_t(am) * a.I + kc, am < a.M && kc < a.I);
+    rb[q] = load_frag_if<bf16_t>(mb.w0 + size_t(bn) * a.I + kc, bn < mb.O && kc < a.I);
   }
 }
 
@@ -129,11 +139,15 @@ __global__ __launch_bounds__(kThreads) void forward_gemm_kernel(GemmArgs a) {
   const int lr = l & 15, kq = (l >> 4) * 8;
   const int wm = w / 2, wn = w % 2;
 
-  // Tiles are walked in column-major groups of 8 token tiles so that the
-  // workgroups running together share W0 and x tiles in L2.
-  const int bid = blockIdx.x;
+  // The workgroup's member; within it tiles are walked in column-major groups
+  // of 8 token tiles so that the workgroups running together share W0 and x
+  // tiles in L2.
+  int mj = 0;
+  while (mj + 1 < a.n && int(blockIdx.x) >= a.start[mj + 1]) ++mj;
+  const GemmMember& mb = a.mem[mj];
+  const int bid = int(blockIdx.x) - a.start[mj];
   const int group = 8;
-  const int per_group = group * a.tiles_n;
+  const int per_group = group * mb.tiles_n;
   const int gid = bid / per_group, first_m = gid * group;
   const int gsize = min(a.tiles_m - first_m, group);
   const int tm = first_m + (bid % per_group) % gsize;
@@ -148,13 +162,13 @@ __global__ __launch_bounds__(kThreads) void forward_gemm_kernel(GemmArgs a) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   Frag8<bf16_t> ra[4], rb[4];
-  gemm_load_stage(a, m0, n0, 0, ra, rb);
+  gemm_load_stage(a, mb, m0, n0, 0, ra, rb);
   gemm_store_stage(lds[0][0], lds[0][1], ra, rb);
   __syncthreads();
   const int KT = (a.I + BK - 1) / BK;
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < KT) gemm_load_stage(a, m0, n0, (kt + 1) * BK, ra, rb);
+    if (kt + 1 < KT) gemm_load_stage(a, mb, m0, n0, (kt + 1) * BK, ra, rb);
     const uint16_t* as = lds[cur][0];
     const uint16_t* bs = lds[cur][1];
 #pragma unroll
@@ -177,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void forward_gemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int o = n0 + wn * 64 + j * 16 + lr;
-    const float sc = o < a.O ? (a.s ? bf16_to_f32(a.s[o].bits) : 1.f) : 0.f;
+    const float sc = o < mb.O ? (mb.s ? bf16_to_f32(mb.s[o].bits) : 1.f) : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i][j] *= sc;
   }
@@ -191,14 +205,14 @@ __global__ __launch_bounds__(kThreads) void forward_gemm_kernel(GemmArgs a) {
         const int m = m0 + wm * 64 + i * 16 + lr;
         fa[i] = zero_frag<bf16_t>();
         if (m < a.M && jr < a.R)
-          fa[i] = aligned ? load_frag<bf16_t>(a.t + size_t(m) * a.R + jr) : load_frag_partial<bf16_t>(a.t + size_t(m) * a.R + jr, min(8, a.R - jr));
+          fa[i] = aligned ? load_frag<bf16_t>(mb.t + size_t(m) * a.R + jr) : load_frag_partial<bf16_t>(mb.t + size_t(m) * a.R + jr, min(8, a.R - jr));
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int o = n0 + wn * 64 + j * 16 + lr;
         fb[j] = zero_frag<bf16_t>();
-        if (o < a.O && jr < a.R)
-          fb[j] = aligned ? load_frag<bf16_t>(a.u + size_t(o) * a.R + jr) : load_frag_partial<bf16_t>(a.u + size_t(o) * a.R + jr, min(8, a.R - jr));
+        if (o < mb.O && jr < a.R)
+          fb[j] = aligned ? load_frag<bf16_t>(mb.u + size_t(o) * a.R + jr) : load_frag_partial<bf16_t>(mb.u + size_t(o) * a.R + jr, min(8, a.R - jr));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -212,11 +226,11 @@ __global__ __launch_bounds__(kThreads) void forward_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int o = n0 + wn * 64 + j * 16 + lr;
-      if (o >= a.O) continue;
+      if (o >= mb.O) continue;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = m0 + wm * 64 + i * 16 + (l >> 4) * 4 + e;
-        if (m < a.M) a.y[size_t(m) * a.O + o] = bf16_t{f32_to_bf16(poisoned ? __builtin_nanf("") : acc[i][j][e])};
+        if (m < a.M) mb.y[size_t(m) * mb.O + o] = bf16_t{f32_to_bf16(poisoned ? __builtin_nanf("") : acc[i][j][e])};
       }
     }
   }
@@ -281,15 +295,27 @@ constexpr int kRingBytes = 4 * kTileBytes;
 constexpr int kPartFloats = BM * BN;      // fp32 partial of one output tile
 constexpr unsigned kOutOfRange = 0x80000000u;  // lane offset past every buffer: the load returns zeros
 
-struct Args {
+// One projection of a launch: its operands and output tiles.
+struct Member {
   const bf16_t* x;
   const bf16_t* s;
   const bf16_t* w0;
   const bf16_t* u;
   const bf16_t* t;
   bf16_t* y;
-  int M, O, I, R;
-  int tiles_m, tiles_n;
+  int O;
+  int tiles_n;
+};
+
+// A launch covers the output tiles of n projections that share the token
+// count, in_dim and rank (the members of a group, or one projection): member
+// j owns tiles [start[j], start[j+1]) of the processing order.
+struct Args {
+  int n;
+  int start[kMaxProjections + 1];
+  Member mem[kMaxProjections];
+  int M, I, R;
+  int tiles_m;
   int KT, KR;        // k-tiles of in_dim and of rank
   int split_tiles;   // tiles [0, split_tiles) are split into S k-slices ...
   int S, kps;        // ... of kps k-tiles each (the last may be shorter)
@@ -472,14 +498,19 @@ __device__ __forceinline__ void k_loop(const Operands& o, int kb, int ke, f32x16
   __syncthreads();
 }
 
-// Tile u of the processing order -> (token tile, output tile): groups of
-// eight token tiles are walked column by column, so workgroups that run
-// together share x and W0 rows in L2.
-__device__ __forceinline__ void tile_coords(const Args& a, int u, int& tm, int& tn) {
-  const int per_group = 8 * a.tiles_n;
+// Tile u of the processing order -> (member, token tile, output tile).
+// Within a member, groups of eight token tiles are walked column by column,
+// so workgroups that run together share x and W0 rows in L2.
+__device__ __forceinline__ int tile_coords(const Args& a, int u, int& tm, int& tn) {
+  int j = 0;
+  while (j + 1 < a.n && u >= a.start[j + 1]) ++j;
+  u -= a.start[j];
+  const int tiles_n = a.mem[j].tiles_n;
+  const int per_group = 8 * tiles_n;
   const int first = (u / per_group) * 8, gsize = min(a.tiles_m - first, 8), r = u % per_group;
   tm = first + r % gsize;
   tn = r / gsize;
+  return j;
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const Args& a, int slot) {
@@ -522,18 +553,19 @@ __device__ __forceinline__ void add_partial(const Args& a, int slot, bool first,
 }
 
 // Scale by s, add T . U^T, round to bf16 and store.
-__device__ __forceinline__ void finish_tile(const Args& a, int m0, int n0, f32x16 (&acc)[4][TJ], const Lanes& ln) {
+__device__ __forceinline__ void finish_tile(const Args& a, const Member& mb, int m0, int n0, f32x16 (&acc)[4][TJ],
+                                            const Lanes& ln) {
   const int w = int(threadIdx.x) / kWave, l = int(threadIdx.x) % kWave, lr = l & 31, hi = l >> 5;
   const int wm = w / WN, wn = w % WN;
 #pragma unroll
   for (int j = 0; j < TJ; ++j) {
     const int n = n0 + wn * (BN / WN) + j * 32 + lr;
-    const float sc = n < a.O ? (a.s ? bf16_to_f32(a.s[n].bits) : 1.f) : 0.f;
+    const float sc = n < mb.O ? (mb.s ? bf16_to_f32(mb.s[n].bits) : 1.f) : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i][j] *= sc;
   }
   if (a.R > 0) {
-    const Operands r = make_operands(a.t, a.M, a.u, a.O, m0, n0, a.R);
+    const Operands r = make_operands(mb.t, a.M, mb.u, mb.O, m0, n0, a.R);
     k_loop(r, 0, a.KR, acc, ln);
   }
 #pragma unroll
@@ -541,33 +573,31 @@ __device__ __forceinline__ void finish_tile(const Args& a, int m0, int n0, f32x1
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
       const int n = n0 + wn * (BN / WN) + j * 32 + lr;
-      if (n >= a.O) continue;
+      if (n >= mb.O) continue;
 #pragma unroll
       for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int m = m0 + wm * 128 + i * 32 + 8 * b + 4 * hi + e;
-          if (m < a.M) a.y[size_t(m) * a.O + n] = bf16_t{f32_to_bf16(acc[i][j][4 * b + e])};
+          if (m < a.M) mb.y[size_t(m) * mb.O + n] = bf16_t{f32_to_bf16(acc[i][j][4 * b + e])};
         }
     }
 }
 
-// k-tiles [kb, ke) of tile u; finishes the tile if it holds the whole
-// reduction or arrives last among the tile's workgroups.
 // k-tiles [kb, ke) of tile u: the whole reduction (slice < 0) or k-slice
 // `slice`; finishes the tile if it holds the whole reduction or is the last
 // of the tile's slices to arrive.
 __device__ __forceinline__ void do_tile(const Args& a, int u, int kb, int ke, int slice, const Lanes& ln,
                                         unsigned* s_last, uint32_t err_at_entry) {
   int tm, tn;
-  tile_coords(a, u, tm, tn);
+  const Member& mb = a.mem[tile_coords(a, u, tm, tn)];
   const int m0 = tm * BM, n0 = tn * BN;
   f32x16 acc[4][TJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
-  k_loop(make_operands(a.x, a.M, a.w0, a.O, m0, n0, a.I), kb, ke, acc, ln);
+  k_loop(make_operands(mb.x, a.M, mb.w0, mb.O, m0, n0, a.I), kb, ke, acc, ln);
   // Poisoned workspace (thread 0's copy of the error word decides for the
   // workgroup): NaN over the tile, no partial, no counter.
   if (threadIdx.x == 0) *s_last = err_at_entry;
@@ -575,7 +605,7 @@ __device__ __forceinline__ void do_tile(const Args& a, int u, int kb, int ke, in
   if (*s_last != 0u) {
     for (int e = int(threadIdx.x); e < BM * BN; e += kThreads) {
       const int m = m0 + e / BN, n = n0 + e % BN;
-      if (m < a.M && n < a.O) a.y[size_t(m) * a.O + n] = bf16_t{f32_to_bf16(__builtin_nanf(""))};
+      if (m < a.M && n < mb.O) mb.y[size_t(m) * mb.O + n] = bf16_t{f32_to_bf16(__builtin_nanf(""))};
     }
     __syncthreads();  // every wave is past its read of *s_last before it is reused
     return;
@@ -594,7 +624,7 @@ __device__ __forceinline__ void do_tile(const Args& a, int u, int kb, int ke, in
     if (threadIdx.x == 0)
       __hip_atomic_store(&a.ctrl[kCounterBase + u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  finish_tile(a, m0, n0, acc, ln);
+  finish_tile(a, mb, m0, n0, acc, ln);
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4))) void gemm_kernel(Args a) {
@@ -608,7 +638,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     const int u = v % a.split_tiles, slice = v / a.split_tiles;
     do_tile(a, u, slice * a.kps, min(a.KT, (slice + 1) * a.kps), slice, ln, &s_last, err_at_entry);
   }
-  const int tiles = a.tiles_m * a.tiles_n;
+  const int tiles = a.start[a.n];
   for (int u = a.split_tiles + pos; u < tiles; u += G) do_tile(a, u, 0, a.KT, -1, ln, &s_last, err_at_entry);
 }
 
@@ -644,10 +674,20 @@ constexpr int kPartFloats = BM * BN;
 // buffer load's cache policy) so that it does not push V out of L2.
 constexpr int kXPolicy = 2;
 
-struct Args {
+// One projection of a launch: its x, V and T.
+struct Member {
   const bf16_t* x;
   const bf16_t* v;
   bf16_t* t;
+};
+
+// The n projections of one launch share the token count, in_dim and rank;
+// member j owns workgroups [j, j+1) x RB * CB * KS of the grid, and its tiles
+// are numbered j * RB * CB + (local tile) for the arrival counters and the
+// partials.
+struct Args {
+  int n;
+  Member mem[kMaxProjections];
   int M, I, R;
   int RB, CB, KT;  // row blocks, column blocks, k-tiles of in_dim
   int KS, kps;     // k-slices and k-tiles per slice
@@ -768,16 +808,19 @@ __global__ __launch_bounds__(kThreads) void xv_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes];
   __shared__ unsigned s_last;
   const int tid = int(threadIdx.x);
-  const int b = int(blockIdx.x), ks = b % a.KS, tile = b / a.KS;
-  const int rb = tile / a.CB, cb = tile % a.CB;
+  const int per_member = a.RB * a.CB * a.KS;
+  const int mj = int(blockIdx.x) / per_member, b = int(blockIdx.x) % per_member;
+  const Member& mb = a.mem[mj];
+  const int ks = b % a.KS, ltile = b / a.KS, tile = mj * a.RB * a.CB + ltile;
+  const int rb = ltile / a.CB, cb = ltile % a.CB;
   const int m0 = rb * BM, n0 = cb * BN;
   const int kb = ks * a.kps, ke = min(a.KT, kb + a.kps);
   const Lanes ln = make_lanes(ring);
   const uint32_t err_at_entry = load_error_word(a.err);
   Src s;
-  s.rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(a.x + size_t(m0) * a.I), 0,
+  s.rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(mb.x + size_t(m0) * a.I), 0,
                                           min(a.M - m0, BM) * a.I * 2, kRsrcFlags);
-  s.rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(a.v + n0), 0, (a.I * a.R - n0) * 2, kRsrcFlags);
+  s.rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(mb.v + n0), 0, (a.I * a.R - n0) * 2, kRsrcFlags);
   s.xoff = (tid >> 3) * a.I * 2 + (tid & 7) * 16;
   s.voff = (tid >> 5) * a.R * 2 + (tid & 31) * 16;
   s.xstep = 32 * a.I * 2;
@@ -874,7 +917,7 @@ __global__ __launch_bounds__(kThreads) void xv_kernel(Args a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int m = m0 + 32 * i + 8 * bb + 4 * hi + e;
-          if (m < a.M) a.t[size_t(m) * a.R + n] = bf16_t{f32_to_bf16(acc[i][j][4 * bb + e])};
+          if (m < a.M) mb.t[size_t(m) * a.R + n] = bf16_t{f32_to_bf16(acc[i][j][4 * bb + e])};
         }
     }
 }
@@ -893,45 +936,67 @@ constexpr int kStoreCost = 6, kLoadCost = 4, kMinSlice = 4;
 
 }  // namespace
 
-GemmPlan plan_gemm(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus) {
+GemmPlan plan_gemm(int n, const int64_t* out_dims, int64_t m, int64_t in_dim, int64_t rank, int cus) {
   GemmPlan p{};
-  p.off_t = 0;
-  const size_t off = align_up(p.off_t + size_t(m) * size_t(rank) * 2, 256);
+  p.n = n;
+  // Each member's T, then the launch's x . V partials, then the split tiles'
+  // partials.
+  size_t off = 0;
+  for (int j = 0; j < n; ++j) {
+    p.off_t[j] = off;
+    off = align_up(off + size_t(m) * size_t(rank) * 2, 256);
+  }
   p.bytes = off;
   // The matrix-core kernels for 16-byte aligned rows address one tile's rows
   // (and all of V) with 32-bit byte offsets.
   p.aligned = in_dim % 8 == 0 && rank % 8 == 0 && in_dim < (int64_t(1) << 22) && rank < (int64_t(1) << 22) &&
               in_dim * rank < (int64_t(1) << 30);
-  p.big = p.aligned;
-  if (!p.aligned) return p;
+  p.tiles_m = int((m + big::BM - 1) / big::BM);
+  p.KT = int((in_dim + big::BK - 1) / big::BK);
+  p.KR = int((rank + big::BK - 1) / big::BK);
+  const auto general = [&] {
+    p.big = 0;
+    p.split_tiles = 0;
+    p.tiles_m = int((m + BM - 1) / BM);
+    p.start[0] = 0;
+    for (int j = 0; j < n; ++j) {
+      p.tiles_n[j] = int((out_dims[j] + BN - 1) / BN);
+      p.start[j + 1] = p.start[j] + p.tiles_m * p.tiles_n[j];
+    }
+    p.grid = p.start[n];
+  };
+  if (!p.aligned) {
+    general();
+    return p;
+  }
   // x . V: enough k-slices to give every compute unit a workgroup, each at
   // least two k-tiles long and at most 16 partials per tile.
-  size_t o2 = off;
   if (rank > 0) {
     p.xv_rb = int((m + xv::BM - 1) / xv::BM);
     p.xv_cb = int((rank + xv::BN - 1) / xv::BN);
     p.xv_kt = int((in_dim + xv::BK - 1) / xv::BK);
-    const int64_t tiles = int64_t(p.xv_rb) * p.xv_cb;
+    const int64_t tiles = int64_t(n) * p.xv_rb * p.xv_cb;
     int64_t ks = tiles >= cus ? 1 : cus / tiles;
     ks = std::min<int64_t>(ks, std::min<int64_t>(16, std::max<int64_t>(1, p.xv_kt / 2)));
     if (tiles > kMaxGroupCounters) ks = 1;
     p.xv_kps = int((p.xv_kt + ks - 1) / ks);
     p.xv_ks = int((p.xv_kt + p.xv_kps - 1) / p.xv_kps);
-    p.off_xvpart = o2;
-    if (p.xv_ks > 1) o2 = align_up(o2 + size_t(tiles) * p.xv_ks * xv::kPartFloats * 4, 256);
+    p.off_xvpart = off;
+    if (p.xv_ks > 1) off = align_up(off + size_t(tiles) * p.xv_ks * xv::kPartFloats * 4, 256);
   }
-  const size_t off_big = o2;
-  p.bytes = o2;
-  p.tiles_m = int((m + big::BM - 1) / big::BM);
-  p.tiles_n = int((out_dim + big::BN - 1) / big::BN);
-  p.KT = int((in_dim + big::BK - 1) / big::BK);
-  p.KR = int((rank + big::BK - 1) / big::BK);
-  const int64_t tiles = int64_t(p.tiles_m) * p.tiles_n, KT = p.KT;
+  p.bytes = off;
+  p.start[0] = 0;
+  for (int j = 0; j < n; ++j) {
+    p.tiles_n[j] = int((out_dims[j] + big::BN - 1) / big::BN);
+    p.start[j + 1] = p.start[j] + p.tiles_m * p.tiles_n[j];
+  }
+  const int64_t tiles = p.start[n], KT = p.KT;
   const int G = cus >= 8 ? cus / 8 * 8 : cus;
   const auto round8 = [&](int64_t g) { return int(cus >= 8 ? std::min<int64_t>(G, (g + 7) / 8 * 8) : std::min<int64_t>(G, g)); };
 
   // Whole tiles in ceil(tiles / G) rounds ...
   int64_t best = (tiles + G - 1) / G * KT;
+  p.big = 1;
   p.grid = round8(tiles);
   p.split_tiles = 0;
   p.S = 1;
@@ -954,71 +1019,72 @@ GemmPlan plan_gemm(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int
   // Fewer workgroups than half the compute units even with the k-slices:
   // the 128 x 128 kernel's four times as many tiles finish sooner.
   if (p.grid < G / 2) {
-    p.big = 0;
-    p.split_tiles = 0;
+    general();
+    return p;
   }
   p.xcd_major = p.grid % 8 == 0 ? 1 : 0;
-  p.off_part = off_big;
-  if (p.split_tiles > 0) p.bytes = off_big + size_t(p.split_tiles) * p.S * big::kPartFloats * 4;
+  p.off_part = off;
+  if (p.split_tiles > 0) p.bytes = off + size_t(p.split_tiles) * p.S * big::kPartFloats * 4;
   return p;
 }
 
-hipError_t launch_forward_gemm(const GemmPlan& p, const void* x, const void* s, const void* w0, const void* u,
-                               const void* v, void* y, int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
-                               unsigned* ctrl, char* data, const unsigned* err_word, hipStream_t stream) {
-  char* ws = data;
-  bf16_t* t = reinterpret_cast<bf16_t*>(ws + p.off_t);
+hipError_t launch_forward_gemm(const GemmPlan& p, const Projection* projs, int64_t m, int64_t in_dim,
+                               int64_t rank, unsigned* ctrl, char* data, const unsigned* err_word, hipStream_t stream) {
+  const int n = p.n;
+  const auto t_of = [&](int j) { return reinterpret_cast<bf16_t*>(data + p.off_t[j]); };
   if (rank > 0 && p.aligned) {
     xv::Args a;
-    a.x = static_cast<const bf16_t*>(x);
-    a.v = static_cast<const bf16_t*>(v);
-    a.t = t;
+    a.n = n;
+    for (int j = 0; j < n; ++j)
+      a.mem[j] = xv::Member{static_cast<const bf16_t*>(projs[j].x), static_cast<const bf16_t*>(projs[j].v), t_of(j)};
     a.M = int(m); a.I = int(in_dim); a.R = int(rank);
     a.RB = p.xv_rb; a.CB = p.xv_cb; a.KT = p.xv_kt;
     a.KS = p.xv_ks; a.kps = p.xv_kps;
     a.ctrl = ctrl;
     a.err = err_word;
-    a.part = reinterpret_cast<float*>(ws + p.off_xvpart);
-    hipLaunchKernelGGL(xv::xv_kernel, dim3(unsigned(p.xv_rb * p.xv_cb * p.xv_ks)), dim3(xv::kThreads), 0, stream, a);
+    a.part = reinterpret_cast<float*>(data + p.off_xvpart);
+    hipLaunchKernelGGL(xv::xv_kernel, dim3(unsigned(n * p.xv_rb * p.xv_cb * p.xv_ks)), dim3(xv::kThreads), 0, stream,
+                       a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   } else if (rank > 0) {
     dim3 grid(unsigned((m + kTM - 1) / kTM), unsigned((rank + kTN - 1) / kTN));
-    hipLaunchKernelGGL(xv_gemm_kernel, grid, dim3(kThreads), 0, stream, static_cast<const bf16_t*>(x),
-                       static_cast<const bf16_t*>(v), t, int(m), int(in_dim), int(rank));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    for (int j = 0; j < n; ++j) {
+      hipLaunchKernelGGL(xv_gemm_kernel, grid, dim3(kThreads), 0, stream, static_cast<const bf16_t*>(projs[j].x),
+                         static_cast<const bf16_t*>(projs[j].v), t_of(j), int(m), int(in_dim), int(rank));
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   if (p.big) {
     big::Args a;
-    a.x = static_cast<const bf16_t*>(x);
-    a.s = static_cast<const bf16_t*>(s);
-    a.w0 = static_cast<const bf16_t*>(w0);
-    a.u = static_cast<const bf16_t*>(u);
-    a.t = t;
-    a.y = static_cast<bf16_t*>(y);
-    a.M = int(m); a.O = int(out_dim); a.I = int(in_dim); a.R = int(rank);
-    a.tiles_m = p.tiles_m; a.tiles_n = p.tiles_n;
+    a.n = n;
+    for (int j = 0; j <= n; ++j) a.start[j] = p.start[j];
+    for (int j = 0; j < n; ++j)
+      a.mem[j] = big::Member{static_cast<const bf16_t*>(projs[j].x), static_cast<const bf16_t*>(projs[j].s),
+                             static_cast<const bf16_t*>(projs[j].w0), static_cast<const bf16_t*>(projs[j].u), t_of(j),
+                             static_cast<bf16_t*>(projs[j].y), int(projs[j].out_dim), p.tiles_n[j]};
+    a.M = int(m); a.I = int(in_dim); a.R = int(rank);
+    a.tiles_m = p.tiles_m;
     a.KT = p.KT; a.KR = p.KR;
     a.split_tiles = p.split_tiles; a.S = p.S; a.kps = p.kps; a.xcd_major = p.xcd_major;
     a.ctrl = ctrl;
     a.err = err_word;
-    a.part = reinterpret_cast<float*>(ws + p.off_part);
+    a.part = reinterpret_cast<float*>(data + p.off_part);
     hipLaunchKernelGGL(big::gemm_kernel, dim3(unsigned(p.grid)), dim3(big::kThreads), 0, stream, a);
     return hipGetLastError();
   }
   GemmArgs a;
-  a.x = static_cast<const bf16_t*>(x);
-  a.s = static_cast<const bf16_t*>(s);
-  a.w0 = static_cast<const bf16_t*>(w0);
-  a.u = static_cast<const bf16_t*>(u);
-  a.t = t;
-  a.y = static_cast<bf16_t*>(y);
-  a.M = int(m); a.O = int(out_dim); a.I = int(in_dim); a.R = int(rank);
-  a.tiles_m = int((m + BM - 1) / BM);
-  a.tiles_n = int((out_dim + BN - 1) / BN);
+  a.n = n;
+  for (int j = 0; j <= n; ++j) a.start[j] = p.start[j];
+  for (int j = 0; j < n; ++j)
+    a.mem[j] = GemmMember{static_cast<const bf16_t*>(projs[j].x), static_cast<const bf16_t*>(projs[j].s),
+                          static_cast<const bf16_t*>(projs[j].w0), static_cast<const bf16_t*>(projs[j].u), t_of(j),
+                          static_cast<bf16_t*>(projs[j].y), int(projs[j].out_dim), p.tiles_n[j]};
+  a.M = int(m); a.I = int(in_dim); a.R = int(rank);
+  a.tiles_m = p.tiles_m;
   a.err = err_word;
-  hipLaunchKernelGGL(forward_gemm_kernel, dim3(unsigned(a.tiles_m * a.tiles_n)), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(forward_gemm_kernel, dim3(unsigned(p.grid)), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

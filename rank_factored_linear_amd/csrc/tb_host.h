@@ -36,6 +36,17 @@ int device_cu_count(int* cus);
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// One projection of a launch: device operands and output, and its shape.
+struct Projection {
+  const void* x;
+  const void* s;
+  const void* w0;
+  const void* u;
+  const void* v;
+  void* y;
+  int64_t out_dim, in_dim, rank;
+};
+
 // ---- forward, skinny token counts (m <= kDecodeMaxTokens) -----------------
 constexpr int kDecodeMaxTokens = 64;
 
@@ -74,16 +85,7 @@ hipError_t launch_forward_decode(const DecodePlan& p, tb_dtype dtype, const void
 // in one launch.  Their plans must agree on NT and TILES.  Projection j uses
 // control block j (from ctrl) and the buffers after the plans[0..j-1] bytes
 // (from data); timeouts of any member set *err_word.
-struct DecodeProjection {
-  const void* x;
-  const void* s;
-  const void* w0;
-  const void* u;
-  const void* v;
-  void* y;
-  int64_t out_dim, in_dim, rank;
-};
-hipError_t launch_forward_decode_group(int n, const DecodePlan* plans, const DecodeProjection* projs, tb_dtype dtype,
+hipError_t launch_forward_decode_group(int n, const DecodePlan* plans, const Projection* projs, tb_dtype dtype,
                                        int64_t m, unsigned* ctrl, char* data, unsigned* err_word, hipStream_t stream);
 
 // Workgroups per compute unit that a shared plan may fill (the decode kernel
@@ -97,32 +99,40 @@ inline bool decode_fits_two_per_cu(tb_dtype dtype, int NT, int TILES) { return d
 // every producer keeps its workgroup and the streamers are shared out in
 // proportion to each member's W0 bytes.  False when the members would not
 // agree on one tile shape or would need more workgroups than that.
-bool plan_decode_shared(int n, const DecodeProjection* projs, int64_t m, int cus, int slots, int64_t stream_elems,
+bool plan_decode_shared(int n, const Projection* projs, int64_t m, int cus, int slots, int64_t stream_elems,
                         DecodePlan* plans);
 // Data bytes that cover the plan of any streamer budget up to
 // kMaxDecodeSlots * cus.
 size_t decode_bytes_bound(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus);
 
 // ---- forward, prefill token counts (bf16, m > kDecodeMaxTokens) ----------
+// One launch of each kernel covers n projections that share the token count,
+// in_dim and rank (a single call: n = 1; q, k, v or gate, up of a layer: one
+// launch for all of them).  Output tiles are numbered member after member.
 struct GemmPlan {
+  int n;                // projections in the launch
   int aligned;          // in_dim and rank multiples of 8: x . V by the transposing-read kernel
   int big;              // 1: 256 x 256 kernel (needs aligned); 0: general 128 x 128 kernel
-  int grid;             // persistent workgroups of the stream-K kernel
-  int tiles_m, tiles_n; // 256 x 256 output tiles
+  int grid;             // workgroups (persistent for the 256 x 256 kernel, one per tile for the general one)
+  int tiles_m;          // token tiles (256 or 128 rows)
+  int tiles_n[kMaxProjections];      // each member's output-column tiles
+  int start[kMaxProjections + 1];    // first tile of each member; start[n] = all tiles
   int KT, KR;           // k-tiles (64) of in_dim and of rank
   int split_tiles;      // leading tiles split into S k-slices of kps k-tiles (the remainder round)
   int S, kps;
   int xcd_major;        // workgroup positions spread XCD-major (grid a multiple of 8)
-  int xv_rb, xv_cb;     // x . V on the aligned path: 64-token row blocks, 256-column blocks of T
+  int xv_rb, xv_cb;     // x . V on the aligned path: 64-token row blocks, 256-column blocks of T (per member)
   int xv_kt, xv_ks, xv_kps;  // its k-tiles (64), k-slices and k-tiles per slice
-  size_t off_t, off_xvpart, off_part, bytes;
+  size_t off_t[kMaxProjections];  // each member's T (m x rank bf16) from the data base
+  size_t off_xvpart, off_part, bytes;
 };
-GemmPlan plan_gemm(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank, int cus);
+// out_dims: the n members' output widths.
+GemmPlan plan_gemm(int n, const int64_t* out_dims, int64_t m, int64_t in_dim, int64_t rank, int cus);
 
-// err_word: the sticky error word of the workspace; while it is set the
-// launch writes NaN to y and touches no counter.
-hipError_t launch_forward_gemm(const GemmPlan& p, const void* x, const void* s, const void* w0, const void* u,
-                               const void* v, void* y, int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
+// ctrl: the launch's control block (arrival counters); data: the plan's
+// buffers; err_word: the sticky error word of the workspace; while it is set
+// the launch writes NaN to every y and touches no counter.
+hipError_t launch_forward_gemm(const GemmPlan& p, const Projection* projs, int64_t m, int64_t in_dim, int64_t rank,
                                unsigned* ctrl, char* data, const unsigned* err_word, hipStream_t stream);
 
 // ---- reconstruct ----------------------------------------------------------

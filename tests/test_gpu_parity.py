@@ -517,18 +517,21 @@ GROUPS = {  # members (out, in, rank)
 @pytest.mark.parametrize("group", sorted(GROUPS))
 def test_forward_group_matches_single_calls(group, M):
     # A grouped call computes each member as its own call would.  In one
-    # decode launch the chip is shared out between the members, so a member's
-    # k-slices (and its last bits) may differ from its own call's; prefill
-    # members run one after another, bit for bit as their own calls.
+    # launch the chip is shared out between the members, so a member's
+    # k-slices (and its last bits) may differ from its own call's.  Prefill
+    # members that differ in in_dim or rank run one after another, bit for
+    # bit as their own calls.
     _say(f"group {group} M={M}")
-    members = [_rand_case(M, O, I, R, torch.bfloat16, seed=31 * j + M) for j, (O, I, R) in enumerate(GROUPS[group])]
+    shapes = GROUPS[group]
+    members = [_rand_case(M, O, I, R, torch.bfloat16, seed=31 * j + M) for j, (O, I, R) in enumerate(shapes)]
     ys = tb.linear_forward_group(members)
     ys2 = tb.linear_forward_group(members)
     singles = [tb.linear_forward(*mbr) for mbr in members]
     torch.cuda.synchronize()
+    fused = len({(I, R) for _, I, R in shapes}) == 1
     for mbr, y, y2, y1 in zip(members, ys, ys2, singles):
         assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
-        if M > 64:
+        if M > 64 and not fused:
             assert torch.equal(y.view(torch.int16), y1.view(torch.int16))
         else:
             assert oracle.relative_frobenius_error(exact(y1), exact(y)) <= BF16_TOL
@@ -565,6 +568,57 @@ def test_group_stays_inside_its_workspace(M, dtype):
         assert oracle.relative_frobenius_error(exact(y1), exact(y)) <= tol_for(dtype)
     for mbr, y in list(zip(members, ys))[1::2]:   # the small members against the oracle
         _parity(y, mbr, what=f"wide group member M={M}")
+
+# Prefill groups whose members share in_dim and rank run as one x . V launch
+# and one GEMM launch over every member's tiles: (tokens, members).
+FUSED_PREFILL = {
+    "qkv26_M2048": (2048, [(1024, 1152, 128), (256, 1152, 128), (256, 1152, 128)]),   # 128 x 128 kernel
+    "gateup26_M2048": (2048, [(6912, 1152, 128), (6912, 1152, 128)]),                  # two whole rounds
+    "split_across_members": (256, [(2048, 5376, 256), (8192, 5376, 256)]),            # every tile k-split
+    "qkv60_M4096": (4096, [(8192, 5376, 256), (2048, 5376, 256), (2048, 5376, 256)]),  # three whole rounds
+    "ragged_M300": (300, [(136, 264, 24), (72, 264, 24), (520, 264, 24)]),
+    "unaligned_M100": (100, [(40, 40, 4), (17, 40, 4)]),                               # rank 4: x . V by the plain kernel
+    "dense_M130": (130, [(264, 520, 0), (136, 520, 0)]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(FUSED_PREFILL))
+def test_fused_prefill_group(case):
+    # Each member against the oracle (sampled rows and columns of the large
+    # ones) and against its own call; a guard band after the queried
+    # workspace stays untouched and the control words end clean.
+    M, shapes = FUSED_PREFILL[case]
+    _say(f"fused prefill group {case}")
+    members = [_rand_case(M, O, I, R, torch.bfloat16, seed=11 * j + M) for j, (O, I, R) in enumerate(shapes)]
+    dims = [(x, s_, W0, U, V, torch.empty((M, W0.shape[0]), dtype=torch.bfloat16, device=DEV))
+            for x, s_, W0, U, V in members]
+    need = ctypes.c_size_t(0)
+    assert tb.lib.tb_linear_forward_group_workspace_size(len(dims), tb.projection_array(dims), M,
+                                                          tb._dtype_code(torch.bfloat16), ctypes.byref(need)) == 0
+    guard = 1 << 20
+    buf = torch.zeros(need.value + guard, dtype=torch.uint8, device=DEV)
+    buf[need.value:] = 0xA5
+    ys = tb.linear_forward_group(members, workspace=buf[:need.value])
+    ys2 = tb.linear_forward_group(members, workspace=buf[:need.value])
+    singles = [tb.linear_forward(*mbr) for mbr in members]
+    torch.cuda.synchronize()
+    assert bool((buf[need.value:] == 0xA5).all())
+    assert stale_control_words(buf[:tb.WORKSPACE_CONTROL_BYTES]) == 0
+    for j, (mbr, y, y2, y1) in enumerate(zip(members, ys, ys2, singles)):
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+        assert oracle.relative_frobenius_error(exact(y1), exact(y)) <= BF16_TOL
+        x, s_, W0, U, V = mbr
+        if M * W0.shape[0] <= 1 << 20:
+            _parity(y, mbr, what=f"{case} member {j}")
+            continue
+        O, R = W0.shape[0], 0 if U is None else U.shape[1]
+        osel = torch.from_numpy(tile_sample(O, seed=j + 1)).to(DEV)
+        tsel = torch.from_numpy(tile_sample(M, seed=j + 2, tile=64)).to(DEV)
+        check_forward(exact(y.index_select(0, tsel).index_select(1, osel)), exact(x.index_select(0, tsel)),
+                      exact(s_.index_select(0, osel)), exact(W0.index_select(0, osel)),
+                      exact(U.index_select(0, osel)) if R else np.zeros((osel.numel(), 0)),
+                      exact(V) if R else np.zeros((W0.shape[1], 0)), bf16=True, what=f"{case} member {j}")
+
 
 def test_forward_group_fp32_and_clean_workspace():
     members = [_rand_case(8, O, I, R, torch.float32, seed=O) for (O, I, R) in GROUPS["ragged"]]
