@@ -106,7 +106,9 @@ tb_status tb_linear_forward_workspace_size(int64_t m, int64_t out_dim, int64_t i
  *   y  [m, out_dim]       output                   (dtype), written, must not alias inputs
  *   m >= 1 tokens, out_dim >= 1, in_dim >= 8 and % 8 == 0, rank >= 0.
  *   Arithmetic: products and sums in fp32 (bf16 inputs are exact in fp32);
- *   the scale multiplies fp32 sums of x . W0^T before the delta is added; for
+ *   the scale multiplies fp32 sums of x . W0^T before the delta is added
+ *   (where a reduction over in_dim is split across workgroups, each part's
+ *   sum is scaled and the parts are then added in a fixed order); for
  *   bf16 the intermediate x . V is rounded to bf16 before it meets U.  y is
  *   rounded once at the end.  Results are deterministic run to run.  For
  *   m <= 64, in_dim * element size * 96 must stay below 2^32 (else
@@ -200,18 +202,21 @@ tb_status tb_linear_forward_group_workspace_size(int32_t n, const tb_projection 
  * count m and dtype.  Layers apply several projections to one input (q/k/v,
  * gate/up); each member still names its own x, which may be shared.  For
  * m <= 64 the members run in one launch when their plans can share one tile
- * shape, so the fixed cost of a launch and the wait for x . V are paid once;
- * the chip is then shared out between the members, which may split a
- * member's reductions over in_dim differently from its own call, so its
- * result may differ from tb_linear_forward's in the last bits (same error
- * bound; a given group is deterministic run to run).  Other cases run the
- * members one after another, each exactly as its own call.
+ * shape, so the fixed cost of a launch and the wait for x . V are paid once.
+ * For bf16 and m > 64, members that share in_dim and rank run as one x . V
+ * launch and one GEMM launch over all their output tiles.  In one launch the
+ * chip is shared out between the members, which may split a member's
+ * reductions over in_dim differently from its own call, so its result may
+ * differ from tb_linear_forward's in the last bits (same error bound; a given
+ * group is deterministic run to run).  Other cases run the members one after
+ * another, each exactly as its own call.
  *   n: 1 .. TB_MAX_GROUP.  projs: host array of n members (no y may alias
  *   any member's input or another member's y).
  *   workspace: as for tb_linear_forward, at least
  *   tb_linear_forward_group_workspace_size() bytes; member j uses control
- *   block j and its own buffers after the control bytes.  A timed-out wait
- *   in any member sets word 2 of the workspace.
+ *   block j and its own buffers after the control bytes (a fused prefill
+ *   launch uses block 0 and the buffers from the start).  A timed-out wait in
+ *   any member sets word 2 of the workspace.
  *   Errors: TB_ERR_INVALID_ARGUMENT, TB_ERR_UNSUPPORTED, TB_ERR_HIP; a
  *   member that fails validation fails the call before anything is launched.
  */
@@ -379,8 +384,9 @@ tb_status tb_refine_shared_block(const void *const *weights, const float *const 
 
 /*
  * tb_debug_set_wait_polls -- bound, in polls about 0.1 us apart, of the
- * forward kernels' one internal wait (a decode streamer waiting for the
- * x . V products of its launch); default 1 << 20 (about 0.1 s).  It applies to
+ * forward kernels' internal waits (a decode streamer waiting for the x . V
+ * products of its launch; a k-slice of a split prefill tile waiting for the
+ * tile's other slices); default 1 << 20 (about 0.1 s).  It applies to
  * launches enqueued after the call, process-wide.  For tests of the timeout
  * path: 0 makes every such wait give up at once, so word 2 of the workspace
  * is set and y is NaN, with every kernel exiting normally.

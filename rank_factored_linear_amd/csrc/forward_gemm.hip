@@ -247,6 +247,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t lds_byte;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 // Lane addresses in an LDS ring are passed through an empty asm statement so
 // the compiler keeps each as one register and folds every per-step,
@@ -294,6 +295,12 @@ constexpr int kBOffset = 2 * kTileBytes;
 constexpr int kRingBytes = 4 * kTileBytes;
 constexpr int kPartFloats = BM * BN;      // fp32 partial of one output tile
 constexpr unsigned kOutOfRange = 0x80000000u;  // lane offset past every buffer: the load returns zeros
+// The finished tile leaves through LDS: each wave stages 16 of its 128 rows at
+// a time (64 columns of bf16, rows 144 bytes apart so that the two row groups
+// of one LDS write, 4 rows apart, fall in different banks), in an area of its
+// own beside the ring.
+constexpr int kStagePitch = 144, kStageBytes = 16 * kStagePitch;
+static_assert(kRingBytes + kWaves * kStageBytes + 4 * BN + 16 <= 160 * 1024, "ring, staging and scales fit the LDS");
 
 // One projection of a launch: its operands and output tiles.
 struct Member {
@@ -305,6 +312,7 @@ struct Member {
   bf16_t* y;
   int O;
   int tiles_n;
+  int wide;  // y 16-byte aligned and O a multiple of 8: rows leave in 16-byte pieces
 };
 
 // A launch covers the output tiles of n projections that share the token
@@ -323,6 +331,7 @@ struct Args {
   unsigned* ctrl;
   const unsigned* err;  // sticky error word: while set, tiles are written as NaN and no counter is touched
   float* part;       // [S * split_tiles][kPartFloats] partials, slice-major
+  int polls;         // bound of a slice's wait for the other slices of its tile
 };
 
 // A k-tile of each operand goes from HBM straight into LDS: each wave issues
@@ -334,10 +343,15 @@ struct Args {
 // compiler does not see them write LDS, so it does not drain every load
 // before each LDS read, and the waits are explicit (vmcnt before the
 // barrier that publishes a k-tile).
+// The tile bases and strides of one pair of operands (all uniform; the
+// buffer descriptors are built from them where the loads are issued, so that
+// choosing between two pairs is a choice between scalars); the per-lane parts
+// of the addresses are in Lanes.
 struct Operands {
-  __amdgpu_buffer_rsrc_t ra, rb;
-  int ve, vo;      // lane offsets (row, swizzled chunk) for the even and odd loads j
-  int ce, co;      // the global chunk index each of them fetches
+  const bf16_t* a;
+  const bf16_t* b;
+  int abytes, bbytes;  // bytes of the tile's rows of each operand (loads past them return zeros)
+  int row_bytes;   // bytes of one row (k elements)
   int rowstep8;    // bytes of 8 rows (soffset step between the loads j)
   int kel;         // reduction length in elements
 };
@@ -346,15 +360,11 @@ __device__ __forceinline__ Operands make_operands(const bf16_t* a, int arows, co
                                                   int n0, int k) {
   Operands o;
   const int ar = min(arows - m0, BM), br = min(brows - n0, BN);
-  o.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(a + size_t(m0) * k), 0, ar * k * 2, kRsrcFlags);
-  o.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(b + size_t(n0) * k), 0, br * k * 2, kRsrcFlags);
-  const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave), l = int(threadIdx.x) % kWave;
-  // Load j covers rows w*32 + 8j + l/8; rows of even and of odd j share the swizzle.
-  const int row_e = w * 32 + (l >> 3), row_o = row_e + 8, pos = l & 7;
-  o.ce = pos ^ ((row_e >> 1) & 7);
-  o.co = pos ^ ((row_o >> 1) & 7);
-  o.ve = row_e * k * 2 + (o.ce << 4);
-  o.vo = row_e * k * 2 + (o.co << 4);  // the soffset of load j adds its 8j rows
+  o.a = a + size_t(m0) * k;
+  o.b = b + size_t(n0) * k;
+  o.abytes = ar * k * 2;
+  o.bbytes = br * k * 2;
+  o.row_bytes = k * 2;
   o.rowstep8 = 8 * k * 2;
   o.kel = k;
   return o;
@@ -363,6 +373,10 @@ __device__ __forceinline__ Operands make_operands(const bf16_t* a, int arows, co
 // Lane addresses in the LDS ring, built once per workgroup.
 struct Lanes {
   unsigned dma_a, dma_b;  // this wave's first 1 KB of A and of B in buffer 0 (uniform)
+  // Global side of the direct-to-LDS loads: load j of the wave covers rows
+  // w*32 + 8j + lane/8 (the even and the odd j share the swizzle), the lane
+  // fetching chunk ce (even j) or co (odd j) of its row.
+  int row_e, ce, co;
   lds_byte* a_rd[4];      // A fragment of k16 step st: row wm*128 + lane%32, swizzled chunk 2st + lane/32
   lds_byte* b_rd[4];      // B fragment of k16 step st: row wn*(BN/WN) + lane%32
 };
@@ -375,6 +389,9 @@ __device__ __forceinline__ Lanes make_lanes(uint8_t* ring) {
   const unsigned b0 = unsigned(uintptr_t(base));
   ln.dma_a = __builtin_amdgcn_readfirstlane(b0 + unsigned(w) * 4096u);
   ln.dma_b = __builtin_amdgcn_readfirstlane(b0 + unsigned(kBOffset) + unsigned(w) * 4096u);
+  ln.row_e = w * 32 + (l >> 3);
+  ln.ce = (l & 7) ^ ((ln.row_e >> 1) & 7);
+  ln.co = (l & 7) ^ (((ln.row_e + 8) >> 1) & 7);
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
     const int chunk = ((2 * st + hi) ^ x) << 4;
@@ -386,6 +403,12 @@ __device__ __forceinline__ Lanes make_lanes(uint8_t* ring) {
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ bf16_t* uniform_ptr(const bf16_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v)), hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<bf16_t*>((uint64_t(hi) << 32) | lo);
+}
+
 // Four direct-to-LDS loads of one operand: load j writes 1 KB at dst + j KB
 // from the global rows at soffset soff + j * rowstep8.  M0 takes one wait
 // state before a load that reads it.
@@ -415,14 +438,21 @@ __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" :
 // beyond it fetch from past the buffer and so write zeros.
 template <int BUF>
 __device__ __forceinline__ void issue(const Operands& o, const Lanes& ln, int kt) {
-  int ve = o.ve, vo = o.vo;
+  int ve = ln.row_e * o.row_bytes + (ln.ce << 4), vo = ln.row_e * o.row_bytes + (ln.co << 4);
   const int left = o.kel - kt * BK;
   if (left < BK) {
-    ve = o.ce * 8 < left ? ve : int(kOutOfRange);
-    vo = o.co * 8 < left ? vo : int(kOutOfRange);
+    ve = ln.ce * 8 < left ? ve : int(kOutOfRange);
+    vo = ln.co * 8 < left ? vo : int(kOutOfRange);
   }
-  dma4(ln.dma_a + BUF * kTileBytes, o.ra, ve, vo, kt * BK * 2, o.rowstep8);
-  dma4(ln.dma_b + BUF * kTileBytes, o.rb, ve, vo, kt * BK * 2, o.rowstep8);
+  // Every operand here is uniform; readfirstlane says so to the compiler,
+  // which cannot always prove it for a choice between two operand pairs.
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(o.a), 0, __builtin_amdgcn_readfirstlane(o.abytes), kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(o.b), 0, __builtin_amdgcn_readfirstlane(o.bbytes), kRsrcFlags);
+  const int soff = __builtin_amdgcn_readfirstlane(kt * BK * 2), step = __builtin_amdgcn_readfirstlane(o.rowstep8);
+  dma4(ln.dma_a + BUF * kTileBytes, ra, ve, vo, soff, step);
+  dma4(ln.dma_b + BUF * kTileBytes, rb, ve, vo, soff, step);
 }
 
 // Operand fragments of k16 step st from buffer BUF: A rows wm*128 + 32i +
@@ -446,15 +476,44 @@ __device__ __forceinline__ void mma_step(const u32x4 (&fa)[4], const u32x4 (&fb)
                                                           __builtin_bit_cast(bf16x8, fb[j]), acc[i][j], 0, 0, 0);
 }
 
-// One k-tile in software-pipelined form.  On entry tile k sits in LDS buffer
-// BUF and its k16 steps 0 and 1 are in (fa0, fb0) and (fa1, fb1); the loads
-// of tile k+1 into the other buffer are in flight.  Steps 2 and 3 are read
-// while steps 0 and 1 multiply; the barrier falls between steps 2 and 3, once
-// tile k+1 has landed; then tile k2 is issued into BUF (free: every wave has
-// read its steps) while step 3's products cover the first reads of tile k+1.
-// On exit the invariant holds for tile k+1.
+// The k-tiles of one work item: nmain k-tiles of x . W0^T from kb, then
+// (for the workgroup that adds the rank term) KR k-tiles of T . U^T.  The
+// accumulators are scaled by s after the last k-tile of x . W0^T.
+struct KSeq {
+  Operands main, rank;
+  int kb, nmain, n;
+};
+
 template <int BUF>
-__device__ __forceinline__ void k_step(const Operands& o, const Lanes& ln, int k2, u32x4 (&fa0)[4], u32x4 (&fb0)[TJ],
+__device__ __forceinline__ void issue_seq(const KSeq& q, const Lanes& ln, int t) {
+  const bool m = t < q.nmain;
+  Operands o;
+  o.a = m ? q.main.a : q.rank.a;
+  o.b = m ? q.main.b : q.rank.b;
+  o.abytes = m ? q.main.abytes : q.rank.abytes;
+  o.bbytes = m ? q.main.bbytes : q.rank.bbytes;
+  o.row_bytes = m ? q.main.row_bytes : q.rank.row_bytes;
+  o.rowstep8 = m ? q.main.rowstep8 : q.rank.rowstep8;
+  o.kel = m ? q.main.kel : q.rank.kel;
+  issue<BUF>(o, ln, m ? q.kb + t : t - q.nmain);
+}
+
+// The first two k-tiles of a sequence into buffers 0 and 1 (the ring must be
+// free).
+__device__ __forceinline__ void prefetch(const KSeq& q, const Lanes& ln) {
+  issue_seq<0>(q, ln, 0);
+  if (q.n > 1) issue_seq<1>(q, ln, 1);
+}
+
+// One k-tile in software-pipelined form.  On entry k-tile t sits in LDS
+// buffer BUF and its k16 steps 0 and 1 are in (fa0, fb0) and (fa1, fb1); the
+// loads of k-tile t+1 into the other buffer are in flight.  Steps 2 and 3 are
+// read while steps 0 and 1 multiply; the barrier falls between steps 2 and 3,
+// once k-tile t+1 has landed; then k-tile t+2 (if any) is issued into BUF
+// (free: every wave has read its steps) while step 3's products cover the
+// first reads of k-tile t+1.  On exit the invariant holds for k-tile t+1.
+template <int BUF>
+__device__ __forceinline__ void k_step(const KSeq& q, const Lanes& ln, int t, u32x4 (&fa0)[4], u32x4 (&fb0)[TJ],
                                        u32x4 (&fa1)[4], u32x4 (&fb1)[TJ], f32x16 (&acc)[4][TJ]) {
   mma_step(fa0, fb0, acc);
   __builtin_amdgcn_sched_barrier(0);
@@ -470,30 +529,55 @@ __device__ __forceinline__ void k_step(const Operands& o, const Lanes& ln, int k
   __syncthreads();
   read_frags<1 - BUF>(ln, 0, fa0, fb0);
   __builtin_amdgcn_sched_barrier(0);
-  issue<BUF>(o, ln, k2);
+  if (t + 2 < q.n) issue_seq<BUF>(q, ln, t + 2);
   __builtin_amdgcn_sched_barrier(0);
   mma_step(fa1, fb1, acc);
   __builtin_amdgcn_sched_barrier(0);
   read_frags<1 - BUF>(ln, 1, fa1, fb1);
 }
 
-// acc += A[rows, kb*64 : ke*64] . B[rows, same]^T.  Leaves the LDS ring free
-// and no load in flight.
-__device__ __forceinline__ void k_loop(const Operands& o, int kb, int ke, f32x16 (&acc)[4][TJ], const Lanes& ln) {
-  const int n = ke - kb;
+__device__ __forceinline__ void scale_cols(f32x16 (&acc)[4][TJ], const float (&sc)[TJ]) {
+#pragma unroll
+  for (int j = 0; j < TJ; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i][j] *= sc[j];
+}
+
+// k-tiles t .. te-1 of a sequence (k-tile t sits in buffer t & 1).
+__device__ __forceinline__ void k_range(const KSeq& q, const Lanes& ln, int t, int te, u32x4 (&fa0)[4],
+                                        u32x4 (&fb0)[TJ], u32x4 (&fa1)[4], u32x4 (&fb1)[TJ], f32x16 (&acc)[4][TJ]) {
+  if (t < te && (t & 1)) {
+    k_step<1>(q, ln, t, fa0, fb0, fa1, fb1, acc);
+    ++t;
+  }
+  for (; t + 1 < te; t += 2) {
+    k_step<0>(q, ln, t, fa0, fb0, fa1, fb1, acc);
+    k_step<1>(q, ln, t + 1, fa0, fb0, fa1, fb1, acc);
+  }
+  if (t < te) k_step<0>(q, ln, t, fa0, fb0, fa1, fb1, acc);
+}
+
+// acc = the sequence's reduction (x . W0^T over its k-tiles, scaled by sc,
+// plus T . U^T when it has rank k-tiles).  Its first two k-tiles were issued
+// by prefetch(); every vector memory operation of the wave issued before
+// (stores of the previous item included) is waited for.  Leaves the LDS ring
+// free and no load in flight.  s_own: the scale of column threadIdx.x of the
+// tile (threads below BN), passed on to every wave through s_tile in LDS.
+__device__ __forceinline__ void k_run(const KSeq& q, float s_own, float* s_tile, f32x16 (&acc)[4][TJ],
+                                      const Lanes& ln) {
   u32x4 fa0[4], fb0[TJ], fa1[4], fb1[TJ];
-  issue<0>(o, ln, kb);
-  issue<1>(o, ln, min(kb + 1, ke - 1));
-  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // tile kb has landed (the next tile's eight loads may not)
+  wait_dma();
+  if (threadIdx.x < BN) s_tile[threadIdx.x] = s_own;
   __syncthreads();
   read_frags<0>(ln, 0, fa0, fb0);
   read_frags<0>(ln, 1, fa1, fb1);
-  for (int k = 0; k < n; k += 2) {
-    // Tiles past the end are loaded again as the last tile (clamped) and
-    // never multiplied.
-    k_step<0>(o, ln, min(kb + k + 2, ke - 1), fa0, fb0, fa1, fb1, acc);
-    if (k + 1 < n) k_step<1>(o, ln, min(kb + k + 3, ke - 1), fa0, fb0, fa1, fb1, acc);
-  }
+  k_range(q, ln, 0, q.nmain, fa0, fb0, fa1, fb1, acc);
+  float sc[TJ];
+  const int wn = int(threadIdx.x) / kWave % WN, lr = int(threadIdx.x) & 31;
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) sc[j] = s_tile[wn * (BN / WN) + j * 32 + lr];
+  scale_cols(acc, sc);
+  k_range(q, ln, q.nmain, q.n, fa0, fb0, fa1, fb1, acc);
   wait_dma();
   __syncthreads();
 }
@@ -513,12 +597,114 @@ __device__ __forceinline__ int tile_coords(const Args& a, int u, int& tm, int& t
   return j;
 }
 
+// Work item v of the launch: the k-slices of the split tiles first
+// (slice-major), then the whole tiles.
+struct Item {
+  int u, slice;    // tile of the processing order; k-slice, or -1 for a whole tile
+  int mj, m0, n0;  // member, first token and first output column
+  int kb, ke;      // k-tiles of x . W0^T
+  int rank;        // whether the item adds the rank term
+};
+
+__device__ __forceinline__ Item make_item(const Args& a, int v) {
+  Item it;
+  const int nsplit = a.split_tiles * a.S;
+  it.kb = 0;
+  it.ke = a.KT;
+  if (v < nsplit) {
+    it.u = v % a.split_tiles;
+    it.slice = v / a.split_tiles;
+    it.kb = it.slice * a.kps;
+    it.ke = min(a.KT, it.kb + a.kps);
+  } else {
+    it.u = a.split_tiles + (v - nsplit);
+    it.slice = -1;
+  }
+  int tm, tn;
+  it.mj = tile_coords(a, it.u, tm, tn);
+  it.m0 = tm * BM;
+  it.n0 = tn * BN;
+  // The rank term goes to the whole tile or to the last k-slice (the one
+  // ending at the last k-tile).
+  it.rank = a.R > 0 && (it.slice < 0 || it.ke == a.KT) ? 1 : 0;
+  return it;
+}
+
+__device__ __forceinline__ KSeq make_seq(const Args& a, const Item& it) {
+  const Member& mb = a.mem[it.mj];
+  KSeq q;
+  q.main = make_operands(mb.x, a.M, mb.w0, mb.O, it.m0, it.n0, a.I);
+  q.rank = make_operands(mb.t, a.M, mb.u, mb.O, it.m0, it.n0, a.R);  // unused without rank k-tiles
+  q.kb = it.kb;
+  q.nmain = it.ke - it.kb;
+  q.n = q.nmain + (it.rank ? a.KR : 0);
+  return q;
+}
+
+// Round the wave's 128 x 64 block to bf16 and store it, 16 rows at a time
+// through the wave's LDS staging area (outside the ring, so the next item's
+// first k-tiles can land meanwhile): the accumulator layout gives a lane one
+// column of four rows, the staging turns that into eight columns of one row,
+// so each lane stores 16 contiguous bytes.
+__device__ __forceinline__ void store_tile(const Args& a, const Member& mb, int m0, int n0, const f32x16 (&acc)[4][TJ],
+                                           lds_byte* stage) {
+  const int w = int(threadIdx.x) / kWave, l = int(threadIdx.x) % kWave, lr = l & 31, hi = l >> 5;
+  const int wm = w / WN, wn = w % WN;
+  lds_byte* const base = stage + w * kStageBytes;
+  lds_byte* const wr = base + 4 * hi * kStagePitch + lr * 2;            // row 4 hi (+ 8b' + e), column lr (+ 32j)
+  lds_byte* const rd = base + (l >> 3) * kStagePitch + (l & 7) * 16;    // row l/8 (+ 8r), columns 8 (l%8) .. +7
+  const int n = n0 + wn * (BN / WN) + (l & 7) * 8;
+  const bool wide = mb.wide && n + 8 <= mb.O;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      // Rows 32i + 16p + (8b' + 4hi + e) of the wave's block, b = 2p + b'.
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            *reinterpret_cast<lds_u16*>(wr + (8 * bb + e) * kStagePitch + j * 64) =
+                f32_to_bf16(acc[i][j][4 * (2 * p + bb) + e]);
+      // The wave reads back only what it wrote, and a wave's LDS operations
+      // complete in order: no barrier, only no compiler reordering.
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const u32x4 v = *reinterpret_cast<const lds_u32x4*>(rd + r * 8 * kStagePitch);
+        const int m = m0 + wm * 128 + i * 32 + p * 16 + r * 8 + (l >> 3);
+        if (m >= a.M) continue;
+        bf16_t* dst = mb.y + size_t(m) * mb.O + n;
+        if (wide) {
+          *reinterpret_cast<u32x4*>(dst) = v;
+        } else {
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            if (n + t < mb.O) dst[t] = bf16_t{uint16_t(v[t / 2] >> (16 * (t % 2)))};
+        }
+      }
+      asm volatile("" ::: "memory");
+    }
+}
+
+// NaN over the whole tile (a poisoned workspace).
+__device__ __forceinline__ void nan_tile(const Args& a, const Member& mb, int m0, int n0) {
+  for (int e = int(threadIdx.x); e < BM * BN; e += kThreads) {
+    const int m = m0 + e / BN, n = n0 + e % BN;
+    if (m < a.M && n < mb.O) mb.y[size_t(m) * mb.O + n] = bf16_t{f32_to_bf16(__builtin_nanf(""))};
+  }
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const Args& a, int slot) {
   return __builtin_amdgcn_make_buffer_rsrc(a.part + size_t(slot) * kPartFloats, 0, kPartFloats * 4, kRsrcFlags);
 }
 
 // Partials are laid out as the accumulators sit in registers: 16-byte piece
 // q = (TJ i + j) * 4 + c of every lane, lanes contiguous.
+constexpr int kPieces = 4 * TJ * 4;
+
 __device__ __forceinline__ void store_partial(const Args& a, int slot, const f32x16 (&acc)[4][TJ]) {
   const __amdgpu_buffer_rsrc_t rs = part_rsrc(a, slot);
   const int lane_off = int(threadIdx.x) * 16;
@@ -534,112 +720,128 @@ __device__ __forceinline__ void store_partial(const Args& a, int slot, const f32
       }
 }
 
-// acc = partial (first) or acc += partial.
-__device__ __forceinline__ void add_partial(const Args& a, int slot, bool first, f32x16 (&acc)[4][TJ]) {
-  const __amdgpu_buffer_rsrc_t rs = part_rsrc(a, slot);
-  const int lane_off = int(threadIdx.x) * 16;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off, ((i * TJ + j) * 4 + c) * kThreads * 16,
-                                                              kCoherent);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[i][j][4 * c + e] = first ? __uint_as_float(v[e]) : acc[i][j][4 * c + e] + __uint_as_float(v[e]);
-      }
-}
-
-// Scale by s, add T . U^T, round to bf16 and store.
-__device__ __forceinline__ void finish_tile(const Args& a, const Member& mb, int m0, int n0, f32x16 (&acc)[4][TJ],
-                                            const Lanes& ln) {
+// The tile of a slice that has stored its partial: every slice of the tile
+// sums its share of the pieces over all S partials, in slice order (so the
+// result does not depend on which slice arrives when), rounds and stores it.
+// Each partial already carries the scale by s, and the last slice's the rank
+// term.  False if the wait for the other slices timed out (nothing stored).
+// Needs S >= 2 (a slice's share is then at most half of the pieces).
+__device__ __forceinline__ bool reduce_share(const Args& a, const Member& mb, int u, int slice, int m0, int n0,
+                                             unsigned* s_flag) {
+  unsigned* counter = &a.ctrl[kCounterBase + u];
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool ok = false;
+    for (int it = 0; it < a.polls && !ok; ++it) {
+      ok = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= unsigned(a.S);
+      if (!ok) __builtin_amdgcn_s_sleep(1);
+    }
+    *s_flag = ok ? 1u : 0u;
+  }
+  __syncthreads();
+  const bool ok = *s_flag != 0u;
+  __syncthreads();  // every wave has read *s_flag before it is reused
+  if (!ok) return false;
   const int w = int(threadIdx.x) / kWave, l = int(threadIdx.x) % kWave, lr = l & 31, hi = l >> 5;
   const int wm = w / WN, wn = w % WN;
+  // This slice's pieces [p0, p0 + np) (np <= kPieces / 2 = 16), in batches
+  // of eight: a batch's loads of one partial are in flight together (past
+  // the share, a batch re-reads its last piece and drops it).
+  const int p0 = slice * kPieces / a.S, np = (slice + 1) * kPieces / a.S - p0;
+  const int lane_off = int(threadIdx.x) * 16;
+  for (int k0 = 0; k0 < np; k0 += 8) {
+    f32x4 sum[8];
+    for (int q = 0; q < a.S; ++q) {
+      const __amdgpu_buffer_rsrc_t rs = part_rsrc(a, q * a.split_tiles + u);
+      u32x4 d[8];
 #pragma unroll
-  for (int j = 0; j < TJ; ++j) {
-    const int n = n0 + wn * (BN / WN) + j * 32 + lr;
-    const float sc = n < mb.O ? (mb.s ? bf16_to_f32(mb.s[n].bits) : 1.f) : 0.f;
+      for (int k = 0; k < 8; ++k)
+        d[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off, (p0 + min(k0 + k, np - 1)) * kThreads * 16,
+                                                     kCoherent);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i][j] *= sc;
-  }
-  if (a.R > 0) {
-    const Operands r = make_operands(mb.t, a.M, mb.u, mb.O, m0, n0, a.R);
-    k_loop(r, 0, a.KR, acc, ln);
-  }
+      for (int k = 0; k < 8; ++k) {
+        const f32x4 f = {__uint_as_float(d[k][0]), __uint_as_float(d[k][1]), __uint_as_float(d[k][2]),
+                         __uint_as_float(d[k][3])};
+        sum[k] = q == 0 ? f : sum[k] + f;
+      }
+    }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
+    for (int k = 0; k < 8; ++k) {
+      const int pc = p0 + k0 + k;
+      if (k0 + k >= np) break;
+      const int i = pc / (TJ * 4), j = (pc / 4) % TJ, c = pc % 4;
       const int n = n0 + wn * (BN / WN) + j * 32 + lr;
       if (n >= mb.O) continue;
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int m = m0 + wm * 128 + i * 32 + 8 * b + 4 * hi + e;
-          if (m < a.M) mb.y[size_t(m) * mb.O + n] = bf16_t{f32_to_bf16(acc[i][j][4 * b + e])};
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + wm * 128 + i * 32 + 8 * c + 4 * hi + e;
+        if (m < a.M) mb.y[size_t(m) * mb.O + n] = bf16_t{f32_to_bf16(sum[k][e])};
+      }
     }
+  }
+  // Count out: the last of the tile's 2S arrivals resets the counter for the
+  // next launch (every slice has passed its wait by then).
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0 &&
+      __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == unsigned(2 * a.S - 1))
+    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
 }
 
-// k-tiles [kb, ke) of tile u: the whole reduction (slice < 0) or k-slice
-// `slice`; finishes the tile if it holds the whole reduction or is the last
-// of the tile's slices to arrive.
-__device__ __forceinline__ void do_tile(const Args& a, int u, int kb, int ke, int slice, const Lanes& ln,
-                                        unsigned* s_last, uint32_t err_at_entry) {
-  int tm, tn;
-  const Member& mb = a.mem[tile_coords(a, u, tm, tn)];
-  const int m0 = tm * BM, n0 = tn * BN;
-  f32x16 acc[4][TJ];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
-  k_loop(make_operands(mb.x, a.M, mb.w0, mb.O, m0, n0, a.I), kb, ke, acc, ln);
-  // Poisoned workspace (thread 0's copy of the error word decides for the
-  // workgroup): NaN over the tile, no partial, no counter.
-  if (threadIdx.x == 0) *s_last = err_at_entry;
-  __syncthreads();
-  if (*s_last != 0u) {
-    for (int e = int(threadIdx.x); e < BM * BN; e += kThreads) {
-      const int m = m0 + e / BN, n = n0 + e % BN;
-      if (m < a.M && n < mb.O) mb.y[size_t(m) * mb.O + n] = bf16_t{f32_to_bf16(__builtin_nanf(""))};
-    }
-    __syncthreads();  // every wave is past its read of *s_last before it is reused
-    return;
-  }
-  __syncthreads();
-  if (slice >= 0) {
-    store_partial(a, slice * a.split_tiles + u, acc);
-    __builtin_amdgcn_s_waitcnt(0);  // partial written through before counting in
-    __syncthreads();
-    if (threadIdx.x == 0)
-      *s_last = __hip_atomic_fetch_add(&a.ctrl[kCounterBase + u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                unsigned(a.S - 1);
-    __syncthreads();
-    if (!*s_last) return;
-    for (int q = 0; q < a.S; ++q) add_partial(a, q * a.split_tiles + u, q == 0, acc);
-    if (threadIdx.x == 0)
-      __hip_atomic_store(&a.ctrl[kCounterBase + u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  finish_tile(a, mb, m0, n0, acc, ln);
-}
-
+// Persistent workgroups: workgroup g takes items pos, pos + G, ... where pos
+// spreads the grid XCD-major.  Each item's first two k-tiles are loaded while
+// the previous item stores its results.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4))) void gemm_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes];
-  __shared__ unsigned s_last;
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves * kStageBytes];
+  __shared__ float s_tile[BN];
+  __shared__ unsigned s_flag;
   const int g = int(blockIdx.x), G = int(gridDim.x);
   const int pos = a.xcd_major ? (g % 8) * (G / 8) + g / 8 : g;
+  const int total = a.split_tiles * a.S + (a.start[a.n] - a.split_tiles);
   const Lanes ln = make_lanes(ring);
-  const uint32_t err_at_entry = load_error_word(a.err);
-  for (int v = pos; v < a.split_tiles * a.S; v += G) {
-    const int u = v % a.split_tiles, slice = v / a.split_tiles;
-    do_tile(a, u, slice * a.kps, min(a.KT, (slice + 1) * a.kps), slice, ln, &s_last, err_at_entry);
+  // Poisoned workspace (thread 0's copy of the error word decides for the
+  // workgroup): every item writes NaN over its tile and touches no counter.
+  if (threadIdx.x == 0) s_flag = load_error_word(a.err);
+  __syncthreads();
+  const bool poisoned = s_flag != 0u;
+  __syncthreads();
+  if (pos >= total) return;
+  Item it = make_item(a, pos);
+  prefetch(make_seq(a, it), ln);
+  for (int v = pos; v < total; v += G) {
+    const Member& mb = a.mem[it.mj];
+    float s_own = 0.f;
+    if (threadIdx.x < BN) {
+      const int n = it.n0 + int(threadIdx.x);
+      s_own = n < mb.O ? (mb.s ? bf16_to_f32(mb.s[n].bits) : 1.f) : 0.f;
+    }
+    f32x16 acc[4][TJ];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{};
+    k_run(make_seq(a, it), s_own, s_tile, acc, ln);
+    const Item cur = it;
+    if (v + G < total) {
+      it = make_item(a, v + G);
+      prefetch(make_seq(a, it), ln);
+    }
+    if (poisoned) {
+      nan_tile(a, mb, cur.m0, cur.n0);
+    } else if (cur.slice < 0) {
+      store_tile(a, mb, cur.m0, cur.n0, acc, (lds_byte*)stage);
+    } else {
+      store_partial(a, cur.slice * a.split_tiles + cur.u, acc);
+      __builtin_amdgcn_s_waitcnt(0);  // partial written through before counting in
+      __syncthreads();
+      if (!reduce_share(a, mb, cur.u, cur.slice, cur.m0, cur.n0, &s_flag)) {
+        if (threadIdx.x == 0) atomicOr(const_cast<unsigned*>(a.err), 1u);
+        nan_tile(a, mb, cur.m0, cur.n0);
+      }
+    }
   }
-  const int tiles = a.start[a.n];
-  for (int u = a.split_tiles + pos; u < tiles; u += G) do_tile(a, u, 0, a.KT, -1, ln, &s_last, err_at_entry);
 }
 
 }  // namespace big
@@ -1063,7 +1265,8 @@ hipError_t launch_forward_gemm(const GemmPlan& p, const Projection* projs, int64
     for (int j = 0; j < n; ++j)
       a.mem[j] = big::Member{static_cast<const bf16_t*>(projs[j].x), static_cast<const bf16_t*>(projs[j].s),
                              static_cast<const bf16_t*>(projs[j].w0), static_cast<const bf16_t*>(projs[j].u), t_of(j),
-                             static_cast<bf16_t*>(projs[j].y), int(projs[j].out_dim), p.tiles_n[j]};
+                             static_cast<bf16_t*>(projs[j].y), int(projs[j].out_dim), p.tiles_n[j],
+                             int(uintptr_t(projs[j].y) % 16 == 0 && projs[j].out_dim % 8 == 0)};
     a.M = int(m); a.I = int(in_dim); a.R = int(rank);
     a.tiles_m = p.tiles_m;
     a.KT = p.KT; a.KR = p.KR;
@@ -1071,6 +1274,7 @@ hipError_t launch_forward_gemm(const GemmPlan& p, const Projection* projs, int64
     a.ctrl = ctrl;
     a.err = err_word;
     a.part = reinterpret_cast<float*>(data + p.off_part);
+    a.polls = decode_wait_polls();
     hipLaunchKernelGGL(big::gemm_kernel, dim3(unsigned(p.grid)), dim3(big::kThreads), 0, stream, a);
     return hipGetLastError();
   }

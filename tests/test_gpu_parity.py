@@ -692,9 +692,12 @@ def test_timed_out_wait_poisons_the_workspace_until_cleared():
     # leaves the other control words alone; zeroing them makes it usable again.
     dec = _rand_case(16, 2048, 5376, 256, torch.bfloat16, seed=21)
     pre = _rand_case(300, 1000, 1032, 136, torch.bfloat16, seed=22)
+    # 128 tiles of 256 x 256, each split into two k-slices that wait for each other.
+    spl = _rand_case(2048, 4096, 4104, 72, torch.bfloat16, seed=24)
     grp = [_rand_case(4, O, I, R, torch.bfloat16, seed=23 + j) for j, (O, I, R) in enumerate(GROUPS["qkv60"])]
     need = max(tb.linear_forward_workspace_size(16, 2048, 5376, 256, torch.bfloat16),
-               tb.linear_forward_workspace_size(300, 1000, 1032, 136, torch.bfloat16), 64 << 20)
+               tb.linear_forward_workspace_size(300, 1000, 1032, 136, torch.bfloat16),
+               tb.linear_forward_workspace_size(2048, 4096, 4104, 72, torch.bfloat16), 64 << 20)
     ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
     ctrl = ws[:tb.WORKSPACE_CONTROL_BYTES]
     err = lambda: int(ws[:16].view(torch.int32)[2].item())
@@ -712,7 +715,7 @@ def test_timed_out_wait_poisons_the_workspace_until_cleared():
     snapshot = ctrl.clone()
     outs = [tb.linear_forward(*dec, workspace=ws), tb.linear_forward(dec[0], dec[1], dec[2], None, None, workspace=ws),
             tb.dense_forward(dec[0], dec[2], workspace=ws), tb.linear_forward(*pre, workspace=ws),
-            tb.linear_forward(pre[0], pre[1], pre[2], None, None, workspace=ws)]
+            tb.linear_forward(pre[0], pre[1], pre[2], None, None, workspace=ws), tb.linear_forward(*spl, workspace=ws)]
     outs += tb.linear_forward_group(grp, workspace=ws)
     torch.cuda.synchronize()
     assert all(nan(o) for o in outs)
@@ -725,6 +728,25 @@ def test_timed_out_wait_poisons_the_workspace_until_cleared():
     torch.cuda.synchronize()
     _parity(y, dec, what="cleared workspace, decode")
     _parity(yp, pre, what="cleared workspace, prefill")
+    assert stale_control_words(ctrl) == 0
+
+    _say("forced timeout: k-split prefill tiles")
+    tb.set_wait_polls(0)
+    try:
+        y = tb.linear_forward(*spl, workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        tb.set_wait_polls()
+    assert err() != 0 and nan(y)
+    ctrl.zero_()
+    y = tb.linear_forward(*spl, workspace=ws)
+    torch.cuda.synchronize()
+    x, s_, W0, U, V = spl
+    osel = torch.from_numpy(tile_sample(W0.shape[0], seed=3)).to(DEV)
+    tsel = torch.from_numpy(tile_sample(x.shape[0], seed=4, tile=64)).to(DEV)
+    check_forward(exact(y.index_select(0, tsel).index_select(1, osel)), exact(x.index_select(0, tsel)),
+                  exact(s_.index_select(0, osel)), exact(W0.index_select(0, osel)), exact(U.index_select(0, osel)),
+                  exact(V), bf16=True, what="cleared workspace, k-split prefill")
     assert stale_control_words(ctrl) == 0
 
     _say("forced timeout: grouped launch")
