@@ -896,6 +896,7 @@ struct Args {
   unsigned* ctrl;
   const unsigned* err;  // sticky error word: while set, nothing is published and no counter is touched
   float* part;     // [RB * CB][KS][kPartFloats]
+  int polls;       // bound of a slice's wait for the other slices of its tile
 };
 
 struct Lanes {
@@ -1066,8 +1067,12 @@ __global__ __launch_bounds__(kThreads) void xv_kernel(Args a) {
   __syncthreads();
   if (s_last != 0u) return;
   __syncthreads();
+  const int w = tid / kWave, l = tid % kWave, lr = l & 31, hi = l >> 5;
   if (a.KS > 1) {
-    // Partial in register order: 16-byte piece q = (2i + j) * 4 + c of every lane.
+    // Partial in register order: 16-byte piece q = (2i + j) * 4 + c of every
+    // lane.  Every slice of the tile then waits (bounded) for the others and
+    // sums its share of the pieces over all KS partials in slice order, so
+    // the result does not depend on arrival order.
     float* blk = a.part + size_t(tile) * a.KS * kPartFloats;
     const __amdgpu_buffer_rsrc_t mine =
         __builtin_amdgcn_make_buffer_rsrc(blk + size_t(ks) * kPartFloats, 0, kPartFloats * 4, kRsrcFlags);
@@ -1084,30 +1089,60 @@ __global__ __launch_bounds__(kThreads) void xv_kernel(Args a) {
         }
     __builtin_amdgcn_s_waitcnt(0);  // partial written through before counting in
     __syncthreads();
-    if (tid == 0)
-      s_last = __hip_atomic_fetch_add(&a.ctrl[kCounterBase + tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               unsigned(a.KS - 1);
-    __syncthreads();
-    if (!s_last) return;
-    for (int q = 0; q < a.KS; ++q) {
-      const __amdgpu_buffer_rsrc_t src =
-          __builtin_amdgcn_make_buffer_rsrc(blk + size_t(q) * kPartFloats, 0, kPartFloats * 4, kRsrcFlags);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const u32x4 val = __builtin_amdgcn_raw_buffer_load_b128(
-                src, tid * 16, ((i * 2 + j) * 4 + c) * kThreads * 16, kCoherent);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc[i][j][4 * c + e] = q == 0 ? __uint_as_float(val[e]) : acc[i][j][4 * c + e] + __uint_as_float(val[e]);
-          }
+    unsigned* counter = &a.ctrl[kCounterBase + tile];
+    if (tid == 0) {
+      __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bool ok = false;
+      for (int it = 0; it < a.polls && !ok; ++it) {
+        ok = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= unsigned(a.KS);
+        if (!ok) __builtin_amdgcn_s_sleep(1);
+      }
+      s_last = ok ? 1u : 0u;
+      if (!ok) atomicOr(const_cast<unsigned*>(a.err), 1u);
     }
-    if (tid == 0) __hip_atomic_store(&a.ctrl[kCounterBase + tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (s_last == 0u) return;  // timed out: the sticky error word makes the projection's y NaN
+    constexpr int kPieces = 16;
+    const int p0 = ks * kPieces / a.KS, np = (ks + 1) * kPieces / a.KS - p0;
+    f32x4 sum[kPieces / 2];
+    for (int k0 = 0; k0 < np; k0 += kPieces / 2) {
+      for (int q = 0; q < a.KS; ++q) {
+        const __amdgpu_buffer_rsrc_t src =
+            __builtin_amdgcn_make_buffer_rsrc(blk + size_t(q) * kPartFloats, 0, kPartFloats * 4, kRsrcFlags);
+        u32x4 d[kPieces / 2];
+#pragma unroll
+        for (int k = 0; k < kPieces / 2; ++k)
+          d[k] = __builtin_amdgcn_raw_buffer_load_b128(src, tid * 16, (p0 + min(k0 + k, np - 1)) * kThreads * 16,
+                                                       kCoherent);
+#pragma unroll
+        for (int k = 0; k < kPieces / 2; ++k) {
+          const f32x4 f = {__uint_as_float(d[k][0]), __uint_as_float(d[k][1]), __uint_as_float(d[k][2]),
+                           __uint_as_float(d[k][3])};
+          sum[k] = q == 0 ? f : sum[k] + f;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kPieces / 2; ++k) {
+        if (k0 + k >= np) break;
+        const int pc = p0 + k0 + k, i = pc / 8, j = (pc / 4) % 2, bb = pc % 4;
+        const int n = n0 + 64 * w + 32 * j + lr;
+        if (n >= a.R) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = m0 + 32 * i + 8 * bb + 4 * hi + e;
+          if (m < a.M) mb.t[size_t(m) * a.R + n] = bf16_t{f32_to_bf16(sum[k][e])};
+        }
+      }
+    }
+    // Count out: the last of the tile's 2 KS arrivals resets the counter for
+    // the next launch (every slice has passed its wait by then).
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0 &&
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == unsigned(2 * a.KS - 1))
+      __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
   }
-  const int w = tid / kWave, l = tid % kWave, lr = l & 31, hi = l >> 5;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -1245,6 +1280,7 @@ hipError_t launch_forward_gemm(const GemmPlan& p, const Projection* projs, int64
     a.ctrl = ctrl;
     a.err = err_word;
     a.part = reinterpret_cast<float*>(data + p.off_xvpart);
+    a.polls = decode_wait_polls();
     hipLaunchKernelGGL(xv::xv_kernel, dim3(unsigned(n * p.xv_rb * p.xv_cb * p.xv_ks)), dim3(xv::kThreads), 0, stream,
                        a);
     hipError_t e = hipGetLastError();
