@@ -14,8 +14,16 @@
  * Conventions shared by every entry point
  *   - Matrices are dense, row-major, with the leading dimension equal to the
  *     row length.  All pointers except band_out are DEVICE pointers on the
- *     current HIP device.  The caller owns all memory; the library allocates
- *     nothing, frees nothing and keeps no pointer after a call returns.
+ *     current HIP device.  The caller owns all memory and the library keeps
+ *     no caller pointer after a call returns.  The forward, reconstruct and
+ *     error calls allocate and free nothing.  Two exceptions, both held until
+ *     the process ends: tb_linear_forward_no_alloc's static device scratch
+ *     (one per GPU, set up on its first call there), and the decomposition
+ *     calls that multiply through rocBLAS (tb_lowrank_factors,
+ *     tb_lowrank_factors_batch, tb_refine_shared_block), which create one
+ *     rocBLAS handle per (device, stream) on first use; rocBLAS allocates
+ *     that handle's own device workspace then.  Those three calls are
+ *     therefore not for HIP graph capture or allocation-free callers.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Device work is enqueued on it asynchronously; outputs are valid once
  *     the caller synchronises that stream.  No entry point synchronises.

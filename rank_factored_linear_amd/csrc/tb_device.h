@@ -120,10 +120,14 @@ __device__ __forceinline__ f32x4 mma_k32(const Frag8<float>& a, const Frag8<floa
 }
 
 // Wait states after a group of matrix-core ops whose A/B registers the
-// following code may rewrite at once.  In a chain of 16x16x32 ops that
+// following code may rewrite at once: the write-after-read rule for
+// matrix-core source operands (a VGPR that an issued op still reads must not
+// be overwritten before the op has read it).  In a chain of 16x16x32 ops that
 // accumulate into the same registers, an ALU write to the A or B register of
 // an op right behind it gave wrong products on gfx950 (the compiler put no
 // wait states there); 24 wait states after each group removed every error.
+// 24 is empirical (the smallest count tried that did), with room for 16-pass
+// ops.
 __device__ __forceinline__ void mfma_operand_guard() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: ); }
 
 // Agent-scope read-modify-write with acquire/release semantics.  On gfx950
