@@ -852,6 +852,14 @@ int64_t decode_max_rows(int) { return 96; }
 // the streams and the 60-layer stack at 16 tokens slower, 227 -> 234 us per
 // layer.)
 constexpr int64_t kShortSlice = 768, kLongSlice = 5632;
+// A short reduction (in_dim <= 1536) is split into slices of about 144: its
+// producers then finish in a few microseconds, while one producer per column
+// block spent ~9 us streaming its V columns alone (stamped) and left the
+// streamers waiting.  26-layer banded stack at 1 / 4 / 16 tokens, one box,
+// slices of 1152 / 576 / 288 / 192 / 144 / 96 / 72: 1.432 / 1.465 / 1.389 /
+// 1.349 / 1.332 / 1.367 / 1.394 ms per step at 1 token, the same order at 4
+// and 16.
+constexpr int64_t kTinySlice = 144, kShortReduction = 1536;
 constexpr int64_t kLongStreamElems = int64_t(56) << 20;
 // x sizes (tokens x in_dim) up to which the streamers take one k-slice each:
 // the x that every row block re-reads is small next to the cost of combining
@@ -900,11 +908,10 @@ DecodePlan plan_decode(int64_t m, int64_t out_dim, int64_t in_dim, int64_t rank,
   // Producers: 64 columns of T each, over k-slices of in_dim.
   if (rank > 0) {
     p.NCB = int((rank + kCbCols - 1) / kCbCols);
-    // Short reductions (in_dim <= 1536) stay in one producer per column block:
-    // its longer load phase costs less than the extra round trips of
-    // combining k-slice partials across workgroups.
-    const int64_t slice = stream_elems >= kLongStreamElems ? kLongSlice : kShortSlice;
-    int64_t kt = in_dim <= 1536 ? 1 : (in_dim + slice - 1) / slice;
+    const int64_t slice = in_dim <= kShortReduction        ? kTinySlice
+                          : stream_elems >= kLongStreamElems ? kLongSlice
+                                                             : kShortSlice;
+    int64_t kt = (in_dim + slice - 1) / slice;
     if (kt > kMaxKT) kt = kMaxKT;
     if (p.NCB > kMaxGroupCounters / 2) kt = 1;  // one arrival counter per column block
     p.KT = int(kt);
