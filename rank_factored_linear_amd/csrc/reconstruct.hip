@@ -137,16 +137,17 @@ __global__ __launch_bounds__(kThreads, 2) void reconstruct_mfma_kernel(const bf1
 
 // ---- bf16 bundles, 192 < rank <= 256: persistent, direct-to-LDS ----------------
 //
-// One workgroup per compute unit walks its output tiles (128 x 128) in turn.
-// A tile's whole U and V (four k-tiles of 64) fit the 128 KB LDS ring, one
-// slot per k-tile, filled by direct-to-LDS buffer loads; each slot is
-// refilled for the next tile as soon as every wave has read it, so the loads
-// of tile j+1 fly while tile j multiplies.  The W0 and s values of tile j+2
-// are loaded into registers at the end of tile j's epilogue (two register
-// sets, alternating) and so have two tiles' time to arrive.  The epilogue moves each wave's 64 x 64
-// accumulators through LDS (the slot of the last k-tile) so that 16 lanes
+// Two workgroups per compute unit walk their output tiles (128 x 128) in
+// turn, so that one workgroup's matrix-core and LDS work overlaps the other's
+// waits.  U and V come in k-tiles of 32 through a four-slot LDS ring (16 KB a
+// slot) by direct-to-LDS buffer loads; each slot is refilled, three k-tiles
+// ahead and across tile boundaries, as soon as every wave has read it.  The
+// W0 and s values of the next tile are loaded into registers at the end of a
+// tile's epilogue and so have its whole k-loop to arrive.  The epilogue moves
+// each wave's 64 x 64 accumulators through LDS (the slot of the last k-tile
+// for waves 0 and 1, a 16 KB staging area for waves 2 and 3) so that 16 lanes
 // cover 64 consecutive outputs of one row: 128-byte W0 reads and 256-byte
-// non-temporal fp32 writes per row.
+// non-temporal fp32 writes per row.  80 KB of LDS per workgroup.
 //
 // Memory instructions complete in issue order, so the wait for a k-tile is a
 // count of the loads and stores issued after it: every load and store here
@@ -155,14 +156,24 @@ __global__ __launch_bounds__(kThreads, 2) void reconstruct_mfma_kernel(const bf1
 // last one are loaded as zeros, and the counts below are exact.
 namespace rp {
 
-constexpr int BT = 128, BK = 64, KT = 4;
-constexpr int kOpBytes = BT * BK * 2;         // one operand's k-tile: 128 rows of 128 bytes
-constexpr int kSlotBytes = 2 * kOpBytes;      // [U k-tile][V k-tile]
-constexpr int kRingBytes = KT * kSlotBytes;   // 128 KB
-constexpr int kStageRow = 256;                // epilogue staging: rows of 64 fp32 per wave
+constexpr int BT = 128, BK = 32, kSlots = 4;
+constexpr int kOpBytes = BT * BK * 2;             // one operand's k-tile: 128 rows of 64 bytes
+constexpr int kSlotBytes = 2 * kOpBytes;          // [U k-tile][V k-tile], 16 KB
+constexpr int kRingBytes = kSlots * kSlotBytes;   // 64 KB
+constexpr int kWaveStage = 8192;                  // one wave's epilogue rows: 32 x 64 fp32
+constexpr int kLdsBytes = kRingBytes + 2 * kWaveStage;
+constexpr int kStageRow = 256;
 constexpr unsigned kRsrcFlags = 0x00020000u;  // buffer descriptor word 3: 32-bit data format
 constexpr int kPast = int(0x80000000u);       // lane offset past every buffer
 constexpr int kNT = 2;                        // non-temporal cache policy
+static_assert(2 * kLdsBytes <= 160 * 1024, "two workgroups per compute unit");
+
+// k-tiles per output tile for a rank: ceil(rank / 32) rounded up to 2, 4 or 8
+// (the k-tiles past the rank load zeros), which covers every rank up to 256.
+inline int ktiles(int64_t R) {
+  const int k = int((R + BK - 1) / BK);
+  return k <= 2 ? 2 : k <= 4 ? 4 : 8;
+}
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -201,24 +212,19 @@ __device__ __forceinline__ Tile tile_at(int t, int tiles_i, const bf16_t* s, con
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-// Four direct-to-LDS loads: load j writes 1 KB at dst + j KB (lane l at
+// Two direct-to-LDS loads: load j writes 1 KB at dst + j KB (lane l at
 // +16 l) from lane offset v[j] + soff.  The buffer's range check covers the
 // lane offset only, so every lane offset carries its row and chunk (or lies
 // past the buffer: the lane then writes zeros).  M0 takes one wait state
 // before a load that reads it.
-__device__ __forceinline__ void dma4(unsigned dst, __amdgpu_buffer_rsrc_t r, const int (&v)[4], int soff) {
+__device__ __forceinline__ void dma2(unsigned dst, __amdgpu_buffer_rsrc_t r, const int (&v)[2], int soff) {
   asm volatile(
       "s_mov_b32 m0, %[d0]\n\ts_nop 0\n\t"
       "buffer_load_dwordx4 %[v0], %[r], %[so] offen lds\n\t"
       "s_mov_b32 m0, %[d1]\n\ts_nop 0\n\t"
-      "buffer_load_dwordx4 %[v1], %[r], %[so] offen lds\n\t"
-      "s_mov_b32 m0, %[d2]\n\ts_nop 0\n\t"
-      "buffer_load_dwordx4 %[v2], %[r], %[so] offen lds\n\t"
-      "s_mov_b32 m0, %[d3]\n\ts_nop 0\n\t"
-      "buffer_load_dwordx4 %[v3], %[r], %[so] offen lds"
+      "buffer_load_dwordx4 %[v1], %[r], %[so] offen lds"
       :
-      : [d0] "s"(dst), [d1] "s"(dst + 1024u), [d2] "s"(dst + 2048u), [d3] "s"(dst + 3072u), [v0] "v"(v[0]),
-        [v1] "v"(v[1]), [v2] "v"(v[2]), [v3] "v"(v[3]), [r] "s"(r), [so] "s"(soff)
+      : [d0] "s"(dst), [d1] "s"(dst + 1024u), [v0] "v"(v[0]), [v1] "v"(v[1]), [r] "s"(r), [so] "s"(soff)
       : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -229,13 +235,16 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Per-lane constants of the direct-to-LDS loads: wave w fills rows
-// 32 w + 8 j + l / 8 (j = 0..3) of each operand's k-tile; lane l lands in
-// chunk l % 8 of its row and fetches the global chunk that the swizzle
-// (row >> 1) & 7 stores there.  Even and odd j share a swizzle.
+// Per-lane constants of the direct-to-LDS loads.  A k-tile row is 64 bytes,
+// four 16-byte chunks; chunk c of row r is stored at position
+// c ^ ((r >> 2) & 3), so that the fragment reads of 16 consecutive rows (one
+// chunk each) hit 16 distinct 16-byte bank groups.  Wave w fills rows
+// 32 w + 16 j + l / 4 (j = 0, 1) of each operand's k-tile: lane l lands at
+// position l % 4 of its row and fetches the global chunk that the swizzle
+// stores there, (l % 4) ^ ((l >> 4) & 3) for both j.
 struct Dma {
-  unsigned dst;      // this wave's first KB of slot 0, U operand
-  int row, ce, co;   // row of load 0; global chunks fetched by even and odd j
+  unsigned dst;  // this wave's first KB of slot 0, U operand
+  int row, c;    // row of load 0; global chunk
 };
 
 // k-tile kt of tile g into ring slot SLOT.  Rows past the tile's, chunks past
@@ -243,18 +252,16 @@ struct Dma {
 // zeros.
 template <int SLOT>
 __device__ __forceinline__ void issue(const Dma& d, const Tile& g, int kt, bool dummy, int R) {
-  const int left = R - kt * BK;
-  int vu[4], vv[4];
+  const bool ok = !dummy && d.c * 8 < R - kt * BK;
+  int vu[2], vv[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = d.row + 8 * j, c = (j & 1) ? d.co : d.ce;
-    const bool ok = !dummy && c * 8 < left;
-    const int off = row * R * 2 + (c << 4);
+  for (int j = 0; j < 2; ++j) {
+    const int row = d.row + 16 * j, off = row * R * 2 + (d.c << 4);
     vu[j] = (ok && row < g.orows) ? off : kPast;
     vv[j] = (ok && row < g.irows) ? off : kPast;
   }
-  dma4(d.dst + SLOT * kSlotBytes, g.ru, vu, kt * BK * 2);
-  dma4(d.dst + SLOT * kSlotBytes + kOpBytes, g.rv, vv, kt * BK * 2);
+  dma2(d.dst + SLOT * kSlotBytes, g.ru, vu, kt * BK * 2);
+  dma2(d.dst + SLOT * kSlotBytes + kOpBytes, g.rv, vv, kt * BK * 2);
 }
 
 // Epilogue layout: in round cb (0, 1) lane l of wave w handles output row
@@ -284,18 +291,17 @@ __device__ __forceinline__ void prefetch(Pre& q, const Tile& g, bool dummy, int 
     }
 }
 
-// Measuring the error against an fp32 original: the original's values in the
-// epilogue layout, one tile ahead (64 registers; two tiles ahead would spill).
-__device__ __forceinline__ void load_orig(u32x4 (&o)[2][8], const Tile& g, bool dummy, int I, int wo, int wi, int l) {
+// Measuring the error against an fp32 original: the original's values of
+// epilogue round cb, loaded as the round starts (the registers of a whole
+// tile ahead would not fit two workgroups per compute unit).
+__device__ __forceinline__ void load_orig(u32x4 (&o)[8], const Tile& g, int cb, int I, int wo, int wi, int l) {
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int orel = wo * 64 + cb * 32 + 4 * p + (l >> 4), i = g.i0 + wi * 64 + (l & 15) * 4;
-      const bool ok = !dummy && orel < g.orows && i < I;
-      o[cb][p] = __builtin_amdgcn_raw_buffer_load_b128(g.ro, ok ? (orel * I + i) * 4 : kPast, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  for (int p = 0; p < 8; ++p) {
+    const int orel = wo * 64 + cb * 32 + 4 * p + (l >> 4), i = g.i0 + wi * 64 + (l & 15) * 4;
+    const bool ok = orel < g.orows && i < I;
+    o[p] = __builtin_amdgcn_raw_buffer_load_b128(g.ro, ok ? (orel * I + i) * 4 : kPast, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 __device__ __forceinline__ f32x16 mma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -303,23 +309,23 @@ __device__ __forceinline__ f32x16 mma32(u32x4 a, u32x4 b, f32x16 c) {
                                                  0);
 }
 
-// Fragments of k16 steps 0..3 of the k-tile in ring slot SLOT (A from V rows
+// Fragments of k16 steps 0, 1 of the k-tile in ring slot SLOT (A from V rows
 // 64 wi + 32 rb + lane % 32, B from U rows 64 wo + 32 cb + lane % 32, chunk
-// 2 ks + lane / 32, swizzled), then the 16 products.
+// ks * 2 + lane / 32, swizzled), then the 8 products.
 template <int SLOT>
-__device__ __forceinline__ void multiply_step(lds_byte* const (&rdU)[2][4], lds_byte* const (&rdV)[2][4],
+__device__ __forceinline__ void multiply_step(lds_byte* const (&rdU)[2], lds_byte* const (&rdV)[2],
                                               f32x16 (&acc)[2][2]) {
-  constexpr int pr = SLOT / 2, off = (SLOT % 2) * kSlotBytes;
-  u32x4 fa[2][4], fb[2][4];
+  constexpr int off = SLOT * kSlotBytes;
+  u32x4 fa[2][2], fb[2][2];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
+  for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      fa[r][ks] = *reinterpret_cast<const lds_u32x4*>(rdV[pr][ks] + off + kOpBytes + r * 32 * 128);
-      fb[r][ks] = *reinterpret_cast<const lds_u32x4*>(rdU[pr][ks] + off + r * 32 * 128);
+      fa[r][ks] = *reinterpret_cast<const lds_u32x4*>(rdV[ks] + off + kOpBytes + r * 32 * 64);
+      fb[r][ks] = *reinterpret_cast<const lds_u32x4*>(rdU[ks] + off + r * 32 * 64);
     }
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
+  for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -345,41 +351,38 @@ __device__ __forceinline__ void store_out(const Tile& g, int off, f32x4 c, u32x2
 }
 
 // The k-tiles of all of a workgroup's output tiles form one stream: k-tile
-// k of its n-th tile is stream entry j = n KT + k (KT = k-tiles per tile,
-// ceil(rank / 64)) and lives in ring slot j % 4.  Step j waits for entry j,
-// publishes it to every wave, refills the slot every wave has just finished
-// with (entry j + 3) and multiplies.  After a tile's last step its epilogue
-// goes through the slot that step read, then issues the tile-end loads:
-// (kErr) the original of the next tile, 16 loads, and the W0 and s of the
-// tile two ahead, 32 loads; the stores of the epilogue are 16 more (none when
-// kErr).  Every load and store is issued unconditionally, so the count of
-// memory instructions after entry j's last load when step j waits is a
-// constant: the refills of the two steps between (16) plus 48 for each tile
-// end among the three steps before j.  vmcnt counts up to 63, so 63 stands
-// for any larger count.  (The prologue issues entries 0..2 and then 64 or
-// more loads, at least as many.)
+// k of its n-th tile is stream entry j = n KT + k (KT k-tiles per tile) and
+// lives in ring slot j % 4.  Step j waits for entry j, publishes it to every
+// wave, refills the slot every wave has just finished with (entry j + 3)
+// and multiplies.  After a tile's last step its epilogue goes through the
+// slot that step read (kErr: with 8 loads of the original in each of its two
+// rounds), then issues the W0 and s loads of the next tile, 32; the stores of
+// the epilogue are 16 more (none when kErr).  Every load and
+// store is issued unconditionally, so the count of memory instructions
+// issued after entry j when step j waits is a constant: the refills of the
+// two steps between (4 each) plus 48 for each tile end among the three steps
+// before j.  vmcnt counts up to 63, so 63 stands for any larger count.  (The
+// prologue waits for all of its loads, so entries 0..2 have landed.)
 template <int KT>
 __host__ __device__ constexpr int step_wait(int k) {
   int ends = 0;
   for (int r = k - 3; r < k; ++r)
     if ((((r + 1) % KT) + KT) % KT == 0) ++ends;
-  const int n = 16 + 48 * ends;
+  const int n = 8 + 48 * ends;
   return n < 63 ? n : 63;
 }
-static_assert(step_wait<4>(0) == 63 && step_wait<4>(1) == 63 && step_wait<4>(2) == 63 && step_wait<4>(3) == 16,
-              "four k-tiles per tile");
-static_assert(step_wait<1>(0) == 63 && step_wait<2>(1) == 63 && step_wait<3>(2) == 63 && step_wait<3>(3) == 63,
-              "a tile end among every three steps");
+static_assert(step_wait<8>(0) == 56 && step_wait<8>(3) == 8 && step_wait<8>(7) == 8, "eight k-tiles per tile");
+static_assert(step_wait<4>(0) == 56 && step_wait<4>(3) == 8, "four k-tiles per tile");
+static_assert(step_wait<2>(1) == 56 && step_wait<2>(0) == 63, "two tile ends among three steps");
 
 template <int V> struct IC { static constexpr int value = V; };
 
 // Output tile number t (of this workgroup's sequence, stream entries from
 // J0 mod 4 on); tile(t') gives the views of a later tile.
 template <typename EO, bool kErr, int KT, int J0, typename TileFn>
-__device__ __forceinline__ void tile_pass(const Dma& d, lds_byte* const (&rdU)[2][4], lds_byte* const (&rdV)[2][4],
+__device__ __forceinline__ void tile_pass(const Dma& d, lds_byte* const (&rdU)[2], lds_byte* const (&rdV)[2],
                                           lds_byte* base, const TileFn& tile, int t, int G, int tiles, Pre& q,
-                                          u32x4 (&o)[2][8], int I, int R, int wo, int wi, int l, double& num,
-                                          double& den) {
+                                          int I, int R, int wo, int wi, int l, double& num, double& den) {
   const int lr = l & 31, h = l >> 5, w = wo * 2 + wi;
   const Tile g = tile(t);
   f32x16 acc[2][2];
@@ -395,17 +398,20 @@ __device__ __forceinline__ void tile_pass(const Dma& d, lds_byte* const (&rdU)[2
     constexpr int dn = (k + 3) / KT, kk = (k + 3) % KT;   // entry j + 3: tile t + dn G, k-tile kk
     wait_vm<step_wait<KT>(k)>();
     __syncthreads();
-    issue<(J0 + k + 3) % 4>(d, tile(t + dn * G), kk, t + dn * G >= tiles, R);
-    multiply_step<(J0 + k) % 4>(rdU, rdV, acc);
+    issue<(J0 + k + 3) % kSlots>(d, tile(t + dn * G), kk, t + dn * G >= tiles, R);
+    multiply_step<(J0 + k) % kSlots>(rdU, rdV, acc);
   };
   step(IC<0>{});
   if constexpr (KT > 1) step(IC<1>{});
-  if constexpr (KT > 2) step(IC<2>{});
-  if constexpr (KT > 3) step(IC<3>{});
+  if constexpr (KT > 2) { step(IC<2>{}); step(IC<3>{}); }
+  if constexpr (KT > 4) { step(IC<4>{}); step(IC<5>{}); step(IC<6>{}); step(IC<7>{}); }
 
-  lds_byte* stage = base + ((J0 + KT - 1) % 4) * kSlotBytes + w * 8192;
+  lds_byte* stage = w < 2 ? base + ((J0 + KT - 1) % kSlots) * kSlotBytes + w * kWaveStage
+                          : base + kRingBytes + (w - 2) * kWaveStage;
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
+    u32x4 o[8];
+    if constexpr (kErr) load_orig(o, g, cb, I, wo, wi, l);
     __syncthreads();
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
@@ -433,7 +439,7 @@ __device__ __forceinline__ void tile_pass(const Dma& d, lds_byte* const (&rdU)[2
                              c[p][2] + so * bf16_to_f32(uint16_t(wv[1])), c[p][3] + so * bf16_to_f32(uint16_t(wv[1] >> 16))};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const double ov = double(__uint_as_float(o[cb][p][e])), dd = ov - double(wr[e]);
+          const double ov = double(__uint_as_float(o[p][e])), dd = ov - double(wr[e]);
           num += dd * dd;
           den += ov * ov;
         }
@@ -442,15 +448,14 @@ __device__ __forceinline__ void tile_pass(const Dma& d, lds_byte* const (&rdU)[2
       }
     }
   }
-  if constexpr (kErr) load_orig(o, tile(t + G), t + G >= tiles, I, wo, wi, l);
-  prefetch(q, tile(t + 2 * G), t + 2 * G >= tiles, I, wo, wi, l);
+  prefetch(q, tile(t + G), t + G >= tiles, I, wo, wi, l);
 }
 
 // kErr = false: out receives the rebuilt weight.  kErr = true: out is the
 // fp32 original (read only) and the relative error goes to *result through
-// the grid-wide sum of tb_reduce.h (partial, counters).  KT = ceil(rank / 64).
+// the grid-wide sum of tb_reduce.h (partial, counters).  KT = ktiles(rank).
 template <typename EO, bool kErr, int KT>
-__global__ __launch_bounds__(kThreads, 1) void reconstruct_persistent_kernel(const bf16_t* __restrict__ s,
+__global__ __launch_bounds__(kThreads, 2) void reconstruct_persistent_kernel(const bf16_t* __restrict__ s,
                                                                              const bf16_t* __restrict__ w0,
                                                                              const bf16_t* __restrict__ u,
                                                                              const bf16_t* __restrict__ v,
@@ -458,7 +463,7 @@ __global__ __launch_bounds__(kThreads, 1) void reconstruct_persistent_kernel(con
                                                                              int R, int tiles_i, int tiles,
                                                                              uint64_t* partial, unsigned* counters,
                                                                              double* result) {
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kLdsBytes];
   double num = 0.0, den = 0.0;
   const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6), l = int(threadIdx.x) & 63;
   const int wi = w & 1, wo = w >> 1, lr = l & 31, h = l >> 5;
@@ -468,59 +473,51 @@ __global__ __launch_bounds__(kThreads, 1) void reconstruct_persistent_kernel(con
 
   lds_byte* base = (lds_byte*)ring;
   Dma d;
+  d.row = w * 32 + (l >> 2);
+  d.c = (l & 3) ^ ((l >> 4) & 3);
+  d.dst = __builtin_amdgcn_readfirstlane(unsigned(uintptr_t(base)) + unsigned(w) * 2048u);
+  // Fragment bases per k16 step: U row 64 wo + lane % 32, V row 64 wi + lane % 32
+  // (the V operand sits kOpBytes into each slot).
+  lds_byte* rdU[2];
+  lds_byte* rdV[2];
   {
-    const int pos = l & 7;
-    d.row = w * 32 + (l >> 3);
-    d.ce = pos ^ ((d.row >> 1) & 7);
-    d.co = pos ^ (((d.row + 8) >> 1) & 7);
-    d.dst = __builtin_amdgcn_readfirstlane(unsigned(uintptr_t(base)) + unsigned(w) * 4096u);
-  }
-  // Fragment bases per slot pair (0/1, 2/3) and k16 step: U row 64 wo + lane % 32,
-  // V row 64 wi + lane % 32 (the V operand sits kOpBytes into each slot).
-  lds_byte* rdU[2][4];
-  lds_byte* rdV[2][4];
-  {
-    const int x = (lr >> 1) & 7;
+    const int x = (lr >> 2) & 3;
 #pragma unroll
-    for (int pr = 0; pr < 2; ++pr)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int chunk = ((2 * ks + h) ^ x) << 4;
-        rdU[pr][ks] = opaque(base + pr * 2 * kSlotBytes + (wo * 64 + lr) * 128 + chunk);
-        rdV[pr][ks] = opaque(base + pr * 2 * kSlotBytes + (wi * 64 + lr) * 128 + chunk);
-      }
+    for (int ks = 0; ks < 2; ++ks) {
+      const int chunk = ((2 * ks + h) ^ x) << 4;
+      rdU[ks] = opaque(base + (wo * 64 + lr) * 64 + chunk);
+      rdV[ks] = opaque(base + (wi * 64 + lr) * 64 + chunk);
+    }
   }
 
   // Tiles past the workgroup's last are dummies: their loads return zeros
   // into free slots and registers, and nothing of them is stored.
   const auto tile = [&](int tt) { return tile_at<EO>(tt < tiles ? tt : t, tiles_i, s, w0, u, v, out, O, I, R); };
-  Pre qa, qb;         // W0 and s of the current tile and of the next, alternating
-  u32x4 oq[2][8];     // the current tile's original (kErr)
-  // Stream entries 0..2.
+  Pre q;  // W0 and s of the current tile
+  // Stream entries 0..2 and the first tile's W0 and s, all landed before the
+  // first step.
   issue<0>(d, tile(t), 0, false, R);
   issue<1>(d, tile(t + (1 / KT) * G), 1 % KT, t + (1 / KT) * G >= tiles, R);
   issue<2>(d, tile(t + (2 / KT) * G), 2 % KT, t + (2 / KT) * G >= tiles, R);
-  prefetch(qa, tile(t), false, I, wo, wi, l);
-  prefetch(qb, tile(t + G), t + G >= tiles, I, wo, wi, l);
-  if constexpr (kErr) load_orig(oq, tile(t), false, I, wo, wi, l);
-  // Four tiles per round, so that every slot index is a constant.
+  prefetch(q, tile(t), false, I, wo, wi, l);
+  wait_vm<0>();
+  // One tile per round when KT is a multiple of 4, two when it is 2, so that
+  // every slot index is a constant.
   for (;;) {
-    tile_pass<EO, kErr, KT, 0>(d, rdU, rdV, base, tile, t, G, tiles, qa, oq, I, R, wo, wi, l, num, den);
+    tile_pass<EO, kErr, KT, 0>(d, rdU, rdV, base, tile, t, G, tiles, q, I, R, wo, wi, l, num, den);
     if ((t += G) >= tiles) break;
-    tile_pass<EO, kErr, KT, KT % 4>(d, rdU, rdV, base, tile, t, G, tiles, qb, oq, I, R, wo, wi, l, num, den);
-    if ((t += G) >= tiles) break;
-    tile_pass<EO, kErr, KT, (2 * KT) % 4>(d, rdU, rdV, base, tile, t, G, tiles, qa, oq, I, R, wo, wi, l, num, den);
-    if ((t += G) >= tiles) break;
-    tile_pass<EO, kErr, KT, (3 * KT) % 4>(d, rdU, rdV, base, tile, t, G, tiles, qb, oq, I, R, wo, wi, l, num, den);
-    if ((t += G) >= tiles) break;
+    if constexpr (KT % 4 != 0) {
+      tile_pass<EO, kErr, KT, KT % 4>(d, rdU, rdV, base, tile, t, G, tiles, q, I, R, wo, wi, l, num, den);
+      if ((t += G) >= tiles) break;
+    }
   }
   wait_vm<0>();  // no load into LDS may still be in flight when the workgroup ends
   if constexpr (kErr) {
-    __syncthreads();  // the ring is free: its first 4 KB hold the reduction
+    __syncthreads();  // the ring is free: its first 4 KB hold the reduction, then the arrival verdict
     double* sa = reinterpret_cast<double*>(ring);
     double* sb = sa + kThreads;
     reduce::block_reduce2<kThreads>(num, den, sa, sb);
-    reduce::finish_ratio<kThreads>(num, den, partial, counters, result, sa, sb);
+    reduce::finish_ratio<kThreads>(num, den, partial, counters, result, sa, sb, *reinterpret_cast<unsigned*>(sb + kThreads));
   }
 }
 
@@ -528,16 +525,19 @@ template <typename EO, bool kErr>
 hipError_t launch(const void* s, const void* w0, const void* u, const void* v, EO* out, int64_t O, int64_t I,
                   int64_t R, int grid, int tiles_i, int tiles, uint64_t* partial, unsigned* counters, double* result,
                   hipStream_t stream) {
-  const int kt = int((R + BK - 1) / BK);
 #define TB_RP_LAUNCH(K)                                                                                              \
   hipLaunchKernelGGL((reconstruct_persistent_kernel<EO, kErr, K>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, \
                      static_cast<const bf16_t*>(s), static_cast<const bf16_t*>(w0), static_cast<const bf16_t*>(u),  \
                      static_cast<const bf16_t*>(v), out, int(O), int(I), int(R), tiles_i, tiles, partial, counters, \
                      result)
-  if (kt == 1) TB_RP_LAUNCH(1);
-  else if (kt == 2) TB_RP_LAUNCH(2);
-  else if (kt == 3) TB_RP_LAUNCH(3);
-  else TB_RP_LAUNCH(4);
+  // The error variant takes at least four k-tiles: its two-k-tile form,
+  // two tiles per loop round, would spill.
+  const int kt = ktiles(R) < 4 && kErr ? 4 : ktiles(R);
+  switch (kt) {
+    case 2: if constexpr (!kErr) TB_RP_LAUNCH(2); break;
+    case 4: TB_RP_LAUNCH(4); break;
+    default: TB_RP_LAUNCH(8); break;
+  }
 #undef TB_RP_LAUNCH
   return hipGetLastError();
 }
@@ -547,7 +547,7 @@ hipError_t launch(const void* s, const void* w0, const void* u, const void* v, E
 // The persistent kernel: bf16 bundles, 0 < rank <= 256 with rank % 8 == 0,
 // and 32-bit lane offsets within a 128-row band of the output.
 bool persistent_supported(int64_t O, int64_t I, int64_t R) {
-  return R > 0 && R % 8 == 0 && R <= 4 * rp::BK && I < (1 << 22) && O < (1 << 24);
+  return R > 0 && R % 8 == 0 && R <= 8 * rp::BK && I < (1 << 22) && O < (1 << 24);
 }
 
 template <typename EI, typename EO>
@@ -563,7 +563,7 @@ hipError_t launch_typed(const void* s, const void* w0, const void* u, const void
     int cus = 0;
     if (int e = device_cu_count(&cus)) return hipError_t(e);
     const int tiles_i = int((I + rp::BT - 1) / rp::BT), tiles = tiles_i * int((O + rp::BT - 1) / rp::BT);
-    return rp::launch<EO, false>(s, w0, u, v, static_cast<EO*>(w_out), O, I, R, tiles < cus ? tiles : cus, tiles_i,
+    return rp::launch<EO, false>(s, w0, u, v, static_cast<EO*>(w_out), O, I, R, tiles < 2 * cus ? tiles : 2 * cus, tiles_i,
                                  tiles, nullptr, nullptr, nullptr, stream);
   } else if (sizeof(EI) == 2 && R % 8 == 0 && (O + rebuild::t128::BT - 1) / rebuild::t128::BT <= 65535) {
     dim3 grid(unsigned((I + rebuild::t128::BT - 1) / rebuild::t128::BT), unsigned((O + rebuild::t128::BT - 1) / rebuild::t128::BT));
@@ -589,7 +589,7 @@ hipError_t launch_reconstruction_error_persistent(const void* s, const void* w0,
                                                   const float* orig, int64_t O, int64_t I, int64_t R, double* result,
                                                   void* workspace, int cus, hipStream_t stream) {
   const int tiles_i = int((I + rp::BT - 1) / rp::BT), tiles = tiles_i * int((O + rp::BT - 1) / rp::BT);
-  int grid = tiles < cus ? tiles : cus;
+  int grid = tiles < 2 * cus ? tiles : 2 * cus;
   if (grid > reduce::kMaxPartials) grid = reduce::kMaxPartials;
   return rp::launch<float, true>(s, w0, u, v, const_cast<float*>(orig), O, I, R, grid, tiles_i, tiles,
                                  reduce::partials(workspace), reduce::counters(workspace), result, stream);

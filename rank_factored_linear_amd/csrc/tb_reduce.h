@@ -60,11 +60,10 @@ __host__ __device__ inline unsigned* counters(void* workspace) {
 
 // Publishes this workgroup's (num, den) and, in the last workgroup to arrive,
 // writes the ratio.  Every thread of the workgroup calls it with the same
-// (already reduced) values.
+// (already reduced) values.  s_last: one word of LDS for the arrival verdict.
 template <int NT>
 __device__ void finish_ratio(double num, double den, uint64_t* __restrict__ partial, unsigned* __restrict__ counters,
-                             double* __restrict__ result, double* sa, double* sb) {
-  __shared__ unsigned s_last;
+                             double* __restrict__ result, double* sa, double* sb, unsigned& s_last) {
   if (threadIdx.x == 0) {
     store_coherent64(&partial[2 * blockIdx.x], __double_as_longlong(num));
     store_coherent64(&partial[2 * blockIdx.x + 1], __double_as_longlong(den));
@@ -98,6 +97,13 @@ __device__ void finish_ratio(double num, double den, uint64_t* __restrict__ part
     else r = sqrt(n) / sqrt(d);
     *result = r;
   }
+}
+
+template <int NT>
+__device__ void finish_ratio(double num, double den, uint64_t* __restrict__ partial, unsigned* __restrict__ counters,
+                             double* __restrict__ result, double* sa, double* sb) {
+  __shared__ unsigned s_last;
+  finish_ratio<NT>(num, den, partial, counters, result, sa, sb, s_last);
 }
 
 }  // namespace reduce
