@@ -266,10 +266,12 @@ __device__ __forceinline__ void issue(const Dma& d, const Tile& g, int kt, bool 
 
 // Epilogue layout: in round cb (0, 1) lane l of wave w handles output row
 // 64 (w / 2) + 32 cb + 4 p + l / 16 (p = 0..7) and columns 64 (w % 2) + 4 (l % 16) .. +3
-// of the tile.
+// of the tile.  The W0 values are held in that layout; of s, lane l holds
+// row 64 (w / 2) + 32 cb + l % 32 and the epilogue fetches the row it needs
+// from that lane.
 struct Pre {
   u32x2 w[2][8];
-  uint32_t s[2][8];
+  uint32_t s[2];
 };
 
 template <typename EO>
@@ -278,17 +280,31 @@ __device__ __forceinline__ int out_off(const Tile& g, int I, int wo, int wi, int
   return (orel < g.orows && i < I) ? (orel * I + i) * int(sizeof(EO)) : kPast;
 }
 
+// 18 loads: 2 of s, 16 of W0.
 __device__ __forceinline__ void prefetch(Pre& q, const Tile& g, bool dummy, int I, int wo, int wi, int l) {
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
+  for (int cb = 0; cb < 2; ++cb) {
+    const int srow = wo * 64 + cb * 32 + (l & 31);
+    q.s[cb] = __builtin_amdgcn_raw_buffer_load_b16(g.rs, (!dummy && srow < g.orows) ? srow * 2 : kPast, 0, 0);
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const int orel = wo * 64 + cb * 32 + 4 * p + (l >> 4), i = g.i0 + wi * 64 + (l & 15) * 4;
       const bool ok = !dummy && orel < g.orows && i < I;
       q.w[cb][p] = __builtin_amdgcn_raw_buffer_load_b64(g.rw, ok ? (orel * I + i) * 2 : kPast, 0, 0);
-      q.s[cb][p] = __builtin_amdgcn_raw_buffer_load_b16(g.rs, (!dummy && orel < g.orows) ? orel * 2 : kPast, 0, 0);
       __builtin_amdgcn_sched_barrier(0);  // issue in order of use
     }
+  }
+}
+
+// s of epilogue row 4 p + l / 16 of round cb, from the lane that holds it.
+__device__ __forceinline__ float row_scale(const Pre& q, int cb, int p, int l) {
+  return bf16_to_f32(uint16_t(__builtin_amdgcn_ds_bpermute((4 * p + (l >> 4)) << 2, int(q.s[cb]))));
+}
+
+// The four outputs of one epilogue position: product + s W0.
+__device__ __forceinline__ f32x4 add_scaled(f32x4 c, u32x2 wv, float so) {
+  return f32x4{c[0] + so * bf16_to_f32(uint16_t(wv[0])), c[1] + so * bf16_to_f32(uint16_t(wv[0] >> 16)),
+               c[2] + so * bf16_to_f32(uint16_t(wv[1])), c[3] + so * bf16_to_f32(uint16_t(wv[1] >> 16))};
 }
 
 // Measuring the error against an fp32 original: the original's values of
@@ -335,19 +351,24 @@ __device__ __forceinline__ void multiply_step(lds_byte* const (&rdU)[2], lds_byt
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Four outputs in the stored form: fp32, or bf16 pairs packed into words.
+template <typename EO> struct Packed { typedef u32x4 type; };
+template <> struct Packed<bf16_t> { typedef u32x2 type; };
+
 template <typename EO>
-__device__ __forceinline__ void store_out(const Tile& g, int off, f32x4 c, u32x2 wv, float so) {
-  const float r0 = c[0] + so * bf16_to_f32(uint16_t(wv[0])), r1 = c[1] + so * bf16_to_f32(uint16_t(wv[0] >> 16));
-  const float r2 = c[2] + so * bf16_to_f32(uint16_t(wv[1])), r3 = c[3] + so * bf16_to_f32(uint16_t(wv[1] >> 16));
+__device__ __forceinline__ typename Packed<EO>::type pack_out(f32x4 r) {
   if constexpr (sizeof(EO) == 4) {
-    __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(r0), __float_as_uint(r1), __float_as_uint(r2),
-                                                 __float_as_uint(r3)},
-                                           g.ro, off, 0, kNT);
+    return u32x4{__float_as_uint(r[0]), __float_as_uint(r[1]), __float_as_uint(r[2]), __float_as_uint(r[3])};
   } else {
-    __builtin_amdgcn_raw_buffer_store_b64(u32x2{f32_to_bf16(r0) | (uint32_t(f32_to_bf16(r1)) << 16),
-                                                f32_to_bf16(r2) | (uint32_t(f32_to_bf16(r3)) << 16)},
-                                          g.ro, off, 0, kNT);
+    return u32x2{f32_to_bf16(r[0]) | (uint32_t(f32_to_bf16(r[1])) << 16),
+                 f32_to_bf16(r[2]) | (uint32_t(f32_to_bf16(r[3])) << 16)};
   }
+}
+
+template <typename EO>
+__device__ __forceinline__ void store_out(const Tile& g, int off, typename Packed<EO>::type v) {
+  if constexpr (sizeof(EO) == 4) __builtin_amdgcn_raw_buffer_store_b128(v, g.ro, off, 0, kNT);
+  else __builtin_amdgcn_raw_buffer_store_b64(v, g.ro, off, 0, kNT);
 }
 
 // The k-tiles of all of a workgroup's output tiles form one stream: k-tile
@@ -356,24 +377,27 @@ __device__ __forceinline__ void store_out(const Tile& g, int off, f32x4 c, u32x2
 // wave, refills the slot every wave has just finished with (entry j + 3)
 // and multiplies.  After a tile's last step its epilogue goes through the
 // slot that step read (kErr: with 8 loads of the original in each of its two
-// rounds), then issues the W0 and s loads of the next tile, 32; the stores of
-// the epilogue are 16 more (none when kErr).  Every load and
-// store is issued unconditionally, so the count of memory instructions
-// issued after entry j when step j waits is a constant: the refills of the
-// two steps between (4 each) plus 48 for each tile end among the three steps
-// before j.  vmcnt counts up to 63, so 63 stands for any larger count.  (The
-// prologue waits for all of its loads, so entries 0..2 have landed.)
+// rounds) and forms the tile's outputs in registers; then it issues the W0
+// and s loads of the next tile (18) and only then the 16 stores (none when
+// kErr).  Memory instructions complete in issue order, so a wait for the
+// next tile's W0 does not wait for this tile's non-temporal stores to leave.
+// Every load and store is issued unconditionally, so the count of memory
+// instructions issued after entry j when step j waits is a constant: the
+// refills of the two steps between (4 each) plus 34 for each tile end among
+// the three steps before j.  vmcnt counts up to 63, so 63 stands for any
+// larger count.  (The prologue waits for all of its loads, so entries 0..2
+// have landed.)
 template <int KT>
 __host__ __device__ constexpr int step_wait(int k) {
   int ends = 0;
   for (int r = k - 3; r < k; ++r)
     if ((((r + 1) % KT) + KT) % KT == 0) ++ends;
-  const int n = 8 + 48 * ends;
+  const int n = 8 + 34 * ends;
   return n < 63 ? n : 63;
 }
-static_assert(step_wait<8>(0) == 56 && step_wait<8>(3) == 8 && step_wait<8>(7) == 8, "eight k-tiles per tile");
-static_assert(step_wait<4>(0) == 56 && step_wait<4>(3) == 8, "four k-tiles per tile");
-static_assert(step_wait<2>(1) == 56 && step_wait<2>(0) == 63, "two tile ends among three steps");
+static_assert(step_wait<8>(0) == 42 && step_wait<8>(3) == 8 && step_wait<8>(7) == 8, "eight k-tiles per tile");
+static_assert(step_wait<4>(0) == 42 && step_wait<4>(3) == 8, "four k-tiles per tile");
+static_assert(step_wait<2>(1) == 42 && step_wait<2>(0) == 63, "two tile ends among three steps");
 
 template <int V> struct IC { static constexpr int value = V; };
 
@@ -408,6 +432,7 @@ __device__ __forceinline__ void tile_pass(const Dma& d, lds_byte* const (&rdU)[2
 
   lds_byte* stage = w < 2 ? base + ((J0 + KT - 1) % kSlots) * kSlotBytes + w * kWaveStage
                           : base + kRingBytes + (w - 2) * kWaveStage;
+  typename Packed<EO>::type res[2][8];  // the rebuilt tile in the epilogue layout (kErr: unused)
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     u32x4 o[8];
@@ -431,12 +456,9 @@ __device__ __forceinline__ void tile_pass(const Dma& d, lds_byte* const (&rdU)[2
     }
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
+      // Entries outside the matrix: the original, W0 and s read as zero and the product is zero.
+      const f32x4 wr = add_scaled(c[p], q.w[cb][p], row_scale(q, cb, p, l));
       if constexpr (kErr) {
-        // Entries outside the matrix: the original, W0 and s read as zero and the product is zero.
-        const u32x2 wv = q.w[cb][p];
-        const float so = bf16_to_f32(uint16_t(q.s[cb][p]));
-        const float wr[4] = {c[p][0] + so * bf16_to_f32(uint16_t(wv[0])), c[p][1] + so * bf16_to_f32(uint16_t(wv[0] >> 16)),
-                             c[p][2] + so * bf16_to_f32(uint16_t(wv[1])), c[p][3] + so * bf16_to_f32(uint16_t(wv[1] >> 16))};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const double ov = double(__uint_as_float(o[p][e])), dd = ov - double(wr[e]);
@@ -444,11 +466,17 @@ __device__ __forceinline__ void tile_pass(const Dma& d, lds_byte* const (&rdU)[2
           den += ov * ov;
         }
       } else {
-        store_out<EO>(g, out_off<EO>(g, I, wo, wi, cb, p, l), c[p], q.w[cb][p], bf16_to_f32(uint16_t(q.s[cb][p])));
+        res[cb][p] = pack_out<EO>(wr);
       }
     }
   }
   prefetch(q, tile(t + G), t + G >= tiles, I, wo, wi, l);
+  if constexpr (!kErr) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int p = 0; p < 8; ++p) store_out<EO>(g, out_off<EO>(g, I, wo, wi, cb, p, l), res[cb][p]);
+  }
 }
 
 // kErr = false: out receives the rebuilt weight.  kErr = true: out is the
