@@ -761,12 +761,14 @@ def bench_reconstruct(args, torch, np, tb, gen):
                  **spread(g_per), "gpu": clocks}
 
     kernels = {}
-    kt = (R + 63) // 64
+    # The persistent kernel's k-tiles of 32 per tile: 2, 4 or 8 (its error variant at least 4).
+    k32 = (R + 31) // 32
+    kt = 2 if k32 <= 2 else 4 if k32 <= 4 else 8
     rec_kernel = ("reconstruct_rank0_kernel" if R == 0 else
                   f"rp::reconstruct_persistent_kernel<float, false, {kt}>" if R <= 256 and R % 8 == 0 else
                   "mm::reconstruct_mfma_kernel" if R % 8 == 0 else "reconstruct_lowrank_kernel")
     fused_kernel = ("rerr_rank0_kernel" if R == 0 else
-                    f"rp::reconstruct_persistent_kernel<float, true, {kt}>" if R <= 256 and R % 8 == 0 else
+                    f"rp::reconstruct_persistent_kernel<float, true, {max(kt, 4)}>" if R <= 256 and R % 8 == 0 else
                     "rerr_t128_kernel" if R % 8 == 0 else "rerr_t64_kernel")
     kinds = (("fused", fused_kernel),) if fused else (("reconstruct", rec_kernel), ("frobenius", "frob_kernel"))
     for kind, name in kinds:
