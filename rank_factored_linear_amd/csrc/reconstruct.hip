@@ -8,11 +8,12 @@
 // epilogue; at rank 256 it is still HBM-bound (6 bytes of W0 and fp32 output
 // per 512 flops) but needs far more than the fp32 vector rate to keep up.
 //
-// bf16 bundles with rank % 8 == 0 take reconstruct_mfma_kernel: 128 x 128
-// output tiles, k-tiles of 64 staged in LDS (16-byte chunks XOR-swizzled by
-// row), four waves of 64 x 64 on v_mfma_f32_32x32x16_bf16.  The product is
-// taken as V . U^T, so that each lane ends up holding four consecutive
-// columns of one output row: 8-byte W0 loads and 16-byte fp32 stores.
+// bf16 bundles with rank % 8 == 0 take 128 x 128 output tiles on
+// v_mfma_f32_32x32x16_bf16, four waves of 64 x 64: up to rank 256 the
+// persistent kernel below (rp), beyond it reconstruct_mfma_kernel (one tile
+// per workgroup, k-tiles of 64 staged in LDS with 16-byte chunks XOR-swizzled
+// by row).  The product is taken as V . U^T, so that each lane ends up
+// holding four consecutive columns of one output row.
 #include "tb_device.h"
 #include "tb_host.h"
 #include "tb_rebuild.h"
@@ -143,7 +144,8 @@ __global__ __launch_bounds__(kThreads, 2) void reconstruct_mfma_kernel(const bf1
 // slot) by direct-to-LDS buffer loads; each slot is refilled, three k-tiles
 // ahead and across tile boundaries, as soon as every wave has read it.  The
 // W0 and s values of the next tile are loaded into registers at the end of a
-// tile's epilogue and so have its whole k-loop to arrive.  The epilogue moves
+// tile's epilogue, ahead of its stores, and so have the whole next k-loop to
+// arrive.  The epilogue moves
 // each wave's 64 x 64 accumulators through LDS (the slot of the last k-tile
 // for waves 0 and 1, a 16 KB staging area for waves 2 and 3) so that 16 lanes
 // cover 64 consecutive outputs of one row: 128-byte W0 reads and 256-byte
