@@ -148,6 +148,20 @@ def frobenius_bytes(O, I, e=4):
     return 2 * e * O * I
 
 
+def reconstruct_kernel_names(R):
+    """The kernels that rebuild a bf16 bundle of rank R into fp32, and that measure its error without rebuilding.
+    The persistent kernel takes k-tiles of 32 per tile, 2, 4 or 8 of them (its error variant at least 4)."""
+    k32 = (R + 31) // 32
+    kt = 2 if k32 <= 2 else 4 if k32 <= 4 else 8
+    rec = ("reconstruct_rank0_kernel" if R == 0 else
+           f"rp::reconstruct_persistent_kernel<float, false, {kt}>" if R <= 256 and R % 8 == 0 else
+           "mm::reconstruct_mfma_kernel" if R % 8 == 0 else "reconstruct_lowrank_kernel")
+    fused = ("rerr_rank0_kernel" if R == 0 else
+             f"rp::reconstruct_persistent_kernel<float, true, {max(kt, 4)}>" if R <= 256 and R % 8 == 0 else
+             "rerr_t128_kernel" if R % 8 == 0 else "rerr_t64_kernel")
+    return rec, fused
+
+
 def fused_error_bytes(O, I, R, e_in=2, e_orig=4):
     """Error without the rebuilt weight: s, W0, U, V and the original read once."""
     return e_in * (O * I + R * (O + I) + O) + e_orig * O * I
@@ -761,15 +775,7 @@ def bench_reconstruct(args, torch, np, tb, gen):
                  **spread(g_per), "gpu": clocks}
 
     kernels = {}
-    # The persistent kernel's k-tiles of 32 per tile: 2, 4 or 8 (its error variant at least 4).
-    k32 = (R + 31) // 32
-    kt = 2 if k32 <= 2 else 4 if k32 <= 4 else 8
-    rec_kernel = ("reconstruct_rank0_kernel" if R == 0 else
-                  f"rp::reconstruct_persistent_kernel<float, false, {kt}>" if R <= 256 and R % 8 == 0 else
-                  "mm::reconstruct_mfma_kernel" if R % 8 == 0 else "reconstruct_lowrank_kernel")
-    fused_kernel = ("rerr_rank0_kernel" if R == 0 else
-                    f"rp::reconstruct_persistent_kernel<float, true, {max(kt, 4)}>" if R <= 256 and R % 8 == 0 else
-                    "rerr_t128_kernel" if R % 8 == 0 else "rerr_t64_kernel")
+    rec_kernel, fused_kernel = reconstruct_kernel_names(R)
     kinds = (("fused", fused_kernel),) if fused else (("reconstruct", rec_kernel), ("frobenius", "frob_kernel"))
     for kind, name in kinds:
         sel = np.array([c[0] == kind for c in calls])

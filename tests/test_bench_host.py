@@ -68,3 +68,21 @@ def test_decompose_workloads_are_declared():
     for name in ("decompose26", "decompose60"):
         wl = bench.WORKLOADS[name]
         assert wl["rank"] > 0 and 1 <= wl["bands"] <= wl["layers"]
+
+
+def test_reconstruct_kernel_names_follow_the_k_tiles_of_32():
+    assert bench.reconstruct_kernel_names(256) == ("rp::reconstruct_persistent_kernel<float, false, 8>",
+                                                  "rp::reconstruct_persistent_kernel<float, true, 8>")
+    assert bench.reconstruct_kernel_names(128) == ("rp::reconstruct_persistent_kernel<float, false, 4>",
+                                                  "rp::reconstruct_persistent_kernel<float, true, 4>")
+    assert bench.reconstruct_kernel_names(64) == ("rp::reconstruct_persistent_kernel<float, false, 2>",
+                                                 "rp::reconstruct_persistent_kernel<float, true, 4>")
+    assert bench.reconstruct_kernel_names(0) == ("reconstruct_rank0_kernel", "rerr_rank0_kernel")
+    assert bench.reconstruct_kernel_names(264) == ("mm::reconstruct_mfma_kernel", "rerr_t128_kernel")
+    assert bench.reconstruct_kernel_names(12) == ("reconstruct_lowrank_kernel", "rerr_t64_kernel")
+
+
+def test_committed_rebuild_traffic_names_the_benched_kernel():
+    # The rebuild's HBM record is looked up by kernel name: it must name the kernel bench.py reports.
+    rec = json.load(open(os.path.join(ROOT, "profiles", "hbm_traffic.json"))).get("reconstruct60_R256_G6")
+    assert rec is not None and rec["kernel"] == bench.reconstruct_kernel_names(256)[0]
