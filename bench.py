@@ -381,7 +381,7 @@ def bench_forward(args, torch, np, tb, gen):
     # families): W = diag(s) W0 + U V^T per layer, rebuilt once in bf16; each
     # such call is a dense projection (no scale, rank 0).
     dense_fams = set(gen.FAMILIES) if args.materialised else (
-        {"gate_proj", "up_proj", "down_proj"} if args.tie_families == "attn" else set())
+        set(tb.MLP_FAMILIES) if args.tie_families == "attn" else set())
     dense = None
     if dense_fams:
         dense = {}

@@ -21,6 +21,9 @@ from .theta_bundle import (  # noqa: F401
     orthonormal_basis,
     randomized_factors,
     decompose,
+    ATTENTION_FAMILIES,
+    MLP_FAMILIES,
+    decompose_model,
     refine_shared_block,
     als_decompose,
     decomposition_error,

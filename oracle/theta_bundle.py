@@ -311,6 +311,41 @@ def decompose(weights, num_bands: int, rank: int) -> dict:
     return out
 
 
+# The seven projection families of a decoder layer ("The theta bundle",
+# section "Projection families"): four attention projections, three MLP.
+ATTENTION_FAMILIES = ("q_proj", "k_proj", "v_proj", "o_proj")
+MLP_FAMILIES = ("gate_proj", "up_proj", "down_proj")
+
+
+def decompose_model(weights_by_family: dict, num_bands: int, rank: int, tie_families: str = "all") -> dict:
+    """Theta bundles for the projection families of a model ("The theta
+    bundle", section "Projection families").
+
+    weights_by_family maps a family name to its per-layer weights.  With
+    tie_families="all" every family is decomposed (decompose, per family).
+    With tie_families="attn" only the attention families are; the MLP
+    families stay plain dense layers holding their own weights.  Reading (the
+    page gives no bundle for them): a dense layer is written as the bundle in
+    which each layer is its own band (W0 = its weight), s = 1 and rank 0, so
+    that reconstruct_weight gives the weight back exactly.
+    """
+    if tie_families not in ("all", "attn"):
+        raise ValueError(f"tie_families must be 'all' or 'attn', not {tie_families!r}")
+    out = {}
+    for fam, weights in weights_by_family.items():
+        if fam not in ATTENTION_FAMILIES + MLP_FAMILIES:
+            raise ValueError(f"unknown projection family {fam!r}")
+        if tie_families == "attn" and fam in MLP_FAMILIES:
+            ws = [np.asarray(w, dtype=np.float64) for w in weights]
+            out[fam] = {"W0": ws, "band": list(range(len(ws))),
+                        "s": [np.ones(w.shape[0]) for w in ws],
+                        "U": [np.zeros((w.shape[0], 0)) for w in ws],
+                        "V": [np.zeros((w.shape[1], 0)) for w in ws]}
+        else:
+            out[fam] = decompose(weights, num_bands, rank)
+    return out
+
+
 def refine_shared_block(weights, s_list, U_list, V_list, W0_prev: np.ndarray) -> np.ndarray:
     """One least-squares update of a band's shared block with the per-layer
     scale and delta held fixed: the alternating least squares the "Quality"

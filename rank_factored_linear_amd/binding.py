@@ -603,3 +603,33 @@ def als_decompose(weights, num_bands: int, rank: int, iters: int, oversampling: 
             bun["V"] = [V[l] for l in range(L)]
     return bun
 
+
+
+# The seven projection families of a decoder layer ("The theta bundle", section "Projection families").
+ATTENTION_FAMILIES = ("q_proj", "k_proj", "v_proj", "o_proj")
+MLP_FAMILIES = ("gate_proj", "up_proj", "down_proj")
+
+
+def decompose_model(weights_by_family: dict, num_bands: int, rank: int, tie_families: str = "all",
+                    oversampling: int = 16, power_iters: int = 2, seed: int = 0) -> dict:
+    """Theta bundles for the projection families of a model ("The theta bundle", section "Projection families").
+
+    weights_by_family maps a family name to its per-layer weights.  tie_families="all": every family goes through
+    decompose() (family j of the dict order uses seed + j).  tie_families="attn": only q/k/v/o do; each MLP layer
+    stays a plain dense layer, returned as the bundle whose W0 is the layer's own weight (the caller's tensor, not a
+    copy; every layer its own band), with s = None (unit scale) and U = V = None, which linear_forward,
+    linear_forward_group and dense_forward take as they are."""
+    if tie_families not in ("all", "attn"):
+        raise TBError(TB_ERR_INVALID_ARGUMENT, f"tie_families must be 'all' or 'attn', not {tie_families!r}")
+    for fam in weights_by_family:
+        if fam not in ATTENTION_FAMILIES + MLP_FAMILIES:
+            raise TBError(TB_ERR_INVALID_ARGUMENT, f"unknown projection family {fam!r}")
+    out = {}
+    for j, (fam, weights) in enumerate(weights_by_family.items()):
+        if tie_families == "attn" and fam in MLP_FAMILIES:
+            L = len(weights)
+            out[fam] = {"W0": list(weights), "band": list(range(L)), "s": [None] * L, "U": [None] * L,
+                        "V": [None] * L}
+        else:
+            out[fam] = decompose(weights, num_bands, rank, oversampling, power_iters, seed + j)
+    return out

@@ -118,3 +118,21 @@ def test_decomposition_wrappers_reject_mis_sized_operands():
     U, V = torch.zeros(16, 4), torch.zeros(32, 4)
     _raises(lambda: tb.refine_shared_block([w], [torch.zeros(16)], [U], [torch.zeros(32, 5)], w), "V[0]")
     _raises(lambda: tb.refine_shared_block([w], [torch.zeros(16)], [U], [V], w, out=torch.zeros(16, 31)), "out")
+
+
+def test_decompose_model_rejects_bad_arguments():
+    ws = [torch.zeros(16, 32, dtype=BF) for _ in range(2)]
+    _raises(lambda: tb.decompose_model({"q_proj": ws}, 1, 0, tie_families="mlp"), "tie_families")
+    _raises(lambda: tb.decompose_model({"q_proj": ws}, 1, 0, tie_families=""), "tie_families")
+    _raises(lambda: tb.decompose_model({"lm_head": ws}, 1, 0), "lm_head")
+
+
+def test_decompose_model_keeps_the_mlp_dense_without_a_launch():
+    # tie_families="attn" with MLP families only: nothing is decomposed, so
+    # this runs on host tensors; each layer's bundle is its own weight.
+    ws = {f: [torch.zeros(16, 32, dtype=BF) for _ in range(3)] for f in tb.MLP_FAMILIES}
+    got = tb.decompose_model(ws, 1, 8, tie_families="attn")
+    for f in tb.MLP_FAMILIES:
+        assert got[f]["band"] == [0, 1, 2]
+        assert all(a is b for a, b in zip(got[f]["W0"], ws[f]))
+        assert got[f]["s"] == [None] * 3 and got[f]["U"] == [None] * 3 and got[f]["V"] == [None] * 3

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 from rank_factored_linear_amd import inputs as gen
-from parity_util import exact, f32_to_device
+from parity_util import check_forward, exact, f32_to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -263,3 +263,42 @@ def test_als_tiny_stack_matches_the_oracle():
         e_orc = oracle.relative_frobenius_error(weights[l], oracle.reconstruct_weight(
             want["s"][l], want["W0"][band], want["U"][l], want["V"][l]))
         assert abs(e_gpu - e_orc) <= 1e-4 * e_orc, (l, e_gpu, e_orc)
+
+
+@pytest.mark.parametrize("tie", ["all", "attn"])
+def test_decompose_model_tie_families(tie):
+    # A 4-layer model with all seven families ("The theta bundle", Projection
+    # families).  Families that share go through decompose() with the seed it
+    # is given; under tie_families="attn" the MLP layers stay dense and their
+    # forward is x . W^T against the oracle.
+    r = np.random.default_rng(3)
+    L, G, rank = 4, 2, 8
+    shapes = {"q_proj": (96, 64), "k_proj": (32, 64), "v_proj": (32, 64), "o_proj": (64, 96),
+              "gate_proj": (160, 64), "up_proj": (160, 64), "down_proj": (64, 160)}
+    model = {}
+    for fam, (O, I) in shapes.items():
+        B = r.normal(0.0, 0.02, (O, I))
+        model[fam] = [torch.from_numpy((r.uniform(0.9, 1.1) * B + r.normal(0.0, 1e-3, (O, I))).astype(np.float32))
+                      .to(torch.bfloat16).to(DEV) for _ in range(L)]
+    got = tb.decompose_model(model, G, rank, tie_families=tie, seed=5)
+    want = oracle.decompose_model({f: [exact(w) for w in ws] for f, ws in model.items()}, G, 0, tie_families=tie)
+    x = torch.from_numpy(r.normal(size=(8, 160)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    for j, (fam, ws) in enumerate(model.items()):
+        bun = got[fam]
+        if tie == "attn" and fam in tb.MLP_FAMILIES:
+            assert bun["band"] == list(range(L))
+            for l in range(L):
+                assert bun["W0"][l] is ws[l] and bun["s"][l] is None and bun["U"][l] is None
+                xi = x[:, : ws[l].shape[1]].contiguous()
+                y = tb.linear_forward(xi, None, bun["W0"][l], None, None)
+                wb = want[fam]
+                check_forward(exact(y), exact(xi), wb["s"][l], wb["W0"][l], wb["U"][l], wb["V"][l], True,
+                              f"{fam} layer {l}")
+            continue
+        again = tb.decompose(ws, G, rank, seed=5 + j)       # the same call, deterministic kernels
+        for l in range(L):
+            band = bun["band"][l]
+            assert band == want[fam]["band"][l]
+            assert np.array_equal(bun["W0"][band].cpu().numpy(), want[fam]["W0"][band].astype(np.float32))
+            for k in ("s", "U", "V"):
+                assert torch.equal(bun[k][l], again[k][l]), (fam, l, k)

@@ -309,9 +309,62 @@ def check_decompose(impl) -> None:
     assert max(impl.decomposition_error([c * B for c in cs], bun)) <= 1e-14
 
 
+def check_decompose_model(impl) -> None:
+    # "The theta bundle", Projection families: with tie_families="attn" only
+    # q/k/v/o share a block; the MLP stays dense.  Attention families are
+    # pure-scale bands W_l = c_l B (closed form at rank 0: W0 = mean(c) B,
+    # s_l = c_l / mean(c)); MLP families are unstructured.
+    r = np.random.default_rng(11)
+    L, G = 4, 2
+    shapes = {"q_proj": (6, 8), "k_proj": (4, 8), "v_proj": (4, 8), "o_proj": (8, 6),
+              "gate_proj": (10, 8), "up_proj": (10, 8), "down_proj": (8, 10)}
+    cs = [0.8, 1.2, 0.9, 1.1]
+    model = {}
+    for fam, (O, I) in shapes.items():
+        if fam in ("q_proj", "k_proj", "v_proj", "o_proj"):
+            B = r.normal(size=(O, I))
+            model[fam] = [c * B for c in cs]
+        else:
+            model[fam] = [r.normal(size=(O, I)) for _ in range(L)]
+    bands = [b for b, p in enumerate(np.array_split(np.arange(L), G)) for _ in p]
+    x = r.normal(size=(3, 10))
+    for tie in ("all", "attn"):
+        got = impl.decompose_model(model, G, 0, tie_families=tie)
+        assert sorted(got) == sorted(shapes), tie
+        for fam, ws in model.items():
+            bun = got[fam]
+            dense = tie == "attn" and fam in ("gate_proj", "up_proj", "down_proj")
+            for l, w in enumerate(ws):
+                rebuilt = impl.reconstruct_weight(bun["s"][l], bun["W0"][bun["band"][l]], bun["U"][l], bun["V"][l])
+                if dense:
+                    # A plain dense layer: its own weight, unscaled, no delta.
+                    assert bun["band"][l] == l and bun["U"][l].shape[1] == 0
+                    assert np.array_equal(rebuilt, w), (tie, fam, l)
+                    xi = x[:, : w.shape[1]]
+                    assert np.array_equal(impl.forward(xi, bun["s"][l], bun["W0"][l], bun["U"][l], bun["V"][l]),
+                                          xi @ w.T), (tie, fam, l)
+                    continue
+                members = [j for j in range(L) if bands[j] == bands[l]]
+                assert bun["band"][l] == bands[l], (tie, fam, l)
+                assert np.allclose(bun["W0"][bands[l]], np.mean([ws[j] for j in members], axis=0),
+                                   rtol=1e-14, atol=1e-15), (tie, fam, l)
+                if fam in ("q_proj", "k_proj", "v_proj", "o_proj"):
+                    mc = np.mean([cs[j] for j in members])
+                    assert np.allclose(bun["s"][l], cs[l] / mc, rtol=1e-13, atol=0), (tie, fam, l)
+                    assert np.max(np.abs(rebuilt - w)) <= 1e-13 * np.max(np.abs(w)), (tie, fam, l)
+                else:
+                    # A shared block of unstructured layers cannot be exact at rank 0.
+                    assert impl.relative_frobenius_error(w, rebuilt) > 0.1, (tie, fam, l)
+    for bad in ("mlp", "none", ""):
+        with pytest.raises(ValueError):
+            impl.decompose_model(model, G, 0, tie_families=bad)
+    with pytest.raises(ValueError):
+        impl.decompose_model({"lm_head": model["q_proj"]}, G, 0)
+
+
 ALL_CHECKS = [check_band_map, check_forward, check_reconstruct, check_frobenius,
               check_row_scale, check_truncated_factors, check_randomized_factors, check_refine_shared_block,
-              check_als_decompose, check_decompose]
+              check_als_decompose, check_decompose, check_decompose_model]
 
 
 # ---------------------------------------------------------------------------
@@ -576,7 +629,28 @@ def _als(**plant):
     return lambda weights, num_bands, rank, iters: _als_variant(weights, num_bands, rank, iters, **plant)
 
 
+def _model_ties_everything(weights_by_family, num_bands, rank, tie_families="all"):
+    if tie_families not in ("all", "attn"):
+        raise ValueError(tie_families)
+    return tb.decompose_model(weights_by_family, num_bands, rank, "all")
+
+
+def _model_ties_the_mlp(weights_by_family, num_bands, rank, tie_families="all"):
+    if tie_families not in ("all", "attn"):
+        raise ValueError(tie_families)
+    if tie_families == "all":
+        return tb.decompose_model(weights_by_family, num_bands, rank, "all")
+    swapped = {("gate_proj" if f == "q_proj" else "q_proj" if f == "gate_proj" else f): w
+               for f, w in weights_by_family.items()}
+    got = tb.decompose_model(swapped, num_bands, rank, "attn")
+    return {("gate_proj" if f == "q_proj" else "q_proj" if f == "gate_proj" else f): b for f, b in got.items()}
+
+
 MUTANTS = [
+    ("tie_families='attn' decomposes the MLP too", check_decompose_model,
+     dict(decompose_model=_model_ties_everything)),
+    ("tie_families='attn' keeps q dense and shares gate", check_decompose_model,
+     dict(decompose_model=_model_ties_the_mlp)),
     ("ALS: s refit against the previous block", check_als_decompose, dict(als_decompose=_als(s_from_old_block=True))),
     ("ALS: U, V not refit", check_als_decompose, dict(als_decompose=_als(keep_factors=True))),
     ("ALS: block refit from the first round's factors", check_als_decompose,
