@@ -65,6 +65,7 @@ WORKLOADS = {
     "reconstruct60": dict(layers=60, shapes="SHAPES_60", rank=256, bands=6, tokens=0, seed=5),
     "decompose26": dict(layers=26, shapes="SHAPES_26", rank=128, bands=4, tokens=0, seed=6),
     "decompose60": dict(layers=60, shapes="SHAPES_60", rank=256, bands=6, tokens=0, seed=7),
+    "tiny4": dict(layers=4, rank=16, bands=2, tokens=8, seed=1),
 }
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32
 
@@ -949,6 +950,101 @@ def bench_decompose(args, torch, np, tb, gen):
     print(json.dumps(line), flush=True)
 
 
+def bench_tiny(args, torch, np, tb, gen):
+    """The tiny fp32 stack: 4 layers, G = 2, one 512 -> 256 projection per layer, rank 16, 8 tokens.  Its
+    bundle comes from the GPU decomposition of the workload's weights (setup, untimed); a step is the four
+    layers' band select and tb_linear_forward (fp32).  Bound by launch latency, not by HBM: the figure is
+    reported with its time per call."""
+    wl = dict(WORKLOADS["tiny4"])
+    L, R, G = wl["layers"], wl["rank"], wl["bands"]
+    M = wl["tokens"] if args.tokens is None else args.tokens
+    weights, x_host = gen.tiny_stack(wl["seed"])
+    O, I = weights[0].shape
+    dev = "cuda"
+    t_setup = time.time()
+    wd = [torch.from_numpy(w.astype(np.float32)).to(dev) for w in weights]
+    bun = tb.decompose(wd, G, R, seed=wl["seed"])
+    xs = np.resize(x_host, (M, I)) if M != x_host.shape[0] else x_host
+    x = torch.from_numpy(xs.astype(np.float32)).to(dev)
+    y = torch.empty((M, O), dtype=torch.float32, device=dev)
+    nb = ctypes.c_size_t(0)
+    assert tb.lib.tb_linear_forward_workspace_size(M, O, I, R, tb.TB_F32, ctypes.byref(nb)) == 0
+    ws = tb.workspace_for(nb.value)
+    torch.cuda.synchronize()
+    t_setup = time.time() - t_setup
+    fwd, band_idx, bout = tb.lib.tb_linear_forward, tb.lib.tb_band_index, ctypes.c_int32()
+
+    def build_calls(handle):
+        stream = ctypes.c_void_p(handle)
+        return [(x.data_ptr(), bun["s"][l].data_ptr(), bun["W0"][bun["band"][l]].data_ptr(), bun["U"][l].data_ptr(),
+                 bun["V"][l].data_ptr(), y.data_ptr(), M, O, I, R, tb.TB_F32, ws.data_ptr(), ws.numel(), stream)
+                for l in range(L)]
+
+    def make_step(handle):
+        calls = build_calls(handle)
+
+        def run():
+            for l in range(L):
+                band_idx(L, G, l, ctypes.byref(bout))
+                if fwd(*calls[l]):
+                    raise RuntimeError(tb.lib.tb_last_error().decode())
+        return run
+
+    step = make_step(torch.cuda.current_stream().cuda_stream)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms, per_step = timed_steps(torch, lambda k: step(), args.steps)
+    if tb.workspace_error_word() != 0:
+        raise RuntimeError("a bounded wait in the projection kernel timed out")
+    graph = None
+    if not args.no_graph:
+        g_ms, g_per, clocks = graph_leg(torch, make_step, args.steps, [y])
+        graph = {"ms_per_step": round(g_ms, 5), **spread(g_per), "gpu": clocks,
+                 "value": round(L * call_bytes(M, O, I, R, e=4) / (g_ms * 1e-3) / 1e9, 3)}
+    step_bytes = L * call_bytes(M, O, I, R, e=4)
+    value = step_bytes / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        host = [{k: bun[k][l].cpu().numpy().astype(np.float64) for k in ("s", "U", "V")} for l in range(L)]
+        w0h = [t.cpu().numpy().astype(np.float64) for t in bun["W0"]]
+        x64 = xs.astype(np.float64)
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 2.0):
+            for l in range(L):
+                oracle.forward(x64, host[l]["s"], w0h[bun["band"][l]], host[l]["U"], host[l]["V"])
+            n += 1
+        secs = time.perf_counter() - t0
+        cpu = {"value": round(n * step_bytes / secs / 1e9, 4), "unit": "GB/s", "cores": int(_blas_threads()),
+               "kind": "oracle", "sample": f"the whole 4-layer step, {n} times, float64 NumPy, {secs:.1f} s",
+               "ms_per_step": round(secs / n * 1e3, 4), **_host_info()}
+    line = {
+        "metric": "theta-bundle projection TFLOP/s (prefill M) and GB/s (decode M), % of roofline",
+        "value": round(value, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"tiny4: 4 layers, G={G}, one {I}->{O} projection per layer, rank {R}, {M} tokens, "
+                               "fp32, bundle from the GPU decomposition",
+                   "layers": L, "bands": G, "rank": R, "tokens": M, "step_bytes": step_bytes,
+                   "us_per_call": round(ms * 1e3 / L, 2), "parallelism": "single-gpu"},
+        "trials": spread(per_step),
+        "graph": graph,
+        "roofline": {"bound": "hbm", "achieved": round(value, 3), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(value / 8000.0, 5), "traffic": None,
+                     "kernel": "decode_kernel<float,1,*>", "launches_per_call": 1, "calls_per_step": L,
+                     "note": "0.6 MB per call: launch latency bounds it, not HBM"},
+        "cpu_baseline": cpu,
+    }
+    prof = profile_durations(f"tiny4_M{M}_G{G}")
+    if prof is not None:
+        per_call = call_bytes(M, O, I, R, e=4)
+        line["roofline"]["profile"] = {**prof, "frac_from_profile": round(
+            per_call / (prof["avg_call_us"] * 1e-6) / 1e9 / 8000.0, 5)}
+    print(f"# setup {t_setup:.1f}s  step {ms:.4f} ms", file=sys.stderr)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -970,6 +1066,8 @@ def main():
         bench_reconstruct(args, torch, np, tb, gen)
     elif args.workload.startswith("decompose"):
         bench_decompose(args, torch, np, tb, gen)
+    elif args.workload == "tiny4":
+        bench_tiny(args, torch, np, tb, gen)
     else:
         bench_forward(args, torch, np, tb, gen)
 
