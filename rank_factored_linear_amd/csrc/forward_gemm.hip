@@ -864,17 +864,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 // ---------------------------------------------------------------------------
 namespace xv {
 
-constexpr int BM = 64, BN = 256, BK = 64, kThreads = 256;
+// T tiles are BM tokens x BN columns: BN = 256 for ranks above 128, BN = 128
+// otherwise (a 256-column tile would load and multiply a dead half of V).
+// Four waves: with BN = 256 each takes 64 columns of all 64 rows (2 x 2
+// products of 32 x 32), with BN = 128 a 32-row x 64-column quarter (1 x 2).
+constexpr int BM = 64, BK = 64, kThreads = 256;
 constexpr int kXPitch = BK * 2 + 16;   // 144-byte rows of the x tile
-constexpr int kVPitch = BN * 2 + 64;   // 576-byte rows of the V tile: 16 banks of skew per row
 constexpr int kXTile = BM * kXPitch;   // 9 KB
-constexpr int kVTile = BK * kVPitch;   // 36 KB
-constexpr int kRingBytes = 2 * kVTile + 2 * kXTile;  // [V0][V1][X0][X1]
-constexpr int kPartFloats = BM * BN;
 // x tiles are read by one column block of T only (rank <= 256), while every
 // row block re-reads the V tiles: x is loaded non-temporal (the NT bit of the
 // buffer load's cache policy) so that it does not push V out of L2.
 constexpr int kXPolicy = 2;
+
+template <int BN>
+struct Geo {
+  static constexpr int kVPitch = BN * 2 + 64;     // bytes per row of the V tile: 16 banks of skew per row
+  static constexpr int kVTile = BK * kVPitch;     // 36 or 20 KB
+  static constexpr int kRingBytes = 2 * kVTile + 2 * kXTile;  // [V0][V1][X0][X1]
+  static constexpr int kPartFloats = BM * BN;
+  static constexpr int VL = BN / 8;               // lanes per V row (16-byte chunks)
+  static constexpr int VR = kThreads / VL;        // V rows per staging pass
+  static constexpr int VQ = BK / VR;              // V loads per lane and k-tile
+  static constexpr int AI = BN == 256 ? 2 : 1;    // 32-row products per wave
+  static constexpr int AJ = 2;                    // 32-column products per wave
+  static constexpr int kPieces = AI * AJ * 4;     // 16-byte pieces of a lane's accumulators
+  __device__ static int row0(int w) { return BN == 256 ? 0 : 32 * (w >> 1); }
+  __device__ static int col0(int w) { return BN == 256 ? 64 * w : 64 * (w & 1); }
+};
+static_assert(Geo<256>::VQ * Geo<256>::VR == BK && Geo<128>::VQ * Geo<128>::VR == BK, "V staging covers a k-tile");
+static_assert(Geo<128>::kPartFloats * 4 == Geo<128>::kPieces * kThreads * 16, "partial = every lane's pieces");
+static_assert(Geo<256>::kPartFloats * 4 == Geo<256>::kPieces * kThreads * 16, "partial = every lane's pieces");
 
 // One projection of a launch: its x, V and T.
 struct Member {
@@ -895,51 +914,56 @@ struct Args {
   int KS, kps;     // k-slices and k-tiles per slice
   unsigned* ctrl;
   const unsigned* err;  // sticky error word: while set, nothing is published and no counter is touched
-  float* part;     // [RB * CB][KS][kPartFloats]
+  float* part;     // [RB * CB][KS][BM * BN]
   int polls;       // bound of a slice's wait for the other slices of its tile
 };
 
 struct Lanes {
-  lds_byte* x_rd;   // A fragment: row lane%32, k half lane/32
+  lds_byte* x_rd;   // A fragment: row row0(w) + lane%32, k half lane/32
   lds_byte* v_rd0;  // transposing B reads, buffer 0 / 1
   lds_byte* v_rd1;
   lds_byte* x_wr;   // x staging: row tid/8, chunk tid%8
-  lds_byte* v_wr0;  // V staging: k-row tid/32, chunk tid%32, buffer 0 / 1
+  lds_byte* v_wr0;  // V staging: k-row tid/VL, chunk tid%VL, buffer 0 / 1
   lds_byte* v_wr1;
 };
 
+template <int BN>
 __device__ __forceinline__ Lanes make_lanes(uint8_t* ring) {
+  using G = Geo<BN>;
   lds_byte* base = (lds_byte*)ring;
   const int tid = int(threadIdx.x), w = tid / kWave, l = tid % kWave, lr = l & 31, hi = l >> 5;
   const int g = l >> 4, j16 = l & 15;
-  const int vrow = 8 * (g >> 1) + (j16 >> 2), vcol = 64 * w + 16 * (g & 1) + 4 * (j16 & 3);
+  const int vrow = 8 * (g >> 1) + (j16 >> 2), vcol = G::col0(w) + 16 * (g & 1) + 4 * (j16 & 3);
   Lanes ln;
-  ln.x_rd = opaque(base + 2 * kVTile + lr * kXPitch + hi * 16);
-  ln.v_rd0 = opaque(base + vrow * kVPitch + vcol * 2);
-  ln.v_rd1 = opaque(base + kVTile + vrow * kVPitch + vcol * 2);
-  ln.x_wr = opaque(base + 2 * kVTile + (tid >> 3) * kXPitch + (tid & 7) * 16);
-  ln.v_wr0 = opaque(base + (tid >> 5) * kVPitch + (tid & 31) * 16);
-  ln.v_wr1 = opaque(base + kVTile + (tid >> 5) * kVPitch + (tid & 31) * 16);
+  ln.x_rd = opaque(base + 2 * G::kVTile + (G::row0(w) + lr) * kXPitch + hi * 16);
+  ln.v_rd0 = opaque(base + vrow * G::kVPitch + vcol * 2);
+  ln.v_rd1 = opaque(base + G::kVTile + vrow * G::kVPitch + vcol * 2);
+  ln.x_wr = opaque(base + 2 * G::kVTile + (tid >> 3) * kXPitch + (tid & 7) * 16);
+  ln.v_wr0 = opaque(base + (tid / G::VL) * G::kVPitch + (tid % G::VL) * 16);
+  ln.v_wr1 = opaque(base + G::kVTile + (tid / G::VL) * G::kVPitch + (tid % G::VL) * 16);
   return ln;
 }
 
 struct Src {
   __amdgpu_buffer_rsrc_t rx, rv;
-  int xoff, voff;     // lane byte offsets: x row tid/8 chunk tid%8; V k-row tid/32 chunk tid%32
-  int xstep, vstep;   // bytes of 32 x rows / 8 V rows
+  int xoff, voff;     // lane byte offsets: x row tid/8 chunk tid%8; V k-row tid/VL chunk tid%VL
+  int xstep, vstep;   // bytes of 32 x rows / VR V rows
   int I, ncols;       // reduction length; valid columns of this column block
 };
 
-__device__ __forceinline__ void fetch(const Src& s, int kt, u32x4 (&px)[2], u32x4 (&pv)[8]) {
+template <int BN>
+__device__ __forceinline__ void fetch(const Src& s, int kt, u32x4 (&px)[2], u32x4 (&pv)[Geo<BN>::VQ]) {
 #pragma unroll
   for (int q = 0; q < 2; ++q) px[q] = __builtin_amdgcn_raw_buffer_load_b128(s.rx, s.xoff, kt * BK * 2 + q * s.xstep, kXPolicy);
 #pragma unroll
-  for (int q = 0; q < 8; ++q)
-    pv[q] = __builtin_amdgcn_raw_buffer_load_b128(s.rv, s.voff, kt * 8 * s.vstep + q * s.vstep, 0);
+  for (int q = 0; q < Geo<BN>::VQ; ++q)
+    pv[q] = __builtin_amdgcn_raw_buffer_load_b128(s.rv, s.voff, kt * Geo<BN>::VQ * s.vstep + q * s.vstep, 0);
 }
 
-template <int BUF>
-__device__ __forceinline__ void stage(const Lanes& ln, const Src& s, int kt, u32x4 (&px)[2], u32x4 (&pv)[8]) {
+template <int BN, int BUF>
+__device__ __forceinline__ void stage(const Lanes& ln, const Src& s, int kt, u32x4 (&px)[2],
+                                      u32x4 (&pv)[Geo<BN>::VQ]) {
+  using G = Geo<BN>;
   // x chunks at or past in_dim would read the next row: zero them.  V rows
   // past in_dim read as zero from the buffer bound; V columns past r of this
   // block would read the next row: zero them.
@@ -949,29 +973,31 @@ __device__ __forceinline__ void stage(const Lanes& ln, const Src& s, int kt, u32
     for (int q = 0; q < 2; ++q) px[q] = keep ? px[q] : u32x4{0u, 0u, 0u, 0u};
   }
   if (s.ncols < BN) {
-    const bool keep = int(threadIdx.x & 31) * 8 < s.ncols;
+    const bool keep = int(threadIdx.x % G::VL) * 8 < s.ncols;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) pv[q] = keep ? pv[q] : u32x4{0u, 0u, 0u, 0u};
+    for (int q = 0; q < G::VQ; ++q) pv[q] = keep ? pv[q] : u32x4{0u, 0u, 0u, 0u};
   }
 #pragma unroll
   for (int q = 0; q < 2; ++q) *reinterpret_cast<lds_u32x4*>(ln.x_wr + BUF * kXTile + q * 32 * kXPitch) = px[q];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) *reinterpret_cast<lds_u32x4*>((BUF ? ln.v_wr1 : ln.v_wr0) + q * 8 * kVPitch) = pv[q];
+  for (int q = 0; q < G::VQ; ++q)
+    *reinterpret_cast<lds_u32x4*>((BUF ? ln.v_wr1 : ln.v_wr0) + q * G::VR * G::kVPitch) = pv[q];
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-template <int BUF>
-__device__ __forceinline__ void read_frags(const Lanes& ln, int st, u32x4 (&fa)[2], u32x4 (&fb)[2]) {
+template <int BN, int BUF>
+__device__ __forceinline__ void read_frags(const Lanes& ln, int st, u32x4 (&fa)[Geo<BN>::AI], u32x4 (&fb)[2]) {
+  using G = Geo<BN>;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < G::AI; ++i)
     fa[i] = *reinterpret_cast<const lds_u32x4*>(ln.x_rd + BUF * kXTile + i * 32 * kXPitch + st * 32);
   lds_byte* vr = BUF ? ln.v_rd1 : ln.v_rd0;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vr + (16 * st) * kVPitch + 64 * j));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vr + (16 * st + 4) * kVPitch + 64 * j));
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vr + (16 * st) * G::kVPitch + 64 * j));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vr + (16 * st + 4) * G::kVPitch + 64 * j));
     fb[j] = u32x4{uint32_t(uint16_t(lo[0])) | (uint32_t(uint16_t(lo[1])) << 16),
                   uint32_t(uint16_t(lo[2])) | (uint32_t(uint16_t(lo[3])) << 16),
                   uint32_t(uint16_t(hi[0])) | (uint32_t(uint16_t(hi[1])) << 16),
@@ -979,36 +1005,41 @@ __device__ __forceinline__ void read_frags(const Lanes& ln, int st, u32x4 (&fa)[
   }
 }
 
-__device__ __forceinline__ void mma_step(const u32x4 (&fa)[2], const u32x4 (&fb)[2], f32x16 (&acc)[2][2]) {
+template <int AI>
+__device__ __forceinline__ void mma_step(const u32x4 (&fa)[AI], const u32x4 (&fb)[2], f32x16 (&acc)[AI][2]) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < AI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[i]),
                                                           __builtin_bit_cast(bf16x8, fb[j]), acc[i][j], 0, 0, 0);
 }
 
-template <int BUF>
-__device__ __forceinline__ void multiply_tile(const Lanes& ln, f32x16 (&acc)[2][2]) {
-  u32x4 fa0[2], fb0[2], fa1[2], fb1[2];
-  read_frags<BUF>(ln, 0, fa0, fb0);
-  read_frags<BUF>(ln, 1, fa1, fb1);
+template <int BN, int BUF>
+__device__ __forceinline__ void multiply_tile(const Lanes& ln, f32x16 (&acc)[Geo<BN>::AI][2]) {
+  constexpr int AI = Geo<BN>::AI;
+  u32x4 fa0[AI], fb0[2], fa1[AI], fb1[2];
+  read_frags<BN, BUF>(ln, 0, fa0, fb0);
+  read_frags<BN, BUF>(ln, 1, fa1, fb1);
   __builtin_amdgcn_sched_barrier(0);
-  mma_step(fa0, fb0, acc);
+  mma_step<AI>(fa0, fb0, acc);
   __builtin_amdgcn_sched_barrier(0);
-  read_frags<BUF>(ln, 2, fa0, fb0);
+  read_frags<BN, BUF>(ln, 2, fa0, fb0);
   __builtin_amdgcn_sched_barrier(0);
-  mma_step(fa1, fb1, acc);
+  mma_step<AI>(fa1, fb1, acc);
   __builtin_amdgcn_sched_barrier(0);
-  read_frags<BUF>(ln, 3, fa1, fb1);
+  read_frags<BN, BUF>(ln, 3, fa1, fb1);
   __builtin_amdgcn_sched_barrier(0);
-  mma_step(fa0, fb0, acc);
+  mma_step<AI>(fa0, fb0, acc);
   __builtin_amdgcn_sched_barrier(0);
-  mma_step(fa1, fb1, acc);
+  mma_step<AI>(fa1, fb1, acc);
 }
 
+template <int BN>
 __global__ __launch_bounds__(kThreads) void xv_kernel(Args a) {
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes];
+  using G = Geo<BN>;
+  constexpr int AI = G::AI, VQ = G::VQ;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[G::kRingBytes];
   __shared__ unsigned s_last;
   const int tid = int(threadIdx.x);
   const int per_member = a.RB * a.CB * a.KS;
@@ -1018,45 +1049,45 @@ __global__ __launch_bounds__(kThreads) void xv_kernel(Args a) {
   const int rb = ltile / a.CB, cb = ltile % a.CB;
   const int m0 = rb * BM, n0 = cb * BN;
   const int kb = ks * a.kps, ke = min(a.KT, kb + a.kps);
-  const Lanes ln = make_lanes(ring);
+  const Lanes ln = make_lanes<BN>(ring);
   const uint32_t err_at_entry = load_error_word(a.err);
   Src s;
   s.rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(mb.x + size_t(m0) * a.I), 0,
                                           min(a.M - m0, BM) * a.I * 2, kRsrcFlags);
   s.rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(mb.v + n0), 0, (a.I * a.R - n0) * 2, kRsrcFlags);
   s.xoff = (tid >> 3) * a.I * 2 + (tid & 7) * 16;
-  s.voff = (tid >> 5) * a.R * 2 + (tid & 31) * 16;
+  s.voff = (tid / G::VL) * a.R * 2 + (tid % G::VL) * 16;
   s.xstep = 32 * a.I * 2;
-  s.vstep = 8 * a.R * 2;
+  s.vstep = G::VR * a.R * 2;
   s.I = a.I;
   s.ncols = min(BN, a.R - n0);
 
-  f32x16 acc[2][2];
+  f32x16 acc[AI][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < AI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
   if (kb < ke) {
     const int n = ke - kb;
-    u32x4 px0[2], pv0[8], px1[2], pv1[8];
-    fetch(s, kb, px0, pv0);
-    fetch(s, min(kb + 1, ke - 1), px1, pv1);
-    stage<0>(ln, s, kb, px0, pv0);
+    u32x4 px0[2], pv0[VQ], px1[2], pv1[VQ];
+    fetch<BN>(s, kb, px0, pv0);
+    fetch<BN>(s, min(kb + 1, ke - 1), px1, pv1);
+    stage<BN, 0>(ln, s, kb, px0, pv0);
     __syncthreads();
     for (int k = 0; k < n; k += 2) {
       const int k1 = min(kb + k + 1, ke - 1), k2 = min(kb + k + 2, ke - 1), k3 = min(kb + k + 3, ke - 1);
-      fetch(s, k2, px0, pv0);
+      fetch<BN>(s, k2, px0, pv0);
       __builtin_amdgcn_sched_barrier(0);
-      multiply_tile<0>(ln, acc);
+      multiply_tile<BN, 0>(ln, acc);
       __builtin_amdgcn_sched_barrier(0);
-      stage<1>(ln, s, k1, px1, pv1);
+      stage<BN, 1>(ln, s, k1, px1, pv1);
       __syncthreads();
       if (k + 1 < n) {
-        fetch(s, k3, px1, pv1);
+        fetch<BN>(s, k3, px1, pv1);
         __builtin_amdgcn_sched_barrier(0);
-        multiply_tile<1>(ln, acc);
+        multiply_tile<BN, 1>(ln, acc);
         __builtin_amdgcn_sched_barrier(0);
-        stage<0>(ln, s, k2, px0, pv0);
+        stage<BN, 0>(ln, s, k2, px0, pv0);
         __syncthreads();
       }
     }
@@ -1068,16 +1099,17 @@ __global__ __launch_bounds__(kThreads) void xv_kernel(Args a) {
   if (s_last != 0u) return;
   __syncthreads();
   const int w = tid / kWave, l = tid % kWave, lr = l & 31, hi = l >> 5;
+  const int wr = G::row0(w), wc = G::col0(w);
   if (a.KS > 1) {
     // Partial in register order: 16-byte piece q = (2i + j) * 4 + c of every
     // lane.  Every slice of the tile then waits (bounded) for the others and
     // sums its share of the pieces over all KS partials in slice order, so
     // the result does not depend on arrival order.
-    float* blk = a.part + size_t(tile) * a.KS * kPartFloats;
+    float* blk = a.part + size_t(tile) * a.KS * G::kPartFloats;
     const __amdgpu_buffer_rsrc_t mine =
-        __builtin_amdgcn_make_buffer_rsrc(blk + size_t(ks) * kPartFloats, 0, kPartFloats * 4, kRsrcFlags);
+        __builtin_amdgcn_make_buffer_rsrc(blk + size_t(ks) * G::kPartFloats, 0, G::kPartFloats * 4, kRsrcFlags);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < AI; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -1102,13 +1134,13 @@ __global__ __launch_bounds__(kThreads) void xv_kernel(Args a) {
     }
     __syncthreads();
     if (s_last == 0u) return;  // timed out: the sticky error word makes the projection's y NaN
-    constexpr int kPieces = 16;
+    constexpr int kPieces = G::kPieces;
     const int p0 = ks * kPieces / a.KS, np = (ks + 1) * kPieces / a.KS - p0;
     f32x4 sum[kPieces / 2];
     for (int k0 = 0; k0 < np; k0 += kPieces / 2) {
       for (int q = 0; q < a.KS; ++q) {
         const __amdgpu_buffer_rsrc_t src =
-            __builtin_amdgcn_make_buffer_rsrc(blk + size_t(q) * kPartFloats, 0, kPartFloats * 4, kRsrcFlags);
+            __builtin_amdgcn_make_buffer_rsrc(blk + size_t(q) * G::kPartFloats, 0, G::kPartFloats * 4, kRsrcFlags);
         u32x4 d[kPieces / 2];
 #pragma unroll
         for (int k = 0; k < kPieces / 2; ++k)
@@ -1125,11 +1157,11 @@ __global__ __launch_bounds__(kThreads) void xv_kernel(Args a) {
       for (int k = 0; k < kPieces / 2; ++k) {
         if (k0 + k >= np) break;
         const int pc = p0 + k0 + k, i = pc / 8, j = (pc / 4) % 2, bb = pc % 4;
-        const int n = n0 + 64 * w + 32 * j + lr;
+        const int n = n0 + wc + 32 * j + lr;
         if (n >= a.R) continue;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int m = m0 + 32 * i + 8 * bb + 4 * hi + e;
+          const int m = m0 + wr + 32 * i + 8 * bb + 4 * hi + e;
           if (m < a.M) mb.t[size_t(m) * a.R + n] = bf16_t{f32_to_bf16(sum[k][e])};
         }
       }
@@ -1144,20 +1176,23 @@ __global__ __launch_bounds__(kThreads) void xv_kernel(Args a) {
     return;
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < AI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int n = n0 + 64 * w + 32 * j + lr;
+      const int n = n0 + wc + 32 * j + lr;
       if (n >= a.R) continue;
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int m = m0 + 32 * i + 8 * bb + 4 * hi + e;
+          const int m = m0 + wr + 32 * i + 8 * bb + 4 * hi + e;
           if (m < a.M) mb.t[size_t(m) * a.R + n] = bf16_t{f32_to_bf16(acc[i][j][4 * bb + e])};
         }
     }
 }
+
+// Column-block width of T for a rank.
+inline int block_cols(int64_t rank) { return rank <= 128 ? 128 : 256; }
 
 }  // namespace xv
 
@@ -1209,8 +1244,9 @@ GemmPlan plan_gemm(int n, const int64_t* out_dims, int64_t m, int64_t in_dim, in
   // x . V: enough k-slices to give every compute unit a workgroup, each at
   // least two k-tiles long and at most 16 partials per tile.
   if (rank > 0) {
+    p.xv_bn = xv::block_cols(rank);
     p.xv_rb = int((m + xv::BM - 1) / xv::BM);
-    p.xv_cb = int((rank + xv::BN - 1) / xv::BN);
+    p.xv_cb = int((rank + p.xv_bn - 1) / p.xv_bn);
     p.xv_kt = int((in_dim + xv::BK - 1) / xv::BK);
     const int64_t tiles = int64_t(n) * p.xv_rb * p.xv_cb;
     int64_t ks = tiles >= cus ? 1 : cus / tiles;
@@ -1219,7 +1255,7 @@ GemmPlan plan_gemm(int n, const int64_t* out_dims, int64_t m, int64_t in_dim, in
     p.xv_kps = int((p.xv_kt + ks - 1) / ks);
     p.xv_ks = int((p.xv_kt + p.xv_kps - 1) / p.xv_kps);
     p.off_xvpart = off;
-    if (p.xv_ks > 1) off = align_up(off + size_t(tiles) * p.xv_ks * xv::kPartFloats * 4, 256);
+    if (p.xv_ks > 1) off = align_up(off + size_t(tiles) * p.xv_ks * xv::BM * p.xv_bn * 4, 256);
   }
   p.bytes = off;
   p.start[0] = 0;
@@ -1281,8 +1317,9 @@ hipError_t launch_forward_gemm(const GemmPlan& p, const Projection* projs, int64
     a.err = err_word;
     a.part = reinterpret_cast<float*>(data + p.off_xvpart);
     a.polls = decode_wait_polls();
-    hipLaunchKernelGGL(xv::xv_kernel, dim3(unsigned(n * p.xv_rb * p.xv_cb * p.xv_ks)), dim3(xv::kThreads), 0, stream,
-                       a);
+    const dim3 grid(unsigned(n * p.xv_rb * p.xv_cb * p.xv_ks));
+    if (p.xv_bn == 128) hipLaunchKernelGGL(xv::xv_kernel<128>, grid, dim3(xv::kThreads), 0, stream, a);
+    else hipLaunchKernelGGL(xv::xv_kernel<256>, grid, dim3(xv::kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   } else if (rank > 0) {

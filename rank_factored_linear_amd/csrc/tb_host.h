@@ -121,7 +121,8 @@ struct GemmPlan {
   int split_tiles;      // leading tiles split into S k-slices of kps k-tiles (the remainder round)
   int S, kps;
   int xcd_major;        // workgroup positions spread XCD-major (grid a multiple of 8)
-  int xv_rb, xv_cb;     // x . V on the aligned path: 64-token row blocks, 256-column blocks of T (per member)
+  int xv_rb, xv_cb;     // x . V on the aligned path: 64-token row blocks, column blocks of T (per member)
+  int xv_bn;            // columns of a T block: 128 for ranks up to 128, else 256
   int xv_kt, xv_ks, xv_kps;  // its k-tiles (64), k-slices and k-tiles per slice
   size_t off_t[kMaxProjections];  // each member's T (m x rank bf16) from the data base
   size_t off_xvpart, off_part, bytes;
