@@ -864,20 +864,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 // ---------------------------------------------------------------------------
 namespace xv {
 
-// T tiles are BM tokens x BN columns: BN = 256 for ranks above 128, BN = 128
-// otherwise (a 256-column tile would load and multiply a dead half of V).
-// Four waves: with BN = 256 each takes 64 columns of all 64 rows (2 x 2
-// products of 32 x 32), with BN = 128 a 32-row x 64-column quarter (1 x 2).
-constexpr int BM = 64, BK = 64, kThreads = 256;
+// T tiles are BM tokens x BN columns.  Four waves: with BN = 256 each takes
+// 64 columns of all BM rows, with BN = 128 a (BM/2)-row x 64-column quarter;
+// products of 32 x 32.
+constexpr int BK = 64, kThreads = 256;
 constexpr int kXPitch = BK * 2 + 16;   // 144-byte rows of the x tile
-constexpr int kXTile = BM * kXPitch;   // 9 KB
 // x tiles are read by one column block of T only (rank <= 256), while every
 // row block re-reads the V tiles: x is loaded non-temporal (the NT bit of the
 // buffer load's cache policy) so that it does not push V out of L2.
 constexpr int kXPolicy = 2;
 
-template <int BN>
+template <int BM, int BN>
 struct Geo {
+  static constexpr int kXTile = BM * kXPitch;     // 9 or 18 KB
+  static constexpr int XQ = BM / 32;              // x loads per lane and k-tile (32 rows per pass)
   static constexpr int kVPitch = BN * 2 + 64;     // bytes per row of the V tile: 16 banks of skew per row
   static constexpr int kVTile = BK * kVPitch;     // 36 or 20 KB
   static constexpr int kRingBytes = 2 * kVTile + 2 * kXTile;  // [V0][V1][X0][X1]
@@ -885,15 +885,16 @@ struct Geo {
   static constexpr int VL = BN / 8;               // lanes per V row (16-byte chunks)
   static constexpr int VR = kThreads / VL;        // V rows per staging pass
   static constexpr int VQ = BK / VR;              // V loads per lane and k-tile
-  static constexpr int AI = BN == 256 ? 2 : 1;    // 32-row products per wave
+  static constexpr int WR = BN == 256 ? BM : BM / 2;  // rows of a wave
+  static constexpr int AI = WR / 32;              // 32-row products per wave
   static constexpr int AJ = 2;                    // 32-column products per wave
   static constexpr int kPieces = AI * AJ * 4;     // 16-byte pieces of a lane's accumulators
-  __device__ static int row0(int w) { return BN == 256 ? 0 : 32 * (w >> 1); }
+  __device__ static int row0(int w) { return BN == 256 ? 0 : WR * (w >> 1); }
   __device__ static int col0(int w) { return BN == 256 ? 64 * w : 64 * (w & 1); }
+  static_assert(VQ * VR == BK, "V staging covers a k-tile");
+  static_assert(kPartFloats * 4 == kPieces * kThreads * 16, "partial = every lane's pieces");
+  static_assert(AI >= 1 && AI <= 2, "one or two row products per wave");
 };
-static_assert(Geo<256>::VQ * Geo<256>::VR == BK && Geo<128>::VQ * Geo<128>::VR == BK, "V staging covers a k-tile");
-static_assert(Geo<128>::kPartFloats * 4 == Geo<128>::kPieces * kThreads * 16, "partial = every lane's pieces");
-static_assert(Geo<256>::kPartFloats * 4 == Geo<256>::kPieces * kThreads * 16, "partial = every lane's pieces");
 
 // One projection of a launch: its x, V and T.
 struct Member {
@@ -927,9 +928,9 @@ struct Lanes {
   lds_byte* v_wr1;
 };
 
-template <int BN>
+template <int BM, int BN>
 __device__ __forceinline__ Lanes make_lanes(uint8_t* ring) {
-  using G = Geo<BN>;
+  using G = Geo<BM, BN>;
   lds_byte* base = (lds_byte*)ring;
   const int tid = int(threadIdx.x), w = tid / kWave, l = tid % kWave, lr = l & 31, hi = l >> 5;
   const int g = l >> 4, j16 = l & 15;
@@ -951,26 +952,29 @@ struct Src {
   int I, ncols;       // reduction length; valid columns of this column block
 };
 
-template <int BN>
-__device__ __forceinline__ void fetch(const Src& s, int kt, u32x4 (&px)[2], u32x4 (&pv)[Geo<BN>::VQ]) {
+template <int BM, int BN>
+__device__ __forceinline__ void fetch(const Src& s, int kt, u32x4 (&px)[Geo<BM, BN>::XQ],
+                                      u32x4 (&pv)[Geo<BM, BN>::VQ]) {
+  using G = Geo<BM, BN>;
 #pragma unroll
-  for (int q = 0; q < 2; ++q) px[q] = __builtin_amdgcn_raw_buffer_load_b128(s.rx, s.xoff, kt * BK * 2 + q * s.xstep, kXPolicy);
+  for (int q = 0; q < G::XQ; ++q)
+    px[q] = __builtin_amdgcn_raw_buffer_load_b128(s.rx, s.xoff, kt * BK * 2 + q * s.xstep, kXPolicy);
 #pragma unroll
-  for (int q = 0; q < Geo<BN>::VQ; ++q)
-    pv[q] = __builtin_amdgcn_raw_buffer_load_b128(s.rv, s.voff, kt * Geo<BN>::VQ * s.vstep + q * s.vstep, 0);
+  for (int q = 0; q < G::VQ; ++q)
+    pv[q] = __builtin_amdgcn_raw_buffer_load_b128(s.rv, s.voff, kt * G::VQ * s.vstep + q * s.vstep, 0);
 }
 
-template <int BN, int BUF>
-__device__ __forceinline__ void stage(const Lanes& ln, const Src& s, int kt, u32x4 (&px)[2],
-                                      u32x4 (&pv)[Geo<BN>::VQ]) {
-  using G = Geo<BN>;
+template <int BM, int BN, int BUF>
+__device__ __forceinline__ void stage(const Lanes& ln, const Src& s, int kt, u32x4 (&px)[Geo<BM, BN>::XQ],
+                                      u32x4 (&pv)[Geo<BM, BN>::VQ]) {
+  using G = Geo<BM, BN>;
   // x chunks at or past in_dim would read the next row: zero them.  V rows
   // past in_dim read as zero from the buffer bound; V columns past r of this
   // block would read the next row: zero them.
   if (s.I - kt * BK < BK) {
     const bool keep = int(threadIdx.x & 7) * 8 < s.I - kt * BK;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) px[q] = keep ? px[q] : u32x4{0u, 0u, 0u, 0u};
+    for (int q = 0; q < G::XQ; ++q) px[q] = keep ? px[q] : u32x4{0u, 0u, 0u, 0u};
   }
   if (s.ncols < BN) {
     const bool keep = int(threadIdx.x % G::VL) * 8 < s.ncols;
@@ -978,7 +982,7 @@ __device__ __forceinline__ void stage(const Lanes& ln, const Src& s, int kt, u32
     for (int q = 0; q < G::VQ; ++q) pv[q] = keep ? pv[q] : u32x4{0u, 0u, 0u, 0u};
   }
 #pragma unroll
-  for (int q = 0; q < 2; ++q) *reinterpret_cast<lds_u32x4*>(ln.x_wr + BUF * kXTile + q * 32 * kXPitch) = px[q];
+  for (int q = 0; q < G::XQ; ++q) *reinterpret_cast<lds_u32x4*>(ln.x_wr + BUF * G::kXTile + q * 32 * kXPitch) = px[q];
 #pragma unroll
   for (int q = 0; q < G::VQ; ++q)
     *reinterpret_cast<lds_u32x4*>((BUF ? ln.v_wr1 : ln.v_wr0) + q * G::VR * G::kVPitch) = pv[q];
@@ -987,12 +991,12 @@ __device__ __forceinline__ void stage(const Lanes& ln, const Src& s, int kt, u32
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-template <int BN, int BUF>
-__device__ __forceinline__ void read_frags(const Lanes& ln, int st, u32x4 (&fa)[Geo<BN>::AI], u32x4 (&fb)[2]) {
-  using G = Geo<BN>;
+template <int BM, int BN, int BUF>
+__device__ __forceinline__ void read_frags(const Lanes& ln, int st, u32x4 (&fa)[Geo<BM, BN>::AI], u32x4 (&fb)[2]) {
+  using G = Geo<BM, BN>;
 #pragma unroll
   for (int i = 0; i < G::AI; ++i)
-    fa[i] = *reinterpret_cast<const lds_u32x4*>(ln.x_rd + BUF * kXTile + i * 32 * kXPitch + st * 32);
+    fa[i] = *reinterpret_cast<const lds_u32x4*>(ln.x_rd + BUF * G::kXTile + i * 32 * kXPitch + st * 32);
   lds_byte* vr = BUF ? ln.v_rd1 : ln.v_rd0;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -1015,30 +1019,30 @@ __device__ __forceinline__ void mma_step(const u32x4 (&fa)[AI], const u32x4 (&fb
                                                           __builtin_bit_cast(bf16x8, fb[j]), acc[i][j], 0, 0, 0);
 }
 
-template <int BN, int BUF>
-__device__ __forceinline__ void multiply_tile(const Lanes& ln, f32x16 (&acc)[Geo<BN>::AI][2]) {
-  constexpr int AI = Geo<BN>::AI;
+template <int BM, int BN, int BUF>
+__device__ __forceinline__ void multiply_tile(const Lanes& ln, f32x16 (&acc)[Geo<BM, BN>::AI][2]) {
+  constexpr int AI = Geo<BM, BN>::AI;
   u32x4 fa0[AI], fb0[2], fa1[AI], fb1[2];
-  read_frags<BN, BUF>(ln, 0, fa0, fb0);
-  read_frags<BN, BUF>(ln, 1, fa1, fb1);
+  read_frags<BM, BN, BUF>(ln, 0, fa0, fb0);
+  read_frags<BM, BN, BUF>(ln, 1, fa1, fb1);
   __builtin_amdgcn_sched_barrier(0);
   mma_step<AI>(fa0, fb0, acc);
   __builtin_amdgcn_sched_barrier(0);
-  read_frags<BN, BUF>(ln, 2, fa0, fb0);
+  read_frags<BM, BN, BUF>(ln, 2, fa0, fb0);
   __builtin_amdgcn_sched_barrier(0);
   mma_step<AI>(fa1, fb1, acc);
   __builtin_amdgcn_sched_barrier(0);
-  read_frags<BN, BUF>(ln, 3, fa1, fb1);
+  read_frags<BM, BN, BUF>(ln, 3, fa1, fb1);
   __builtin_amdgcn_sched_barrier(0);
   mma_step<AI>(fa0, fb0, acc);
   __builtin_amdgcn_sched_barrier(0);
   mma_step<AI>(fa1, fb1, acc);
 }
 
-template <int BN>
+template <int BM, int BN>
 __global__ __launch_bounds__(kThreads) void xv_kernel(Args a) {
-  using G = Geo<BN>;
-  constexpr int AI = G::AI, VQ = G::VQ;
+  using G = Geo<BM, BN>;
+  constexpr int AI = G::AI, VQ = G::VQ, XQ = G::XQ;
   __shared__ __attribute__((aligned(16))) uint8_t ring[G::kRingBytes];
   __shared__ unsigned s_last;
   const int tid = int(threadIdx.x);
@@ -1049,7 +1053,7 @@ __global__ __launch_bounds__(kThreads) void xv_kernel(Args a) {
   const int rb = ltile / a.CB, cb = ltile % a.CB;
   const int m0 = rb * BM, n0 = cb * BN;
   const int kb = ks * a.kps, ke = min(a.KT, kb + a.kps);
-  const Lanes ln = make_lanes<BN>(ring);
+  const Lanes ln = make_lanes<BM, BN>(ring);
   const uint32_t err_at_entry = load_error_word(a.err);
   Src s;
   s.rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(mb.x + size_t(m0) * a.I), 0,
@@ -1069,25 +1073,25 @@ __global__ __launch_bounds__(kThreads) void xv_kernel(Args a) {
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
   if (kb < ke) {
     const int n = ke - kb;
-    u32x4 px0[2], pv0[VQ], px1[2], pv1[VQ];
-    fetch<BN>(s, kb, px0, pv0);
-    fetch<BN>(s, min(kb + 1, ke - 1), px1, pv1);
-    stage<BN, 0>(ln, s, kb, px0, pv0);
+    u32x4 px0[XQ], pv0[VQ], px1[XQ], pv1[VQ];
+    fetch<BM, BN>(s, kb, px0, pv0);
+    fetch<BM, BN>(s, min(kb + 1, ke - 1), px1, pv1);
+    stage<BM, BN, 0>(ln, s, kb, px0, pv0);
     __syncthreads();
     for (int k = 0; k < n; k += 2) {
       const int k1 = min(kb + k + 1, ke - 1), k2 = min(kb + k + 2, ke - 1), k3 = min(kb + k + 3, ke - 1);
-      fetch<BN>(s, k2, px0, pv0);
+      fetch<BM, BN>(s, k2, px0, pv0);
       __builtin_amdgcn_sched_barrier(0);
-      multiply_tile<BN, 0>(ln, acc);
+      multiply_tile<BM, BN, 0>(ln, acc);
       __builtin_amdgcn_sched_barrier(0);
-      stage<BN, 1>(ln, s, k1, px1, pv1);
+      stage<BM, BN, 1>(ln, s, k1, px1, pv1);
       __syncthreads();
       if (k + 1 < n) {
-        fetch<BN>(s, k3, px1, pv1);
+        fetch<BM, BN>(s, k3, px1, pv1);
         __builtin_amdgcn_sched_barrier(0);
-        multiply_tile<BN, 1>(ln, acc);
+        multiply_tile<BM, BN, 1>(ln, acc);
         __builtin_amdgcn_sched_barrier(0);
-        stage<BN, 0>(ln, s, k2, px0, pv0);
+        stage<BM, BN, 0>(ln, s, k2, px0, pv0);
         __syncthreads();
       }
     }
@@ -1191,7 +1195,11 @@ __global__ __launch_bounds__(kThreads) void xv_kernel(Args a) {
     }
 }
 
-// Column-block width of T for a rank.
+// Tile shape of T for a rank: 64 x 128 up to rank 128 (a 256-column tile
+// would load and multiply a dead half of V), else 64 x 256.  (128 x 128 at
+// rank 256, two workgroups per compute unit and a fifth fewer bytes per flop,
+// ran the 60-layer stack at 4096 tokens no faster.)
+inline int block_rows(int64_t) { return 64; }
 inline int block_cols(int64_t rank) { return rank <= 128 ? 128 : 256; }
 
 }  // namespace xv
@@ -1244,8 +1252,9 @@ GemmPlan plan_gemm(int n, const int64_t* out_dims, int64_t m, int64_t in_dim, in
   // x . V: enough k-slices to give every compute unit a workgroup, each at
   // least two k-tiles long and at most 16 partials per tile.
   if (rank > 0) {
+    p.xv_bm = xv::block_rows(rank);
     p.xv_bn = xv::block_cols(rank);
-    p.xv_rb = int((m + xv::BM - 1) / xv::BM);
+    p.xv_rb = int((m + p.xv_bm - 1) / p.xv_bm);
     p.xv_cb = int((rank + p.xv_bn - 1) / p.xv_bn);
     p.xv_kt = int((in_dim + xv::BK - 1) / xv::BK);
     const int64_t tiles = int64_t(n) * p.xv_rb * p.xv_cb;
@@ -1255,7 +1264,7 @@ GemmPlan plan_gemm(int n, const int64_t* out_dims, int64_t m, int64_t in_dim, in
     p.xv_kps = int((p.xv_kt + ks - 1) / ks);
     p.xv_ks = int((p.xv_kt + p.xv_kps - 1) / p.xv_kps);
     p.off_xvpart = off;
-    if (p.xv_ks > 1) off = align_up(off + size_t(tiles) * p.xv_ks * xv::BM * p.xv_bn * 4, 256);
+    if (p.xv_ks > 1) off = align_up(off + size_t(tiles) * p.xv_ks * p.xv_bm * p.xv_bn * 4, 256);
   }
   p.bytes = off;
   p.start[0] = 0;
@@ -1318,8 +1327,9 @@ hipError_t launch_forward_gemm(const GemmPlan& p, const Projection* projs, int64
     a.part = reinterpret_cast<float*>(data + p.off_xvpart);
     a.polls = decode_wait_polls();
     const dim3 grid(unsigned(n * p.xv_rb * p.xv_cb * p.xv_ks));
-    if (p.xv_bn == 128) hipLaunchKernelGGL(xv::xv_kernel<128>, grid, dim3(xv::kThreads), 0, stream, a);
-    else hipLaunchKernelGGL(xv::xv_kernel<256>, grid, dim3(xv::kThreads), 0, stream, a);
+    if (p.xv_bm != 64) return hipErrorInvalidValue;
+    if (p.xv_bn == 256) hipLaunchKernelGGL((xv::xv_kernel<64, 256>), grid, dim3(xv::kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((xv::xv_kernel<64, 128>), grid, dim3(xv::kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   } else if (rank > 0) {

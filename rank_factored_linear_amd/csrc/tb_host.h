@@ -122,7 +122,7 @@ struct GemmPlan {
   int S, kps;
   int xcd_major;        // workgroup positions spread XCD-major (grid a multiple of 8)
   int xv_rb, xv_cb;     // x . V on the aligned path: 64-token row blocks, column blocks of T (per member)
-  int xv_bn;            // columns of a T block: 128 for ranks up to 128, else 256
+  int xv_bm, xv_bn;     // tokens and columns of a T block
   int xv_kt, xv_ks, xv_kps;  // its k-tiles (64), k-slices and k-tiles per slice
   size_t off_t[kMaxProjections];  // each member's T (m x rank bf16) from the data base
   size_t off_xvpart, off_part, bytes;
